@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 decode path on one MI355X.
+
+Default workload: a Llama-2-110M-shaped decode step at batch 1 (12 layers of
+wq/wk/wv/wo 768x768, w1/w3 2048x768, w2 768x2048, plus a 32000x768
+classifier; 85 Q8_0 matvecs per step with weights N(0, 0.02) and a fresh
+N(0,1) activation per matvec, quantized to Q8_0 before use), 200 sequential
+steps.  One step = one activation-quantization launch + one launch of the
+decode engine over all 85 products.
+
+Prints ONE JSON line: throughput (algorithmic bytes / s over the timed
+steps), tokens/s, the roofline of the dominant kernel (the decode engine,
+timed with HIP events on the stream it runs on) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Other workloads (one JSON line each), for the per-configuration tables:
+  --workload c1      768x768 matvec
+  --workload c3      GPT-2-124M-shaped batch-8 decode step (49 products)
+  --workload c4b1    MoE expert FFN, 30 layers, 1 token
+  --workload c4b16   MoE expert FFN, 30 layers, 16 tokens
+  --workload c5a     prefill GEMM 512x4096 x 14336x4096
+  --workload c5b     vocabulary projection 262144x2048
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q8_0 matvec achieved HBM GB/s (% of peak) and decode tokens/s-equivalent"
+HBM_PEAK_GBS = 8000.0
+BB = 34          # bytes per Q8_0 block
+QK = 32
+
+
+def q8_bytes(rows, k):
+    return rows * (k // QK) * BB
+
+
+# ---------------------------------------------------------------------------
+# workload definitions (shapes only)
+
+LLAMA_STACKS = [  # (name, n, k, batch): same-shape projections stacked
+    ("wq_wk_wv_wo", 768, 768, 48),
+    ("w1_w3", 2048, 768, 24),
+    ("w2", 768, 2048, 12),
+    ("classifier", 32000, 768, 1),
+]
+
+GPT2_STACKS = [
+    ("c_attn", 2304, 768, 12),
+    ("attn_c_proj", 768, 768, 12),
+    ("c_fc", 3072, 768, 12),
+    ("mlp_c_proj", 768, 3072, 12),
+    ("lm_head", 50257, 768, 1),
+]
+
+
+class StepPlan:
+    """Stacks of same-shape products executed by one engine launch per step."""
+
+    def __init__(self, stacks, m, device, q, synth, tag):
+        import torch
+        self.stacks = stacks
+        self.m = m
+        self.q = q
+        self.w = []
+        for name, n, k, batch in stacks:
+            wf = synth.normal_f32_torch((batch * n, k), 0.02, device, 0, tag, name)
+            self.w.append(q.q8_0_quantize_rows(wf))
+            del wf
+        torch.cuda.synchronize()
+        self.k_total = sum(k * batch for _, n, k, batch in stacks)   # activation floats / token
+        self.nb_total = self.k_total // QK
+        self.xq = torch.empty((m, self.nb_total * BB), dtype=torch.uint8, device=device)
+        self.n_out = sum(n * batch for _, n, k, batch in stacks)
+        self.y = torch.empty((m, self.n_out), dtype=torch.float32, device=device)
+        self.descs = []
+        xoff = 0
+        yoff = 0
+        for (name, n, k, batch), w in zip(stacks, self.w):
+            nb = k // QK
+            self.descs.append(q.make_desc(
+                w, (self.xq, xoff), (self.y, yoff), n, k, m=m, batch=batch,
+                w_batch_stride=n * nb, x_row_stride=self.nb_total, x_batch_stride=nb,
+                y_row_stride=self.n_out, y_batch_stride=n))
+            xoff += batch * nb
+            yoff += batch * n
+        self.w_bytes = sum(q8_bytes(batch * n, k) for _, n, k, batch in stacks)
+        self.x_bytes = m * self.nb_total * BB
+        self.y_bytes = m * self.n_out * 4
+        self.engine_bytes = self.w_bytes + self.x_bytes + self.y_bytes
+        self.quant_bytes = m * self.k_total * 4 + self.x_bytes
+        self.products = m * sum(n * k * batch for _, n, k, batch in stacks)   # MACs
+
+    def step(self, x_step):
+        """x_step: fp32 [m][k_total] of this step."""
+        self.q.q8_0_quantize_rows(x_step, y=self.xq)
+        self.q.q8_0_matmul_batched(self.descs, self.y)
+
+
+def time_steps(plan, xs, steps, warmup):
+    """Returns (total seconds, mean engine-kernel seconds, mean quantize seconds)."""
+    import torch
+    n_in = xs.shape[0]
+    for i in range(warmup):
+        plan.step(xs[i % n_in])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        e = evs[i]
+        e[0].record()
+        plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
+        e[1].record()
+        plan.q.q8_0_matmul_batched(plan.descs, plan.y)
+        e[2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total = t_start.elapsed_time(t_end) / 1e3
+    eng = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3 / steps
+    qnt = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3 / steps
+    return total, eng, qnt
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload shapes)
+
+def cpu_baseline_steps(stacks, m, sample_steps, threads):
+    import oracle
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    ws = []
+    for name, n, k, batch in stacks:
+        ws.append([oracle.quantize_rows(synth.normal_f32((n, k), 0.02, "cpu", name, b))
+                   for b in range(batch)])
+    work_bytes = 0
+    jobs = []
+    for s in range(sample_steps):
+        for (name, n, k, batch), wl in zip(stacks, ws):
+            for b in range(batch):
+                xq = oracle.quantize_rows(synth.normal_f32((m, k), 1.0, "cpu-x", name, b, s))
+                jobs.append((wl[b], xq, n, k))
+                work_bytes += q8_bytes(n, k) + xq.nbytes + m * n * 4
+
+    def run(job_part):
+        w, xq, n, k, lo, hi = job_part
+        oracle.matmul(w, xq, n, k, m, lo, hi)
+
+    parts = []
+    for w, xq, n, k in jobs:
+        step = max(1, -(-n // threads))
+        for lo in range(0, n, step):
+            parts.append((w, xq, n, k, lo, min(n, lo + step)))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, parts))
+    dt = time.perf_counter() - t0
+    return work_bytes / dt / 1e9, dt, work_bytes
+
+
+# ---------------------------------------------------------------------------
+
+def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
+    import torch
+    dev = "cuda"
+    plan = StepPlan(stacks, m, dev, q, synth, name)
+    n_in = min(args.steps + args.warmup, n_steps_cfg)
+    xs = synth.normal_f32_torch((n_in, m, plan.k_total), 1.0, dev, 0, name, "x")
+    torch.cuda.synchronize()
+    total, eng, qnt = time_steps(plan, xs, args.steps, args.warmup)
+    bytes_step = plan.engine_bytes + plan.quant_bytes
+    value = bytes_step * args.steps / total / 1e9
+    tok_s = m * args.steps / total
+    achieved = plan.engine_bytes / eng / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 dot, fp32 scale (Q8_0)",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init, no checkpoint)",
+        "config": {"workload": wl_desc, "batch": m, "products_per_step": sum(
+            b for _, _, _, b in stacks), "launches_per_step": 2,
+            "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": bytes_step},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tok_s, 1),
+        "roofline": {"bound": "hbm", "kernel": "stream_kernel (decode engine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(eng * 1e6, 3),
+                     "bytes_per_launch": plan.engine_bytes},
+        "quantize_kernel_avg_us": round(qnt * 1e6, 3),
+    }
+    return out, plan
+
+
+# ---------------------------------------------------------------------------
+# the other configurations (one JSON line each; not the headline)
+
+def _time_launches(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3
+
+
+def run_extra(args, q, synth):
+    import torch
+    dev = "cuda"
+    wl = args.workload
+    res = {"workload": wl, "steps": args.steps, "warmup": args.warmup}
+    if wl in ("c1", "c5b"):
+        n, k = (768, 768) if wl == "c1" else (262144, 2048)
+        wf = synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w")
+        w = q.q8_0_quantize_rows(wf)
+        del wf
+        x = q.q8_0_quantize_rows(synth.normal_f32_torch((1, k), 1.0, dev, 0, wl, "x"))
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        total = _time_launches(lambda: q.q8_0_matvec(w, x, n, k, y=y), args.steps, args.warmup)
+        nbytes = q8_bytes(n, k) + q8_bytes(1, k) + 4 * n
+        t = total / args.steps
+        res.update(shape=[n, k], us_per_matvec=round(t * 1e6, 3),
+                   gbs=round(nbytes / t / 1e9, 1), pct_of_hbm_peak=round(nbytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
+                   tokens_per_s_equiv=round(1 / t, 1), bytes_per_launch=nbytes)
+    elif wl == "c5a":
+        m, n, k = 512, 14336, 4096
+        w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w"))
+        x = q.q8_0_quantize_rows(synth.normal_f32_torch((m, k), 1.0, dev, 0, wl, "x"))
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        total = _time_launches(lambda: q.q8_0_matmul(w, x, n, k, m, y=y), args.steps,
+                               args.warmup)
+        t = total / args.steps
+        ops = 2.0 * m * n * k
+        res.update(shape=[m, n, k], us_per_gemm=round(t * 1e6, 2),
+                   tops=round(ops / t / 1e12, 2), pct_of_int8_peak=round(ops / t / 5.0e15 * 100, 2),
+                   prompt_tokens_per_s=round(m / t, 1))
+    elif wl in ("c4b1", "c4b16"):
+        n_tok = 1 if wl == "c4b1" else 16
+        L, E, n_embd, n_ff, U = 30, 128, 2048, 768, 8
+        layers = []
+        active_bytes = 0
+        for l in range(L):
+            wug = q.q8_0_quantize_rows(synth.normal_f32_torch((E * 2 * n_ff, n_embd), 0.02, dev,
+                                                              0, wl, "ug", l))
+            wd = q.q8_0_quantize_rows(synth.normal_f32_torch((E * n_embd, n_ff), 0.02, dev, 0,
+                                                             wl, "down", l))
+            ids = synth.expert_ids(n_tok, U, E, 0, wl, "ids", l)
+            cw = synth.combine_weights(n_tok, U, 0, wl, "cw", l)
+            xf = synth.normal_f32_torch((n_tok, n_embd), 1.0, dev, 0, wl, "x", l)
+            n_act = len(np.unique(ids))
+            active_bytes += n_act * (q8_bytes(2 * n_ff, n_embd) + q8_bytes(n_embd, n_ff))
+            layers.append(dict(wug=wug, wd=wd, ids=torch.from_numpy(ids).to(dev),
+                               cw=torch.from_numpy(cw).to(dev), xf=xf,
+                               xq=q.q8_empty(n_tok, n_embd, dev),
+                               h=torch.empty((n_tok, U, n_ff), dtype=torch.float32, device=dev),
+                               out=torch.empty((n_tok, n_embd), dtype=torch.float32, device=dev),
+                               ws=q.moe_workspace(n_tok, n_embd, n_ff, E, U, dev)))
+        torch.cuda.synchronize()
+
+        def step():
+            for d in layers:
+                q.q8_0_quantize_rows(d["xf"], y=d["xq"])
+                q.moe_up_gate_swiglu(d["wug"], d["xq"], d["ids"], n_embd, n_ff, E, d["ws"],
+                                     h=d["h"])
+                q.moe_down_combine(d["wd"], d["h"], d["ids"], d["cw"], n_ff, n_embd, E, d["ws"],
+                                   out=d["out"])
+        total = _time_launches(step, args.steps, args.warmup)
+        t = total / args.steps
+        res.update(tokens=n_tok, layers=L, active_weight_bytes=active_bytes,
+                   us_per_step=round(t * 1e6, 2), gbs=round(active_bytes / t / 1e9, 1),
+                   pct_of_hbm_peak=round(active_bytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
+                   tokens_per_s=round(n_tok / t, 1))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-steps", type=int, default=48)
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with the rocprofv3-derived HBM bytes per launch")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import moe_expert_ffn_q8_amd as q
+    import synth
+
+    if args.workload == "c2":
+        out, plan = bench_decode(args, q, synth, LLAMA_STACKS, 1, "c2",
+                                 "llama2-110m-shaped Q8_0 decode step, batch 1, 85 matvecs, "
+                                 "200 sequential steps", 200)
+        stacks, m = LLAMA_STACKS, 1
+    elif args.workload == "c3":
+        out, plan = bench_decode(args, q, synth, GPT2_STACKS, 8, "c3",
+                                 "gpt2-124m-shaped Q8_0 decode step, batch 8, 49 matmuls", 200)
+        stacks, m = GPT2_STACKS, 8
+    else:
+        print(json.dumps(run_extra(args, q, synth)))
+        return
+
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f)
+        out["roofline"]["traffic"] = t.get("bytes_per_launch")
+
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        gbs, dt, nbytes = cpu_baseline_steps(stacks, m, args.cpu_sample_steps, threads)
+        out["cpu_baseline"] = {
+            "value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{args.cpu_sample_steps} steps of the same workload shapes "
+                      f"({nbytes / 1e9:.2f} GB of Q8_0 products, weights and inputs from "
+                      f"the seeded numpy generator), oracle matmul split by rows over "
+                      f"{threads} threads, {dt:.1f} s wall",
+            "tokens_per_s": round(m * args.cpu_sample_steps / dt, 2),
+        }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * q8moe.h -- C ABI of the MI355X (gfx950) Q8_0 decode library (libq8moe.so).
+ *
+ * The operations are the hot path of token-by-token LLM decode with Q8_0
+ * weights: activation quantization, the Q8_0 x Q8_0 matrix-vector product, its
+ * small-batch and prefill forms, and the mixture-of-experts expert FFN
+ * (mul_mat_id over a combined up_gate tensor, SwiGLU, down projection and the
+ * weighted combine over a token's active experts).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [XEON]  "GPUなしで13年前のXeon上でGemma 4 26Bを毎秒5トークンで実行する"
+ *          (Gemma 4 26B-A4B Q8_0 on a 2013 dual Xeon, ja.news.hada.io).
+ *  [NARR]  "narray-llm" README (Llama 2 110M int8 (Q8_0) table; kernels per
+ *          token table).
+ *
+ * ---------------------------------------------------------------------------
+ * Data format.  A Q8_0 block holds 32 values: an IEEE binary16 scale d
+ * (little-endian, first) followed by 32 signed 8-bit codes q[j]; value j is
+ * d*q[j].  A block is 34 bytes with 2-byte alignment.  A row of k values is
+ * k/32 blocks back to back; a matrix [n][k] is n such rows back to back.  This
+ * is the plain reading of the format the pages name but do not print
+ * ([XEON] summary and the section on the broken op paths; [NARR] Llama 2 110M
+ * int8 table).
+ *
+ * Quantization rule (per 32-block, fp32): d = max|x| / 127 (IEEE division),
+ * q = round(x / d) with ties away from zero (codes saturate at +-127, which is
+ * reachable only when d is an fp32 subnormal), d stored rounded to nearest-even
+ * binary16; an all-zero block stores d = +0 and zero codes.
+ *
+ * Block dot product: s = sum_j qw[j]*qx[j] is exact in int32; the fp32 result
+ * is sum_b (f32(dw_b) * f32(dx_b)) * s_b (the product of the two scales is
+ * exact in fp32).  The order of the fp32 sum over blocks is fixed per launch
+ * shape (results are deterministic run to run) but is not the sequential
+ * order; results agree with the exact sum within a few fp32 ulps.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every entry point.
+ *  - Pointers are DEVICE pointers owned by the caller (the library never
+ *    allocates, frees or synchronizes).  Matrices of blocks must start on a
+ *    16-byte boundary; fp32 arrays on a 4-byte boundary, and the fp32 input of
+ *    q8_0_quantize_rows on a 16-byte boundary with a row stride that is a
+ *    multiple of 4 floats.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously on it and ordered with everything else on it.
+ *  - Return value: Q8_OK (0), or a negative q8_status.  On a negative status
+ *    nothing has been enqueued and no output has been touched.  Arguments are
+ *    checked on the host before any HIP call, so argument errors are reported
+ *    the same way with or without a GPU.
+ *  - Outputs are always fully overwritten, never accumulated into.  No
+ *    operation is skipped silently: an unsupported shape is an error.
+ *  - Sizes are int64_t; k, n_embd and n_ff must be multiples of 32.
+ *  - Calls are reentrant; two calls that write the same output or the same
+ *    workspace race unless they are ordered on one stream.
+ */
+#ifndef Q8MOE_H
+#define Q8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One Q8_0 block: 34 bytes, 2-byte aligned (no padding). */
+typedef struct q8_0_block {
+    uint16_t d;       /* binary16 bits of the scale */
+    int8_t qs[32];    /* codes */
+} q8_0_block;
+
+typedef enum q8_status {
+    Q8_OK = 0,
+    Q8_E_NULL = -1,         /* a required pointer is NULL */
+    Q8_E_SHAPE = -2,        /* a size is <= 0 (or < 0 where 0 is allowed), or not a multiple of 32 */
+    Q8_E_ALIGN = -3,        /* a pointer or stride breaks the alignment rules above */
+    Q8_E_UNSUPPORTED = -4,  /* valid but outside what this build supports (stated per call) */
+    Q8_E_WORKSPACE = -5,    /* workspace missing or smaller than the ..._workspace_bytes() value */
+    Q8_E_HIP = -6           /* the HIP runtime reported an error when enqueuing */
+} q8_status;
+
+/* Human-readable name of a status; never NULL. */
+const char *q8_status_str(int status);
+
+/* Library version string. */
+const char *q8_version(void);
+
+/* ---------------------------------------------------------------------------
+ * q8_0_quantize_rows -- activation quantization (the role of
+ * quantize_row_q8_0 / quantize_row_q8_0_x4, [XEON] three-part fix, compile-fix
+ * part).
+ *   x      fp32 [n_rows][x_row_stride], the first k values of each row are used
+ *   y      Q8_0 [n_rows][k/32] blocks, written
+ * n_rows >= 0 (0 is a no-op), k > 0 and k % 32 == 0, x_row_stride >= k.
+ * The bytes written are identical to the quantization rule above, bit for bit.
+ */
+int q8_0_quantize_rows(const float *x, int64_t x_row_stride, q8_0_block *y,
+                       int64_t n_rows, int64_t k, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * q8_0_matvec -- y[n] = W[n][k] . x[k]: the batch-1 decode product (the Q8_0
+ * mul_mat whose plain fallback worked on the old Xeon, [XEON] section on the
+ * broken op paths; the block dot of ggml_vec_dot_q8_0_q8_0, [XEON] section on
+ * narrowing down the cause).
+ *   w  Q8_0 [n][k/32] (16-byte aligned), x  Q8_0 [k/32], y  fp32 [n] (written)
+ * n >= 0, k > 0, k % 32 == 0.
+ */
+int q8_0_matvec(const q8_0_block *w, const q8_0_block *x, float *y,
+                int64_t n, int64_t k, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * q8_0_matmul -- Y[m][n] = X[m][k] . W[n][k]^T for m token rows: batched decode
+ * (small m, weights streamed once for all rows) and prefill (large m, int8
+ * matrix cores).  Same arithmetic as q8_0_matvec for every (m, n).
+ *   w  Q8_0 [n][k/32], x  Q8_0 [m][k/32], y  fp32 [m][n] (written)
+ * m >= 0, n >= 0, k > 0, k % 32 == 0.
+ */
+int q8_0_matmul(const q8_0_block *w, const q8_0_block *x, float *y,
+                int64_t n, int64_t k, int64_t m, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * q8_0_matmul_batched -- several independent products in one launch, for
+ * sequencing a decode step with few kernel launches (launch count per token
+ * is the cost the [NARR] kernels-per-token table tracks).  Descriptor i
+ * computes, for every b < batch:
+ *   Y_b[m][n] = X_b[m][k] . W_b[n][k]^T
+ * with W_b = w + b*w_batch_stride (blocks), X_b row r = x + b*x_batch_stride +
+ * r*x_row_stride (blocks), Y_b row r = y + b*y_batch_stride + r*y_row_stride
+ * (floats).  All outputs of all descriptors must be disjoint.
+ * descs is a HOST array, read before the call returns.
+ * Limits: n_desc <= 32 per call (Q8_E_UNSUPPORTED above), m <= 16 for every
+ * descriptor (larger m: use q8_0_matmul).  W_b must be 16-byte aligned.
+ */
+typedef struct q8_0_matmul_desc {
+    const q8_0_block *w;
+    const q8_0_block *x;
+    float *y;
+    int64_t n, k, m, batch;
+    int64_t w_batch_stride;   /* blocks */
+    int64_t x_row_stride;     /* blocks, >= k/32 when m > 1 */
+    int64_t x_batch_stride;   /* blocks */
+    int64_t y_row_stride;     /* floats, >= n when m > 1 */
+    int64_t y_batch_stride;   /* floats */
+} q8_0_matmul_desc;
+
+int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Mixture-of-experts expert FFN ([XEON] sections on the broken op paths and on
+ * the three-part fix, runtime graph fallback).  Per token t and active slot
+ * u < n_used with expert e = ids[t][u]:
+ *   g  = W_ug[e][j]        . x_t   (gate rows j < n_ff, the first half)
+ *   up = W_ug[e][n_ff + j] . x_t   (up rows, the second half)
+ *   h[t][u][j] = silu(g) * up = g / (1 + exp(-g)) * up        (fp32)
+ *   out[t] = sum over u ascending of cw[t][u] * (W_d[e] . q(h[t][u]))
+ * where q() is the quantization rule above applied to each h row.  The gate
+ * and up products use the same quantized token row; the fused computation
+ * gives the numbers of the split form (two mul_mat_id on row views + silu*up).
+ * Each active expert's weight rows are streamed once per call, for all of the
+ * slots routed to it.
+ *
+ * ids: int32 [n_tok][n_used], each in [0, n_expert).  An id outside that range
+ * cannot be seen on the host; the kernels skip such a slot's products, write
+ * NaN to its h row (up_gate) or to the output rows of its token (down), and set
+ * the int32 error word at the start of the workspace to 1.  The word is cleared
+ * at the start of every call; read it after the call to check.
+ *
+ * Workspace: caller-owned device memory of at least moe_workspace_bytes(...)
+ * bytes, 256-byte aligned; contents need not be initialised and are
+ * overwritten.  One workspace must not be shared by calls that may run
+ * concurrently.
+ */
+size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                           int64_t n_expert, int64_t n_used);
+
+/*   w_up_gate  Q8_0 [n_expert][2*n_ff][n_embd/32]  (ggml [n_embd, 2*n_ff, n_expert])
+ *   x          Q8_0 [n_tok][n_embd/32]             (quantized token activations)
+ *   ids        int32 [n_tok][n_used]
+ *   h          fp32 [n_tok][n_used][n_ff]          (written)
+ * n_tok >= 0, n_embd % 32 == 0, n_ff % 32 == 0, 1 <= n_used <= 16.
+ * Q8_E_UNSUPPORTED when n_tok*n_used > 4096 (the prefill form is separate). */
+int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const q8_0_block *x,
+                       const int32_t *ids, float *h,
+                       int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                       int64_t n_expert, int64_t n_used,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*   w_down  Q8_0 [n_expert][n_embd][n_ff/32]  (ggml [n_ff, n_embd, n_expert])
+ *   h       fp32 [n_tok][n_used][n_ff]        (quantized inside, rule above)
+ *   ids     int32 [n_tok][n_used];  cw  fp32 [n_tok][n_used] combine weights
+ *   out     fp32 [n_tok][n_embd]              (written)
+ * Same limits as moe_up_gate_swiglu. */
+int moe_down_combine(const q8_0_block *w_down, const float *h,
+                     const int32_t *ids, const float *cw, float *out,
+                     int64_t n_tok, int64_t n_ff, int64_t n_embd,
+                     int64_t n_expert, int64_t n_used,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Validation exports (same kernels, with an extra output), for testing.
+ *
+ * q8_0_matmul_blocksums: the per-block int32 sums s[m][n][b] that q8_0_matmul
+ * forms for W[n][k], X[m][k] (m <= 16), written to sums (int32 [m][n][k/32]).
+ * y receives the usual fp32 result.
+ */
+int q8_0_matmul_blocksums(const q8_0_block *w, const q8_0_block *x, float *y,
+                          int32_t *sums, int64_t n, int64_t k, int64_t m,
+                          void *stream);
+
+/* moe_route: the grouping of (t,u) slots by expert that the MoE kernels use:
+ * counts[e] (int32 [n_expert]), offsets[e] (int32 [n_expert+1], exclusive
+ * prefix of counts), pairs (int32 [n_tok*n_used]): t*n_used+u of every slot,
+ * grouped by ascending expert, ascending (t,u) within an expert.  Slots with
+ * an out-of-range id are left out (offsets[n_expert] then counts the rest)
+ * and set the error word in ws.  Same limits as moe_up_gate_swiglu. */
+int moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets,
+              int32_t *pairs, int64_t n_tok, int64_t n_expert, int64_t n_used,
+              void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8MOE_H */

@@ -1,0 +1,17 @@
+"""moe_expert_ffn_q8_amd: Q8_0 decode matvec and MoE expert FFN for MI355X (gfx950).
+
+The product is libq8moe.so (hand-written HIP kernels behind a C ABI, declared
+in include/q8moe.h); this package is its thin Python binding.  Importing it
+fails if the library has not been built: there is no CPU fallback.
+"""
+from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, Q8Error, Q8MatmulDesc, make_desc,
+                   moe_down_combine, moe_error_word, moe_route, moe_up_gate_swiglu,
+                   moe_workspace, moe_workspace_bytes, q8_0_matmul, q8_0_matmul_batched,
+                   q8_0_matmul_blocksums, q8_0_matvec, q8_0_quantize_rows, q8_empty, raw,
+                   status_str, version)
+
+__all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "Q8Error", "Q8MatmulDesc", "make_desc",
+           "moe_down_combine", "moe_error_word", "moe_route", "moe_up_gate_swiglu",
+           "moe_workspace", "moe_workspace_bytes", "q8_0_matmul", "q8_0_matmul_batched",
+           "q8_0_matmul_blocksums", "q8_0_matvec", "q8_0_quantize_rows", "q8_empty", "raw",
+           "status_str", "version"]

@@ -1,0 +1,246 @@
+"""ctypes binding of libq8moe.so: the same names as the C ABI (include/q8moe.h).
+
+Argument marshalling only: every computation happens in the HIP kernels of the
+library.  Tensors are torch tensors on the GPU; Q8_0 data is a uint8 tensor
+whose last dimension is (k/32)*34 bytes.  Work is enqueued on torch's current
+stream of the tensors' device.  A negative status raises Q8Error.
+
+There is no fallback: if libq8moe.so is missing or cannot be loaded, importing
+this module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+QK = 32
+BLOCK_BYTES = 34
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8moe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                      "python moe_expert_ffn_q8_amd/build.py")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_size = ctypes.c_size_t
+
+
+class Q8MatmulDesc(ctypes.Structure):
+    _fields_ = [("w", _vp), ("x", _vp), ("y", _vp),
+                ("n", _i64), ("k", _i64), ("m", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_row_stride", _i64), ("x_batch_stride", _i64),
+                ("y_row_stride", _i64), ("y_batch_stride", _i64)]
+
+
+_SIGS = {
+    "q8_status_str": (ctypes.c_char_p, [_int]),
+    "q8_version": (ctypes.c_char_p, []),
+    "q8_0_quantize_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp]),
+    "q8_0_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "q8_0_matmul": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q8_0_matmul_batched": (_int, [ctypes.POINTER(Q8MatmulDesc), _i64, _vp]),
+    "moe_workspace_bytes": (_size, [_i64, _i64, _i64, _i64, _i64]),
+    "moe_up_gate_swiglu": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                                  _size, _vp]),
+    "moe_down_combine": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                                _size, _vp]),
+    "q8_0_matmul_blocksums": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "moe_route": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]),
+}
+
+EXPORTS = tuple(_SIGS)
+
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+STATUS = {0: "Q8_OK", -1: "Q8_E_NULL", -2: "Q8_E_SHAPE", -3: "Q8_E_ALIGN",
+          -4: "Q8_E_UNSUPPORTED", -5: "Q8_E_WORKSPACE", -6: "Q8_E_HIP"}
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _lib.q8_status_str(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise Q8Error(fn, rc)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    if t is None or not t.is_cuda:
+        return None
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+
+
+def status_str(status):
+    return _lib.q8_status_str(int(status)).decode()
+
+
+def version():
+    return _lib.q8_version().decode()
+
+
+def q8_empty(rows, k, device):
+    """Uninitialised Q8_0 storage for [rows][k] values (uint8 [rows][k/32*34])."""
+    return torch.empty((rows, k // QK * BLOCK_BYTES), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+
+def q8_0_quantize_rows(x, y=None, k=None):
+    """x: fp32 [n_rows][stride] (or [k]) -> y: uint8 [n_rows][k/32*34]."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x: GPU fp32 with unit column stride")
+    n_rows = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if y is None:
+        y = q8_empty(n_rows, k, x.device)
+    _need(y, torch.uint8, "y")
+    _check("q8_0_quantize_rows", _lib.q8_0_quantize_rows(
+        _ptr(x), x.stride(0) if n_rows > 1 else k, _ptr(y), n_rows, k, _stream(x)))
+    return y
+
+
+def q8_0_matvec(w, x, n, k, y=None):
+    _need(w, torch.uint8, "w")
+    _need(x, torch.uint8, "x")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, "y")
+    _check("q8_0_matvec", _lib.q8_0_matvec(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(w)))
+    return y
+
+
+def q8_0_matmul(w, x, n, k, m, y=None):
+    _need(w, torch.uint8, "w")
+    _need(x, torch.uint8, "x")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, "y")
+    _check("q8_0_matmul", _lib.q8_0_matmul(_ptr(w), _ptr(x), _ptr(y), n, k, m, _stream(w)))
+    return y
+
+
+def make_desc(w, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
+              x_batch_stride=0, y_row_stride=None, y_batch_stride=0):
+    """One q8_0_matmul_desc.  w, x, y are (tensor, element offset) pairs or tensors;
+    strides are in blocks (w, x) and floats (y)."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    nb = k // QK
+    return Q8MatmulDesc(addr(w, BLOCK_BYTES), addr(x, BLOCK_BYTES), addr(y, 4), n, k, m, batch,
+                        w_batch_stride, nb if x_row_stride is None else x_row_stride,
+                        x_batch_stride, n if y_row_stride is None else y_row_stride,
+                        y_batch_stride)
+
+
+def q8_0_matmul_batched(descs, stream_of):
+    """descs: list of Q8MatmulDesc; stream_of: a tensor on the target device."""
+    arr = (Q8MatmulDesc * len(descs))(*descs)
+    _check("q8_0_matmul_batched", _lib.q8_0_matmul_batched(arr, len(descs), _stream(stream_of)))
+
+
+def q8_0_matmul_blocksums(w, x, n, k, m):
+    _need(w, torch.uint8, "w")
+    _need(x, torch.uint8, "x")
+    y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    s = torch.empty((m, n, k // QK), dtype=torch.int32, device=w.device)
+    _check("q8_0_matmul_blocksums", _lib.q8_0_matmul_blocksums(
+        _ptr(w), _ptr(x), _ptr(y), _ptr(s), n, k, m, _stream(w)))
+    return y, s
+
+
+def moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used):
+    return int(_lib.moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used))
+
+
+def moe_workspace(n_tok, n_embd, n_ff, n_expert, n_used, device):
+    nbytes = moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used)
+    if nbytes == 0:
+        raise Q8Error("moe_workspace_bytes", -4)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_up_gate_swiglu(w_up_gate, x, ids, n_embd, n_ff, n_expert, ws, h=None):
+    """h[t][u][j] = silu(gate) * up; returns h fp32 [n_tok][n_used][n_ff]."""
+    _need(w_up_gate, torch.uint8, "w_up_gate")
+    _need(x, torch.uint8, "x")
+    _need(ids, torch.int32, "ids")
+    _need(ws, torch.uint8, "ws")
+    n_tok, n_used = ids.shape
+    if h is None:
+        h = torch.empty((n_tok, n_used, n_ff), dtype=torch.float32, device=ids.device)
+    _need(h, torch.float32, "h")
+    _check("moe_up_gate_swiglu", _lib.moe_up_gate_swiglu(
+        _ptr(w_up_gate), _ptr(x), _ptr(ids), _ptr(h), n_tok, n_embd, n_ff, n_expert, n_used,
+        _ptr(ws), ws.numel(), _stream(ids)))
+    return h
+
+
+def moe_down_combine(w_down, h, ids, cw, n_ff, n_embd, n_expert, ws, out=None):
+    """out[t] = sum_u cw[t][u] * down_e(q(h[t][u])); returns fp32 [n_tok][n_embd]."""
+    _need(w_down, torch.uint8, "w_down")
+    _need(h, torch.float32, "h")
+    _need(ids, torch.int32, "ids")
+    _need(cw, torch.float32, "cw")
+    _need(ws, torch.uint8, "ws")
+    n_tok, n_used = ids.shape
+    if out is None:
+        out = torch.empty((n_tok, n_embd), dtype=torch.float32, device=ids.device)
+    _need(out, torch.float32, "out")
+    _check("moe_down_combine", _lib.moe_down_combine(
+        _ptr(w_down), _ptr(h), _ptr(ids), _ptr(cw), _ptr(out), n_tok, n_ff, n_embd, n_expert,
+        n_used, _ptr(ws), ws.numel(), _stream(ids)))
+    return out
+
+
+def moe_route(ids, n_expert, ws):
+    _need(ids, torch.int32, "ids")
+    n_tok, n_used = ids.shape
+    dev = ids.device
+    counts = torch.empty(n_expert, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n_expert + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(max(n_tok * n_used, 1), dtype=torch.int32, device=dev)
+    _check("moe_route", _lib.moe_route(_ptr(ids), _ptr(counts), _ptr(offsets), _ptr(pairs),
+                                       n_tok, n_expert, n_used, _ptr(ws), ws.numel(),
+                                       _stream(ids)))
+    return counts, offsets, pairs[: n_tok * n_used]
+
+
+def moe_error_word(ws):
+    """The int32 error word at the start of a MoE workspace (1 = an id was out of range)."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+# Raw access for tests of the argument checks (no tensors needed).
+raw = _lib

@@ -1,0 +1,222 @@
+// abi.cpp -- the extern "C" entry points of libq8moe.so (see include/q8moe.h).
+//
+// Every entry point validates its arguments on the host, before any HIP call,
+// and returns a negative status without enqueuing anything when they are
+// wrong.  Nothing here allocates, frees or synchronizes.
+#include "q8moe.h"
+
+#include <string.h>
+
+#include "q8_internal.h"
+#include "q8_moe.h"
+
+namespace {
+
+constexpr int64_t kQK = 32;
+constexpr int64_t kBB = 34;
+
+inline bool aligned(const void *p, uintptr_t a) { return (((uintptr_t)p) % a) == 0; }
+
+inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+inline int hip_status(int rc) { return rc == 0 ? Q8_OK : (rc < 0 ? rc : Q8_E_HIP); }
+
+int check_k(int64_t k)
+{
+    if (k <= 0 || k % kQK != 0) return Q8_E_SHAPE;
+    return Q8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q8_status_str(int status)
+{
+    switch (status) {
+        case Q8_OK: return "ok";
+        case Q8_E_NULL: return "null pointer";
+        case Q8_E_SHAPE: return "bad shape";
+        case Q8_E_ALIGN: return "misaligned pointer or stride";
+        case Q8_E_UNSUPPORTED: return "unsupported by this build";
+        case Q8_E_WORKSPACE: return "workspace missing or too small";
+        case Q8_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *q8_version(void) { return "q8moe 0.1 gfx950"; }
+
+int q8_0_quantize_rows(const float *x, int64_t x_row_stride, q8_0_block *y, int64_t n_rows,
+                       int64_t k, void *stream)
+{
+    if (int rc = check_k(k)) return rc;
+    if (n_rows < 0 || x_row_stride < k) return Q8_E_SHAPE;
+    if (n_rows == 0) return Q8_OK;
+    if (!x || !y) return Q8_E_NULL;
+    if (!aligned(x, 16) || x_row_stride % 4 != 0 || !aligned(y, 2)) return Q8_E_ALIGN;
+    return hip_status(q8::launch_quantize_rows(x, x_row_stride, y, n_rows, k, as_stream(stream)));
+}
+
+static int matmul_impl(const q8_0_block *w, const q8_0_block *x, float *y, int32_t *sums,
+                       int64_t n, int64_t k, int64_t m, void *stream)
+{
+    if (int rc = check_k(k)) return rc;
+    if (n < 0 || m < 0) return Q8_E_SHAPE;
+    if (n == 0 || m == 0) return Q8_OK;
+    if (!w || !x || !y) return Q8_E_NULL;
+    if (!aligned(w, 2) || !aligned(x, 2) || !aligned(y, 4) || (sums && !aligned(sums, 4)))
+        return Q8_E_ALIGN;
+    const int64_t nb = k / kQK;
+    for (int64_t m0 = 0; m0 < m; m0 += q8::kStreamMaxM) {
+        const int64_t mc = (m - m0) < q8::kStreamMaxM ? (m - m0) : q8::kStreamMaxM;
+        q8::StreamDesc d;
+        memset(&d, 0, sizeof(d));
+        d.w = (const uint8_t *)w;
+        d.x = (const uint8_t *)x + m0 * nb * kBB;
+        d.y = y + m0 * n;
+        d.sums = sums ? sums + m0 * n * nb : nullptr;
+        d.n = n; d.nb = nb; d.m = mc; d.batch = 1;
+        d.w_bstride = 0; d.x_bstride = 0; d.y_bstride = 0;
+        d.x_rstride = nb * kBB;
+        d.y_rstride = n;
+        int rc = q8::launch_stream(&d, 1, as_stream(stream));
+        if (rc) return hip_status(rc);
+    }
+    return Q8_OK;
+}
+
+int q8_0_matvec(const q8_0_block *w, const q8_0_block *x, float *y, int64_t n, int64_t k,
+                void *stream)
+{
+    return matmul_impl(w, x, y, nullptr, n, k, 1, stream);
+}
+
+int q8_0_matmul(const q8_0_block *w, const q8_0_block *x, float *y, int64_t n, int64_t k,
+                int64_t m, void *stream)
+{
+    return matmul_impl(w, x, y, nullptr, n, k, m, stream);
+}
+
+int q8_0_matmul_blocksums(const q8_0_block *w, const q8_0_block *x, float *y, int32_t *sums,
+                          int64_t n, int64_t k, int64_t m, void *stream)
+{
+    if (!sums && n > 0 && m > 0) return Q8_E_NULL;
+    if (m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
+    return matmul_impl(w, x, y, sums, n, k, m, stream);
+}
+
+int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    q8::StreamDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    for (int64_t i = 0; i < n_desc; ++i) {
+        const q8_0_matmul_desc &s = descs[i];
+        if (int rc = check_k(s.k)) return rc;
+        if (s.n < 0 || s.m < 0 || s.batch < 0) return Q8_E_SHAPE;
+        if (s.m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
+        if (s.n == 0 || s.m == 0 || s.batch == 0) continue;
+        if (!s.w || !s.x || !s.y) return Q8_E_NULL;
+        const int64_t nb = s.k / kQK;
+        if (s.m > 1 && (s.x_row_stride < nb || s.y_row_stride < s.n)) return Q8_E_SHAPE;
+        if (s.batch > 1 && (s.w_batch_stride < s.n * nb || s.x_batch_stride < 0 ||
+                            s.y_batch_stride < 0))
+            return Q8_E_SHAPE;
+        if (!aligned(s.w, 2) || !aligned(s.x, 2) || !aligned(s.y, 4)) return Q8_E_ALIGN;
+        q8::StreamDesc &o = d[nd++];
+        memset(&o, 0, sizeof(o));
+        o.w = (const uint8_t *)s.w;
+        o.x = (const uint8_t *)s.x;
+        o.y = s.y;
+        o.n = s.n; o.nb = nb; o.m = s.m; o.batch = s.batch;
+        o.w_bstride = s.w_batch_stride * kBB;
+        o.x_rstride = s.x_row_stride * kBB;
+        o.x_bstride = s.x_batch_stride * kBB;
+        o.y_rstride = s.y_row_stride;
+        o.y_bstride = s.y_batch_stride;
+    }
+    return hip_status(q8::launch_stream(d, nd, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Mixture of experts
+
+static int moe_check(int64_t n_tok, int64_t n_in, int64_t n_out_rows, int64_t n_expert,
+                     int64_t n_used)
+{
+    if (n_tok < 0 || n_expert <= 0 || n_used <= 0) return Q8_E_SHAPE;
+    if (check_k(n_in) || check_k(n_out_rows)) return Q8_E_SHAPE;
+    if (n_used > q8::kMoeMaxUsed) return Q8_E_UNSUPPORTED;
+    if (n_tok * n_used > q8::kMoeMaxSlots) return Q8_E_UNSUPPORTED;
+    if (n_expert > q8::kMoeMaxExperts) return Q8_E_UNSUPPORTED;
+    return Q8_OK;
+}
+
+size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                           int64_t n_used)
+{
+    if (moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return 0;
+    return q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
+}
+
+int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const q8_0_block *x, const int32_t *ids,
+                       float *h, int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                       int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    if (!ws) return Q8_E_WORKSPACE;
+    if (ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
+    if (!aligned(ws, 256)) return Q8_E_ALIGN;
+    if (n_tok > 0 && (!w_up_gate || !x || !ids || !h)) return Q8_E_NULL;
+    if (!aligned(w_up_gate, 16) || !aligned(x, 2) || !aligned(ids, 4) || !aligned(h, 4))
+        return Q8_E_ALIGN;
+    q8::MoeUpGateArgs a;
+    a.w = (const uint8_t *)w_up_gate; a.x = (const uint8_t *)x; a.ids = ids; a.h = h;
+    a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
+    a.n_used = n_used; a.ws = ws;
+    return hip_status(q8::launch_moe_up_gate(a, as_stream(stream)));
+}
+
+int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *ids,
+                     const float *cw, float *out, int64_t n_tok, int64_t n_ff, int64_t n_embd,
+                     int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes, void *stream)
+{
+    if (int rc = moe_check(n_tok, n_ff, n_embd, n_expert, n_used)) return rc;
+    if (!ws) return Q8_E_WORKSPACE;
+    if (ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
+    if (!aligned(ws, 256)) return Q8_E_ALIGN;
+    if (n_tok > 0 && (!w_down || !h || !ids || !cw || !out)) return Q8_E_NULL;
+    if (!aligned(w_down, 16) || !aligned(h, 16) || !aligned(ids, 4) || !aligned(cw, 4) ||
+        !aligned(out, 4))
+        return Q8_E_ALIGN;
+    q8::MoeDownArgs a;
+    a.w = (const uint8_t *)w_down; a.h = h; a.ids = ids; a.cw = cw; a.out = out;
+    a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
+    a.n_used = n_used; a.ws = ws;
+    return hip_status(q8::launch_moe_down(a, as_stream(stream)));
+}
+
+int moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *pairs,
+              int64_t n_tok, int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
+              void *stream)
+{
+    if (n_tok < 0 || n_expert <= 0 || n_used <= 0) return Q8_E_SHAPE;
+    if (n_used > q8::kMoeMaxUsed || n_tok * n_used > q8::kMoeMaxSlots ||
+        n_expert > q8::kMoeMaxExperts)
+        return Q8_E_UNSUPPORTED;
+    if (!ws) return Q8_E_WORKSPACE;
+    if (ws_bytes < 256) return Q8_E_WORKSPACE;
+    if (!aligned(ws, 256)) return Q8_E_ALIGN;
+    if (!counts || !offsets || (n_tok > 0 && (!ids || !pairs))) return Q8_E_NULL;
+    if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pairs, 4))
+        return Q8_E_ALIGN;
+    return hip_status(q8::launch_moe_route(ids, counts, offsets, pairs, n_tok, n_expert, n_used,
+                                           ws, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// q8_internal.h -- host-side declarations shared by the translation units of
+// libq8moe (launchers called by the C ABI layer in abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+// One matrix product of the streaming (decode) engine, already validated.
+struct StreamDesc {
+    const uint8_t *w;      // [batch][n][nb] blocks (16-byte aligned per matrix)
+    const uint8_t *x;      // activations, rows of nb blocks
+    float *y;
+    int32_t *sums;         // optional int32 [m][n][nb] (validation; batch must be 1)
+    int64_t n, nb, m, batch;
+    int64_t w_bstride;     // bytes
+    int64_t x_rstride;     // bytes
+    int64_t x_bstride;     // bytes
+    int64_t y_rstride;     // floats
+    int64_t y_bstride;     // floats
+};
+
+// Limits of the streaming engine (checked by the ABI layer).
+constexpr int kStreamMaxJobs = 32;
+constexpr int kStreamMaxM = 16;
+constexpr int kStreamMaxNb = 256;   // k <= 8192 on the fast path
+
+// True when the fast streaming kernel handles this descriptor (else the
+// generic kernel is used).
+bool stream_fast_ok(const StreamDesc &d);
+
+// Enqueue descriptors; returns 0 or a negative q8_status.
+int launch_stream(const StreamDesc *d, int n, hipStream_t stream);
+
+int launch_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_rows,
+                         int64_t k, hipStream_t stream);
+
+// Largest dynamic LDS a workgroup may use on the current device.
+int max_lds_bytes();
+
+}  // namespace q8

@@ -1,0 +1,333 @@
+// stream.hip -- the decode engine: Q8_0 x Q8_0 products with few token rows
+// (m <= 16), streaming every weight byte from HBM exactly once.
+//
+// The block arithmetic is the dot product behind ggml_vec_dot_q8_0_q8_0 on
+// the Gemma-4-on-Xeon page ("GPUなしで13年前のXeon上でGemma 4 26Bを毎秒5トーク
+// ンで実行する", section on narrowing down the cause): an exact int32 sum of 32
+// code products per block, then (d_w * d_x) * s in fp32.
+//
+// Work decomposition (gfx950, wave64):
+//  * A weight row of nb blocks is nb/4 "quads" of 4 blocks (136 B).  A tile is
+//    R = floor(64 / (nb/4)) whole rows, so each lane of a wave owns one quad
+//    (lanes past R*(nb/4) idle).  With nb % 8 == 0 a tile starts on a 16-byte
+//    boundary and is rows*nb*17/8 16-byte chunks long.
+//  * A wave loads its tile with fully coalesced 16-byte non-temporal loads
+//    (1 KB per instruction, up to 9 per lane), writes the chunks to its own
+//    8.5 KB LDS slot in the same order, then every lane reads back its quad
+//    with 17 8-byte LDS reads (lane stride 136 B: conflict-free).  The next
+//    tile's loads are issued before the current tile is computed.
+//  * Activations: the workgroup copies the m token rows of its matrix into
+//    LDS once, as a "masked image" (the same 34-byte block layout with the
+//    scale bytes zeroed) plus an fp32 scale array.  A lane's quad column is
+//    the same for every tile, so with m == 1 the lane keeps its 34 image dwords
+//    and 4 scales in registers for the whole kernel.
+//  * Per quad and token: 34 v_dot4 (one per weight dword, no byte shuffling),
+//    giving the four exact block sums; then 4 fp32 scale products.
+//  * The nb/4 lanes of a row are combined in a fixed order through LDS, so a
+//    launch shape always gives the same bits.
+//
+// Rows with nb % 8 != 0, nb > 256 or a weight matrix not on a 16-byte boundary
+// go to a plain generic kernel (one wave per row, 2-byte loads).
+#include <string.h>
+
+#include "q8_device.h"
+#include "q8_internal.h"
+
+namespace q8 {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+
+struct StreamJob {
+    const uint8_t *w;
+    const uint8_t *x;
+    float *y;
+    int32_t *sums;
+    int64_t w_bstride;   // bytes
+    int64_t x_bstride;   // bytes
+    int64_t y_bstride;   // floats
+    int32_t x_rstride;   // bytes
+    int32_t y_rstride;   // floats
+    int32_t n, nb, m, batch;
+    int32_t wg0;             // first workgroup of this job
+    int32_t tiles_per_wg;
+    int32_t rows_per_tile;   // R
+    int32_t tiles_per_batch; // ceil(n / R)
+    int32_t wg_per_batch;    // ceil(tiles_per_batch / tiles_per_wg)
+};
+
+struct StreamArgs {
+    StreamJob job[kStreamMaxJobs];
+    int32_t n_jobs;
+    int32_t nb_max;
+};
+
+static_assert(sizeof(StreamArgs) <= 4000, "kernel arguments must stay below 4 KB");
+
+template <int MT, bool SUMS>
+__global__ __launch_bounds__(kThreads) void stream_kernel(const StreamArgs args)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+
+    int j = 0;
+    for (int i = 1; i < args.n_jobs; ++i)
+        if (args.job[i].wg0 <= (int)blockIdx.x) j = i;
+    const StreamJob &J = args.job[j];
+
+    const int wg = (int)blockIdx.x - J.wg0;
+    const int bi = wg / J.wg_per_batch;
+    const int wb = wg - bi * J.wg_per_batch;
+    const int t0 = wb * J.tiles_per_wg;
+    const int t1 = min(t0 + J.tiles_per_wg, J.tiles_per_batch);
+    const int nb = J.nb;
+    const int Q = nb >> 2;             // quads per row
+    const int R = J.rows_per_tile;
+    const int M = J.m;
+    const int n = J.n;
+    const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+
+    const uint8_t *W = J.w + (int64_t)bi * J.w_bstride;
+    const uint8_t *X = J.x + (int64_t)bi * J.x_bstride;
+    float *Y = J.y + (int64_t)bi * J.y_bstride;
+
+    uint8_t *stage = smem + wave * kStageBytes;
+    float *red = (float *)(smem + kWaves * kStageBytes) + wave * MT * kWave;
+    uint8_t *ximg = smem + kWaves * kStageBytes + kWaves * MT * kWave * 4;
+    const int img_row = nb * kBlockBytes;
+    float *xsc = (float *)(ximg + MT * args.nb_max * kBlockBytes);
+
+    // ---- activations -> masked image + fp32 scales (whole workgroup) ----
+    const int halves = M * nb * 17;
+    for (int i = tid; i < halves; i += kThreads) {
+        const int r = i / (nb * 17);
+        const int rem = i - r * nb * 17;
+        const int b = rem / 17;
+        const int h = rem - b * 17;
+        const uint32_t v = load_u16(X + (int64_t)r * J.x_rstride + b * kBlockBytes + 2 * h);
+        uint16_t *img16 = (uint16_t *)(ximg + r * img_row);
+        if (h == 0) {
+            xsc[r * nb + b] = half_bits_to_float(v);
+            img16[b * 17] = 0;
+        } else {
+            img16[b * 17 + h] = (uint16_t)v;
+        }
+    }
+    __syncthreads();
+
+    const int c = lane % Q;            // this lane's quad column (same for every tile)
+    uint32_t xr[kQuadDwords];
+    float xd0 = 0.f, xd1 = 0.f, xd2 = 0.f, xd3 = 0.f;
+    if (MT == 1) {
+        lds_quad(ximg + kQuadBytes * c, xr);
+        const float4 s = *(const float4 *)(xsc + 4 * c);
+        xd0 = s.x; xd1 = s.y; xd2 = s.z; xd3 = s.w;
+    }
+
+    u32x4 g[kTileLoads];
+    auto issue = [&](int tt) {
+        const int row0 = tt * R;
+        const int rows = min(R, n - row0);
+        tile_issue(W + (int64_t)row0 * row_bytes, rows * nb * 17 / 8, lane, g);
+    };
+
+    int t = t0 + wave;
+    if (t < t1) issue(t);
+    for (; t < t1; t += kWaves) {
+        const int row0 = t * R;
+        const int rows = min(R, n - row0);
+        const int live = rows * Q;
+        uint32_t wq[kQuadDwords];
+        tile_to_quad(stage, g, lane, live, wq);
+        if (t + kWaves < t1) issue(t + kWaves);
+
+        float dw0, dw1, dw2, dw3;
+        quad_scales(wq, dw0, dw1, dw2, dw3);
+        const int row = row0 + lane / Q;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < M) {
+                uint32_t xt[kQuadDwords];
+                const uint32_t *xq = xr;
+                float4 dx = make_float4(xd0, xd1, xd2, xd3);
+                if (MT != 1) {
+                    lds_quad(ximg + m * img_row + kQuadBytes * c, xt);
+                    xq = xt;
+                    dx = *(const float4 *)(xsc + m * nb + 4 * c);
+                }
+                int s[4];
+                const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, s);
+                red[m * kWave + lane] = (lane < live) ? acc : 0.0f;
+                if (SUMS && lane < live) {
+                    int32_t *o = J.sums + ((int64_t)m * n + row) * nb + 4 * c;
+                    o[0] = s[0]; o[1] = s[1]; o[2] = s[2]; o[3] = s[3];
+                }
+            }
+        }
+        wave_lds_sync();
+        for (int i = lane; i < rows * M; i += kWave) {
+            const int m = i / rows;
+            const int r = i - m * rows;
+            const float *p = red + m * kWave + r * Q;
+            float acc = p[0];
+            for (int cc = 1; cc < Q; ++cc) acc += p[cc];
+            Y[(int64_t)m * J.y_rstride + row0 + r] = acc;
+        }
+        wave_lds_sync();
+    }
+}
+
+// Generic path: one wave per (matrix, row); lanes stride over blocks with
+// 2-byte loads; fixed-order xor-tree reduction.
+__global__ __launch_bounds__(kWave) void stream_generic_kernel(StreamDesc d)
+{
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int64_t bi = blockIdx.y;
+    const uint8_t *Wr = d.w + bi * d.w_bstride + row * d.nb * kBlockBytes;
+    for (int64_t m = 0; m < d.m; ++m) {
+        const uint8_t *Xr = d.x + bi * d.x_bstride + m * d.x_rstride;
+        float acc = 0.0f;
+        for (int64_t b = lane; b < d.nb; b += kWave) {
+            const uint8_t *wb = Wr + b * kBlockBytes;
+            const uint8_t *xb = Xr + b * kBlockBytes;
+            int s = 0;
+            for (int h = 1; h < 17; ++h) {
+                const uint32_t wv = load_u16(wb + 2 * h);
+                const uint32_t xv = load_u16(xb + 2 * h);
+                s += (int)(int8_t)(wv & 0xff) * (int)(int8_t)(xv & 0xff);
+                s += (int)(int8_t)(wv >> 8) * (int)(int8_t)(xv >> 8);
+            }
+            if (d.sums) d.sums[(m * d.n + row) * d.nb + b] = s;
+            acc = fmaf(half_bits_to_float(load_u16(wb)) * half_bits_to_float(load_u16(xb)),
+                       (float)s, acc);
+        }
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+        if (lane == 0) d.y[bi * d.y_bstride + m * d.y_rstride + row] = acc;
+    }
+}
+
+bool stream_fast_ok(const StreamDesc &d)
+{
+    if (d.nb % 8 != 0 || d.nb > kStreamMaxNb) return false;
+    if (((uintptr_t)d.w) % 16 != 0 || d.w_bstride % 16 != 0) return false;
+    if (d.m > kStreamMaxM) return false;
+    if (d.n > (int64_t)1 << 30 || d.batch > (int64_t)1 << 20) return false;
+    if (d.x_rstride > ((int64_t)1 << 31) - 1 || d.y_rstride > ((int64_t)1 << 31) - 1) return false;
+    return true;
+}
+
+static int g_max_lds = 0;
+
+int max_lds_bytes()
+{
+    if (g_max_lds == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 65536;
+        g_max_lds = v;
+    }
+    return g_max_lds;
+}
+
+template <int MT, bool SUMS>
+static int launch_fast_mt(const StreamArgs &a, int grid, size_t lds, hipStream_t stream)
+{
+    hipLaunchKernelGGL((stream_kernel<MT, SUMS>), dim3(grid), dim3(kThreads), lds, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+static int launch_fast(const StreamDesc *d, int n, hipStream_t stream)
+{
+    StreamArgs a;
+    memset(&a, 0, sizeof(a));
+    int64_t total_tiles = 0;
+    int mmax = 1, nbmax = 8;
+    bool sums = false;
+    for (int i = 0; i < n; ++i) {
+        const int64_t Q = d[i].nb / 4;
+        const int64_t R = 64 / Q;
+        total_tiles += d[i].batch * ((d[i].n + R - 1) / R);
+        if (d[i].m > mmax) mmax = (int)d[i].m;
+        if (d[i].nb > nbmax) nbmax = (int)d[i].nb;
+        if (d[i].sums) sums = true;
+    }
+    // Tiles per wave: enough waves to fill 256 CUs several times over, and
+    // more tiles per wave (so each wave prefetches) once there are plenty.
+    int64_t per_wave = total_tiles / (256 * 8 * kWaves);
+    if (per_wave < 1) per_wave = 1;
+    if (per_wave > 16) per_wave = 16;
+    int64_t wg_total = 0;
+    for (int i = 0; i < n; ++i) {
+        StreamJob &J = a.job[i];
+        const int64_t Q = d[i].nb / 4;
+        const int64_t R = 64 / Q;
+        const int64_t tpb = (d[i].n + R - 1) / R;
+        int64_t tpw = per_wave * kWaves;
+        if (total_tiles < 256 * kWaves) tpw = 1;           // small problems: spread wide
+        else if (total_tiles < 256 * 8 * kWaves) tpw = 2;
+        if (tpw > tpb) tpw = tpb;
+        const int64_t wpb = (tpb + tpw - 1) / tpw;
+        J.w = d[i].w; J.x = d[i].x; J.y = d[i].y; J.sums = d[i].sums;
+        J.w_bstride = d[i].w_bstride; J.x_bstride = d[i].x_bstride; J.y_bstride = d[i].y_bstride;
+        J.x_rstride = (int32_t)d[i].x_rstride; J.y_rstride = (int32_t)d[i].y_rstride;
+        J.n = (int32_t)d[i].n; J.nb = (int32_t)d[i].nb; J.m = (int32_t)d[i].m;
+        J.batch = (int32_t)d[i].batch;
+        J.wg0 = (int32_t)wg_total;
+        J.tiles_per_wg = (int32_t)tpw;
+        J.rows_per_tile = (int32_t)R;
+        J.tiles_per_batch = (int32_t)tpb;
+        J.wg_per_batch = (int32_t)wpb;
+        wg_total += d[i].batch * wpb;
+    }
+    if (wg_total > ((int64_t)1 << 31) - 1) return -4;
+    a.n_jobs = n;
+    a.nb_max = nbmax;
+    int mt = 1;
+    while (mt < mmax) mt <<= 1;
+    const size_t lds = (size_t)kWaves * kStageBytes + (size_t)kWaves * mt * kWave * 4 +
+                       (size_t)mt * nbmax * kBlockBytes + (size_t)mt * nbmax * 4;
+    if (lds > (size_t)max_lds_bytes()) return -4;
+    const int grid = (int)wg_total;
+    if (sums) {
+        switch (mt) {
+            case 1: return launch_fast_mt<1, true>(a, grid, lds, stream);
+            case 2: return launch_fast_mt<2, true>(a, grid, lds, stream);
+            case 4: return launch_fast_mt<4, true>(a, grid, lds, stream);
+            case 8: return launch_fast_mt<8, true>(a, grid, lds, stream);
+            default: return launch_fast_mt<16, true>(a, grid, lds, stream);
+        }
+    }
+    switch (mt) {
+        case 1: return launch_fast_mt<1, false>(a, grid, lds, stream);
+        case 2: return launch_fast_mt<2, false>(a, grid, lds, stream);
+        case 4: return launch_fast_mt<4, false>(a, grid, lds, stream);
+        case 8: return launch_fast_mt<8, false>(a, grid, lds, stream);
+        default: return launch_fast_mt<16, false>(a, grid, lds, stream);
+    }
+}
+
+int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
+{
+    StreamDesc fast[kStreamMaxJobs];
+    int nf = 0;
+    for (int i = 0; i < n; ++i) {
+        if (d[i].n == 0 || d[i].m == 0 || d[i].batch == 0) continue;
+        if (stream_fast_ok(d[i])) {
+            fast[nf++] = d[i];
+        } else {
+            if (d[i].n > 0x7fffffff || d[i].batch > 65535) return -4;
+            hipLaunchKernelGGL(stream_generic_kernel, dim3((unsigned)d[i].n, (unsigned)d[i].batch),
+                               dim3(kWave), 0, stream, d[i]);
+            if (hipGetLastError() != hipSuccess) return -6;
+        }
+    }
+    if (nf == 0) return 0;
+    return launch_fast(fast, nf, stream);
+}
+
+}  // namespace q8

@@ -18,3 +18,18 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a GPU: skip them (with the reason) where there is none."""
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU in this environment")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

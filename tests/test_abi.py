@@ -1,0 +1,129 @@
+"""The C ABI: the library loads, exports every function include/q8moe.h
+declares, and rejects bad arguments on the host with the documented status
+before touching the GPU (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8moe.h")
+
+Q8_OK, Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_UNSUPPORTED, Q8_E_WORKSPACE = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import moe_expert_ffn_q8_amd as q
+    return q.raw
+
+
+def test_exports_everything_declared(lib):
+    names = declared_functions()
+    assert len(names) >= 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr)
+    import moe_expert_ffn_q8_amd as q
+    assert set(names) == set(q.EXPORTS)
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert lib.q8_status_str(s)
+
+
+A = 1 << 20          # a fake, suitably aligned address: never dereferenced
+
+
+def test_quantize_rows_checks(lib):
+    f = lib.q8_0_quantize_rows
+    assert f(A, 64, A, 1, 33, None) == Q8_E_SHAPE          # k % 32
+    assert f(A, 64, A, 1, 0, None) == Q8_E_SHAPE
+    assert f(A, 16, A, 1, 32, None) == Q8_E_SHAPE          # stride < k
+    assert f(A, 64, A, -1, 64, None) == Q8_E_SHAPE
+    assert f(A, 64, A, 0, 64, None) == Q8_OK               # no rows: no-op
+    assert f(None, 64, A, 1, 64, None) == Q8_E_NULL
+    assert f(A + 4, 64, A, 1, 64, None) == Q8_E_ALIGN      # fp32 input needs 16 B
+    assert f(A, 66, A, 2, 64, None) == Q8_E_ALIGN          # stride multiple of 4
+    assert f(A, 64, A + 1, 1, 64, None) == Q8_E_ALIGN
+
+
+def test_matvec_matmul_checks(lib):
+    assert lib.q8_0_matvec(A, A, A, 10, 40, None) == Q8_E_SHAPE
+    assert lib.q8_0_matvec(A, A, A, -1, 64, None) == Q8_E_SHAPE
+    assert lib.q8_0_matvec(A, A, A, 0, 64, None) == Q8_OK
+    assert lib.q8_0_matvec(None, A, A, 10, 64, None) == Q8_E_NULL
+    assert lib.q8_0_matvec(A, None, A, 10, 64, None) == Q8_E_NULL
+    assert lib.q8_0_matvec(A, A, None, 10, 64, None) == Q8_E_NULL
+    assert lib.q8_0_matvec(A + 1, A, A, 10, 64, None) == Q8_E_ALIGN
+    assert lib.q8_0_matvec(A, A, A + 2, 10, 64, None) == Q8_E_ALIGN
+    assert lib.q8_0_matmul(A, A, A, 10, 64, -3, None) == Q8_E_SHAPE
+    assert lib.q8_0_matmul(A, A, A, 10, 64, 0, None) == Q8_OK
+    assert lib.q8_0_matmul_blocksums(A, A, A, None, 10, 64, 1, None) == Q8_E_NULL
+    assert lib.q8_0_matmul_blocksums(A, A, A, A, 10, 64, 17, None) == Q8_E_UNSUPPORTED
+
+
+def test_batched_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    D = q.Q8MatmulDesc
+    def call(*ds):
+        arr = (D * len(ds))(*ds)
+        return lib.q8_0_matmul_batched(arr, len(ds), None)
+    ok = dict(w=A, x=A, y=A, n=8, k=64, m=1, batch=1, w_batch_stride=0, x_row_stride=2,
+              x_batch_stride=0, y_row_stride=8, y_batch_stride=0)
+    assert lib.q8_0_matmul_batched(None, 0, None) == Q8_OK
+    assert lib.q8_0_matmul_batched(None, 1, None) == Q8_E_NULL
+    assert lib.q8_0_matmul_batched(None, -1, None) == Q8_E_SHAPE
+    assert call(D(**{**ok, "k": 48})) == Q8_E_SHAPE
+    assert call(D(**{**ok, "m": 17})) == Q8_E_UNSUPPORTED
+    assert call(D(**{**ok, "m": 2, "x_row_stride": 1})) == Q8_E_SHAPE
+    assert call(D(**{**ok, "batch": 2, "w_batch_stride": 3})) == Q8_E_SHAPE
+    assert call(D(**{**ok, "w": None})) == Q8_E_NULL
+    assert call(D(**{**ok, "y": A + 2})) == Q8_E_ALIGN
+    assert call(D(**{**ok, "n": 0})) == Q8_OK
+    arr = (D * 33)(*([D(**{**ok, "n": 0})] * 33))
+    assert lib.q8_0_matmul_batched(arr, 33, None) == Q8_E_UNSUPPORTED
+
+
+def test_moe_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    ws_bytes = q.moe_workspace_bytes(4, 256, 64, 8, 2)
+    assert ws_bytes >= 256
+    assert q.moe_workspace_bytes(4, 250, 64, 8, 2) == 0
+    assert q.moe_workspace_bytes(4, 256, 64, 8, 17) == 0
+    ug = lib.moe_up_gate_swiglu
+    args = [A, A, A, A, 4, 256, 64, 8, 2, A, ws_bytes, None]
+    def with_(i, v):
+        a = list(args)
+        a[i] = v
+        return ug(*a)
+    assert with_(5, 250) == Q8_E_SHAPE              # n_embd % 32
+    assert with_(6, 48) == Q8_E_SHAPE               # n_ff % 32
+    assert with_(8, 0) == Q8_E_SHAPE                # n_used
+    assert with_(8, 17) == Q8_E_UNSUPPORTED
+    assert with_(4, 1025) == Q8_E_UNSUPPORTED       # too many slots
+    assert with_(7, 0) == Q8_E_SHAPE
+    assert with_(9, None) == Q8_E_WORKSPACE
+    assert with_(10, ws_bytes - 1) == Q8_E_WORKSPACE
+    assert with_(9, A + 16) == Q8_E_ALIGN
+    assert with_(0, None) == Q8_E_NULL
+    assert with_(3, A + 2) == Q8_E_ALIGN
+    dc = lib.moe_down_combine
+    dargs = [A, A, A, A, A, 4, 64, 256, 8, 2, A, ws_bytes, None]
+    assert dc(*dargs[:4], None, *dargs[5:]) == Q8_E_NULL
+    a = list(dargs); a[1] = A + 4
+    assert dc(*a) == Q8_E_ALIGN                     # h needs 16 B
+    a = list(dargs); a[11] = 8
+    assert dc(*a) == Q8_E_WORKSPACE
+    assert lib.moe_route(A, A, A, A, 4, 8, 2, None, 256, None) == Q8_E_WORKSPACE
+    assert lib.moe_route(A, None, A, A, 4, 8, 2, A, 256, None) == Q8_E_NULL

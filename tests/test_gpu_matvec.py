@@ -1,0 +1,146 @@
+"""GPU parity of q8_0_matvec / q8_0_matmul (streaming engine) against the
+oracle: exact int32 block sums, fp32 outputs within 1e-5 per-row relative L2,
+every output written (outputs are pre-filled with NaN), bitwise determinism."""
+import numpy as np
+import pytest
+
+from gpu_cases import acts_q8, assert_rows_close, nan_like, to_gpu, weights_q8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import moe_expert_ffn_q8_amd as q
+    return q
+
+
+def test_c1_matvec_768(q, orc):
+    """The 768 x 768 matvec, seed 0 (weights N(0,0.02), activation N(0,1))."""
+    n = k = 768
+    w = weights_q8(orc, n, k, 0, "c1", "w")
+    x = acts_q8(orc, 1, k, 0, "c1", "x")
+    ref = orc.matmul(w, x, n, k, 1)
+    y = nan_like((n,))
+    q.q8_0_matvec(to_gpu(w), to_gpu(x), n, k, y=y)
+    assert_rows_close(y.cpu().numpy()[None, :], ref)
+    _, sums = q.q8_0_matmul_blocksums(to_gpu(w), to_gpu(x), n, k, 1)
+    assert np.array_equal(sums.cpu().numpy(), orc.matmul_blocksums(w, x, n, k, 1))
+
+
+@pytest.mark.parametrize("n,k", [(1000, 256), (777, 768), (1031, 2048), (200, 3072),
+                                 (130, 4096), (37, 8192), (513, 1024)])
+def test_matvec_shapes(q, orc, n, k):
+    w = weights_q8(orc, n, k, "mv", n, k)
+    x = acts_q8(orc, 1, k, "mv-x", n, k)
+    ref = orc.matmul(w, x, n, k, 1)
+    y = nan_like((n,))
+    wg, xg = to_gpu(w), to_gpu(x)
+    q.q8_0_matvec(wg, xg, n, k, y=y)
+    assert_rows_close(y.cpu().numpy()[None, :], ref)
+    y2 = q.q8_0_matvec(wg, xg, n, k)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    _, sums = q.q8_0_matmul_blocksums(wg, xg, n, k, 1)
+    assert np.array_equal(sums.cpu().numpy(), orc.matmul_blocksums(w, x, n, k, 1))
+
+
+@pytest.mark.parametrize("n,k", [(65, 96), (40, 16384), (3, 32)])
+def test_matvec_generic_path(q, orc, n, k):
+    """k/32 not a multiple of 8, or k above the fast path's limit."""
+    w = weights_q8(orc, n, k, "gen", n, k)
+    x = acts_q8(orc, 1, k, "gen-x", n, k)
+    y = nan_like((n,))
+    q.q8_0_matvec(to_gpu(w), to_gpu(x), n, k, y=y)
+    assert_rows_close(y.cpu().numpy()[None, :], orc.matmul(w, x, n, k, 1))
+    _, sums = q.q8_0_matmul_blocksums(to_gpu(w), to_gpu(x), n, k, 1)
+    assert np.array_equal(sums.cpu().numpy(), orc.matmul_blocksums(w, x, n, k, 1))
+
+
+def test_matvec_misaligned_weights(q, orc):
+    """A weight matrix starting 2 bytes past a 16-byte boundary (generic path)."""
+    import torch
+    n, k = 50, 512
+    w = weights_q8(orc, n, k, "mis")
+    x = acts_q8(orc, 1, k, "mis-x")
+    buf = torch.zeros(w.size + 16, dtype=torch.uint8, device="cuda")
+    buf[2:2 + w.size] = to_gpu(w.reshape(-1))
+    y = nan_like((n,))
+    rc = q.raw.q8_0_matvec(buf.data_ptr() + 2, to_gpu(x).data_ptr(), y.data_ptr(), n, k,
+                           torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    assert_rows_close(y.cpu().numpy()[None, :], orc.matmul(w, x, n, k, 1))
+
+
+@pytest.mark.parametrize("n,k,m", [(300, 768, 2), (129, 2048, 3), (1000, 768, 8),
+                                   (257, 3072, 8), (100, 4096, 16), (90, 512, 5),
+                                   (70, 768, 17), (33, 1024, 40)])
+def test_matmul_small_m(q, orc, n, k, m):
+    w = weights_q8(orc, n, k, "mm", n, k, m)
+    x = acts_q8(orc, m, k, "mm-x", n, k, m)
+    ref = orc.matmul(w, x, n, k, m)
+    y = nan_like((m, n))
+    q.q8_0_matmul(to_gpu(w), to_gpu(x), n, k, m, y=y)
+    assert_rows_close(y.cpu().numpy(), ref)
+    if m <= 16:
+        _, sums = q.q8_0_matmul_blocksums(to_gpu(w), to_gpu(x), n, k, m)
+        assert np.array_equal(sums.cpu().numpy(), orc.matmul_blocksums(w, x, n, k, m))
+
+
+def test_batched_descriptors(q, orc):
+    """Several products in one launch: two weight stacks with a batch
+    dimension, a strided activation layout, and a single matrix."""
+    import torch
+    specs = [  # (n, k, m, batch)
+        (96, 768, 1, 5), (160, 256, 1, 3), (50, 2048, 1, 1), (70, 768, 4, 2)]
+    descs, checks, keep = [], [], []
+    for i, (n, k, m, batch) in enumerate(specs):
+        nb = k // 32
+        w = weights_q8(orc, batch * n, k, "bd-w", i)
+        # activations: rows of all batch entries in one [batch*m][k] block, with a
+        # larger row stride (2 extra blocks) to exercise strides
+        xs = acts_q8(orc, batch * m, k, "bd-x", i)
+        stride = nb + 2
+        xbuf = np.zeros((batch * m, stride * 34), dtype=np.uint8)
+        xbuf[:, : nb * 34] = xs
+        wg, xg = to_gpu(w), to_gpu(xbuf)
+        y = nan_like((batch, m, n + 3))
+        keep += [wg, xg, y]
+        descs.append(q.make_desc(wg, xg, y, n, k, m=m, batch=batch, w_batch_stride=n * nb,
+                                 x_row_stride=stride, x_batch_stride=m * stride,
+                                 y_row_stride=n + 3, y_batch_stride=m * (n + 3)))
+        checks.append((w, xs, y, n, k, m, batch))
+    q.q8_0_matmul_batched(descs, keep[0])
+    torch.cuda.synchronize()
+    for w, xs, y, n, k, m, batch in checks:
+        nb34 = k // 32 * 34
+        yy = y.cpu().numpy()
+        for b in range(batch):
+            ref = orc.matmul(w[b * n:(b + 1) * n], xs[b * m:(b + 1) * m], n, k, m)
+            assert_rows_close(yy[b, :, :n], ref)
+            assert np.all(np.isnan(yy[b, :, n:]))      # padding columns untouched
+
+
+def test_c5b_vocab_projection_full_size(q, orc):
+    """262144 x 2048 at full size: weights drawn on the GPU (torch's generator),
+    quantized by the library; sampled rows are re-quantized by the oracle from
+    the same fp32 values (bytes must match) and their outputs computed by the
+    oracle."""
+    import torch
+    import synth
+    n, k = 262144, 2048
+    wf = synth.normal_f32_torch((n, k), 0.02, "cuda", 0, "c5b", "w")
+    wq = q.q8_0_quantize_rows(wf)
+    xf = synth.normal_f32((1, k), 1.0, 0, "c5b", "x")
+    xq = orc.quantize_rows(xf)
+    y = nan_like((n,))
+    q.q8_0_matvec(wq, to_gpu(xq), n, k, y=y)
+    rows = np.unique(np.concatenate([np.arange(8), n - 1 - np.arange(8),
+                                     np.random.default_rng(0).integers(0, n, 4096)]))
+    rows_t = torch.from_numpy(rows).cuda()
+    w_rows = orc.quantize_rows(wf[rows_t].cpu().numpy())
+    assert np.array_equal(wq[rows_t].cpu().numpy(), w_rows)
+    ref = orc.matmul(w_rows, xq, rows.size, k, 1)
+    yy = y.cpu().numpy()
+    assert np.all(np.isfinite(yy))
+    assert_rows_close(yy[rows][None, :], ref)
+    del wf
