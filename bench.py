@@ -104,30 +104,63 @@ class StepPlan:
         self.q.q8_0_matmul_batched(self.descs, self.y)
 
 
+def capture(fn):
+    """Capture fn()'s launches (on torch's current stream) in a HIP graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                      # one eager pass on the capture stream first
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps=1):
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    g.replay()                    # untimed: first replay after instantiation
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / reps
+
+
 def time_steps(plan, xs, steps, warmup):
-    """Returns (total seconds, mean engine-kernel seconds, mean quantize seconds)."""
+    """The K timed steps are captured in one HIP graph (2 launches per step:
+    activation quantization, then the engine over every product of the step)
+    and replayed once inside the timed region.  Returns (total seconds for K
+    steps, mean engine launch seconds, mean quantize launch seconds); the
+    per-kernel means come from graphs of K launches of that kernel alone."""
     import torch
     n_in = xs.shape[0]
     for i in range(warmup):
         plan.step(xs[i % n_in])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(steps):
-        e = evs[i]
-        e[0].record()
-        plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
-        e[1].record()
-        plan.q.q8_0_matmul_batched(plan.descs, plan.y)
-        e[2].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    total = t_start.elapsed_time(t_end) / 1e3
-    eng = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3 / steps
-    qnt = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3 / steps
+
+    def all_steps():
+        for i in range(steps):
+            plan.step(xs[i % n_in])
+    g_all = capture(all_steps)
+    total = time_graph(g_all)
+
+    def eng_only():
+        for _ in range(steps):
+            plan.q.q8_0_matmul_batched(plan.descs, plan.y)
+    eng = time_graph(capture(eng_only)) / steps
+
+    def qnt_only():
+        for i in range(steps):
+            plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
+    qnt = time_graph(capture(qnt_only)) / steps
     return total, eng, qnt
 
 
@@ -195,7 +228,7 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
         "dtype": "int8 dot, fp32 scale (Q8_0)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init, no checkpoint)",
         "config": {"workload": wl_desc, "batch": m, "products_per_step": sum(
-            b for _, _, _, b in stacks), "launches_per_step": 2,
+            b for _, _, _, b in stacks), "launches_per_step": 2, "timing": "HIP graph of the K steps, one replay timed with HIP events",
             "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": bytes_step},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tok_s, 1),
@@ -213,18 +246,17 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
 # the other configurations (one JSON line each; not the headline)
 
 def _time_launches(fn, steps, warmup):
+    """Seconds for `steps` calls of fn, captured in one HIP graph and replayed
+    once (after `warmup` eager calls and one untimed replay)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / 1e3
+
+    def many():
+        for _ in range(steps):
+            fn()
+    return time_graph(capture(many))
 
 
 def run_extra(args, q, synth):
@@ -274,7 +306,6 @@ def run_extra(args, q, synth):
             active_bytes += n_act * (q8_bytes(2 * n_ff, n_embd) + q8_bytes(n_embd, n_ff))
             layers.append(dict(wug=wug, wd=wd, ids=torch.from_numpy(ids).to(dev),
                                cw=torch.from_numpy(cw).to(dev), xf=xf,
-                               xq=q.q8_empty(n_tok, n_embd, dev),
                                h=torch.empty((n_tok, U, n_ff), dtype=torch.float32, device=dev),
                                out=torch.empty((n_tok, n_embd), dtype=torch.float32, device=dev),
                                ws=q.moe_workspace(n_tok, n_embd, n_ff, E, U, dev)))
@@ -282,8 +313,7 @@ def run_extra(args, q, synth):
 
         def step():
             for d in layers:
-                q.q8_0_quantize_rows(d["xf"], y=d["xq"])
-                q.moe_up_gate_swiglu(d["wug"], d["xq"], d["ids"], n_embd, n_ff, E, d["ws"],
+                q.moe_up_gate_swiglu(d["wug"], d["xf"], d["ids"], n_embd, n_ff, E, d["ws"],
                                      h=d["h"])
                 q.moe_down_combine(d["wd"], d["h"], d["ids"], d["cw"], n_ff, n_embd, E, d["ws"],
                                    out=d["out"])

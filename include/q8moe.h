@@ -125,7 +125,8 @@ int q8_0_matmul(const q8_0_block *w, const q8_0_block *x, float *y,
  *   Y_b[m][n] = X_b[m][k] . W_b[n][k]^T
  * with W_b = w + b*w_batch_stride (blocks), X_b row r = x + b*x_batch_stride +
  * r*x_row_stride (blocks), Y_b row r = y + b*y_batch_stride + r*y_row_stride
- * (floats).  All outputs of all descriptors must be disjoint.
+ * (floats).  All outputs of all descriptors must be disjoint; with batch > 1
+ * the call rejects y_batch_stride < n and w_batch_stride < n*k/32 (Q8_E_SHAPE).
  * descs is a HOST array, read before the call returns.
  * Limits: n_desc <= 32 per call (Q8_E_UNSUPPORTED above), m <= 16 for every
  * descriptor (larger m: use q8_0_matmul).  W_b must be 16-byte aligned.
@@ -148,11 +149,13 @@ int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *str
  * Mixture-of-experts expert FFN ([XEON] sections on the broken op paths and on
  * the three-part fix, runtime graph fallback).  Per token t and active slot
  * u < n_used with expert e = ids[t][u]:
- *   g  = W_ug[e][j]        . x_t   (gate rows j < n_ff, the first half)
- *   up = W_ug[e][n_ff + j] . x_t   (up rows, the second half)
+ *   g  = W_ug[e][j]        . q(x_t)   (gate rows j < n_ff, the first half)
+ *   up = W_ug[e][n_ff + j] . q(x_t)   (up rows, the second half)
  *   h[t][u][j] = silu(g) * up = g / (1 + exp(-g)) * up        (fp32)
  *   out[t] = sum over u ascending of cw[t][u] * (W_d[e] . q(h[t][u]))
- * where q() is the quantization rule above applied to each h row.  The gate
+ * where q() is the quantization rule above, applied to each token row x_t and
+ * to each h row inside the calls (the bytes equal q8_0_quantize_rows of those
+ * rows), as the activations reach mul_mat_id in fp32.  The gate
  * and up products use the same quantized token row; the fused computation
  * gives the numbers of the split form (two mul_mat_id on row views + silu*up).
  * Each active expert's weight rows are streamed once per call, for all of the
@@ -173,12 +176,13 @@ size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff,
                            int64_t n_expert, int64_t n_used);
 
 /*   w_up_gate  Q8_0 [n_expert][2*n_ff][n_embd/32]  (ggml [n_embd, 2*n_ff, n_expert])
- *   x          Q8_0 [n_tok][n_embd/32]             (quantized token activations)
+ *   x          fp32 [n_tok][n_embd], 16-byte aligned (token activations)
  *   ids        int32 [n_tok][n_used]
  *   h          fp32 [n_tok][n_used][n_ff]          (written)
  * n_tok >= 0, n_embd % 32 == 0, n_ff % 32 == 0, 1 <= n_used <= 16.
- * Q8_E_UNSUPPORTED when n_tok*n_used > 4096 (the prefill form is separate). */
-int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const q8_0_block *x,
+ * Q8_E_UNSUPPORTED when n_tok*n_used > 1024 (decode sizes; the prefill form of
+ * the expert FFN is separate). */
+int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const float *x,
                        const int32_t *ids, float *h,
                        int64_t n_tok, int64_t n_embd, int64_t n_ff,
                        int64_t n_expert, int64_t n_used,

@@ -192,9 +192,10 @@ def moe_workspace(n_tok, n_embd, n_ff, n_expert, n_used, device):
 
 
 def moe_up_gate_swiglu(w_up_gate, x, ids, n_embd, n_ff, n_expert, ws, h=None):
-    """h[t][u][j] = silu(gate) * up; returns h fp32 [n_tok][n_used][n_ff]."""
+    """h[t][u][j] = silu(gate) * up from fp32 token rows x [n_tok][n_embd]
+    (quantized inside); returns h fp32 [n_tok][n_used][n_ff]."""
     _need(w_up_gate, torch.uint8, "w_up_gate")
-    _need(x, torch.uint8, "x")
+    _need(x, torch.float32, "x")
     _need(ids, torch.int32, "ids")
     _need(ws, torch.uint8, "ws")
     n_tok, n_used = ids.shape

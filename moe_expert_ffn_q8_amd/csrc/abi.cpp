@@ -123,8 +123,10 @@ int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *str
         if (!s.w || !s.x || !s.y) return Q8_E_NULL;
         const int64_t nb = s.k / kQK;
         if (s.m > 1 && (s.x_row_stride < nb || s.y_row_stride < s.n)) return Q8_E_SHAPE;
+        // batch entries must not write the same outputs (a common mistake: a
+        // zero output batch stride)
         if (s.batch > 1 && (s.w_batch_stride < s.n * nb || s.x_batch_stride < 0 ||
-                            s.y_batch_stride < 0))
+                            s.y_batch_stride < s.n))
             return Q8_E_SHAPE;
         if (!aligned(s.w, 2) || !aligned(s.x, 2) || !aligned(s.y, 4)) return Q8_E_ALIGN;
         q8::StreamDesc &o = d[nd++];
@@ -163,7 +165,7 @@ size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t 
     return q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
 }
 
-int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const q8_0_block *x, const int32_t *ids,
+int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const float *x, const int32_t *ids,
                        float *h, int64_t n_tok, int64_t n_embd, int64_t n_ff,
                        int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
                        void *stream)
@@ -173,10 +175,10 @@ int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const q8_0_block *x, const i
     if (ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
     if (!aligned(ws, 256)) return Q8_E_ALIGN;
     if (n_tok > 0 && (!w_up_gate || !x || !ids || !h)) return Q8_E_NULL;
-    if (!aligned(w_up_gate, 16) || !aligned(x, 2) || !aligned(ids, 4) || !aligned(h, 4))
+    if (!aligned(w_up_gate, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(h, 4))
         return Q8_E_ALIGN;
     q8::MoeUpGateArgs a;
-    a.w = (const uint8_t *)w_up_gate; a.x = (const uint8_t *)x; a.ids = ids; a.h = h;
+    a.w = (const uint8_t *)w_up_gate; a.x = x; a.ids = ids; a.h = h;
     a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
     a.n_used = n_used; a.ws = ws;
     return hip_status(q8::launch_moe_up_gate(a, as_stream(stream)));

@@ -105,31 +105,37 @@ __device__ void pick_expert(const int32_t *ids, int n_slots, int n_expert, int r
     __syncthreads();
 }
 
-// Copy Q8_0 token rows into the masked image (scale bytes zeroed) + fp32 scales.
-__device__ void stage_rows_q8(const uint8_t *x, int64_t row_bytes_src, const int *rows_of,
-                              int mc, int nb, uint8_t *ximg, float *xsc)
+// Quantize mc fp32 rows (row m starts at base + row_index[m] * row_floats)
+// into the masked image (nb*34 bytes per row, scale bytes zero) plus fp32
+// scales, with the activation quantization rule (same code as the quantizer:
+// the bytes equal q8_0_quantize_rows of those rows).  All threads of the
+// workgroup take part; 8 lanes per block.
+__device__ void quantize_rows_to_image(const float *base, int64_t row_floats, const int *row_index,
+                                       int mc, int nb, uint8_t *ximg, float *xsc)
 {
+    const int tid = threadIdx.x;
+    const int li = tid & 7;
     const int img_row = nb * kBlockBytes;
-    const int halves = mc * nb * 17;
-    for (int i = threadIdx.x; i < halves; i += kThreads) {
-        const int m = i / (nb * 17);
-        const int rem = i - m * nb * 17;
-        const int b = rem / 17;
-        const int hh = rem - b * 17;
-        const uint32_t v = load_u16(x + (int64_t)rows_of[m] * row_bytes_src + b * kBlockBytes + 2 * hh);
+    const int step = (int)blockDim.x / 8;
+    for (int bi = tid >> 3; bi < mc * nb; bi += step) {
+        const int m = bi / nb;
+        const int b = bi - m * nb;
+        const float4 v = *(const float4 *)(base + (int64_t)row_index[m] * row_floats + b * kQK + 4 * li);
+        uint32_t codes, dbits;
+        quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
         uint16_t *img16 = (uint16_t *)(ximg + m * img_row);
-        if (hh == 0) {
-            xsc[m * nb + b] = half_bits_to_float(v);
+        if (li == 0) {
             img16[b * 17] = 0;
-        } else {
-            img16[b * 17 + hh] = (uint16_t)v;
+            xsc[m * nb + b] = half_bits_to_float(dbits);
         }
+        img16[b * 17 + 1 + 2 * li] = (uint16_t)(codes & 0xffffu);
+        img16[b * 17 + 2 + 2 * li] = (uint16_t)(codes >> 16);
     }
 }
 
 struct UgParams {
     const uint8_t *w;
-    const uint8_t *x;
+    const float *x;        // fp32 [n_tok][n_embd]
     const int32_t *ids;
     float *h;
     int32_t *err;
@@ -184,12 +190,24 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
 
+    // The wave walks a sequence of half-tiles (gate rows of tile t, up rows of
+    // tile t, gate rows of tile t+4, ...) with one half-tile of loads in
+    // flight ahead of the one being computed.
+    u32x4 g[kTileLoads];
+    auto issue = [&](int tt, bool up) {
+        const int j0 = tt * p.R;
+        const int rows = min(p.R, p.n_ff - j0);
+        tile_issue(We + (int64_t)((up ? p.n_ff : 0) + j0) * row_bytes, rows * nb * 17 / 8, lane, g);
+    };
+
     for (int c0 = 0; c0 < count; c0 += MT) {
         const int mc = min(MT, count - c0);
         __syncthreads();
         if (tid < mc) rows_of[tid] = ps.slots[c0 + tid] / p.n_used;
+        // the first half-tile does not depend on the activations: issue it first
+        if (t0 + wave < t1) issue(t0 + wave, false);
         __syncthreads();
-        stage_rows_q8(p.x, row_bytes, rows_of, mc, nb, ximg, xsc);
+        quantize_rows_to_image(p.x, (int64_t)nb * kQK, rows_of, mc, nb, ximg, xsc);
         __syncthreads();
 
         uint32_t xr[kQuadDwords];
@@ -202,33 +220,29 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
         for (int t = t0 + wave; t < t1; t += kWaves) {
             const int j0 = t * p.R;
             const int rows = min(p.R, p.n_ff - j0);
-            const int chunks = rows * nb * 17 / 8;
             const int live = rows * Q;
-            u32x4 gg[kTileLoads], gu[kTileLoads];
-            tile_issue(We + (int64_t)j0 * row_bytes, chunks, lane, gg);
-            tile_issue(We + (int64_t)(p.n_ff + j0) * row_bytes, chunks, lane, gu);
-#pragma unroll
+#pragma unroll 1
             for (int half = 0; half < 2; ++half) {
                 uint32_t wq[kQuadDwords];
-                tile_to_quad(stage, half == 0 ? gg : gu, lane, live, wq);
+                tile_to_quad(stage, g, lane, live, wq);
+                if (half == 0) issue(t, true);
+                else if (t + kWaves < t1) issue(t + kWaves, false);
                 float dw0, dw1, dw2, dw3;
                 quad_scales(wq, dw0, dw1, dw2, dw3);
                 float *red = half == 0 ? redg : redu;
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    if (m < mc) {
-                        uint32_t xt[kQuadDwords];
-                        const uint32_t *xq = xr;
-                        float4 dx = xd1;
-                        if (MT != 1) {
-                            lds_quad(ximg + m * img_row + kQuadBytes * c, xt);
-                            xq = xt;
-                            dx = *(const float4 *)(xsc + m * nb + 4 * c);
-                        }
-                        int s[4];
-                        const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, s);
-                        red[m * kWave + lane] = (lane < live) ? acc : 0.0f;
+#pragma unroll 1
+                for (int m = 0; m < mc; ++m) {
+                    uint32_t xt[kQuadDwords];
+                    const uint32_t *xq = xr;
+                    float4 dx = xd1;
+                    if (MT != 1) {
+                        lds_quad(ximg + m * img_row + kQuadBytes * c, xt);
+                        xq = xt;
+                        dx = *(const float4 *)(xsc + m * nb + 4 * c);
                     }
+                    int sb[4];
+                    const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, sb);
+                    red[m * kWave + lane] = (lane < live) ? acc : 0.0f;
                 }
             }
             wave_lds_sync();
@@ -237,12 +251,12 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
                 const int r = i - m * rows;
                 const float *pg = redg + m * kWave + r * Q;
                 const float *pu = redu + m * kWave + r * Q;
-                float g = pg[0], u = pu[0];
+                float gs = pg[0], us = pu[0];
                 for (int cc = 1; cc < Q; ++cc) {
-                    g += pg[cc];
-                    u += pu[cc];
+                    gs += pg[cc];
+                    us += pu[cc];
                 }
-                const float hv = g / (1.0f + expf(-g)) * u;
+                const float hv = gs / (1.0f + expf(-gs)) * us;
                 p.h[(int64_t)ps.slots[c0 + m] * p.n_ff + j0 + r] = hv;
             }
             wave_lds_sync();
@@ -291,26 +305,19 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
 
+    u32x4 g[kTileLoads];
+    auto issue = [&](int tt) {
+        const int r0 = tt * p.R;
+        tile_issue(We + (int64_t)r0 * row_bytes, min(p.R, p.n_rows - r0) * nb * 17 / 8, lane, g);
+    };
+
     for (int c0 = 0; c0 < count; c0 += MT) {
         const int mc = min(MT, count - c0);
+        int t = t0 + wave;
+        if (t < t1) issue(t);        // independent of h: overlap with the h loads
         __syncthreads();
         // quantize the h rows of this chunk's slots into the masked image
-        for (int bi = tid >> 3; bi < mc * nb; bi += kThreads / 8) {
-            const int m = bi / nb;
-            const int b = bi - m * nb;
-            const int li = tid & 7;
-            const float4 v = *(const float4 *)(p.h + (int64_t)ps.slots[c0 + m] * p.n_ff +
-                                                b * kQK + 4 * li);
-            uint32_t codes, dbits;
-            quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
-            uint16_t *img16 = (uint16_t *)(ximg + m * img_row);
-            if (li == 0) {
-                img16[b * 17] = 0;
-                xsc[m * nb + b] = half_bits_to_float(dbits);
-            }
-            img16[b * 17 + 1 + 2 * li] = (uint16_t)(codes & 0xffffu);
-            img16[b * 17 + 2 + 2 * li] = (uint16_t)(codes >> 16);
-        }
+        quantize_rows_to_image(p.h, p.n_ff, ps.slots + c0, mc, nb, ximg, xsc);
         __syncthreads();
 
         uint32_t xr[kQuadDwords];
@@ -320,23 +327,13 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
             xd1 = *(const float4 *)(xsc + 4 * c);
         }
 
-        u32x4 g[kTileLoads];
-        int t = t0 + wave;
-        if (t < t1) {
-            const int r0 = t * p.R;
-            tile_issue(We + (int64_t)r0 * row_bytes, min(p.R, p.n_rows - r0) * nb * 17 / 8, lane, g);
-        }
         for (; t < t1; t += kWaves) {
             const int row0 = t * p.R;
             const int rows = min(p.R, p.n_rows - row0);
             const int live = rows * Q;
             uint32_t wq[kQuadDwords];
             tile_to_quad(stage, g, lane, live, wq);
-            if (t + kWaves < t1) {
-                const int r0 = (t + kWaves) * p.R;
-                tile_issue(We + (int64_t)r0 * row_bytes, min(p.R, p.n_rows - r0) * nb * 17 / 8,
-                           lane, g);
-            }
+            if (t + kWaves < t1) issue(t + kWaves);
             float dw0, dw1, dw2, dw3;
             quad_scales(wq, dw0, dw1, dw2, dw3);
 #pragma unroll
@@ -366,6 +363,120 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
             }
             wave_lds_sync();
         }
+    }
+}
+
+// Row-major down projection with the combine fused in (small slot counts,
+// i.e. decode at one or two tokens).  A workgroup owns R output rows for all
+// slots: wave w streams those rows of the experts of slots w, w + kRowWaves,
+// ..., the per-slot results meet in LDS and the workgroup writes
+//   out[t][row] = sum over u ascending of cw[t][u] * y[t*n_used+u][row]
+// directly: no workspace round trip and no combine launch.  Every workgroup
+// quantizes all slots' h rows into its LDS image (same rule as the quantizer).
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = kRowWaves * kWave;
+constexpr int kRowsMaxSlots = 16;
+
+struct DrParams {
+    const uint8_t *w;
+    const float *h;
+    const int32_t *ids;
+    const float *cw;
+    float *out;
+    int32_t *err;
+    int n_used, n_slots, n_expert, nb, n_ff, n_rows, R;
+};
+
+__global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrParams p)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_e[kRowsMaxSlots];
+    __shared__ int s_rows[kRowsMaxSlots];
+    __shared__ float ys[kRowsMaxSlots][kWave];
+    __shared__ float red[kRowWaves][kWave];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int nb = p.nb;
+    const int Q = nb >> 2;
+    const int img_row = nb * kBlockBytes;
+    uint8_t *stage = smem + wave * kStageBytes;
+    uint8_t *ximg = smem + kRowWaves * kStageBytes;
+    float *xsc = (float *)(ximg + kRowsMaxSlots * img_row);
+
+    const int row0 = blockIdx.x * p.R;
+    const int rows = min(p.R, p.n_rows - row0);
+    const int live = rows * Q;
+    const int c = lane % Q;
+    const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+
+    if (tid < p.n_slots) {
+        const int e = p.ids[tid];
+        s_e[tid] = (e >= 0 && e < p.n_expert) ? e : -1;
+        s_rows[tid] = tid;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && tid == 0) {
+        int bad = 0;
+        for (int s = 0; s < p.n_slots; ++s) bad |= (s_e[s] < 0);
+        *p.err = bad;
+    }
+
+    u32x4 g[kTileLoads];
+    auto next_slot = [&](int s) {
+        while (s < p.n_slots && s_e[s] < 0) s += kRowWaves;
+        return s;
+    };
+    auto issue = [&](int s) {
+        const uint8_t *base = p.w + ((int64_t)s_e[s] * p.n_rows + row0) * row_bytes;
+        tile_issue(base, rows * nb * 17 / 8, lane, g);
+    };
+    int s = next_slot(wave);
+    if (s < p.n_slots) issue(s);           // weights first: independent of h
+
+    quantize_rows_to_image(p.h, p.n_ff, s_rows, p.n_slots, nb, ximg, xsc);
+    __syncthreads();
+
+    while (s < p.n_slots) {
+        uint32_t wq[kQuadDwords];
+        tile_to_quad(stage, g, lane, live, wq);
+        const int sn = next_slot(s + kRowWaves);
+        if (sn < p.n_slots) issue(sn);
+        float dw0, dw1, dw2, dw3;
+        quad_scales(wq, dw0, dw1, dw2, dw3);
+        uint32_t xq[kQuadDwords];
+        lds_quad(ximg + s * img_row + kQuadBytes * c, xq);
+        const float4 dx = *(const float4 *)(xsc + s * nb + 4 * c);
+        int sb[4];
+        const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, sb);
+        red[wave][lane] = (lane < live) ? acc : 0.0f;
+        wave_lds_sync();
+        if (lane < rows) {
+            const float *pr = &red[wave][lane * Q];
+            float y = pr[0];
+            for (int cc = 1; cc < Q; ++cc) y += pr[cc];
+            ys[s][lane] = y;
+        }
+        wave_lds_sync();
+        s = sn;
+    }
+    __syncthreads();
+
+    const int n_tok = p.n_slots / p.n_used;
+    for (int i = tid; i < n_tok * rows; i += kRowThreads) {
+        const int t = i / rows;
+        const int r = i - t * rows;
+        bool bad = false;
+        for (int u = 0; u < p.n_used; ++u) bad |= (s_e[t * p.n_used + u] < 0);
+        float acc;
+        if (bad) {
+            acc = __builtin_nanf("");
+        } else {
+            acc = p.cw[t * p.n_used] * ys[t * p.n_used][r];
+            for (int u = 1; u < p.n_used; ++u)
+                acc = fmaf(p.cw[t * p.n_used + u], ys[t * p.n_used + u][r], acc);
+        }
+        p.out[(int64_t)t * p.n_rows + row0 + r] = acc;
     }
 }
 
@@ -424,6 +535,104 @@ __global__ __launch_bounds__(kThreads) void moe_route_kernel(const int32_t *ids,
     if (tid == 0) offsets[n_expert] = pos;
 }
 
+// ---------------------------------------------------------------------------
+// Generic expert kernels: any n_embd, n_ff that are multiples of 32 (used when
+// the block count per row is not a multiple of 8 or exceeds the fast path's
+// limit).  One wave per (slot, row); lanes stride over blocks with 2-byte
+// loads; fixed-order xor-tree reduction.
+
+__device__ __forceinline__ float generic_row_dot(const uint8_t *w, const uint8_t *x, int nb,
+                                                 int lane)
+{
+    float acc = 0.0f;
+    for (int b = lane; b < nb; b += kWave) {
+        const uint8_t *wb = w + b * kBlockBytes;
+        const uint8_t *xb = x + b * kBlockBytes;
+        int s = 0;
+        for (int hh = 1; hh < 17; ++hh) {
+            const uint32_t wv = load_u16(wb + 2 * hh);
+            const uint32_t xv = load_u16(xb + 2 * hh);
+            s += (int)(int8_t)(wv & 0xff) * (int)(int8_t)(xv & 0xff);
+            s += (int)(int8_t)(wv >> 8) * (int)(int8_t)(xv >> 8);
+        }
+        acc = fmaf(half_bits_to_float(load_u16(wb)) * half_bits_to_float(load_u16(xb)),
+                   (float)s, acc);
+    }
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    return acc;
+}
+
+__device__ __forceinline__ void generic_flag_invalid(const int32_t *ids, int n_slots,
+                                                     int n_expert, int32_t *err)
+{
+    if (blockIdx.x != 0 || blockIdx.y != 0 || threadIdx.x != 0) return;
+    int bad = 0;
+    for (int s = 0; s < n_slots; ++s) bad |= (ids[s] < 0 || ids[s] >= n_expert);
+    *err = bad;
+}
+
+// grid (n_slots, ceil(n_ff / 4)); 4 waves, one j each.  The slot's token row
+// is quantized into LDS first (same rule and code as the quantizer).
+__device__ void quantize_row_to_blocks(const float *src, int nb, uint8_t *dst)
+{
+    const int tid = threadIdx.x;
+    for (int bi = tid >> 3; bi < nb; bi += kThreads / 8) {
+        const int li = tid & 7;
+        const float4 v = *(const float4 *)(src + bi * kQK + 4 * li);
+        uint32_t codes, dbits;
+        quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+        uint16_t *b16 = (uint16_t *)(dst + bi * kBlockBytes);
+        if (li == 0) b16[0] = (uint16_t)dbits;
+        b16[1 + 2 * li] = (uint16_t)(codes & 0xffffu);
+        b16[2 + 2 * li] = (uint16_t)(codes >> 16);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void moe_up_gate_generic_kernel(UgParams p)
+{
+    extern __shared__ __align__(16) uint8_t xq[];      // nb blocks of 34 B
+    generic_flag_invalid(p.ids, p.n_slots, p.n_expert, p.err);
+    const int s = blockIdx.x;
+    const int e = p.ids[s];
+    quantize_row_to_blocks(p.x + (int64_t)(s / p.n_used) * p.nb * kQK, p.nb, xq);
+    __syncthreads();
+    const int j = blockIdx.y * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (j >= p.n_ff) return;
+    float *dst = p.h + (int64_t)s * p.n_ff + j;
+    if (e < 0 || e >= p.n_expert) {
+        if (lane == 0) *dst = __builtin_nanf("");
+        return;
+    }
+    const int64_t row_bytes = (int64_t)p.nb * kBlockBytes;
+    const uint8_t *We = p.w + (int64_t)e * 2 * p.n_ff * row_bytes;
+    const uint8_t *xr = xq;
+    const float g = generic_row_dot(We + (int64_t)j * row_bytes, xr, p.nb, lane);
+    const float u = generic_row_dot(We + (int64_t)(p.n_ff + j) * row_bytes, xr, p.nb, lane);
+    if (lane == 0) *dst = g / (1.0f + expf(-g)) * u;
+}
+
+// grid (n_slots, ceil(n_rows / 4)); the slot's h row is quantized into LDS
+// first (same rule and code as the activation quantizer).
+__global__ __launch_bounds__(kThreads) void moe_down_generic_kernel(DnParams p)
+{
+    extern __shared__ __align__(16) uint8_t hq[];      // nb blocks of 34 B
+    generic_flag_invalid(p.ids, p.n_slots, p.n_expert, p.err);
+    const int s = blockIdx.x;
+    const int e = p.ids[s];
+    if (e < 0 || e >= p.n_expert) return;              // the combine writes NaN
+    const int tid = threadIdx.x;
+    quantize_row_to_blocks(p.h + (int64_t)s * p.n_ff, p.nb, hq);
+    __syncthreads();
+    const int row = blockIdx.y * kWaves + (tid >> 6);
+    const int lane = tid & 63;
+    if (row >= p.n_rows) return;
+    const int64_t row_bytes = (int64_t)p.nb * kBlockBytes;
+    const uint8_t *wr = p.w + ((int64_t)e * p.n_rows + row) * row_bytes;
+    const float y = generic_row_dot(wr, hq, p.nb, lane);
+    if (lane == 0) p.yslot[(int64_t)s * p.n_rows + row] = y;
+}
+
 int pick_mt(int64_t n_tok)
 {
     if (n_tok <= 1) return 1;
@@ -469,7 +678,7 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
 {
     if (a.n_tok == 0) return 0;
     const int64_t nb = a.n_embd / kQK;
-    if (nb % 8 != 0 || nb > kStreamMaxNb) return -4;
+    const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
     UgParams p;
     p.w = a.w; p.x = a.x; p.ids = a.ids; p.h = a.h; p.err = (int32_t *)a.ws;
     p.n_slots = (int)(a.n_tok * a.n_used);
@@ -477,12 +686,19 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
     p.n_expert = (int)a.n_expert;
     p.nb = (int)nb;
     p.n_ff = (int)a.n_ff;
-    p.R = (int)(64 / (nb / 4));
+    p.R = fast ? (int)(64 / (nb / 4)) : 1;
     p.tiles_per_expert = (p.n_ff + p.R - 1) / p.R;
     const int64_t active = a.n_expert < p.n_slots ? a.n_expert : p.n_slots;
     p.tiles_per_wg = tiles_per_wg_for(active, p.tiles_per_expert);
     p.wgs_per_expert = (p.tiles_per_expert + p.tiles_per_wg - 1) / p.tiles_per_wg;
     const int64_t grid = active * p.wgs_per_expert;
+    if (!fast) {
+        const size_t lds = (size_t)nb * kBlockBytes;
+        if (lds > (size_t)max_lds_bytes()) return -4;
+        dim3 g((unsigned)p.n_slots, (unsigned)((p.n_ff + kWaves - 1) / kWaves));
+        hipLaunchKernelGGL(moe_up_gate_generic_kernel, g, dim3(kThreads), lds, stream, p);
+        return hipGetLastError() == hipSuccess ? 0 : -6;
+    }
     if (grid > 0x7fffffff) return -4;
     switch (pick_mt(a.n_tok)) {
         case 1: return launch_ug_mt<1>(p, (int)grid, stream);
@@ -506,7 +722,22 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
 {
     if (a.n_tok == 0) return 0;
     const int64_t nb = a.n_ff / kQK;
-    if (nb % 8 != 0 || nb > kStreamMaxNb) return -4;
+    const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
+    const int64_t n_slots = a.n_tok * a.n_used;
+    if (fast && n_slots <= kRowsMaxSlots) {
+        DrParams r;
+        r.w = a.w; r.h = a.h; r.ids = a.ids; r.cw = a.cw; r.out = a.out;
+        r.err = (int32_t *)a.ws;
+        r.n_used = (int)a.n_used; r.n_slots = (int)n_slots; r.n_expert = (int)a.n_expert;
+        r.nb = (int)nb; r.n_ff = (int)a.n_ff; r.n_rows = (int)a.n_embd;
+        r.R = (int)(64 / (nb / 4));
+        const size_t lds = (size_t)kRowWaves * kStageBytes + (size_t)kRowsMaxSlots * nb * kBlockBytes +
+                           (size_t)kRowsMaxSlots * nb * 4;
+        if (lds > (size_t)max_lds_bytes()) return -4;
+        const unsigned grid = (unsigned)((a.n_embd + r.R - 1) / r.R);
+        hipLaunchKernelGGL(moe_down_rows_kernel, dim3(grid), dim3(kRowThreads), lds, stream, r);
+        return hipGetLastError() == hipSuccess ? 0 : -6;
+    }
     DnParams p;
     p.w = a.w; p.h = a.h; p.ids = a.ids;
     p.yslot = (float *)((uint8_t *)a.ws + 256);
@@ -517,15 +748,21 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
     p.nb = (int)nb;
     p.n_ff = (int)a.n_ff;
     p.n_rows = (int)a.n_embd;
-    p.R = (int)(64 / (nb / 4));
+    p.R = fast ? (int)(64 / (nb / 4)) : 1;
     p.tiles_per_expert = (p.n_rows + p.R - 1) / p.R;
     const int64_t active = a.n_expert < p.n_slots ? a.n_expert : p.n_slots;
     p.tiles_per_wg = tiles_per_wg_for(active, p.tiles_per_expert);
     p.wgs_per_expert = (p.tiles_per_expert + p.tiles_per_wg - 1) / p.tiles_per_wg;
     const int64_t grid = active * p.wgs_per_expert;
-    if (grid > 0x7fffffff) return -4;
     int rc;
-    switch (pick_mt(a.n_tok)) {
+    if (fast && grid > 0x7fffffff) return -4;
+    if (!fast) {
+        const size_t lds = (size_t)nb * kBlockBytes;
+        if (lds > (size_t)max_lds_bytes()) return -4;
+        dim3 g((unsigned)p.n_slots, (unsigned)((p.n_rows + kWaves - 1) / kWaves));
+        hipLaunchKernelGGL(moe_down_generic_kernel, g, dim3(kThreads), lds, stream, p);
+        rc = hipGetLastError() == hipSuccess ? 0 : -6;
+    } else switch (pick_mt(a.n_tok)) {
         case 1: rc = launch_dn_mt<1>(p, (int)grid, stream); break;
         case 2: rc = launch_dn_mt<2>(p, (int)grid, stream); break;
         default: rc = launch_dn_mt<4>(p, (int)grid, stream); break;

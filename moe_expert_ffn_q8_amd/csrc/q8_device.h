@@ -105,16 +105,23 @@ constexpr int kStageBytes = kWave * kQuadBytes;            // 8704: one wave's L
 constexpr int kStageChunks = kStageBytes / 16;             // 544
 constexpr int kTileLoads = (kStageChunks + kWave - 1) / kWave;   // 9 per lane
 
-// Issue the coalesced 16-byte loads of one wave-tile into registers.
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format,
+// no swizzle): loads past num_records return zero instead of faulting.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCacheNT = 2;          // aux bit: non-temporal (streaming) load
+
+// Issue the coalesced 16-byte loads of one wave-tile into registers, through a
+// raw buffer resource bounded to the tile: chunk i of lane l is load u with
+// i = 64u + l, and chunks past the tile read as zero without a predicate (so
+// no per-load masks or 64-bit addresses stay live in registers).
 __device__ __forceinline__ void tile_issue(const uint8_t *base, int chunks, int lane,
                                            u32x4 (&g)[kTileLoads])
 {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, chunks * 16, kBufferWord3);
 #pragma unroll
-    for (int u = 0; u < kTileLoads; ++u) {
-        const int i = u * kWave + lane;
-        if (i < chunks) g[u] = load_nt16(base + 16 * (int64_t)i);
-        else g[u] = (u32x4){0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < kTileLoads; ++u)
+        g[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (u * kWave + lane), 0, kCacheNT);
 }
 
 // Write the loaded chunks to the wave's LDS slot in load order, then read back

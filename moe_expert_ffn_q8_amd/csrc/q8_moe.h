@@ -13,7 +13,7 @@ constexpr int kMoeMaxExperts = 1024;
 
 struct MoeUpGateArgs {
     const uint8_t *w;       // [n_expert][2*n_ff][n_embd/32] blocks
-    const uint8_t *x;       // [n_tok][n_embd/32] blocks
+    const float *x;         // fp32 [n_tok][n_embd], quantized inside
     const int32_t *ids;     // [n_tok][n_used]
     float *h;               // [n_tok][n_used][n_ff]
     int64_t n_tok, n_embd, n_ff, n_expert, n_used;

@@ -99,6 +99,18 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const StreamArgs args)
     const int img_row = nb * kBlockBytes;
     float *xsc = (float *)(ximg + MT * args.nb_max * kBlockBytes);
 
+    u32x4 g[kTileLoads];
+    auto issue = [&](int tt) {
+        const int row0 = tt * R;
+        const int rows = min(R, n - row0);
+        tile_issue(W + (int64_t)row0 * row_bytes, rows * nb * 17 / 8, lane, g);
+    };
+
+    // The first tile's weight loads do not depend on the activations: issue
+    // them before the activation round trip so the two latencies overlap.
+    int t = t0 + wave;
+    if (t < t1) issue(t);
+
     // ---- activations -> masked image + fp32 scales (whole workgroup) ----
     const int halves = M * nb * 17;
     for (int i = tid; i < halves; i += kThreads) {
@@ -126,15 +138,6 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const StreamArgs args)
         xd0 = s.x; xd1 = s.y; xd2 = s.z; xd3 = s.w;
     }
 
-    u32x4 g[kTileLoads];
-    auto issue = [&](int tt) {
-        const int row0 = tt * R;
-        const int rows = min(R, n - row0);
-        tile_issue(W + (int64_t)row0 * row_bytes, rows * nb * 17 / 8, lane, g);
-    };
-
-    int t = t0 + wave;
-    if (t < t1) issue(t);
     for (; t < t1; t += kWaves) {
         const int row0 = t * R;
         const int rows = min(R, n - row0);
@@ -176,6 +179,160 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const StreamArgs args)
             Y[(int64_t)m * J.y_rstride + row0 + r] = acc;
         }
         wave_lds_sync();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Flat engine for m <= 2 (decode at batch 1 and 2).
+//
+// Every tile of every job and batch entry is numbered in one flat space; each
+// workgroup is a single wave that takes a contiguous slice of that space (the
+// same number of tiles for every wave, sized from the occupancy so the whole
+// grid is resident at once and finishes together).  The wave keeps the next
+// tile's loads in flight while it computes the current one.  A lane's
+// activation quad (4 blocks) is loaded straight from global memory into
+// registers, with the scale halfwords masked out, whenever the wave moves to
+// a new (job, batch entry); there is no workgroup-wide staging and no barrier.
+
+struct FlatJob {
+    const uint8_t *w;
+    const uint8_t *x;
+    float *y;
+    int32_t *sums;
+    int64_t w_bstride;   // bytes
+    int64_t x_bstride;   // bytes
+    int64_t y_bstride;   // floats
+    int32_t x_rstride;   // bytes
+    int32_t y_rstride;   // floats
+    int32_t n, nb, m, batch;
+    int32_t R;           // rows per tile
+    int32_t tpb;         // tiles per batch entry
+    int32_t tile0;       // first flat tile of this job
+    int32_t x_al8;       // activation rows start on 8-byte boundaries
+};
+
+struct FlatArgs {
+    FlatJob job[kStreamMaxJobs];
+    int32_t n_jobs;
+    int32_t total_tiles;
+    int32_t tiles_per_wave;
+};
+
+static_assert(sizeof(FlatArgs) <= 4000, "kernel arguments must stay below 4 KB");
+
+// Load one activation quad (136 B) into registers as a masked image + scales.
+__device__ __forceinline__ void load_x_quad(const uint8_t *p, bool al8, uint32_t (&q)[kQuadDwords],
+                                            float4 &d)
+{
+    if (al8) {
+        const u32x2 *src = (const u32x2 *)p;
+#pragma unroll
+        for (int v = 0; v < 17; ++v) {
+            const u32x2 t = src[v];
+            q[2 * v] = t.x;
+            q[2 * v + 1] = t.y;
+        }
+    } else {
+        const uint16_t *src = (const uint16_t *)p;
+#pragma unroll
+        for (int v = 0; v < kQuadDwords; ++v)
+            q[v] = (uint32_t)src[2 * v] | ((uint32_t)src[2 * v + 1] << 16);
+    }
+    d.x = half_bits_to_float(q[0]);
+    d.y = half_bits_to_float(q[8] >> 16);
+    d.z = half_bits_to_float(q[17]);
+    d.w = half_bits_to_float(q[25] >> 16);
+    q[0] &= 0xffff0000u;
+    q[8] &= 0x0000ffffu;
+    q[17] &= 0xffff0000u;
+    q[25] &= 0x0000ffffu;
+}
+
+template <int MT, bool SUMS>
+__global__ __launch_bounds__(kWave) void stream_flat_kernel(const FlatArgs a)
+{
+    __shared__ __align__(16) uint8_t stage[kStageBytes];
+    __shared__ float red[MT * kWave];
+    const int lane = threadIdx.x;
+    const int t_begin = blockIdx.x * a.tiles_per_wave;
+    const int t_end = min(t_begin + a.tiles_per_wave, a.total_tiles);
+    if (t_begin >= t_end) return;
+
+    int jj = 0;
+    for (int i = 1; i < a.n_jobs; ++i)
+        if (a.job[i].tile0 <= t_begin) jj = i;
+    int loc = t_begin - a.job[jj].tile0;
+
+    u32x4 g[kTileLoads];
+    auto issue = [&](int j, int l) {
+        const FlatJob &J = a.job[j];
+        const int bi = l / J.tpb;
+        const int row0 = (l - bi * J.tpb) * J.R;
+        const int rows = min(J.R, J.n - row0);
+        const uint8_t *base = J.w + (int64_t)bi * J.w_bstride +
+                              (int64_t)row0 * J.nb * kBlockBytes;
+        tile_issue(base, rows * J.nb * 17 / 8, lane, g);
+    };
+
+    issue(jj, loc);
+    int jx = -1, bx = -1;
+    uint32_t xr[MT][kQuadDwords];
+    float4 xd[MT];
+    for (int t = t_begin; t < t_end; ++t) {
+        const FlatJob &J = a.job[jj];
+        const int bi = loc / J.tpb;
+        const int row0 = (loc - bi * J.tpb) * J.R;
+        const int rows = min(J.R, J.n - row0);
+        const int Q = J.nb >> 2;
+        const int live = rows * Q;
+        const int c = lane % Q;
+        const int M = J.m;
+
+        int jn = jj, ln = loc + 1;
+        if (ln == J.batch * J.tpb) {
+            jn = jj + 1;
+            ln = 0;
+        }
+        uint32_t wq[kQuadDwords];
+        tile_to_quad(stage, g, lane, live, wq);
+        if (t + 1 < t_end) issue(jn, ln);
+
+        if (jj != jx || bi != bx) {
+            const uint8_t *X = J.x + (int64_t)bi * J.x_bstride + kQuadBytes * c;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < M) load_x_quad(X + (int64_t)m * J.x_rstride, J.x_al8 != 0, xr[m], xd[m]);
+            jx = jj;
+            bx = bi;
+        }
+
+        float dw0, dw1, dw2, dw3;
+        quad_scales(wq, dw0, dw1, dw2, dw3);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < M) {
+                int sb[4];
+                const float acc = quad_dot(wq, xr[m], dw0, dw1, dw2, dw3, xd[m], sb);
+                red[m * kWave + lane] = (lane < live) ? acc : 0.0f;
+                if (SUMS && lane < live) {
+                    int32_t *o = J.sums + ((int64_t)m * J.n + row0 + lane / Q) * J.nb + 4 * c;
+                    o[0] = sb[0]; o[1] = sb[1]; o[2] = sb[2]; o[3] = sb[3];
+                }
+            }
+        }
+        wave_lds_sync();
+        float *Y = J.y + (int64_t)bi * J.y_bstride;
+        for (int i = lane; i < rows * M; i += kWave) {
+            const int m = i / rows;
+            const int r = i - m * rows;
+            const float *pr = red + m * kWave + r * Q;
+            float acc = pr[0];
+            for (int cc = 1; cc < Q; ++cc) acc += pr[cc];
+            Y[(int64_t)m * J.y_rstride + row0 + r] = acc;
+        }
+        wave_lds_sync();
+        jj = jn;
+        loc = ln;
     }
 }
 
@@ -239,6 +396,80 @@ static int launch_fast_mt(const StreamArgs &a, int grid, size_t lds, hipStream_t
 {
     hipLaunchKernelGGL((stream_kernel<MT, SUMS>), dim3(grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+struct DevInfo {
+    int cus = 0;
+    int flat_waves_per_cu[3] = {0, 0, 0};   // index: MT (1, 2)
+};
+static DevInfo g_dev;
+
+template <int MT, bool SUMS>
+static int flat_resident_per_cu()
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_flat_kernel<MT, SUMS>, kWave, 0) !=
+            hipSuccess || blocks <= 0)
+        blocks = 8;
+    return blocks;
+}
+
+template <int MT, bool SUMS>
+static int launch_flat_mt(const StreamDesc *d, int n, hipStream_t stream)
+{
+    if (g_dev.cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        g_dev.cus = v;
+    }
+    static int per_cu = 0;
+    if (per_cu == 0) per_cu = flat_resident_per_cu<MT, SUMS>();
+    FlatArgs a;
+    memset(&a, 0, sizeof(a));
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        FlatJob &J = a.job[i];
+        const int64_t Q = d[i].nb / 4;
+        const int64_t R = 64 / Q;
+        const int64_t tpb = (d[i].n + R - 1) / R;
+        J.w = d[i].w; J.x = d[i].x; J.y = d[i].y; J.sums = d[i].sums;
+        J.w_bstride = d[i].w_bstride; J.x_bstride = d[i].x_bstride; J.y_bstride = d[i].y_bstride;
+        J.x_rstride = (int32_t)d[i].x_rstride; J.y_rstride = (int32_t)d[i].y_rstride;
+        J.n = (int32_t)d[i].n; J.nb = (int32_t)d[i].nb; J.m = (int32_t)d[i].m;
+        J.batch = (int32_t)d[i].batch;
+        J.R = (int32_t)R;
+        J.tpb = (int32_t)tpb;
+        J.tile0 = (int32_t)total;
+        J.x_al8 = (((uintptr_t)d[i].x) % 8 == 0 && d[i].x_rstride % 8 == 0 &&
+                   d[i].x_bstride % 8 == 0) ? 1 : 0;
+        total += d[i].batch * tpb;
+    }
+    if (total > 0x7fffffff) return -4;
+    const int64_t waves = (int64_t)g_dev.cus * per_cu;
+    int64_t tpw = (total + waves - 1) / waves;
+    if (tpw < 1) tpw = 1;
+    a.n_jobs = n;
+    a.total_tiles = (int32_t)total;
+    a.tiles_per_wave = (int32_t)tpw;
+    const int64_t grid = (total + tpw - 1) / tpw;
+    hipLaunchKernelGGL((stream_flat_kernel<MT, SUMS>), dim3((unsigned)grid), dim3(kWave), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+static int launch_flat(const StreamDesc *d, int n, hipStream_t stream)
+{
+    int mmax = 1;
+    bool sums = false;
+    for (int i = 0; i < n; ++i) {
+        if (d[i].m > mmax) mmax = (int)d[i].m;
+        if (d[i].sums) sums = true;
+    }
+    if (sums) return mmax == 1 ? launch_flat_mt<1, true>(d, n, stream)
+                               : launch_flat_mt<2, true>(d, n, stream);
+    return mmax == 1 ? launch_flat_mt<1, false>(d, n, stream) : launch_flat_mt<2, false>(d, n, stream);
 }
 
 static int launch_fast(const StreamDesc *d, int n, hipStream_t stream)
@@ -327,6 +558,10 @@ int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
         }
     }
     if (nf == 0) return 0;
+    int mmax = 1;
+    for (int i = 0; i < nf; ++i)
+        if (fast[i].m > mmax) mmax = (int)fast[i].m;
+    if (mmax <= 2) return launch_flat(fast, nf, stream);
     return launch_fast(fast, nf, stream);
 }
 

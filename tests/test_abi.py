@@ -88,6 +88,7 @@ def test_batched_checks(lib):
     assert call(D(**{**ok, "m": 17})) == Q8_E_UNSUPPORTED
     assert call(D(**{**ok, "m": 2, "x_row_stride": 1})) == Q8_E_SHAPE
     assert call(D(**{**ok, "batch": 2, "w_batch_stride": 3})) == Q8_E_SHAPE
+    assert call(D(**{**ok, "batch": 2, "w_batch_stride": 16, "y_batch_stride": 0})) == Q8_E_SHAPE
     assert call(D(**{**ok, "w": None})) == Q8_E_NULL
     assert call(D(**{**ok, "y": A + 2})) == Q8_E_ALIGN
     assert call(D(**{**ok, "n": 0})) == Q8_OK

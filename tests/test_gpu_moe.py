@@ -40,7 +40,7 @@ def _run(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, tag, ids=None):
     ws = q.moe_workspace(n_tok, n_embd, n_ff, n_expert, n_used, "cuda")
     ws.fill_(0x7F)
     h = nan_like((n_tok, n_used, n_ff))
-    q.moe_up_gate_swiglu(to_gpu(w_ug), to_gpu(xq), to_gpu(ids), n_embd, n_ff, n_expert, ws, h=h)
+    q.moe_up_gate_swiglu(to_gpu(w_ug), to_gpu(xf), to_gpu(ids), n_embd, n_ff, n_expert, ws, h=h)
     assert q.moe_error_word(ws) == 0
     h_gpu = h.cpu().numpy()
     h_ref = orc.moe_up_gate_swiglu(w_ug, xq, ids, n_embd, n_ff, n_expert)
@@ -60,7 +60,12 @@ def _run(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, tag, ids=None):
 
 @pytest.mark.parametrize("n_tok,n_embd,n_ff,n_expert,n_used", [
     (1, 256, 64, 8, 2), (3, 512, 96, 6, 4), (16, 256, 128, 32, 8), (5, 768, 160, 4, 4),
-    (2, 2048, 768, 16, 8), (1, 4096, 256, 4, 1), (7, 256, 32, 1, 1)])
+    (2, 2048, 768, 16, 8), (1, 4096, 256, 4, 1), (7, 256, 32, 1, 1),
+    (1, 256, 256, 8, 8),      # row-major down (8 slots)
+    (2, 512, 512, 8, 8),      # row-major down (16 slots, two per wave)
+    (3, 256, 256, 8, 8),      # expert-major down, several slots per expert
+    (9, 768, 256, 64, 4),     # up_gate with 4 tokens per chunk
+    (40, 256, 256, 4, 2)])    # many slots per expert: several chunks
 def test_moe_small(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
     _run(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, f"moe-{n_tok}-{n_embd}-{n_ff}")
 
@@ -87,29 +92,41 @@ def test_route_exact(q, orc, n_tok, n_used, n_expert):
     _route_check(q, orc, ids, n_expert)
 
 
-def test_invalid_ids_flagged(q, orc):
-    n_tok, n_embd, n_ff, n_expert, n_used = 3, 256, 64, 4, 2
-    w_ug, w_d, xf, _, cw = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used, "moe-bad")
-    ids = np.array([[0, 1], [2, 7], [3, 1]], dtype=np.int32)       # 7 is out of range
+@pytest.mark.parametrize("n_tok,n_embd,n_ff", [
+    (3, 256, 64),      # generic up_gate and down kernels (64/32 = 2 blocks per row)
+    (3, 256, 256),     # fast up_gate, row-major down with the fused combine
+    (10, 512, 256),    # fast up_gate (several tokens per expert), expert-major down
+    (12, 320, 256)])   # generic up_gate (10 blocks per row), expert-major down
+def test_invalid_ids_flagged(q, orc, n_tok, n_embd, n_ff):
+    n_expert, n_used = 4, 2
+    w_ug, w_d, xf, _, cw = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used,
+                                 f"moe-bad-{n_tok}-{n_embd}-{n_ff}")
+    ids = (np.arange(n_tok * n_used).reshape(n_tok, n_used) % n_expert).astype(np.int32)
+    ids[1, 1] = 7                                                  # out of range
     xq = orc.quantize_rows(xf)
     ws = q.moe_workspace(n_tok, n_embd, n_ff, n_expert, n_used, "cuda")
-    h = q.moe_up_gate_swiglu(to_gpu(w_ug), to_gpu(xq), to_gpu(ids), n_embd, n_ff, n_expert, ws)
+    h = q.moe_up_gate_swiglu(to_gpu(w_ug), to_gpu(xf), to_gpu(ids), n_embd, n_ff, n_expert, ws)
     assert q.moe_error_word(ws) == 1
     hh = h.cpu().numpy()
     assert np.all(np.isnan(hh[1, 1]))
-    good = [(0, 0), (0, 1), (1, 0), (2, 0), (2, 1)]
     ref = orc.moe_up_gate_swiglu(w_ug, xq, np.where(ids < n_expert, ids, 0), n_embd, n_ff,
                                  n_expert)
-    for t, u in good:
-        assert rel_l2_rows(hh[t, u][None], ref[t, u][None])[0] <= TOL
+    for t in range(n_tok):
+        for u in range(n_used):
+            if (t, u) != (1, 1):
+                assert rel_l2_rows(hh[t, u][None], ref[t, u][None])[0] <= TOL
     hh[1, 1] = 0.0
     out = q.moe_down_combine(to_gpu(w_d), to_gpu(hh), to_gpu(ids), to_gpu(cw), n_ff, n_embd,
                              n_expert, ws).cpu().numpy()
     assert q.moe_error_word(ws) == 1
-    assert np.all(np.isnan(out[1])) and np.all(np.isfinite(out[[0, 2]]))
+    assert np.all(np.isnan(out[1]))
+    good = [t for t in range(n_tok) if t != 1]
+    assert np.all(np.isfinite(out[good]))
+    ref_out = orc.moe_down_combine(w_d, hh[good], ids[good], cw[good], n_ff, n_embd, n_expert)
+    assert_rows_close(out[good], ref_out)
     c, o, p = q.moe_route(to_gpu(ids), n_expert, ws)
     assert q.moe_error_word(ws) == 1
-    assert int(o.cpu()[-1]) == 5
+    assert int(o.cpu()[-1]) == n_tok * n_used - 1
     # a clean call clears the word again
     q.moe_route(to_gpu(np.zeros((1, 2), np.int32)), n_expert, ws)
     assert q.moe_error_word(ws) == 0
