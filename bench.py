@@ -264,7 +264,17 @@ def run_extra(args, q, synth):
     dev = "cuda"
     wl = args.workload
     res = {"workload": wl, "steps": args.steps, "warmup": args.warmup}
-    if wl in ("c1", "c5b"):
+    if wl == "copy":
+        # calibration for hardware byte counters: a plain device-to-device copy of
+        # a known size (256 MiB read + 256 MiB written per launch)
+        nbytes = 256 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        total = _time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
+        t = total / args.steps
+        res.update(bytes_read_per_launch=nbytes, bytes_written_per_launch=nbytes,
+                   us_per_copy=round(t * 1e6, 2), gbs=round(2 * nbytes / t / 1e9, 1))
+    elif wl in ("c1", "c5b"):
         n, k = (768, 768) if wl == "c1" else (262144, 2048)
         wf = synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w")
         w = q.q8_0_quantize_rows(wf)
@@ -332,7 +342,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b"])
+                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=48)
     ap.add_argument("--traffic", default=None,

@@ -25,9 +25,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, build_dir=BUILD, defines=()):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,17 +41,19 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, lib=LIB, build_dir=BUILD, defines=()):
+    """Compile every source and link `lib`.  `defines` are extra -D options
+    (build-time tuning knobs such as Q8_WEIGHT_CACHE_POLICY)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -10,13 +10,13 @@
 //   out[t]     = sum_u cw[t][u] * (W_d[e] . q(h[t][u]))
 //
 // Design:
-//  * Expert-major gather.  Workgroups are laid out as (active-expert rank,
-//    part); every workgroup scans the ids itself (an LDS bitmap of the active
-//    experts, then a ballot compaction of the slots routed to its expert in
-//    ascending (t,u) order), so no routing kernel and no host sync are needed,
-//    and each active expert's rows are streamed from HBM once per call for all
-//    of its slots.  Workgroups whose rank is past the number of active experts
-//    exit after the scan.
+//  * Expert-major gather.  Workgroups are laid out as (slot, part).  The
+//    workgroup of slot s reads e = ids[s], issues its first weight loads at
+//    once, and with one ballot pass over the ids decides whether s is the first
+//    slot naming e; if so it serves every slot routed to e (ascending (t,u)
+//    order), otherwise it exits.  So no routing kernel and no host sync are
+//    needed, and each active expert's rows are streamed from HBM once per call
+//    for all of its slots.
 //  * The weight tiles go through the same engine as the decode products
 //    (coalesced 16-byte loads -> per-wave LDS slot -> one 4-block quad per
 //    lane, v_dot4 against a masked activation image).
@@ -26,6 +26,8 @@
 //    into the masked image (same rule and code as the activation quantizer),
 //    writes per-slot outputs to the workspace, and a small kernel combines the
 //    n_used slot outputs of each token in ascending u order (deterministic).
+//    For few slots (decode at one or two tokens) a row-major kernel instead
+//    streams a row band of every slot's expert and combines in LDS: one launch.
 //  * Ids outside [0, n_expert) never match an expert; workgroup 0 records them
 //    in the error word of the workspace and writes NaN into what they would
 //    have produced.
@@ -39,10 +41,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kBitmapWords = kMoeMaxExperts / 32;
 
 struct PickShared {
-    uint32_t bitmap[kBitmapWords];
     int invalid;
     int expert;
     int count;
@@ -50,8 +50,8 @@ struct PickShared {
     int slots[kMoeMaxSlots];
 };
 
-// Build the ascending list of slots routed to expert e with wave 0 (ballot
-// compaction in slot order).  Returns the count (valid in wave 0).
+// Build the ascending list of slots routed to expert e with one wave (ballot
+// compaction in slot order).  Returns the count (valid in that wave).
 __device__ int build_slot_list(const int32_t *ids, int n_slots, int e, int *list, int lane)
 {
     int cnt = 0;
@@ -65,42 +65,35 @@ __device__ int build_slot_list(const int32_t *ids, int n_slots, int e, int *list
     return cnt;
 }
 
-// All threads of the workgroup: find the expert of rank `rank` among the
-// active experts (ascending id) and its slot list.  Sets ps.expert (-1 when
-// the rank is past the active count), ps.count and ps.slots, and ps.invalid.
-__device__ void pick_expert(const int32_t *ids, int n_slots, int n_expert, int rank,
-                            PickShared &ps)
+// Workgroup for slot s with expert e = ids[s]: the workgroup owns the expert
+// when e is in range and s is the first slot that names it; it then serves
+// every slot routed to e (listed in ascending (t,u) order).  One ballot pass
+// of wave 0 over the ids finds ownership, the slot list and whether any id is
+// out of range.  Sets ps.expert (-1: nothing to do), ps.count, ps.slots,
+// ps.invalid; ends with a workgroup barrier.
+__device__ void pick_by_slot(const int32_t *ids, int n_slots, int n_expert, int s, int e,
+                             PickShared &ps)
 {
     const int tid = threadIdx.x;
-    for (int i = tid; i < kBitmapWords; i += kThreads) ps.bitmap[i] = 0u;
-    if (tid == 0) ps.invalid = 0;
-    __syncthreads();
-    for (int s = tid; s < n_slots; s += kThreads) {
-        const int e = ids[s];
-        if (e >= 0 && e < n_expert) atomicOr(&ps.bitmap[e >> 5], 1u << (e & 31));
-        else atomicOr(&ps.invalid, 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int e = -1, cum = 0;
-        const int words = (n_expert + 31) >> 5;
-        for (int w = 0; w < words; ++w) {
-            const int c = __popc(ps.bitmap[w]);
-            if (rank < cum + c) {
-                uint32_t bits = ps.bitmap[w];
-                for (int k = 0; k < rank - cum; ++k) bits &= bits - 1u;
-                e = 32 * w + (__ffs(bits) - 1);
-                break;
-            }
-            cum += c;
+    if (tid < kWave) {
+        int cnt = 0;
+        bool first = true, bad = false;
+        for (int base = 0; base < n_slots; base += kWave) {
+            const int i = base + tid;
+            const bool in = i < n_slots;
+            const int v = in ? ids[i] : 0;
+            bad |= __ballot(in && (v < 0 || v >= n_expert)) != 0;
+            const bool hit = in && v == e;
+            const uint64_t m = __ballot(hit);
+            first &= __ballot(hit && i < s) == 0;
+            if (hit) ps.slots[cnt + __popcll(m & __lanemask_lt())] = i;
+            cnt += __popcll(m);
         }
-        ps.expert = e;
-    }
-    __syncthreads();
-    const int e = ps.expert;
-    if (e >= 0 && tid < kWave) {
-        const int cnt = build_slot_list(ids, n_slots, e, ps.slots, tid);
-        if (tid == 0) ps.count = cnt;
+        if (tid == 0) {
+            ps.invalid = bad ? 1 : 0;
+            ps.expert = (e >= 0 && e < n_expert && first) ? e : -1;
+            ps.count = cnt;
+        }
     }
     __syncthreads();
 }
@@ -165,27 +158,12 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
     PickShared &ps = *(PickShared *)(xsc + MT * nb);
     int *rows_of = (int *)(&ps + 1);     // MT token rows of the current chunk
 
-    const int rank = blockIdx.x / p.wgs_per_expert;
-    const int part = blockIdx.x - rank * p.wgs_per_expert;
-    pick_expert(p.ids, p.n_slots, p.n_expert, rank, ps);
-
-    if (blockIdx.x == 0) {
-        if (tid == 0) *p.err = ps.invalid ? 1 : 0;
-        if (ps.invalid) {
-            for (int s = 0; s < p.n_slots; ++s) {
-                const int e = p.ids[s];
-                if (e < 0 || e >= p.n_expert)
-                    for (int j = tid; j < p.n_ff; j += kThreads)
-                        p.h[(int64_t)s * p.n_ff + j] = __builtin_nanf("");
-            }
-        }
-    }
-    const int e = ps.expert;
-    if (e < 0) return;
-    const int count = ps.count;
-
+    const int slot = blockIdx.x / p.wgs_per_expert;
+    const int part = blockIdx.x - slot * p.wgs_per_expert;
+    const int e0 = p.ids[slot];
+    const bool e0_ok = e0 >= 0 && e0 < p.n_expert;
     const int64_t row_bytes = (int64_t)nb * kBlockBytes;
-    const uint8_t *We = p.w + (int64_t)e * 2 * p.n_ff * row_bytes;
+    const uint8_t *We = p.w + (int64_t)(e0_ok ? e0 : 0) * 2 * p.n_ff * row_bytes;
     const int t0 = part * p.tiles_per_wg;
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
@@ -199,13 +177,31 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
         const int rows = min(p.R, p.n_ff - j0);
         tile_issue(We + (int64_t)((up ? p.n_ff : 0) + j0) * row_bytes, rows * nb * 17 / 8, lane, g);
     };
+    // the first half-tile depends only on ids[slot]: issue it before the scan
+    // and the activation round trip (dropped if another slot owns the expert)
+    if (e0_ok && t0 + wave < t1) issue(t0 + wave, false);
+    pick_by_slot(p.ids, p.n_slots, p.n_expert, slot, e0, ps);
+
+    if (blockIdx.x == 0) {
+        if (tid == 0) *p.err = ps.invalid ? 1 : 0;
+        if (ps.invalid) {
+            for (int s = 0; s < p.n_slots; ++s) {
+                const int e = p.ids[s];
+                if (e < 0 || e >= p.n_expert)
+                    for (int j = tid; j < p.n_ff; j += kThreads)
+                        p.h[(int64_t)s * p.n_ff + j] = __builtin_nanf("");
+            }
+        }
+    }
+    if (ps.expert < 0) return;
+    const int count = ps.count;
 
     for (int c0 = 0; c0 < count; c0 += MT) {
         const int mc = min(MT, count - c0);
         __syncthreads();
         if (tid < mc) rows_of[tid] = ps.slots[c0 + tid] / p.n_used;
-        // the first half-tile does not depend on the activations: issue it first
-        if (t0 + wave < t1) issue(t0 + wave, false);
+        // later chunks restart the tile walk: issue its first half-tile now
+        if (c0 > 0 && t0 + wave < t1) issue(t0 + wave, false);
         __syncthreads();
         quantize_rows_to_image(p.x, (int64_t)nb * kQK, rows_of, mc, nb, ximg, xsc);
         __syncthreads();
@@ -291,16 +287,12 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
     float *xsc = (float *)(ximg + MT * img_row);
     PickShared &ps = *(PickShared *)(xsc + MT * nb);
 
-    const int rank = blockIdx.x / p.wgs_per_expert;
-    const int part = blockIdx.x - rank * p.wgs_per_expert;
-    pick_expert(p.ids, p.n_slots, p.n_expert, rank, ps);
-    if (blockIdx.x == 0 && tid == 0) *p.err = ps.invalid ? 1 : 0;
-    const int e = ps.expert;
-    if (e < 0) return;
-    const int count = ps.count;
-
+    const int slot = blockIdx.x / p.wgs_per_expert;
+    const int part = blockIdx.x - slot * p.wgs_per_expert;
+    const int e0 = p.ids[slot];
+    const bool e0_ok = e0 >= 0 && e0 < p.n_expert;
     const int64_t row_bytes = (int64_t)nb * kBlockBytes;
-    const uint8_t *We = p.w + (int64_t)e * p.n_rows * row_bytes;
+    const uint8_t *We = p.w + (int64_t)(e0_ok ? e0 : 0) * p.n_rows * row_bytes;
     const int t0 = part * p.tiles_per_wg;
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
@@ -310,11 +302,17 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
         const int r0 = tt * p.R;
         tile_issue(We + (int64_t)r0 * row_bytes, min(p.R, p.n_rows - r0) * nb * 17 / 8, lane, g);
     };
+    // depends only on ids[slot]: issue before the scan and the h round trip
+    if (e0_ok && t0 + wave < t1) issue(t0 + wave);
+    pick_by_slot(p.ids, p.n_slots, p.n_expert, slot, e0, ps);
+    if (blockIdx.x == 0 && tid == 0) *p.err = ps.invalid ? 1 : 0;
+    if (ps.expert < 0) return;
+    const int count = ps.count;
 
     for (int c0 = 0; c0 < count; c0 += MT) {
         const int mc = min(MT, count - c0);
         int t = t0 + wave;
-        if (t < t1) issue(t);        // independent of h: overlap with the h loads
+        if (c0 > 0 && t < t1) issue(t);
         __syncthreads();
         // quantize the h rows of this chunk's slots into the masked image
         quantize_rows_to_image(p.h, p.n_ff, ps.slots + c0, mc, nb, ximg, xsc);
@@ -410,6 +408,17 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
     const int c = lane % Q;
     const int64_t row_bytes = (int64_t)nb * kBlockBytes;
 
+    u32x4 g[kTileLoads];
+    auto issue_e = [&](int e) {
+        const uint8_t *base = p.w + ((int64_t)e * p.n_rows + row0) * row_bytes;
+        tile_issue(base, rows * nb * 17 / 8, lane, g);
+    };
+    // this wave's first slot's weights depend only on its id: issue them before
+    // anything else
+    const int e_first = wave < p.n_slots ? p.ids[wave] : -1;
+    const bool first_ok = e_first >= 0 && e_first < p.n_expert;
+    if (first_ok) issue_e(e_first);
+
     if (tid < p.n_slots) {
         const int e = p.ids[tid];
         s_e[tid] = (e >= 0 && e < p.n_expert) ? e : -1;
@@ -422,17 +431,12 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
         *p.err = bad;
     }
 
-    u32x4 g[kTileLoads];
     auto next_slot = [&](int s) {
         while (s < p.n_slots && s_e[s] < 0) s += kRowWaves;
         return s;
     };
-    auto issue = [&](int s) {
-        const uint8_t *base = p.w + ((int64_t)s_e[s] * p.n_rows + row0) * row_bytes;
-        tile_issue(base, rows * nb * 17 / 8, lane, g);
-    };
     int s = next_slot(wave);
-    if (s < p.n_slots) issue(s);           // weights first: independent of h
+    if (!first_ok && s < p.n_slots) issue_e(s_e[s]);
 
     quantize_rows_to_image(p.h, p.n_ff, s_rows, p.n_slots, nb, ximg, xsc);
     __syncthreads();
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
         uint32_t wq[kQuadDwords];
         tile_to_quad(stage, g, lane, live, wq);
         const int sn = next_slot(s + kRowWaves);
-        if (sn < p.n_slots) issue(sn);
+        if (sn < p.n_slots) issue_e(s_e[sn]);
         float dw0, dw1, dw2, dw3;
         quad_scales(wq, dw0, dw1, dw2, dw3);
         uint32_t xq[kQuadDwords];
@@ -691,7 +695,7 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
     const int64_t active = a.n_expert < p.n_slots ? a.n_expert : p.n_slots;
     p.tiles_per_wg = tiles_per_wg_for(active, p.tiles_per_expert);
     p.wgs_per_expert = (p.tiles_per_expert + p.tiles_per_wg - 1) / p.tiles_per_wg;
-    const int64_t grid = active * p.wgs_per_expert;
+    const int64_t grid = (int64_t)p.n_slots * p.wgs_per_expert;
     if (!fast) {
         const size_t lds = (size_t)nb * kBlockBytes;
         if (lds > (size_t)max_lds_bytes()) return -4;
@@ -753,7 +757,7 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
     const int64_t active = a.n_expert < p.n_slots ? a.n_expert : p.n_slots;
     p.tiles_per_wg = tiles_per_wg_for(active, p.tiles_per_expert);
     p.wgs_per_expert = (p.tiles_per_expert + p.tiles_per_wg - 1) / p.tiles_per_wg;
-    const int64_t grid = active * p.wgs_per_expert;
+    const int64_t grid = (int64_t)p.n_slots * p.wgs_per_expert;
     int rc;
     if (fast && grid > 0x7fffffff) return -4;
     if (!fast) {

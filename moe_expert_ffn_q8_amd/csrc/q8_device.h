@@ -108,7 +108,12 @@ constexpr int kTileLoads = (kStageChunks + kWave - 1) / kWave;   // 9 per lane
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format,
 // no swizzle): loads past num_records return zero instead of faulting.
 constexpr int kBufferWord3 = 0x00020000;
-constexpr int kCacheNT = 2;          // aux bit: non-temporal (streaming) load
+// Cache policy of the weight stream (aux bits of the buffer load): 2 = nt,
+// non-temporal streaming.  A build option so the policy can be measured.
+#ifndef Q8_WEIGHT_CACHE_POLICY
+#define Q8_WEIGHT_CACHE_POLICY 2
+#endif
+constexpr int kCacheNT = Q8_WEIGHT_CACHE_POLICY;
 
 // Issue the coalesced 16-byte loads of one wave-tile into registers, through a
 // raw buffer resource bounded to the tile: chunk i of lane l is load u with
