@@ -278,6 +278,17 @@ __global__ __launch_bounds__(kWave) void stream_flat_kernel(const FlatArgs a)
     int jx = -1, bx = -1;
     uint32_t xr[MT][kQuadDwords];
     float4 xd[MT];
+    {   // the first tile's activations, in flight together with its weights
+        const FlatJob &J = a.job[jj];
+        const int bi = loc / J.tpb;
+        const int c = lane % (J.nb >> 2);
+        const uint8_t *X = J.x + (int64_t)bi * J.x_bstride + kQuadBytes * c;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < J.m) load_x_quad(X + (int64_t)m * J.x_rstride, J.x_al8 != 0, xr[m], xd[m]);
+        jx = jj;
+        bx = bi;
+    }
     for (int t = t_begin; t < t_end; ++t) {
         const FlatJob &J = a.job[jj];
         const int bi = loc / J.tpb;
