@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libq8moe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "stream.hip", "moe.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "stream.hip", "moe.hip", "gemm.hip", "abi.cpp"]
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -68,6 +68,11 @@ static int matmul_impl(const q8_0_block *w, const q8_0_block *x, float *y, int32
     if (!aligned(w, 2) || !aligned(x, 2) || !aligned(y, 4) || (sums && !aligned(sums, 4)))
         return Q8_E_ALIGN;
     const int64_t nb = k / kQK;
+    // many token rows: the matrix-core kernel (weights read once per 128 rows)
+    if (!sums && m > q8::kStreamMaxM && aligned(w, 16) && aligned(x, 16) &&
+        q8::gemm_ok(n, nb, m))
+        return hip_status(q8::launch_gemm((const uint8_t *)w, (const uint8_t *)x, y, n, nb, m, n,
+                                          as_stream(stream)));
     for (int64_t m0 = 0; m0 < m; m0 += q8::kStreamMaxM) {
         const int64_t mc = (m - m0) < q8::kStreamMaxM ? (m - m0) : q8::kStreamMaxM;
         q8::StreamDesc d;

@@ -1,0 +1,236 @@
+// gemm.hip -- the prefill product Y[m][n] = X[m][k] . W[n][k]^T for many token
+// rows, on the gfx950 int8 matrix cores.
+//
+// The arithmetic is the same as the decode engine's (the block dot product of
+// ggml_vec_dot_q8_0_q8_0, on the Gemma-4-on-Xeon page, "GPUなしで13年前のXeon
+// 上でGemma 4 26Bを毎秒5トークンで実行する", section on narrowing down the
+// cause): an exact int32 sum per 32-block, then (d_x * d_w) * s in fp32.  Prompt
+// evaluation is the compute-bound side of the same path (that page reports it
+// separately from decode).
+//
+// v_mfma_i32_32x32x32_i8 has K = 32, exactly one Q8_0 block: one instruction
+// gives the exact int32 block sums of a 32x32 (token x weight-row) tile, and
+// blocks never mix inside an integer sum, so every block's tile is rescaled by
+// its own scales into fp32 accumulators (3 VALU operations per element per
+// block: convert, scale product, fused multiply-add).  That rescale, not the
+// matrix core, bounds this kernel: 48 VALU instructions per lane against one
+// MFMA per 32x32 tile and block.
+//
+// Work decomposition:
+//  * Workgroup = 4 waves, output tile 128 tokens x 128 weight rows; wave
+//    (wm, wn) computes the 64 x 64 quadrant (wm, wn) as 2 x 2 MFMA tiles.
+//  * K is walked in steps of 8 blocks (272 bytes per row, 16-byte aligned when
+//    k/32 is a multiple of 8).  A step of both operands (2 x 128 rows x 272 B)
+//    is loaded with coalesced 16-byte buffer loads (rows past m or n read as
+//    zero), kept in registers while the previous step is computed, then
+//    written to LDS as is; the block scales are unpacked once per step into
+//    fp32 arrays.  Operand fragments are read back with 4-byte LDS reads and
+//    byte-aligned with v_alignbyte where a block's codes start 2 bytes past a
+//    dword.
+//  * Operand layout of the MFMA: lane l supplies row l%32 of its tile and the
+//    16 codes of k-group l/32 (A = tokens, B = weight rows, same byte order, so
+//    the integer sum covers the block's 32 codes once); result register r of
+//    lane l holds token 8*(r/4) + 4*(l/32) + r%4, weight row l%32.
+//  * Workgroups that share a weight tile are placed on the same XCD (its L2).
+#include <string.h>
+
+#include "q8_device.h"
+#include "q8_internal.h"
+
+namespace q8 {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kGThreads = 256;
+constexpr int kBM = 128;                 // tokens per workgroup tile
+constexpr int kBN = 128;                 // weight rows per workgroup tile
+constexpr int kStepBlocks = 8;           // blocks per K step
+constexpr int kStepRowBytes = kStepBlocks * kBlockBytes;    // 272
+constexpr int kStepChunks = kStepRowBytes / 16;             // 17 per row
+constexpr int kStageRows = kBM + kBN;                       // 256
+constexpr int kStageLoads = kStageRows * kStepChunks / kGThreads;   // 17 per thread
+
+static_assert(kStageRows * kStepChunks % kGThreads == 0, "whole loads per thread");
+
+struct GemmArgs {
+    const uint8_t *w;      // [n][nb] blocks
+    const uint8_t *x;      // [m][nb] blocks
+    float *y;              // [m][ldy]
+    int m, n, nb, ldy;
+    int tiles_n, tiles_m;
+};
+
+// 16 code bytes of a block fragment from the staged LDS rows: `off` is 2-byte
+// aligned; the compiler resolves the alignment per unrolled block.
+__device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
+{
+    const uint32_t *p = (const uint32_t *)(row + (off & ~3));
+    if ((off & 3) == 0) return (v4i){(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+    const uint32_t d0 = p[0], d1 = p[1], d2 = p[2], d3 = p[3], d4 = p[4];
+    return (v4i){(int)__builtin_amdgcn_alignbyte(d1, d0, 2), (int)__builtin_amdgcn_alignbyte(d2, d1, 2),
+                 (int)__builtin_amdgcn_alignbyte(d3, d2, 2), (int)__builtin_amdgcn_alignbyte(d4, d3, 2)};
+}
+
+__global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
+{
+    __shared__ __align__(16) uint8_t stage[kStageRows * kStepRowBytes];   // 69632 B
+    __shared__ __align__(16) float sc[kStepBlocks][kStageRows];           // 8192 B
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5;           // k-group of this lane
+    const int li = lane & 31;
+
+    // Tile order: the tiles_m token tiles of one weight tile are consecutive
+    // in `work`, and work is spread so that they share an XCD (workgroups are
+    // dealt to the 8 XCDs round robin by blockIdx.x).
+    const int nwg = a.tiles_n * a.tiles_m;
+    int work = blockIdx.x;
+    {
+        const int per_xcd = (nwg + 7) / 8;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int cand = xcd * per_xcd + slot;
+        // only a bijection when nwg is a multiple of 8; otherwise keep the
+        // plain order
+        if ((nwg & 7) == 0) work = cand;
+    }
+    const int tn = work / a.tiles_m;
+    const int tm = work - tn * a.tiles_m;
+    const int m0 = tm * kBM, n0 = tn * kBN;
+
+    const int64_t row_bytes = (int64_t)a.nb * kBlockBytes;
+    const int steps = a.nb / kStepBlocks;
+
+    // Buffer resources over the whole operand rows of this tile: rows past m
+    // or n fall outside num_records and read as zero.
+    const int xr_rows = min(kBM, a.m - m0), wr_rows = min(kBN, a.n - n0);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.x + (int64_t)m0 * row_bytes), 0, (int)(xr_rows * row_bytes), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.w + (int64_t)n0 * row_bytes), 0, (int)(wr_rows * row_bytes), kBufferWord3);
+
+    // flat chunk f = tid + 256*u over [0, 256 rows x 17 chunks): rows 0..127
+    // are tokens, 128..255 weight rows
+    u32x4 g[kStageLoads];
+    auto issue = [&](int st) {
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int f = tid + kGThreads * u;
+            const int r = f / kStepChunks;
+            const int c = f - r * kStepChunks;
+            const int off = (int)((r & (kBM - 1)) * row_bytes) + st * kStepRowBytes + 16 * c;
+            g[u] = r < kBM ? __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0)
+                           : __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kCacheNT);
+        }
+    };
+
+    float acc[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    issue(0);
+    for (int st = 0; st < steps; ++st) {
+        __syncthreads();                       // previous step's readers are done
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int f = tid + kGThreads * u;
+            const int r = f / kStepChunks;
+            const int c = f - r * kStepChunks;
+            *(u32x4 *)(stage + r * kStepRowBytes + 16 * c) = g[u];
+        }
+        __syncthreads();
+        if (st + 1 < steps) issue(st + 1);
+        // unpack the step's block scales: sc[block][row]
+#pragma unroll
+        for (int i = 0; i < kStepBlocks * kStageRows / kGThreads; ++i) {
+            const int e = tid + kGThreads * i;
+            const int r = e & (kStageRows - 1);
+            const int b = e >> 8;
+            sc[b][r] = half_bits_to_float(*(const uint16_t *)(stage + r * kStepRowBytes + b * kBlockBytes));
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int b = 0; b < kStepBlocks; ++b) {
+            const int off = b * kBlockBytes + 2 + 16 * h;
+            v4i A[2], B[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                A[i] = lds_codes16(stage + (64 * wm + 32 * i + li) * kStepRowBytes, off);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                B[j] = lds_codes16(stage + (kBM + 64 * wn + 32 * j + li) * kStepRowBytes, off);
+            float dw[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dw[j] = sc[b][kBM + 64 * wn + 32 * j + li];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                float dx[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *(const float4 *)&sc[b][64 * wm + 32 * i + 8 * q + 4 * h];
+                    dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    v16i s = {0};
+                    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], s, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] = fmaf(dx[r] * dw[j], (float)s[r], acc[i][j][r]);
+                }
+            }
+        }
+    }
+
+    // store: token m0 + 64wm + 32i + 8(r/4) + 4h + r%4, weight row n0 + 64wn + 32j + li
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + 64 * wn + 32 * j + li;
+            if (n >= a.n) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < a.m) a.y[(int64_t)m * a.ldy + n] = acc[i][j][r];
+            }
+        }
+}
+
+}  // namespace
+
+bool gemm_ok(int64_t n, int64_t nb, int64_t m)
+{
+    if (nb % kStepBlocks != 0) return false;
+    // buffer-resource ranges are 32-bit: a tile's rows must fit
+    const int64_t row_bytes = nb * kBlockBytes;
+    if (row_bytes * kBM > 0x7fffffffLL) return false;
+    if (n > 0x7fffffffLL || m > 0x7fffffffLL) return false;
+    return true;
+}
+
+int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t nb, int64_t m,
+                int64_t ldy, hipStream_t stream)
+{
+    GemmArgs a;
+    a.w = w; a.x = x; a.y = y;
+    a.m = (int)m; a.n = (int)n; a.nb = (int)nb; a.ldy = (int)ldy;
+    a.tiles_n = (int)((n + kBN - 1) / kBN);
+    a.tiles_m = (int)((m + kBM - 1) / kBM);
+    const int64_t grid = (int64_t)a.tiles_n * a.tiles_m;
+    if (grid > 0x7fffffff) return -4;
+    hipLaunchKernelGGL(gemm_q8_kernel, dim3((unsigned)grid), dim3(kGThreads), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // namespace q8

@@ -36,6 +36,11 @@ int launch_stream(const StreamDesc *d, int n, hipStream_t stream);
 int launch_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_rows,
                          int64_t k, hipStream_t stream);
 
+// Prefill product on the int8 matrix cores (m token rows, any m >= 1).
+bool gemm_ok(int64_t n, int64_t nb, int64_t m);
+int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t nb, int64_t m,
+                int64_t ldy, hipStream_t stream);
+
 // Largest dynamic LDS a workgroup may use on the current device.
 int max_lds_bytes();
 

@@ -144,3 +144,44 @@ def test_c5b_vocab_projection_full_size(q, orc):
     assert np.all(np.isfinite(yy))
     assert_rows_close(yy[rows][None, :], ref)
     del wf
+
+
+@pytest.mark.parametrize("m,n,k", [(17, 70, 768), (128, 128, 256), (129, 257, 512),
+                                   (200, 300, 2048), (512, 96, 4096), (33, 1000, 768),
+                                   (256, 40, 3072)])
+def test_prefill_gemm_shapes(q, orc, m, n, k):
+    """The matrix-core path (m > 16): ragged m and n on both sides of the
+    128 x 128 tile, every K step size the library uses."""
+    w = weights_q8(orc, n, k, "gemm", m, n, k)
+    x = acts_q8(orc, m, k, "gemm-x", m, n, k)
+    ref = orc.matmul(w, x, n, k, m)
+    y = nan_like((m, n))
+    q.q8_0_matmul(to_gpu(w), to_gpu(x), n, k, m, y=y)
+    yy = y.cpu().numpy()
+    assert_rows_close(yy, ref)
+    y2 = q.q8_0_matmul(to_gpu(w), to_gpu(x), n, k, m)
+    assert np.array_equal(yy.view(np.uint32), y2.cpu().numpy().view(np.uint32))
+
+
+def test_c5a_prefill_full_size(q, orc):
+    """512 tokens x K=4096 against 14336 x 4096 weights: the full prefill
+    product; the oracle checks 96 sampled weight rows for all 512 tokens (and
+    the first and last rows)."""
+    import torch
+    import synth
+    m, n, k = 512, 14336, 4096
+    wf = synth.normal_f32_torch((n, k), 0.02, "cuda", 0, "c5a", "w")
+    wq = q.q8_0_quantize_rows(wf)
+    xf = synth.normal_f32((m, k), 1.0, 0, "c5a", "x")
+    xq = orc.quantize_rows(xf)
+    y = nan_like((m, n))
+    q.q8_0_matmul(wq, to_gpu(xq), n, k, m, y=y)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, n - 1],
+                                     np.random.default_rng(5).integers(0, n, 96)]))
+    rows_t = torch.from_numpy(rows).cuda()
+    w_rows = orc.quantize_rows(wf[rows_t].cpu().numpy())
+    assert np.array_equal(wq[rows_t].cpu().numpy(), w_rows)
+    ref = orc.matmul(w_rows, xq, rows.size, k, m)
+    yy = y.cpu().numpy()
+    assert np.all(np.isfinite(yy))
+    assert_rows_close(yy[:, rows], ref)
