@@ -20,7 +20,10 @@ ARCH = "gfx950"
 
 SOURCES = ["quantize.hip", "stream.hip", "moe.hip", "gemm.hip", "abi.cpp"]
 
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# no packed fp32 instructions in device code; MFMA results in VGPRs (the
+# rescale of each int32 block tile then needs no accumulator-register copies)
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
 

@@ -11,20 +11,23 @@
 // v_mfma_i32_32x32x32_i8 has K = 32, exactly one Q8_0 block: one instruction
 // gives the exact int32 block sums of a 32x32 (token x weight-row) tile, and
 // blocks never mix inside an integer sum, so every block's tile is rescaled by
-// its own scales into fp32 accumulators (3 VALU operations per element per
-// block: convert, scale product, fused multiply-add).  That rescale, not the
-// matrix core, bounds this kernel: 48 VALU instructions per lane against one
-// MFMA per 32x32 tile and block.
+// its own scales into fp32 accumulators: per element and block a convert, a
+// scale product and a fused multiply-add on the VALU (3 operations against
+// 1/16 of an MFMA per lane), and that rescale, not the int8 matrix core,
+// bounds this kernel.  (Build option Q8_GEMM_OUTER=1 forms the rank-1 scale
+// products of a block as an outer product on the fp32 matrix core instead,
+// same register layout, leaving 2 VALU operations; with this compiler's
+// schedule it measured slower, so it is off.)
 //
 // Work decomposition:
 //  * Workgroup = 4 waves, output tile 128 tokens x 128 weight rows; wave
 //    (wm, wn) computes the 64 x 64 quadrant (wm, wn) as 2 x 2 MFMA tiles.
-//  * K is walked in steps of 8 blocks (272 bytes per row, 16-byte aligned when
-//    k/32 is a multiple of 8).  A step of both operands (2 x 128 rows x 272 B)
-//    is loaded with coalesced 16-byte buffer loads (rows past m or n read as
-//    zero), kept in registers while the previous step is computed, then
-//    written to LDS as is; the block scales are unpacked once per step into
-//    fp32 arrays.  Operand fragments are read back with 4-byte LDS reads and
+//  * K is walked in steps of 4 blocks (136 bytes per row).  A step of both
+//    operands (2 x 128 rows)
+//    goes straight from HBM to LDS with coalesced 16-byte buffer loads in LDS
+//    DMA mode (rows past m or n read as zero), double-buffered so the next
+//    step streams in while the current one is computed; the block scales are
+//    unpacked once per step into fp32 arrays.  Operand fragments are read back with 4-byte LDS reads and
 //    byte-aligned with v_alignbyte where a block's codes start 2 bytes past a
 //    dword.
 //  * Operand layout of the MFMA: lane l supplies row l%32 of its tile and the
@@ -43,15 +46,30 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kGThreads = 256;
 constexpr int kBM = 128;                 // tokens per workgroup tile
 constexpr int kBN = 128;                 // weight rows per workgroup tile
-constexpr int kStepBlocks = 8;           // blocks per K step
-constexpr int kStepRowBytes = kStepBlocks * kBlockBytes;    // 272
-constexpr int kStepChunks = kStepRowBytes / 16;             // 17 per row
+#ifndef Q8_GEMM_STEP_BLOCKS
+#define Q8_GEMM_STEP_BLOCKS 4
+#endif
+#ifndef Q8_GEMM_STAGE_BUFS
+#define Q8_GEMM_STAGE_BUFS 2
+#endif
+constexpr int kStepBlocks = Q8_GEMM_STEP_BLOCKS;           // blocks per K step (4 or 8)
+constexpr int kStepRowBytes = kStepBlocks * kBlockBytes;    // 136 or 272 bytes of a row
+constexpr int kStepChunks = (kStepRowBytes + 15) / 16;      // 9 or 17 16-byte chunks
+constexpr int kRowStride = 16 * kStepChunks;                // staged row: 144 or 272 B
 constexpr int kStageRows = kBM + kBN;                       // 256
-constexpr int kStageLoads = kStageRows * kStepChunks / kGThreads;   // 17 per thread
+constexpr int kStageLoads = kStageRows * kStepChunks / kGThreads;   // 9 or 17 per thread
+constexpr int kStageBufs = Q8_GEMM_STAGE_BUFS;
+#ifndef Q8_GEMM_OUTER
+#define Q8_GEMM_OUTER 0          // scale products on the fp32 matrix core (1) or the VALU (0)
+#endif
+static_assert(kStepBlocks == 4 || kStepBlocks == 8, "K step of 4 or 8 blocks");
+// the token/weight row boundary falls on a wave boundary of the load pattern
+static_assert((kBM * kStepChunks) % 64 == 0, "uniform buffer resource per load");
 
 static_assert(kStageRows * kStepChunks % kGThreads == 0, "whole loads per thread");
 
@@ -76,8 +94,10 @@ __device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
 
 __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
 {
-    __shared__ __align__(16) uint8_t stage[kStageRows * kStepRowBytes];   // 69632 B
-    __shared__ __align__(16) float sc[kStepBlocks][kStageRows];           // 8192 B
+    // K-step buffers in LDS (kStageBufs: 1 = two workgroups per CU hide each
+    // other's loads; 2 = step st+1 streams in while st is computed)
+    __shared__ __align__(16) uint8_t stage[kStageBufs][kStageRows * kRowStride];
+    __shared__ __align__(16) float sc[kStepBlocks][kStageRows];              // 8192 B
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -91,14 +111,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
     // dealt to the 8 XCDs round robin by blockIdx.x).
     const int nwg = a.tiles_n * a.tiles_m;
     int work = blockIdx.x;
-    {
-        const int per_xcd = (nwg + 7) / 8;
-        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        const int cand = xcd * per_xcd + slot;
-        // only a bijection when nwg is a multiple of 8; otherwise keep the
-        // plain order
-        if ((nwg & 7) == 0) work = cand;
-    }
+    if ((nwg & 7) == 0) work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
     const int tn = work / a.tiles_m;
     const int tm = work - tn * a.tiles_m;
     const int m0 = tm * kBM, n0 = tn * kBN;
@@ -106,26 +119,35 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
     const int64_t row_bytes = (int64_t)a.nb * kBlockBytes;
     const int steps = a.nb / kStepBlocks;
 
-    // Buffer resources over the whole operand rows of this tile: rows past m
-    // or n fall outside num_records and read as zero.
+    // Buffer resources over the operand rows of this tile: rows past m or n
+    // fall outside num_records and read as zero.
     const int xr_rows = min(kBM, a.m - m0), wr_rows = min(kBN, a.n - n0);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.x + (int64_t)m0 * row_bytes), 0, (int)(xr_rows * row_bytes), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.w + (int64_t)n0 * row_bytes), 0, (int)(wr_rows * row_bytes), kBufferWord3);
 
-    // flat chunk f = tid + 256*u over [0, 256 rows x 17 chunks): rows 0..127
-    // are tokens, 128..255 weight rows
-    u32x4 g[kStageLoads];
-    auto issue = [&](int st) {
+    // Chunk f = 64*wave + lane + 256*u of a step (row f/C, 16-byte chunk f%C
+    // with C = kStepChunks; rows 0..127 tokens, 128..255 weight rows) lands at
+    // LDS byte 16*f of the step buffer, because a staged row is 16*C bytes.
+    // That is the LDS DMA pattern (64 lanes -> 1 KB contiguous per
+    // instruction), and a (u, wave) pair never straddles the token/weight
+    // boundary, so its buffer resource is uniform.  With 4-block steps a row's
+    // 136 bytes are fetched as 9 chunks (8 bytes past the step, read but not
+    // used; past the operand they read as zero).
+    auto issue = [&](int st, int buf) {
 #pragma unroll
         for (int u = 0; u < kStageLoads; ++u) {
-            const int f = tid + kGThreads * u;
+            const int f = 64 * wave + lane + kGThreads * u;
             const int r = f / kStepChunks;
             const int c = f - r * kStepChunks;
             const int off = (int)((r & (kBM - 1)) * row_bytes) + st * kStepRowBytes + 16 * c;
-            g[u] = r < kBM ? __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0)
-                           : __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kCacheNT);
+            auto *dst = (__attribute__((address_space(3))) void *)(
+                &stage[buf][16 * (64 * wave + kGThreads * u)]);
+            if (kGThreads * u + 64 * wave < kBM * kStepChunks)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, off, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off, 0, 0, kCacheNT);
         }
     };
 
@@ -137,58 +159,75 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    issue(0);
+    issue(0, 0);
     for (int st = 0; st < steps; ++st) {
-        __syncthreads();                       // previous step's readers are done
-#pragma unroll
-        for (int u = 0; u < kStageLoads; ++u) {
-            const int f = tid + kGThreads * u;
-            const int r = f / kStepChunks;
-            const int c = f - r * kStepChunks;
-            *(u32x4 *)(stage + r * kStepRowBytes + 16 * c) = g[u];
-        }
-        __syncthreads();
-        if (st + 1 < steps) issue(st + 1);
-        // unpack the step's block scales: sc[block][row]
+        const int buf = kStageBufs == 2 ? (st & 1) : 0;
+        __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's DMA for st landed
+        __syncthreads();                       // ... and every wave's; st-1 fully consumed
+        if (kStageBufs == 2 && st + 1 < steps) issue(st + 1, buf ^ 1);
+        const uint8_t *sb = stage[buf];
 #pragma unroll
         for (int i = 0; i < kStepBlocks * kStageRows / kGThreads; ++i) {
             const int e = tid + kGThreads * i;
             const int r = e & (kStageRows - 1);
             const int b = e >> 8;
-            sc[b][r] = half_bits_to_float(*(const uint16_t *)(stage + r * kStepRowBytes + b * kBlockBytes));
+            sc[b][r] = half_bits_to_float(*(const uint16_t *)(sb + r * kRowStride + b * kBlockBytes));
         }
         __syncthreads();
 
-#pragma unroll
+#ifndef Q8_GEMM_UNROLL
+#define Q8_GEMM_UNROLL 4
+#endif
+#pragma unroll Q8_GEMM_UNROLL
         for (int b = 0; b < kStepBlocks; ++b) {
             const int off = b * kBlockBytes + 2 + 16 * h;
             v4i A[2], B[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                A[i] = lds_codes16(stage + (64 * wm + 32 * i + li) * kStepRowBytes, off);
+                A[i] = lds_codes16(sb + (64 * wm + 32 * i + li) * kRowStride, off);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                B[j] = lds_codes16(stage + (kBM + 64 * wn + 32 * j + li) * kStepRowBytes, off);
-            float dw[2];
+                B[j] = lds_codes16(sb + (kBM + 64 * wn + 32 * j + li) * kRowStride, off);
+            // Scale products of the block as outer products on the fp32 matrix
+            // core: P(i,j) = dx_i (x) dw_j with k = 2 and the second k row zero,
+            // so P lands in the same 32x32 register layout as the int32 tile
+            // (exact: a product of two binary16 values fits fp32).
+            float adx[2], bdw[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) dw[j] = sc[b][kBM + 64 * wn + 32 * j + li];
+            for (int i = 0; i < 2; ++i) adx[i] = h == 0 ? sc[b][64 * wm + 32 * i + li] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bdw[j] = sc[b][kBM + 64 * wn + 32 * j + li];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 float dx[16];
+                if (!Q8_GEMM_OUTER) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *(const float4 *)&sc[b][64 * wm + 32 * i + 8 * q + 4 * h];
-                    dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = *(const float4 *)&sc[b][64 * wm + 32 * i + 8 * q + 4 * h];
+                        dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     v16i s = {0};
                     s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], s, 0, 0, 0);
+                    if (Q8_GEMM_OUTER) {
+                        v16f pz = {0.f};
+                        const v16f P = __builtin_amdgcn_mfma_f32_32x32x2f32(adx[i], bdw[j], pz, 0, 0, 0);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] = fmaf(dx[r] * dw[j], (float)s[r], acc[i][j][r]);
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] = fmaf(P[r], (float)s[r], acc[i][j][r]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] = fmaf(dx[r] * bdw[j], (float)s[r], acc[i][j][r]);
+                    }
                 }
             }
+        }
+        if (kStageBufs == 1 && st + 1 < steps) {
+            __syncthreads();                   // every wave is done reading the buffer
+            issue(st + 1, 0);
         }
     }
 
@@ -211,7 +250,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
 
 bool gemm_ok(int64_t n, int64_t nb, int64_t m)
 {
-    if (nb % kStepBlocks != 0) return false;
+    if (nb % 8 != 0) return false;
     // buffer-resource ranges are 32-bit: a tile's rows must fit
     const int64_t row_bytes = nb * kBlockBytes;
     if (row_bytes * kBM > 0x7fffffffLL) return false;
