@@ -232,7 +232,7 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
             "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": bytes_step},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tok_s, 1),
-        "roofline": {"bound": "hbm", "kernel": "stream_kernel (decode engine)",
+        "roofline": {"bound": "hbm", "kernel": "stream_flat_kernel (decode engine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(eng * 1e6, 3),
@@ -336,6 +336,59 @@ def run_extra(args, q, synth):
     return res
 
 
+def read_traffic(path):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    kernel sources have changed since the counters were taken."""
+    import hashlib
+    with open(path) as f:
+        t = json.load(f)
+    h = hashlib.sha256()
+    for fn in t["source_files"]:
+        with open(os.path.join(ROOT, fn), "rb") as g:
+            h.update(g.read())
+    return t["bytes_per_launch"] if h.hexdigest()[:16] == t["source_hash"] else None
+
+
+# ---------------------------------------------------------------------------
+# profile summaries (reads a rocprofv3 rocpd database; no GPU needed)
+
+def _short(name, width=72):
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def rocpd_summary(db):
+    """Per-kernel dispatch statistics and per-dispatch PMC counter means."""
+    import collections
+    import sqlite3
+    c = sqlite3.connect(db)
+    out = []
+    kd = collections.defaultdict(list)
+    try:
+        for name, start, end in c.execute("select name, start, end from kernels"):
+            kd[name].append((end - start) / 1e3)
+    except sqlite3.OperationalError:
+        pass
+    if kd:
+        tot = sum(sum(v) for v in kd.values())
+        out.append(f"{'kernel':72s} {'calls':>6s} {'mean_us':>9s} {'min_us':>8s} "
+                   f"{'max_us':>8s} {'total%':>7s}")
+        for k, v in sorted(kd.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{_short(k):72s} {len(v):6d} {sum(v) / len(v):9.3f} {min(v):8.3f} "
+                       f"{max(v):8.3f} {100 * sum(v) / tot:7.2f}")
+    pm = collections.defaultdict(list)
+    try:
+        for name, ctr, val in c.execute("select name, counter_name, counter_value from pmc_events"):
+            pm[(name, ctr)].append(val)
+    except sqlite3.OperationalError:
+        pass
+    if pm:
+        out.append(f"{'kernel':72s} {'counter':>12s} {'dispatches':>10s} {'mean/dispatch':>14s}")
+        for (k, ctr), v in sorted(pm.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{_short(k):72s} {ctr:>12s} {len(v):10d} {sum(v) / len(v):14.1f}")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,7 +400,12 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=48)
     ap.add_argument("--traffic", default=None,
                     help="JSON file with the rocprofv3-derived HBM bytes per launch")
+    ap.add_argument("--rocpd-summary", default=None, metavar="DB",
+                    help="print a kernel / counter summary of a rocprofv3 database and exit")
     args = ap.parse_args()
+    if args.rocpd_summary:
+        print(rocpd_summary(args.rocpd_summary))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -375,10 +433,15 @@ def main():
         print(json.dumps(run_extra(args, q, synth)))
         return
 
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            t = json.load(f)
-        out["roofline"]["traffic"] = t.get("bytes_per_launch")
+    traffic_file = args.traffic or (os.path.join(ROOT, "profiles",
+                                                "stream_flat_kernel_llama110m_decode_step.traffic.json")
+                                    if args.workload == "c2" else None)
+    if traffic_file and os.path.exists(traffic_file):
+        t = read_traffic(traffic_file)
+        out["roofline"]["traffic"] = t
+        out["roofline"]["traffic_source"] = (
+            os.path.relpath(traffic_file, ROOT) if t is not None else
+            "counters taken on older kernel sources: not applicable")
 
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
