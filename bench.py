@@ -232,7 +232,8 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
             "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": bytes_step},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tok_s, 1),
-        "roofline": {"bound": "hbm", "kernel": "stream_flat_kernel (decode engine)",
+        "roofline": {"bound": "hbm", "kernel": ("stream_flat_kernel (decode engine)" if m <= 2 else
+                                                "stream_mfma_kernel (small-batch decode engine)"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(eng * 1e6, 3),

@@ -115,6 +115,23 @@ constexpr int kBufferWord3 = 0x00020000;
 #endif
 constexpr int kCacheNT = Q8_WEIGHT_CACHE_POLICY;
 
+// Values that are the same in every lane of a wave but that the compiler
+// cannot prove so (they derive from threadIdx.x / 64, from LDS or from a
+// ballot): read from the first lane into scalar registers, so that a buffer
+// resource built from them needs no per-lane waterfall loop around each load.
+__device__ __forceinline__ int wave_uniform(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ const uint8_t *wave_uniform(const uint8_t *p)
+{
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const uint8_t *)(((uint64_t)hi << 32) | lo);
+}
+
 // Issue the coalesced 16-byte loads of one wave-tile into registers, through a
 // raw buffer resource bounded to the tile: chunk i of lane l is load u with
 // i = 64u + l, and chunks past the tile read as zero without a predicate (so
@@ -122,8 +139,8 @@ constexpr int kCacheNT = Q8_WEIGHT_CACHE_POLICY;
 __device__ __forceinline__ void tile_issue(const uint8_t *base, int chunks, int lane,
                                            u32x4 (&g)[kTileLoads])
 {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, chunks * 16, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)wave_uniform(base), 0, wave_uniform(chunks) * 16, kBufferWord3);
 #pragma unroll
     for (int u = 0; u < kTileLoads; ++u)
         g[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (u * kWave + lane), 0, kCacheNT);

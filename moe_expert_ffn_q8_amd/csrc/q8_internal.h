@@ -33,6 +33,11 @@ bool stream_fast_ok(const StreamDesc &d);
 // Enqueue descriptors; returns 0 or a negative q8_status.
 int launch_stream(const StreamDesc *d, int n, hipStream_t stream);
 
+// Matrix-core engine for 3 <= m <= 16 (all descriptors on the fast path).
+bool small_m_ok(const StreamDesc *d, int n);
+size_t small_m_lds_bytes(int64_t m, int64_t nb);
+int launch_small_m(const StreamDesc *d, int n, hipStream_t stream);
+
 int launch_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_rows,
                          int64_t k, hipStream_t stream);
 

@@ -573,6 +573,7 @@ int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
     for (int i = 0; i < nf; ++i)
         if (fast[i].m > mmax) mmax = (int)fast[i].m;
     if (mmax <= 2) return launch_flat(fast, nf, stream);
+    if (small_m_ok(fast, nf)) return launch_small_m(fast, nf, stream);
     return launch_fast(fast, nf, stream);
 }
 

@@ -86,6 +86,28 @@ def test_matmul_small_m(q, orc, n, k, m):
         assert np.array_equal(sums.cpu().numpy(), orc.matmul_blocksums(w, x, n, k, m))
 
 
+@pytest.mark.parametrize("m", [3, 8, 13])
+def test_matmul_small_m_unaligned_activations(q, orc, m):
+    """Activation rows that start 2 bytes past a dword boundary (an odd block
+    offset and an odd row stride in blocks): the engine takes them with
+    halfword loads."""
+    import torch
+    n, k = 100, 768
+    nb = k // 32
+    w = weights_q8(orc, n, k, "mu", m)
+    xs = acts_q8(orc, m, k, "mu-x", m)
+    stride = nb + 1
+    xbuf = np.zeros((m * stride + 1, 34), dtype=np.uint8)
+    for r in range(m):
+        xbuf[1 + r * stride: 1 + r * stride + nb] = xs[r].reshape(nb, 34)
+    wg, xg = to_gpu(w), to_gpu(xbuf)
+    y = nan_like((m, n))
+    d = q.make_desc(wg, (xg, 1), y, n, k, m=m, x_row_stride=stride)
+    q.q8_0_matmul_batched([d], wg)
+    torch.cuda.synchronize()
+    assert_rows_close(y.cpu().numpy(), orc.matmul(w, xs, n, k, m))
+
+
 def test_batched_descriptors(q, orc):
     """Several products in one launch: two weight stacks with a batch
     dimension, a strided activation layout, and a single matrix."""
