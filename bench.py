@@ -328,12 +328,30 @@ def run_extra(args, q, synth):
                                      h=d["h"])
                 q.moe_down_combine(d["wd"], d["h"], d["ids"], d["cw"], n_ff, n_embd, E, d["ws"],
                                    out=d["out"])
+        # the same work with the layers grouped: one up_gate and one down
+        # launch per step (the layers' inputs are independent synthetic rows)
+        ug = [dict(w_up_gate=d["wug"], x=d["xf"], ids=d["ids"], h=d["h"], ws=d["ws"])
+              for d in layers]
+        dn = [dict(w_down=d["wd"], h=d["h"], ids=d["ids"], cw=d["cw"], out=d["out"], ws=d["ws"])
+              for d in layers]
+
+        def step_grouped():
+            q.moe_up_gate_swiglu_batched(ug, n_embd, n_ff, E)
+            q.moe_down_combine_batched(dn, n_ff, n_embd, E)
         total = _time_launches(step, args.steps, args.warmup)
+        total_g = _time_launches(step_grouped, args.steps, args.warmup)
         t = total / args.steps
+        tg = total_g / args.steps
         res.update(tokens=n_tok, layers=L, active_weight_bytes=active_bytes,
                    us_per_step=round(t * 1e6, 2), gbs=round(active_bytes / t / 1e9, 1),
                    pct_of_hbm_peak=round(active_bytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
-                   tokens_per_s=round(n_tok / t, 1))
+                   tokens_per_s=round(n_tok / t, 1),
+                   timing="two launches per layer, layer after layer",
+                   grouped={"timing": "all layers in one up_gate and one down launch",
+                            "us_per_step": round(tg * 1e6, 2),
+                            "gbs": round(active_bytes / tg / 1e9, 1),
+                            "pct_of_hbm_peak": round(active_bytes / tg / 1e9 / HBM_PEAK_GBS * 100, 2),
+                            "tokens_per_s": round(n_tok / tg, 1)})
     return res
 
 

@@ -199,6 +199,42 @@ int moe_down_combine(const q8_0_block *w_down, const float *h,
                      int64_t n_expert, int64_t n_used,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Grouped forms: n_desc independent layers (or micro-batches) of the same
+ * shape in one launch per 32 descriptors, each with its own weights, inputs,
+ * outputs and workspace; per layer the results are those of the single-layer
+ * call (same kernels, same bits).  For a layer stack whose layers do not feed
+ * each other within the call, e.g. layers of separate requests, or synthetic
+ * per-layer inputs.  Workspaces of different descriptors must not overlap;
+ * every other rule and limit is that of the single-layer call.  n_desc == 0
+ * does nothing; a descriptor that fails a check fails the whole call before
+ * anything is enqueued. */
+typedef struct {
+    const q8_0_block *w_up_gate;
+    const float *x;
+    const int32_t *ids;
+    float *h;
+    void *ws;
+    size_t ws_bytes;
+} moe_up_gate_desc;
+
+int moe_up_gate_swiglu_batched(const moe_up_gate_desc *descs, int64_t n_desc,
+                               int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                               int64_t n_expert, int64_t n_used, void *stream);
+
+typedef struct {
+    const q8_0_block *w_down;
+    const float *h;
+    const int32_t *ids;
+    const float *cw;
+    float *out;
+    void *ws;
+    size_t ws_bytes;
+} moe_down_desc;
+
+int moe_down_combine_batched(const moe_down_desc *descs, int64_t n_desc,
+                             int64_t n_tok, int64_t n_ff, int64_t n_embd,
+                             int64_t n_expert, int64_t n_used, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Validation exports (same kernels, with an extra output), for testing.
  *

@@ -38,6 +38,16 @@ class Q8MatmulDesc(ctypes.Structure):
                 ("y_row_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class MoeUpGateDesc(ctypes.Structure):
+    _fields_ = [("w_up_gate", _vp), ("x", _vp), ("ids", _vp), ("h", _vp), ("ws", _vp),
+                ("ws_bytes", _size)]
+
+
+class MoeDownDesc(ctypes.Structure):
+    _fields_ = [("w_down", _vp), ("h", _vp), ("ids", _vp), ("cw", _vp), ("out", _vp),
+                ("ws", _vp), ("ws_bytes", _size)]
+
+
 _SIGS = {
     "q8_status_str": (ctypes.c_char_p, [_int]),
     "q8_version": (ctypes.c_char_p, []),
@@ -50,6 +60,10 @@ _SIGS = {
                                   _size, _vp]),
     "moe_down_combine": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                 _size, _vp]),
+    "moe_up_gate_swiglu_batched": (_int, [ctypes.POINTER(MoeUpGateDesc), _i64, _i64, _i64, _i64,
+                                          _i64, _i64, _vp]),
+    "moe_down_combine_batched": (_int, [ctypes.POINTER(MoeDownDesc), _i64, _i64, _i64, _i64, _i64,
+                                        _i64, _vp]),
     "q8_0_matmul_blocksums": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "moe_route": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]),
 }
@@ -223,6 +237,47 @@ def moe_down_combine(w_down, h, ids, cw, n_ff, n_embd, n_expert, ws, out=None):
         _ptr(w_down), _ptr(h), _ptr(ids), _ptr(cw), _ptr(out), n_tok, n_ff, n_embd, n_expert,
         n_used, _ptr(ws), ws.numel(), _stream(ids)))
     return out
+
+
+def moe_up_gate_swiglu_batched(layers, n_embd, n_ff, n_expert):
+    """Grouped up_gate over independent layers of one shape.  layers: list of
+    dicts with w_up_gate, x, ids, h (written), ws; returns the list of h."""
+    if not layers:
+        return []
+    for d in layers:
+        _need(d["w_up_gate"], torch.uint8, "w_up_gate")
+        _need(d["x"], torch.float32, "x")
+        _need(d["ids"], torch.int32, "ids")
+        _need(d["h"], torch.float32, "h")
+        _need(d["ws"], torch.uint8, "ws")
+    n_tok, n_used = layers[0]["ids"].shape
+    arr = (MoeUpGateDesc * len(layers))(*[
+        MoeUpGateDesc(_ptr(d["w_up_gate"]), _ptr(d["x"]), _ptr(d["ids"]), _ptr(d["h"]),
+                      _ptr(d["ws"]), d["ws"].numel()) for d in layers])
+    _check("moe_up_gate_swiglu_batched", _lib.moe_up_gate_swiglu_batched(
+        arr, len(layers), n_tok, n_embd, n_ff, n_expert, n_used, _stream(layers[0]["ids"])))
+    return [d["h"] for d in layers]
+
+
+def moe_down_combine_batched(layers, n_ff, n_embd, n_expert):
+    """Grouped down projection + combine over independent layers of one shape.
+    layers: list of dicts with w_down, h, ids, cw, out (written), ws."""
+    if not layers:
+        return []
+    for d in layers:
+        _need(d["w_down"], torch.uint8, "w_down")
+        _need(d["h"], torch.float32, "h")
+        _need(d["ids"], torch.int32, "ids")
+        _need(d["cw"], torch.float32, "cw")
+        _need(d["out"], torch.float32, "out")
+        _need(d["ws"], torch.uint8, "ws")
+    n_tok, n_used = layers[0]["ids"].shape
+    arr = (MoeDownDesc * len(layers))(*[
+        MoeDownDesc(_ptr(d["w_down"]), _ptr(d["h"]), _ptr(d["ids"]), _ptr(d["cw"]), _ptr(d["out"]),
+                    _ptr(d["ws"]), d["ws"].numel()) for d in layers])
+    _check("moe_down_combine_batched", _lib.moe_down_combine_batched(
+        arr, len(layers), n_tok, n_ff, n_embd, n_expert, n_used, _stream(layers[0]["ids"])))
+    return [d["out"] for d in layers]
 
 
 def moe_route(ids, n_expert, ws):

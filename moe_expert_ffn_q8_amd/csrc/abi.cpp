@@ -7,6 +7,8 @@
 
 #include <string.h>
 
+#include <algorithm>
+
 #include "q8_internal.h"
 #include "q8_moe.h"
 
@@ -170,23 +172,87 @@ size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t 
     return q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
 }
 
+static int check_up_gate_desc(const moe_up_gate_desc &d, int64_t n_tok, int64_t n_embd,
+                              int64_t n_ff, int64_t n_expert, int64_t n_used)
+{
+    if (!d.ws) return Q8_E_WORKSPACE;
+    if (d.ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
+    if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
+    if (n_tok > 0 && (!d.w_up_gate || !d.x || !d.ids || !d.h)) return Q8_E_NULL;
+    if (!aligned(d.w_up_gate, 16) || !aligned(d.x, 16) || !aligned(d.ids, 4) || !aligned(d.h, 4))
+        return Q8_E_ALIGN;
+    return Q8_OK;
+}
+
+static int check_down_desc(const moe_down_desc &d, int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                           int64_t n_expert, int64_t n_used)
+{
+    if (!d.ws) return Q8_E_WORKSPACE;
+    if (d.ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
+    if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
+    if (n_tok > 0 && (!d.w_down || !d.h || !d.ids || !d.cw || !d.out)) return Q8_E_NULL;
+    if (!aligned(d.w_down, 16) || !aligned(d.h, 16) || !aligned(d.ids, 4) || !aligned(d.cw, 4) ||
+        !aligned(d.out, 4))
+        return Q8_E_ALIGN;
+    return Q8_OK;
+}
+
+int moe_up_gate_swiglu_batched(const moe_up_gate_desc *descs, int64_t n_desc, int64_t n_tok,
+                               int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                               void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    for (int64_t i = 0; i < n_desc; ++i)
+        if (int rc = check_up_gate_desc(descs[i], n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    for (int64_t i0 = 0; i0 < n_desc; i0 += q8::kMoeMaxLayers) {
+        q8::MoeUpGateArgs a;
+        a.n_layers = (int)std::min<int64_t>(q8::kMoeMaxLayers, n_desc - i0);
+        for (int l = 0; l < a.n_layers; ++l) {
+            const moe_up_gate_desc &d = descs[i0 + l];
+            a.layer[l] = {(const uint8_t *)d.w_up_gate, d.x, d.ids, d.h, d.ws};
+        }
+        a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
+        a.n_used = n_used;
+        if (int rc = hip_status(q8::launch_moe_up_gate(a, as_stream(stream)))) return rc;
+    }
+    return Q8_OK;
+}
+
 int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const float *x, const int32_t *ids,
                        float *h, int64_t n_tok, int64_t n_embd, int64_t n_ff,
                        int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
                        void *stream)
 {
     if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
-    if (!ws) return Q8_E_WORKSPACE;
-    if (ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
-    if (!aligned(ws, 256)) return Q8_E_ALIGN;
-    if (n_tok > 0 && (!w_up_gate || !x || !ids || !h)) return Q8_E_NULL;
-    if (!aligned(w_up_gate, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(h, 4))
-        return Q8_E_ALIGN;
-    q8::MoeUpGateArgs a;
-    a.w = (const uint8_t *)w_up_gate; a.x = x; a.ids = ids; a.h = h;
-    a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
-    a.n_used = n_used; a.ws = ws;
-    return hip_status(q8::launch_moe_up_gate(a, as_stream(stream)));
+    const moe_up_gate_desc d = {w_up_gate, x, ids, h, ws, ws_bytes};
+    return moe_up_gate_swiglu_batched(&d, 1, n_tok, n_embd, n_ff, n_expert, n_used, stream);
+}
+
+int moe_down_combine_batched(const moe_down_desc *descs, int64_t n_desc, int64_t n_tok,
+                             int64_t n_ff, int64_t n_embd, int64_t n_expert, int64_t n_used,
+                             void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (int rc = moe_check(n_tok, n_ff, n_embd, n_expert, n_used)) return rc;
+    for (int64_t i = 0; i < n_desc; ++i)
+        if (int rc = check_down_desc(descs[i], n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    for (int64_t i0 = 0; i0 < n_desc; i0 += q8::kMoeMaxLayers) {
+        q8::MoeDownArgs a;
+        a.n_layers = (int)std::min<int64_t>(q8::kMoeMaxLayers, n_desc - i0);
+        for (int l = 0; l < a.n_layers; ++l) {
+            const moe_down_desc &d = descs[i0 + l];
+            a.layer[l] = {(const uint8_t *)d.w_down, d.h, d.ids, d.cw, d.out, d.ws};
+        }
+        a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
+        a.n_used = n_used;
+        if (int rc = hip_status(q8::launch_moe_down(a, as_stream(stream)))) return rc;
+    }
+    return Q8_OK;
 }
 
 int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *ids,
@@ -194,18 +260,8 @@ int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *id
                      int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes, void *stream)
 {
     if (int rc = moe_check(n_tok, n_ff, n_embd, n_expert, n_used)) return rc;
-    if (!ws) return Q8_E_WORKSPACE;
-    if (ws_bytes < q8::moe_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_WORKSPACE;
-    if (!aligned(ws, 256)) return Q8_E_ALIGN;
-    if (n_tok > 0 && (!w_down || !h || !ids || !cw || !out)) return Q8_E_NULL;
-    if (!aligned(w_down, 16) || !aligned(h, 16) || !aligned(ids, 4) || !aligned(cw, 4) ||
-        !aligned(out, 4))
-        return Q8_E_ALIGN;
-    q8::MoeDownArgs a;
-    a.w = (const uint8_t *)w_down; a.h = h; a.ids = ids; a.cw = cw; a.out = out;
-    a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert;
-    a.n_used = n_used; a.ws = ws;
-    return hip_status(q8::launch_moe_down(a, as_stream(stream)));
+    const moe_down_desc d = {w_down, h, ids, cw, out, ws, ws_bytes};
+    return moe_down_combine_batched(&d, 1, n_tok, n_ff, n_embd, n_expert, n_used, stream);
 }
 
 int moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *pairs,

@@ -31,6 +31,8 @@
 //  * Ids outside [0, n_expert) never match an expert; workgroup 0 records them
 //    in the error word of the workspace and writes NaN into what they would
 //    have produced.
+#include <string.h>
+
 #include "q8_device.h"
 #include "q8_internal.h"
 #include "q8_moe.h"
@@ -41,6 +43,15 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
+
+// Loads complete in issue order (one counter per wave), so a small load issued
+// after a tile's weight loads can only be used once those weights have
+// arrived.  The kernels below therefore issue their latency-critical small
+// loads (the ids for the ownership scan, activation or h rows) before the
+// weights.
+constexpr int kPickRegs = 4;          // slots 0..255: ids preloaded in registers
+constexpr int kPrePass = 4;           // prefetched row blocks per thread (256 threads)
+constexpr int kDnPrePass = 8;         // the same for the 512-thread down kernel
 
 struct PickShared {
     int invalid;
@@ -65,6 +76,21 @@ __device__ int build_slot_list(const int32_t *ids, int n_slots, int e, int *list
     return cnt;
 }
 
+// The ids of slots 0 .. 64*kPickRegs-1, one per lane of wave 0 (issued
+// before the weight loads).
+struct IdsPre {
+    int v[kPickRegs];
+};
+
+// Every lane loads (from a clamped in-range index, n_slots >= 1): the loads are
+// unconditional, so the wait for them never has to cover later loads.
+__device__ __forceinline__ void preload_ids(const int32_t *ids, int n_slots, IdsPre &ip)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int c = 0; c < kPickRegs; ++c) ip.v[c] = ids[min(c * kWave + lane, n_slots - 1)];
+}
+
 // Workgroup for slot s with expert e = ids[s]: the workgroup owns the expert
 // when e is in range and s is the first slot that names it; it then serves
 // every slot routed to e (listed in ascending (t,u) order).  One ballot pass
@@ -72,22 +98,27 @@ __device__ int build_slot_list(const int32_t *ids, int n_slots, int e, int *list
 // out of range.  Sets ps.expert (-1: nothing to do), ps.count, ps.slots,
 // ps.invalid; ends with a workgroup barrier.
 __device__ void pick_by_slot(const int32_t *ids, int n_slots, int n_expert, int s, int e,
-                             PickShared &ps)
+                             const IdsPre &ip, PickShared &ps)
 {
     const int tid = threadIdx.x;
     if (tid < kWave) {
         int cnt = 0;
         bool first = true, bad = false;
-        for (int base = 0; base < n_slots; base += kWave) {
-            const int i = base + tid;
+        auto step = [&](int i, int v) {
             const bool in = i < n_slots;
-            const int v = in ? ids[i] : 0;
             bad |= __ballot(in && (v < 0 || v >= n_expert)) != 0;
             const bool hit = in && v == e;
             const uint64_t m = __ballot(hit);
             first &= __ballot(hit && i < s) == 0;
             if (hit) ps.slots[cnt + __popcll(m & __lanemask_lt())] = i;
             cnt += __popcll(m);
+        };
+#pragma unroll
+        for (int c = 0; c < kPickRegs; ++c)
+            if (c * kWave < n_slots) step(c * kWave + tid, ip.v[c]);
+        for (int base = kPickRegs * kWave; base < n_slots; base += kWave) {
+            const int i = base + tid;
+            step(i, i < n_slots ? ids[i] : 0);
         }
         if (tid == 0) {
             ps.invalid = bad ? 1 : 0;
@@ -98,40 +129,92 @@ __device__ void pick_by_slot(const int32_t *ids, int n_slots, int n_expert, int 
     __syncthreads();
 }
 
-// Quantize mc fp32 rows (row m starts at base + row_index[m] * row_floats)
-// into the masked image (nb*34 bytes per row, scale bytes zero) plus fp32
-// scales, with the activation quantization rule (same code as the quantizer:
-// the bytes equal q8_0_quantize_rows of those rows).  All threads of the
-// workgroup take part; 8 lanes per block.
+// Quantize one 32-value block held as 4 values by each of 8 lanes into image
+// row m (scale bytes zero) and the fp32 scale array.
+__device__ __forceinline__ void quantize_to_image(float4 v, int m, int b, int nb, uint8_t *ximg,
+                                                  float *xsc)
+{
+    const int li = threadIdx.x & 7;
+    uint32_t codes, dbits;
+    quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+    uint16_t *img16 = (uint16_t *)(ximg + m * nb * kBlockBytes);
+    if (li == 0) {
+        img16[b * 17] = 0;
+        xsc[m * nb + b] = half_bits_to_float(dbits);
+    }
+    img16[b * 17 + 1 + 2 * li] = (uint16_t)(codes & 0xffffu);
+    img16[b * 17 + 2 + 2 * li] = (uint16_t)(codes >> 16);
+}
+
+// Quantize fp32 rows m_begin..mc-1 (row m starts at base + row_index[m] *
+// row_floats) into the masked image (nb*34 bytes per row, scale bytes zero)
+// plus fp32 scales, with the activation quantization rule (same code as the
+// quantizer: the bytes equal q8_0_quantize_rows of those rows).  All threads
+// of the workgroup take part; 8 lanes per block.
 __device__ void quantize_rows_to_image(const float *base, int64_t row_floats, const int *row_index,
-                                       int mc, int nb, uint8_t *ximg, float *xsc)
+                                       int m_begin, int mc, int nb, uint8_t *ximg, float *xsc)
 {
     const int tid = threadIdx.x;
     const int li = tid & 7;
-    const int img_row = nb * kBlockBytes;
     const int step = (int)blockDim.x / 8;
-    for (int bi = tid >> 3; bi < mc * nb; bi += step) {
+    for (int bi = m_begin * nb + (tid >> 3); bi < mc * nb; bi += step) {
         const int m = bi / nb;
         const int b = bi - m * nb;
         const float4 v = *(const float4 *)(base + (int64_t)row_index[m] * row_floats + b * kQK + 4 * li);
-        uint32_t codes, dbits;
-        quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
-        uint16_t *img16 = (uint16_t *)(ximg + m * img_row);
-        if (li == 0) {
-            img16[b * 17] = 0;
-            xsc[m * nb + b] = half_bits_to_float(dbits);
-        }
-        img16[b * 17 + 1 + 2 * li] = (uint16_t)(codes & 0xffffu);
-        img16[b * 17 + 2 + 2 * li] = (uint16_t)(codes >> 16);
+        quantize_to_image(v, m, b, nb, ximg, xsc);
     }
 }
 
-struct UgParams {
+// Two-step form for rows known before the weights are issued: prefetch_rows
+// loads the blocks of rows 0..mc-1 (row m at rows0 + m * row_floats) into
+// registers, quantize_prefetched writes them into image rows m_out+m.  Needs
+// mc * nb <= P * blockDim.x / 8.
+// The loads are unconditional (indices past the rows are clamped to the last
+// block), so that later waits are exact counts.
+template <int P>
+__device__ __forceinline__ void prefetch_rows(const float *rows0, int64_t row_floats, int mc, int nb,
+                                              float4 (&v)[P])
+{
+    const int tid = threadIdx.x;
+    const int step = (int)blockDim.x / 8;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int bi = min((tid >> 3) + i * step, mc * nb - 1);
+        const int m = bi / nb;
+        const int b = bi - m * nb;
+        v[i] = *(const float4 *)(rows0 + (int64_t)m * row_floats + b * kQK + 4 * (tid & 7));
+    }
+}
+
+template <int P>
+__device__ __forceinline__ void quantize_prefetched(const float4 (&v)[P], int mc, int nb, int m_out,
+                                                    uint8_t *ximg, float *xsc)
+{
+    const int step = (int)blockDim.x / 8;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int bi = ((int)threadIdx.x >> 3) + i * step;
+        if (bi < mc * nb) {
+            const int m = bi / nb;
+            quantize_to_image(v[i], m_out + m, bi - m * nb, nb, ximg, xsc);
+        }
+    }
+}
+
+// Per-layer pointers of a launch (up to kMoeMaxLayers independent layers of
+// the same shape in one grid).
+struct UgLayer {
     const uint8_t *w;
     const float *x;        // fp32 [n_tok][n_embd]
     const int32_t *ids;
     float *h;
     int32_t *err;
+};
+
+struct UgParams {
+    UgLayer layer[kMoeMaxLayers];
+    int n_layers;
+    int wgs_per_layer;     // n_slots * wgs_per_expert
     int n_slots, n_used, n_expert, nb, n_ff;
     int R;                 // rows per wave-tile
     int tiles_per_expert;  // ceil(n_ff / R)
@@ -139,12 +222,14 @@ struct UgParams {
     int tiles_per_wg;
 };
 
+static_assert(sizeof(UgParams) <= 4000, "kernel arguments must stay below 4 KB");
+
 template <int MT>
 __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = wave_uniform(tid >> 6);
     const int lane = tid & 63;
     const int nb = p.nb;
     const int Q = nb >> 2;
@@ -158,38 +243,51 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
     PickShared &ps = *(PickShared *)(xsc + MT * nb);
     int *rows_of = (int *)(&ps + 1);     // MT token rows of the current chunk
 
-    const int slot = blockIdx.x / p.wgs_per_expert;
-    const int part = blockIdx.x - slot * p.wgs_per_expert;
-    const int e0 = p.ids[slot];
+    const int li = blockIdx.x / p.wgs_per_layer;
+    const int wl = blockIdx.x - li * p.wgs_per_layer;      // workgroup within the layer
+    const UgLayer &L = p.layer[li];
+    const int slot = wl / p.wgs_per_expert;
+    const int part = wl - slot * p.wgs_per_expert;
+    const int e0 = L.ids[slot];
     const bool e0_ok = e0 >= 0 && e0 < p.n_expert;
     const int64_t row_bytes = (int64_t)nb * kBlockBytes;
-    const uint8_t *We = p.w + (int64_t)(e0_ok ? e0 : 0) * 2 * p.n_ff * row_bytes;
+    const uint8_t *We = L.w + (int64_t)(e0_ok ? e0 : 0) * 2 * p.n_ff * row_bytes;
     const int t0 = part * p.tiles_per_wg;
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
 
-    // The wave walks a sequence of half-tiles (gate rows of tile t, up rows of
-    // tile t, gate rows of tile t+4, ...) with one half-tile of loads in
-    // flight ahead of the one being computed.
-    u32x4 g[kTileLoads];
-    auto issue = [&](int tt, bool up) {
-        const int j0 = tt * p.R;
-        const int rows = min(p.R, p.n_ff - j0);
-        tile_issue(We + (int64_t)((up ? p.n_ff : 0) + j0) * row_bytes, rows * nb * 17 / 8, lane, g);
-    };
-    // the first half-tile depends only on ids[slot]: issue it before the scan
-    // and the activation round trip (dropped if another slot owns the expert)
-    if (e0_ok && t0 + wave < t1) issue(t0 + wave, false);
-    pick_by_slot(p.ids, p.n_slots, p.n_expert, slot, e0, ps);
+    // Small loads first: the ids for the ownership scan and the token row of
+    // this workgroup's own slot (the first row of its first chunk when it owns
+    // the expert).
+    IdsPre ip;
+    preload_ids(L.ids, p.n_slots, ip);
+    const bool x_pre = nb <= kPrePass * (kThreads / 8);
+    float4 xv[kPrePass];
+    prefetch_rows<kPrePass>(L.x + (int64_t)(slot / p.n_used) * nb * kQK, 0, 1, nb, xv);
 
-    if (blockIdx.x == 0) {
-        if (tid == 0) *p.err = ps.invalid ? 1 : 0;
+    // The gate and up rows of a tile are loaded together (two register sets);
+    // the wave's next pair is issued once both are staged.  The first pair
+    // depends only on ids[slot] (dropped if another slot owns the expert).
+    // Issues are unconditional: a tile that does not exist gets a zero-length
+    // buffer (zeros, no memory traffic), so every wait is an exact count.
+    u32x4 gg[kTileLoads], gu[kTileLoads];
+    auto issue = [&](int tt, bool real) {
+        const int j0 = tt * p.R;
+        const int chunks = real ? min(p.R, p.n_ff - j0) * nb * 17 / 8 : 0;
+        tile_issue(We + (int64_t)(real ? j0 : 0) * row_bytes, chunks, lane, gg);
+        tile_issue(We + (int64_t)(real ? p.n_ff + j0 : 0) * row_bytes, chunks, lane, gu);
+    };
+    issue(t0 + wave, e0_ok && t0 + wave < t1);
+    pick_by_slot(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
+
+    if (wl == 0) {
+        if (tid == 0) *L.err = ps.invalid ? 1 : 0;
         if (ps.invalid) {
             for (int s = 0; s < p.n_slots; ++s) {
-                const int e = p.ids[s];
+                const int e = L.ids[s];
                 if (e < 0 || e >= p.n_expert)
                     for (int j = tid; j < p.n_ff; j += kThreads)
-                        p.h[(int64_t)s * p.n_ff + j] = __builtin_nanf("");
+                        L.h[(int64_t)s * p.n_ff + j] = __builtin_nanf("");
             }
         }
     }
@@ -200,10 +298,15 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
         const int mc = min(MT, count - c0);
         __syncthreads();
         if (tid < mc) rows_of[tid] = ps.slots[c0 + tid] / p.n_used;
-        // later chunks restart the tile walk: issue its first half-tile now
-        if (c0 > 0 && t0 + wave < t1) issue(t0 + wave, false);
+        // later chunks restart the tile walk: issue its first pair now
+        if (c0 > 0) issue(t0 + wave, t0 + wave < t1);
         __syncthreads();
-        quantize_rows_to_image(p.x, (int64_t)nb * kQK, rows_of, mc, nb, ximg, xsc);
+        int m_begin = 0;
+        if (c0 == 0 && x_pre) {      // ps.slots[0] is this slot: its row is in registers
+            quantize_prefetched<kPrePass>(xv, 1, nb, 0, ximg, xsc);
+            m_begin = 1;
+        }
+        quantize_rows_to_image(L.x, (int64_t)nb * kQK, rows_of, m_begin, mc, nb, ximg, xsc);
         __syncthreads();
 
         uint32_t xr[kQuadDwords];
@@ -217,12 +320,11 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
             const int j0 = t * p.R;
             const int rows = min(p.R, p.n_ff - j0);
             const int live = rows * Q;
-#pragma unroll 1
+#pragma unroll
             for (int half = 0; half < 2; ++half) {
                 uint32_t wq[kQuadDwords];
-                tile_to_quad(stage, g, lane, live, wq);
-                if (half == 0) issue(t, true);
-                else if (t + kWaves < t1) issue(t + kWaves, false);
+                tile_to_quad(stage, half == 0 ? gg : gu, lane, live, wq);
+                if (half == 1) issue(t + kWaves, t + kWaves < t1);
                 float dw0, dw1, dw2, dw3;
                 quad_scales(wq, dw0, dw1, dw2, dw3);
                 float *red = half == 0 ? redg : redu;
@@ -253,29 +355,37 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
                     us += pu[cc];
                 }
                 const float hv = gs / (1.0f + expf(-gs)) * us;
-                p.h[(int64_t)ps.slots[c0 + m] * p.n_ff + j0 + r] = hv;
+                L.h[(int64_t)ps.slots[c0 + m] * p.n_ff + j0 + r] = hv;
             }
             wave_lds_sync();
         }
     }
 }
 
-struct DnParams {
+struct DnLayer {
     const uint8_t *w;
     const float *h;
     const int32_t *ids;
     float *yslot;        // [n_slots][n_rows]
     int32_t *err;
+};
+
+struct DnParams {
+    DnLayer layer[kMoeMaxLayers];
+    int n_layers;
+    int wgs_per_layer;
     int n_slots, n_used, n_expert, nb, n_ff, n_rows;
     int R, tiles_per_expert, wgs_per_expert, tiles_per_wg;
 };
+
+static_assert(sizeof(DnParams) <= 4000, "kernel arguments must stay below 4 KB");
 
 template <int MT>
 __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = wave_uniform(tid >> 6);
     const int lane = tid & 63;
     const int nb = p.nb;
     const int Q = nb >> 2;
@@ -287,12 +397,15 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
     float *xsc = (float *)(ximg + MT * img_row);
     PickShared &ps = *(PickShared *)(xsc + MT * nb);
 
-    const int slot = blockIdx.x / p.wgs_per_expert;
-    const int part = blockIdx.x - slot * p.wgs_per_expert;
-    const int e0 = p.ids[slot];
+    const int li = blockIdx.x / p.wgs_per_layer;
+    const int wl = blockIdx.x - li * p.wgs_per_layer;      // workgroup within the layer
+    const DnLayer &L = p.layer[li];
+    const int slot = wl / p.wgs_per_expert;
+    const int part = wl - slot * p.wgs_per_expert;
+    const int e0 = L.ids[slot];
     const bool e0_ok = e0 >= 0 && e0 < p.n_expert;
     const int64_t row_bytes = (int64_t)nb * kBlockBytes;
-    const uint8_t *We = p.w + (int64_t)(e0_ok ? e0 : 0) * p.n_rows * row_bytes;
+    const uint8_t *We = L.w + (int64_t)(e0_ok ? e0 : 0) * p.n_rows * row_bytes;
     const int t0 = part * p.tiles_per_wg;
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
@@ -302,10 +415,12 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
         const int r0 = tt * p.R;
         tile_issue(We + (int64_t)r0 * row_bytes, min(p.R, p.n_rows - r0) * nb * 17 / 8, lane, g);
     };
+    IdsPre ip;
+    preload_ids(L.ids, p.n_slots, ip);
     // depends only on ids[slot]: issue before the scan and the h round trip
     if (e0_ok && t0 + wave < t1) issue(t0 + wave);
-    pick_by_slot(p.ids, p.n_slots, p.n_expert, slot, e0, ps);
-    if (blockIdx.x == 0 && tid == 0) *p.err = ps.invalid ? 1 : 0;
+    pick_by_slot(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
+    if (wl == 0 && tid == 0) *L.err = ps.invalid ? 1 : 0;
     if (ps.expert < 0) return;
     const int count = ps.count;
 
@@ -315,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
         if (c0 > 0 && t < t1) issue(t);
         __syncthreads();
         // quantize the h rows of this chunk's slots into the masked image
-        quantize_rows_to_image(p.h, p.n_ff, ps.slots + c0, mc, nb, ximg, xsc);
+        quantize_rows_to_image(L.h, p.n_ff, ps.slots + c0, 0, mc, nb, ximg, xsc);
         __syncthreads();
 
         uint32_t xr[kQuadDwords];
@@ -357,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
                 const float *pr = red + m * kWave + r * Q;
                 float acc = pr[0];
                 for (int cc = 1; cc < Q; ++cc) acc += pr[cc];
-                p.yslot[(int64_t)ps.slots[c0 + m] * p.n_rows + row0 + r] = acc;
+                L.yslot[(int64_t)ps.slots[c0 + m] * p.n_rows + row0 + r] = acc;
             }
             wave_lds_sync();
         }
@@ -375,15 +490,23 @@ constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowsMaxSlots = 16;
 
-struct DrParams {
+struct DrLayer {
     const uint8_t *w;
     const float *h;
     const int32_t *ids;
     const float *cw;
     float *out;
     int32_t *err;
+};
+
+struct DrParams {
+    DrLayer layer[kMoeMaxLayers];
+    int n_layers;
+    int wgs_per_layer;     // ceil(n_rows / R)
     int n_used, n_slots, n_expert, nb, n_ff, n_rows, R;
 };
+
+static_assert(sizeof(DrParams) <= 4000, "kernel arguments must stay below 4 KB");
 
 __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrParams p)
 {
@@ -393,7 +516,7 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
     __shared__ float ys[kRowsMaxSlots][kWave];
     __shared__ float red[kRowWaves][kWave];
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = wave_uniform(tid >> 6);
     const int lane = tid & 63;
     const int nb = p.nb;
     const int Q = nb >> 2;
@@ -402,33 +525,42 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
     uint8_t *ximg = smem + kRowWaves * kStageBytes;
     float *xsc = (float *)(ximg + kRowsMaxSlots * img_row);
 
-    const int row0 = blockIdx.x * p.R;
+    const int li = blockIdx.x / p.wgs_per_layer;
+    const int wl = blockIdx.x - li * p.wgs_per_layer;      // row band within the layer
+    const DrLayer &L = p.layer[li];
+    const int row0 = wl * p.R;
     const int rows = min(p.R, p.n_rows - row0);
     const int live = rows * Q;
     const int c = lane % Q;
     const int64_t row_bytes = (int64_t)nb * kBlockBytes;
 
     u32x4 g[kTileLoads];
+    // e < 0: a zero-length buffer (zeros, no memory traffic), so that the
+    // issue is unconditional and later waits are exact counts
     auto issue_e = [&](int e) {
-        const uint8_t *base = p.w + ((int64_t)e * p.n_rows + row0) * row_bytes;
-        tile_issue(base, rows * nb * 17 / 8, lane, g);
+        const uint8_t *base = L.w + ((int64_t)(e < 0 ? 0 : e) * p.n_rows + row0) * row_bytes;
+        tile_issue(base, e < 0 ? 0 : rows * nb * 17 / 8, lane, g);
     };
-    // this wave's first slot's weights depend only on its id: issue them before
-    // anything else
-    const int e_first = wave < p.n_slots ? p.ids[wave] : -1;
+    // Small loads before the weights: every slot's id and, when they fit in
+    // registers, every slot's h row.  This wave's first weights depend only on
+    // its slot's id (a scalar load).
+    const int e_first = wave < p.n_slots ? L.ids[wave] : -1;
     const bool first_ok = e_first >= 0 && e_first < p.n_expert;
-    if (first_ok) issue_e(e_first);
+    const int e_mine = L.ids[min(tid, p.n_slots - 1)];
+    const bool h_pre = p.n_slots * nb <= kDnPrePass * (kRowThreads / 8);
+    float4 hv[kDnPrePass];
+    prefetch_rows<kDnPrePass>(L.h, p.n_ff, p.n_slots, nb, hv);
+    issue_e(first_ok ? e_first : -1);
 
     if (tid < p.n_slots) {
-        const int e = p.ids[tid];
-        s_e[tid] = (e >= 0 && e < p.n_expert) ? e : -1;
+        s_e[tid] = (e_mine >= 0 && e_mine < p.n_expert) ? e_mine : -1;
         s_rows[tid] = tid;
     }
     __syncthreads();
-    if (blockIdx.x == 0 && tid == 0) {
+    if (wl == 0 && tid == 0) {
         int bad = 0;
         for (int s = 0; s < p.n_slots; ++s) bad |= (s_e[s] < 0);
-        *p.err = bad;
+        *L.err = bad;
     }
 
     auto next_slot = [&](int s) {
@@ -438,7 +570,8 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
     int s = next_slot(wave);
     if (!first_ok && s < p.n_slots) issue_e(s_e[s]);
 
-    quantize_rows_to_image(p.h, p.n_ff, s_rows, p.n_slots, nb, ximg, xsc);
+    if (h_pre) quantize_prefetched<kDnPrePass>(hv, p.n_slots, nb, 0, ximg, xsc);
+    else quantize_rows_to_image(L.h, p.n_ff, s_rows, 0, p.n_slots, nb, ximg, xsc);
     __syncthreads();
 
     while (s < p.n_slots) {
@@ -476,39 +609,51 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
         if (bad) {
             acc = __builtin_nanf("");
         } else {
-            acc = p.cw[t * p.n_used] * ys[t * p.n_used][r];
+            acc = L.cw[t * p.n_used] * ys[t * p.n_used][r];
             for (int u = 1; u < p.n_used; ++u)
-                acc = fmaf(p.cw[t * p.n_used + u], ys[t * p.n_used + u][r], acc);
+                acc = fmaf(L.cw[t * p.n_used + u], ys[t * p.n_used + u][r], acc);
         }
-        p.out[(int64_t)t * p.n_rows + row0 + r] = acc;
+        L.out[(int64_t)t * p.n_rows + row0 + r] = acc;
     }
 }
 
 // out[t][n] = sum over u ascending of cw[t][u] * yslot[t*n_used+u][n]; a token
-// with an out-of-range id gets NaN.
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restrict__ yslot,
-                                                          const int32_t *__restrict__ ids,
-                                                          const float *__restrict__ cw,
-                                                          float *__restrict__ out, int n_rows,
-                                                          int n_used, int n_expert)
+// with an out-of-range id gets NaN.  grid (ceil(n_rows/256), n_tok, n_layers).
+struct CbLayer {
+    const float *yslot;
+    const int32_t *ids;
+    const float *cw;
+    float *out;
+};
+
+struct CbParams {
+    CbLayer layer[kMoeMaxLayers];
+    int n_rows, n_used, n_expert;
+};
+
+static_assert(sizeof(CbParams) <= 4000, "kernel arguments must stay below 4 KB");
+
+__global__ __launch_bounds__(256) void moe_combine_kernel(const CbParams p)
 {
+    const CbLayer &L = p.layer[blockIdx.z];
     const int t = blockIdx.y;
     const int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= n_rows) return;
+    if (n >= p.n_rows) return;
     bool bad = false;
-    for (int u = 0; u < n_used; ++u) {
-        const int e = ids[t * n_used + u];
-        bad |= (e < 0 || e >= n_expert);
+    for (int u = 0; u < p.n_used; ++u) {
+        const int e = L.ids[t * p.n_used + u];
+        bad |= (e < 0 || e >= p.n_expert);
     }
     float acc;
     if (bad) {
         acc = __builtin_nanf("");
     } else {
-        const float *y = yslot + (int64_t)t * n_used * n_rows + n;
-        acc = cw[t * n_used] * y[0];
-        for (int u = 1; u < n_used; ++u) acc = fmaf(cw[t * n_used + u], y[(int64_t)u * n_rows], acc);
+        const float *y = L.yslot + (int64_t)t * p.n_used * p.n_rows + n;
+        acc = L.cw[t * p.n_used] * y[0];
+        for (int u = 1; u < p.n_used; ++u)
+            acc = fmaf(L.cw[t * p.n_used + u], y[(int64_t)u * p.n_rows], acc);
     }
-    out[(int64_t)t * n_rows + n] = acc;
+    L.out[(int64_t)t * p.n_rows + n] = acc;
 }
 
 __global__ __launch_bounds__(kThreads) void moe_route_kernel(const int32_t *ids, int32_t *counts,
@@ -592,24 +737,25 @@ __device__ void quantize_row_to_blocks(const float *src, int nb, uint8_t *dst)
     }
 }
 
-__global__ __launch_bounds__(kThreads) void moe_up_gate_generic_kernel(UgParams p)
+__global__ __launch_bounds__(kThreads) void moe_up_gate_generic_kernel(const UgParams p)
 {
     extern __shared__ __align__(16) uint8_t xq[];      // nb blocks of 34 B
-    generic_flag_invalid(p.ids, p.n_slots, p.n_expert, p.err);
+    const UgLayer &L = p.layer[blockIdx.z];
+    generic_flag_invalid(L.ids, p.n_slots, p.n_expert, L.err);
     const int s = blockIdx.x;
-    const int e = p.ids[s];
-    quantize_row_to_blocks(p.x + (int64_t)(s / p.n_used) * p.nb * kQK, p.nb, xq);
+    const int e = L.ids[s];
+    quantize_row_to_blocks(L.x + (int64_t)(s / p.n_used) * p.nb * kQK, p.nb, xq);
     __syncthreads();
     const int j = blockIdx.y * kWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (j >= p.n_ff) return;
-    float *dst = p.h + (int64_t)s * p.n_ff + j;
+    float *dst = L.h + (int64_t)s * p.n_ff + j;
     if (e < 0 || e >= p.n_expert) {
         if (lane == 0) *dst = __builtin_nanf("");
         return;
     }
     const int64_t row_bytes = (int64_t)p.nb * kBlockBytes;
-    const uint8_t *We = p.w + (int64_t)e * 2 * p.n_ff * row_bytes;
+    const uint8_t *We = L.w + (int64_t)e * 2 * p.n_ff * row_bytes;
     const uint8_t *xr = xq;
     const float g = generic_row_dot(We + (int64_t)j * row_bytes, xr, p.nb, lane);
     const float u = generic_row_dot(We + (int64_t)(p.n_ff + j) * row_bytes, xr, p.nb, lane);
@@ -618,23 +764,24 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_generic_kernel(UgParams 
 
 // grid (n_slots, ceil(n_rows / 4)); the slot's h row is quantized into LDS
 // first (same rule and code as the activation quantizer).
-__global__ __launch_bounds__(kThreads) void moe_down_generic_kernel(DnParams p)
+__global__ __launch_bounds__(kThreads) void moe_down_generic_kernel(const DnParams p)
 {
     extern __shared__ __align__(16) uint8_t hq[];      // nb blocks of 34 B
-    generic_flag_invalid(p.ids, p.n_slots, p.n_expert, p.err);
+    const DnLayer &L = p.layer[blockIdx.z];
+    generic_flag_invalid(L.ids, p.n_slots, p.n_expert, L.err);
     const int s = blockIdx.x;
-    const int e = p.ids[s];
+    const int e = L.ids[s];
     if (e < 0 || e >= p.n_expert) return;              // the combine writes NaN
     const int tid = threadIdx.x;
-    quantize_row_to_blocks(p.h + (int64_t)s * p.n_ff, p.nb, hq);
+    quantize_row_to_blocks(L.h + (int64_t)s * p.n_ff, p.nb, hq);
     __syncthreads();
     const int row = blockIdx.y * kWaves + (tid >> 6);
     const int lane = tid & 63;
     if (row >= p.n_rows) return;
     const int64_t row_bytes = (int64_t)p.nb * kBlockBytes;
-    const uint8_t *wr = p.w + ((int64_t)e * p.n_rows + row) * row_bytes;
+    const uint8_t *wr = L.w + ((int64_t)e * p.n_rows + row) * row_bytes;
     const float y = generic_row_dot(wr, hq, p.nb, lane);
-    if (lane == 0) p.yslot[(int64_t)s * p.n_rows + row] = y;
+    if (lane == 0) L.yslot[(int64_t)s * p.n_rows + row] = y;
 }
 
 int pick_mt(int64_t n_tok)
@@ -680,11 +827,16 @@ static int tiles_per_wg_for(int64_t active, int64_t tiles_per_expert)
 
 int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
 {
-    if (a.n_tok == 0) return 0;
+    if (a.n_tok == 0 || a.n_layers == 0) return 0;
     const int64_t nb = a.n_embd / kQK;
     const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
     UgParams p;
-    p.w = a.w; p.x = a.x; p.ids = a.ids; p.h = a.h; p.err = (int32_t *)a.ws;
+    memset(&p, 0, sizeof(p));
+    for (int l = 0; l < a.n_layers; ++l) {
+        const MoeUpGateArgs::Layer &A = a.layer[l];
+        p.layer[l] = UgLayer{A.w, A.x, A.ids, A.h, (int32_t *)A.ws};
+    }
+    p.n_layers = a.n_layers;
     p.n_slots = (int)(a.n_tok * a.n_used);
     p.n_used = (int)a.n_used;
     p.n_expert = (int)a.n_expert;
@@ -692,14 +844,15 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
     p.n_ff = (int)a.n_ff;
     p.R = fast ? (int)(64 / (nb / 4)) : 1;
     p.tiles_per_expert = (p.n_ff + p.R - 1) / p.R;
-    const int64_t active = a.n_expert < p.n_slots ? a.n_expert : p.n_slots;
+    const int64_t active = a.n_layers * (a.n_expert < p.n_slots ? a.n_expert : p.n_slots);
     p.tiles_per_wg = tiles_per_wg_for(active, p.tiles_per_expert);
     p.wgs_per_expert = (p.tiles_per_expert + p.tiles_per_wg - 1) / p.tiles_per_wg;
-    const int64_t grid = (int64_t)p.n_slots * p.wgs_per_expert;
+    p.wgs_per_layer = p.n_slots * p.wgs_per_expert;
+    const int64_t grid = (int64_t)a.n_layers * p.wgs_per_layer;
     if (!fast) {
         const size_t lds = (size_t)nb * kBlockBytes;
         if (lds > (size_t)max_lds_bytes()) return -4;
-        dim3 g((unsigned)p.n_slots, (unsigned)((p.n_ff + kWaves - 1) / kWaves));
+        dim3 g((unsigned)p.n_slots, (unsigned)((p.n_ff + kWaves - 1) / kWaves), (unsigned)a.n_layers);
         hipLaunchKernelGGL(moe_up_gate_generic_kernel, g, dim3(kThreads), lds, stream, p);
         return hipGetLastError() == hipSuccess ? 0 : -6;
     }
@@ -724,28 +877,41 @@ static int launch_dn_mt(const DnParams &p, int grid, hipStream_t stream)
 
 int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
 {
-    if (a.n_tok == 0) return 0;
+    if (a.n_tok == 0 || a.n_layers == 0) return 0;
     const int64_t nb = a.n_ff / kQK;
     const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
     const int64_t n_slots = a.n_tok * a.n_used;
     if (fast && n_slots <= kRowsMaxSlots) {
         DrParams r;
-        r.w = a.w; r.h = a.h; r.ids = a.ids; r.cw = a.cw; r.out = a.out;
-        r.err = (int32_t *)a.ws;
+        memset(&r, 0, sizeof(r));
+        for (int l = 0; l < a.n_layers; ++l) {
+            const MoeDownArgs::Layer &A = a.layer[l];
+            r.layer[l] = DrLayer{A.w, A.h, A.ids, A.cw, A.out, (int32_t *)A.ws};
+        }
+        r.n_layers = a.n_layers;
         r.n_used = (int)a.n_used; r.n_slots = (int)n_slots; r.n_expert = (int)a.n_expert;
         r.nb = (int)nb; r.n_ff = (int)a.n_ff; r.n_rows = (int)a.n_embd;
         r.R = (int)(64 / (nb / 4));
+        r.wgs_per_layer = (int)((a.n_embd + r.R - 1) / r.R);
         const size_t lds = (size_t)kRowWaves * kStageBytes + (size_t)kRowsMaxSlots * nb * kBlockBytes +
                            (size_t)kRowsMaxSlots * nb * 4;
         if (lds > (size_t)max_lds_bytes()) return -4;
-        const unsigned grid = (unsigned)((a.n_embd + r.R - 1) / r.R);
-        hipLaunchKernelGGL(moe_down_rows_kernel, dim3(grid), dim3(kRowThreads), lds, stream, r);
+        const int64_t grid = (int64_t)a.n_layers * r.wgs_per_layer;
+        if (grid > 0x7fffffff) return -4;
+        hipLaunchKernelGGL(moe_down_rows_kernel, dim3((unsigned)grid), dim3(kRowThreads), lds, stream, r);
         return hipGetLastError() == hipSuccess ? 0 : -6;
     }
     DnParams p;
-    p.w = a.w; p.h = a.h; p.ids = a.ids;
-    p.yslot = (float *)((uint8_t *)a.ws + 256);
-    p.err = (int32_t *)a.ws;
+    memset(&p, 0, sizeof(p));
+    CbParams cb;
+    memset(&cb, 0, sizeof(cb));
+    for (int l = 0; l < a.n_layers; ++l) {
+        const MoeDownArgs::Layer &A = a.layer[l];
+        float *yslot = (float *)((uint8_t *)A.ws + 256);
+        p.layer[l] = DnLayer{A.w, A.h, A.ids, yslot, (int32_t *)A.ws};
+        cb.layer[l] = CbLayer{yslot, A.ids, A.cw, A.out};
+    }
+    p.n_layers = a.n_layers;
     p.n_slots = (int)(a.n_tok * a.n_used);
     p.n_used = (int)a.n_used;
     p.n_expert = (int)a.n_expert;
@@ -754,16 +920,17 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
     p.n_rows = (int)a.n_embd;
     p.R = fast ? (int)(64 / (nb / 4)) : 1;
     p.tiles_per_expert = (p.n_rows + p.R - 1) / p.R;
-    const int64_t active = a.n_expert < p.n_slots ? a.n_expert : p.n_slots;
+    const int64_t active = a.n_layers * (a.n_expert < p.n_slots ? a.n_expert : p.n_slots);
     p.tiles_per_wg = tiles_per_wg_for(active, p.tiles_per_expert);
     p.wgs_per_expert = (p.tiles_per_expert + p.tiles_per_wg - 1) / p.tiles_per_wg;
-    const int64_t grid = (int64_t)p.n_slots * p.wgs_per_expert;
+    p.wgs_per_layer = p.n_slots * p.wgs_per_expert;
+    const int64_t grid = (int64_t)a.n_layers * p.wgs_per_layer;
     int rc;
     if (fast && grid > 0x7fffffff) return -4;
     if (!fast) {
         const size_t lds = (size_t)nb * kBlockBytes;
         if (lds > (size_t)max_lds_bytes()) return -4;
-        dim3 g((unsigned)p.n_slots, (unsigned)((p.n_rows + kWaves - 1) / kWaves));
+        dim3 g((unsigned)p.n_slots, (unsigned)((p.n_rows + kWaves - 1) / kWaves), (unsigned)a.n_layers);
         hipLaunchKernelGGL(moe_down_generic_kernel, g, dim3(kThreads), lds, stream, p);
         rc = hipGetLastError() == hipSuccess ? 0 : -6;
     } else switch (pick_mt(a.n_tok)) {
@@ -772,9 +939,11 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
         default: rc = launch_dn_mt<4>(p, (int)grid, stream); break;
     }
     if (rc) return rc;
-    dim3 cgrid((unsigned)((a.n_embd + 255) / 256), (unsigned)a.n_tok);
-    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, p.yslot, a.ids, a.cw,
-                       a.out, (int)a.n_embd, (int)a.n_used, (int)a.n_expert);
+    cb.n_rows = (int)a.n_embd;
+    cb.n_used = (int)a.n_used;
+    cb.n_expert = (int)a.n_expert;
+    dim3 cgrid((unsigned)((a.n_embd + 255) / 256), (unsigned)a.n_tok, (unsigned)a.n_layers);
+    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, cb);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

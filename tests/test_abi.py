@@ -128,3 +128,39 @@ def test_moe_checks(lib):
     assert dc(*a) == Q8_E_WORKSPACE
     assert lib.moe_route(A, A, A, A, 4, 8, 2, None, 256, None) == Q8_E_WORKSPACE
     assert lib.moe_route(A, None, A, A, 4, 8, 2, A, 256, None) == Q8_E_NULL
+
+
+def test_moe_batched_checks(lib):
+    """Grouped MoE calls: every descriptor is checked before anything is
+    enqueued (no valid launch here: there is no GPU)."""
+    import ctypes
+    import moe_expert_ffn_q8_amd as q
+    ws_bytes = q.moe_workspace_bytes(4, 256, 64, 8, 2)
+    good = q.MoeUpGateDesc(A, A, A, A, A, ws_bytes)
+    ug = lib.moe_up_gate_swiglu_batched
+
+    def call(descs, n=None, shape=(4, 256, 64, 8, 2)):
+        arr = (q.MoeUpGateDesc * max(len(descs), 1))(*descs)
+        return ug(arr, len(descs) if n is None else n, *shape, None)
+
+    assert call([good], n=-1) == Q8_E_SHAPE
+    assert call([], n=0) == Q8_OK                      # nothing to do
+    assert ug(None, 2, 4, 256, 64, 8, 2, None) == Q8_E_NULL
+    assert call([good], shape=(4, 250, 64, 8, 2)) == Q8_E_SHAPE
+    assert call([good], shape=(4, 256, 64, 8, 17)) == Q8_E_UNSUPPORTED
+    bad_ws = q.MoeUpGateDesc(A, A, A, A, A, ws_bytes - 1)
+    assert call([good, bad_ws]) == Q8_E_WORKSPACE     # the second descriptor fails
+    bad_align = q.MoeUpGateDesc(A, A + 4, A, A, A, ws_bytes)
+    assert call([good, good, bad_align]) == Q8_E_ALIGN
+    bad_null = q.MoeUpGateDesc(A, A, None, A, A, ws_bytes)
+    assert call([bad_null]) == Q8_E_NULL
+
+    dn = lib.moe_down_combine_batched
+    dgood = q.MoeDownDesc(A, A, A, A, A, A, ws_bytes)
+    darr = (q.MoeDownDesc * 2)(dgood, q.MoeDownDesc(A, A, A, A, None, A, ws_bytes))
+    assert dn(darr, 2, 4, 64, 256, 8, 2, None) == Q8_E_NULL
+    darr = (q.MoeDownDesc * 2)(dgood, q.MoeDownDesc(A, A + 4, A, A, A, A, ws_bytes))
+    assert dn(darr, 2, 4, 64, 256, 8, 2, None) == Q8_E_ALIGN
+    assert dn(darr, -3, 4, 64, 256, 8, 2, None) == Q8_E_SHAPE
+    assert dn(None, 0, 4, 64, 256, 8, 2, None) == Q8_OK
+    assert ctypes.sizeof(q.MoeUpGateDesc) == 48 and ctypes.sizeof(q.MoeDownDesc) == 56

@@ -174,3 +174,75 @@ def test_moe_full_layer_shape(q, orc, n_tok):
     """One layer at the full expert shape: n_embd 2048, n_ff 768, 128 experts,
     8 active per token, batch 1 and 16."""
     _run(q, orc, n_tok, 2048, 768, 128, 8, f"c4-layer-{n_tok}")
+
+
+def _batched_layers(q, orc, n_layers, n_tok, n_embd, n_ff, n_expert, n_used, tag, bad_layer=None):
+    import torch
+    layers, refs = [], []
+    for l in range(n_layers):
+        w_ug, w_d, xf, ids, cw = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used, f"{tag}-{l}")
+        if l == bad_layer:
+            ids = ids.copy()
+            ids[0, 0] = n_expert           # out of range: this layer only
+        ws = q.moe_workspace(n_tok, n_embd, n_ff, n_expert, n_used, "cuda")
+        ws.fill_(0x7F)
+        layers.append(dict(w_up_gate=to_gpu(w_ug), x=to_gpu(xf), ids=to_gpu(ids),
+                           h=nan_like((n_tok, n_used, n_ff)), ws=ws, w_down=to_gpu(w_d),
+                           cw=to_gpu(cw), out=nan_like((n_tok, n_embd))))
+        refs.append(dict(w_ug=w_ug, w_d=w_d, xq=orc.quantize_rows(xf), ids=ids, cw=cw))
+    return layers, refs
+
+
+@pytest.mark.parametrize("n_layers,n_tok,n_embd,n_ff,n_expert,n_used", [
+    (3, 1, 512, 256, 16, 8),      # decode: row-major down kernel
+    (5, 4, 256, 128, 8, 4),       # expert-major down + combine
+    (33, 1, 256, 64, 8, 2),       # more descriptors than one launch takes
+    (2, 3, 256, 96, 6, 4)])       # generic kernels (k/32 not a multiple of 8)
+def test_moe_batched_layers(q, orc, n_layers, n_tok, n_embd, n_ff, n_expert, n_used):
+    """Grouped calls over independent layers: each layer's h and output match
+    the oracle, and are bitwise equal to the single-layer calls."""
+    import torch
+    layers, refs = _batched_layers(q, orc, n_layers, n_tok, n_embd, n_ff, n_expert, n_used,
+                                   f"mb-{n_layers}-{n_tok}-{n_ff}")
+    q.moe_up_gate_swiglu_batched(layers, n_embd, n_ff, n_expert)
+    q.moe_down_combine_batched(layers, n_ff, n_embd, n_expert)
+    torch.cuda.synchronize()
+    for d, r in zip(layers, refs):
+        assert q.moe_error_word(d["ws"]) == 0
+        h_gpu = d["h"].cpu().numpy()
+        h_ref = orc.moe_up_gate_swiglu(r["w_ug"], r["xq"], r["ids"], n_embd, n_ff, n_expert)
+        assert_rows_close(h_gpu.reshape(-1, n_ff), h_ref.reshape(-1, n_ff))
+        out_ref = orc.moe_down_combine(r["w_d"], h_gpu, r["ids"], r["cw"], n_ff, n_embd, n_expert)
+        assert_rows_close(d["out"].cpu().numpy(), out_ref)
+        # same bits as the single-layer calls
+        h1 = nan_like(tuple(d["h"].shape))
+        q.moe_up_gate_swiglu(d["w_up_gate"], d["x"], d["ids"], n_embd, n_ff, n_expert, d["ws"],
+                             h=h1)
+        o1 = nan_like(tuple(d["out"].shape))
+        q.moe_down_combine(d["w_down"], h1, d["ids"], d["cw"], n_ff, n_embd, n_expert, d["ws"],
+                           out=o1)
+        assert torch.equal(h1, d["h"]) and torch.equal(o1, d["out"])
+
+
+def test_moe_batched_invalid_id_one_layer(q, orc):
+    """An out-of-range id in one layer sets that layer's error word and NaNs
+    only; the other layers are unaffected."""
+    import torch
+    n_layers, n_tok, n_embd, n_ff, n_expert, n_used = 3, 1, 256, 64, 8, 4
+    layers, refs = _batched_layers(q, orc, n_layers, n_tok, n_embd, n_ff, n_expert, n_used,
+                                   "mb-bad", bad_layer=1)
+    q.moe_up_gate_swiglu_batched(layers, n_embd, n_ff, n_expert)
+    q.moe_down_combine_batched(layers, n_ff, n_embd, n_expert)
+    torch.cuda.synchronize()
+    for l, (d, r) in enumerate(zip(layers, refs)):
+        h = d["h"].cpu().numpy()
+        out = d["out"].cpu().numpy()
+        if l == 1:
+            assert q.moe_error_word(d["ws"]) == 1
+            assert np.all(np.isnan(h[0, 0])) and np.all(np.isnan(out[0]))
+            assert not np.any(np.isnan(h[0, 1:]))
+        else:
+            assert q.moe_error_word(d["ws"]) == 0
+            assert not np.any(np.isnan(h)) and not np.any(np.isnan(out))
+            out_ref = orc.moe_down_combine(r["w_d"], h, r["ids"], r["cw"], n_ff, n_embd, n_expert)
+            assert_rows_close(out, out_ref)
