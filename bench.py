@@ -96,12 +96,37 @@ class StepPlan:
         self.y_bytes = m * self.n_out * 4
         self.engine_bytes = self.w_bytes + self.x_bytes + self.y_bytes
         self.quant_bytes = m * self.k_total * 4 + self.x_bytes
+        # one fused launch per step: weights + fp32 activations read, outputs written
+        self.fused_bytes = self.w_bytes + m * self.k_total * 4 + self.y_bytes
         self.products = m * sum(n * k * batch for _, n, k, batch in stacks)   # MACs
+        self._f32_descs = {}
+
+    def descs_f32(self, x_step):
+        """Descriptors of the fused launch reading the fp32 rows of x_step."""
+        key = x_step.data_ptr()
+        if key not in self._f32_descs:
+            descs, xoff, yoff = [], 0, 0
+            for (name, n, k, batch), w in zip(self.stacks, self.w):
+                nb = k // QK
+                descs.append(self.q.make_f32_desc(
+                    w, (x_step, xoff), (self.y, yoff), n, k, m=self.m, batch=batch,
+                    w_batch_stride=n * nb, x_row_stride=self.k_total, x_batch_stride=k,
+                    y_row_stride=self.n_out, y_batch_stride=n))
+                xoff += batch * k
+                yoff += batch * n
+            self._f32_descs[key] = descs
+        return self._f32_descs[key]
 
     def step(self, x_step):
-        """x_step: fp32 [m][k_total] of this step."""
+        """x_step: fp32 [m][k_total] of this step: a quantize launch, then one
+        launch of every product of the step."""
         self.q.q8_0_quantize_rows(x_step, y=self.xq)
         self.q.q8_0_matmul_batched(self.descs, self.y)
+
+    def step_fused(self, x_step):
+        """The same step as one launch with the activations quantized inside
+        (every wave quantizes the rows it needs; slower here, see the JSON)."""
+        self.q.q8_0_matmul_f32_batched(self.descs_f32(x_step), self.y)
 
 
 def capture(fn):
@@ -137,20 +162,21 @@ def time_graph(g, reps=1):
 def time_steps(plan, xs, steps, warmup):
     """The K timed steps are captured in one HIP graph (2 launches per step:
     activation quantization, then the engine over every product of the step)
-    and replayed once inside the timed region.  Returns (total seconds for K
-    steps, mean engine launch seconds, mean quantize launch seconds); the
-    per-kernel means come from graphs of K launches of that kernel alone."""
+    and replayed once inside the timed region.  The per-kernel means come from
+    graphs of K launches of that kernel alone; for reference the same steps are
+    also timed with the quantization fused into the product launch.  Returns a
+    dict of seconds."""
     import torch
     n_in = xs.shape[0]
     for i in range(warmup):
         plan.step(xs[i % n_in])
+        plan.step_fused(xs[i % n_in])
     torch.cuda.synchronize()
 
     def all_steps():
         for i in range(steps):
             plan.step(xs[i % n_in])
-    g_all = capture(all_steps)
-    total = time_graph(g_all)
+    total = time_graph(capture(all_steps))
 
     def eng_only():
         for _ in range(steps):
@@ -161,7 +187,12 @@ def time_steps(plan, xs, steps, warmup):
         for i in range(steps):
             plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
     qnt = time_graph(capture(qnt_only)) / steps
-    return total, eng, qnt
+
+    def all_fused():
+        for i in range(steps):
+            plan.step_fused(xs[i % n_in])
+    total_fused = time_graph(capture(all_fused))
+    return dict(total=total, eng=eng, qnt=qnt, total_fused=total_fused)
 
 
 # ---------------------------------------------------------------------------
@@ -209,11 +240,13 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
     n_in = min(args.steps + args.warmup, n_steps_cfg)
     xs = synth.normal_f32_torch((n_in, m, plan.k_total), 1.0, dev, 0, name, "x")
     torch.cuda.synchronize()
-    total, eng, qnt = time_steps(plan, xs, args.steps, args.warmup)
+    t = time_steps(plan, xs, args.steps, args.warmup)
     bytes_step = plan.engine_bytes + plan.quant_bytes
-    value = bytes_step * args.steps / total / 1e9
-    tok_s = m * args.steps / total
-    achieved = plan.engine_bytes / eng / 1e9
+    value = bytes_step * args.steps / t["total"] / 1e9
+    tok_s = m * args.steps / t["total"]
+    achieved = plan.engine_bytes / t["eng"] / 1e9
+    kernel = ("stream_flat_kernel (decode engine)" if m <= 2 else
+              "stream_mfma_kernel (small-batch decode engine)")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -221,24 +254,28 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total / args.steps * 1e3, 5),
+        "ms_per_step": round(t["total"] / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 dot, fp32 scale (Q8_0)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init, no checkpoint)",
         "config": {"workload": wl_desc, "batch": m, "products_per_step": sum(
-            b for _, _, _, b in stacks), "launches_per_step": 2, "timing": "HIP graph of the K steps, one replay timed with HIP events",
+            b for _, _, _, b in stacks), "launches_per_step": 2,
+            "timing": "HIP graph of the K steps, one replay timed with HIP events",
             "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": bytes_step},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tok_s, 1),
-        "roofline": {"bound": "hbm", "kernel": ("stream_flat_kernel (decode engine)" if m <= 2 else
-                                                "stream_mfma_kernel (small-batch decode engine)"),
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_launch_us": round(eng * 1e6, 3),
+                     "avg_launch_us": round(t["eng"] * 1e6, 3),
                      "bytes_per_launch": plan.engine_bytes},
-        "quantize_kernel_avg_us": round(qnt * 1e6, 3),
+        "quantize_kernel_avg_us": round(t["qnt"] * 1e6, 3),
+        "fused_reference": {
+            "timing": "the same steps as one launch each, activations quantized inside it",
+            "ms_per_step": round(t["total_fused"] / args.steps * 1e3, 5),
+            "gbs": round(plan.fused_bytes * args.steps / t["total_fused"] / 1e9, 1)},
     }
     return out, plan
 
@@ -280,7 +317,8 @@ def run_extra(args, q, synth):
         wf = synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w")
         w = q.q8_0_quantize_rows(wf)
         del wf
-        x = q.q8_0_quantize_rows(synth.normal_f32_torch((1, k), 1.0, dev, 0, wl, "x"))
+        xf = synth.normal_f32_torch((1, k), 1.0, dev, 0, wl, "x")
+        x = q.q8_0_quantize_rows(xf)
         y = torch.empty(n, dtype=torch.float32, device=dev)
         total = _time_launches(lambda: q.q8_0_matvec(w, x, n, k, y=y), args.steps, args.warmup)
         nbytes = q8_bytes(n, k) + q8_bytes(1, k) + 4 * n
@@ -288,6 +326,14 @@ def run_extra(args, q, synth):
         res.update(shape=[n, k], us_per_matvec=round(t * 1e6, 3),
                    gbs=round(nbytes / t / 1e9, 1), pct_of_hbm_peak=round(nbytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
                    tokens_per_s_equiv=round(1 / t, 1), bytes_per_launch=nbytes)
+        # from fp32 activations: quantize launch + matvec, or one fused launch
+        t2 = _time_launches(lambda: (q.q8_0_quantize_rows(xf, y=x), q.q8_0_matvec(w, x, n, k, y=y)),
+                            args.steps, args.warmup) / args.steps
+        fd = [q.make_f32_desc(w, xf, y, n, k)]
+        tf = _time_launches(lambda: q.q8_0_matmul_f32_batched(fd, w), args.steps,
+                            args.warmup) / args.steps
+        res.update(from_fp32={"us_quantize_then_matvec": round(t2 * 1e6, 3),
+                              "us_fused": round(tf * 1e6, 3)})
     elif wl == "c5a":
         m, n, k = 512, 14336, 4096
         w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w"))

@@ -145,6 +145,32 @@ typedef struct q8_0_matmul_desc {
 
 int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *stream);
 
+/* q8_0_matmul_f32_batched: the same products with fp32 activations, quantized
+ * inside the launch by the activation rule (quantize_row_q8_0, [XEON] section
+ * on narrowing down the cause; the bytes equal q8_0_quantize_rows of the rows),
+ * so a decode step is one launch instead of a quantize launch and a product
+ * launch.  Results are bitwise equal to q8_0_quantize_rows followed by
+ * q8_0_matmul_batched on the same descriptors.
+ *   x  fp32 rows, 16-byte aligned; x_row_stride and x_batch_stride in floats,
+ *      multiples of 4 (x_row_stride >= k when m > 1)
+ *   w  16-byte aligned, w_batch_stride (blocks) a multiple of 8
+ * Streaming engines only: k % 256 == 0 and k <= 8192 (else Q8_E_UNSUPPORTED;
+ * quantize with q8_0_quantize_rows and use q8_0_matmul_batched), m <= 16.
+ * Other rules as q8_0_matmul_batched. */
+typedef struct {
+    const q8_0_block *w;
+    const float *x;
+    float *y;
+    int64_t n, k, m, batch;
+    int64_t w_batch_stride;   /* blocks */
+    int64_t x_row_stride;     /* floats */
+    int64_t x_batch_stride;   /* floats */
+    int64_t y_row_stride;     /* floats */
+    int64_t y_batch_stride;   /* floats */
+} q8_0_matmul_f32_desc;
+
+int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Mixture-of-experts expert FFN ([XEON] sections on the broken op paths and on
  * the three-part fix, runtime graph fallback).  Per token t and active slot

@@ -38,6 +38,13 @@ class Q8MatmulDesc(ctypes.Structure):
                 ("y_row_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class Q8MatmulF32Desc(ctypes.Structure):
+    _fields_ = [("w", _vp), ("x", _vp), ("y", _vp),
+                ("n", _i64), ("k", _i64), ("m", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_row_stride", _i64), ("x_batch_stride", _i64),
+                ("y_row_stride", _i64), ("y_batch_stride", _i64)]
+
+
 class MoeUpGateDesc(ctypes.Structure):
     _fields_ = [("w_up_gate", _vp), ("x", _vp), ("ids", _vp), ("h", _vp), ("ws", _vp),
                 ("ws_bytes", _size)]
@@ -55,6 +62,7 @@ _SIGS = {
     "q8_0_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "q8_0_matmul": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q8_0_matmul_batched": (_int, [ctypes.POINTER(Q8MatmulDesc), _i64, _vp]),
+    "q8_0_matmul_f32_batched": (_int, [ctypes.POINTER(Q8MatmulF32Desc), _i64, _vp]),
     "moe_workspace_bytes": (_size, [_i64, _i64, _i64, _i64, _i64]),
     "moe_up_gate_swiglu": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                   _size, _vp]),
@@ -182,6 +190,28 @@ def q8_0_matmul_batched(descs, stream_of):
     """descs: list of Q8MatmulDesc; stream_of: a tensor on the target device."""
     arr = (Q8MatmulDesc * len(descs))(*descs)
     _check("q8_0_matmul_batched", _lib.q8_0_matmul_batched(arr, len(descs), _stream(stream_of)))
+
+
+def make_f32_desc(w, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
+                  x_batch_stride=0, y_row_stride=None, y_batch_stride=0):
+    """One q8_0_matmul_f32_desc (fp32 activations, quantized inside).  w, x, y
+    are (tensor, element offset) pairs or tensors; strides are in blocks (w)
+    and floats (x, y)."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    return Q8MatmulF32Desc(addr(w, BLOCK_BYTES), addr(x, 4), addr(y, 4), n, k, m, batch,
+                           w_batch_stride, k if x_row_stride is None else x_row_stride,
+                           x_batch_stride, n if y_row_stride is None else y_row_stride,
+                           y_batch_stride)
+
+
+def q8_0_matmul_f32_batched(descs, stream_of):
+    """descs: list of Q8MatmulF32Desc; stream_of: a tensor on the target device."""
+    arr = (Q8MatmulF32Desc * len(descs))(*descs)
+    _check("q8_0_matmul_f32_batched",
+           _lib.q8_0_matmul_f32_batched(arr, len(descs), _stream(stream_of)))
 
 
 def q8_0_matmul_blocksums(w, x, n, k, m):

@@ -151,6 +151,47 @@ int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *str
     return hip_status(q8::launch_stream(d, nd, as_stream(stream)));
 }
 
+int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    q8::StreamDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    for (int64_t i = 0; i < n_desc; ++i) {
+        const q8_0_matmul_f32_desc &s = descs[i];
+        if (int rc = check_k(s.k)) return rc;
+        if (s.n < 0 || s.m < 0 || s.batch < 0) return Q8_E_SHAPE;
+        if (s.m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
+        if (s.n == 0 || s.m == 0 || s.batch == 0) continue;
+        if (!s.w || !s.x || !s.y) return Q8_E_NULL;
+        const int64_t nb = s.k / kQK;
+        if (s.m > 1 && (s.x_row_stride < s.k || s.y_row_stride < s.n)) return Q8_E_SHAPE;
+        if (s.batch > 1 && (s.w_batch_stride < s.n * nb || s.x_batch_stride < 0 ||
+                            s.y_batch_stride < s.n))
+            return Q8_E_SHAPE;
+        if (!aligned(s.w, 16) || !aligned(s.x, 16) || !aligned(s.y, 4) ||
+            (s.m > 1 && s.x_row_stride % 4 != 0) || (s.batch > 1 && s.x_batch_stride % 4 != 0))
+            return Q8_E_ALIGN;
+        q8::StreamDesc &o = d[nd++];
+        memset(&o, 0, sizeof(o));
+        o.w = (const uint8_t *)s.w;
+        o.x = (const uint8_t *)s.x;
+        o.y = s.y;
+        o.n = s.n; o.nb = nb; o.m = s.m; o.batch = s.batch;
+        o.w_bstride = s.w_batch_stride * kBB;
+        o.x_rstride = (s.m > 1 ? s.x_row_stride : s.k) * 4;
+        o.x_bstride = s.x_batch_stride * 4;
+        o.y_rstride = s.y_row_stride;
+        o.y_bstride = s.y_batch_stride;
+        o.x_f32 = 1;
+        // the fused quantization exists in the streaming engines only
+        if (!q8::stream_fast_ok(o)) return Q8_E_UNSUPPORTED;
+    }
+    return hip_status(q8::launch_stream(d, nd, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------------------
 // Mixture of experts
 

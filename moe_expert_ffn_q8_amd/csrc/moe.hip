@@ -134,16 +134,7 @@ __device__ void pick_by_slot(const int32_t *ids, int n_slots, int n_expert, int 
 __device__ __forceinline__ void quantize_to_image(float4 v, int m, int b, int nb, uint8_t *ximg,
                                                   float *xsc)
 {
-    const int li = threadIdx.x & 7;
-    uint32_t codes, dbits;
-    quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
-    uint16_t *img16 = (uint16_t *)(ximg + m * nb * kBlockBytes);
-    if (li == 0) {
-        img16[b * 17] = 0;
-        xsc[m * nb + b] = half_bits_to_float(dbits);
-    }
-    img16[b * 17 + 1 + 2 * li] = (uint16_t)(codes & 0xffffu);
-    img16[b * 17 + 2 + 2 * li] = (uint16_t)(codes >> 16);
+    quantize8_to_image(v, ximg + m * nb * kBlockBytes, xsc + m * nb, b, threadIdx.x & 7);
 }
 
 // Quantize fp32 rows m_begin..mc-1 (row m starts at base + row_index[m] *

@@ -218,4 +218,22 @@ __device__ __forceinline__ void quantize_block8(float v0, float v1, float v2, fl
     codes = packed;
 }
 
+// Quantize the block held by 8 lanes (4 values each, lane & 7 = position) into
+// a masked-image row (scale bytes zero; codes at the block's byte offsets) and
+// its fp32 scale: the image bytes are those of q8_0_quantize_rows with the
+// scale bytes cleared.
+__device__ __forceinline__ void quantize8_to_image(float4 v, uint8_t *img_row, float *sc_row,
+                                                   int b, int li)
+{
+    uint32_t codes, dbits;
+    quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+    uint16_t *img16 = (uint16_t *)img_row;
+    if (li == 0) {
+        img16[b * 17] = 0;
+        sc_row[b] = half_bits_to_float(dbits);
+    }
+    img16[b * 17 + 1 + 2 * li] = (uint16_t)(codes & 0xffffu);
+    img16[b * 17 + 2 + 2 * li] = (uint16_t)(codes >> 16);
+}
+
 }  // namespace q8

@@ -19,6 +19,7 @@ struct StreamDesc {
     int64_t x_bstride;     // bytes
     int64_t y_rstride;     // floats
     int64_t y_bstride;     // floats
+    int x_f32;             // x is fp32 rows (quantized inside) instead of Q8_0 blocks
 };
 
 // Limits of the streaming engine (checked by the ABI layer).

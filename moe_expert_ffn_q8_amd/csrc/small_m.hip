@@ -88,6 +88,7 @@ struct SmJob {
     int32_t wpb;         // workgroups per batch entry
     int32_t wg0;         // first workgroup of this job
     int32_t x_al4;       // activation rows start on 4-byte boundaries
+    int32_t x_f32;       // fp32 activation rows, quantized into the image here
 };
 
 struct SmArgs {
@@ -163,6 +164,56 @@ __device__ void build_a_image(const uint8_t *X, int x_rstride, bool al4, int m, 
     if (tid < kZeroPad / 4) xsc[nb * MT + tid] = 0.0f;
 }
 
+// The same image from fp32 activation rows, quantized here with the
+// activation rule (8 lanes per (block, token), as the quantizer does; the
+// codes are those of q8_0_quantize_rows).  A lane holds codes 4*li .. 4*li+3
+// of its block; the virtual dword li of an even block is made from the high
+// half of lane li-1 and the low half of lane li (lane 0: its low half and the
+// high half of lane 7).  Loads go in batches of kFB per thread; the first
+// batch is issued by the caller before the weights (first_batch).
+constexpr int kFB = 8;
+
+template <int MT>
+__device__ __forceinline__ void a_f32_load(const uint8_t *X, int x_rstride, int m, int nb, int pass0,
+                                           int tid, float4 (&v)[kFB])
+{
+    const int items = nb * MT;
+#pragma unroll
+    for (int i = 0; i < kFB; ++i) {
+        int it = min((tid >> 3) + (pass0 + i) * (kSmThreads / 8), items - 1);
+        int b = it / MT;
+        int t = it - b * MT;
+        if (t >= m) t = m - 1;                    // clamped: always a real load
+        v[i] = *(const float4 *)(X + (int64_t)t * x_rstride + b * 128 + (tid & 7) * 16);
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void a_f32_store(int m, int nb, int pass0, int tid, const float4 (&v)[kFB],
+                                            uint8_t *img, float *xsc)
+{
+    const int items = nb * MT;
+    const int li = tid & 7;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < kFB; ++i) {
+        const int it = (tid >> 3) + (pass0 + i) * (kSmThreads / 8);
+        if (it < items) {
+            const int b = it / MT;
+            const int t = it - b * MT;
+            uint32_t codes, dbits;
+            quantize_block8(v[i].x, v[i].y, v[i].z, v[i].w, codes, dbits);
+            const uint32_t prev = (uint32_t)__shfl((int)codes, (lane & ~7) | ((li + 7) & 7));
+            uint32_t vd = codes;
+            if ((b & 1) == 0)
+                vd = li == 0 ? (codes & 0xffffu) | (prev & 0xffff0000u) : (prev >> 16) | (codes << 16);
+            if (t >= m) vd = 0;
+            *(uint32_t *)(img + ((b * 4 + (li >> 1)) * MT + t) * 8 + (li & 1) * 4) = vd;
+            if (li == 0) xsc[b * MT + t] = t < m ? half_bits_to_float(dbits) : 0.0f;
+        }
+    }
+}
+
 template <int MT, bool SUMS>
 __global__ __launch_bounds__(kSmThreads) void stream_mfma_kernel(const SmArgs a)
 {
@@ -233,11 +284,26 @@ __global__ __launch_bounds__(kSmThreads) void stream_mfma_kernel(const SmArgs a)
         }
     };
 
-    // Weights first: their latency overlaps the activation image copy.
+    if (J.x_f32) {
+        // fp32 activations: the first batch of row loads goes out before the
+        // weights, so waiting for it does not wait for the weights
+        const int passes = (nb * MT * 8 + kSmThreads - 1) / kSmThreads;
+        float4 v[kFB];
+        a_f32_load<MT>(X, J.x_rstride, m, nb, 0, tid, v);
 #pragma unroll
-    for (int s = 0; s < kDepth; ++s) issue(g[s]);
-
-    build_a_image<MT>(X, J.x_rstride, J.x_al4 != 0, m, nb, img, xsc, tid);
+        for (int s = 0; s < kDepth; ++s) issue(g[s]);
+        a_f32_store<MT>(m, nb, 0, tid, v, img, xsc);
+        for (int p0 = kFB; p0 < passes; p0 += kFB) {
+            a_f32_load<MT>(X, J.x_rstride, m, nb, p0, tid, v);
+            a_f32_store<MT>(m, nb, p0, tid, v, img, xsc);
+        }
+        if (tid < kZeroPad / 4) xsc[nb * MT + tid] = 0.0f;
+    } else {
+        // Weights first: their latency overlaps the activation image copy.
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) issue(g[s]);
+        build_a_image<MT>(X, J.x_rstride, J.x_al4 != 0, m, nb, img, xsc, tid);
+    }
     __syncthreads();
 
     const uint32_t sel = grp == 0 ? 0x05040302u : 0x03020100u;
@@ -425,6 +491,7 @@ int launch_small_m(const StreamDesc *d, int n, hipStream_t stream)
         J.wg0 = (int32_t)wg_total;
         J.x_al4 = (((uintptr_t)d[i].x) % 4 == 0 && d[i].x_rstride % 4 == 0 &&
                    d[i].x_bstride % 4 == 0) ? 1 : 0;
+        J.x_f32 = d[i].x_f32;
         wg_total += d[i].batch * wpb;
     }
     if (wg_total > 0x7fffffff) return -4;

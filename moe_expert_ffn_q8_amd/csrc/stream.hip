@@ -216,6 +216,7 @@ struct FlatArgs {
     int32_t n_jobs;
     int32_t total_tiles;
     int32_t tiles_per_wave;
+    int32_t nb_max;      // XF: LDS image row length (blocks)
 };
 
 static_assert(sizeof(FlatArgs) <= 4000, "kernel arguments must stay below 4 KB");
@@ -248,11 +249,64 @@ __device__ __forceinline__ void load_x_quad(const uint8_t *p, bool al8, uint32_t
     q[25] &= 0x0000ffffu;
 }
 
-template <int MT, bool SUMS>
-__global__ __launch_bounds__(kWave) void stream_flat_kernel(const FlatArgs a)
+// fp32 activations (XF): the wave quantizes the M rows of a (job, batch entry)
+// into its LDS image, 8 lanes per block with the activation rule (the bytes
+// are those of q8_0_quantize_rows), then every lane takes its quad.  The first
+// kXPre passes of loads can be issued early (before the weights) into
+// registers; longer rows load the rest pass by pass.
+constexpr int kXPre = 3;
+
+template <int P>
+__device__ __forceinline__ void xf_prefetch(const uint8_t *X, int rstride, int M, int nb, int lane,
+                                            float4 (&v)[P])
+{
+    const int items = M * nb;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int it = min((lane >> 3) + 8 * i, items - 1);     // clamped: always a real load
+        const int row = it / nb;
+        const int b = it - row * nb;
+        v[i] = *(const float4 *)(X + (int64_t)row * rstride + b * 128 + (lane & 7) * 16);
+    }
+}
+
+template <int P>
+__device__ __forceinline__ void xf_quantize(const uint8_t *X, int rstride, int M, int nb, int lane,
+                                            const float4 (&v)[P], uint8_t *img, float *sc)
+{
+    const int items = M * nb;
+    const int img_row = nb * kBlockBytes;
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int it = (lane >> 3) + 8 * i;
+        if (it < items) {
+            const int row = it / nb;
+            const int b = it - row * nb;
+            quantize8_to_image(v[i], img + row * img_row, sc + row * nb, b, lane & 7);
+        }
+    }
+    for (int it0 = 8 * P; it0 < items; it0 += 8) {
+        const int it = it0 + (lane >> 3);
+        if (it < items) {
+            const int row = it / nb;
+            const int b = it - row * nb;
+            const float4 x = *(const float4 *)(X + (int64_t)row * rstride + b * 128 + (lane & 7) * 16);
+            quantize8_to_image(x, img + row * img_row, sc + row * nb, b, lane & 7);
+        }
+    }
+    wave_lds_sync();
+}
+
+template <int MT, bool SUMS, bool XF>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 1)))
+void stream_flat_kernel(const FlatArgs a)
 {
     __shared__ __align__(16) uint8_t stage[kStageBytes];
     __shared__ float red[MT * kWave];
+    extern __shared__ __align__(16) uint8_t xf_lds[];   // XF: MT image rows, then scales
+    uint8_t *xf_img = xf_lds;
+    float *xf_sc = (float *)(xf_lds + ((MT * a.nb_max * kBlockBytes + 15) & ~15));
     const int lane = threadIdx.x;
     const int t_begin = blockIdx.x * a.tiles_per_wave;
     const int t_end = min(t_begin + a.tiles_per_wave, a.total_tiles);
@@ -274,11 +328,35 @@ __global__ __launch_bounds__(kWave) void stream_flat_kernel(const FlatArgs a)
         tile_issue(base, rows * J.nb * 17 / 8, lane, g);
     };
 
-    issue(jj, loc);
     int jx = -1, bx = -1;
     uint32_t xr[MT][kQuadDwords];
     float4 xd[MT];
-    {   // the first tile's activations, in flight together with its weights
+    // XF: lanes take their quads from the wave's freshly quantized image
+    auto xf_take = [&](const FlatJob &J, int c) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < J.m) {
+                lds_quad(xf_img + m * J.nb * kBlockBytes + kQuadBytes * c, xr[m]);
+                xd[m] = *(const float4 *)(xf_sc + m * J.nb + 4 * c);
+            }
+        }
+    };
+    if (XF) {
+        // the first job's fp32 rows are loaded before the weights, so the
+        // wait for them does not cover the tile loads
+        const FlatJob &J = a.job[jj];
+        const int bi = loc / J.tpb;
+        const uint8_t *X = J.x + (int64_t)bi * J.x_bstride;
+        float4 xv[kXPre];
+        xf_prefetch<kXPre>(X, J.x_rstride, J.m, J.nb, lane, xv);
+        issue(jj, loc);
+        xf_quantize<kXPre>(X, J.x_rstride, J.m, J.nb, lane, xv, xf_img, xf_sc);
+        xf_take(J, lane % (J.nb >> 2));
+        jx = jj;
+        bx = bi;
+    } else {
+        issue(jj, loc);
+        // the first tile's activations, in flight together with its weights
         const FlatJob &J = a.job[jj];
         const int bi = loc / J.tpb;
         const int c = lane % (J.nb >> 2);
@@ -304,18 +382,30 @@ __global__ __launch_bounds__(kWave) void stream_flat_kernel(const FlatArgs a)
             jn = jj + 1;
             ln = 0;
         }
-        uint32_t wq[kQuadDwords];
-        tile_to_quad(stage, g, lane, live, wq);
-        if (t + 1 < t_end) issue(jn, ln);
-
+        // A new (job, batch entry): its activations first, while this tile's
+        // weights are still in flight and before the next tile is issued, so
+        // the wait covers only loads needed now (and the tile's quad is not
+        // live yet, which keeps the register peak low).
         if (jj != jx || bi != bx) {
-            const uint8_t *X = J.x + (int64_t)bi * J.x_bstride + kQuadBytes * c;
+            if (XF) {
+                const uint8_t *X = J.x + (int64_t)bi * J.x_bstride;
+                float4 xv[kXPre];
+                xf_prefetch<kXPre>(X, J.x_rstride, M, J.nb, lane, xv);
+                xf_quantize<kXPre>(X, J.x_rstride, M, J.nb, lane, xv, xf_img, xf_sc);
+                xf_take(J, c);
+            } else {
+                const uint8_t *X = J.x + (int64_t)bi * J.x_bstride + kQuadBytes * c;
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                if (m < M) load_x_quad(X + (int64_t)m * J.x_rstride, J.x_al8 != 0, xr[m], xd[m]);
+                for (int m = 0; m < MT; ++m)
+                    if (m < M) load_x_quad(X + (int64_t)m * J.x_rstride, J.x_al8 != 0, xr[m], xd[m]);
+            }
             jx = jj;
             bx = bi;
         }
+
+        uint32_t wq[kQuadDwords];
+        tile_to_quad(stage, g, lane, live, wq);
+        if (t + 1 < t_end) issue(jn, ln);
 
         float dw0, dw1, dw2, dw3;
         quad_scales(wq, dw0, dw1, dw2, dw3);
@@ -380,6 +470,8 @@ __global__ __launch_bounds__(kWave) void stream_generic_kernel(StreamDesc d)
 bool stream_fast_ok(const StreamDesc &d)
 {
     if (d.nb % 8 != 0 || d.nb > kStreamMaxNb) return false;
+    if (d.x_f32 && (((uintptr_t)d.x) % 16 != 0 || d.x_rstride % 16 != 0 || d.x_bstride % 16 != 0))
+        return false;
     if (((uintptr_t)d.w) % 16 != 0 || d.w_bstride % 16 != 0) return false;
     if (d.m > kStreamMaxM) return false;
     if (d.n > (int64_t)1 << 30 || d.batch > (int64_t)1 << 20) return false;
@@ -415,17 +507,17 @@ struct DevInfo {
 };
 static DevInfo g_dev;
 
-template <int MT, bool SUMS>
-static int flat_resident_per_cu()
+template <int MT, bool SUMS, bool XF>
+static int flat_resident_per_cu(size_t lds)
 {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_flat_kernel<MT, SUMS>, kWave, 0) !=
-            hipSuccess || blocks <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_flat_kernel<MT, SUMS, XF>, kWave,
+                                                     lds) != hipSuccess || blocks <= 0)
         blocks = 8;
     return blocks;
 }
 
-template <int MT, bool SUMS>
+template <int MT, bool SUMS, bool XF>
 static int launch_flat_mt(const StreamDesc *d, int n, hipStream_t stream)
 {
     if (g_dev.cus == 0) {
@@ -436,10 +528,19 @@ static int launch_flat_mt(const StreamDesc *d, int n, hipStream_t stream)
             v = 256;
         g_dev.cus = v;
     }
-    static int per_cu = 0;
-    if (per_cu == 0) per_cu = flat_resident_per_cu<MT, SUMS>();
+    int64_t nb_max = 8;
+    for (int i = 0; i < n; ++i)
+        if (d[i].nb > nb_max) nb_max = d[i].nb;
+    const size_t lds = XF ? (size_t)((MT * nb_max * kBlockBytes + 15) & ~15) + (size_t)MT * nb_max * 4 : 0;
+    if (lds + kStageBytes + MT * kWave * 4 > (size_t)max_lds_bytes()) return -4;
+    // occupancy for this image size (cached per size class: one entry per
+    // 16 blocks of row length)
+    static int per_cu_cache[kStreamMaxNb / 16 + 1] = {0};
+    int &per_cu = per_cu_cache[XF ? nb_max / 16 : 0];
+    if (per_cu == 0) per_cu = flat_resident_per_cu<MT, SUMS, XF>(lds);
     FlatArgs a;
     memset(&a, 0, sizeof(a));
+    a.nb_max = (int32_t)nb_max;
     int64_t total = 0;
     for (int i = 0; i < n; ++i) {
         FlatJob &J = a.job[i];
@@ -466,7 +567,8 @@ static int launch_flat_mt(const StreamDesc *d, int n, hipStream_t stream)
     a.total_tiles = (int32_t)total;
     a.tiles_per_wave = (int32_t)tpw;
     const int64_t grid = (total + tpw - 1) / tpw;
-    hipLaunchKernelGGL((stream_flat_kernel<MT, SUMS>), dim3((unsigned)grid), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL((stream_flat_kernel<MT, SUMS, XF>), dim3((unsigned)grid), dim3(kWave), lds, stream,
+                       a);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -478,9 +580,13 @@ static int launch_flat(const StreamDesc *d, int n, hipStream_t stream)
         if (d[i].m > mmax) mmax = (int)d[i].m;
         if (d[i].sums) sums = true;
     }
-    if (sums) return mmax == 1 ? launch_flat_mt<1, true>(d, n, stream)
-                               : launch_flat_mt<2, true>(d, n, stream);
-    return mmax == 1 ? launch_flat_mt<1, false>(d, n, stream) : launch_flat_mt<2, false>(d, n, stream);
+    if (d[0].x_f32)
+        return mmax == 1 ? launch_flat_mt<1, false, true>(d, n, stream)
+                         : launch_flat_mt<2, false, true>(d, n, stream);
+    if (sums) return mmax == 1 ? launch_flat_mt<1, true, false>(d, n, stream)
+                               : launch_flat_mt<2, true, false>(d, n, stream);
+    return mmax == 1 ? launch_flat_mt<1, false, false>(d, n, stream)
+                     : launch_flat_mt<2, false, false>(d, n, stream);
 }
 
 static int launch_fast(const StreamDesc *d, int n, hipStream_t stream)
@@ -561,6 +667,8 @@ int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
         if (d[i].n == 0 || d[i].m == 0 || d[i].batch == 0) continue;
         if (stream_fast_ok(d[i])) {
             fast[nf++] = d[i];
+        } else if (d[i].x_f32) {
+            return -4;                 // checked by the caller: fast shapes only
         } else {
             if (d[i].n > 0x7fffffff || d[i].batch > 65535) return -4;
             hipLaunchKernelGGL(stream_generic_kernel, dim3((unsigned)d[i].n, (unsigned)d[i].batch),
@@ -574,6 +682,7 @@ int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
         if (fast[i].m > mmax) mmax = (int)fast[i].m;
     if (mmax <= 2) return launch_flat(fast, nf, stream);
     if (small_m_ok(fast, nf)) return launch_small_m(fast, nf, stream);
+    if (fast[0].x_f32) return -4;      // fp32 activations: matrix-core engine only
     return launch_fast(fast, nf, stream);
 }
 

@@ -164,3 +164,31 @@ def test_moe_batched_checks(lib):
     assert dn(darr, -3, 4, 64, 256, 8, 2, None) == Q8_E_SHAPE
     assert dn(None, 0, 4, 64, 256, 8, 2, None) == Q8_OK
     assert ctypes.sizeof(q.MoeUpGateDesc) == 48 and ctypes.sizeof(q.MoeDownDesc) == 56
+
+
+def test_matmul_f32_checks(lib):
+    """fp32-activation products: host checks (no launch without a GPU)."""
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_0_matmul_f32_batched
+
+    def call(**kw):
+        base = dict(w=A, x=A, y=A, n=64, k=768, m=1, batch=1, w_batch_stride=0, x_row_stride=768,
+                    x_batch_stride=0, y_row_stride=64, y_batch_stride=0)
+        base.update(kw)
+        d = q.Q8MatmulF32Desc(*[base[k] for k, _ in q.Q8MatmulF32Desc._fields_])
+        arr = (q.Q8MatmulF32Desc * 1)(d)
+        return f(arr, 1, None)
+
+    assert call(k=100) == Q8_E_SHAPE                 # k % 32
+    assert call(k=96) == Q8_E_UNSUPPORTED            # k/32 not a multiple of 8: no fused engine
+    assert call(k=16384) == Q8_E_UNSUPPORTED         # longer rows than the engines take
+    assert call(m=17) == Q8_E_UNSUPPORTED
+    assert call(x=A + 4) == Q8_E_ALIGN               # fp32 rows need 16 B
+    assert call(w=A + 2) == Q8_E_ALIGN
+    assert call(m=2, x_row_stride=770) == Q8_E_ALIGN
+    assert call(m=2, x_row_stride=512) == Q8_E_SHAPE
+    assert call(batch=2, w_batch_stride=64 * 24, y_batch_stride=0) == Q8_E_SHAPE
+    assert call(y=None) == Q8_E_NULL
+    assert f(None, 1, None) == Q8_E_NULL
+    assert f(None, 0, None) == Q8_OK
+    assert f(None, -1, None) == Q8_E_SHAPE

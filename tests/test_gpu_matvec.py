@@ -4,6 +4,8 @@ every output written (outputs are pre-filled with NaN), bitwise determinism."""
 import numpy as np
 import pytest
 
+import synth
+
 from gpu_cases import acts_q8, assert_rows_close, nan_like, to_gpu, weights_q8
 
 pytestmark = pytest.mark.gpu
@@ -207,3 +209,74 @@ def test_c5a_prefill_full_size(q, orc):
     yy = y.cpu().numpy()
     assert np.all(np.isfinite(yy))
     assert_rows_close(yy[:, rows], ref)
+
+
+@pytest.mark.parametrize("n,k,m,batch", [(300, 768, 1, 1), (1000, 2048, 1, 1), (257, 768, 2, 3),
+                                         (129, 3072, 3, 1), (1000, 768, 8, 2), (100, 4096, 16, 1),
+                                         (70, 256, 5, 4), (33, 8192, 1, 1), (40, 8192, 2, 1)])
+def test_matmul_f32_fused(q, orc, n, k, m, batch):
+    """fp32 activations quantized inside the product launch: bitwise equal to
+    q8_0_quantize_rows followed by q8_0_matmul_batched, and within tolerance of
+    the oracle.  Rows longer than the early-load window (k > 768 at m = 1)
+    take the pass-by-pass path."""
+    import torch
+    nb = k // 32
+    w = weights_q8(orc, batch * n, k, "f32", n, k, m)
+    stride = k + 12                       # padded fp32 rows (floats, multiple of 4)
+    xf = synth.normal_f32((batch * m, k), 1.0, "f32-x", n, k, m)
+    xbuf = np.zeros((batch * m, stride), dtype=np.float32)
+    xbuf[:, :k] = xf
+    wg, xg = to_gpu(w), to_gpu(xbuf)
+    y1 = nan_like((batch, m, n))
+    d = q.make_f32_desc(wg, xg, y1, n, k, m=m, batch=batch, w_batch_stride=n * nb,
+                        x_row_stride=stride, x_batch_stride=m * stride, y_row_stride=n,
+                        y_batch_stride=m * n)
+    q.q8_0_matmul_f32_batched([d], wg)
+    # two-step reference on the GPU
+    xq = q.q8_0_quantize_rows(torch.from_numpy(xf).cuda())
+    y2 = nan_like((batch, m, n))
+    d2 = q.make_desc(wg, xq, y2, n, k, m=m, batch=batch, w_batch_stride=n * nb,
+                     x_row_stride=nb, x_batch_stride=m * nb, y_row_stride=n, y_batch_stride=m * n)
+    q.q8_0_matmul_batched([d2], wg)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    xq_ref = orc.quantize_rows(xf)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    yy = y1.cpu().numpy()
+    for b in range(batch):
+        ref = orc.matmul(w[b * n:(b + 1) * n], xq_ref[b * m:(b + 1) * m], n, k, m)
+        assert_rows_close(yy[b], ref)
+
+
+@pytest.mark.parametrize("m", [1, 2, 6])
+def test_matmul_f32_fused_many_jobs(q, orc, m):
+    """Several products of different widths in one fused launch (waves cross
+    from one product to the next mid-range and requantize), against the
+    two-launch path, bitwise."""
+    import torch
+    specs = [(96, 768, 5), (160, 2048, 2), (50, 256, 1), (700, 768, 1), (64, 4096, 1)]
+    k_total = sum(k * b for _, k, b in specs)
+    xf = synth.normal_f32((m, k_total), 1.0, "f32-many", m)
+    xg = to_gpu(xf)
+    xq = q.q8_0_quantize_rows(xg)
+    nb_total = k_total // 32
+    n_out = sum(n * b for n, _, b in specs)
+    y1, y2 = nan_like((m, n_out)), nan_like((m, n_out))
+    d1, d2, keep = [], [], []
+    xoff = yoff = 0
+    for i, (n, k, b) in enumerate(specs):
+        nb = k // 32
+        w = to_gpu(weights_q8(orc, b * n, k, "f32-many-w", i))
+        keep.append(w)
+        d1.append(q.make_f32_desc(w, (xg, xoff), (y1, yoff), n, k, m=m, batch=b,
+                                  w_batch_stride=n * nb, x_row_stride=k_total, x_batch_stride=k,
+                                  y_row_stride=n_out, y_batch_stride=n))
+        d2.append(q.make_desc(w, (xq, xoff // 32), (y2, yoff), n, k, m=m, batch=b,
+                              w_batch_stride=n * nb, x_row_stride=nb_total, x_batch_stride=nb,
+                              y_row_stride=n_out, y_batch_stride=n))
+        xoff += b * k
+        yoff += b * n
+    q.q8_0_matmul_f32_batched(d1, xg)
+    q.q8_0_matmul_batched(d2, xg)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
