@@ -384,20 +384,20 @@ def run_extra(args, q, synth):
         def step_grouped():
             q.moe_up_gate_swiglu_batched(ug, n_embd, n_ff, E)
             q.moe_down_combine_batched(dn, n_ff, n_embd, E)
-        total = _time_launches(step, args.steps, args.warmup)
-        total_g = _time_launches(step_grouped, args.steps, args.warmup)
-        t = total / args.steps
-        tg = total_g / args.steps
-        res.update(tokens=n_tok, layers=L, active_weight_bytes=active_bytes,
-                   us_per_step=round(t * 1e6, 2), gbs=round(active_bytes / t / 1e9, 1),
-                   pct_of_hbm_peak=round(active_bytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
-                   tokens_per_s=round(n_tok / t, 1),
-                   timing="two launches per layer, layer after layer",
-                   grouped={"timing": "all layers in one up_gate and one down launch",
-                            "us_per_step": round(tg * 1e6, 2),
-                            "gbs": round(active_bytes / tg / 1e9, 1),
-                            "pct_of_hbm_peak": round(active_bytes / tg / 1e9 / HBM_PEAK_GBS * 100, 2),
-                            "tokens_per_s": round(n_tok / tg, 1)})
+        res.update(tokens=n_tok, layers=L, active_weight_bytes=active_bytes)
+        if args.moe_mode in ("both", "layers"):
+            t = _time_launches(step, args.steps, args.warmup) / args.steps
+            res.update(us_per_step=round(t * 1e6, 2), gbs=round(active_bytes / t / 1e9, 1),
+                       pct_of_hbm_peak=round(active_bytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
+                       tokens_per_s=round(n_tok / t, 1),
+                       timing="two launches per layer, layer after layer")
+        if args.moe_mode in ("both", "grouped"):
+            tg = _time_launches(step_grouped, args.steps, args.warmup) / args.steps
+            res.update(grouped={"timing": "all layers in one up_gate and one down launch",
+                                "us_per_step": round(tg * 1e6, 2),
+                                "gbs": round(active_bytes / tg / 1e9, 1),
+                                "pct_of_hbm_peak": round(active_bytes / tg / 1e9 / HBM_PEAK_GBS * 100, 2),
+                                "tokens_per_s": round(n_tok / tg, 1)})
     return res
 
 
@@ -462,6 +462,9 @@ def main():
     ap.add_argument("--workload", default="c2",
                     choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
+                    help="c4b1/c4b16: time the layer-after-layer launches, the grouped "
+                         "launches, or both")
     ap.add_argument("--cpu-sample-steps", type=int, default=48)
     ap.add_argument("--traffic", default=None,
                     help="JSON file with the rocprofv3-derived HBM bytes per launch")
