@@ -98,12 +98,6 @@ struct SmArgs {
 
 static_assert(sizeof(SmArgs) <= 4000, "kernel arguments must stay below 4 KB");
 
-// Write the m activation rows of one matrix as the A image: for block b,
-// lane group g (virtual dwords 2g, 2g+1) and token t, 8 bytes at
-// ((b*4 + g)*MT + t)*8; then the fp32 block scales at [b][t].  Tokens m..MT-1
-// are zero, and so are kZeroPad bytes after the scales (lanes past MT read
-// their operands there instead of branching).  One thread per (block, token);
-// with 4-byte aligned rows every dword is one load.
 __device__ __forceinline__ _Float16 half_lo(uint32_t v)
 {
     return __builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
@@ -114,11 +108,18 @@ __device__ __forceinline__ _Float16 half_hi(uint32_t v)
     return __builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
+// Write the m activation rows of one matrix as the A image: for block b,
+// lane group g (virtual dwords 2g, 2g+1) and token t, 8 bytes at
+// ((b*4 + g)*MT + t)*8; then the fp32 block scales at [b][t].  Tokens m..MT-1
+// are zero, and so are kZeroPad bytes after the scales (lanes past MT read
+// their operands there instead of branching).  One thread per (block, token),
+// items first_item.. (the earlier ones may have been written by a_q8_store);
+// with 4-byte aligned rows every dword is one load.
 template <int MT>
 __device__ void build_a_image(const uint8_t *X, int x_rstride, bool al4, int m, int nb,
-                              uint8_t *img, float *xsc, int tid)
+                              uint8_t *img, float *xsc, int tid, int first_item)
 {
-    for (int i = tid; i < nb * MT; i += kSmThreads) {
+    for (int i = first_item + tid; i < nb * MT; i += kSmThreads) {
         const int b = i / MT;
         const int t = i - b * MT;
         uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -214,6 +215,65 @@ __device__ __forceinline__ void a_f32_store(int m, int nb, int pass0, int tid, c
     }
 }
 
+// Early form of the Q8_0 image copy for 4-byte aligned rows: the 9 dwords of
+// up to kQP items (block, token) per thread are loaded before the weights
+// (a_q8_load), and written once the weights are in flight (a_q8_store); the
+// loads are unconditional (clamped item and token), so later waits are exact.
+// The 9 dwords start at the block for an even block (scale | q0 q1, ..., q30
+// q31 | next scale) and 2 bytes before it for an odd block (previous q30 q31 |
+// scale, then the 8 aligned code dwords); neither reaches past the row.
+constexpr int kQP = 2;
+
+template <int MT>
+__device__ __forceinline__ void a_q8_load(const uint8_t *X, int x_rstride, int m, int nb, int tid,
+                                          uint32_t (&d)[kQP][9])
+{
+    const int items = nb * MT;
+#pragma unroll
+    for (int j = 0; j < kQP; ++j) {
+        const int it = min(tid + j * kSmThreads, items - 1);
+        const int b = it / MT;
+        const int t = min(it - b * MT, m - 1);
+        const uint32_t *p = (const uint32_t *)(X + (int64_t)t * x_rstride + b * kBlockBytes -
+                                               ((b & 1) ? 2 : 0));
+#pragma unroll
+        for (int i = 0; i < 9; ++i) d[j][i] = p[i];
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void a_q8_store(int m, int nb, int tid, const uint32_t (&d)[kQP][9],
+                                           uint8_t *img, float *xsc)
+{
+    const int items = nb * MT;
+#pragma unroll
+    for (int j = 0; j < kQP; ++j) {
+        const int it = tid + j * kSmThreads;
+        if (it < items) {
+            const int b = it / MT;
+            const int t = it - b * MT;
+            uint32_t v[8];
+            uint32_t dbits;
+            if ((b & 1) == 0) {
+                dbits = d[j][0] & 0xffffu;
+                v[0] = (d[j][0] >> 16) | (d[j][8] << 16);
+#pragma unroll
+                for (int k = 1; k < 8; ++k) v[k] = d[j][k];
+            } else {
+                dbits = d[j][0] >> 16;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = d[j][k + 1];
+            }
+            const bool live = t < m;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(u32x2 *)(img + ((b * 4 + g) * MT + t) * 8) =
+                    live ? (u32x2){v[2 * g], v[2 * g + 1]} : (u32x2){0u, 0u};
+            xsc[it] = live ? half_bits_to_float(dbits) : 0.0f;
+        }
+    }
+}
+
 template <int MT, bool SUMS>
 __global__ __launch_bounds__(kSmThreads) void stream_mfma_kernel(const SmArgs a)
 {
@@ -298,11 +358,21 @@ __global__ __launch_bounds__(kSmThreads) void stream_mfma_kernel(const SmArgs a)
             a_f32_store<MT>(m, nb, p0, tid, v, img, xsc);
         }
         if (tid < kZeroPad / 4) xsc[nb * MT + tid] = 0.0f;
-    } else {
-        // Weights first: their latency overlaps the activation image copy.
+    } else if (J.x_al4) {
+        // the first kQP items per thread are loaded before the weights
+        uint32_t d[kQP][9];
+        a_q8_load<MT>(X, J.x_rstride, m, nb, tid, d);
 #pragma unroll
         for (int s = 0; s < kDepth; ++s) issue(g[s]);
-        build_a_image<MT>(X, J.x_rstride, J.x_al4 != 0, m, nb, img, xsc, tid);
+        a_q8_store<MT>(m, nb, tid, d, img, xsc);
+        if (nb * MT > kQP * kSmThreads)
+            build_a_image<MT>(X, J.x_rstride, true, m, nb, img, xsc, tid, kQP * kSmThreads);
+        else if (tid < kZeroPad / 4)
+            xsc[nb * MT + tid] = 0.0f;
+    } else {
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) issue(g[s]);
+        build_a_image<MT>(X, J.x_rstride, false, m, nb, img, xsc, tid, 0);
     }
     __syncthreads();
 
