@@ -805,6 +805,10 @@ static int launch_ug_mt(const UgParams &p, int grid, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
+// Tiles per workgroup: about 8 resident workgroups' worth of waves per CU
+// share the tiles, at most 8 tiles per wave.  Smaller work units (more
+// workgroups) were measured slower: each workgroup pays the ownership scan and
+// the activation quantization before it streams.
 static int tiles_per_wg_for(int64_t active, int64_t tiles_per_expert)
 {
     const int64_t total = active * tiles_per_expert;
