@@ -123,6 +123,26 @@ class StepPlan:
         self.q.q8_0_quantize_rows(x_step, y=self.xq)
         self.q.q8_0_matmul_batched(self.descs, self.y)
 
+    def cold_descs(self, copies):
+        """Descriptor sets over `copies` separate copies of the weights (for a
+        cold-cache timing: consecutive steps read different copies)."""
+        sets = [self.descs]
+        self._cold_w = []
+        for c in range(1, copies):
+            ws = [w.clone() for w in self.w]
+            self._cold_w.append(ws)
+            descs, xoff, yoff = [], 0, 0
+            for (name, n, k, batch), w in zip(self.stacks, ws):
+                nb = k // QK
+                descs.append(self.q.make_desc(
+                    w, (self.xq, xoff), (self.y, yoff), n, k, m=self.m, batch=batch,
+                    w_batch_stride=n * nb, x_row_stride=self.nb_total, x_batch_stride=nb,
+                    y_row_stride=self.n_out, y_batch_stride=n))
+                xoff += batch * nb
+                yoff += batch * n
+            sets.append(descs)
+        return sets
+
     def step_fused(self, x_step):
         """The same step as one launch with the activations quantized inside
         (every wave quantizes the rows it needs; slower here, see the JSON)."""
@@ -192,7 +212,22 @@ def time_steps(plan, xs, steps, warmup):
         for i in range(steps):
             plan.step_fused(xs[i % n_in])
     total_fused = time_graph(capture(all_fused))
-    return dict(total=total, eng=eng, qnt=qnt, total_fused=total_fused)
+
+    # cold reference: consecutive steps read different copies of the weights,
+    # together well over the 256 MB Infinity Cache
+    copies = max(2, -(-3 * 256 * 2**20 // plan.w_bytes))
+    sets = plan.cold_descs(copies)
+
+    def all_cold():
+        for i in range(steps):
+            plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
+            plan.q.q8_0_matmul_batched(sets[i % copies], plan.y)
+    for i in range(copies):
+        plan.q.q8_0_matmul_batched(sets[i], plan.y)
+    total_cold = time_graph(capture(all_cold))
+    plan._cold_w = []
+    return dict(total=total, eng=eng, qnt=qnt, total_fused=total_fused, total_cold=total_cold,
+                copies=copies)
 
 
 # ---------------------------------------------------------------------------
@@ -215,15 +250,15 @@ def cpu_baseline_steps(stacks, m, sample_steps, threads):
                 jobs.append((wl[b], xq, n, k))
                 work_bytes += q8_bytes(n, k) + xq.nbytes + m * n * 4
 
-    def run(job_part):
-        w, xq, n, k, lo, hi = job_part
+    def run(part):
+        w, xq, n, k, lo, hi = part
         oracle.matmul(w, xq, n, k, m, lo, hi)
 
-    parts = []
-    for w, xq, n, k in jobs:
-        step = max(1, -(-n // threads))
-        for lo in range(0, n, step):
-            parts.append((w, xq, n, k, lo, min(n, lo + step)))
+    # the products are independent: they go to the threads whole, the large
+    # ones in slices of 4096 rows (thin row slices of small products cost more
+    # in per-call overhead than they save)
+    parts = [(w, xq, n, k, lo, min(n, lo + 4096)) for w, xq, n, k in jobs
+             for lo in range(0, n, 4096)]
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(run, parts))
@@ -272,6 +307,11 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
                      "avg_launch_us": round(t["eng"] * 1e6, 3),
                      "bytes_per_launch": plan.engine_bytes},
         "quantize_kernel_avg_us": round(t["qnt"] * 1e6, 3),
+        "cold_reference": {
+            "timing": f"the same steps reading {t['copies']} rotating copies of the weights "
+                      f"({t['copies'] * plan.w_bytes / 2**20:.0f} MiB, > the 256 MB Infinity Cache)",
+            "ms_per_step": round(t["total_cold"] / args.steps * 1e3, 5),
+            "gbs": round(bytes_step * args.steps / t["total_cold"] / 1e9, 1)},
         "fused_reference": {
             "timing": "the same steps as one launch each, activations quantized inside it",
             "ms_per_step": round(t["total_fused"] / args.steps * 1e3, 5),
@@ -302,7 +342,18 @@ def run_extra(args, q, synth):
     dev = "cuda"
     wl = args.workload
     res = {"workload": wl, "steps": args.steps, "warmup": args.warmup}
-    if wl == "copy":
+    if wl == "readbw":
+        # achievable read bandwidth for context: the library's plain streaming
+        # read (q8_read_probe) over 2 GiB
+        nbytes = 2 << 30
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+        total = _time_launches(lambda: q.q8_read_probe(src, sink), max(10, args.steps // 10), 3)
+        t = total / max(10, args.steps // 10)
+        res.update(bytes_read_per_launch=nbytes, us_per_read=round(t * 1e6, 2),
+                   gbs=round(nbytes / t / 1e9, 1),
+                   pct_of_hbm_peak=round(nbytes / t / 1e9 / HBM_PEAK_GBS * 100, 2))
+    elif wl == "copy":
         # calibration for hardware byte counters: a plain device-to-device copy of
         # a known size (256 MiB read + 256 MiB written per launch)
         nbytes = 256 << 20
@@ -454,18 +505,29 @@ def rocpd_summary(db):
     return "\n".join(out)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy"])
+                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy", "readbw"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
                     help="c4b1/c4b16: time the layer-after-layer launches, the grouped "
                          "launches, or both")
-    ap.add_argument("--cpu-sample-steps", type=int, default=48)
+    ap.add_argument("--cpu-sample-steps", type=int, default=200)
     ap.add_argument("--traffic", default=None,
                     help="JSON file with the rocprofv3-derived HBM bytes per launch")
     ap.add_argument("--rocpd-summary", default=None, metavar="DB",
@@ -514,13 +576,18 @@ def main():
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         gbs, dt, nbytes = cpu_baseline_steps(stacks, m, args.cpu_sample_steps, threads)
+        gbs1, dt1, nbytes1 = cpu_baseline_steps(stacks, m, max(1, args.cpu_sample_steps // 16), 1)
         out["cpu_baseline"] = {
             "value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{args.cpu_sample_steps} steps of the same workload shapes "
                       f"({nbytes / 1e9:.2f} GB of Q8_0 products, weights and inputs from "
-                      f"the seeded numpy generator), oracle matmul split by rows over "
-                      f"{threads} threads, {dt:.1f} s wall",
+                      f"the seeded numpy generator), oracle products (slices of <= 4096 "
+                      f"rows) spread over {threads} threads, {dt:.1f} s wall",
             "tokens_per_s": round(m * args.cpu_sample_steps / dt, 2),
+            "one_thread": {"value": round(gbs1, 3), "unit": "GB/s",
+                           "sample": f"{max(1, args.cpu_sample_steps // 16)} steps, "
+                                     f"{nbytes1 / 1e9:.2f} GB, {dt1:.1f} s wall"},
+            "cpu_model": cpu_model(),
         }
     print(json.dumps(out))
 

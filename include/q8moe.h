@@ -282,6 +282,14 @@ int moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets,
               int32_t *pairs, int64_t n_tok, int64_t n_expert, int64_t n_used,
               void *ws, size_t ws_bytes, void *stream);
 
+/* q8_read_probe: a plain streaming read of `bytes` bytes at p (16-byte
+ * aligned, a multiple of 16) with the engines' load pattern, the device
+ * analogue of a host memory-bandwidth probe, for reporting the achievable
+ * read rate beside the datasheet peak.  Writes one word per workgroup to sink
+ * (at most 4096 words are used; Q8_E_WORKSPACE if sink_words is too small). */
+int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words,
+                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,7 @@ _SIGS = {
                                         _i64, _vp]),
     "q8_0_matmul_blocksums": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "moe_route": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]),
+    "q8_read_probe": (_int, [_vp, _i64, _vp, _i64, _vp]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -321,6 +322,12 @@ def moe_route(ids, n_expert, ws):
                                        n_tok, n_expert, n_used, _ptr(ws), ws.numel(),
                                        _stream(ids)))
     return counts, offsets, pairs[: n_tok * n_used]
+
+
+def q8_read_probe(buf, sink):
+    """Stream-read the bytes of `buf` (a GPU tensor); sink: int32 GPU tensor."""
+    _check("q8_read_probe", _lib.q8_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
+                                               _ptr(sink), sink.numel(), _stream(buf)))
 
 
 def moe_error_word(ws):

@@ -305,6 +305,15 @@ int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *id
     return moe_down_combine_batched(&d, 1, n_tok, n_ff, n_embd, n_expert, n_used, stream);
 }
 
+int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words, void *stream)
+{
+    if (bytes < 0 || sink_words < 0) return Q8_E_SHAPE;
+    if (bytes == 0) return Q8_OK;
+    if (!p || !sink) return Q8_E_NULL;
+    if (!aligned(p, 16) || bytes % 16 != 0 || !aligned(sink, 4)) return Q8_E_ALIGN;
+    return hip_status(q8::launch_read_probe(p, bytes, sink, sink_words, as_stream(stream)));
+}
+
 int moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *pairs,
               int64_t n_tok, int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
               void *stream)

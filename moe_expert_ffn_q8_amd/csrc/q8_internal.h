@@ -47,6 +47,11 @@ bool gemm_ok(int64_t n, int64_t nb, int64_t m);
 int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t nb, int64_t m,
                 int64_t ldy, hipStream_t stream);
 
+// Streaming-read probe (measurement): reads `bytes` from p, writes one word
+// per workgroup (at most 4096) to sink.
+int launch_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words,
+                      hipStream_t stream);
+
 // Largest dynamic LDS a workgroup may use on the current device.
 int max_lds_bytes();
 

@@ -192,3 +192,12 @@ def test_matmul_f32_checks(lib):
     assert f(None, 1, None) == Q8_E_NULL
     assert f(None, 0, None) == Q8_OK
     assert f(None, -1, None) == Q8_E_SHAPE
+
+
+def test_read_probe_checks(lib):
+    f = lib.q8_read_probe
+    assert f(A, -16, A, 4096, None) == Q8_E_SHAPE
+    assert f(A, 0, None, 0, None) == Q8_OK
+    assert f(None, 1024, A, 4096, None) == Q8_E_NULL
+    assert f(A + 8, 1024, A, 4096, None) == Q8_E_ALIGN
+    assert f(A, 1000, A, 4096, None) == Q8_E_ALIGN

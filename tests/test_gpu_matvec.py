@@ -280,3 +280,19 @@ def test_matmul_f32_fused_many_jobs(q, orc, m):
     q.q8_0_matmul_batched(d2, xg)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_read_probe(q):
+    """The streaming-read probe reads every byte: a buffer whose 16-byte
+    chunks xor to a known word gives that word's fold in the sink."""
+    import torch
+    n = 1 << 22
+    buf = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32)[0] = 0x5A5A5A5A     # one nonzero word in the first range
+    sink = torch.full((4096,), -1, dtype=torch.int32, device="cuda")
+    q.q8_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    s = sink.cpu().numpy()
+    assert s[0] == 0x5A5A5A5A                 # lane 0 folds with lane 1 (which read zeros)
+    assert (s[1:64] == 0).all()               # 64 ranges of 64 KB, the rest read zeros
+    assert (s[64:] == -1).all()               # no workgroup past the buffer
