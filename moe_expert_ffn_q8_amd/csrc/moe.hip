@@ -52,6 +52,20 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kPickRegs = 4;          // slots 0..255: ids preloaded in registers
 constexpr int kPrePass = 4;           // prefetched row blocks per thread (256 threads)
 constexpr int kDnPrePass = 8;         // the same for the 512-thread down kernel
+// With one token (MT == 1 below) the slots name distinct experts, every
+// workgroup owns its slot's expert, and its first weight tile is issued before
+// the ownership scan.  With several tokens a large share of the slots repeat an
+// expert named by an earlier slot (at 16 tokens over 128 experts with 8 per
+// token about a third of them): those workgroups exit after the scan, so the
+// first tile is issued only once ownership is known and the activation image
+// is built (the small loads then also run ahead of the weights).  Measured on
+// 30 layers at 16 tokens: 1975 us per step against 2042 us with the early
+// issue; at one token the early issue is 1% faster.
+template <int MT>
+constexpr bool issue_after_pick()
+{
+    return MT > 1;
+}
 
 struct PickShared {
     int invalid;
@@ -268,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
         tile_issue(We + (int64_t)(real ? j0 : 0) * row_bytes, chunks, lane, gg);
         tile_issue(We + (int64_t)(real ? p.n_ff + j0 : 0) * row_bytes, chunks, lane, gu);
     };
-    issue(t0 + wave, e0_ok && t0 + wave < t1);
+    if (!issue_after_pick<MT>()) issue(t0 + wave, e0_ok && t0 + wave < t1);
     pick_by_slot(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
 
     if (wl == 0) {
@@ -299,6 +313,7 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
         }
         quantize_rows_to_image(L.x, (int64_t)nb * kQK, rows_of, m_begin, mc, nb, ximg, xsc);
         __syncthreads();
+        if (issue_after_pick<MT>() && c0 == 0) issue(t0 + wave, t0 + wave < t1);
 
         uint32_t xr[kQuadDwords];
         float4 xd1 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -401,15 +416,18 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
     const int t1 = min(t0 + p.tiles_per_wg, p.tiles_per_expert);
     const int c = lane % Q;
 
+    // Unconditional issues (a tile that does not exist is a zero-length
+    // buffer), so every wait is an exact count.
     u32x4 g[kTileLoads];
-    auto issue = [&](int tt) {
-        const int r0 = tt * p.R;
-        tile_issue(We + (int64_t)r0 * row_bytes, min(p.R, p.n_rows - r0) * nb * 17 / 8, lane, g);
+    auto issue = [&](int tt, bool real) {
+        const int r0 = real ? tt * p.R : 0;
+        tile_issue(We + (int64_t)r0 * row_bytes, real ? min(p.R, p.n_rows - r0) * nb * 17 / 8 : 0,
+                   lane, g);
     };
     IdsPre ip;
     preload_ids(L.ids, p.n_slots, ip);
     // depends only on ids[slot]: issue before the scan and the h round trip
-    if (e0_ok && t0 + wave < t1) issue(t0 + wave);
+    if (!issue_after_pick<MT>()) issue(t0 + wave, e0_ok && t0 + wave < t1);
     pick_by_slot(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
     if (wl == 0 && tid == 0) *L.err = ps.invalid ? 1 : 0;
     if (ps.expert < 0) return;
@@ -418,11 +436,12 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
     for (int c0 = 0; c0 < count; c0 += MT) {
         const int mc = min(MT, count - c0);
         int t = t0 + wave;
-        if (c0 > 0 && t < t1) issue(t);
+        if (c0 > 0) issue(t, t < t1);
         __syncthreads();
         // quantize the h rows of this chunk's slots into the masked image
         quantize_rows_to_image(L.h, p.n_ff, ps.slots + c0, 0, mc, nb, ximg, xsc);
         __syncthreads();
+        if (issue_after_pick<MT>() && c0 == 0) issue(t, t < t1);
 
         uint32_t xr[kQuadDwords];
         float4 xd1 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
             const int live = rows * Q;
             uint32_t wq[kQuadDwords];
             tile_to_quad(stage, g, lane, live, wq);
-            if (t + kWaves < t1) issue(t + kWaves);
+            issue(t + kWaves, t + kWaves < t1);
             float dw0, dw1, dw2, dw3;
             quad_scales(wq, dw0, dw1, dw2, dw3);
 #pragma unroll
