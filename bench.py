@@ -143,6 +143,14 @@ class StepPlan:
             sets.append(descs)
         return sets
 
+    def step_one(self, x_step):
+        """The same step as one launch in which each activation row is quantized
+        once (q8_0_matmul_f32_step; m <= 2)."""
+        descs = self.descs_f32(x_step)
+        if getattr(self, "_step_ws", None) is None:
+            self._step_ws = self.q.q8_0_matmul_f32_step_workspace(descs, self.y.device)
+        self.q.q8_0_matmul_f32_step(descs, self._step_ws)
+
     def step_fused(self, x_step):
         """The same step as one launch with the activations quantized inside
         (every wave quantizes the rows it needs; slower here, see the JSON)."""
@@ -188,9 +196,12 @@ def time_steps(plan, xs, steps, warmup):
     dict of seconds."""
     import torch
     n_in = xs.shape[0]
+    one = plan.m <= 2
     for i in range(warmup):
         plan.step(xs[i % n_in])
         plan.step_fused(xs[i % n_in])
+        if one:
+            plan.step_one(xs[i % n_in])
     torch.cuda.synchronize()
 
     def all_steps():
@@ -213,6 +224,13 @@ def time_steps(plan, xs, steps, warmup):
             plan.step_fused(xs[i % n_in])
     total_fused = time_graph(capture(all_fused))
 
+    total_one = None
+    if one:
+        def all_one():
+            for i in range(steps):
+                plan.step_one(xs[i % n_in])
+        total_one = time_graph(capture(all_one))
+
     # cold reference: consecutive steps read different copies of the weights,
     # together well over the 256 MB Infinity Cache
     copies = max(2, -(-3 * 256 * 2**20 // plan.w_bytes))
@@ -227,7 +245,7 @@ def time_steps(plan, xs, steps, warmup):
     total_cold = time_graph(capture(all_cold))
     plan._cold_w = []
     return dict(total=total, eng=eng, qnt=qnt, total_fused=total_fused, total_cold=total_cold,
-                copies=copies)
+                copies=copies, total_one=total_one)
 
 
 # ---------------------------------------------------------------------------
@@ -317,6 +335,12 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
             "ms_per_step": round(t["total_fused"] / args.steps * 1e3, 5),
             "gbs": round(plan.fused_bytes * args.steps / t["total_fused"] / 1e9, 1)},
     }
+    if t["total_one"] is not None:
+        out["one_launch_reference"] = {
+            "timing": "the same steps as one launch each, every activation row quantized once "
+                      "inside it by the launch's first workgroups",
+            "ms_per_step": round(t["total_one"] / args.steps * 1e3, 5),
+            "gbs": round(plan.fused_bytes * args.steps / t["total_one"] / 1e9, 1)}
     return out, plan
 
 
@@ -383,8 +407,12 @@ def run_extra(args, q, synth):
         fd = [q.make_f32_desc(w, xf, y, n, k)]
         tf = _time_launches(lambda: q.q8_0_matmul_f32_batched(fd, w), args.steps,
                             args.warmup) / args.steps
+        sws = q.q8_0_matmul_f32_step_workspace(fd, dev)
+        ts = _time_launches(lambda: q.q8_0_matmul_f32_step(fd, sws), args.steps,
+                            args.warmup) / args.steps
         res.update(from_fp32={"us_quantize_then_matvec": round(t2 * 1e6, 3),
-                              "us_fused": round(tf * 1e6, 3)})
+                              "us_fused": round(tf * 1e6, 3),
+                              "us_one_launch_quantize_once": round(ts * 1e6, 3)})
     elif wl == "c5a":
         m, n, k = 512, 14336, 4096
         w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w"))

@@ -171,6 +171,35 @@ typedef struct {
 
 int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *stream);
 
+/* q8_0_matmul_f32_step: the products of q8_0_matmul_f32_batched (same
+ * descriptors and rules) for m <= 2, as one launch in which every activation
+ * row is quantized once: the first workgroups quantize the rows into the
+ * workspace, and each product tile waits (on a per-row ready counter in the
+ * workspace) for the rows it reads.  This is the whole decode step of the
+ * narray-llm README's Llama 2 110M int8 table (every matvec's input
+ * re-quantized, [NARR] sections on the measurement and on kernels per token)
+ * in one launch.  Results are bitwise equal to q8_0_quantize_rows followed by
+ * q8_0_matmul_batched.
+ *   m > 2 for any descriptor: Q8_E_UNSUPPORTED (use q8_0_matmul_f32_batched).
+ * Workspace: device memory of at least q8_0_matmul_f32_step_ws_bytes(descs,
+ * n_desc) bytes, 256-byte aligned, ZERO-FILLED before its first use.  Every
+ * call that completes leaves its counters at zero again, so it can be reused
+ * (also across replays of a captured graph) without clearing.  After a call:
+ *   - int32 at byte 0 is the error word: 1 if a tile's bounded wait for its
+ *     rows ran out (the outputs of that call are then invalid); the library
+ *     never clears it (zero-fill the workspace again after reading 1);
+ *   - the quantized rows of descriptor i start at byte
+ *     256 + sum over j < i of align256(batch_j * m_j * k_j/32 * 34), batch
+ *     entry b at b * m_i * k_i/32 * 34 within them (the bytes of
+ *     q8_0_quantize_rows); the counters and flags follow the rows.
+ * One workspace must not be shared by calls that may run concurrently.
+ * q8_0_matmul_f32_step_ws_bytes returns the byte count, or a negative status
+ * for descriptors q8_0_matmul_f32_step would reject. */
+int64_t q8_0_matmul_f32_step_ws_bytes(const q8_0_matmul_f32_desc *descs, int64_t n_desc);
+
+int q8_0_matmul_f32_step(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *ws,
+                         int64_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Mixture-of-experts expert FFN ([XEON] sections on the broken op paths and on
  * the three-part fix, runtime graph fallback).  Per token t and active slot

@@ -8,12 +8,14 @@ from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDes
                    Q8MatmulDesc, Q8MatmulF32Desc, make_desc, make_f32_desc, moe_down_combine, moe_down_combine_batched,
                    moe_error_word, moe_route, moe_up_gate_swiglu, moe_up_gate_swiglu_batched,
                    moe_workspace, moe_workspace_bytes, q8_0_matmul, q8_0_matmul_batched,
-                   q8_0_matmul_blocksums, q8_0_matmul_f32_batched, q8_0_matvec,
+                   q8_0_matmul_blocksums, q8_0_matmul_f32_batched, q8_0_matmul_f32_step,
+                   q8_0_matmul_f32_step_workspace, q8_0_matmul_f32_step_ws_bytes, q8_0_matvec,
                    q8_0_quantize_rows, q8_empty, q8_read_probe, raw, status_str, version)
 
 __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGateDesc", "Q8Error",
            "Q8MatmulDesc", "Q8MatmulF32Desc", "make_desc", "make_f32_desc", "moe_down_combine", "moe_down_combine_batched",
            "moe_error_word", "moe_route", "moe_up_gate_swiglu", "moe_up_gate_swiglu_batched",
            "moe_workspace", "moe_workspace_bytes", "q8_0_matmul", "q8_0_matmul_batched",
-           "q8_0_matmul_blocksums", "q8_0_matmul_f32_batched", "q8_0_matvec", "q8_0_quantize_rows", "q8_empty", "q8_read_probe", "raw",
+           "q8_0_matmul_blocksums", "q8_0_matmul_f32_batched", "q8_0_matmul_f32_step",
+           "q8_0_matmul_f32_step_workspace", "q8_0_matmul_f32_step_ws_bytes", "q8_0_matvec", "q8_0_quantize_rows", "q8_empty", "q8_read_probe", "raw",
            "status_str", "version"]

@@ -63,6 +63,8 @@ _SIGS = {
     "q8_0_matmul": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q8_0_matmul_batched": (_int, [ctypes.POINTER(Q8MatmulDesc), _i64, _vp]),
     "q8_0_matmul_f32_batched": (_int, [ctypes.POINTER(Q8MatmulF32Desc), _i64, _vp]),
+    "q8_0_matmul_f32_step_ws_bytes": (_i64, [ctypes.POINTER(Q8MatmulF32Desc), _i64]),
+    "q8_0_matmul_f32_step": (_int, [ctypes.POINTER(Q8MatmulF32Desc), _i64, _vp, _i64, _vp]),
     "moe_workspace_bytes": (_size, [_i64, _i64, _i64, _i64, _i64]),
     "moe_up_gate_swiglu": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                   _size, _vp]),
@@ -213,6 +215,30 @@ def q8_0_matmul_f32_batched(descs, stream_of):
     arr = (Q8MatmulF32Desc * len(descs))(*descs)
     _check("q8_0_matmul_f32_batched",
            _lib.q8_0_matmul_f32_batched(arr, len(descs), _stream(stream_of)))
+
+
+def q8_0_matmul_f32_step_ws_bytes(descs):
+    """Workspace bytes q8_0_matmul_f32_step needs for these descriptors."""
+    arr = (Q8MatmulF32Desc * max(1, len(descs)))(*descs)
+    n = int(_lib.q8_0_matmul_f32_step_ws_bytes(arr, len(descs)))
+    if n < 0:
+        raise Q8Error("q8_0_matmul_f32_step_ws_bytes", n)
+    return n
+
+
+def q8_0_matmul_f32_step_workspace(descs, device):
+    """A zero-filled workspace for q8_0_matmul_f32_step (uint8 tensor)."""
+    n = q8_0_matmul_f32_step_ws_bytes(descs)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def q8_0_matmul_f32_step(descs, ws, stream_of=None):
+    """descs: list of Q8MatmulF32Desc (m <= 2); ws: the zero-filled uint8
+    workspace tensor (reused across calls)."""
+    _need(ws, torch.uint8, "ws")
+    arr = (Q8MatmulF32Desc * max(1, len(descs)))(*descs)
+    _check("q8_0_matmul_f32_step", _lib.q8_0_matmul_f32_step(
+        arr, len(descs), _ptr(ws), ws.numel(), _stream(ws if stream_of is None else stream_of)))
 
 
 def q8_0_matmul_blocksums(w, x, n, k, m):

@@ -151,19 +151,23 @@ int q8_0_matmul_batched(const q8_0_matmul_desc *descs, int64_t n_desc, void *str
     return hip_status(q8::launch_stream(d, nd, as_stream(stream)));
 }
 
-int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *stream)
+}  // extern "C"
+
+// Validation shared by the fp32-activation entry points: fills d[0..nd) with
+// the descriptors that have work; step = the one-launch step form (m <= 2).
+static int f32_descs(const q8_0_matmul_f32_desc *descs, int64_t n_desc, bool step,
+                     q8::StreamDesc *d, int &nd)
 {
+    nd = 0;
     if (n_desc < 0) return Q8_E_SHAPE;
     if (n_desc == 0) return Q8_OK;
     if (!descs) return Q8_E_NULL;
     if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
-    q8::StreamDesc d[q8::kStreamMaxJobs];
-    int nd = 0;
     for (int64_t i = 0; i < n_desc; ++i) {
         const q8_0_matmul_f32_desc &s = descs[i];
         if (int rc = check_k(s.k)) return rc;
         if (s.n < 0 || s.m < 0 || s.batch < 0) return Q8_E_SHAPE;
-        if (s.m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
+        if (s.m > (step ? 2 : q8::kStreamMaxM)) return Q8_E_UNSUPPORTED;
         if (s.n == 0 || s.m == 0 || s.batch == 0) continue;
         if (!s.w || !s.x || !s.y) return Q8_E_NULL;
         const int64_t nb = s.k / kQK;
@@ -187,9 +191,41 @@ int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, v
         o.y_bstride = s.y_batch_stride;
         o.x_f32 = 1;
         // the fused quantization exists in the streaming engines only
-        if (!q8::stream_fast_ok(o)) return Q8_E_UNSUPPORTED;
+        if (step ? !q8::step_ok(o) : !q8::stream_fast_ok(o)) return Q8_E_UNSUPPORTED;
     }
+    return Q8_OK;
+}
+
+extern "C" {
+
+int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *stream)
+{
+    q8::StreamDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    if (int rc = f32_descs(descs, n_desc, false, d, nd)) return rc;
+    if (nd == 0) return Q8_OK;
     return hip_status(q8::launch_stream(d, nd, as_stream(stream)));
+}
+
+int64_t q8_0_matmul_f32_step_ws_bytes(const q8_0_matmul_f32_desc *descs, int64_t n_desc)
+{
+    q8::StreamDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    if (int rc = f32_descs(descs, n_desc, true, d, nd)) return rc;
+    return (int64_t)q8::step_ws_bytes(d, nd);
+}
+
+int q8_0_matmul_f32_step(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void *ws,
+                         int64_t ws_bytes, void *stream)
+{
+    q8::StreamDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    if (int rc = f32_descs(descs, n_desc, true, d, nd)) return rc;
+    if (nd == 0) return Q8_OK;
+    if (!ws) return Q8_E_WORKSPACE;
+    if (!aligned(ws, 256)) return Q8_E_ALIGN;
+    if (ws_bytes < 0 || (uint64_t)ws_bytes < q8::step_ws_bytes(d, nd)) return Q8_E_WORKSPACE;
+    return hip_status(q8::launch_step(d, nd, ws, as_stream(stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -179,6 +179,34 @@ __device__ __forceinline__ void lds_quad(const uint8_t *p, uint32_t (&q)[kQuadDw
     }
 }
 
+// Load one activation quad (136 B) into registers as a masked image + scales.
+__device__ __forceinline__ void load_x_quad(const uint8_t *p, bool al8, uint32_t (&q)[kQuadDwords],
+                                            float4 &d)
+{
+    if (al8) {
+        const u32x2 *src = (const u32x2 *)p;
+#pragma unroll
+        for (int v = 0; v < 17; ++v) {
+            const u32x2 t = src[v];
+            q[2 * v] = t.x;
+            q[2 * v + 1] = t.y;
+        }
+    } else {
+        const uint16_t *src = (const uint16_t *)p;
+#pragma unroll
+        for (int v = 0; v < kQuadDwords; ++v)
+            q[v] = (uint32_t)src[2 * v] | ((uint32_t)src[2 * v + 1] << 16);
+    }
+    d.x = half_bits_to_float(q[0]);
+    d.y = half_bits_to_float(q[8] >> 16);
+    d.z = half_bits_to_float(q[17]);
+    d.w = half_bits_to_float(q[25] >> 16);
+    q[0] &= 0xffff0000u;
+    q[8] &= 0x0000ffffu;
+    q[17] &= 0xffff0000u;
+    q[25] &= 0x0000ffffu;
+}
+
 // fp32 contribution of one quad: sum_b (d_w,b * d_x,b) * s_b, in block order.
 __device__ __forceinline__ float quad_dot(const uint32_t (&wq)[kQuadDwords],
                                           const uint32_t *xq, float dw0, float dw1, float dw2,

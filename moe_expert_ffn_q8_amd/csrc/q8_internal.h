@@ -39,6 +39,13 @@ bool small_m_ok(const StreamDesc *d, int n);
 size_t small_m_lds_bytes(int64_t m, int64_t nb);
 int launch_small_m(const StreamDesc *d, int n, hipStream_t stream);
 
+// One-launch decode step from fp32 activations (m <= 2, fast shapes): the
+// rows are quantized once into the workspace by the first workgroups of the
+// launch, the product tiles wait for their entry's rows.
+bool step_ok(const StreamDesc &d);
+size_t step_ws_bytes(const StreamDesc *d, int n);
+int launch_step(const StreamDesc *d, int n, void *ws, hipStream_t stream);
+
 int launch_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_rows,
                          int64_t k, hipStream_t stream);
 

@@ -221,34 +221,6 @@ struct FlatArgs {
 
 static_assert(sizeof(FlatArgs) <= 4000, "kernel arguments must stay below 4 KB");
 
-// Load one activation quad (136 B) into registers as a masked image + scales.
-__device__ __forceinline__ void load_x_quad(const uint8_t *p, bool al8, uint32_t (&q)[kQuadDwords],
-                                            float4 &d)
-{
-    if (al8) {
-        const u32x2 *src = (const u32x2 *)p;
-#pragma unroll
-        for (int v = 0; v < 17; ++v) {
-            const u32x2 t = src[v];
-            q[2 * v] = t.x;
-            q[2 * v + 1] = t.y;
-        }
-    } else {
-        const uint16_t *src = (const uint16_t *)p;
-#pragma unroll
-        for (int v = 0; v < kQuadDwords; ++v)
-            q[v] = (uint32_t)src[2 * v] | ((uint32_t)src[2 * v + 1] << 16);
-    }
-    d.x = half_bits_to_float(q[0]);
-    d.y = half_bits_to_float(q[8] >> 16);
-    d.z = half_bits_to_float(q[17]);
-    d.w = half_bits_to_float(q[25] >> 16);
-    q[0] &= 0xffff0000u;
-    q[8] &= 0x0000ffffu;
-    q[17] &= 0xffff0000u;
-    q[25] &= 0x0000ffffu;
-}
-
 // fp32 activations (XF): the wave quantizes the M rows of a (job, batch entry)
 // into its LDS image, 8 lanes per block with the activation rule (the bytes
 // are those of q8_0_quantize_rows), then every lane takes its quad.  The first

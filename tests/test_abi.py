@@ -43,6 +43,7 @@ def test_status_strings(lib):
 
 
 A = 1 << 20          # a fake, suitably aligned address: never dereferenced
+WS = 1 << 24         # a fake 256-byte-aligned workspace address (never dereferenced)
 
 
 def test_quantize_rows_checks(lib):
@@ -192,6 +193,50 @@ def test_matmul_f32_checks(lib):
     assert f(None, 1, None) == Q8_E_NULL
     assert f(None, 0, None) == Q8_OK
     assert f(None, -1, None) == Q8_E_SHAPE
+
+
+def test_matmul_f32_step_checks(lib):
+    """One-launch step: host checks and the workspace size (no launch without
+    a GPU)."""
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_0_matmul_f32_step
+    g = lib.q8_0_matmul_f32_step_ws_bytes
+
+    def desc(**kw):
+        base = dict(w=A, x=A, y=A, n=64, k=768, m=1, batch=1, w_batch_stride=0, x_row_stride=768,
+                    x_batch_stride=0, y_row_stride=64, y_batch_stride=0)
+        base.update(kw)
+        return q.Q8MatmulF32Desc(*[base[k] for k, _ in q.Q8MatmulF32Desc._fields_])
+
+    def arr(*ds):
+        return (q.Q8MatmulF32Desc * len(ds))(*ds)
+
+    def call(ws=WS, ws_bytes=1 << 20, **kw):
+        return f(arr(desc(**kw)), 1, ws, ws_bytes, None)
+
+    # workspace: 256 B header, each descriptor's quantized rows (256-aligned),
+    # 256 B of counter per batch entry, an int32 flag per tile (256-aligned);
+    # a tile is 64 / (k/128) rows
+    assert g(arr(desc()), 1) == 256 + 1024 + 256 + 256         # 24 blocks = 816 B; 7 tiles
+    two = arr(desc(batch=40, w_batch_stride=64 * 24, x_batch_stride=768, y_batch_stride=64),
+              desc(n=10, k=2048, m=2, x_row_stride=2048, y_row_stride=10))
+    img = (40 * 24 * 34 + 255) // 256 * 256 + (2 * 64 * 34 + 255) // 256 * 256
+    tiles = 40 * 7 + 3                                          # R = 10 and R = 4
+    assert g(two, 2) == 256 + img + 41 * 256 + (4 * tiles + 255) // 256 * 256
+    assert g(arr(desc(m=3, x_row_stride=768, y_row_stride=64)), 1) == Q8_E_UNSUPPORTED
+    assert g(None, 0) == 256
+    assert call(m=3, x_row_stride=768) == Q8_E_UNSUPPORTED     # m <= 2 only
+    assert call(k=96) == Q8_E_UNSUPPORTED
+    assert call(k=100) == Q8_E_SHAPE
+    assert call(x=A + 4) == Q8_E_ALIGN
+    assert call(y=None) == Q8_E_NULL
+    assert call(ws=None) == Q8_E_WORKSPACE
+    assert call(ws_bytes=1791) == Q8_E_WORKSPACE
+    assert call(ws=WS + 16) == Q8_E_ALIGN
+    assert call(n=0, ws=None) == Q8_OK                          # nothing to do
+    assert f(None, 0, None, 0, None) == Q8_OK
+    assert f(None, 1, WS, 1 << 20, None) == Q8_E_NULL
+    assert f(None, -1, WS, 1 << 20, None) == Q8_E_SHAPE
 
 
 def test_read_probe_checks(lib):
