@@ -413,6 +413,51 @@ def run_extra(args, q, synth):
         res.update(from_fp32={"us_quantize_then_matvec": round(t2 * 1e6, 3),
                               "us_fused": round(tf * 1e6, 3),
                               "us_one_launch_quantize_once": round(ts * 1e6, 3)})
+    elif wl == "ffn":
+        # dense FFN up_gate + SwiGLU of the Llama-2-110M layers (n_embd 768,
+        # n_ff 2048, 12 layers in one launch, batch 1): fused launch against the
+        # two-product form (one batched product over both halves + elementwise)
+        L, n_ff, k = 12, 2048, 768
+        nb = k // QK
+        w = q.q8_0_quantize_rows(synth.normal_f32_torch((L * 2 * n_ff, k), 0.02, dev, 0, wl, "w"))
+        x = q.q8_0_quantize_rows(synth.normal_f32_torch((1, L * k), 1.0, dev, 0, wl, "x"))
+        h = torch.empty((1, L * n_ff), dtype=torch.float32, device=dev)
+        d = [q.make_up_gate_desc(w, x, h, n_ff, k, batch=L, w_batch_stride=2 * n_ff * nb,
+                                 x_batch_stride=nb, h_batch_stride=n_ff)]
+        total = _time_launches(lambda: q.q8_0_up_gate_swiglu_batched(d, w), args.steps, args.warmup)
+        t = total / args.steps
+        nbytes = q8_bytes(L * 2 * n_ff, k) + q8_bytes(L, k) + 4 * L * n_ff
+        y = torch.empty((1, L * 2 * n_ff), dtype=torch.float32, device=dev)
+        d2 = [q.make_desc(w, x, y, 2 * n_ff, k, batch=L, w_batch_stride=2 * n_ff * nb,
+                          x_batch_stride=nb, y_batch_stride=2 * n_ff)]
+        yv = y.view(L, 2, n_ff)
+        hv = h.view(L, n_ff)
+
+        def two_product():
+            q.q8_0_matmul_batched(d2, w)
+            torch.mul(torch.nn.functional.silu(yv[:, 0]), yv[:, 1], out=hv)
+        t2 = _time_launches(two_product, args.steps, args.warmup) / args.steps
+        res.update(shape={"layers": L, "n_ff": n_ff, "n_embd": k, "batch": 1},
+                   us_per_launch=round(t * 1e6, 3), gbs=round(nbytes / t / 1e9, 1),
+                   pct_of_hbm_peak=round(nbytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
+                   bytes_per_launch=nbytes,
+                   two_product_reference={"us": round(t2 * 1e6, 3),
+                                          "timing": "q8_0_matmul_batched over both halves, "
+                                                    "then torch silu and multiply"})
+        if not args.no_cpu_baseline:
+            # the oracle's dense up_gate on the same 12 layers (seeded numpy
+            # inputs of the same shapes), one host thread
+            import oracle
+            wl_h = [oracle.quantize_rows(synth.normal_f32((2 * n_ff, k), 0.02, "cpu-ffn", i))
+                    for i in range(L)]
+            xs_h = [oracle.quantize_rows(synth.normal_f32((1, k), 1.0, "cpu-ffn-x", i))
+                    for i in range(L)]
+            t0 = time.perf_counter()
+            for wi, xi in zip(wl_h, xs_h):
+                oracle.up_gate_swiglu(wi, xi, k, n_ff)
+            dt = time.perf_counter() - t0
+            res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                   "kind": "oracle", "sample": f"the 12 layers once, {dt:.2f} s"}
     elif wl == "c5a":
         m, n, k = 512, 14336, 4096
         w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w"))
@@ -550,7 +595,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy", "readbw"])
+                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy", "readbw", "ffn"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
                     help="c4b1/c4b16: time the layer-after-layer launches, the grouped "

@@ -201,6 +201,38 @@ int q8_0_matmul_f32_step(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void
                          int64_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * q8_0_up_gate_swiglu_batched -- the dense FFN up_gate with SwiGLU in one pass
+ * (FUSED_UP_GATE, named beside MOE_FUSED_UP_GATE in the [XEON] section on the
+ * broken op paths; the split form two products + silu(gate)*up is the one the
+ * [XEON] three-part fix, runtime graph fallback, builds).  Descriptor i
+ * computes, for every b < batch and token row t < m:
+ *   h_b[t][j] = silu(W_b[j] . X_b[t]) * (W_b[n_ff + j] . X_b[t]),  j < n_ff
+ * with silu(g) = g / (1 + exp(-g)) in fp32, W_b = w + b*w_batch_stride (blocks),
+ * the combined weight [2*n_ff][n_embd/32] with the gate rows first (16-byte
+ * aligned), X_b row t = x + b*x_batch_stride + t*x_row_stride (Q8_0 blocks, as
+ * q8_0_quantize_rows writes them), h_b row t = h + b*h_batch_stride +
+ * t*h_row_stride (floats, written).  Each gate and up sum is bitwise the
+ * q8_0_matmul_batched result for that row.
+ * Limits: m <= 2 (Q8_E_UNSUPPORTED above); n_embd/32 a multiple of 8 and
+ * n_embd <= 8192, w_batch_stride*34 a multiple of 16 (else Q8_E_UNSUPPORTED /
+ * Q8_E_ALIGN); n_desc <= 32.  With batch > 1: w_batch_stride >= 2*n_ff*n_embd/32
+ * and h_batch_stride >= n_ff (Q8_E_SHAPE).  descs is a HOST array.
+ */
+typedef struct q8_0_up_gate_desc {
+    const q8_0_block *w;
+    const q8_0_block *x;
+    float *h;
+    int64_t n_ff, n_embd, m, batch;
+    int64_t w_batch_stride;   /* blocks */
+    int64_t x_row_stride;     /* blocks, >= n_embd/32 when m > 1 */
+    int64_t x_batch_stride;   /* blocks */
+    int64_t h_row_stride;     /* floats, >= n_ff when m > 1 */
+    int64_t h_batch_stride;   /* floats */
+} q8_0_up_gate_desc;
+
+int q8_0_up_gate_swiglu_batched(const q8_0_up_gate_desc *descs, int64_t n_desc, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Mixture-of-experts expert FFN ([XEON] sections on the broken op paths and on
  * the three-part fix, runtime graph fallback).  Per token t and active slot
  * u < n_used with expert e = ids[t][u]:

@@ -5,7 +5,8 @@ in include/q8moe.h); this package is its thin Python binding.  Importing it
 fails if the library has not been built: there is no CPU fallback.
 """
 from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDesc, Q8Error,
-                   Q8MatmulDesc, Q8MatmulF32Desc, make_desc, make_f32_desc, moe_down_combine, moe_down_combine_batched,
+                   Q8MatmulDesc, Q8MatmulF32Desc, Q8UpGateDesc, make_desc, make_f32_desc,
+                   make_up_gate_desc, q8_0_up_gate_swiglu_batched, moe_down_combine, moe_down_combine_batched,
                    moe_error_word, moe_route, moe_up_gate_swiglu, moe_up_gate_swiglu_batched,
                    moe_workspace, moe_workspace_bytes, q8_0_matmul, q8_0_matmul_batched,
                    q8_0_matmul_blocksums, q8_0_matmul_f32_batched, q8_0_matmul_f32_step,
@@ -13,7 +14,8 @@ from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDes
                    q8_0_quantize_rows, q8_empty, q8_read_probe, raw, status_str, version)
 
 __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGateDesc", "Q8Error",
-           "Q8MatmulDesc", "Q8MatmulF32Desc", "make_desc", "make_f32_desc", "moe_down_combine", "moe_down_combine_batched",
+           "Q8MatmulDesc", "Q8MatmulF32Desc", "Q8UpGateDesc", "make_desc", "make_f32_desc",
+           "make_up_gate_desc", "q8_0_up_gate_swiglu_batched", "moe_down_combine", "moe_down_combine_batched",
            "moe_error_word", "moe_route", "moe_up_gate_swiglu", "moe_up_gate_swiglu_batched",
            "moe_workspace", "moe_workspace_bytes", "q8_0_matmul", "q8_0_matmul_batched",
            "q8_0_matmul_blocksums", "q8_0_matmul_f32_batched", "q8_0_matmul_f32_step",

@@ -38,6 +38,13 @@ class Q8MatmulDesc(ctypes.Structure):
                 ("y_row_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class Q8UpGateDesc(ctypes.Structure):
+    _fields_ = [("w", _vp), ("x", _vp), ("h", _vp),
+                ("n_ff", _i64), ("n_embd", _i64), ("m", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_row_stride", _i64), ("x_batch_stride", _i64),
+                ("h_row_stride", _i64), ("h_batch_stride", _i64)]
+
+
 class Q8MatmulF32Desc(ctypes.Structure):
     _fields_ = [("w", _vp), ("x", _vp), ("y", _vp),
                 ("n", _i64), ("k", _i64), ("m", _i64), ("batch", _i64),
@@ -63,6 +70,7 @@ _SIGS = {
     "q8_0_matmul": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q8_0_matmul_batched": (_int, [ctypes.POINTER(Q8MatmulDesc), _i64, _vp]),
     "q8_0_matmul_f32_batched": (_int, [ctypes.POINTER(Q8MatmulF32Desc), _i64, _vp]),
+    "q8_0_up_gate_swiglu_batched": (_int, [ctypes.POINTER(Q8UpGateDesc), _i64, _vp]),
     "q8_0_matmul_f32_step_ws_bytes": (_i64, [ctypes.POINTER(Q8MatmulF32Desc), _i64]),
     "q8_0_matmul_f32_step": (_int, [ctypes.POINTER(Q8MatmulF32Desc), _i64, _vp, _i64, _vp]),
     "moe_workspace_bytes": (_size, [_i64, _i64, _i64, _i64, _i64]),
@@ -187,6 +195,29 @@ def make_desc(w, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
                         w_batch_stride, nb if x_row_stride is None else x_row_stride,
                         x_batch_stride, n if y_row_stride is None else y_row_stride,
                         y_batch_stride)
+
+
+def make_up_gate_desc(w, x, h, n_ff, n_embd, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
+                      x_batch_stride=0, h_row_stride=None, h_batch_stride=0):
+    """One q8_0_up_gate_desc.  w (combined [2*n_ff][n_embd/32] blocks, gate rows
+    first), x (Q8_0 rows), h are (tensor, element offset) pairs or tensors;
+    strides are in blocks (w, x) and floats (h)."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    nb = n_embd // QK
+    return Q8UpGateDesc(addr(w, BLOCK_BYTES), addr(x, BLOCK_BYTES), addr(h, 4), n_ff, n_embd, m,
+                        batch, w_batch_stride, nb if x_row_stride is None else x_row_stride,
+                        x_batch_stride, n_ff if h_row_stride is None else h_row_stride,
+                        h_batch_stride)
+
+
+def q8_0_up_gate_swiglu_batched(descs, stream_of):
+    """descs: list of Q8UpGateDesc; stream_of: a tensor on the target device."""
+    arr = (Q8UpGateDesc * max(1, len(descs)))(*descs)
+    _check("q8_0_up_gate_swiglu_batched",
+           _lib.q8_0_up_gate_swiglu_batched(arr, len(descs), _stream(stream_of)))
 
 
 def q8_0_matmul_batched(descs, stream_of):

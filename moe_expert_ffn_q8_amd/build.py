@@ -18,8 +18,8 @@ LIB = os.path.join(HERE, "libq8moe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "stream.hip", "step.hip", "small_m.hip", "moe.hip", "gemm.hip",
-           "probe.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "stream.hip", "step.hip", "ffn.hip", "small_m.hip", "moe.hip",
+           "gemm.hip", "probe.hip", "abi.cpp"]
 
 # no packed fp32 instructions in device code; MFMA results in VGPRs (the
 # rescale of each int32 block tile then needs no accumulator-register copies)

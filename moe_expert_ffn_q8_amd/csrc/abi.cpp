@@ -228,6 +228,46 @@ int q8_0_matmul_f32_step(const q8_0_matmul_f32_desc *descs, int64_t n_desc, void
     return hip_status(q8::launch_step(d, nd, ws, as_stream(stream)));
 }
 
+int q8_0_up_gate_swiglu_batched(const q8_0_up_gate_desc *descs, int64_t n_desc, void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    q8::StreamDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    for (int64_t i = 0; i < n_desc; ++i) {
+        const q8_0_up_gate_desc &s = descs[i];
+        if (int rc = check_k(s.n_embd)) return rc;
+        if (s.n_ff < 0 || s.m < 0 || s.batch < 0) return Q8_E_SHAPE;
+        if (s.m > 2) return Q8_E_UNSUPPORTED;
+        if (s.n_ff == 0 || s.m == 0 || s.batch == 0) continue;
+        if (!s.w || !s.x || !s.h) return Q8_E_NULL;
+        const int64_t nb = s.n_embd / kQK;
+        if (s.m > 1 && (s.x_row_stride < nb || s.h_row_stride < s.n_ff)) return Q8_E_SHAPE;
+        if (s.batch > 1 && (s.w_batch_stride < 2 * s.n_ff * nb || s.x_batch_stride < 0 ||
+                            s.h_batch_stride < s.n_ff))
+            return Q8_E_SHAPE;
+        if (!aligned(s.w, 16) || !aligned(s.x, 2) || !aligned(s.h, 4) ||
+            (s.batch > 1 && (s.w_batch_stride * kBB) % 16 != 0))
+            return Q8_E_ALIGN;
+        q8::StreamDesc &o = d[nd++];
+        memset(&o, 0, sizeof(o));
+        o.w = (const uint8_t *)s.w;
+        o.x = (const uint8_t *)s.x;
+        o.y = s.h;
+        o.n = s.n_ff; o.nb = nb; o.m = s.m; o.batch = s.batch;
+        o.w_bstride = s.w_batch_stride * kBB;
+        o.x_rstride = s.x_row_stride * kBB;
+        o.x_bstride = s.x_batch_stride * kBB;
+        o.y_rstride = s.h_row_stride;
+        o.y_bstride = s.h_batch_stride;
+        if (!q8::stream_fast_ok(o)) return Q8_E_UNSUPPORTED;
+    }
+    if (nd == 0) return Q8_OK;
+    return hip_status(q8::launch_dense_up_gate(d, nd, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------------------
 // Mixture of experts
 

@@ -46,6 +46,9 @@ bool step_ok(const StreamDesc &d);
 size_t step_ws_bytes(const StreamDesc *d, int n);
 int launch_step(const StreamDesc *d, int n, void *ws, hipStream_t stream);
 
+// Dense FFN up_gate + SwiGLU (m <= 2, fast shapes): d[i].n = n_ff, d[i].y = h.
+int launch_dense_up_gate(const StreamDesc *d, int n, hipStream_t stream);
+
 int launch_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_rows,
                          int64_t k, hipStream_t stream);
 

@@ -15,6 +15,8 @@ Parity status of each function (the pins live in tests/test_oracle_*.py):
                                   dequantize-then-fp64 matmul)
   moe_up_gate_swiglu ........... pinned (split-path identity, dense special
                                   case, dequantized fp64 brute force)
+  up_gate_swiglu (dense) ....... pinned (split form, dequantized fp64 brute
+                                  force, exact small case)
   moe_route .................... pinned (invariants, brute force)
   moe_down_combine ............. pinned (one-hot / single-expert reductions,
                                   dequantized fp64 brute force)
@@ -239,6 +241,19 @@ def moe_up_gate_swiglu_split(w_ug, x, ids, n_embd, n_ff, n_expert):
     g = mul_mat_id(w_ug, 2 * n_ff, 0, n_ff, x, ids, n_embd, n_expert)
     u = mul_mat_id(w_ug, 2 * n_ff, n_ff, n_ff, x, ids, n_embd, n_expert)
     return fused_mul_silu(g, u).reshape(g.shape)
+
+
+def up_gate_swiglu(w_ug, x, n_embd, n_ff):
+    """Dense FFN up_gate: h[t][j] (fp64) = silu(W[j] . x_t) * (W[n_ff + j] . x_t)
+    for one combined weight [2*n_ff][n_embd] (gate rows first) and Q8_0 rows
+    x [m][n_embd/32] -- the MoE form with a single expert that every token
+    uses (FUSED_UP_GATE beside MOE_FUSED_UP_GATE on the Gemma-4-on-Xeon page,
+    section on the broken op paths)."""
+    nb = n_embd // QK
+    x = _blocks(x)
+    m = x.size // (nb * BLOCK_BYTES)
+    ids = np.zeros((m, 1), dtype=np.int32)
+    return moe_up_gate_swiglu(w_ug, x, ids, n_embd, n_ff, 1)[:, 0, :]
 
 
 def moe_route(ids, n_expert):

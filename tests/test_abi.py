@@ -239,6 +239,38 @@ def test_matmul_f32_step_checks(lib):
     assert f(None, -1, WS, 1 << 20, None) == Q8_E_SHAPE
 
 
+def test_up_gate_checks(lib):
+    """Dense up_gate: host checks (no launch without a GPU)."""
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_0_up_gate_swiglu_batched
+
+    def call(**kw):
+        base = dict(w=A, x=A, h=A, n_ff=64, n_embd=768, m=1, batch=1, w_batch_stride=0,
+                    x_row_stride=24, x_batch_stride=0, h_row_stride=64, h_batch_stride=0)
+        base.update(kw)
+        d = q.Q8UpGateDesc(*[base[k] for k, _ in q.Q8UpGateDesc._fields_])
+        return f((q.Q8UpGateDesc * 1)(d), 1, None)
+
+    assert call(n_embd=100) == Q8_E_SHAPE
+    assert call(n_ff=-1) == Q8_E_SHAPE
+    assert call(m=3) == Q8_E_UNSUPPORTED
+    assert call(n_embd=96) == Q8_E_UNSUPPORTED          # k/32 not a multiple of 8
+    assert call(n_embd=16384) == Q8_E_UNSUPPORTED
+    assert call(w=A + 2) == Q8_E_ALIGN
+    assert call(x=A + 1) == Q8_E_ALIGN
+    assert call(m=2, x_row_stride=23) == Q8_E_SHAPE
+    assert call(m=2, h_row_stride=63) == Q8_E_SHAPE
+    assert call(batch=2, w_batch_stride=64 * 24) == Q8_E_SHAPE        # < 2 n_ff rows
+    assert call(batch=2, w_batch_stride=2 * 64 * 24, h_batch_stride=0) == Q8_E_SHAPE
+    assert call(batch=2, w_batch_stride=2 * 64 * 24 + 1, h_batch_stride=64) == Q8_E_ALIGN
+    assert call(h=None) == Q8_E_NULL
+    assert call(n_ff=0, h=None) == Q8_OK
+    assert f(None, 0, None) == Q8_OK
+    assert f(None, 1, None) == Q8_E_NULL
+    many = (q.Q8UpGateDesc * 33)()
+    assert f(many, 33, None) == Q8_E_UNSUPPORTED
+
+
 def test_read_probe_checks(lib):
     f = lib.q8_read_probe
     assert f(A, -16, A, 4096, None) == Q8_E_SHAPE

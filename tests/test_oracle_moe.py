@@ -11,6 +11,8 @@
   output unchanged up to fp64 rounding.
 - Routing: invariants and a brute-force sort.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -168,3 +170,51 @@ def test_route_rejects_bad_ids(orc):
         orc.moe_route(np.array([[0, 5]], dtype=np.int32), 5)
     with pytest.raises(ValueError):
         orc.moe_route(np.array([[-1, 2]], dtype=np.int32), 5)
+
+
+def _q8_block(d_bits, codes):
+    """One hand-built Q8_0 block: binary16 scale bits + 32 int8 codes."""
+    b = np.zeros(34, dtype=np.uint8)
+    b[0:2] = np.array([d_bits], dtype=np.uint16).view(np.uint8)
+    b[2:] = np.asarray(codes, dtype=np.int8).view(np.uint8)
+    return b
+
+
+def test_dense_up_gate_exact_case(orc):
+    """Dense up_gate on hand-built blocks (scales 1.0 and 0.5, binary16 0x3C00 and
+    0x3800): gate row j sums to 32*(j+1), up row j to -32*(j+1) against an
+    all-ones activation, so h = silu(32(j+1)) * (-32(j+1)); swapping the halves
+    would give silu(-32(j+1)) * 32(j+1) (about -0) instead."""
+    n_ff, n_embd = 3, 64
+    ones = np.ones(32, dtype=np.int8)
+    rows = []
+    for j in range(n_ff):          # gate rows: (j+1) * ones at scale 1.0, second block zero
+        rows.append(np.concatenate([_q8_block(0x3C00, (j + 1) * ones), _q8_block(0, 0 * ones)]))
+    for j in range(n_ff):          # up rows: -2(j+1) * ones at scale 0.5 in the second block
+        rows.append(np.concatenate([_q8_block(0, 0 * ones), _q8_block(0x3800, -2 * (j + 1) * ones)]))
+    w = np.concatenate(rows)
+    x = np.concatenate([_q8_block(0x3C00, ones), _q8_block(0x3C00, ones)])
+    h = orc.up_gate_swiglu(w, x, n_embd, n_ff)
+    assert h.shape == (1, n_ff)
+    for j in range(n_ff):
+        g, u = 32.0 * (j + 1), -32.0 * (j + 1)
+        np.testing.assert_allclose(h[0, j], g / (1.0 + math.exp(-g)) * u, rtol=1e-15)
+
+
+def test_dense_up_gate_vs_dequantized_and_split(orc):
+    """Dense up_gate against dequantize-then-fp64 numpy, and equal bit for bit
+    to the split form (oracle products of the two halves, then silu * up)."""
+    m, n_embd, n_ff = 3, 768, 80
+    w_f = synth.normal_f32((2 * n_ff, n_embd), 0.02, "test", "dense-ug", "w")
+    x_f = synth.normal_f32((m, n_embd), 1.0, "test", "dense-ug", "x")
+    w = orc.quantize_rows(w_f)
+    x = orc.quantize_rows(x_f)
+    h = orc.up_gate_swiglu(w, x, n_embd, n_ff)
+    W = dequant(w, n_embd)
+    X = dequant(x, n_embd)
+    g = X @ W[:n_ff].T
+    up = X @ W[n_ff:].T
+    np.testing.assert_allclose(h, _silu(g) * up, rtol=1e-11, atol=1e-14)
+    gg = orc.matmul(w, x, 2 * n_ff, n_embd, m)
+    split = orc.fused_mul_silu(gg[:, :n_ff].copy(), gg[:, n_ff:].copy()).reshape(m, n_ff)
+    assert np.array_equal(h, split)
