@@ -522,6 +522,41 @@ def run_extra(args, q, synth):
                                 "gbs": round(active_bytes / tg / 1e9, 1),
                                 "pct_of_hbm_peak": round(active_bytes / tg / 1e9 / HBM_PEAK_GBS * 100, 2),
                                 "tokens_per_s": round(n_tok / tg, 1)})
+    elif wl == "c4p":
+        # prompt evaluation through the same expert FFN: 512 tokens of one layer
+        # (grouped int8 matrix-core GEMMs: routing, quantization, up_gate+SwiGLU,
+        # quantization of h, down, combine)
+        n_tok, E, n_embd, n_ff, U = 512, 128, 2048, 768, 8
+        wug = q.q8_0_quantize_rows(synth.normal_f32_torch((E * 2 * n_ff, n_embd), 0.02, dev, 0,
+                                                          wl, "ug"))
+        wd = q.q8_0_quantize_rows(synth.normal_f32_torch((E * n_embd, n_ff), 0.02, dev, 0, wl,
+                                                         "down"))
+        ids_h = synth.expert_ids(n_tok, U, E, 0, wl, "ids")
+        ids = torch.from_numpy(ids_h).to(dev)
+        cw = torch.from_numpy(synth.combine_weights(n_tok, U, 0, wl, "cw")).to(dev)
+        xf = synth.normal_f32_torch((n_tok, n_embd), 1.0, dev, 0, wl, "x")
+        h = torch.empty((n_tok, U, n_ff), dtype=torch.float32, device=dev)
+        out = torch.empty((n_tok, n_embd), dtype=torch.float32, device=dev)
+        ws = q.moe_workspace(n_tok, n_embd, n_ff, E, U, dev)
+        n_act = len(np.unique(ids_h))
+        active_bytes = n_act * (q8_bytes(2 * n_ff, n_embd) + q8_bytes(n_embd, n_ff))
+        macs = n_tok * U * (n_embd * 2 * n_ff + n_ff * n_embd)
+
+        def up():
+            q.moe_up_gate_swiglu(wug, xf, ids, n_embd, n_ff, E, ws, h=h)
+
+        def down():
+            q.moe_down_combine(wd, h, ids, cw, n_ff, n_embd, E, ws, out=out)
+        t_up = _time_launches(up, args.steps, args.warmup) / args.steps
+        t_dn = _time_launches(down, args.steps, args.warmup) / args.steps
+        t = _time_launches(lambda: (up(), down()), args.steps, args.warmup) / args.steps
+        res.update(tokens=n_tok, shape={"n_embd": n_embd, "n_ff": n_ff, "n_expert": E, "n_used": U},
+                   active_experts=n_act, active_weight_bytes=active_bytes,
+                   us_per_layer=round(t * 1e6, 2), prompt_tokens_per_s=round(n_tok / t, 1),
+                   gbs=round(active_bytes / t / 1e9, 1),
+                   pct_of_hbm_peak=round(active_bytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
+                   tops=round(2 * macs / t / 1e12, 2),
+                   us_up_gate_call=round(t_up * 1e6, 2), us_down_call=round(t_dn * 1e6, 2))
     return res
 
 
@@ -595,7 +630,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c5a", "c5b", "copy", "readbw", "ffn"])
+                    choices=["c1", "c2", "c3", "c4b1", "c4b16", "c4p", "c5a", "c5b", "copy", "readbw",
+                             "ffn"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
                     help="c4b1/c4b16: time the layer-after-layer launches, the grouped "

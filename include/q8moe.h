@@ -266,9 +266,16 @@ size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff,
  *   x          fp32 [n_tok][n_embd], 16-byte aligned (token activations)
  *   ids        int32 [n_tok][n_used]
  *   h          fp32 [n_tok][n_used][n_ff]          (written)
- * n_tok >= 0, n_embd % 32 == 0, n_ff % 32 == 0, 1 <= n_used <= 16.
- * Q8_E_UNSUPPORTED when n_tok*n_used > 1024 (decode sizes; the prefill form of
- * the expert FFN is separate). */
+ * n_tok >= 0, n_embd % 32 == 0, n_ff % 32 == 0, 1 <= n_used <= 16,
+ * n_expert <= 1024.
+ * Up to 16 tokens per call (decode) the expert-major streaming kernels run.
+ * With more tokens (prompt evaluation) the call routes the slots into tiles of
+ * at most 32 per expert and runs grouped GEMMs on the int8 matrix cores; that
+ * path needs n_embd % 128 == 0 and n_ff % 128 == 0, n_tok <= 8192 and
+ * n_tok*n_used <= 65536.  Other shapes with more than 16 tokens run on the
+ * streaming kernels up to n_tok*n_used = 1024, else Q8_E_UNSUPPORTED.  Both
+ * paths compute the same quantities; their fp32 sums may differ in the last
+ * bits (different summation order), each within the stated tolerance. */
 int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const float *x,
                        const int32_t *ids, float *h,
                        int64_t n_tok, int64_t n_embd, int64_t n_ff,

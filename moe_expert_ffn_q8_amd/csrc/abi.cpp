@@ -271,14 +271,18 @@ int q8_0_up_gate_swiglu_batched(const q8_0_up_gate_desc *descs, int64_t n_desc, 
 // ---------------------------------------------------------------------------
 // Mixture of experts
 
-static int moe_check(int64_t n_tok, int64_t n_in, int64_t n_out_rows, int64_t n_expert,
+// Shape checks shared by the expert-FFN calls.  Up to 1024 slots any shape
+// runs (decode kernels); more tokens take the prefill path, which needs
+// n_embd/32 and n_ff/32 to be multiples of 4.
+static int moe_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                      int64_t n_used)
 {
     if (n_tok < 0 || n_expert <= 0 || n_used <= 0) return Q8_E_SHAPE;
-    if (check_k(n_in) || check_k(n_out_rows)) return Q8_E_SHAPE;
+    if (check_k(n_embd) || check_k(n_ff)) return Q8_E_SHAPE;
     if (n_used > q8::kMoeMaxUsed) return Q8_E_UNSUPPORTED;
-    if (n_tok * n_used > q8::kMoeMaxSlots) return Q8_E_UNSUPPORTED;
     if (n_expert > q8::kMoeMaxExperts) return Q8_E_UNSUPPORTED;
+    if (n_tok * n_used > q8::kMoeMaxSlots && !q8::moe_prefill_ok(n_tok, n_embd, n_ff, n_expert, n_used))
+        return Q8_E_UNSUPPORTED;
     return Q8_OK;
 }
 
@@ -355,7 +359,7 @@ int moe_down_combine_batched(const moe_down_desc *descs, int64_t n_desc, int64_t
     if (n_desc < 0) return Q8_E_SHAPE;
     if (n_desc == 0) return Q8_OK;
     if (!descs) return Q8_E_NULL;
-    if (int rc = moe_check(n_tok, n_ff, n_embd, n_expert, n_used)) return rc;
+    if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
     for (int64_t i = 0; i < n_desc; ++i)
         if (int rc = check_down_desc(descs[i], n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
     for (int64_t i0 = 0; i0 < n_desc; i0 += q8::kMoeMaxLayers) {
@@ -376,7 +380,7 @@ int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *id
                      const float *cw, float *out, int64_t n_tok, int64_t n_ff, int64_t n_embd,
                      int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes, void *stream)
 {
-    if (int rc = moe_check(n_tok, n_ff, n_embd, n_expert, n_used)) return rc;
+    if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
     const moe_down_desc d = {w_down, h, ids, cw, out, ws, ws_bytes};
     return moe_down_combine_batched(&d, 1, n_tok, n_ff, n_embd, n_expert, n_used, stream);
 }

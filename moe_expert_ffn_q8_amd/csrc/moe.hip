@@ -803,11 +803,28 @@ int pick_mt(int64_t n_tok)
 
 }  // namespace
 
+int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, float *out,
+                       int64_t n_tok, int64_t n_rows, int64_t n_used, int64_t n_expert,
+                       hipStream_t stream)
+{
+    if (n_tok == 0) return 0;
+    if (n_tok > 65535) return -4;
+    CbParams cb;
+    memset(&cb, 0, sizeof(cb));
+    cb.layer[0] = CbLayer{yslot, ids, cw, out};
+    cb.n_rows = (int)n_rows;
+    cb.n_used = (int)n_used;
+    cb.n_expert = (int)n_expert;
+    dim3 cgrid((unsigned)((n_rows + 255) / 256), (unsigned)n_tok, 1);
+    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, cb);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 size_t moe_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                     int64_t n_used)
 {
-    (void)n_ff;
-    (void)n_expert;
+    if (moe_prefill_ok(n_tok, n_embd, n_ff, n_expert, n_used))
+        return moe_prefill_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
     const size_t slots = (size_t)(n_tok * n_used);
     const size_t y = slots * (size_t)n_embd * 4;
     return 256 + ((y + 255) / 256) * 256;
@@ -842,6 +859,15 @@ static int tiles_per_wg_for(int64_t active, int64_t tiles_per_expert)
 int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
 {
     if (a.n_tok == 0 || a.n_layers == 0) return 0;
+    if (moe_prefill_ok(a.n_tok, a.n_embd, a.n_ff, a.n_expert, a.n_used)) {
+        for (int l = 0; l < a.n_layers; ++l) {
+            const MoeUpGateArgs::Layer &L = a.layer[l];
+            if (int rc = launch_moe_prefill_up_gate(L.w, L.x, L.ids, L.h, L.ws, a.n_tok, a.n_embd,
+                                                    a.n_ff, a.n_expert, a.n_used, stream))
+                return rc;
+        }
+        return 0;
+    }
     const int64_t nb = a.n_embd / kQK;
     const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
     UgParams p;
@@ -892,6 +918,15 @@ static int launch_dn_mt(const DnParams &p, int grid, hipStream_t stream)
 int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
 {
     if (a.n_tok == 0 || a.n_layers == 0) return 0;
+    if (moe_prefill_ok(a.n_tok, a.n_embd, a.n_ff, a.n_expert, a.n_used)) {
+        for (int l = 0; l < a.n_layers; ++l) {
+            const MoeDownArgs::Layer &L = a.layer[l];
+            if (int rc = launch_moe_prefill_down(L.w, L.h, L.ids, L.cw, L.out, L.ws, a.n_tok,
+                                                 a.n_embd, a.n_ff, a.n_expert, a.n_used, stream))
+                return rc;
+        }
+        return 0;
+    }
     const int64_t nb = a.n_ff / kQK;
     const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
     const int64_t n_slots = a.n_tok * a.n_used;

@@ -11,6 +11,9 @@ constexpr int kMoeMaxUsed = 16;      // active experts per token
 constexpr int kMoeMaxSlots = 1024;   // n_tok * n_used per call (decode sizes)
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeMaxLayers = 32;    // independent layers of one shape per launch
+constexpr int kMoeDecodeMaxTok = 16;        // more tokens per call: the prefill path
+constexpr int kMoePrefillMaxTok = 8192;
+constexpr int kMoePrefillMaxSlots = 65536;
 
 // One launch covers n_layers independent layers of the same shape; every
 // layer has its own weights, inputs, outputs and workspace.
@@ -39,8 +42,9 @@ struct MoeDownArgs {
     int64_t n_tok, n_embd, n_ff, n_expert, n_used;
 };
 
-// Workspace: [0, 256) error word; [256, ...) per-slot down outputs fp32
-// [n_tok*n_used][n_embd].
+// Workspace (decode path): [0, 256) error word; [256, ...) per-slot down
+// outputs fp32 [n_tok*n_used][n_embd].  The prefill path's layout is larger
+// (routing tables, quantized rows); moe_ws_bytes covers the path a shape takes.
 size_t moe_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                     int64_t n_used);
 
@@ -49,5 +53,23 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream);
 int launch_moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *pairs,
                      int64_t n_tok, int64_t n_expert, int64_t n_used, void *ws,
                      hipStream_t stream);
+
+// out[t] = sum over u ascending of cw[t][u] * yslot[t*n_used+u] (NaN for a
+// token with an out-of-range id); one launch.
+int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, float *out,
+                       int64_t n_tok, int64_t n_rows, int64_t n_used, int64_t n_expert,
+                       hipStream_t stream);
+
+// Prefill path (n_tok > kMoeDecodeMaxTok, K = n_embd and n_ff in multiples of
+// 4 blocks): routing + quantization + grouped int8 GEMM per call.
+bool moe_prefill_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
+size_t moe_prefill_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                            int64_t n_used);
+int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *ids, float *h,
+                               void *ws, int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                               int64_t n_expert, int64_t n_used, hipStream_t stream);
+int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids, const float *cw,
+                            float *out, void *ws, int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                            int64_t n_expert, int64_t n_used, hipStream_t stream);
 
 }  // namespace q8

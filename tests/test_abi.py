@@ -131,6 +131,34 @@ def test_moe_checks(lib):
     assert lib.moe_route(A, None, A, A, 4, 8, 2, A, 256, None) == Q8_E_NULL
 
 
+def test_moe_prefill_checks(lib):
+    """More than 16 tokens: the prefill path's workspace (routing tables, the
+    quantized token rows; or the quantized h rows and the per-slot outputs)
+    and its shape limits."""
+    import moe_expert_ffn_q8_amd as q
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+
+    n_tok, n_embd, n_ff, n_expert, n_used = 512, 2048, 768, 128, 8
+    slots = n_tok * n_used
+    max_tiles = slots // 32 + n_expert + 1
+    data = 256 + a256((n_expert + 1) * 4) + a256(slots * 4) + a256(max_tiles * 16)
+    down = data + a256(slots * (n_ff // 32) * 34) + a256(slots * n_embd * 4)
+    up = data + a256(n_tok * (n_embd // 32) * 34)
+    ws = q.moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used)
+    assert ws == max(up, down)
+    assert ws > q.moe_workspace_bytes(16, n_embd, n_ff, n_expert, n_used)
+    ug = lib.moe_up_gate_swiglu
+    assert ug(A, A, A, A, n_tok, n_embd, n_ff, n_expert, n_used, A, ws - 1, None) == Q8_E_WORKSPACE
+    assert ug(A, A, A, A, 8193, n_embd, n_ff, n_expert, n_used, A, 1 << 40, None) == Q8_E_UNSUPPORTED
+    # 1600 slots with n_ff/32 = 3 (not a multiple of 4): no prefill path, too many slots
+    assert ug(A, A, A, A, 200, 256, 96, 8, 8, A, 1 << 40, None) == Q8_E_UNSUPPORTED
+    assert q.moe_workspace_bytes(200, 256, 96, 8, 8) == 0
+    # 20 tokens x 8 with n_ff/32 = 3: 160 slots stay on the streaming kernels
+    assert q.moe_workspace_bytes(20, 256, 96, 8, 8) == 256 + a256(160 * 256 * 4)
+
+
 def test_moe_batched_checks(lib):
     """Grouped MoE calls: every descriptor is checked before anything is
     enqueued (no valid launch here: there is no GPU)."""
