@@ -54,16 +54,12 @@ constexpr int kBN = 128;                 // weight rows per workgroup tile
 #ifndef Q8_GEMM_STEP_BLOCKS
 #define Q8_GEMM_STEP_BLOCKS 4
 #endif
-#ifndef Q8_GEMM_STAGE_BUFS
-#define Q8_GEMM_STAGE_BUFS 2
-#endif
 constexpr int kStepBlocks = Q8_GEMM_STEP_BLOCKS;           // blocks per K step (4 or 8)
 constexpr int kStepRowBytes = kStepBlocks * kBlockBytes;    // 136 or 272 bytes of a row
 constexpr int kStepChunks = (kStepRowBytes + 15) / 16;      // 9 or 17 16-byte chunks
 constexpr int kRowStride = 16 * kStepChunks;                // staged row: 144 or 272 B
 constexpr int kStageRows = kBM + kBN;                       // 256
 constexpr int kStageLoads = kStageRows * kStepChunks / kGThreads;   // 9 or 17 per thread
-constexpr int kStageBufs = Q8_GEMM_STAGE_BUFS;
 #ifndef Q8_GEMM_OUTER
 #define Q8_GEMM_OUTER 0          // scale products on the fp32 matrix core (1) or the VALU (0)
 #endif
@@ -94,9 +90,11 @@ __device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
 
 __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
 {
-    // K-step buffers in LDS (kStageBufs: 1 = two workgroups per CU hide each
-    // other's loads; 2 = step st+1 streams in while st is computed)
-    __shared__ __align__(16) uint8_t stage[kStageBufs][kStageRows * kRowStride];
+    // Two K-step buffers as separate LDS objects: the compiler then orders an
+    // LDS read only after the DMA loads into the buffer it reads (with one
+    // stage-indexed array every read waited for the next step's loads too).
+    __shared__ __align__(16) uint8_t stage0[kStageRows * kRowStride];
+    __shared__ __align__(16) uint8_t stage1[kStageRows * kRowStride];
     __shared__ __align__(16) float sc[kStepBlocks][kStageRows];              // 8192 B
 
     const int tid = threadIdx.x;
@@ -135,15 +133,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
     // boundary, so its buffer resource is uniform.  With 4-block steps a row's
     // 136 bytes are fetched as 9 chunks (8 bytes past the step, read but not
     // used; past the operand they read as zero).
-    auto issue = [&](int st, int buf) {
+    auto issue = [&](int st, uint8_t *sbuf, bool real) {
 #pragma unroll
         for (int u = 0; u < kStageLoads; ++u) {
             const int f = 64 * wave + lane + kGThreads * u;
             const int r = f / kStepChunks;
             const int c = f - r * kStepChunks;
-            const int off = (int)((r & (kBM - 1)) * row_bytes) + st * kStepRowBytes + 16 * c;
-            auto *dst = (__attribute__((address_space(3))) void *)(
-                &stage[buf][16 * (64 * wave + kGThreads * u)]);
+            // a step past the end loads zeros (offset past both ranges), so
+            // issues are unconditional and every wait count is exact
+            const int off = real ? (int)((r & (kBM - 1)) * row_bytes) + st * kStepRowBytes + 16 * c
+                                 : 0x7ffffff0;
+            auto *dst = (__attribute__((address_space(3))) void *)(&sbuf[16 * (64 * wave + kGThreads * u)]);
             if (kGThreads * u + 64 * wave < kBM * kStepChunks)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, off, 0, 0, 0);
             else
@@ -159,13 +159,15 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    issue(0, 0);
-    for (int st = 0; st < steps; ++st) {
-        const int buf = kStageBufs == 2 ? (st & 1) : 0;
-        __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's DMA for st landed
-        __syncthreads();                       // ... and every wave's; st-1 fully consumed
-        if (kStageBufs == 2 && st + 1 < steps) issue(st + 1, buf ^ 1);
-        const uint8_t *sb = stage[buf];
+    // Step st: wait for this wave's loads of st, barrier (every wave's
+    // landed; every wave is done with st-1, whose buffer the next issue
+    // fills), issue st+1, unpack the scales, barrier, compute.  Raw barriers
+    // with explicit waits: the workgroup fence of __syncthreads would also
+    // wait for the loads of st+1.
+    auto body = [&](int st, const uint8_t *sb, uint8_t *next) {
+        __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's loads of st landed
+        __builtin_amdgcn_s_barrier();
+        issue(st + 1, next, st + 1 < steps);
 #pragma unroll
         for (int i = 0; i < kStepBlocks * kStageRows / kGThreads; ++i) {
             const int e = tid + kGThreads * i;
@@ -173,12 +175,12 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
             const int b = e >> 8;
             sc[b][r] = half_bits_to_float(*(const uint16_t *)(sb + r * kRowStride + b * kBlockBytes));
         }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the scales are written
+        __builtin_amdgcn_s_barrier();
 
-#ifndef Q8_GEMM_UNROLL
-#define Q8_GEMM_UNROLL 4
-#endif
-#pragma unroll Q8_GEMM_UNROLL
+        // two blocks per unrolled iteration: the full unroll of a step keeps
+        // too many operands live (256 VGPRs and spills against 176)
+#pragma unroll 2
         for (int b = 0; b < kStepBlocks; ++b) {
             const int off = b * kBlockBytes + 2 + 16 * h;
             v4i A[2], B[2];
@@ -225,10 +227,12 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
                 }
             }
         }
-        if (kStageBufs == 1 && st + 1 < steps) {
-            __syncthreads();                   // every wave is done reading the buffer
-            issue(st + 1, 0);
-        }
+    };
+
+    issue(0, stage0, true);
+    for (int st = 0; st < steps; st += 2) {
+        body(st, stage0, stage1);
+        if (st + 1 < steps) body(st + 1, stage1, stage0);
     }
 
     // store: token m0 + 64wm + 32i + 8(r/4) + 4h + r%4, weight row n0 + 64wn + 32j + li
