@@ -298,7 +298,8 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
     value = bytes_step * args.steps / t["total"] / 1e9
     tok_s = m * args.steps / t["total"]
     achieved = plan.engine_bytes / t["eng"] / 1e9
-    kernel = ("stream_flat_kernel (decode engine)" if m <= 2 else
+    kernel = ("stream_pair_kernel (decode engine, two tiles per workgroup)" if m == 1 else
+              "stream_flat_kernel (decode engine)" if m == 2 else
               "stream_mfma_kernel (small-batch decode engine)")
     out = {
         "metric": METRIC,
@@ -673,7 +674,7 @@ def main():
         return
 
     traffic_file = args.traffic or (os.path.join(ROOT, "profiles",
-                                                "stream_flat_kernel_llama110m_decode_step.traffic.json")
+                                                "stream_pair_kernel_llama110m_decode_step.traffic.json")
                                     if args.workload == "c2" else None)
     if traffic_file and os.path.exists(traffic_file):
         t = read_traffic(traffic_file)

@@ -170,6 +170,43 @@ def test_c5b_vocab_projection_full_size(q, orc):
     del wf
 
 
+def test_matvec_paired_tiles_odd_and_straddling(q, orc):
+    """Launches of 8192 tiles or more take two tiles per workgroup: an odd tile
+    count (8193 one-row tiles at k = 8192: the last workgroup has a single
+    tile) and a pair that straddles two descriptors (8191 tiles of one product
+    and 1 tile of another in one batched call), against the oracle on sampled
+    and boundary rows."""
+    import torch
+    k = 8192
+    nb = k // 32
+    x = acts_q8(orc, 1, k, "pair-x")
+    xg = to_gpu(x)
+    rng = np.random.default_rng(5)
+    # odd count: 8193 rows -> 8193 tiles
+    n = 8193
+    w = weights_q8(orc, n, k, "pair-w", n)
+    wg = to_gpu(w)
+    y = nan_like((n,))
+    q.q8_0_matvec(wg, xg, n, k, y=y)
+    rows = np.unique(np.concatenate([[0, 1, n - 3, n - 2, n - 1], rng.integers(0, n, 200)]))
+    ref = orc.matmul(np.ascontiguousarray(w.reshape(n, nb * 34)[rows]), x, rows.size, k, 1)
+    yy = y.cpu().numpy()
+    assert np.all(np.isfinite(yy))
+    assert_rows_close(yy[rows][None, :], ref)
+    # a pair across two descriptors: tiles 8190 (last of the first) and 8191
+    n1, n2, k2 = 8191, 5, 768
+    w2 = weights_q8(orc, n2, k2, "pair-w2")
+    x2 = acts_q8(orc, 1, k2, "pair-x2")
+    y1, y2 = nan_like((n1,)), nan_like((n2,))
+    d = [q.make_desc(wg, xg, y1, n1, k), q.make_desc(to_gpu(w2), to_gpu(x2), y2, n2, k2)]
+    q.q8_0_matmul_batched(d, wg)
+    torch.cuda.synchronize()
+    rows1 = np.unique(np.concatenate([[0, n1 - 2, n1 - 1], rng.integers(0, n1, 100)]))
+    ref1 = orc.matmul(np.ascontiguousarray(w.reshape(n, nb * 34)[rows1]), x, rows1.size, k, 1)
+    assert_rows_close(y1.cpu().numpy()[rows1][None, :], ref1)
+    assert_rows_close(y2.cpu().numpy()[None, :], orc.matmul(w2, x2, n2, k2, 1))
+
+
 @pytest.mark.parametrize("m,n,k", [(17, 70, 768), (128, 128, 256), (129, 257, 512),
                                    (200, 300, 2048), (512, 96, 4096), (33, 1000, 768),
                                    (256, 40, 3072)])
