@@ -369,8 +369,11 @@ def run_extra(args, q, synth):
     res = {"workload": wl, "steps": args.steps, "warmup": args.warmup}
     if wl == "readbw":
         # achievable read bandwidth for context: the library's plain streaming
-        # read (q8_read_probe) over 2 GiB
-        nbytes = 2 << 30
+        # read (q8_read_probe) over 2 GiB, or --read-bytes (e.g. the 116.9 MB of
+        # the Llama-110M-shaped step, to see the ramp and tail of a launch that
+        # size)
+        nbytes = args.read_bytes if args.read_bytes else 2 << 30
+        nbytes = (nbytes + 65535) // 65536 * 65536
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
         sink = torch.zeros(4096, dtype=torch.int32, device=dev)
         total = _time_launches(lambda: q.q8_read_probe(src, sink), max(10, args.steps // 10), 3)
@@ -634,6 +637,8 @@ def main():
                     choices=["c1", "c2", "c3", "c4b1", "c4b16", "c4p", "c5a", "c5b", "copy", "readbw",
                              "ffn"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-bytes", type=int, default=0,
+                    help="readbw workload: bytes per read launch (default 2 GiB)")
     ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
                     help="c4b1/c4b16: time the layer-after-layer launches, the grouped "
                          "launches, or both")
