@@ -42,14 +42,15 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kPThreads = 256;
+constexpr int kPWaves = 8;
+constexpr int kPThreads = kPWaves * kWave;    // 512
 constexpr int kPBM = 32;                      // slots per tile
-constexpr int kPBN = 128;                     // output columns per workgroup (4 waves x 32)
+constexpr int kPBRows = kPWaves * 32;         // staged weight rows: one 32-row MFMA tile per wave
 constexpr int kPStep = 4;                     // blocks per K step
 constexpr int kPStepBytes = kPStep * kBlockBytes;    // 136 bytes of a row
 constexpr int kPChunks = 9;                   // 16-byte chunks fetched per staged row
 constexpr int kPRowStride = 16 * kPChunks;    // 144
-constexpr int kPAChunks = 512;                // 32 rows x 9 = 288, padded to 2 loads per thread
+constexpr int kPAChunks = 512;                // 32 rows x 9 = 288, padded to one load per thread
 constexpr int kRouteThreads = 1024;
 
 struct TileEntry {
@@ -154,18 +155,27 @@ __device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
                  (int)__builtin_amdgcn_alignbyte(d3, d2, 2), (int)__builtin_amdgcn_alignbyte(d4, d3, 2)};
 }
 
+// Output columns per workgroup: up_gate pairs waves w and w + 4 (gate and up
+// rows of the same 32 columns), down gives every wave its own 32 columns.
+template <bool UG>
+constexpr int pg_cols()
+{
+    return UG ? kPBRows / 2 : kPBRows;
+}
+
 template <bool UG>
 __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
 {
-    constexpr int kBRows = UG ? 2 * kPBN : kPBN;          // staged weight rows
-    constexpr int kBChunks = kBRows * kPChunks;           // 2304 or 1152
-    constexpr int kBLoads = (kBChunks + kPThreads - 1) / kPThreads;    // 9 or 5 per thread
-    constexpr int kALoads = kPAChunks / kPThreads;        // 2 per thread
+    constexpr int kBChunks = kPBRows * kPChunks;          // 2304
+    constexpr int kBLoads = (kBChunks + kPThreads - 1) / kPThreads;    // 5 per thread
+    constexpr int kALoads = kPAChunks / kPThreads;        // 1 per thread
     constexpr int kLoads = kALoads + kBLoads;             // per thread and step (all threads alike)
     constexpr int kBPad = kBLoads * kPThreads;            // B chunks incl. padding
-    constexpr int kRows = kPBM + kBRows;
+    constexpr int kRows = kPBM + kPBRows;
     constexpr int kStage = 16 * (kPAChunks + kBPad);
+    constexpr int kCols = pg_cols<UG>();
     static_assert(kPAChunks % kPThreads == 0, "whole A loads per thread");
+    static_assert(kStage >= 4 * kWave * 16 * 4, "the epilogue exchange fits a stage buffer");
     // three K-step buffers as separate LDS objects: the compiler then orders
     // an LDS read only after the DMA loads into the buffer it reads (one array
     // indexed by stage would make every read wait for every DMA in flight)
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
     __shared__ int a_slot[kPBM];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = wave_uniform(tid >> 6);
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int li = lane & 31;
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
     const int mt = work - nt * a.max_tiles;
     if (nt >= a.tiles_n || mt >= a.hdr[1]) return;
     const TileEntry te = a.tiles[mt];
-    const int n0 = nt * kPBN;
+    const int n0 = nt * kCols;
     const int64_t row_bytes = (int64_t)a.nb * kBlockBytes;
 
     if (tid < kPBM) {
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
             const int c = f - i * kPChunks;
             // rows past the expert's (clamped to its end) and padding read as zero
             const int wrow = f >= kBChunks ? a.w_rows :
-                             min(UG ? (i < kPBN ? n0 + i : a.n_out + n0 + i - kPBN) : n0 + i, a.w_rows);
+                             min(UG ? (i < kCols ? n0 + i : a.n_out + n0 + i - kCols) : n0 + i, a.w_rows);
             const int off = real ? (int)(wrow * row_bytes) + st * kPStepBytes + 16 * c
                                  : (int)a.expert_bytes + 16 * c;
             auto *dst = (__attribute__((address_space(3))) void *)(
@@ -238,11 +248,9 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
         }
     };
 
-    float acc[UG ? 2 : 1][16];
+    float acc[16];
 #pragma unroll
-    for (int q = 0; q < (UG ? 2 : 1); ++q)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
     // Step st: wait for this wave's loads of st (the loads of st+1 stay in
     // flight), barrier (every wave's landed, and every wave is done with
@@ -266,26 +274,23 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the scales are written
         __builtin_amdgcn_s_barrier();
+        const int wr = 32 * wave + li;
 #pragma unroll
         for (int b = 0; b < kPStep; ++b) {
             const int off = b * kBlockBytes + 2 + 16 * h;
             const v4i A = lds_codes16(sa + li * kPRowStride, off);
+            const v4i B = lds_codes16(sw + wr * kPRowStride, off);
+            const float dw = sc[b][kPBM + wr];
             float dx[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 v = *(const float4 *)&sc[b][8 * q + 4 * h];
                 dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
             }
+            v16i s = {0};
+            s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, s, 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < (UG ? 2 : 1); ++q) {
-                const int wr = q * kPBN + 32 * wave + li;
-                const v4i B = lds_codes16(sw + wr * kPRowStride, off);
-                const float dw = sc[b][kPBM + wr];
-                v16i s = {0};
-                s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, s, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[q][r] = fmaf(dx[r] * dw, (float)s[r], acc[q][r]);
-            }
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf(dx[r] * dw, (float)s[r], acc[r]);
         }
     };
 
@@ -297,21 +302,34 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
         if (st + 2 < steps) body(st + 2, stage2, stage1);
     }
 
-    // slot row 8(r/4) + 4h + r%4 of the tile, column n0 + 32 wave + li
-    const int col = n0 + 32 * wave + li;
-    if (col >= a.n_out) return;
+    // slot row 8(r/4) + 4h + r%4 of the tile; column n0 + 32 (wave % 4) + li
+    // (up_gate: waves 4..7 hand their up tiles to waves 0..3 through LDS, in
+    // the same register layout)
+    const int col = n0 + 32 * (UG ? (wave & 3) : wave) + li;
+    if (UG) {
+        float *xch = (float *)stage0;
+        __syncthreads();                       // every wave is done with the stage buffers
+        if (wave >= 4) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= te.rows) continue;
-        float v;
-        if (UG) {
-            const float g = acc[0][r];
-            v = g / (1.0f + expf(-g)) * acc[UG ? 1 : 0][r];
-        } else {
-            v = acc[0][r];
+            for (int r = 0; r < 16; ++r) xch[((wave - 4) * 16 + r) * kWave + lane] = acc[r];
         }
-        a.out[(int64_t)a_slot[row] * a.n_out + col] = v;
+        __syncthreads();
+        if (wave >= 4 || col >= a.n_out) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row >= te.rows) continue;
+            const float g = acc[r];
+            const float u = xch[(wave * 16 + r) * kWave + lane];
+            a.out[(int64_t)a_slot[row] * a.n_out + col] = g / (1.0f + expf(-g)) * u;
+        }
+    } else {
+        if (col >= a.n_out) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row < te.rows) a.out[(int64_t)a_slot[row] * a.n_out + col] = acc[r];
+        }
     }
 }
 
@@ -380,7 +398,7 @@ int launch_grouped(const uint8_t *A, int64_t a_bytes, const uint8_t *w, int64_t 
     p.nb = (int)nb;
     p.n_used = (int)n_used;
     p.max_tiles = (int)L.max_tiles;
-    p.tiles_n = (int)((n_out + kPBN - 1) / kPBN);
+    p.tiles_n = (int)((n_out + pg_cols<UG>() - 1) / pg_cols<UG>());
     int64_t grid = L.max_tiles * p.tiles_n;
     grid = (grid + 7) & ~(int64_t)7;
     if (grid > 0x7fffffff) return -4;
