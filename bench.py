@@ -336,6 +336,16 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
             "ms_per_step": round(t["total_fused"] / args.steps * 1e3, 5),
             "gbs": round(plan.fused_bytes * args.steps / t["total_fused"] / 1e9, 1)},
     }
+    # context: a plain streaming read of the same number of bytes per launch
+    # (q8_read_probe; non-temporal 16-byte loads, no arithmetic)
+    probe_bytes = (plan.engine_bytes + 65535) // 65536 * 65536
+    src = torch.ones(probe_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    tp = _time_launches(lambda: q.q8_read_probe(src, sink), args.steps, 5) / args.steps
+    del src
+    out["roofline"]["read_probe_same_bytes"] = {
+        "bytes": probe_bytes, "us": round(tp * 1e6, 3), "gbs": round(probe_bytes / tp / 1e9, 1),
+        "engine_over_probe": round(tp / t["eng"], 4)}
     if t["total_one"] is not None:
         out["one_launch_reference"] = {
             "timing": "the same steps as one launch each, every activation row quantized once "
