@@ -20,6 +20,9 @@ Parity status of each function (the pins live in tests/test_oracle_*.py):
   moe_route .................... pinned (invariants, brute force)
   moe_down_combine ............. pinned (one-hot / single-expert reductions,
                                   dequantized fp64 brute force)
+  repack_r8, matvec_r8 ......... pinned (hand-listed byte positions of a small
+                                  case, byte multiset, matvec identity with the
+                                  native layout)
 """
 import ctypes
 import os
@@ -69,6 +72,9 @@ def _load():
         "or_moe_down_combine": (ctypes.c_int, [_u8p, _f32p, _i32p, _f32p, _f64p, _u8p,
                                                _i64, _i64, _i64, _i64, _i64, _i64p, _i64,
                                                _u8p]),
+        "or_r8_bytes": (ctypes.c_int64, [_i64, _i64]),
+        "or_repack_r8": (ctypes.c_int, [_u8p, _u8p, _i64, _i64]),
+        "or_matvec_r8": (ctypes.c_int, [_u8p, _u8p, _f64p, _i64, _i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -306,6 +312,38 @@ def moe_ffn(w_ug, w_d, x_f32, ids, cw, n_embd, n_ff, n_expert):
     h = moe_up_gate_swiglu(w_ug, xq, ids, n_embd, n_ff, n_expert)
     out = moe_down_combine(w_d, h.astype(np.float32), ids, cw, n_ff, n_embd, n_expert)
     return out, h
+
+
+# --------------------------------------------------------------------------
+# Row-interleaved weight layout (R8): groups of 8 rows, scales then codes,
+# both ordered by (block, row); see q8_oracle.c
+# --------------------------------------------------------------------------
+
+def r8_bytes(n, k):
+    v = int(_load().or_r8_bytes(n, k))
+    if v < 0:
+        raise ValueError(f"oracle r8_bytes: status {v}")
+    return v
+
+
+def repack_r8(w, n, k):
+    """Native rows uint8 [n][k/32*34] -> uint8 [r8_bytes(n, k)]."""
+    nb = k // QK
+    w = _blocks(w, n * nb * BLOCK_BYTES)
+    out = np.empty(r8_bytes(n, k), dtype=np.uint8)
+    _check(_load().or_repack_r8(_p(w, _u8p), _p(out, _u8p), n, k), "repack_r8")
+    return out
+
+
+def matvec_r8(w_r8, x, n, k):
+    """y[n] (fp64) for weights in the R8 layout and one Q8_0 activation row."""
+    nb = k // QK
+    w_r8 = _blocks(w_r8, r8_bytes(n, k))
+    x = _blocks(x, nb * BLOCK_BYTES)
+    y = np.empty(n, dtype=np.float64)
+    _check(_load().or_matvec_r8(_p(w_r8, _u8p), _p(x, _u8p), _p(y, _f64p), n, k),
+           "matvec_r8")
+    return y
 
 
 # --------------------------------------------------------------------------

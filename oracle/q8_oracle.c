@@ -381,3 +381,83 @@ void or_f16_to_f32_array(const uint16_t *h, float *x, int64_t n)
 {
     for (int64_t i = 0; i < n; i++) x[i] = or_f16_to_f32(h[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Row-interleaved weight layout (R8)                                        */
+/* ------------------------------------------------------------------------ */
+
+/* The Gemma-4-on-Xeon page (section on the fallback's cost and the repacking
+   bug) describes an option that, at startup, reorders the quantized weights
+   into an interleaved form named Q8_0_R8, built for one instruction set.  The
+   page gives no byte layout.  This library's reading, used for GPU streaming:
+   rows are taken in groups of 8 (the last group padded with rows whose
+   scale and codes are all zero); a group of 8 rows of nb blocks is 272*nb
+   bytes, the 8*nb binary16 scales first, ordered by (block, row), then the
+   codes, ordered by (block, row, position).  Group g starts at byte
+   g*272*nb.  The data are the same bytes as the native rows, moved. */
+
+#define OR8 8
+
+static int64_t r8_group_bytes(int64_t nb) { return (int64_t)OR8 * OBLK * nb; }
+
+/* Byte offset, inside its group, of the scale of row r (0..7) at block b. */
+static int64_t r8_scale_at(int64_t b, int r) { return 2 * (b * OR8 + r); }
+
+/* Byte offset, inside its group, of code j of row r at block b. */
+static int64_t r8_code_at(int64_t nb, int64_t b, int r, int j)
+{
+    return 2 * OR8 * nb + (b * OR8 + r) * OQK + j;
+}
+
+int64_t or_r8_bytes(int64_t n, int64_t k)
+{
+    if (n < 0 || k <= 0 || k % OQK != 0) return -2;
+    return (n + OR8 - 1) / OR8 * r8_group_bytes(k / OQK);
+}
+
+/* Native rows [n][k/32] blocks -> the R8 layout (or_r8_bytes(n, k) bytes). */
+int or_repack_r8(const uint8_t *w, uint8_t *out, int64_t n, int64_t k)
+{
+    if (n < 0 || k <= 0 || k % OQK != 0) return -2;
+    int64_t nb = k / OQK;
+    int64_t groups = (n + OR8 - 1) / OR8;
+    for (int64_t g = 0; g < groups; g++) {
+        uint8_t *gp = out + g * r8_group_bytes(nb);
+        for (int r = 0; r < OR8; r++) {
+            int64_t row = g * OR8 + r;
+            for (int64_t b = 0; b < nb; b++) {
+                const uint8_t *blk = row < n ? w + (row * nb + b) * OBLK : NULL;
+                gp[r8_scale_at(b, r)] = blk ? blk[0] : 0;
+                gp[r8_scale_at(b, r) + 1] = blk ? blk[1] : 0;
+                for (int j = 0; j < OQK; j++)
+                    gp[r8_code_at(nb, b, r, j)] = blk ? blk[2 + j] : 0;
+            }
+        }
+    }
+    return 0;
+}
+
+/* y[i] (fp64) = sum over blocks, ascending, of d_w*d_x*s for row i read from
+   the R8 layout; the same sum, in the same order, as or_matmul on the native
+   rows. */
+int or_matvec_r8(const uint8_t *w_r8, const uint8_t *x, double *y, int64_t n, int64_t k)
+{
+    if (n < 0 || k <= 0 || k % OQK != 0) return -2;
+    int64_t nb = k / OQK;
+    for (int64_t i = 0; i < n; i++) {
+        const uint8_t *gp = w_r8 + (i / OR8) * r8_group_bytes(nb);
+        int r = (int)(i % OR8);
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *xb = x + b * OBLK;
+            uint16_t dh = (uint16_t)(gp[r8_scale_at(b, r)] |
+                                     ((uint16_t)gp[r8_scale_at(b, r) + 1] << 8));
+            int32_t s = 0;
+            for (int j = 0; j < OQK; j++)
+                s += (int)(int8_t)gp[r8_code_at(nb, b, r, j)] * blk_code(xb, j);
+            acc += ((double)or_f16_to_f32(dh) * (double)blk_scale(xb)) * (double)s;
+        }
+        y[i] = acc;
+    }
+    return 0;
+}
