@@ -472,6 +472,53 @@ def run_extra(args, q, synth):
             dt = time.perf_counter() - t0
             res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
                                    "kind": "oracle", "sample": f"the 12 layers once, {dt:.2f} s"}
+    elif wl == "r8":
+        # the row-interleaved weight layout (repacked once, outside the timed
+        # region) against native rows: one matvec per launch, the vocabulary
+        # projection and the Llama-110M matrix shapes
+        shapes = [(262144, 2048), (32000, 768), (2048, 768), (768, 2048), (768, 768)]
+        rows_out = []
+        for n, k in shapes:
+            w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w", n, k))
+            x = q.q8_0_quantize_rows(synth.normal_f32_torch((1, k), 1.0, dev, 0, wl, "x", n, k))
+            y = torch.empty(n, dtype=torch.float32, device=dev)
+            t_rp = _time_launches(lambda: q.q8_0_repack_r8(w, n, k), 3, 1) / 3
+            wr = q.q8_0_repack_r8(w, n, k)
+            tn = _time_launches(lambda: q.q8_0_matvec(w, x, n, k, y=y), args.steps,
+                                args.warmup) / args.steps
+            tr = _time_launches(lambda: q.q8_0_matvec_r8(wr, x, n, k, y=y), args.steps,
+                                args.warmup) / args.steps
+            nbytes = q8_bytes(n, k) + q8_bytes(1, k) + 4 * n
+            rows_out.append({"shape": [n, k], "bytes_per_launch": nbytes,
+                             "native_us": round(tn * 1e6, 3), "r8_us": round(tr * 1e6, 3),
+                             "native_gbs": round(nbytes / tn / 1e9, 1),
+                             "r8_gbs": round(nbytes / tr / 1e9, 1),
+                             "r8_over_native_time": round(tr / tn, 4),
+                             "repack_us_once": round(t_rp * 1e6, 1)})
+            del w, wr
+        big = rows_out[0]
+        res.update(shapes=rows_out, us_per_matvec=big["r8_us"], gbs=big["r8_gbs"],
+                   pct_of_hbm_peak=round(big["r8_gbs"] / HBM_PEAK_GBS * 100, 2),
+                   roofline={"bound": "hbm", "achieved": big["r8_gbs"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(big["r8_gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": None, "kernel": "r8_matvec_kernel"})
+        if not args.no_cpu_baseline:
+            # the oracle's R8 matvec on 4096 rows of the vocabulary shape
+            import oracle
+            n, k = 4096, 2048
+            wh = oracle.quantize_rows(synth.normal_f32((n, k), 0.02, "cpu-r8", n))
+            xh = oracle.quantize_rows(synth.normal_f32((1, k), 1.0, "cpu-r8-x", n))
+            wrh = oracle.repack_r8(wh, n, k)
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 5.0:
+                oracle.matvec_r8(wrh, xh, n, k)
+                reps += 1
+            dt = time.perf_counter() - t0
+            nb_cpu = q8_bytes(n, k) + q8_bytes(1, k) + 4 * n
+            res["cpu_baseline"] = {"value": round(reps * nb_cpu / dt / 1e9, 3), "unit": "GB/s",
+                                   "cores": 1, "kind": "oracle",
+                                   "sample": f"{reps} R8 matvecs of 4096 x 2048, {dt:.1f} s"}
     elif wl == "c5a":
         m, n, k = 512, 14336, 4096
         w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w"))
@@ -645,7 +692,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
                     choices=["c1", "c2", "c3", "c4b1", "c4b16", "c4p", "c5a", "c5b", "copy", "readbw",
-                             "ffn"])
+                             "ffn", "r8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-bytes", type=int, default=0,
                     help="readbw workload: bytes per read launch (default 2 GiB)")

@@ -118,6 +118,35 @@ int q8_0_matmul(const q8_0_block *w, const q8_0_block *x, float *y,
                 int64_t n, int64_t k, int64_t m, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Row-interleaved weights (R8).  The [XEON] section on the fallback's cost and
+ * the repacking bug describes a startup option that reorders quantized weights
+ * into an interleaved form, Q8_0_R8; the page gives no byte layout.  This
+ * library's layout (same bytes as the native rows, moved once at load time):
+ * rows in groups of 8, the last group padded with zero rows; group g takes
+ * 272*(k/32) bytes at g*272*(k/32):
+ *   bytes [0, 16*(k/32))     the binary16 scales, little-endian, the one of
+ *                            row 8g+r at block b at index 8*b + r
+ *   then the codes           the 32 codes of row 8g+r at block b at byte
+ *                            16*(k/32) + 32*(8*b + r)
+ *
+ * q8_0_r8_bytes -- the size of that layout for n rows of k values (a negative
+ * status for a bad shape).
+ *
+ * q8_0_repack_r8 -- writes the layout of native rows w (Q8_0 [n][k/32]) to
+ * w_r8 (q8_0_r8_bytes(n, k) bytes, 16-byte aligned, written in full,
+ * padding included).  w and w_r8 must not overlap.
+ *
+ * q8_0_matvec_r8 -- y[n] = W[n][k] . x[k] with W in the R8 layout: the
+ * arithmetic of q8_0_matvec (exact int32 block sums, (d_w*d_x)*s in fp32).
+ *   w_r8 (16-byte aligned), x  Q8_0 [k/32], y  fp32 [n] (written)
+ * n >= 0, k > 0, k % 32 == 0, k <= 32768 (Q8_E_UNSUPPORTED above).
+ */
+int64_t q8_0_r8_bytes(int64_t n, int64_t k);
+int q8_0_repack_r8(const q8_0_block *w, void *w_r8, int64_t n, int64_t k, void *stream);
+int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, int64_t k,
+                   void *stream);
+
+/* ---------------------------------------------------------------------------
  * q8_0_matmul_batched -- several independent products in one launch, for
  * sequencing a decode step with few kernel launches (launch count per token
  * is the cost the [NARR] kernels-per-token table tracks).  Descriptor i

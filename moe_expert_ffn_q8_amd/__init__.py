@@ -11,7 +11,7 @@ from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDes
                    moe_workspace, moe_workspace_bytes, q8_0_matmul, q8_0_matmul_batched,
                    q8_0_matmul_blocksums, q8_0_matmul_f32_batched, q8_0_matmul_f32_step,
                    q8_0_matmul_f32_step_workspace, q8_0_matmul_f32_step_ws_bytes, q8_0_matvec,
-                   q8_0_quantize_rows, q8_empty, q8_read_probe, raw, status_str, version)
+                   q8_0_matvec_r8, q8_0_quantize_rows, q8_0_r8_bytes, q8_0_repack_r8, q8_empty, q8_read_probe, raw, status_str, version)
 
 __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGateDesc", "Q8Error",
            "Q8MatmulDesc", "Q8MatmulF32Desc", "Q8UpGateDesc", "make_desc", "make_f32_desc",
@@ -19,5 +19,6 @@ __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGate
            "moe_error_word", "moe_route", "moe_up_gate_swiglu", "moe_up_gate_swiglu_batched",
            "moe_workspace", "moe_workspace_bytes", "q8_0_matmul", "q8_0_matmul_batched",
            "q8_0_matmul_blocksums", "q8_0_matmul_f32_batched", "q8_0_matmul_f32_step",
-           "q8_0_matmul_f32_step_workspace", "q8_0_matmul_f32_step_ws_bytes", "q8_0_matvec", "q8_0_quantize_rows", "q8_empty", "q8_read_probe", "raw",
+           "q8_0_matmul_f32_step_workspace", "q8_0_matmul_f32_step_ws_bytes", "q8_0_matvec",
+           "q8_0_matvec_r8", "q8_0_quantize_rows", "q8_0_r8_bytes", "q8_0_repack_r8", "q8_empty", "q8_read_probe", "raw",
            "status_str", "version"]

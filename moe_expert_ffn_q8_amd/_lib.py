@@ -85,6 +85,9 @@ _SIGS = {
     "q8_0_matmul_blocksums": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "moe_route": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]),
     "q8_read_probe": (_int, [_vp, _i64, _vp, _i64, _vp]),
+    "q8_0_r8_bytes": (_i64, [_i64, _i64]),
+    "q8_0_repack_r8": (_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q8_0_matvec_r8": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -169,6 +172,33 @@ def q8_0_matvec(w, x, n, k, y=None):
         y = torch.empty(n, dtype=torch.float32, device=w.device)
     _need(y, torch.float32, "y")
     _check("q8_0_matvec", _lib.q8_0_matvec(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(w)))
+    return y
+
+
+def q8_0_r8_bytes(n, k):
+    v = _lib.q8_0_r8_bytes(n, k)
+    _check("q8_0_r8_bytes", v if v < 0 else 0)
+    return int(v)
+
+
+def q8_0_repack_r8(w, n, k, out=None):
+    """Native Q8_0 rows (uint8 GPU tensor) -> the row-interleaved (R8) layout."""
+    _need(w, torch.uint8, "w")
+    if out is None:
+        out = torch.empty(q8_0_r8_bytes(n, k), dtype=torch.uint8, device=w.device)
+    _need(out, torch.uint8, "out")
+    _check("q8_0_repack_r8", _lib.q8_0_repack_r8(_ptr(w), _ptr(out), n, k, _stream(w)))
+    return out
+
+
+def q8_0_matvec_r8(w_r8, x, n, k, y=None):
+    _need(w_r8, torch.uint8, "w_r8")
+    _need(x, torch.uint8, "x")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w_r8.device)
+    _need(y, torch.float32, "y")
+    _check("q8_0_matvec_r8", _lib.q8_0_matvec_r8(_ptr(w_r8), _ptr(x), _ptr(y), n, k,
+                                                 _stream(w_r8)))
     return y
 
 

@@ -385,6 +385,37 @@ int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *id
     return moe_down_combine_batched(&d, 1, n_tok, n_ff, n_embd, n_expert, n_used, stream);
 }
 
+int64_t q8_0_r8_bytes(int64_t n, int64_t k)
+{
+    if (int rc = check_k(k)) return rc;
+    if (n < 0) return Q8_E_SHAPE;
+    return q8::r8_bytes(n, k / kQK);
+}
+
+int q8_0_repack_r8(const q8_0_block *w, void *w_r8, int64_t n, int64_t k, void *stream)
+{
+    if (int rc = check_k(k)) return rc;
+    if (n < 0) return Q8_E_SHAPE;
+    if (n == 0) return Q8_OK;
+    if (!w || !w_r8) return Q8_E_NULL;
+    if (!aligned(w, 2) || !aligned(w_r8, 16)) return Q8_E_ALIGN;
+    return hip_status(q8::launch_r8_repack((const uint8_t *)w, (uint8_t *)w_r8, n, k / kQK,
+                                           as_stream(stream)));
+}
+
+int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, int64_t k,
+                   void *stream)
+{
+    if (int rc = check_k(k)) return rc;
+    if (n < 0) return Q8_E_SHAPE;
+    if (n == 0) return Q8_OK;
+    if (!w_r8 || !x || !y) return Q8_E_NULL;
+    if (!aligned(w_r8, 16) || !aligned(x, 2) || !aligned(y, 4)) return Q8_E_ALIGN;
+    if (!q8::r8_matvec_ok(n, k / kQK)) return Q8_E_UNSUPPORTED;
+    return hip_status(q8::launch_r8_matvec((const uint8_t *)w_r8, (const uint8_t *)x, y, n,
+                                           k / kQK, as_stream(stream)));
+}
+
 int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words, void *stream)
 {
     if (bytes < 0 || sink_words < 0) return Q8_E_SHAPE;

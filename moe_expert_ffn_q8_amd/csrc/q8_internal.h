@@ -57,6 +57,16 @@ bool gemm_ok(int64_t n, int64_t nb, int64_t m);
 int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t nb, int64_t m,
                 int64_t ldy, hipStream_t stream);
 
+// Row-interleaved weight layout (R8): 8-row groups of 272*nb bytes, the
+// group's scales first, ordered by (block, row), then its codes, ordered by
+// (block, row, position); the last group padded with zero rows.
+constexpr int64_t kR8MaxNb = 1024;   // k <= 32768 (the activation row is staged in LDS, 36 B per block)
+int64_t r8_bytes(int64_t n, int64_t nb);
+int launch_r8_repack(const uint8_t *w, uint8_t *out, int64_t n, int64_t nb, hipStream_t stream);
+bool r8_matvec_ok(int64_t n, int64_t nb);
+int launch_r8_matvec(const uint8_t *w_r8, const uint8_t *x, float *y, int64_t n, int64_t nb,
+                     hipStream_t stream);
+
 // Streaming-read probe (measurement): reads `bytes` from p, writes one word
 // per workgroup (at most 4096) to sink.
 int launch_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words,

@@ -306,3 +306,30 @@ def test_read_probe_checks(lib):
     assert f(None, 1024, A, 4096, None) == Q8_E_NULL
     assert f(A + 8, 1024, A, 4096, None) == Q8_E_ALIGN
     assert f(A, 1000, A, 4096, None) == Q8_E_ALIGN
+
+
+def test_r8_checks(lib):
+    assert lib.q8_0_r8_bytes(9, 64) == 2 * 8 * 2 * 34
+    assert lib.q8_0_r8_bytes(16, 64) == 16 * 2 * 34
+    assert lib.q8_0_r8_bytes(0, 64) == 0
+    assert lib.q8_0_r8_bytes(4, 48) == Q8_E_SHAPE
+    assert lib.q8_0_r8_bytes(-1, 64) == Q8_E_SHAPE
+    rp = lib.q8_0_repack_r8
+    assert rp(A, A, 10, 40, None) == Q8_E_SHAPE
+    assert rp(A, A, -1, 64, None) == Q8_E_SHAPE
+    assert rp(A, A, 0, 64, None) == Q8_OK
+    assert rp(None, A, 10, 64, None) == Q8_E_NULL
+    assert rp(A, None, 10, 64, None) == Q8_E_NULL
+    assert rp(A + 1, A, 10, 64, None) == Q8_E_ALIGN
+    assert rp(A, A + 8, 10, 64, None) == Q8_E_ALIGN        # the R8 buffer needs 16 B
+    mv = lib.q8_0_matvec_r8
+    assert mv(A, A, A, 10, 40, None) == Q8_E_SHAPE
+    assert mv(A, A, A, -1, 64, None) == Q8_E_SHAPE
+    assert mv(A, A, A, 0, 64, None) == Q8_OK
+    assert mv(None, A, A, 10, 64, None) == Q8_E_NULL
+    assert mv(A, None, A, 10, 64, None) == Q8_E_NULL
+    assert mv(A, A, None, 10, 64, None) == Q8_E_NULL
+    assert mv(A + 8, A, A, 10, 64, None) == Q8_E_ALIGN
+    assert mv(A, A + 1, A, 10, 64, None) == Q8_E_ALIGN
+    assert mv(A, A, A + 2, 10, 64, None) == Q8_E_ALIGN
+    assert mv(A, A, A, 10, 32768 + 32, None) == Q8_E_UNSUPPORTED
