@@ -5,12 +5,14 @@ Default workload: a Llama-2-110M-shaped decode step at batch 1 (12 layers of
 wq/wk/wv/wo 768x768, w1/w3 2048x768, w2 768x2048, plus a 32000x768
 classifier; 85 Q8_0 matvecs per step with weights N(0, 0.02) and a fresh
 N(0,1) activation per matvec, quantized to Q8_0 before use), 200 sequential
-steps.  One step = one activation-quantization launch + one launch of the
-decode engine over all 85 products.
+steps.  The weights are repacked once, at load and outside the timed region,
+into the row-interleaved R8 layout; one step is then ONE launch over all 85
+products in which every workgroup quantizes the fp32 activation row of its
+matrix (the native-layout forms of the same step are timed beside it).
 
 Prints ONE JSON line: throughput (algorithmic bytes / s over the timed
-steps), tokens/s, the roofline of the dominant kernel (the decode engine,
-timed with HIP events on the stream it runs on) and the CPU oracle timed on a
+steps), tokens/s, the roofline of the dominant kernel (the step launch, timed
+with HIP events on the stream it runs on) and the CPU oracle timed on a
 bounded sample of the same workload.
 
 Other workloads (one JSON line each), for the per-configuration tables:
@@ -151,10 +153,82 @@ class StepPlan:
             self._step_ws = self.q.q8_0_matmul_f32_step_workspace(descs, self.y.device)
         self.q.q8_0_matmul_f32_step(descs, self._step_ws)
 
+    def setup_r8(self):
+        """Repack every stack into the row-interleaved (R8) layout (m = 1; the
+        stacks' row counts are multiples of 8, so matrix b of a stack starts at
+        b * q8_0_r8_bytes(n, k)) and build the descriptors of one launch."""
+        q = self.q
+        self.w_r8, self.descs_r8 = [], []
+        xoff = yoff = 0
+        for (name, n, k, batch), w in zip(self.stacks, self.w):
+            nb = k // QK
+            mb = q.q8_0_r8_bytes(n, k)
+            wr = torch_empty_u8(batch * mb, w.device)
+            for b in range(batch):
+                q.q8_0_repack_r8(w[b * n:(b + 1) * n], n, k, out=wr[b * mb:(b + 1) * mb])
+            self.w_r8.append(wr)
+            self.descs_r8.append(q.make_r8_desc(wr, (self.xq, xoff), (self.y, yoff), n, k,
+                                                batch=batch, w_batch_stride=mb, x_batch_stride=nb,
+                                                y_batch_stride=n))
+            xoff += batch * nb
+            yoff += batch * n
+
+    def descs_r8_f32(self, x_step):
+        key = ("r8", x_step.data_ptr())
+        if key not in self._f32_descs:
+            descs, xoff, yoff = [], 0, 0
+            for (name, n, k, batch), wr in zip(self.stacks, self.w_r8):
+                mb = self.q.q8_0_r8_bytes(n, k)
+                descs.append(self.q.make_r8_f32_desc(
+                    wr, (x_step, xoff), (self.y, yoff), n, k, batch=batch, w_batch_stride=mb,
+                    x_batch_stride=k, y_batch_stride=n))
+                xoff += batch * k
+                yoff += batch * n
+            self._f32_descs[key] = descs
+        return self._f32_descs[key]
+
+    def cold_r8(self, copies):
+        """Descriptor builders over `copies` separate copies of the R8 weights
+        (each maps an fp32 step input to the descriptors of one launch)."""
+        sets = [self.descs_r8_f32]
+        self._cold_w = []
+        for c in range(1, copies):
+            ws = [w.clone() for w in self.w_r8]
+            self._cold_w.append(ws)
+
+            def build(x_step, ws=ws):
+                descs, xoff, yoff = [], 0, 0
+                for (name, n, k, batch), wr in zip(self.stacks, ws):
+                    descs.append(self.q.make_r8_f32_desc(
+                        wr, (x_step, xoff), (self.y, yoff), n, k, batch=batch,
+                        w_batch_stride=self.q.q8_0_r8_bytes(n, k), x_batch_stride=k,
+                        y_batch_stride=n))
+                    xoff += batch * k
+                    yoff += batch * n
+                return descs
+            sets.append(build)
+        return sets
+
+    def step_r8_one(self, x_step):
+        """The step over the R8 weights as one launch: every workgroup
+        quantizes the fp32 activation row of its matrix into LDS."""
+        self.q.q8_0_matvec_r8_f32_batched(self.descs_r8_f32(x_step), self.y)
+
+    def step_r8(self, x_step):
+        """The step over the R8 weights: the quantize launch, then one launch
+        of every product."""
+        self.q.q8_0_quantize_rows(x_step, y=self.xq)
+        self.q.q8_0_matvec_r8_batched(self.descs_r8, self.y)
+
     def step_fused(self, x_step):
         """The same step as one launch with the activations quantized inside
         (every wave quantizes the rows it needs; slower here, see the JSON)."""
         self.q.q8_0_matmul_f32_batched(self.descs_f32(x_step), self.y)
+
+
+def torch_empty_u8(nbytes, device):
+    import torch
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def capture(fn):
@@ -188,64 +262,79 @@ def time_graph(g, reps=1):
 
 
 def time_steps(plan, xs, steps, warmup):
-    """The K timed steps are captured in one HIP graph (2 launches per step:
-    activation quantization, then the engine over every product of the step)
-    and replayed once inside the timed region.  The per-kernel means come from
-    graphs of K launches of that kernel alone; for reference the same steps are
-    also timed with the quantization fused into the product launch.  Returns a
-    dict of seconds."""
+    """The K timed steps of each form are captured in one HIP graph and
+    replayed once inside the timed region; per-kernel means come from graphs
+    of K launches of that kernel alone.  Forms: native layout with 2 launches
+    per step (quantize, engine), the same with quantization fused into every
+    wave, one launch with each row quantized once (m <= 2); and for m = 1 the
+    R8 layout with 2 launches and with 1 launch.  Returns a dict of seconds
+    (totals over the K steps, per-launch means)."""
     import torch
     n_in = xs.shape[0]
     one = plan.m <= 2
+    r8 = plan.m == 1
+    if r8:
+        plan.setup_r8()
     for i in range(warmup):
         plan.step(xs[i % n_in])
         plan.step_fused(xs[i % n_in])
         if one:
             plan.step_one(xs[i % n_in])
+        if r8:
+            plan.step_r8(xs[i % n_in])
+            plan.step_r8_one(xs[i % n_in])
     torch.cuda.synchronize()
 
-    def all_steps():
-        for i in range(steps):
-            plan.step(xs[i % n_in])
-    total = time_graph(capture(all_steps))
+    def graph_of(fn):
+        def body():
+            for i in range(steps):
+                fn(xs[i % n_in])
+        return time_graph(capture(body))
+
+    out = dict(total=graph_of(plan.step), total_fused=graph_of(plan.step_fused),
+               total_one=graph_of(plan.step_one) if one else None,
+               total_r8=graph_of(plan.step_r8) if r8 else None,
+               total_r8_one=graph_of(plan.step_r8_one) if r8 else None)
 
     def eng_only():
         for _ in range(steps):
             plan.q.q8_0_matmul_batched(plan.descs, plan.y)
-    eng = time_graph(capture(eng_only)) / steps
+    out["eng"] = time_graph(capture(eng_only)) / steps
 
     def qnt_only():
         for i in range(steps):
             plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
-    qnt = time_graph(capture(qnt_only)) / steps
-
-    def all_fused():
-        for i in range(steps):
-            plan.step_fused(xs[i % n_in])
-    total_fused = time_graph(capture(all_fused))
-
-    total_one = None
-    if one:
-        def all_one():
-            for i in range(steps):
-                plan.step_one(xs[i % n_in])
-        total_one = time_graph(capture(all_one))
+    out["qnt"] = time_graph(capture(qnt_only)) / steps
+    if r8:
+        def eng_r8_only():
+            for _ in range(steps):
+                plan.q.q8_0_matvec_r8_batched(plan.descs_r8, plan.y)
+        out["eng_r8"] = time_graph(capture(eng_r8_only)) / steps
 
     # cold reference: consecutive steps read different copies of the weights,
     # together well over the 256 MB Infinity Cache
     copies = max(2, -(-3 * 256 * 2**20 // plan.w_bytes))
-    sets = plan.cold_descs(copies)
+    out["copies"] = copies
+    if r8:
+        sets = plan.cold_r8(copies)
 
-    def all_cold():
-        for i in range(steps):
-            plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
-            plan.q.q8_0_matmul_batched(sets[i % copies], plan.y)
-    for i in range(copies):
-        plan.q.q8_0_matmul_batched(sets[i], plan.y)
-    total_cold = time_graph(capture(all_cold))
+        def all_cold():
+            for i in range(steps):
+                plan.q.q8_0_matvec_r8_f32_batched(sets[i % copies](xs[i % n_in]), plan.y)
+        for i in range(copies):
+            plan.q.q8_0_matvec_r8_f32_batched(sets[i](xs[0]), plan.y)
+    else:
+        sets = plan.cold_descs(copies)
+
+        def all_cold():
+            for i in range(steps):
+                plan.q.q8_0_quantize_rows(xs[i % n_in], y=plan.xq)
+                plan.q.q8_0_matmul_batched(sets[i % copies], plan.y)
+        for i in range(copies):
+            plan.q.q8_0_matmul_batched(sets[i], plan.y)
+    out["total_cold"] = time_graph(capture(all_cold))
     plan._cold_w = []
-    return dict(total=total, eng=eng, qnt=qnt, total_fused=total_fused, total_cold=total_cold,
-                copies=copies, total_one=total_one)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -294,64 +383,98 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
     xs = synth.normal_f32_torch((n_in, m, plan.k_total), 1.0, dev, 0, name, "x")
     torch.cuda.synchronize()
     t = time_steps(plan, xs, args.steps, args.warmup)
-    bytes_step = plan.engine_bytes + plan.quant_bytes
-    value = bytes_step * args.steps / t["total"] / 1e9
-    tok_s = m * args.steps / t["total"]
-    achieved = plan.engine_bytes / t["eng"] / 1e9
-    kernel = ("stream_pair_kernel (decode engine, two tiles per workgroup)" if m == 1 else
-              "stream_flat_kernel (decode engine)" if m == 2 else
-              "stream_mfma_kernel (small-batch decode engine)")
+    K = args.steps
+    two_bytes = plan.engine_bytes + plan.quant_bytes      # quantize launch + engine launch
+    if m == 1:
+        # headline: R8 weights, one launch per step (weights + fp32 rows read,
+        # outputs written)
+        total, step_bytes, launch_bytes = t["total_r8_one"], plan.fused_bytes, plan.fused_bytes
+        launch_s = total / K
+        kernel = ("r8_matvec_kernel<true> (one launch per step over the R8 weights; every "
+                  "workgroup quantizes the fp32 activation row of its matrix)")
+        launches = 1
+    else:
+        total, step_bytes, launch_bytes = t["total"], two_bytes, plan.engine_bytes
+        launch_s = t["eng"]
+        kernel = ("stream_flat_kernel (decode engine)" if m == 2 else
+                  "stream_mfma_kernel (small-batch decode engine)")
+        launches = 2
+    value = step_bytes * K / total / 1e9
+    achieved = launch_bytes / launch_s / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(t["total"] / args.steps * 1e3, 5),
+        "ms_per_step": round(total / K * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 dot, fp32 scale (Q8_0)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init, no checkpoint)",
         "config": {"workload": wl_desc, "batch": m, "products_per_step": sum(
-            b for _, _, _, b in stacks), "launches_per_step": 2,
+            b for _, _, _, b in stacks), "launches_per_step": launches,
             "timing": "HIP graph of the K steps, one replay timed with HIP events",
-            "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": bytes_step},
+            "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": step_bytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(tok_s, 1),
+        "tokens_per_s": round(m * K / total, 1),
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_launch_us": round(t["eng"] * 1e6, 3),
-                     "bytes_per_launch": plan.engine_bytes},
-        "quantize_kernel_avg_us": round(t["qnt"] * 1e6, 3),
-        "cold_reference": {
-            "timing": f"the same steps reading {t['copies']} rotating copies of the weights "
-                      f"({t['copies'] * plan.w_bytes / 2**20:.0f} MiB, > the 256 MB Infinity Cache)",
-            "ms_per_step": round(t["total_cold"] / args.steps * 1e3, 5),
-            "gbs": round(bytes_step * args.steps / t["total_cold"] / 1e9, 1)},
-        "fused_reference": {
-            "timing": "the same steps as one launch each, activations quantized inside it",
-            "ms_per_step": round(t["total_fused"] / args.steps * 1e3, 5),
-            "gbs": round(plan.fused_bytes * args.steps / t["total_fused"] / 1e9, 1)},
+                     "avg_launch_us": round(launch_s * 1e6, 3),
+                     "bytes_per_launch": launch_bytes},
     }
+    if m == 1:
+        out["config"]["weights"] = ("Q8_0, repacked once at load (outside the timed region) into "
+                                    "the row-interleaved R8 layout: the same bytes, moved")
     # context: a plain streaming read of the same number of bytes per launch
     # (q8_read_probe; non-temporal 16-byte loads, no arithmetic)
-    probe_bytes = (plan.engine_bytes + 65535) // 65536 * 65536
+    probe_bytes = (launch_bytes + 65535) // 65536 * 65536
     src = torch.ones(probe_bytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(4096, dtype=torch.int32, device=dev)
-    tp = _time_launches(lambda: q.q8_read_probe(src, sink), args.steps, 5) / args.steps
+    tp = _time_launches(lambda: q.q8_read_probe(src, sink), K, 5) / K
     del src
     out["roofline"]["read_probe_same_bytes"] = {
         "bytes": probe_bytes, "us": round(tp * 1e6, 3), "gbs": round(probe_bytes / tp / 1e9, 1),
-        "engine_over_probe": round(tp / t["eng"], 4)}
+        "kernel_over_probe": round(tp / launch_s, 4)}
+    out["cold_reference"] = {
+        "timing": f"the same steps reading {t['copies']} rotating copies of the weights "
+                  f"({t['copies'] * plan.w_bytes / 2**20:.0f} MiB, > the 256 MB Infinity Cache)",
+        "ms_per_step": round(t["total_cold"] / K * 1e3, 5),
+        "gbs": round(step_bytes * K / t["total_cold"] / 1e9, 1)}
+    if m == 1:
+        out["r8_two_launch_reference"] = {
+            "timing": "R8 weights: quantize launch + one q8_0_matvec_r8_batched launch per step",
+            "ms_per_step": round(t["total_r8"] / K * 1e3, 5),
+            "gbs": round(two_bytes * K / t["total_r8"] / 1e9, 1),
+            "engine_avg_launch_us": round(t["eng_r8"] * 1e6, 3),
+            "engine_gbs": round(plan.engine_bytes / t["eng_r8"] / 1e9, 1)}
+        out["native_layout_reference"] = {
+            "timing": "native Q8_0 rows: quantize launch + one q8_0_matmul_batched launch per "
+                      "step (stream_pair_kernel)",
+            "ms_per_step": round(t["total"] / K * 1e3, 5),
+            "gbs": round(two_bytes * K / t["total"] / 1e9, 1),
+            "engine_avg_launch_us": round(t["eng"] * 1e6, 3),
+            "engine_gbs": round(plan.engine_bytes / t["eng"] / 1e9, 1),
+            "engine_frac": round(plan.engine_bytes / t["eng"] / 1e9 / HBM_PEAK_GBS, 4),
+            "quantize_kernel_avg_us": round(t["qnt"] * 1e6, 3)}
+        nt = os.path.join(ROOT, "profiles", "stream_pair_kernel_llama110m_decode_step.traffic.json")
+        if os.path.exists(nt):
+            out["native_layout_reference"]["engine_traffic"] = read_traffic(nt)
+    else:
+        out["quantize_kernel_avg_us"] = round(t["qnt"] * 1e6, 3)
+    out["fused_reference"] = {
+        "timing": "native rows, one launch per step, every wave quantizing the rows it reads",
+        "ms_per_step": round(t["total_fused"] / K * 1e3, 5),
+        "gbs": round(plan.fused_bytes * K / t["total_fused"] / 1e9, 1)}
     if t["total_one"] is not None:
         out["one_launch_reference"] = {
-            "timing": "the same steps as one launch each, every activation row quantized once "
+            "timing": "native rows, one launch per step, every activation row quantized once "
                       "inside it by the launch's first workgroups",
-            "ms_per_step": round(t["total_one"] / args.steps * 1e3, 5),
-            "gbs": round(plan.fused_bytes * args.steps / t["total_one"] / 1e9, 1)}
+            "ms_per_step": round(t["total_one"] / K * 1e3, 5),
+            "gbs": round(plan.fused_bytes * K / t["total_one"] / 1e9, 1)}
     return out, plan
 
 
@@ -699,7 +822,8 @@ def main():
     ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
                     help="c4b1/c4b16: time the layer-after-layer launches, the grouped "
                          "launches, or both")
-    ap.add_argument("--cpu-sample-steps", type=int, default=200)
+    ap.add_argument("--cpu-sample-steps", type=int, default=1700,
+                    help="steps of the CPU oracle sample (about 10 s of work on 16 host threads)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with the rocprofv3-derived HBM bytes per launch")
     ap.add_argument("--rocpd-summary", default=None, metavar="DB",
@@ -736,7 +860,7 @@ def main():
         return
 
     traffic_file = args.traffic or (os.path.join(ROOT, "profiles",
-                                                "stream_pair_kernel_llama110m_decode_step.traffic.json")
+                                                "r8_matvec_kernel_llama110m_decode_step.traffic.json")
                                     if args.workload == "c2" else None)
     if traffic_file and os.path.exists(traffic_file):
         t = read_traffic(traffic_file)

@@ -146,6 +146,45 @@ int q8_0_repack_r8(const q8_0_block *w, void *w_r8, int64_t n, int64_t k, void *
 int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, int64_t k,
                    void *stream);
 
+/* q8_0_matvec_r8_batched -- several R8 products in one launch (a decode step's
+ * matrices).  Descriptor i computes, for every b < batch:
+ *   y + b*y_batch_stride  =  W_b . (x + b*x_batch_stride)
+ * with W_b the R8 layout at w_r8 + b*w_batch_stride BYTES (a multiple of 16,
+ * at least q8_0_r8_bytes(n, k) when batch > 1), x_batch_stride in blocks,
+ * y_batch_stride in floats (>= n when batch > 1).  Same limits as
+ * q8_0_matvec_r8 per descriptor; n_desc <= 32.  descs is a HOST array.
+ */
+typedef struct q8_0_r8_desc {
+    const void *w_r8;
+    const q8_0_block *x;
+    float *y;
+    int64_t n, k, batch;
+    int64_t w_batch_stride;   /* bytes */
+    int64_t x_batch_stride;   /* blocks */
+    int64_t y_batch_stride;   /* floats */
+} q8_0_r8_desc;
+
+int q8_0_matvec_r8_batched(const q8_0_r8_desc *descs, int64_t n_desc, void *stream);
+
+/* q8_0_matvec_r8_f32_batched -- the same products from fp32 activation rows:
+ * every row is quantized inside the launch by the rule above (the bytes of
+ * q8_0_quantize_rows), so a decode step is one launch.  x + b*x_batch_stride
+ * (floats; x 16-byte aligned, x_batch_stride a multiple of 4) is the fp32 row
+ * of matrix b.  Results are bitwise those of q8_0_quantize_rows followed by
+ * q8_0_matvec_r8_batched.  Same limits otherwise.
+ */
+typedef struct q8_0_r8_f32_desc {
+    const void *w_r8;
+    const float *x;
+    float *y;
+    int64_t n, k, batch;
+    int64_t w_batch_stride;   /* bytes */
+    int64_t x_batch_stride;   /* floats */
+    int64_t y_batch_stride;   /* floats */
+} q8_0_r8_f32_desc;
+
+int q8_0_matvec_r8_f32_batched(const q8_0_r8_f32_desc *descs, int64_t n_desc, void *stream);
+
 /* ---------------------------------------------------------------------------
  * q8_0_matmul_batched -- several independent products in one launch, for
  * sequencing a decode step with few kernel launches (launch count per token

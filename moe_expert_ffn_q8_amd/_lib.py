@@ -38,6 +38,18 @@ class Q8MatmulDesc(ctypes.Structure):
                 ("y_row_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class Q8R8Desc(ctypes.Structure):
+    _fields_ = [("w_r8", _vp), ("x", _vp), ("y", _vp),
+                ("n", _i64), ("k", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_batch_stride", _i64), ("y_batch_stride", _i64)]
+
+
+class Q8R8F32Desc(ctypes.Structure):
+    _fields_ = [("w_r8", _vp), ("x", _vp), ("y", _vp),
+                ("n", _i64), ("k", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_batch_stride", _i64), ("y_batch_stride", _i64)]
+
+
 class Q8UpGateDesc(ctypes.Structure):
     _fields_ = [("w", _vp), ("x", _vp), ("h", _vp),
                 ("n_ff", _i64), ("n_embd", _i64), ("m", _i64), ("batch", _i64),
@@ -88,6 +100,8 @@ _SIGS = {
     "q8_0_r8_bytes": (_i64, [_i64, _i64]),
     "q8_0_repack_r8": (_int, [_vp, _vp, _i64, _i64, _vp]),
     "q8_0_matvec_r8": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "q8_0_matvec_r8_batched": (_int, [ctypes.POINTER(Q8R8Desc), _i64, _vp]),
+    "q8_0_matvec_r8_f32_batched": (_int, [ctypes.POINTER(Q8R8F32Desc), _i64, _vp]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -200,6 +214,46 @@ def q8_0_matvec_r8(w_r8, x, n, k, y=None):
     _check("q8_0_matvec_r8", _lib.q8_0_matvec_r8(_ptr(w_r8), _ptr(x), _ptr(y), n, k,
                                                  _stream(w_r8)))
     return y
+
+
+def make_r8_desc(w_r8, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride=0,
+                 y_batch_stride=0):
+    """One q8_0_r8_desc.  w_r8 (bytes), x (blocks), y (floats) are (tensor,
+    element offset) pairs or tensors; w_batch_stride in bytes, x_batch_stride
+    in blocks, y_batch_stride in floats."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    return Q8R8Desc(addr(w_r8, 1), addr(x, BLOCK_BYTES), addr(y, 4), n, k, batch,
+                    w_batch_stride, x_batch_stride, y_batch_stride)
+
+
+def q8_0_matvec_r8_batched(descs, stream_of):
+    """descs: list of Q8R8Desc; stream_of: a tensor on the target device."""
+    arr = (Q8R8Desc * max(1, len(descs)))(*descs)
+    _check("q8_0_matvec_r8_batched",
+           _lib.q8_0_matvec_r8_batched(arr, len(descs), _stream(stream_of)))
+
+
+def make_r8_f32_desc(w_r8, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride=0,
+                     y_batch_stride=0):
+    """One q8_0_r8_f32_desc.  w_r8 (bytes), x (floats), y (floats) are (tensor,
+    element offset) pairs or tensors; w_batch_stride in bytes, the others in
+    floats."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    return Q8R8F32Desc(addr(w_r8, 1), addr(x, 4), addr(y, 4), n, k, batch,
+                       w_batch_stride, x_batch_stride, y_batch_stride)
+
+
+def q8_0_matvec_r8_f32_batched(descs, stream_of):
+    """descs: list of Q8R8F32Desc; stream_of: a tensor on the target device."""
+    arr = (Q8R8F32Desc * max(1, len(descs)))(*descs)
+    _check("q8_0_matvec_r8_f32_batched",
+           _lib.q8_0_matvec_r8_f32_batched(arr, len(descs), _stream(stream_of)))
 
 
 def q8_0_matmul(w, x, n, k, m, y=None):

@@ -403,17 +403,79 @@ int q8_0_repack_r8(const q8_0_block *w, void *w_r8, int64_t n, int64_t k, void *
                                            as_stream(stream)));
 }
 
+}  // extern "C"
+
+// Validation shared by the R8 entry points; x_f32: activation rows are fp32
+// (x_batch_stride in floats) instead of Q8_0 blocks.
+static int r8_launch(const void *const *w, const void *const *x, float *const *y,
+                     const int64_t *n, const int64_t *k, const int64_t *batch, const int64_t *ws,
+                     const int64_t *xs, const int64_t *ys, int64_t n_desc, bool x_f32,
+                     void *stream)
+{
+    q8::R8Desc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    for (int64_t i = 0; i < n_desc; ++i) {
+        if (int rc = check_k(k[i])) return rc;
+        if (n[i] < 0 || batch[i] < 0) return Q8_E_SHAPE;
+        if (n[i] == 0 || batch[i] == 0) continue;
+        if (!w[i] || !x[i] || !y[i]) return Q8_E_NULL;
+        const int64_t nb = k[i] / kQK;
+        if (batch[i] > 1 && (ws[i] < q8::r8_bytes(n[i], nb) || xs[i] < 0 || ys[i] < n[i]))
+            return Q8_E_SHAPE;
+        if (!aligned(w[i], 16) || !aligned(x[i], x_f32 ? 16 : 2) || !aligned(y[i], 4) ||
+            (batch[i] > 1 && (ws[i] % 16 != 0 || (x_f32 && xs[i] % 4 != 0))))
+            return Q8_E_ALIGN;
+        if (!q8::r8_matvec_ok(n[i], nb, batch[i])) return Q8_E_UNSUPPORTED;
+        q8::R8Desc &o = d[nd++];
+        o.w = (const uint8_t *)w[i];
+        o.x = (const uint8_t *)x[i];
+        o.y = y[i];
+        o.n = n[i]; o.nb = nb; o.batch = batch[i];
+        o.w_bstride = batch[i] > 1 ? ws[i] : 0;
+        o.x_bstride = batch[i] > 1 ? xs[i] * (x_f32 ? 4 : kBB) : 0;
+        o.y_bstride = batch[i] > 1 ? ys[i] : 0;
+    }
+    if (nd == 0) return Q8_OK;
+    return hip_status(q8::launch_r8_matvec(d, nd, x_f32, as_stream(stream)));
+}
+
+template <class Desc>
+static int r8_batched(const Desc *descs, int64_t n_desc, bool x_f32, void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    const void *w[q8::kStreamMaxJobs], *x[q8::kStreamMaxJobs];
+    float *y[q8::kStreamMaxJobs];
+    int64_t n[q8::kStreamMaxJobs], k[q8::kStreamMaxJobs], b[q8::kStreamMaxJobs];
+    int64_t ws[q8::kStreamMaxJobs], xs[q8::kStreamMaxJobs], ys[q8::kStreamMaxJobs];
+    for (int64_t i = 0; i < n_desc; ++i) {
+        w[i] = descs[i].w_r8; x[i] = descs[i].x; y[i] = descs[i].y;
+        n[i] = descs[i].n; k[i] = descs[i].k; b[i] = descs[i].batch;
+        ws[i] = descs[i].w_batch_stride; xs[i] = descs[i].x_batch_stride;
+        ys[i] = descs[i].y_batch_stride;
+    }
+    return r8_launch(w, x, y, n, k, b, ws, xs, ys, n_desc, x_f32, stream);
+}
+
+extern "C" {
+
+int q8_0_matvec_r8_batched(const q8_0_r8_desc *descs, int64_t n_desc, void *stream)
+{
+    return r8_batched(descs, n_desc, false, stream);
+}
+
+int q8_0_matvec_r8_f32_batched(const q8_0_r8_f32_desc *descs, int64_t n_desc, void *stream)
+{
+    return r8_batched(descs, n_desc, true, stream);
+}
+
 int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, int64_t k,
                    void *stream)
 {
-    if (int rc = check_k(k)) return rc;
-    if (n < 0) return Q8_E_SHAPE;
-    if (n == 0) return Q8_OK;
-    if (!w_r8 || !x || !y) return Q8_E_NULL;
-    if (!aligned(w_r8, 16) || !aligned(x, 2) || !aligned(y, 4)) return Q8_E_ALIGN;
-    if (!q8::r8_matvec_ok(n, k / kQK)) return Q8_E_UNSUPPORTED;
-    return hip_status(q8::launch_r8_matvec((const uint8_t *)w_r8, (const uint8_t *)x, y, n,
-                                           k / kQK, as_stream(stream)));
+    const q8_0_r8_desc d = {w_r8, x, y, n, k, 1, 0, 0, 0};
+    return q8_0_matvec_r8_batched(&d, 1, stream);
 }
 
 int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words, void *stream)

@@ -63,9 +63,19 @@ int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t
 constexpr int64_t kR8MaxNb = 1024;   // k <= 32768 (the activation row is staged in LDS, 36 B per block)
 int64_t r8_bytes(int64_t n, int64_t nb);
 int launch_r8_repack(const uint8_t *w, uint8_t *out, int64_t n, int64_t nb, hipStream_t stream);
-bool r8_matvec_ok(int64_t n, int64_t nb);
-int launch_r8_matvec(const uint8_t *w_r8, const uint8_t *x, float *y, int64_t n, int64_t nb,
-                     hipStream_t stream);
+// Matrix-vector products over R8 weights, several descriptors per launch
+// (already validated): `batch` matrices each, strides in bytes (w, x) and
+// floats (y); x_f32: the activation rows are fp32 (16-byte aligned), quantized
+// inside the launch.
+struct R8Desc {
+    const uint8_t *w;
+    const uint8_t *x;
+    float *y;
+    int64_t n, nb, batch;
+    int64_t w_bstride, x_bstride, y_bstride;
+};
+bool r8_matvec_ok(int64_t n, int64_t nb, int64_t batch);
+int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream);
 
 // Streaming-read probe (measurement): reads `bytes` from p, writes one word
 // per workgroup (at most 4096) to sink.

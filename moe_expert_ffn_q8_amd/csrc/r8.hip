@@ -23,6 +23,8 @@
 // (two lanes of 16 codes each, joined by a lane swap), then (d_w*d_x)*s in
 // fp32; a lane accumulates its blocks in ascending order, the four lanes of a
 // row are then added in a fixed tree.
+#include <string.h>
+
 #include "q8_device.h"
 #include "q8_internal.h"
 
@@ -32,20 +34,40 @@ namespace {
 
 constexpr int kR8Rows = 8;
 constexpr int kR8GroupBlockBytes = kR8Rows * kBlockBytes;   // 272 per block column
-constexpr int kR8Threads = 256;
-constexpr int kR8Waves = kR8Threads / kWave;                // one group per wave
+#ifndef Q8_R8_WAVES
+#define Q8_R8_WAVES 4
+#endif
+constexpr int kR8Waves = Q8_R8_WAVES;                       // one group per wave
+constexpr int kR8Threads = kR8Waves * kWave;
+constexpr int kR8QBlocks = kR8Threads / 8;                  // blocks quantized per pass
 #ifndef Q8_R8_SLICES
 #define Q8_R8_SLICES 8
 #endif
 constexpr int kR8Slices = Q8_R8_SLICES;   // 1 KB slices of a group in flight per wave
+constexpr int kR8QuickNb = 64;                              // rows staged from registers
+constexpr int kR8QuickLoads = 16 * kR8QuickNb / kR8Threads;  // 2-byte loads per thread
 
-struct R8Args {
-    const uint8_t *w;    // R8 layout
-    const uint8_t *x;    // one Q8_0 row [nb] blocks
-    float *y;            // [n]
+// One descriptor of a launch: `batch` matrices of n rows of nb blocks in the
+// R8 layout, each with its own activation row and output vector.  Workgroups
+// are numbered across descriptors: a matrix takes wgpm consecutive workgroups
+// of 4 groups each.
+struct R8Job {
+    const uint8_t *w;
+    const uint8_t *x;      // Q8_0 row of matrix 0
+    float *y;
+    int64_t w_bstride;     // bytes between matrices
+    int64_t x_bstride;     // bytes between activation rows
+    int64_t y_bstride;     // floats between output vectors
     int64_t n;
     int nb;
-    int64_t groups;
+    int gpm;               // groups per matrix
+    int wgpm;              // workgroups per matrix
+    int wg0;               // first workgroup of the descriptor
+};
+
+struct R8Args {
+    R8Job job[kStreamMaxJobs];
+    int n_jobs;
 };
 
 // One thread per (group, row, block), block fastest: reads one native block
@@ -76,49 +98,115 @@ __global__ __launch_bounds__(256) void r8_repack_kernel(const uint8_t *__restric
     dst[1] = (u32x4){c[4], c[5], c[6], c[7]};
 }
 
+// XF: the activation rows are fp32 and every workgroup quantizes its row
+// into LDS itself (the bytes of q8_0_quantize_rows), so a decode step needs no
+// separate quantization launch.
+template <bool XF>
 __global__ __launch_bounds__(kR8Threads) void r8_matvec_kernel(const R8Args a)
 {
-    // the activation row, codes realigned to 32 bytes per block, scales as fp32
-    extern __shared__ __align__(16) uint8_t r8_lds[];
-    const int nb = a.nb;
-    uint8_t *xc = r8_lds;
-    float *xd = (float *)(r8_lds + 32 * nb);
-    {
-        uint16_t *xc16 = (uint16_t *)xc;
-        for (int e = threadIdx.x; e < 16 * nb; e += kR8Threads) {
-            const int b = e >> 4, p = e & 15;
-            xc16[16 * b + p] = *(const uint16_t *)(a.x + b * kBlockBytes + 2 + 2 * p);
-        }
-        for (int b = threadIdx.x; b < nb; b += kR8Threads)
-            xd[b] = half_bits_to_float(load_u16(a.x + b * kBlockBytes));
-    }
-    __syncthreads();
-
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * kR8Waves + wave;
-    if (g >= a.groups) return;
+    int j = 0;
+    while (j + 1 < a.n_jobs && (int)blockIdx.x >= a.job[j + 1].wg0) ++j;
+    const R8Job &jb = a.job[j];
+    const int rel = (int)blockIdx.x - jb.wg0;
+    const int mb = rel / jb.wgpm;
+    const int g = (rel - mb * jb.wgpm) * kR8Waves + wave;
+    const bool active = g < jb.gpm;          // the last workgroup of a matrix may hold idle waves
+    const int nb = jb.nb;
 
     // buffer resource bounded to the group: slices past its end read as zero
     const int gbytes = kR8GroupBlockBytes * nb;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)wave_uniform(a.w + g * gbytes), 0, gbytes, kBufferWord3);
+        (void *)wave_uniform(jb.w + mb * jb.w_bstride + (int64_t)g * gbytes), 0,
+        wave_uniform(active ? gbytes : 0), kBufferWord3);
     const int half = lane & 1;
     const int bs = lane >> 4;
     const int code0 = 16 * nb + 16 * lane;     // + 1024 per slice
     const int scale0 = 2 * (lane >> 1);        // + 64 per slice
     const int slices = (nb + 3) >> 2;
 
-    float acc = 0.0f;
-    for (int i0 = 0; i0 < slices; i0 += kR8Slices) {
-        u32x4 c[kR8Slices];
-        uint32_t sb[kR8Slices];
+    u32x4 c[kR8Slices];
+    uint32_t sb[kR8Slices];
+    auto issue = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < kR8Slices; ++u)
             c[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, code0 + 1024 * (i0 + u), 0, kCacheNT);
 #pragma unroll
         for (int u = 0; u < kR8Slices; ++u)
             sb[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, scale0 + 64 * (i0 + u), 0, kCacheNT);
+    };
+    // The activation row goes to LDS: codes realigned to 32 bytes per block,
+    // then the binary16 scale bits.  Up to 64 blocks (k <= 2048) every thread
+    // loads its share into registers first and the group's first slices are
+    // issued behind those loads, so that the LDS writes wait for the row only
+    // (loads complete in issue order) while the weights are in flight.
+    extern __shared__ __align__(16) uint8_t r8_lds[];
+    uint8_t *xc = r8_lds;
+    uint16_t *xc16 = (uint16_t *)xc;
+    uint16_t *xd16 = (uint16_t *)(r8_lds + 32 * nb);
+    const uint8_t *x = jb.x + mb * jb.x_bstride;
+    const int tid = threadIdx.x;
+    if (XF) {
+        // 8 lanes per 32-value block, 4 values each; kR8QBlocks blocks per pass
+        const float *xf = (const float *)x;
+        const int li = tid & 7;
+        const int passes = (nb + kR8QBlocks - 1) / kR8QBlocks;
+        auto quantize_pass = [&](int p, float4 v) {
+            const int b = (tid >> 3) + kR8QBlocks * p;
+            uint32_t codes, dbits;
+            quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+            if (b < nb) {
+                *(uint32_t *)(xc + 32 * b + 4 * li) = codes;
+                if (li == 0) xd16[b] = (uint16_t)dbits;
+            }
+        };
+        auto load_pass = [&](int p) {
+            const int b = min((tid >> 3) + kR8QBlocks * p, nb - 1);
+            return *(const float4 *)(xf + 32 * b + 4 * li);
+        };
+        if (passes <= 2) {
+            const float4 v0 = load_pass(0);
+            const float4 v1 = load_pass(passes > 1 ? 1 : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(0);
+            __builtin_amdgcn_sched_barrier(0);
+            quantize_pass(0, v0);
+            if (passes > 1) quantize_pass(1, v1);
+        } else {
+            for (int p = 0; p < passes; ++p) quantize_pass(p, load_pass(p));
+            issue(0);
+        }
+    } else if (nb <= kR8QuickNb) {
+        uint32_t xv[kR8QuickLoads];
+#pragma unroll
+        for (int u = 0; u < kR8QuickLoads; ++u) {
+            const int e = min(tid + kR8Threads * u, 16 * nb - 1);
+            xv[u] = load_u16(x + (e >> 4) * kBlockBytes + 2 + 2 * (e & 15));
+        }
+        const uint32_t xs = load_u16(x + min(tid, nb - 1) * kBlockBytes);
+        // keep the row's loads, then the weights, then the LDS writes in this order
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kR8QuickLoads; ++u) {
+            const int e = tid + kR8Threads * u;
+            if (e < 16 * nb) xc16[e] = (uint16_t)xv[u];
+        }
+        if (tid < nb) xd16[tid] = (uint16_t)xs;
+    } else {
+        for (int e = tid; e < 16 * nb; e += kR8Threads)
+            xc16[e] = *(const uint16_t *)(x + (e >> 4) * kBlockBytes + 2 + 2 * (e & 15));
+        for (int b = tid; b < nb; b += kR8Threads)
+            xd16[b] = *(const uint16_t *)(x + b * kBlockBytes);
+        issue(0);
+    }
+    __syncthreads();
+    if (!active) return;
+
+    float acc = 0.0f;
+    for (int i0 = 0;;) {
         // every slice of the pass is computed (a branch here would make the
         // compiler wait for each load in turn): slices past the group read as
         // zero codes and their scales are masked, so they add exact zeros
@@ -135,15 +223,18 @@ __global__ __launch_bounds__(kR8Threads) void r8_matvec_kernel(const R8Args a)
             // the other half of the block from the neighbouring lane (quad_perm 1,0,3,2)
             s += __builtin_amdgcn_mov_dpp(s, 0xB1, 0xF, 0xF, false);
             const float dw = live ? half_bits_to_float(sb[u]) : 0.0f;
-            acc = fmaf(dw * xd[bb], (float)s, acc);
+            acc = fmaf(dw * half_bits_to_float(xd16[bb]), (float)s, acc);
         }
+        i0 += kR8Slices;
+        if (i0 >= slices) break;
+        issue(i0);
     }
     // the four lanes of a row (block residues 0..3), fixed order
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
     if ((lane & 0x31) == 0) {
-        const int64_t row = g * kR8Rows + ((lane >> 1) & 7);
-        if (row < a.n) a.y[row] = acc;
+        const int64_t row = (int64_t)g * kR8Rows + ((lane >> 1) & 7);
+        if (row < jb.n) jb.y[mb * jb.y_bstride + row] = acc;
     }
 }
 
@@ -164,23 +255,43 @@ int launch_r8_repack(const uint8_t *w, uint8_t *out, int64_t n, int64_t nb, hipS
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-bool r8_matvec_ok(int64_t n, int64_t nb)
+bool r8_matvec_ok(int64_t n, int64_t nb, int64_t batch)
 {
     // group offsets inside the buffer resource are 32-bit; the activation row
-    // is staged in LDS (36 bytes per block)
-    return nb <= kR8MaxNb && (int64_t)kR8GroupBlockBytes * nb < 0x7fffffffLL &&
-           (n + kR8Rows - 1) / kR8Rows / kR8Waves < 0x7fffffffLL;
+    // is staged in LDS (34 bytes per block); workgroup numbers are 32-bit
+    const int64_t gpm = (n + kR8Rows - 1) / kR8Rows;
+    return nb <= kR8MaxNb && (gpm + kR8Waves - 1) / kR8Waves * batch < 0x7fffffffLL;
 }
 
-int launch_r8_matvec(const uint8_t *w_r8, const uint8_t *x, float *y, int64_t n, int64_t nb,
-                     hipStream_t stream)
+int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream)
 {
     R8Args a;
-    a.w = w_r8; a.x = x; a.y = y; a.n = n; a.nb = (int)nb;
-    a.groups = (n + kR8Rows - 1) / kR8Rows;
-    const int64_t grid = (a.groups + kR8Waves - 1) / kR8Waves;
-    const size_t lds = (size_t)36 * nb;
-    hipLaunchKernelGGL(r8_matvec_kernel, dim3((unsigned)grid), dim3(kR8Threads), lds, stream, a);
+    memset(&a, 0, sizeof(a));
+    int64_t wg = 0;
+    int nb_max = 1;
+    int nj = 0;
+    for (int i = 0; i < n_desc; ++i) {
+        if (d[i].n == 0 || d[i].batch == 0) continue;
+        R8Job &j = a.job[nj++];
+        j.w = d[i].w; j.x = d[i].x; j.y = d[i].y;
+        j.w_bstride = d[i].w_bstride; j.x_bstride = d[i].x_bstride; j.y_bstride = d[i].y_bstride;
+        j.n = d[i].n;
+        j.nb = (int)d[i].nb;
+        j.gpm = (int)((d[i].n + kR8Rows - 1) / kR8Rows);
+        j.wgpm = (j.gpm + kR8Waves - 1) / kR8Waves;
+        j.wg0 = (int)wg;
+        wg += (int64_t)j.wgpm * d[i].batch;
+        if (wg > 0x7fffffffLL) return -4;
+        nb_max = j.nb > nb_max ? j.nb : nb_max;
+    }
+    if (nj == 0) return 0;
+    a.n_jobs = nj;
+    if (x_f32)
+        hipLaunchKernelGGL(r8_matvec_kernel<true>, dim3((unsigned)wg), dim3(kR8Threads),
+                           (size_t)34 * nb_max, stream, a);
+    else
+        hipLaunchKernelGGL(r8_matvec_kernel<false>, dim3((unsigned)wg), dim3(kR8Threads),
+                           (size_t)34 * nb_max, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

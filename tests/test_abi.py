@@ -333,3 +333,44 @@ def test_r8_checks(lib):
     assert mv(A, A + 1, A, 10, 64, None) == Q8_E_ALIGN
     assert mv(A, A, A + 2, 10, 64, None) == Q8_E_ALIGN
     assert mv(A, A, A, 10, 32768 + 32, None) == Q8_E_UNSUPPORTED
+
+
+def test_r8_batched_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_0_matvec_r8_batched
+
+    def call(*descs, n_desc=None):
+        arr = (q.Q8R8Desc * max(1, len(descs)))(*descs)
+        return f(arr, len(descs) if n_desc is None else n_desc, None)
+
+    ok = q.Q8R8Desc(A, A, A, 64, 768, 2, 64 * 24 * 34, 24, 64)
+    assert f(None, 0, None) == Q8_OK
+    assert f(None, 1, None) == Q8_E_NULL
+    assert call(ok, n_desc=-1) == Q8_E_SHAPE
+    assert call(*([ok] * 33)) == Q8_E_UNSUPPORTED
+    assert call(q.Q8R8Desc(A, A, A, 64, 40, 1, 0, 0, 0)) == Q8_E_SHAPE      # k % 32
+    assert call(q.Q8R8Desc(A, A, A, -1, 64, 1, 0, 0, 0)) == Q8_E_SHAPE
+    assert call(q.Q8R8Desc(None, None, None, 0, 64, 1, 0, 0, 0)) == Q8_OK   # empty
+    assert call(q.Q8R8Desc(None, A, A, 8, 64, 1, 0, 0, 0)) == Q8_E_NULL
+    # batch > 1: strides must separate the matrices and outputs
+    assert call(q.Q8R8Desc(A, A, A, 64, 768, 2, 64 * 24 * 34 - 16, 24, 64)) == Q8_E_SHAPE
+    assert call(q.Q8R8Desc(A, A, A, 64, 768, 2, 64 * 24 * 34, 24, 63)) == Q8_E_SHAPE
+    assert call(q.Q8R8Desc(A, A, A, 64, 768, 2, 64 * 24 * 34 + 8, 24, 64)) == Q8_E_ALIGN
+    assert call(q.Q8R8Desc(A + 8, A, A, 64, 768, 1, 0, 0, 0)) == Q8_E_ALIGN
+    assert call(q.Q8R8Desc(A, A, A, 64, 32768 + 32, 1, 0, 0, 0)) == Q8_E_UNSUPPORTED
+
+
+def test_r8_f32_batched_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_0_matvec_r8_f32_batched
+
+    def call(*descs):
+        arr = (q.Q8R8F32Desc * max(1, len(descs)))(*descs)
+        return f(arr, len(descs), None)
+
+    assert f(None, 0, None) == Q8_OK
+    assert call(q.Q8R8F32Desc(A, A + 8, A, 64, 768, 1, 0, 0, 0)) == Q8_E_ALIGN    # fp32 x: 16 B
+    assert call(q.Q8R8F32Desc(A, A, A, 64, 768, 2, 64 * 24 * 34, 770, 64)) == Q8_E_ALIGN
+    assert call(q.Q8R8F32Desc(A, A, A, 64, 768, 2, 64 * 24 * 34, -4, 64)) == Q8_E_SHAPE
+    assert call(q.Q8R8F32Desc(A, A, A, 64, 40, 1, 0, 0, 0)) == Q8_E_SHAPE
+    assert call(q.Q8R8F32Desc(A, A, A, 64, 32768 + 32, 1, 0, 0, 0)) == Q8_E_UNSUPPORTED

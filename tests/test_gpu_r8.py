@@ -103,3 +103,69 @@ def test_r8_limits(q):
     w = torch.zeros(64, dtype=torch.uint8, device="cuda")
     with pytest.raises(q.Q8Error):
         q.q8_0_matvec_r8(w, w, 1, 32768 + 32)
+
+
+def test_r8_batched_step(q, orc):
+    """Several descriptors in one launch, stacks of matrices with gaps between
+    output vectors (the gaps must stay untouched), a ragged row count, and both
+    activation staging paths (k <= 2048 and k = 8192)."""
+    import torch
+    cases = [(777, 768, 3), (64, 2048, 2), (13, 96, 1), (5, 8192, 2), (2048, 768, 2)]
+    descs, refs, keep = [], [], []
+    for ci, (n, k, batch) in enumerate(cases):
+        nb = k // 32
+        mb = q.q8_0_r8_bytes(n, k)
+        ws = [weights_q8(orc, n, k, "r8b", ci, b) for b in range(batch)]
+        xs = acts_q8(orc, batch, k, "r8b-x", ci)
+        wr = torch.cat([q.q8_0_repack_r8(to_gpu(w), n, k) for w in ws])
+        xg = to_gpu(xs.reshape(-1))
+        ys = n + 7                                   # a gap after every output vector
+        y = nan_like((batch * ys,))
+        descs.append(q.make_r8_desc(wr, xg, y, n, k, batch=batch, w_batch_stride=mb,
+                                    x_batch_stride=nb, y_batch_stride=ys))
+        refs.append([orc.matvec_r8(orc.repack_r8(ws[b], n, k), xs[b], n, k)
+                     for b in range(batch)])
+        keep.append((wr, xg, y, n, ys))
+    q.q8_0_matvec_r8_batched(descs, keep[0][0])
+    for (wr, xg, y, n, ys), ref in zip(keep, refs):
+        yy = y.cpu().numpy().reshape(-1, ys)
+        assert np.all(np.isnan(yy[:, n:])), "a gap between output vectors was written"
+        assert_rows_close(yy[:, :n], np.stack(ref))
+
+
+def test_r8_f32_batched_quantizes_inside(q, orc):
+    """fp32 activation rows quantized inside the launch: bitwise equal to
+    q8_0_quantize_rows followed by q8_0_matvec_r8_batched, and within the
+    tolerance of the oracle on the oracle's quantization of the same rows;
+    one and two quantization passes held in registers (k <= 2048) and the
+    looped form (k = 4096, 8192), ragged block counts."""
+    import torch
+    cases = [(777, 768, 3), (64, 2048, 2), (13, 96, 1), (40, 4096, 2), (5, 8192, 1),
+             (100, 1056, 1)]
+    d8, d32, refs, keep = [], [], [], []
+    for ci, (n, k, batch) in enumerate(cases):
+        nb = k // 32
+        mb = q.q8_0_r8_bytes(n, k)
+        ws = [weights_q8(orc, n, k, "r8f", ci, b) for b in range(batch)]
+        xf = synth.normal_f32((batch, k), 1.0, "r8f-x", ci)
+        wr = torch.cat([q.q8_0_repack_r8(to_gpu(w), n, k) for w in ws])
+        xg = to_gpu(xf.reshape(-1))
+        xq = q.q8_0_quantize_rows(xg.view(batch, k))
+        y8 = nan_like((batch * n,))
+        y32 = nan_like((batch * n,))
+        d8.append(q.make_r8_desc(wr, xq, y8, n, k, batch=batch, w_batch_stride=mb,
+                                 x_batch_stride=nb, y_batch_stride=n))
+        d32.append(q.make_r8_f32_desc(wr, xg, y32, n, k, batch=batch, w_batch_stride=mb,
+                                      x_batch_stride=k, y_batch_stride=n))
+        xo = orc.quantize_rows(xf)
+        assert np.array_equal(xq.cpu().numpy(), xo)
+        refs.append(np.stack([orc.matvec_r8(orc.repack_r8(ws[b], n, k), xo[b], n, k)
+                              for b in range(batch)]))
+        keep.append((wr, xg, xq, y8, y32, n, batch))
+    q.q8_0_matvec_r8_batched(d8, keep[0][0])
+    q.q8_0_matvec_r8_f32_batched(d32, keep[0][0])
+    for (wr, xg, xq, y8, y32, n, batch), ref in zip(keep, refs):
+        a = y8.cpu().numpy()
+        b = y32.cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert_rows_close(b.reshape(batch, n), ref)
