@@ -23,6 +23,14 @@ Parity status of each function (the pins live in tests/test_oracle_*.py):
   repack_r8, matvec_r8 ......... pinned (hand-listed byte positions of a small
                                   case, byte multiset, matvec identity with the
                                   native layout)
+  quantize_rows_q8_1 ........... pinned (d and codes equal the pinned Q8_0
+                                  quantizer's, hand-computed s values)
+  kq_scale_min, kq_dequantize .. pinned (hand-packed 6-bit fields and hand-made
+                                  Q4_K / Q5_K super-blocks with values listed
+                                  by hand)
+  kq_matvec .................... pinned (dequantize-then-fp64 numpy product,
+                                  per-sub-block integer-sum identity, exact
+                                  small cases)
 """
 import ctypes
 import os
@@ -75,6 +83,11 @@ def _load():
         "or_r8_bytes": (ctypes.c_int64, [_i64, _i64]),
         "or_repack_r8": (ctypes.c_int, [_u8p, _u8p, _i64, _i64]),
         "or_matvec_r8": (ctypes.c_int, [_u8p, _u8p, _f64p, _i64, _i64]),
+        "or_quantize_rows_q8_1": (ctypes.c_int, [_f32p, _i64, _u8p, _i64, _i64]),
+        "or_kq_scale_min": (None, [_u8p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                   ctypes.POINTER(ctypes.c_int)]),
+        "or_kq_dequantize_rows": (ctypes.c_int, [ctypes.c_int, _u8p, _f64p, _i64, _i64]),
+        "or_kq_matvec": (ctypes.c_int, [ctypes.c_int, _u8p, _u8p, _f64p, _i64, _i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -343,6 +356,60 @@ def matvec_r8(w_r8, x, n, k):
     y = np.empty(n, dtype=np.float64)
     _check(_load().or_matvec_r8(_p(w_r8, _u8p), _p(x, _u8p), _p(y, _f64p), n, k),
            "matvec_r8")
+    return y
+
+
+# --------------------------------------------------------------------------
+# Q8_1 activations and the K-quant weights (Q4_K = type 4, Q5_K = type 5);
+# layouts in q8_oracle.c
+# --------------------------------------------------------------------------
+
+Q8_1_BLOCK_BYTES = 36
+KQ_BLOCK_BYTES = {4: 144, 5: 176}
+QKK = 256
+
+
+def quantize_rows_q8_1(x):
+    """x: fp32 [n_rows][k] (2-D) or [k] -> uint8 [n_rows][k/32*36]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    n_rows, k = x.shape
+    out = np.empty((n_rows, k // QK * Q8_1_BLOCK_BYTES), dtype=np.uint8)
+    _check(_load().or_quantize_rows_q8_1(_p(x, _f32p), k, _p(out, _u8p), n_rows, k),
+           "quantize_rows_q8_1")
+    return out
+
+
+def kq_scale_min(b12, j):
+    b12 = np.ascontiguousarray(b12, dtype=np.uint8)
+    sc, m = ctypes.c_int(), ctypes.c_int()
+    _load().or_kq_scale_min(_p(b12, _u8p), j, ctypes.byref(sc), ctypes.byref(m))
+    return sc.value, m.value
+
+
+def _kq_bytes(t):
+    if t not in KQ_BLOCK_BYTES:
+        raise ValueError(f"unknown K-quant type {t}")
+    return KQ_BLOCK_BYTES[t]
+
+
+def kq_dequantize(t, w, n, k):
+    """Super-blocks uint8 [n][k/256*bytes] -> fp64 [n][k]."""
+    _kq_bytes(t)
+    w = _blocks(w, n * (k // QKK) * KQ_BLOCK_BYTES[t])
+    out = np.empty((n, k), dtype=np.float64)
+    _check(_load().or_kq_dequantize_rows(t, _p(w, _u8p), _p(out, _f64p), n, k), "kq_dequantize")
+    return out
+
+
+def kq_matvec(t, w, x, n, k):
+    """y[n] (fp64) for K-quant weights of type t and one Q8_1 activation row."""
+    _kq_bytes(t)
+    w = _blocks(w, n * (k // QKK) * KQ_BLOCK_BYTES[t])
+    x = _blocks(x, k // QK * Q8_1_BLOCK_BYTES)
+    y = np.empty(n, dtype=np.float64)
+    _check(_load().or_kq_matvec(t, _p(w, _u8p), _p(x, _u8p), _p(y, _f64p), n, k), "kq_matvec")
     return y
 
 

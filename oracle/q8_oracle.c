@@ -461,3 +461,142 @@ int or_matvec_r8(const uint8_t *w_r8, const uint8_t *x, double *y, int64_t n, in
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Q8_1 activations and the 4/5-bit K-quant weight formats                  */
+/* ------------------------------------------------------------------------ */
+
+/* The Gemma-4-on-Xeon page names a second activation quantizer,
+   quantize_row_q8_1_x4_T, beside the Q8_0 one (section on the three-part fix,
+   compile fix), and the other pages run models stored as Q4_K_M and Q5_K_M
+   (the Nemotron review's closing section; the ARM page's server commands).
+   None of them prints a layout.  Readings used here:
+
+   Q8_1 block, 36 bytes: binary16 d, binary16 s, 32 int8 codes.  d and the
+   codes follow the Q8_0 rule exactly; s = binary16(d32 * sum of the codes),
+   with d32 = amax/127 the unrounded fp32 scale, the product in fp32.
+
+   K-quant super-block of 256 values = 8 sub-blocks of 32:
+     Q4_K, 144 bytes: binary16 d, binary16 dmin, 12 bytes of 6-bit sub-block
+       scales sc[8] and mins m[8], 128 bytes of 4-bit codes.
+     Q5_K, 176 bytes: the same 16-byte header, 32 bytes of high bits, then the
+       128 bytes of low 4-bit codes.
+   6-bit fields: for j < 4, sc[j] = b[j] & 63 and m[j] = b[j+4] & 63; for
+   j >= 4, the low 4 bits of sc[j] and m[j] are the low and high nibble of
+   b[j+4], and their top 2 bits are the top 2 bits of b[j-4] and b[j].
+   4-bit codes: sub-blocks 2c and 2c+1 share the 32 bytes at 32c: the low
+   nibble of byte 32c+l is value l of sub-block 2c, the high nibble value l of
+   sub-block 2c+1.  Q5_K adds 16 * bit j of high-bit byte l to value l of
+   sub-block j.
+   Value l of sub-block j: d * sc[j] * q - dmin * m[j]. */
+
+#define OBLK81 36
+#define OQKK 256
+#define OBLK_Q4K 144
+#define OBLK_Q5K 176
+
+void or_quantize_block_q8_1(const float *x, uint8_t *out)
+{
+    uint8_t q0[OBLK];
+    or_quantize_block(x, q0);                 /* d and codes by the Q8_0 rule */
+    float amax = 0.0f;
+    for (int j = 0; j < OQK; j++) {
+        float a = fabsf(x[j]);
+        if (a > amax) amax = a;
+    }
+    float d32 = amax / 127.0f;
+    int sum = 0;
+    for (int j = 0; j < OQK; j++) sum += blk_code(q0, j);
+    uint16_t sh = or_f32_to_f16(d32 * (float)sum);
+    out[0] = q0[0];
+    out[1] = q0[1];
+    out[2] = (uint8_t)(sh & 0xff);
+    out[3] = (uint8_t)(sh >> 8);
+    memcpy(out + 4, q0 + 2, OQK);
+}
+
+int or_quantize_rows_q8_1(const float *x, int64_t row_stride, uint8_t *out,
+                          int64_t n_rows, int64_t k)
+{
+    if (k <= 0 || k % OQK != 0 || n_rows < 0 || row_stride < k) return -2;
+    int64_t nb = k / OQK;
+    for (int64_t r = 0; r < n_rows; r++)
+        for (int64_t b = 0; b < nb; b++)
+            or_quantize_block_q8_1(x + r * row_stride + b * OQK, out + (r * nb + b) * OBLK81);
+    return 0;
+}
+
+static int kq_block_bytes(int type)
+{
+    return type == 4 ? OBLK_Q4K : type == 5 ? OBLK_Q5K : -1;
+}
+
+/* The 6-bit scale and min of sub-block j (0..7) from the 12 packed bytes. */
+void or_kq_scale_min(const uint8_t *b, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = b[j] & 63;
+        *m = b[j + 4] & 63;
+    } else {
+        *sc = (b[j + 4] & 15) | ((b[j - 4] >> 6) << 4);
+        *m = (b[j + 4] >> 4) | ((b[j] >> 6) << 4);
+    }
+}
+
+/* Unsigned code (0..15 or 0..31) of value l of sub-block j. */
+static int kq_code(int type, const uint8_t *blk, int j, int l)
+{
+    const uint8_t *qs = blk + (type == 4 ? 16 : 48);
+    int byte = qs[32 * (j / 2) + l];
+    int q = (j % 2) ? (byte >> 4) : (byte & 15);
+    if (type == 5) q += 16 * ((blk[16 + l] >> j) & 1);
+    return q;
+}
+
+/* Value l of sub-block j in fp64 (exact: at most 22 significant bits each side). */
+static double kq_value(int type, const uint8_t *blk, int j, int l)
+{
+    double d = or_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    double dmin = or_f16_to_f32((uint16_t)(blk[2] | (blk[3] << 8)));
+    int sc, m;
+    or_kq_scale_min(blk + 4, j, &sc, &m);
+    return d * sc * kq_code(type, blk, j, l) - dmin * m;
+}
+
+/* w: [n][k/256] super-blocks -> out fp64 [n][k]. */
+int or_kq_dequantize_rows(int type, const uint8_t *w, double *out, int64_t n, int64_t k)
+{
+    int bb = kq_block_bytes(type);
+    if (bb < 0 || k <= 0 || k % OQKK != 0 || n < 0) return -2;
+    int64_t ns = k / OQKK;
+    for (int64_t i = 0; i < n; i++)
+        for (int64_t s = 0; s < ns; s++)
+            for (int j = 0; j < 8; j++)
+                for (int l = 0; l < OQK; l++)
+                    out[i * k + s * OQKK + j * OQK + l] =
+                        kq_value(type, w + (i * ns + s) * bb, j, l);
+    return 0;
+}
+
+/* y[i] (fp64) = sum over the k values, ascending, of the dequantized weight
+   times the dequantized Q8_1 activation d_x * q_x. */
+int or_kq_matvec(int type, const uint8_t *w, const uint8_t *x, double *y, int64_t n, int64_t k)
+{
+    int bb = kq_block_bytes(type);
+    if (bb < 0 || k <= 0 || k % OQKK != 0 || n < 0) return -2;
+    int64_t ns = k / OQKK;
+    for (int64_t i = 0; i < n; i++) {
+        double acc = 0.0;
+        for (int64_t s = 0; s < ns; s++) {
+            const uint8_t *blk = w + (i * ns + s) * bb;
+            for (int j = 0; j < 8; j++) {
+                const uint8_t *xb = x + (s * 8 + j) * OBLK81;
+                double dx = or_f16_to_f32((uint16_t)(xb[0] | (xb[1] << 8)));
+                for (int l = 0; l < OQK; l++)
+                    acc += kq_value(type, blk, j, l) * (dx * (double)(int8_t)xb[4 + l]);
+            }
+        }
+        y[i] = acc;
+    }
+    return 0;
+}
