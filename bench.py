@@ -642,6 +642,80 @@ def run_extra(args, q, synth):
             res["cpu_baseline"] = {"value": round(reps * nb_cpu / dt / 1e9, 3), "unit": "GB/s",
                                    "cores": 1, "kind": "oracle",
                                    "sample": f"{reps} R8 matvecs of 4096 x 2048, {dt:.1f} s"}
+    elif wl == "kq":
+        # 4/5-bit K-quant weights (Q4_K, Q5_K) against Q8_1 activations: the
+        # vocabulary projection and the Llama-110M-shaped step (85 products:
+        # one Q8_1 quantize launch + one kq_matvec_batched launch)
+        out_t = {}
+        for t in (4, 5):
+            bb = synth.KQ_BYTES[t]
+            n, k = 262144, 2048
+            w = synth.kq_blocks_torch(t, n, k, dev, 0, wl, t)
+            xf = synth.normal_f32_torch((1, k), 1.0, dev, 0, wl, "x", t)
+            x = q.q8_1_quantize_rows(xf)
+            y = torch.empty(n, dtype=torch.float32, device=dev)
+            tv = _time_launches(lambda: q.kq_matvec(t, w, x, n, k, y=y), args.steps,
+                                args.warmup) / args.steps
+            vb = n * (k // 256) * bb + (k // 32) * 36 + 4 * n
+            del w
+            # the step: stacks as in the default workload
+            ws, descs = [], []
+            k_tot = sum(kk * b for _, nn, kk, b in LLAMA_STACKS)
+            n_tot = sum(nn * b for _, nn, kk, b in LLAMA_STACKS)
+            xs = synth.normal_f32_torch((1, k_tot), 1.0, dev, 0, wl, "step-x", t)
+            xq = torch.empty(k_tot // 32 * 36, dtype=torch.uint8, device=dev)
+            ys = torch.empty(n_tot, dtype=torch.float32, device=dev)
+            xoff = yoff = 0
+            wbytes = 0
+            for name, nn, kk, b in LLAMA_STACKS:
+                wt = synth.kq_blocks_torch(t, b * nn, kk, dev, 0, wl, name, t)
+                ws.append(wt)
+                wbytes += wt.numel()
+                descs.append(q.make_kq_desc(wt, (xq, xoff * 36), (ys, yoff), nn, kk, batch=b,
+                                            w_batch_stride=nn * (kk // 256),
+                                            x_batch_stride=kk // 32, y_batch_stride=nn))
+                xoff += b * kk // 32
+                yoff += b * nn
+
+            def kstep():
+                q.q8_1_quantize_rows(xs, y=xq.view(1, -1))
+                q.kq_matvec_batched(t, descs, xq)
+            ts = _time_launches(kstep, args.steps, args.warmup) / args.steps
+            te = _time_launches(lambda: q.kq_matvec_batched(t, descs, xq), args.steps,
+                                args.warmup) / args.steps
+            sb = wbytes + xq.numel() + 4 * n_tot
+            out_t["q4_k" if t == 4 else "q5_k"] = {
+                "bits_per_weight": bb * 8 / 256,
+                "vocab_262144x2048": {"us": round(tv * 1e6, 3), "bytes_per_launch": vb,
+                                      "gbs": round(vb / tv / 1e9, 1),
+                                      "frac": round(vb / tv / 1e9 / HBM_PEAK_GBS, 4)},
+                "llama110m_step": {"us_per_step": round(ts * 1e6, 3),
+                                   "tokens_per_s": round(1 / ts, 1),
+                                   "engine_us": round(te * 1e6, 3), "engine_bytes": sb,
+                                   "engine_gbs": round(sb / te / 1e9, 1),
+                                   "engine_frac": round(sb / te / 1e9 / HBM_PEAK_GBS, 4)}}
+            del ws
+        res.update(formats=out_t)
+        v4 = out_t["q4_k"]["vocab_262144x2048"]
+        res.update(roofline={"bound": "hbm", "kernel": "kq_matvec_kernel<4> (Q4_K, vocabulary "
+                             "projection 262144 x 2048)", "achieved": v4["gbs"],
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": v4["frac"],
+                             "traffic": None})
+        if not args.no_cpu_baseline:
+            import oracle
+            n, k = 2048, 2048
+            wh = synth.kq_blocks(4, n, k, "cpu-kq")
+            xh = oracle.quantize_rows_q8_1(synth.normal_f32((1, k), 1.0, "cpu-kq-x"))
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 5.0:
+                oracle.kq_matvec(4, wh, xh, n, k)
+                reps += 1
+            dt = time.perf_counter() - t0
+            nb_cpu = wh.nbytes + xh.nbytes + 4 * n
+            res["cpu_baseline"] = {"value": round(reps * nb_cpu / dt / 1e9, 3), "unit": "GB/s",
+                                   "cores": 1, "kind": "oracle",
+                                   "sample": f"{reps} Q4_K matvecs of 2048 x 2048, {dt:.1f} s"}
     elif wl == "c5a":
         m, n, k = 512, 14336, 4096
         w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, wl, "w"))
@@ -815,7 +889,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
                     choices=["c1", "c2", "c3", "c4b1", "c4b16", "c4p", "c5a", "c5b", "copy", "readbw",
-                             "ffn", "r8"])
+                             "ffn", "r8", "kq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-bytes", type=int, default=0,
                     help="readbw workload: bytes per read launch (default 2 GiB)")

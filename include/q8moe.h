@@ -186,6 +186,56 @@ typedef struct q8_0_r8_f32_desc {
 int q8_0_matvec_r8_f32_batched(const q8_0_r8_f32_desc *descs, int64_t n_desc, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Q8_1 activations and 4/5-bit K-quant weights.  [XEON] (three-part fix,
+ * compile fix) names a Q8_1 activation quantizer beside the Q8_0 one; the
+ * other pages serve Q4_K_M / Q5_K_M model files ([NEMO] closing section; the
+ * ARM page's server commands).  No page prints a layout; this library reads:
+ *   Q8_1 block, 36 bytes: binary16 d, binary16 s, 32 int8 codes.  d and the
+ *     codes follow the Q8_0 rule; s = binary16(d32 * sum of the codes), d32 =
+ *     amax/127 unrounded, the product in fp32.
+ *   Super-block of 256 values, 8 sub-blocks of 32:
+ *     Q4_K (type 4), 144 bytes: binary16 d, binary16 dmin, 12 bytes of 6-bit
+ *       sub-block scales sc[8] and mins m[8] (j < 4: sc = byte j & 63,
+ *       m = byte j+4 & 63; j >= 4: low 4 bits from the low / high nibble of
+ *       byte j+4, top 2 bits from the top bits of byte j-4 / byte j), then
+ *       128 bytes of 4-bit codes (byte 32c+l: low nibble = value l of
+ *       sub-block 2c, high nibble = value l of sub-block 2c+1);
+ *     Q5_K (type 5), 176 bytes: the same 16-byte header, 32 bytes of high bits
+ *       (bit j of byte l adds 16 to value l of sub-block j), then the 128
+ *       bytes of low 4-bit codes.
+ *   Value l of sub-block j = d * sc[j] * q - dmin * m[j].
+ *
+ * q8_1_quantize_rows -- fp32 rows (16-byte aligned, row stride a multiple of
+ * 4 floats, >= k) -> Q8_1 [n_rows][k/32] blocks (4-byte aligned).
+ *
+ * kq_matvec_batched -- y + b*y_batch_stride = W_b . x_b for every descriptor
+ * and b < batch: W_b = w + b*w_batch_stride SUPER-BLOCKS of K-quant `type`
+ * ([n][k/256], 16-byte aligned), x_b = x + b*x_batch_stride Q8_1 blocks (one
+ * row of k/32), y fp32 [n] (written); per sub-block the exact int32 sums of
+ * code products and of activation codes, then (d*sc*d_x)*S - (dmin*m*d_x)*Q
+ * in fp32 (s of the Q8_1 blocks is not read).  k % 256 == 0, k <= 8192
+ * (Q8_E_UNSUPPORTED above, and for a type other than 4 or 5); n_desc <= 32;
+ * with batch > 1 the strides must separate matrices and outputs (Q8_E_SHAPE).
+ * q4_k_matvec / q5_k_matvec -- one product.
+ */
+int q8_1_quantize_rows(const float *x, int64_t x_row_stride, void *y, int64_t n_rows,
+                       int64_t k, void *stream);
+
+typedef struct kq_matvec_desc {
+    const void *w;
+    const void *x;
+    float *y;
+    int64_t n, k, batch;
+    int64_t w_batch_stride;   /* super-blocks */
+    int64_t x_batch_stride;   /* Q8_1 blocks */
+    int64_t y_batch_stride;   /* floats */
+} kq_matvec_desc;
+
+int kq_matvec_batched(int type, const kq_matvec_desc *descs, int64_t n_desc, void *stream);
+int q4_k_matvec(const void *w, const void *x, float *y, int64_t n, int64_t k, void *stream);
+int q5_k_matvec(const void *w, const void *x, float *y, int64_t n, int64_t k, void *stream);
+
+/* ---------------------------------------------------------------------------
  * q8_0_matmul_batched -- several independent products in one launch, for
  * sequencing a decode step with few kernel launches (launch count per token
  * is the cost the [NARR] kernels-per-token table tracks).  Descriptor i

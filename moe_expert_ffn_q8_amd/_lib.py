@@ -50,6 +50,12 @@ class Q8R8F32Desc(ctypes.Structure):
                 ("w_batch_stride", _i64), ("x_batch_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class KqMatvecDesc(ctypes.Structure):
+    _fields_ = [("w", _vp), ("x", _vp), ("y", _vp),
+                ("n", _i64), ("k", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_batch_stride", _i64), ("y_batch_stride", _i64)]
+
+
 class Q8UpGateDesc(ctypes.Structure):
     _fields_ = [("w", _vp), ("x", _vp), ("h", _vp),
                 ("n_ff", _i64), ("n_embd", _i64), ("m", _i64), ("batch", _i64),
@@ -102,6 +108,10 @@ _SIGS = {
     "q8_0_matvec_r8": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "q8_0_matvec_r8_batched": (_int, [ctypes.POINTER(Q8R8Desc), _i64, _vp]),
     "q8_0_matvec_r8_f32_batched": (_int, [ctypes.POINTER(Q8R8F32Desc), _i64, _vp]),
+    "q8_1_quantize_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp]),
+    "kq_matvec_batched": (_int, [_int, ctypes.POINTER(KqMatvecDesc), _i64, _vp]),
+    "q4_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "q5_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -254,6 +264,57 @@ def q8_0_matvec_r8_f32_batched(descs, stream_of):
     arr = (Q8R8F32Desc * max(1, len(descs)))(*descs)
     _check("q8_0_matvec_r8_f32_batched",
            _lib.q8_0_matvec_r8_f32_batched(arr, len(descs), _stream(stream_of)))
+
+
+Q8_1_BLOCK_BYTES = 36
+KQ_BLOCK_BYTES = {4: 144, 5: 176}
+
+
+def q8_1_quantize_rows(x, k=None, y=None):
+    """x: fp32 [n_rows][stride] (or [k]) -> y: uint8 [n_rows][k/32*36] (Q8_1)."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x: GPU fp32 with unit column stride")
+    n_rows = x.shape[0]
+    k = x.shape[1] if k is None else k
+    if y is None:
+        y = torch.empty((n_rows, k // QK * Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    _need(y, torch.uint8, "y")
+    _check("q8_1_quantize_rows", _lib.q8_1_quantize_rows(
+        _ptr(x), x.stride(0) if n_rows > 1 else k, _ptr(y), n_rows, k, _stream(x)))
+    return y
+
+
+def kq_matvec(t, w, x, n, k, y=None):
+    """One product over K-quant weights (t = 4: Q4_K, t = 5: Q5_K) and a Q8_1 row."""
+    _need(w, torch.uint8, "w")
+    _need(x, torch.uint8, "x")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, "y")
+    fn = {4: _lib.q4_k_matvec, 5: _lib.q5_k_matvec}.get(t)
+    if fn is None:
+        raise ValueError(f"unknown K-quant type {t}")
+    _check("q4_k_matvec" if t == 4 else "q5_k_matvec",
+           fn(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(w)))
+    return y
+
+
+def make_kq_desc(w, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride=0, y_batch_stride=0):
+    """One kq_matvec_desc.  w (bytes), x (bytes), y (floats) are (tensor, element
+    offset) pairs or tensors; strides in super-blocks, Q8_1 blocks, floats."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    return KqMatvecDesc(addr(w, 1), addr(x, 1), addr(y, 4), n, k, batch, w_batch_stride,
+                        x_batch_stride, y_batch_stride)
+
+
+def kq_matvec_batched(t, descs, stream_of):
+    arr = (KqMatvecDesc * max(1, len(descs)))(*descs)
+    _check("kq_matvec_batched", _lib.kq_matvec_batched(t, arr, len(descs), _stream(stream_of)))
 
 
 def q8_0_matmul(w, x, n, k, m, y=None):

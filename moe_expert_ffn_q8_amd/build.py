@@ -19,7 +19,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["quantize.hip", "stream.hip", "step.hip", "ffn.hip", "small_m.hip", "moe.hip",
-           "moe_gemm.hip", "gemm.hip", "r8.hip", "probe.hip", "abi.cpp"]
+           "moe_gemm.hip", "gemm.hip", "r8.hip", "kquant.hip", "probe.hip",
+           "abi.cpp"]
 
 # no packed fp32 instructions in device code; MFMA results in VGPRs (the
 # rescale of each int32 block tile then needs no accumulator-register copies)

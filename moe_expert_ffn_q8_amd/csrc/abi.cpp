@@ -478,6 +478,63 @@ int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, i
     return q8_0_matvec_r8_batched(&d, 1, stream);
 }
 
+int q8_1_quantize_rows(const float *x, int64_t x_row_stride, void *y, int64_t n_rows, int64_t k,
+                       void *stream)
+{
+    if (int rc = check_k(k)) return rc;
+    if (n_rows < 0 || x_row_stride < k) return Q8_E_SHAPE;
+    if (n_rows == 0) return Q8_OK;
+    if (!x || !y) return Q8_E_NULL;
+    if (!aligned(x, 16) || x_row_stride % 4 != 0 || !aligned(y, 4)) return Q8_E_ALIGN;
+    return hip_status(q8::launch_q8_1_quantize_rows(x, x_row_stride, y, n_rows, k,
+                                                    as_stream(stream)));
+}
+
+int kq_matvec_batched(int type, const kq_matvec_desc *descs, int64_t n_desc, void *stream)
+{
+    if (type != 4 && type != 5) return Q8_E_UNSUPPORTED;
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    const int64_t bb = type == 4 ? 144 : 176;
+    q8::KqDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    for (int64_t i = 0; i < n_desc; ++i) {
+        const kq_matvec_desc &s = descs[i];
+        if (s.k <= 0 || s.k % 256 != 0 || s.n < 0 || s.batch < 0) return Q8_E_SHAPE;
+        if (s.n == 0 || s.batch == 0) continue;
+        if (!s.w || !s.x || !s.y) return Q8_E_NULL;
+        if (s.batch > 1 && (s.w_batch_stride < s.n * (s.k / 256) || s.x_batch_stride < 0 ||
+                            s.y_batch_stride < s.n))
+            return Q8_E_SHAPE;
+        if (!aligned(s.w, 16) || !aligned(s.x, 4) || !aligned(s.y, 4)) return Q8_E_ALIGN;
+        if (!q8::kq_matvec_ok(type, s.n, s.k, s.batch)) return Q8_E_UNSUPPORTED;
+        q8::KqDesc &o = d[nd++];
+        o.w = (const uint8_t *)s.w;
+        o.x = (const uint8_t *)s.x;
+        o.y = s.y;
+        o.n = s.n; o.k = s.k; o.batch = s.batch;
+        o.w_bstride = s.batch > 1 ? s.w_batch_stride * bb : 0;
+        o.x_bstride = s.batch > 1 ? s.x_batch_stride * 36 : 0;
+        o.y_bstride = s.batch > 1 ? s.y_batch_stride : 0;
+    }
+    if (nd == 0) return Q8_OK;
+    return hip_status(q8::launch_kq_matvec(type, d, nd, as_stream(stream)));
+}
+
+int q4_k_matvec(const void *w, const void *x, float *y, int64_t n, int64_t k, void *stream)
+{
+    const kq_matvec_desc d = {w, x, y, n, k, 1, 0, 0, 0};
+    return kq_matvec_batched(4, &d, 1, stream);
+}
+
+int q5_k_matvec(const void *w, const void *x, float *y, int64_t n, int64_t k, void *stream)
+{
+    const kq_matvec_desc d = {w, x, y, n, k, 1, 0, 0, 0};
+    return kq_matvec_batched(5, &d, 1, stream);
+}
+
 int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words, void *stream)
 {
     if (bytes < 0 || sink_words < 0) return Q8_E_SHAPE;

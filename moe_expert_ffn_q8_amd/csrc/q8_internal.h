@@ -77,6 +77,22 @@ struct R8Desc {
 bool r8_matvec_ok(int64_t n, int64_t nb, int64_t batch);
 int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream);
 
+// Q8_1 activations (36-byte blocks: binary16 d and s, 32 codes) and the
+// decode product over K-quant weights (type 4 = Q4_K, 144-byte super-blocks
+// of 256 values; type 5 = Q5_K, 176 bytes) against one Q8_1 row per matrix.
+constexpr int64_t kKqMaxS = 32;      // super-blocks per row: k <= 8192
+struct KqDesc {
+    const uint8_t *w;
+    const uint8_t *x;
+    float *y;
+    int64_t n, k, batch;
+    int64_t w_bstride, x_bstride, y_bstride;   // bytes, bytes, floats
+};
+int launch_q8_1_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_rows,
+                              int64_t k, hipStream_t stream);
+bool kq_matvec_ok(int type, int64_t n, int64_t k, int64_t batch);
+int launch_kq_matvec(int type, const KqDesc *d, int n_desc, hipStream_t stream);
+
 // Streaming-read probe (measurement): reads `bytes` from p, writes one word
 // per workgroup (at most 4096) to sink.
 int launch_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words,

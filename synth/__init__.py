@@ -79,3 +79,37 @@ def normal_f32_torch(shape, sigma, device, *key, chunk=1 << 26):
         e = min(flat.numel(), s + chunk)
         flat[s:e].normal_(mean=0.0, std=float(sigma), generator=gen)
     return out
+
+
+# K-quant super-blocks (256 values): random bytes everywhere except the two
+# binary16 super-block scales, which get positive values of the size that
+# N(0, 0.02) weights would give (d ~ 0.02/40 for the 6-bit scales, dmin ~
+# 0.02/20 for the mins).  Byte counts per super-block: 144 (Q4_K), 176 (Q5_K).
+KQ_BYTES = {4: 144, 5: 176}
+
+
+def kq_blocks(t, n, k, *key):
+    """uint8 [n][k/256 * bytes] random super-blocks of type t (4 or 5)."""
+    g = rng(*key)
+    w = g.integers(0, 256, size=(n, k // 256, KQ_BYTES[t]), dtype=np.uint8)
+    d = (g.uniform(0.5, 1.5, size=(n, k // 256)) * (0.02 / 40)).astype(np.float16).view(np.uint16)
+    dm = (g.uniform(0.5, 1.5, size=(n, k // 256)) * (0.02 / 20)).astype(np.float16).view(np.uint16)
+    w[..., 0], w[..., 1] = d & 0xFF, d >> 8
+    w[..., 2], w[..., 3] = dm & 0xFF, dm >> 8
+    return w.reshape(n, -1)
+
+
+def kq_blocks_torch(t, n, k, device, *key):
+    """The same kind of super-blocks drawn on `device` with torch's generator
+    (not bit-identical to kq_blocks)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(key_seed(*key))
+    nb = KQ_BYTES[t]
+    w = torch.randint(0, 256, (n, k // 256, nb), dtype=torch.uint8, device=device, generator=gen)
+    u = torch.empty((n, k // 256, 2), dtype=torch.float32, device=device).uniform_(0.5, 1.5,
+                                                                                 generator=gen)
+    u[..., 0] *= 0.02 / 40
+    u[..., 1] *= 0.02 / 20
+    w[..., 0:4] = u.to(torch.float16).contiguous().view(torch.uint8).view(n, k // 256, 4)
+    return w.view(n, -1)

@@ -374,3 +374,32 @@ def test_r8_f32_batched_checks(lib):
     assert call(q.Q8R8F32Desc(A, A, A, 64, 768, 2, 64 * 24 * 34, -4, 64)) == Q8_E_SHAPE
     assert call(q.Q8R8F32Desc(A, A, A, 64, 40, 1, 0, 0, 0)) == Q8_E_SHAPE
     assert call(q.Q8R8F32Desc(A, A, A, 64, 32768 + 32, 1, 0, 0, 0)) == Q8_E_UNSUPPORTED
+
+
+def test_kq_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_1_quantize_rows
+    assert f(A, 64, A, 1, 33, None) == Q8_E_SHAPE
+    assert f(A, 16, A, 1, 32, None) == Q8_E_SHAPE
+    assert f(A, 64, A, 0, 64, None) == Q8_OK
+    assert f(None, 64, A, 1, 64, None) == Q8_E_NULL
+    assert f(A + 4, 64, A, 1, 64, None) == Q8_E_ALIGN
+    assert f(A, 64, A + 2, 1, 64, None) == Q8_E_ALIGN
+    for mv in (lib.q4_k_matvec, lib.q5_k_matvec):
+        assert mv(A, A, A, 10, 128, None) == Q8_E_SHAPE           # k % 256
+        assert mv(A, A, A, -1, 256, None) == Q8_E_SHAPE
+        assert mv(A, A, A, 0, 256, None) == Q8_OK
+        assert mv(None, A, A, 10, 256, None) == Q8_E_NULL
+        assert mv(A + 8, A, A, 10, 256, None) == Q8_E_ALIGN
+        assert mv(A, A + 2, A, 10, 256, None) == Q8_E_ALIGN
+        assert mv(A, A, A + 2, 10, 256, None) == Q8_E_ALIGN
+        assert mv(A, A, A, 10, 8192 + 256, None) == Q8_E_UNSUPPORTED
+    g = lib.kq_matvec_batched
+
+    def call(t, *descs):
+        arr = (q.KqMatvecDesc * max(1, len(descs)))(*descs)
+        return g(t, arr, len(descs), None)
+
+    assert call(6, q.KqMatvecDesc(A, A, A, 8, 256, 1, 0, 0, 0)) == Q8_E_UNSUPPORTED
+    assert call(4, q.KqMatvecDesc(A, A, A, 8, 256, 2, 7, 8, 8)) == Q8_E_SHAPE     # w stride
+    assert call(4, q.KqMatvecDesc(A, A, A, 8, 256, 2, 8, 8, 7)) == Q8_E_SHAPE     # y stride
