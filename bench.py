@@ -697,10 +697,12 @@ def run_extra(args, q, synth):
             del ws
         res.update(formats=out_t)
         v4 = out_t["q4_k"]["vocab_262144x2048"]
+        tf = os.path.join(ROOT, "profiles", "kq_matvec_kernel_q4k_vocab.traffic.json")
         res.update(roofline={"bound": "hbm", "kernel": "kq_matvec_kernel<4> (Q4_K, vocabulary "
                              "projection 262144 x 2048)", "achieved": v4["gbs"],
                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": v4["frac"],
-                             "traffic": None})
+                             "avg_launch_us": v4["us"], "bytes_per_launch": v4["bytes_per_launch"],
+                             "traffic": read_traffic(tf) if os.path.exists(tf) else None})
         if not args.no_cpu_baseline:
             import oracle
             n, k = 2048, 2048
