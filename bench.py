@@ -154,9 +154,10 @@ class StepPlan:
         self.q.q8_0_matmul_f32_step(descs, self._step_ws)
 
     def setup_r8(self):
-        """Repack every stack into the row-interleaved (R8) layout (m = 1; the
-        stacks' row counts are multiples of 8, so matrix b of a stack starts at
-        b * q8_0_r8_bytes(n, k)) and build the descriptors of one launch."""
+        """Repack every stack into the row-interleaved (R8) layout (matrix b of
+        a stack starts at b * q8_0_r8_bytes(n, k)) and build the descriptors of
+        one launch: the matvec engine at m = 1, the small-batch matrix-core
+        engine above."""
         q = self.q
         self.w_r8, self.descs_r8 = [], []
         xoff = yoff = 0
@@ -167,11 +168,23 @@ class StepPlan:
             for b in range(batch):
                 q.q8_0_repack_r8(w[b * n:(b + 1) * n], n, k, out=wr[b * mb:(b + 1) * mb])
             self.w_r8.append(wr)
-            self.descs_r8.append(q.make_r8_desc(wr, (self.xq, xoff), (self.y, yoff), n, k,
-                                                batch=batch, w_batch_stride=mb, x_batch_stride=nb,
-                                                y_batch_stride=n))
+            if self.m == 1:
+                self.descs_r8.append(q.make_r8_desc(wr, (self.xq, xoff), (self.y, yoff), n, k,
+                                                    batch=batch, w_batch_stride=mb,
+                                                    x_batch_stride=nb, y_batch_stride=n))
+            else:
+                self.descs_r8.append(q.make_r8_mm_desc(
+                    wr, (self.xq, xoff), (self.y, yoff), n, k, m=self.m, batch=batch,
+                    w_batch_stride=mb, x_row_stride=self.nb_total, x_batch_stride=nb,
+                    y_row_stride=self.n_out, y_batch_stride=n))
             xoff += batch * nb
             yoff += batch * n
+
+    def r8_engine(self):
+        if self.m == 1:
+            self.q.q8_0_matvec_r8_batched(self.descs_r8, self.y)
+        else:
+            self.q.q8_0_matmul_r8_batched(self.descs_r8, self.y)
 
     def descs_r8_f32(self, x_step):
         key = ("r8", x_step.data_ptr())
@@ -218,7 +231,7 @@ class StepPlan:
         """The step over the R8 weights: the quantize launch, then one launch
         of every product."""
         self.q.q8_0_quantize_rows(x_step, y=self.xq)
-        self.q.q8_0_matvec_r8_batched(self.descs_r8, self.y)
+        self.r8_engine()
 
     def step_fused(self, x_step):
         """The same step as one launch with the activations quantized inside
@@ -272,7 +285,8 @@ def time_steps(plan, xs, steps, warmup):
     import torch
     n_in = xs.shape[0]
     one = plan.m <= 2
-    r8 = plan.m == 1
+    r8 = plan.m <= 16
+    r8_one = plan.m == 1
     if r8:
         plan.setup_r8()
     for i in range(warmup):
@@ -282,6 +296,7 @@ def time_steps(plan, xs, steps, warmup):
             plan.step_one(xs[i % n_in])
         if r8:
             plan.step_r8(xs[i % n_in])
+        if r8_one:
             plan.step_r8_one(xs[i % n_in])
     torch.cuda.synchronize()
 
@@ -294,7 +309,7 @@ def time_steps(plan, xs, steps, warmup):
     out = dict(total=graph_of(plan.step), total_fused=graph_of(plan.step_fused),
                total_one=graph_of(plan.step_one) if one else None,
                total_r8=graph_of(plan.step_r8) if r8 else None,
-               total_r8_one=graph_of(plan.step_r8_one) if r8 else None)
+               total_r8_one=graph_of(plan.step_r8_one) if r8_one else None)
 
     def eng_only():
         for _ in range(steps):
@@ -308,14 +323,14 @@ def time_steps(plan, xs, steps, warmup):
     if r8:
         def eng_r8_only():
             for _ in range(steps):
-                plan.q.q8_0_matvec_r8_batched(plan.descs_r8, plan.y)
+                plan.r8_engine()
         out["eng_r8"] = time_graph(capture(eng_r8_only)) / steps
 
     # cold reference: consecutive steps read different copies of the weights,
     # together well over the 256 MB Infinity Cache
     copies = max(2, -(-3 * 256 * 2**20 // plan.w_bytes))
     out["copies"] = copies
-    if r8:
+    if r8_one:
         sets = plan.cold_r8(copies)
 
         def all_cold():
@@ -465,6 +480,14 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
             out["native_layout_reference"]["engine_traffic"] = read_traffic(nt)
     else:
         out["quantize_kernel_avg_us"] = round(t["qnt"] * 1e6, 3)
+        if t["total_r8"] is not None:
+            out["r8_layout_reference"] = {
+                "timing": "R8 weights: quantize launch + one q8_0_matmul_r8_batched launch per "
+                          "step (r8_mm_kernel, int8 matrix cores)",
+                "ms_per_step": round(t["total_r8"] / K * 1e3, 5),
+                "gbs": round(two_bytes * K / t["total_r8"] / 1e9, 1),
+                "engine_avg_launch_us": round(t["eng_r8"] * 1e6, 3),
+                "engine_gbs": round(plan.engine_bytes / t["eng_r8"] / 1e9, 1)}
     out["fused_reference"] = {
         "timing": "native rows, one launch per step, every wave quantizing the rows it reads",
         "ms_per_step": round(t["total_fused"] / K * 1e3, 5),

@@ -185,6 +185,33 @@ typedef struct q8_0_r8_f32_desc {
 
 int q8_0_matvec_r8_f32_batched(const q8_0_r8_f32_desc *descs, int64_t n_desc, void *stream);
 
+/* q8_0_matmul_r8_batched -- batched small-batch decode over R8 weights (the
+ * products of a decode step at 1..16 token rows, on the int8 matrix cores).
+ * Descriptor i computes, for every b < batch and token row t < m:
+ *   y_b[t][0..n) = W_b . X_b[t]
+ * with W_b the R8 layout at w_r8 + b*w_batch_stride BYTES (a multiple of 16,
+ * >= q8_0_r8_bytes(n, k) when batch > 1), X_b[t] = x + b*x_batch_stride +
+ * t*x_row_stride (Q8_0 blocks; x_row_stride >= k/32 when m > 1), y_b[t] = y +
+ * b*y_batch_stride + t*y_row_stride (floats; y_row_stride >= n when m > 1,
+ * y_batch_stride >= n when batch > 1).  Arithmetic of q8_0_matmul (exact int32
+ * block sums, (d_w*d_x)*s in fp32).  m <= 16 (Q8_E_UNSUPPORTED above, and when
+ * 36*m'*k/32 bytes of staged activations exceed the workgroup's LDS, m' = 8
+ * for m <= 8 else 16); n_desc <= 32.  descs is a HOST array.
+ */
+typedef struct q8_0_r8_mm_desc {
+    const void *w_r8;
+    const q8_0_block *x;
+    float *y;
+    int64_t n, k, m, batch;
+    int64_t w_batch_stride;   /* bytes */
+    int64_t x_row_stride;     /* blocks */
+    int64_t x_batch_stride;   /* blocks */
+    int64_t y_row_stride;     /* floats */
+    int64_t y_batch_stride;   /* floats */
+} q8_0_r8_mm_desc;
+
+int q8_0_matmul_r8_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Q8_1 activations and 4/5-bit K-quant weights.  [XEON] (three-part fix,
  * compile fix) names a Q8_1 activation quantizer beside the Q8_0 one; the

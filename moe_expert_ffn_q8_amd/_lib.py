@@ -50,6 +50,13 @@ class Q8R8F32Desc(ctypes.Structure):
                 ("w_batch_stride", _i64), ("x_batch_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class Q8R8MmDesc(ctypes.Structure):
+    _fields_ = [("w_r8", _vp), ("x", _vp), ("y", _vp),
+                ("n", _i64), ("k", _i64), ("m", _i64), ("batch", _i64),
+                ("w_batch_stride", _i64), ("x_row_stride", _i64), ("x_batch_stride", _i64),
+                ("y_row_stride", _i64), ("y_batch_stride", _i64)]
+
+
 class KqMatvecDesc(ctypes.Structure):
     _fields_ = [("w", _vp), ("x", _vp), ("y", _vp),
                 ("n", _i64), ("k", _i64), ("batch", _i64),
@@ -108,6 +115,7 @@ _SIGS = {
     "q8_0_matvec_r8": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "q8_0_matvec_r8_batched": (_int, [ctypes.POINTER(Q8R8Desc), _i64, _vp]),
     "q8_0_matvec_r8_f32_batched": (_int, [ctypes.POINTER(Q8R8F32Desc), _i64, _vp]),
+    "q8_0_matmul_r8_batched": (_int, [ctypes.POINTER(Q8R8MmDesc), _i64, _vp]),
     "q8_1_quantize_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp]),
     "kq_matvec_batched": (_int, [_int, ctypes.POINTER(KqMatvecDesc), _i64, _vp]),
     "q4_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
@@ -264,6 +272,28 @@ def q8_0_matvec_r8_f32_batched(descs, stream_of):
     arr = (Q8R8F32Desc * max(1, len(descs)))(*descs)
     _check("q8_0_matvec_r8_f32_batched",
            _lib.q8_0_matvec_r8_f32_batched(arr, len(descs), _stream(stream_of)))
+
+
+def make_r8_mm_desc(w_r8, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
+                    x_batch_stride=0, y_row_stride=None, y_batch_stride=0):
+    """One q8_0_r8_mm_desc.  w_r8 (bytes), x (blocks), y (floats) are (tensor,
+    element offset) pairs or tensors; w_batch_stride in bytes, x strides in
+    blocks, y strides in floats."""
+    def addr(t, unit):
+        if isinstance(t, tuple):
+            return t[0].data_ptr() + t[1] * unit
+        return t.data_ptr()
+    nb = k // QK
+    return Q8R8MmDesc(addr(w_r8, 1), addr(x, BLOCK_BYTES), addr(y, 4), n, k, m, batch,
+                      w_batch_stride, nb if x_row_stride is None else x_row_stride,
+                      x_batch_stride, n if y_row_stride is None else y_row_stride,
+                      y_batch_stride)
+
+
+def q8_0_matmul_r8_batched(descs, stream_of):
+    arr = (Q8R8MmDesc * max(1, len(descs)))(*descs)
+    _check("q8_0_matmul_r8_batched",
+           _lib.q8_0_matmul_r8_batched(arr, len(descs), _stream(stream_of)))
 
 
 Q8_1_BLOCK_BYTES = 36

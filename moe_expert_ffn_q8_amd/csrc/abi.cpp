@@ -471,6 +471,45 @@ int q8_0_matvec_r8_f32_batched(const q8_0_r8_f32_desc *descs, int64_t n_desc, vo
     return r8_batched(descs, n_desc, true, stream);
 }
 
+int q8_0_matmul_r8_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, void *stream)
+{
+    if (n_desc < 0) return Q8_E_SHAPE;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    q8::R8MmDesc d[q8::kStreamMaxJobs];
+    int nd = 0;
+    for (int64_t i = 0; i < n_desc; ++i) {
+        const q8_0_r8_mm_desc &s = descs[i];
+        if (int rc = check_k(s.k)) return rc;
+        if (s.n < 0 || s.m < 0 || s.batch < 0) return Q8_E_SHAPE;
+        if (s.m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
+        if (s.n == 0 || s.m == 0 || s.batch == 0) continue;
+        if (!s.w_r8 || !s.x || !s.y) return Q8_E_NULL;
+        const int64_t nb = s.k / kQK;
+        if (s.m > 1 && (s.x_row_stride < nb || s.y_row_stride < s.n)) return Q8_E_SHAPE;
+        if (s.batch > 1 && (s.w_batch_stride < q8::r8_bytes(s.n, nb) || s.x_batch_stride < 0 ||
+                            s.y_batch_stride < s.n))
+            return Q8_E_SHAPE;
+        if (!aligned(s.w_r8, 16) || !aligned(s.x, 2) || !aligned(s.y, 4) ||
+            (s.batch > 1 && s.w_batch_stride % 16 != 0))
+            return Q8_E_ALIGN;
+        if (!q8::r8_mm_ok(s.n, nb, s.m, s.batch)) return Q8_E_UNSUPPORTED;
+        q8::R8MmDesc &o = d[nd++];
+        o.w = (const uint8_t *)s.w_r8;
+        o.x = (const uint8_t *)s.x;
+        o.y = s.y;
+        o.n = s.n; o.nb = nb; o.m = s.m; o.batch = s.batch;
+        o.w_bstride = s.batch > 1 ? s.w_batch_stride : 0;
+        o.x_rstride = (s.m > 1 ? s.x_row_stride : nb) * kBB;
+        o.x_bstride = s.batch > 1 ? s.x_batch_stride * kBB : 0;
+        o.y_rstride = s.m > 1 ? s.y_row_stride : s.n;
+        o.y_bstride = s.batch > 1 ? s.y_batch_stride : 0;
+    }
+    if (nd == 0) return Q8_OK;
+    return hip_status(q8::launch_r8_mm(d, nd, as_stream(stream)));
+}
+
 int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, int64_t k,
                    void *stream)
 {

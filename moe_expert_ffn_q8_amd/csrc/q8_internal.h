@@ -77,6 +77,18 @@ struct R8Desc {
 bool r8_matvec_ok(int64_t n, int64_t nb, int64_t batch);
 int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream);
 
+// Small-batch products (1 <= m <= 16 token rows, Q8_0 activations) over R8
+// weights on the int8 matrix cores; strides in bytes (w, x) and floats (y).
+struct R8MmDesc {
+    const uint8_t *w;
+    const uint8_t *x;
+    float *y;
+    int64_t n, nb, m, batch;
+    int64_t w_bstride, x_rstride, x_bstride, y_rstride, y_bstride;
+};
+bool r8_mm_ok(int64_t n, int64_t nb, int64_t m, int64_t batch);
+int launch_r8_mm(const R8MmDesc *d, int n_desc, hipStream_t stream);
+
 // Q8_1 activations (36-byte blocks: binary16 d and s, 32 codes) and the
 // decode product over K-quant weights (type 4 = Q4_K, 144-byte super-blocks
 // of 256 values; type 5 = Q5_K, 176 bytes) against one Q8_1 row per matrix.

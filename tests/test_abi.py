@@ -403,3 +403,25 @@ def test_kq_checks(lib):
     assert call(6, q.KqMatvecDesc(A, A, A, 8, 256, 1, 0, 0, 0)) == Q8_E_UNSUPPORTED
     assert call(4, q.KqMatvecDesc(A, A, A, 8, 256, 2, 7, 8, 8)) == Q8_E_SHAPE     # w stride
     assert call(4, q.KqMatvecDesc(A, A, A, 8, 256, 2, 8, 8, 7)) == Q8_E_SHAPE     # y stride
+
+
+def test_r8_mm_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    f = lib.q8_0_matmul_r8_batched
+
+    def call(*descs):
+        arr = (q.Q8R8MmDesc * max(1, len(descs)))(*descs)
+        return f(arr, len(descs), None)
+
+    D = q.Q8R8MmDesc
+    assert f(None, 0, None) == Q8_OK
+    assert call(D(A, A, A, 64, 768, 17, 1, 0, 24, 0, 64, 0)) == Q8_E_UNSUPPORTED     # m > 16
+    assert call(D(A, A, A, 64, 768, 8, 1, 0, 23, 0, 64, 0)) == Q8_E_SHAPE            # x row stride
+    assert call(D(A, A, A, 64, 768, 8, 1, 0, 24, 0, 63, 0)) == Q8_E_SHAPE            # y row stride
+    assert call(D(A, A, A, 64, 768, 8, 2, 16, 24, 192, 64, 512)) == Q8_E_SHAPE        # w stride
+    assert call(D(A, A, A, 64, 768, 8, 2, 64 * 24 * 34 + 8, 24, 192, 64, 512)) == Q8_E_ALIGN
+    assert call(D(A + 8, A, A, 64, 768, 8, 1, 0, 24, 0, 64, 0)) == Q8_E_ALIGN
+    assert call(D(A, A + 1, A, 64, 768, 8, 1, 0, 24, 0, 64, 0)) == Q8_E_ALIGN
+    assert call(D(A, A, A, 64, 40, 8, 1, 0, 24, 0, 64, 0)) == Q8_E_SHAPE              # k % 32
+    assert call(D(None, A, A, 64, 768, 8, 1, 0, 24, 0, 64, 0)) == Q8_E_NULL
+    assert call(D(A, A, A, 64, 768, 0, 1, 0, 24, 0, 64, 0)) == Q8_OK                 # no rows

@@ -169,3 +169,67 @@ def test_r8_f32_batched_quantizes_inside(q, orc):
         b = y32.cpu().numpy()
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
         assert_rows_close(b.reshape(batch, n), ref)
+
+
+MM_CASES = [(777, 768, 8, 1), (2304, 768, 8, 2), (40, 3072, 8, 1), (100, 96, 5, 1),
+            (33, 32, 3, 2), (300, 2048, 16, 1), (129, 768, 9, 2), (64, 4096, 2, 1),
+            (50257 // 8 * 8 + 3, 768, 8, 1), (17, 8192, 16, 1), (8, 768, 1, 1)]
+
+
+@pytest.mark.parametrize("n,k,m,batch", MM_CASES)
+def test_r8_matmul_small_batch(q, orc, n, k, m, batch):
+    """1..16 token rows over R8 weights on the matrix cores: within 1e-5 of
+    the oracle per token row, bitwise repeatable; batch entries with strided
+    activation and output rows and gaps that must stay untouched."""
+    import torch
+    nb = k // 32
+    mb = q.q8_0_r8_bytes(n, k)
+    ws = [weights_q8(orc, n, k, "r8mm", n, k, m, b) for b in range(batch)]
+    xs = [acts_q8(orc, m, k, "r8mm-x", n, k, m, b) for b in range(batch)]
+    wr = torch.cat([q.q8_0_repack_r8(to_gpu(w), n, k) for w in ws])
+    xrs = nb + 3                                 # activation row stride (blocks)
+    xbuf = np.zeros((batch, m, xrs * 34), dtype=np.uint8)
+    for b in range(batch):
+        xbuf[b, :, :nb * 34] = xs[b]
+    xg = to_gpu(xbuf.reshape(-1))
+    yrs, ybs = n + 5, m * (n + 5) + 11
+    y = nan_like((batch * ybs,))
+    d = [q.make_r8_mm_desc(wr, xg, y, n, k, m=m, batch=batch, w_batch_stride=mb,
+                           x_row_stride=xrs, x_batch_stride=m * xrs, y_row_stride=yrs,
+                           y_batch_stride=ybs)]
+    q.q8_0_matmul_r8_batched(d, wr)
+    yy = y.cpu().numpy()
+    for b in range(batch):
+        got = yy[b * ybs:b * ybs + m * yrs].reshape(m, yrs)
+        assert np.all(np.isnan(got[:, n:])), "a gap was written"
+        assert_rows_close(got[:, :n], orc.matmul(ws[b], xs[b], n, k, m))
+    assert np.all(np.isnan(yy.reshape(batch, ybs)[:, m * yrs:]))
+    y2 = nan_like((batch * ybs,))
+    d2 = [q.make_r8_mm_desc(wr, xg, y2, n, k, m=m, batch=batch, w_batch_stride=mb,
+                            x_row_stride=xrs, x_batch_stride=m * xrs, y_row_stride=yrs,
+                            y_batch_stride=ybs)]
+    q.q8_0_matmul_r8_batched(d2, wr)
+    a, c = yy, y2.cpu().numpy()
+    fin = ~np.isnan(a)
+    assert np.array_equal(a[fin].view(np.uint32), c[fin].view(np.uint32))
+
+
+def test_r8_matmul_unit_scales_exact(q, orc):
+    """Every scale 1: the fp32 outputs are integers below 2^24, exact."""
+    g = np.random.default_rng(5)
+    n, k, m = 96, 2048, 8
+    nb = k // 32
+
+    def unit_blocks(rows):
+        b = np.zeros((rows, nb, 34), dtype=np.uint8)
+        b[:, :, 0], b[:, :, 1] = 0x00, 0x3C
+        b[:, :, 2:] = g.integers(-40, 41, size=(rows, nb, 32)).astype(np.int8).view(np.uint8)
+        return b.reshape(rows, nb * 34)
+
+    w, x = unit_blocks(n), unit_blocks(m)
+    y = nan_like((m, n))
+    q.q8_0_matmul_r8_batched([q.make_r8_mm_desc(q.q8_0_repack_r8(to_gpu(w), n, k), to_gpu(x), y,
+                                                n, k, m=m)], y)
+    ref = orc.matmul(w, x, n, k, m)
+    assert np.all(np.abs(ref) < 2 ** 24)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
