@@ -17,7 +17,9 @@
 // bounds this kernel.  (Build option Q8_GEMM_OUTER=1 forms the rank-1 scale
 // products of a block as an outer product on the fp32 matrix core instead,
 // same register layout, leaving 2 VALU operations; with this compiler's
-// schedule it measured slower, so it is off.)
+// schedule it measured slower, so it is off.  The same outer product from a
+// K = 16 binary16 product (v_mfma_f32_32x32x16_f16, the scales' own bits)
+// measured 138.6 to 142.8 us against 133.4 us.)
 //
 // Work decomposition:
 //  * Workgroup = 4 waves, output tile 128 tokens x 128 weight rows; wave
