@@ -23,14 +23,14 @@
 // its 4 (m <= 8) or 8 (m <= 16) live values by d_w*d_x and accumulates them.
 // Rows of 64 blocks or more are split over 2 or 4 waves of the workgroup
 // (partial sums added in a fixed order through LDS); the blocks stream through
-// two register buffers of 4 blocks each.
+// two register buffers of 2 blocks each (68 VGPRs; 3, 4, 6 or 8 blocks per
+// buffer measured slower).
 //
-// Measured on the GPT-2-shaped batch-8 step (49 products, 136 MB): 27.5 us per
-// launch, the same as the native-layout matrix-core engine (27.1 us).  What
+// Measured on the GPT-2-shaped batch-8 step (49 products, 136 MB): 26.8 us per
+// launch, level with the native-layout matrix-core engine (27.1 us).  What
 // cost time on the way: activation loads made conditional (the compiler then
 // waited for each in turn: 35 us), staging before the weight issue (31 us);
-// more waves per unit, 8 or 16 waves per workgroup and 3 to 8 blocks per
-// buffer did not help.
+// more waves per unit and 8 or 16 waves per workgroup did not help.
 #include <string.h>
 
 #include "q8_device.h"
@@ -51,7 +51,7 @@ constexpr int kMmWaves = Q8_R8MM_WAVES;
 constexpr int kMmThreads = kMmWaves * kWave;
 constexpr int kMmGroups = 4;                            // 32 weight rows per wave
 #ifndef Q8_R8MM_SLICES
-#define Q8_R8MM_SLICES 4
+#define Q8_R8MM_SLICES 2
 #endif
 constexpr int kMmSlices = Q8_R8MM_SLICES;              // blocks per register buffer (two)
 
