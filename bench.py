@@ -792,6 +792,23 @@ def run_extra(args, q, synth):
             q.moe_up_gate_swiglu_batched(ug, n_embd, n_ff, E)
             q.moe_down_combine_batched(dn, n_ff, n_embd, E)
         res.update(tokens=n_tok, layers=L, active_weight_bytes=active_bytes)
+        # the same layers over expert weights repacked once into the R8 layout:
+        # one moe_r8_ffn_batched call (2 launches) per step
+        r8l = []
+        for d in layers:
+            r8l.append(dict(w_up_gate_r8=q.q8_0_repack_r8(d["wug"], E * 2 * n_ff, n_embd),
+                            w_down_r8=q.q8_0_repack_r8(d["wd"], E * n_embd, n_ff), x=d["xf"],
+                            ids=d["ids"], cw=d["cw"], h=d["h"], out=d["out"],
+                            ws=q.moe_r8_workspace(n_tok, n_embd, n_ff, E, U, dev)))
+        tr = _time_launches(lambda: q.moe_r8_ffn_batched(r8l, n_embd, n_ff, E), args.steps,
+                            args.warmup) / args.steps
+        res.update(r8_layout={"timing": "expert weights repacked once into the R8 layout; "
+                                        "all layers in one moe_r8_ffn_batched call (2 launches)",
+                              "us_per_step": round(tr * 1e6, 2),
+                              "gbs": round(active_bytes / tr / 1e9, 1),
+                              "pct_of_hbm_peak": round(active_bytes / tr / 1e9 / HBM_PEAK_GBS * 100, 2),
+                              "tokens_per_s": round(n_tok / tr, 1)})
+        del r8l
         if args.moe_mode in ("both", "layers"):
             t = _time_launches(step, args.steps, args.warmup) / args.steps
             res.update(us_per_step=round(t * 1e6, 2), gbs=round(active_bytes / t / 1e9, 1),

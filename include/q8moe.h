@@ -475,6 +475,41 @@ int moe_down_combine_batched(const moe_down_desc *descs, int64_t n_desc,
                              int64_t n_expert, int64_t n_used, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_r8_ffn_batched -- the whole decode expert FFN (the moe_up_gate_swiglu
+ * and moe_down_combine arithmetic, same h and out) over expert weights
+ * repacked once into the R8 layout (q8_0_repack_r8): w_up_gate_r8 = the
+ * combined tensor as n_expert*2*n_ff rows of n_embd values, w_down_r8 = the
+ * down tensor as n_expert*n_embd rows of n_ff values.  Two launches per call,
+ * several layers of one shape per launch.  h [n_tok][n_used][n_ff] and out
+ * [n_tok][n_embd] are written; x, ids, cw as for the native calls.  Each
+ * slot streams its expert's rows (repeated experts across tokens are read
+ * once per slot), so it serves decode at one or a few tokens.
+ * Limits: n_embd % 32 == 0, n_ff % 32 == 0, n_ff <= 2048, n_embd <= 32768,
+ * n_tok*n_used <= 1024, n_used <= 16, n_expert <= 1024 (Q8_E_UNSUPPORTED).
+ * Out-of-range ids: the error word (first int32 of ws, set every call), NaN
+ * h rows for such slots and NaN output rows for their tokens.
+ * Workspace: moe_r8_workspace_bytes(...) bytes, 256-byte aligned (0 for an
+ * unsupported shape); one workspace per layer, not shared by concurrent calls.
+ */
+typedef struct moe_r8_ffn_desc {
+    const void *w_up_gate_r8;
+    const void *w_down_r8;
+    const float *x;
+    const int32_t *ids;
+    const float *cw;
+    float *h;
+    float *out;
+    void *ws;
+    size_t ws_bytes;
+} moe_r8_ffn_desc;
+
+size_t moe_r8_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                              int64_t n_used);
+int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                       int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                       void *stream);
+
+/* ---------------------------------------------------------------------------
  * Validation exports (same kernels, with an extra output), for testing.
  *
  * q8_0_matmul_blocksums: the per-block int32 sums s[m][n][b] that q8_0_matmul

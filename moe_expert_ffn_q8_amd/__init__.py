@@ -14,7 +14,8 @@ from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDes
                    q8_0_matvec_r8, q8_0_matvec_r8_batched, make_r8_desc, Q8R8Desc,
                    q8_0_matvec_r8_f32_batched, make_r8_f32_desc, Q8R8F32Desc,
                    q8_1_quantize_rows, kq_matvec, kq_matvec_batched, make_kq_desc, KqMatvecDesc,
-                   q8_0_matmul_r8_batched, make_r8_mm_desc, Q8R8MmDesc, q8_0_quantize_rows, q8_0_r8_bytes, q8_0_repack_r8, q8_empty, q8_read_probe, raw, status_str, version)
+                   q8_0_matmul_r8_batched, make_r8_mm_desc, Q8R8MmDesc,
+                   moe_r8_workspace, moe_r8_ffn_batched, MoeR8FfnDesc, q8_0_quantize_rows, q8_0_r8_bytes, q8_0_repack_r8, q8_empty, q8_read_probe, raw, status_str, version)
 
 __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGateDesc", "Q8Error",
            "Q8MatmulDesc", "Q8MatmulF32Desc", "Q8UpGateDesc", "make_desc", "make_f32_desc",
@@ -26,5 +27,6 @@ __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGate
            "q8_0_matvec_r8", "q8_0_matvec_r8_batched", "make_r8_desc", "Q8R8Desc",
            "q8_0_matvec_r8_f32_batched", "make_r8_f32_desc", "Q8R8F32Desc",
            "q8_1_quantize_rows", "kq_matvec", "kq_matvec_batched", "make_kq_desc", "KqMatvecDesc",
-           "q8_0_matmul_r8_batched", "make_r8_mm_desc", "Q8R8MmDesc", "q8_0_quantize_rows", "q8_0_r8_bytes", "q8_0_repack_r8", "q8_empty", "q8_read_probe", "raw",
+           "q8_0_matmul_r8_batched", "make_r8_mm_desc", "Q8R8MmDesc",
+           "moe_r8_workspace", "moe_r8_ffn_batched", "MoeR8FfnDesc", "q8_0_quantize_rows", "q8_0_r8_bytes", "q8_0_repack_r8", "q8_empty", "q8_read_probe", "raw",
            "status_str", "version"]

@@ -57,6 +57,11 @@ class Q8R8MmDesc(ctypes.Structure):
                 ("y_row_stride", _i64), ("y_batch_stride", _i64)]
 
 
+class MoeR8FfnDesc(ctypes.Structure):
+    _fields_ = [("w_up_gate_r8", _vp), ("w_down_r8", _vp), ("x", _vp), ("ids", _vp), ("cw", _vp),
+                ("h", _vp), ("out", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
+
+
 class KqMatvecDesc(ctypes.Structure):
     _fields_ = [("w", _vp), ("x", _vp), ("y", _vp),
                 ("n", _i64), ("k", _i64), ("batch", _i64),
@@ -117,6 +122,9 @@ _SIGS = {
     "q8_0_matvec_r8_f32_batched": (_int, [ctypes.POINTER(Q8R8F32Desc), _i64, _vp]),
     "q8_0_matmul_r8_batched": (_int, [ctypes.POINTER(Q8R8MmDesc), _i64, _vp]),
     "q8_1_quantize_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp]),
+    "moe_r8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
+    "moe_r8_ffn_batched": (_int, [ctypes.POINTER(MoeR8FfnDesc), _i64, _i64, _i64, _i64, _i64,
+                                  _i64, _vp]),
     "kq_matvec_batched": (_int, [_int, ctypes.POINTER(KqMatvecDesc), _i64, _vp]),
     "q4_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "q5_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
@@ -560,6 +568,37 @@ def q8_read_probe(buf, sink):
     """Stream-read the bytes of `buf` (a GPU tensor); sink: int32 GPU tensor."""
     _check("q8_read_probe", _lib.q8_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
                                                _ptr(sink), sink.numel(), _stream(buf)))
+
+
+def moe_r8_workspace(n_tok, n_embd, n_ff, n_expert, n_used, device):
+    nbytes = _lib.moe_r8_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used)
+    if nbytes == 0:
+        raise Q8Error("moe_r8_workspace_bytes", -4)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert):
+    """The decode expert FFN over R8 expert weights for independent layers of
+    one shape.  layers: list of dicts with w_up_gate_r8, w_down_r8, x, ids, cw,
+    h (written), out (written), ws."""
+    if not layers:
+        return
+    for d in layers:
+        _need(d["w_up_gate_r8"], torch.uint8, "w_up_gate_r8")
+        _need(d["w_down_r8"], torch.uint8, "w_down_r8")
+        _need(d["x"], torch.float32, "x")
+        _need(d["ids"], torch.int32, "ids")
+        _need(d["cw"], torch.float32, "cw")
+        _need(d["h"], torch.float32, "h")
+        _need(d["out"], torch.float32, "out")
+        _need(d["ws"], torch.uint8, "ws")
+    n_tok, n_used = layers[0]["ids"].shape
+    arr = (MoeR8FfnDesc * len(layers))(*[
+        MoeR8FfnDesc(_ptr(d["w_up_gate_r8"]), _ptr(d["w_down_r8"]), _ptr(d["x"]), _ptr(d["ids"]),
+                     _ptr(d["cw"]), _ptr(d["h"]), _ptr(d["out"]), _ptr(d["ws"]), d["ws"].numel())
+        for d in layers])
+    _check("moe_r8_ffn_batched", _lib.moe_r8_ffn_batched(
+        arr, len(layers), n_tok, n_embd, n_ff, n_expert, n_used, _stream(layers[0]["ids"])))
 
 
 def moe_error_word(ws):

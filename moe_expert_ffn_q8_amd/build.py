@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["quantize.hip", "stream.hip", "step.hip", "ffn.hip", "small_m.hip", "moe.hip",
-           "moe_gemm.hip", "gemm.hip", "r8.hip", "r8_mm.hip", "kquant.hip", "probe.hip",
+           "moe_gemm.hip", "moe_r8.hip", "gemm.hip", "r8.hip", "r8_mm.hip", "kquant.hip", "probe.hip",
            "abi.cpp"]
 
 # no packed fp32 instructions in device code; MFMA results in VGPRs (the

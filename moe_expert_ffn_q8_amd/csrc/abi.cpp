@@ -574,6 +574,48 @@ int q5_k_matvec(const void *w, const void *x, float *y, int64_t n, int64_t k, vo
     return kq_matvec_batched(5, &d, 1, stream);
 }
 
+size_t moe_r8_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                              int64_t n_used)
+{
+    if (n_tok < 0 || n_expert <= 0 || n_used <= 0 || check_k(n_embd) || check_k(n_ff)) return 0;
+    if (!q8::moe_r8_ok(n_tok, n_embd, n_ff, n_expert, n_used)) return 0;
+    return q8::moe_r8_ws_bytes(n_tok, n_ff, n_used);
+}
+
+int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                       int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                       void *stream)
+{
+    if (n_desc < 0 || n_tok < 0 || n_expert <= 0 || n_used <= 0) return Q8_E_SHAPE;
+    if (check_k(n_embd) || check_k(n_ff)) return Q8_E_SHAPE;
+    if (!q8::moe_r8_ok(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_UNSUPPORTED;
+    if (n_desc == 0) return Q8_OK;
+    if (!descs) return Q8_E_NULL;
+    if (n_desc > 4096) return Q8_E_UNSUPPORTED;
+    const size_t need = q8::moe_r8_ws_bytes(n_tok, n_ff, n_used);
+    q8::MoeR8Layer l[4096 / 64];
+    for (int64_t i0 = 0; i0 < n_desc; i0 += 64) {
+        const int nl = (int)std::min<int64_t>(64, n_desc - i0);
+        for (int i = 0; i < nl; ++i) {
+            const moe_r8_ffn_desc &d = descs[i0 + i];
+            if (!d.ws) return Q8_E_WORKSPACE;
+            if (d.ws_bytes < need) return Q8_E_WORKSPACE;
+            if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
+            if (n_tok > 0 && (!d.w_up_gate_r8 || !d.w_down_r8 || !d.x || !d.ids || !d.cw ||
+                              !d.h || !d.out))
+                return Q8_E_NULL;
+            if (!aligned(d.w_up_gate_r8, 16) || !aligned(d.w_down_r8, 16) || !aligned(d.x, 16) ||
+                !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, 4) || !aligned(d.out, 4))
+                return Q8_E_ALIGN;
+            l[i] = {d.w_up_gate_r8, d.w_down_r8, d.x, d.ids, d.cw, d.h, d.out, d.ws};
+        }
+        if (int rc = hip_status(q8::launch_moe_r8_ffn(l, nl, n_tok, n_embd, n_ff, n_expert, n_used,
+                                                      as_stream(stream))))
+            return rc;
+    }
+    return Q8_OK;
+}
+
 int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words, void *stream)
 {
     if (bytes < 0 || sink_words < 0) return Q8_E_SHAPE;

@@ -72,4 +72,23 @@ int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids
                             float *out, void *ws, int64_t n_tok, int64_t n_embd, int64_t n_ff,
                             int64_t n_expert, int64_t n_used, hipStream_t stream);
 
+// Decode expert FFN over R8 weights (up_gate + SwiGLU, down + combine in two
+// launches per call): the combined up_gate tensor repacked as n_expert*2*n_ff
+// rows, the down tensor as n_expert*n_embd rows.  Workspace: [0, 256) error
+// word, then the quantized h rows [n_tok*n_used][n_ff/32] blocks.
+struct MoeR8Layer {
+    const void *w_up_gate;
+    const void *w_down;
+    const float *x;
+    const int32_t *ids;
+    const float *cw;
+    float *h;
+    float *out;
+    void *ws;
+};
+bool moe_r8_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
+size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_ff, int64_t n_used);
+int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
+                      int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream);
+
 }  // namespace q8

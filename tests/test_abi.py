@@ -425,3 +425,29 @@ def test_r8_mm_checks(lib):
     assert call(D(A, A, A, 64, 40, 8, 1, 0, 24, 0, 64, 0)) == Q8_E_SHAPE              # k % 32
     assert call(D(None, A, A, 64, 768, 8, 1, 0, 24, 0, 64, 0)) == Q8_E_NULL
     assert call(D(A, A, A, 64, 768, 0, 1, 0, 24, 0, 64, 0)) == Q8_OK                 # no rows
+
+
+def test_moe_r8_checks(lib):
+    import moe_expert_ffn_q8_amd as q
+    f = lib.moe_r8_ffn_batched
+    need = lib.moe_r8_workspace_bytes(1, 2048, 768, 128, 8)
+    assert need == 256 + (8 * 24 * 34 + 255) // 256 * 256
+    assert lib.moe_r8_workspace_bytes(1, 2048, 768 + 16, 128, 8) == 0      # n_ff % 32
+    assert lib.moe_r8_workspace_bytes(1, 2048, 4096, 128, 8) == 0           # n_ff > 2048
+
+    def call(d, n_tok=1, n_embd=2048, n_ff=768, n_expert=128, n_used=8):
+        arr = (q.MoeR8FfnDesc * 1)(d)
+        return f(arr, 1, n_tok, n_embd, n_ff, n_expert, n_used, None)
+
+    D = q.MoeR8FfnDesc
+    ok = D(A, A, A, A, A, A, A, WS, need)
+    assert call(ok, n_ff=4096) == Q8_E_UNSUPPORTED
+    assert call(ok, n_used=17) == Q8_E_UNSUPPORTED
+    assert call(ok, n_embd=2047) == Q8_E_SHAPE
+    assert call(D(A, A, A, A, A, A, A, WS, need - 1)) == Q8_E_WORKSPACE
+    assert call(D(A, A, A, A, A, A, A, None, need)) == Q8_E_WORKSPACE
+    assert call(D(A, A, A, A, A, A, A, WS + 16, need)) == Q8_E_ALIGN
+    assert call(D(None, A, A, A, A, A, A, WS, need)) == Q8_E_NULL
+    assert call(D(A, A + 8, A, A, A, A, A, WS, need)) == Q8_E_ALIGN
+    assert call(D(A, A, A + 4, A, A, A, A, WS, need)) == Q8_E_ALIGN
+    assert call(ok, n_tok=0) == Q8_OK

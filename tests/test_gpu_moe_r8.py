@@ -1,0 +1,98 @@
+"""GPU parity of the decode expert FFN over R8 expert weights
+(moe_r8_ffn_batched) against the oracle, with the stage-boundary protocol of
+the native expert FFN: h per (t,u) row against the oracle's h from the same
+quantized token rows; out against the oracle's down + combine fed the GPU's
+own h; error word and NaN rows for out-of-range ids."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_cases import assert_rows_close, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import moe_expert_ffn_q8_amd as q
+    return q
+
+
+def _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, tag, ids=None):
+    import torch
+    w_ug = orc.quantize_rows(synth.normal_f32((n_expert * 2 * n_ff, n_embd), 0.02, tag, "ug"))
+    w_d = orc.quantize_rows(synth.normal_f32((n_expert * n_embd, n_ff), 0.02, tag, "down"))
+    xf = synth.normal_f32((n_tok, n_embd), 1.0, tag, "x")
+    if ids is None:
+        ids = synth.expert_ids(n_tok, n_used, n_expert, tag, "ids")
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    cw = synth.combine_weights(n_tok, n_used, tag, "cw")
+    d = dict(w_up_gate_r8=q.q8_0_repack_r8(to_gpu(w_ug), n_expert * 2 * n_ff, n_embd),
+             w_down_r8=q.q8_0_repack_r8(to_gpu(w_d), n_expert * n_embd, n_ff),
+             x=to_gpu(xf), ids=to_gpu(ids), cw=to_gpu(cw),
+             h=torch.full((n_tok, n_used, n_ff), float("nan"), device="cuda"),
+             out=torch.full((n_tok, n_embd), float("nan"), device="cuda"),
+             ws=q.moe_r8_workspace(n_tok, n_embd, n_ff, n_expert, n_used, "cuda").fill_(0x7F))
+    return d, dict(w_ug=w_ug, w_d=w_d, xq=orc.quantize_rows(xf), ids=ids, cw=cw)
+
+
+def _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used):
+    assert q.moe_error_word(d["ws"]) == 0
+    h = d["h"].cpu().numpy()
+    h_ref = orc.moe_up_gate_swiglu(c["w_ug"], c["xq"], c["ids"], n_embd, n_ff, n_expert)
+    assert_rows_close(h.reshape(-1, n_ff), h_ref.reshape(-1, n_ff))
+    out_ref = orc.moe_down_combine(c["w_d"], h, c["ids"], c["cw"], n_ff, n_embd, n_expert)
+    assert_rows_close(d["out"].cpu().numpy(), out_ref)
+
+
+@pytest.mark.parametrize("n_tok,n_embd,n_ff,n_expert,n_used", [
+    (1, 256, 96, 8, 2), (1, 512, 128, 16, 4), (3, 768, 256, 32, 8), (16, 512, 192, 16, 8),
+    (1, 2048, 768, 128, 8), (16, 2048, 768, 128, 8), (1, 1024, 2048, 32, 16), (4, 224, 32, 4, 3)])
+def test_moe_r8_ffn(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
+    d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, f"r8moe-{n_tok}-{n_embd}-{n_ff}-{n_expert}-{n_used}")
+    q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+    _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
+
+
+def test_moe_r8_ffn_repeated_experts(q, orc):
+    """Every token names the same 4 experts (each expert read once per slot)."""
+    n_tok, n_embd, n_ff, n_expert, n_used = 6, 512, 128, 4, 4
+    ids = np.tile(np.array([2, 0, 3, 1], dtype=np.int32), (n_tok, 1))
+    d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, "r8moe-rep", ids=ids)
+    q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+    _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
+
+
+def test_moe_r8_ffn_layers(q, orc):
+    """Three independent layers in one call."""
+    shape = (2, 512, 160, 8, 4)
+    pairs = [_layer(q, orc, *shape, f"r8moe-l{i}") for i in range(3)]
+    q.moe_r8_ffn_batched([d for d, _ in pairs], shape[1], shape[2], shape[3])
+    for d, c in pairs:
+        _check(q, orc, d, c, *shape)
+
+
+def test_moe_r8_ffn_invalid_ids(q, orc):
+    n_tok, n_embd, n_ff, n_expert, n_used = 4, 256, 64, 8, 3
+    ids = synth.expert_ids(n_tok, n_used, n_expert, "r8moe-bad", "ids")
+    ids[1, 2] = n_expert + 5
+    ids[3, 0] = -1
+    d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, "r8moe-bad", ids=ids)
+    q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+    assert q.moe_error_word(d["ws"]) == 1
+    h = d["h"].cpu().numpy()
+    out = d["out"].cpu().numpy()
+    assert np.all(np.isnan(h[1, 2])) and np.all(np.isnan(h[3, 0]))
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[3]))
+    good = [0, 2]
+    ok_ids = c["ids"][good]
+    h_ref = orc.moe_up_gate_swiglu(c["w_ug"], c["xq"][good], ok_ids, n_embd, n_ff, n_expert)
+    assert_rows_close(h[good].reshape(-1, n_ff), h_ref.reshape(-1, n_ff))
+    out_ref = orc.moe_down_combine(c["w_d"], h[good], ok_ids, c["cw"][good], n_ff, n_embd,
+                                   n_expert)
+    assert_rows_close(out[good], out_ref)
+    # the next valid call clears the word
+    d2, c2 = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, "r8moe-bad2")
+    d2["ws"] = d["ws"]
+    q.moe_r8_ffn_batched([d2], n_embd, n_ff, n_expert)
+    _check(q, orc, d2, c2, n_tok, n_embd, n_ff, n_expert, n_used)
