@@ -15,17 +15,28 @@
 //     slots grouped by expert, and a tile table -- expert e's c_e slots make
 //     ceil(c_e / 32) tiles of at most 32 slots.  Slots with an out-of-range id
 //     are left out; they set the error word and (up_gate call) get NaN h rows.
-//  2. the token rows (up_gate) or h rows (down) quantized into the workspace by
-//     the quantizer kernel (bytes of q8_0_quantize_rows).
-//  3. grouped GEMM: workgroup = (tile, block of 128 output columns).  A = the
-//     tile's quantized rows, gathered straight from the workspace into LDS by
-//     per-lane offsets of the LDS-DMA buffer loads; B = the expert's weight
-//     rows; one v_mfma_i32_32x32x32_i8 per 32-block (K = 32 = one block) gives
-//     exact int32 block sums, rescaled per block into fp32 accumulators as in
-//     the prefill GEMM.  up_gate: wave w holds the 32 x 32 gate tile of columns
-//     [n0 + 32w, n0 + 32w + 32) and the up tile of the same columns in the same
-//     register layout, so the epilogue writes silu(g) * u element by element.
-//     down: per-slot rows [slot][n_embd] into the workspace.
+//  2. the token rows (up_gate) or h rows (down) quantized into the workspace
+//     (codes and scales of q8_0_quantize_rows) in a layout made for the matrix
+//     core: per row and block 32 code bytes, then the scales as fp32 in an
+//     array of their own.  The codes of even blocks are stored rotated by two
+//     bytes (code j at byte (j - 2) mod 32); the weight operand below uses the
+//     same order, and a block's integer sum does not depend on the order of
+//     its 32 products.
+//  3. grouped GEMM: workgroup = (tile, block of output columns), 8 waves, one
+//     32 x 32 tile of v_mfma_i32_32x32x32_i8 per wave (K = 32 = one block, so
+//     each instruction gives exact int32 block sums, rescaled per block into
+//     fp32 accumulators).  A = the tile's quantized rows, copied into LDS once
+//     (up to 64 blocks at a time) by LDS-DMA loads, laid out so that every
+//     operand read is one conflict-free 16-byte read.  B = the wave's own 32
+//     weight rows, streamed straight from HBM into registers, 8 blocks in
+//     flight: a native 34-byte block holds its codes 2 bytes past a dword
+//     boundary in every other block, so a lane loads the dword-aligned 16
+//     bytes that the rotated order starts with plus the dword holding the
+//     scale (and, for the second half of an even block, codes 0 and 1).  No
+//     barrier inside the K loop.  up_gate: waves 0..3 hold gate tiles, waves
+//     4..7 the up tiles of the same 128 columns; the up tiles go through LDS
+//     and the epilogue writes silu(g) * u element by element.  down: per-slot
+//     rows [slot][n_embd] into the workspace.
 //  4. down only: the decode path's combine kernel (ascending u per token).
 // Every output element is a sum over its own row and column only, so the
 // order of slots inside an expert's tiles does not change any result.
@@ -45,12 +56,13 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int kPWaves = 8;
 constexpr int kPThreads = kPWaves * kWave;    // 512
 constexpr int kPBM = 32;                      // slots per tile
-constexpr int kPBRows = kPWaves * 32;         // staged weight rows: one 32-row MFMA tile per wave
-constexpr int kPStep = 4;                     // blocks per K step
-constexpr int kPStepBytes = kPStep * kBlockBytes;    // 136 bytes of a row
-constexpr int kPChunks = 9;                   // 16-byte chunks fetched per staged row
-constexpr int kPRowStride = 16 * kPChunks;    // 144
-constexpr int kPAChunks = 512;                // 32 rows x 9 = 288, padded to one load per thread
+constexpr int kPChunk = 32;                   // blocks of the A tile staged in LDS at a time
+constexpr int kPDepth = 8;                    // blocks of the two weight stages of a wave
+constexpr int kPSlots = 11;                   // 16-byte LDS slots per weight row and stage
+constexpr int kPStageLoads = (32 * kPSlots + kWave - 1) / kWave;     // 6 DMA loads per stage
+constexpr int kPWaveStage = kPStageLoads * kWave * 16;    // 6 KB: every DMA lane writes inside
+constexpr int kPAlign = 4;                    // K in blocks must be a multiple of this
+constexpr int kQaTileBlocks = 32;             // blocks per quantizer pass (256 threads)
 constexpr int kRouteThreads = 1024;
 
 struct TileEntry {
@@ -129,61 +141,89 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const Ro
     }
 }
 
+// fp32 rows -> the tile layout of the A operand: codes [row][nb][32] (even
+// blocks rotated by two bytes), scales [row][nb] as fp32.  Eight lanes own a
+// block, four values each, with the rule and the bytes of q8_0_quantize_rows.
+__global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restrict__ x,
+                                                          int64_t row_stride,
+                                                          uint8_t *__restrict__ codes,
+                                                          float *__restrict__ scales, int64_t nb,
+                                                          int64_t total_blocks)
+{
+    const int tid = threadIdx.x;
+    const int li = tid & 7;
+    for (int64_t blk0 = (int64_t)blockIdx.x * kQaTileBlocks; blk0 < total_blocks;
+         blk0 += (int64_t)gridDim.x * kQaTileBlocks) {
+        const int64_t g = blk0 + (tid >> 3);
+        const bool live = g < total_blocks;
+        int64_t b = 0;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) {
+            const int64_t r = g / nb;
+            b = g - r * nb;
+            v = *(const float4 *)(x + r * row_stride + b * kQK + 4 * li);
+        }
+        uint32_t c, dbits;
+        quantize_block8(v.x, v.y, v.z, v.w, c, dbits);
+        // codes 4li+2 .. 4li+5: the upper half of this lane's word and the
+        // lower half of the next lane's (lane 7 wraps to codes 0 and 1)
+        const uint32_t nxt = (uint32_t)__shfl((int)c, (tid & ~7) | ((tid + 1) & 7));
+        const uint32_t out = (b & 1) ? c : __builtin_amdgcn_alignbyte(nxt, c, 2);
+        if (live) {
+            ((uint32_t *)codes)[g * 8 + li] = out;
+            if (li == 0) scales[g] = half_bits_to_float(dbits);
+        }
+    }
+}
+
+int launch_qa_quantize(const float *x, int64_t row_stride, uint8_t *codes, float *scales,
+                       int64_t n_rows, int64_t nb, hipStream_t stream)
+{
+    const int64_t total = n_rows * nb;
+    if (total == 0) return 0;
+    const int64_t tiles = (total + kQaTileBlocks - 1) / kQaTileBlocks;
+    const int64_t max_grid = 256 * 64;
+    const unsigned grid = (unsigned)(tiles < max_grid ? tiles : max_grid);
+    hipLaunchKernelGGL(qa_quantize_kernel, dim3(grid), dim3(256), 0, stream, x, row_stride, codes,
+                       scales, nb, total);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 struct PgArgs {
-    const uint8_t *a;       // quantized A rows: token rows (up_gate) or slot rows (down)
-    int64_t a_bytes;        // size of the A array (rows past it read as zero)
-    const uint8_t *w;       // weights [n_expert][w_rows][nb] blocks
-    int64_t expert_bytes;   // w_rows * nb * 34
-    int w_rows;             // weight rows per expert (2 n_ff or n_embd)
-    const int32_t *hdr;     // [1] = tile count
+    const uint8_t *a_codes;  // A rows, tile layout: token rows (up_gate) or slot rows (down)
+    const float *a_scales;
+    int a_rows;              // rows of the A arrays
+    const uint8_t *w;        // weights [n_expert][w_rows][nb] native blocks
+    int64_t expert_bytes;    // w_rows * nb * 34
+    const int32_t *hdr;      // [1] = tile count
     const int32_t *pairs;
     const TileEntry *tiles;
-    float *out;             // up_gate: h [slot][n_out]; down: yslot [slot][n_out]
-    int n_out;              // n_ff (up_gate) or n_embd (down)
-    int nb;                 // blocks per A / weight row (K / 32)
-    int n_used;             // up_gate: A row of slot s is token s / n_used
+    float *out;              // up_gate: h [slot][n_out]; down: yslot [slot][n_out]
+    int n_out;               // n_ff (up_gate) or n_embd (down)
+    int nb;                  // blocks per A / weight row (K / 32)
+    int n_used;              // up_gate: A row of slot s is token s / n_used
     int max_tiles, tiles_n;
 };
-
-// 16 code bytes of a block fragment from a staged LDS row (`off` 2-byte aligned).
-__device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
-{
-    const uint32_t *p = (const uint32_t *)(row + (off & ~3));
-    if ((off & 3) == 0) return (v4i){(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
-    const uint32_t d0 = p[0], d1 = p[1], d2 = p[2], d3 = p[3], d4 = p[4];
-    return (v4i){(int)__builtin_amdgcn_alignbyte(d1, d0, 2), (int)__builtin_amdgcn_alignbyte(d2, d1, 2),
-                 (int)__builtin_amdgcn_alignbyte(d3, d2, 2), (int)__builtin_amdgcn_alignbyte(d4, d3, 2)};
-}
 
 // Output columns per workgroup: up_gate pairs waves w and w + 4 (gate and up
 // rows of the same 32 columns), down gives every wave its own 32 columns.
 template <bool UG>
 constexpr int pg_cols()
 {
-    return UG ? kPBRows / 2 : kPBRows;
+    return UG ? 32 * kPWaves / 2 : 32 * kPWaves;
 }
 
 template <bool UG>
 __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
 {
-    constexpr int kBChunks = kPBRows * kPChunks;          // 2304
-    constexpr int kBLoads = (kBChunks + kPThreads - 1) / kPThreads;    // 5 per thread
-    constexpr int kALoads = kPAChunks / kPThreads;        // 1 per thread
-    constexpr int kLoads = kALoads + kBLoads;             // per thread and step (all threads alike)
-    constexpr int kBPad = kBLoads * kPThreads;            // B chunks incl. padding
-    constexpr int kRows = kPBM + kPBRows;
-    constexpr int kStage = 16 * (kPAChunks + kBPad);
-    constexpr int kCols = pg_cols<UG>();
-    static_assert(kPAChunks % kPThreads == 0, "whole A loads per thread");
-    static_assert(kStage >= 4 * kWave * 16 * 4, "the epilogue exchange fits a stage buffer");
-    // three K-step buffers as separate LDS objects: the compiler then orders
-    // an LDS read only after the DMA loads into the buffer it reads (one array
-    // indexed by stage would make every read wait for every DMA in flight)
-    __shared__ __align__(16) uint8_t stage0[kStage];
-    __shared__ __align__(16) uint8_t stage1[kStage];
-    __shared__ __align__(16) uint8_t stage2[kStage];
-    __shared__ __align__(16) float sc[kPStep][kRows];
-    __shared__ int a_off[kPBM];
+    // A tile: codes [b][half][row][16 bytes] (1 KB per block), scales [b][row]
+    __shared__ __align__(16) uint8_t la[kPChunk * 1024];
+    __shared__ __align__(16) float ldx[kPChunk * kPBM];
+    // weights: two stages of 4 blocks per wave, as separate LDS objects so
+    // that a read of one stage waits only for the copies into that stage
+    __shared__ __align__(16) uint8_t bst0[kPWaves * kPWaveStage];
+    __shared__ __align__(16) uint8_t bst1[kPWaves * kPWaveStage];
+    __shared__ int a_row[kPBM];
     __shared__ int a_slot[kPBM];
 
     const int tid = threadIdx.x;
@@ -200,121 +240,151 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
     const int mt = work - nt * a.max_tiles;
     if (nt >= a.tiles_n || mt >= a.hdr[1]) return;
     const TileEntry te = a.tiles[mt];
-    const int n0 = nt * kCols;
-    const int64_t row_bytes = (int64_t)a.nb * kBlockBytes;
+    const int nb = a.nb;
+    const int steps = nb / 4;
 
     if (tid < kPBM) {
         const bool live = tid < te.rows;
         const int s = live ? a.pairs[te.row0 + tid] : -1;
         a_slot[tid] = s;
-        a_off[tid] = live ? (int)((UG ? s / a.n_used : s) * row_bytes) : (int)a.a_bytes;
+        a_row[tid] = live ? (UG ? s / a.n_used : s) : -1;
     }
-    __syncthreads();
 
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)a.a, 0, (int)a.a_bytes, kBufferWord3);
+    // this wave's 32 weight rows; rows past the output read as zero
+    const int cbase = pg_cols<UG>() * nt + 32 * (UG ? (wave & 3) : wave);
+    const int col = cbase + li;
+    const bool wave_live = cbase < a.n_out;
+    const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+    const int past = (int)a.expert_bytes;            // any offset here reads zero
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.w + (int64_t)te.expert * a.expert_bytes), 0, (int)a.expert_bytes, kBufferWord3);
-    const int steps = a.nb / kPStep;
+        (void *)(a.w + (int64_t)te.expert * a.expert_bytes), 0, past, kBufferWord3);
 
-    // chunk f of a step lands at LDS byte 16 f of the stage buffer (row f / 9,
-    // 16-byte chunk f % 9 of the row's 136 bytes; A rows first, padded to 512
-    // chunks, then the weight rows).  Every thread issues kLoads loads per
-    // step (padding chunks read past the buffers' ends: zeros, no traffic), so
-    // one wait count covers "this step landed, the next ones in flight".
-    auto issue = [&](int st, uint8_t *base, bool real) {
+    // A stage of 4 blocks (136 bytes of a row) in 11 slots of 16 bytes per row:
+    // slots 0-3 bytes 4..68 (halves of blocks 0 and 1 in the rotated order),
+    // 4-7 bytes 72..136 (blocks 2 and 3), 8 bytes 0..16 (block 0's scale and
+    // codes 0,1), 9 bytes 64..80 (the same for block 2), 10 unused.  The row
+    // pitch of 11 slots keeps 16-byte reads of 8 consecutive rows on distinct
+    // banks.  DMA load u, lane l fills slot 64u + l of the wave's 32 x 11.
+    int boff[kPStageLoads];
 #pragma unroll
-        for (int u = 0; u < kALoads; ++u) {
-            const int f = 64 * wave + lane + kPThreads * u;
-            const int r = f / kPChunks;
-            const int c = f - r * kPChunks;
-            const int off = (r < kPBM && real ? a_off[r] + st * kPStepBytes : (int)a.a_bytes) + 16 * c;
-            auto *dst = (__attribute__((address_space(3))) void *)(base + 16 * (64 * wave + kPThreads * u));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, off, 0, 0, 0);
-        }
+    for (int u = 0; u < kPStageLoads; ++u) {
+        const int f = kWave * u + lane;
+        const int r = f / kPSlots, q = f - r * kPSlots;
+        const int wr = UG && wave >= 4 ? a.n_out + cbase + r : cbase + r;
+        const int in_row = q < 4 ? 4 + 16 * q : q < 8 ? 72 + 16 * (q - 4) : q == 8 ? 0 : 64;
+        boff[u] = (r < 32 && q < 10 && wave_live) ? (int)(wr * row_bytes) + in_row : -1;
+    }
+    auto issue_b = [&](int st, uint8_t *stage) {
+        uint8_t *wbase = stage + wave * kPWaveStage;
+        __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's reads of the stage are done
 #pragma unroll
-        for (int u = 0; u < kBLoads; ++u) {
-            const int f = 64 * wave + lane + kPThreads * u;
-            const int i = f / kPChunks;
-            const int c = f - i * kPChunks;
-            // rows past the expert's (clamped to its end) and padding read as zero
-            const int wrow = f >= kBChunks ? a.w_rows :
-                             min(UG ? (i < kCols ? n0 + i : a.n_out + n0 + i - kCols) : n0 + i, a.w_rows);
-            const int off = real ? (int)(wrow * row_bytes) + st * kPStepBytes + 16 * c
-                                 : (int)a.expert_bytes + 16 * c;
-            auto *dst = (__attribute__((address_space(3))) void *)(
-                base + 16 * (kPAChunks + 64 * wave + kPThreads * u));
+        for (int u = 0; u < kPStageLoads; ++u) {
+            const int off = boff[u] >= 0 && st < steps ? boff[u] + st * 4 * kBlockBytes : past;
+            auto *dst = (__attribute__((address_space(3))) void *)(wbase + 1024 * u);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off, 0, 0, kCacheNT);
         }
     };
+    issue_b(0, bst0);
+    issue_b(1, bst1);
 
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-    // Step st: wait for this wave's loads of st (the loads of st+1 stay in
-    // flight), barrier (every wave's landed, and every wave is done with
-    // st-1), issue st+2 into the buffer of st-1, unpack the scales, barrier,
-    // compute.  Raw barriers with explicit waits: a workgroup fence would
-    // also wait for the loads still in flight.  Issues are unconditional (a
-    // step past the end loads zeros without traffic), so one wait count
-    // always holds and the compiler's own tracking of which buffer each load
-    // fills stays exact.
-    auto body = [&](int st, const uint8_t *cur, uint8_t *next2) {
-        __builtin_amdgcn_s_waitcnt(0x3f70 | (kLoads & 15) | ((kLoads >> 4) << 14));
-        __builtin_amdgcn_s_barrier();
-        issue(st + 2, next2, st + 2 < steps);
-        const uint8_t *sa = cur;
-        const uint8_t *sw = cur + 16 * kPAChunks;
-        for (int e = tid; e < kPStep * kRows; e += kPThreads) {
-            const int b = e / kRows;
-            const int r = e - b * kRows;
-            const int ro = r < kPBM ? r * kPRowStride : 16 * kPAChunks + (r - kPBM) * kPRowStride;
-            sc[b][r] = half_bits_to_float(*(const uint16_t *)(cur + ro + b * kBlockBytes));
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the scales are written
-        __builtin_amdgcn_s_barrier();
-        const int wr = 32 * wave + li;
+    const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.a_codes, 0, a.a_rows * nb * 32, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.a_scales, 0, a.a_rows * nb * 4, kBufferWord3);
+    const int a_past = a.a_rows * nb * 32;
+
+    // The 4 blocks of a stage: every LDS operand is read first (the weight
+    // halves from slot 11 li + 2j + h, the scale dwords, the token codes and
+    // scales), then the 4 products are formed and rescaled in block order.
+    auto compute = [&](const uint8_t *stage, int bi0) {
+        const uint8_t *wb = stage + wave * kPWaveStage;
+        u32x4 c[4], av[4];
+        uint32_t d[4];
+        float dx[4][16];
 #pragma unroll
-        for (int b = 0; b < kPStep; ++b) {
-            const int off = b * kBlockBytes + 2 + 16 * h;
-            const v4i A = lds_codes16(sa + li * kPRowStride, off);
-            const v4i B = lds_codes16(sw + wr * kPRowStride, off);
-            const float dw = sc[b][kPBM + wr];
-            float dx[16];
+        for (int j = 0; j < 4; ++j) {
+            c[j] = *(const u32x4 *)(wb + 16 * (kPSlots * li + 2 * j + h));
+            // even j: the dword at the block's start (scale, codes 0 and 1);
+            // odd j: the last dword of the previous block's second half
+            const int dw_at = (j & 1) == 0 ? 4 * (kPSlots * li + 8 + j / 2) + j / 2
+                                           : 4 * (kPSlots * li + 2 * j - 1) + 3;
+            d[j] = ((const uint32_t *)wb)[dw_at];
+            av[j] = *(const u32x4 *)(la + 1024 * (bi0 + j) + 16 * lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 v = *(const float4 *)&sc[b][8 * q + 4 * h];
-                dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                const float4 v = *(const float4 *)&ldx[kPBM * (bi0 + j) + 8 * q + 4 * h];
+                dx[j][4 * q + 0] = v.x; dx[j][4 * q + 1] = v.y;
+                dx[j][4 * q + 2] = v.z; dx[j][4 * q + 3] = v.w;
             }
-            v16i s = {0};
-            s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, s, 0, 0, 0);
+        }
+        v16i sres[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = fmaf(dx[r] * dw, (float)s[r], acc[r]);
+        for (int j = 0; j < 4; ++j) {
+            u32x4 cj = c[j];
+            if ((j & 1) == 0 && h) cj.w = (cj.w & 0xffffu) | (d[j] & 0xffff0000u);
+            sres[j] = (v16i){0};
+            sres[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                (v4i){(int)av[j].x, (int)av[j].y, (int)av[j].z, (int)av[j].w},
+                (v4i){(int)cj.x, (int)cj.y, (int)cj.z, (int)cj.w}, sres[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t sbits = (j & 1) == 0 ? (d[j] & 0xffffu) : (d[j] >> 16);
+            const float dw = half_bits_to_float(sbits);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf(dx[j][r] * dw, (float)sres[j][r], acc[r]);
         }
     };
 
-    issue(0, stage0, true);
-    issue(1, stage1, 1 < steps);
-    for (int st = 0; st < steps; st += 3) {
-        body(st, stage0, stage2);
-        if (st + 1 < steps) body(st + 1, stage1, stage0);
-        if (st + 2 < steps) body(st + 2, stage2, stage1);
+    for (int kb0 = 0; kb0 < nb; kb0 += kPChunk) {
+        // blocks of this chunk, padded to whole stage pairs (the padding reads zero)
+        const int kc = min(kPChunk, (nb - kb0 + kPDepth - 1) / kPDepth * kPDepth);
+        __syncthreads();                 // a_row written; the previous chunk fully read
+        const int ar = a_row[li];
+        // codes: one DMA instruction per block (64 lanes x 16 bytes = 1 KB)
+        for (int bi = wave; bi < kc; bi += kPWaves) {
+            const int b = kb0 + bi;
+            const int off = ar >= 0 && b < nb ? (ar * nb + b) * 32 + 16 * h : a_past;
+            auto *dst = (__attribute__((address_space(3))) void *)(la + 1024 * bi);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, dst, 16, off, 0, 0, 0);
+        }
+        // scales: one dword DMA instruction per two blocks
+        for (int q = wave; 2 * q < kc; q += kPWaves) {
+            const int b = kb0 + 2 * q + h;
+            const int off = ar >= 0 && b < nb ? (ar * nb + b) * 4 : a_past;
+            auto *dst = (__attribute__((address_space(3))) void *)(ldx + 64 * q);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, dst, 4, off, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): every copy of this wave landed
+        __syncthreads();
+
+        // two stages per iteration: wait for the older stage (the newer one's
+        // 6 copies stay in flight), compute its 4 blocks, refill it 2 stages on
+        for (int bi0 = 0; bi0 < kc; bi0 += kPDepth) {
+            const int st = (kb0 + bi0) / 4;
+            __builtin_amdgcn_s_waitcnt(0x3f70 | kPStageLoads);
+            compute(bst0, bi0);
+            issue_b(st + 2, bst0);
+            __builtin_amdgcn_s_waitcnt(0x3f70 | kPStageLoads);
+            compute(bst1, bi0 + 4);
+            issue_b(st + 3, bst1);
+        }
     }
 
-    // slot row 8(r/4) + 4h + r%4 of the tile; column n0 + 32 (wave % 4) + li
-    // (up_gate: waves 4..7 hand their up tiles to waves 0..3 through LDS, in
-    // the same register layout)
-    const int col = n0 + 32 * (UG ? (wave & 3) : wave) + li;
+    // slot row 8(r/4) + 4h + r%4 of the tile; column `col`
     if (UG) {
-        float *xch = (float *)stage0;
-        __syncthreads();                       // every wave is done with the stage buffers
+        float *xch = (float *)la;
+        __syncthreads();                       // every wave is done with the A tile
         if (wave >= 4) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) xch[((wave - 4) * 16 + r) * kWave + lane] = acc[r];
         }
         __syncthreads();
-        if (wave >= 4 || col >= a.n_out) return;
+        if (wave >= 4 || !wave_live) return;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = 8 * (r >> 2) + 4 * h + (r & 3);
@@ -324,7 +394,7 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
             a.out[(int64_t)a_slot[row] * a.n_out + col] = g / (1.0f + expf(-g)) * u;
         }
     } else {
-        if (col >= a.n_out) return;
+        if (!wave_live) return;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = 8 * (r >> 2) + 4 * h + (r & 3);
@@ -338,9 +408,10 @@ size_t align256(size_t v)
     return (v + 255) & ~(size_t)255;
 }
 
-// Workspace layout of the prefill path.
+// Workspace layout of the prefill path (the up_gate call's token rows and the
+// down call's slot rows share the data region).
 struct PrefillWs {
-    size_t offsets, pairs, tiles, data, hq, yslot, total;
+    size_t offsets, pairs, tiles, data, xq_scales, hq_scales, yslot, total;
     int64_t max_tiles;
 };
 
@@ -349,16 +420,18 @@ PrefillWs prefill_layout(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_
 {
     PrefillWs L;
     const int64_t slots = n_tok * n_used;
+    const int64_t nbe = n_embd / kQK, nbf = n_ff / kQK;
     L.max_tiles = slots / kPBM + n_expert + 1;
     L.offsets = 256;
     L.pairs = L.offsets + align256((size_t)(n_expert + 1) * 4);
     L.tiles = L.pairs + align256((size_t)slots * 4);
     L.data = L.tiles + align256((size_t)L.max_tiles * sizeof(TileEntry));
-    const size_t xq = align256((size_t)n_tok * (n_embd / kQK) * kBlockBytes);
-    L.hq = L.data;
-    L.yslot = L.hq + align256((size_t)slots * (n_ff / kQK) * kBlockBytes);
-    const size_t down = L.yslot + align256((size_t)slots * n_embd * 4);
-    L.total = down > L.data + xq ? down : L.data + xq;
+    L.xq_scales = L.data + align256((size_t)n_tok * nbe * 32);
+    const size_t up_end = L.xq_scales + align256((size_t)n_tok * nbe * 4);
+    L.hq_scales = L.data + align256((size_t)slots * nbf * 32);
+    L.yslot = L.hq_scales + align256((size_t)slots * nbf * 4);
+    const size_t down_end = L.yslot + align256((size_t)slots * n_embd * 4);
+    L.total = down_end > up_end ? down_end : up_end;
     return L;
 }
 
@@ -380,16 +453,16 @@ int launch_route(const int32_t *ids, uint8_t *ws, const PrefillWs &L, float *h_n
 }
 
 template <bool UG>
-int launch_grouped(const uint8_t *A, int64_t a_bytes, const uint8_t *w, int64_t w_rows, int64_t nb,
-                   uint8_t *ws, const PrefillWs &L, float *out, int64_t n_out, int64_t n_used,
-                   hipStream_t stream)
+int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows, const uint8_t *w,
+                   int64_t w_rows, int64_t nb, uint8_t *ws, const PrefillWs &L, float *out,
+                   int64_t n_out, int64_t n_used, hipStream_t stream)
 {
     PgArgs p;
-    p.a = A;
-    p.a_bytes = a_bytes;
+    p.a_codes = a_codes;
+    p.a_scales = a_scales;
+    p.a_rows = (int)a_rows;
     p.w = w;
     p.expert_bytes = w_rows * nb * kBlockBytes;
-    p.w_rows = (int)w_rows;
     p.hdr = (const int32_t *)ws;
     p.pairs = (const int32_t *)(ws + L.pairs);
     p.tiles = (const TileEntry *)(ws + L.tiles);
@@ -412,9 +485,9 @@ bool moe_prefill_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_exper
 {
     if (n_tok <= kMoeDecodeMaxTok) return false;
     const int64_t nbe = n_embd / kQK, nbf = n_ff / kQK;
-    if (nbe % kPStep != 0 || nbf % kPStep != 0) return false;
+    if (nbe % kPAlign != 0 || nbf % kPAlign != 0) return false;
     if (n_tok > kMoePrefillMaxTok || n_tok * n_used > kMoePrefillMaxSlots) return false;
-    // buffer-resource ranges and LDS-DMA offsets are 32-bit
+    // buffer-resource ranges and offsets are 32-bit
     const int64_t ug_expert = 2 * n_ff * nbe * kBlockBytes, dn_expert = n_embd * nbf * kBlockBytes;
     const int64_t xq = n_tok * nbe * kBlockBytes, hq = n_tok * n_used * nbf * kBlockBytes;
     const int64_t lim = 0x7f000000LL;   // leaves room for a row past the end
@@ -437,9 +510,9 @@ int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *
     const int64_t nb = n_embd / kQK;
     if (int rc = launch_route(ids, ws, L, h, n_tok * n_used, n_expert, n_ff, stream)) return rc;
     uint8_t *xq = ws + L.data;
-    if (int rc = launch_quantize_rows(x, n_embd, xq, n_tok, n_embd, stream)) return rc < 0 ? -6 : rc;
-    return launch_grouped<true>(xq, n_tok * nb * kBlockBytes, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used,
-                                stream);
+    float *xs = (float *)(ws + L.xq_scales);
+    if (int rc = launch_qa_quantize(x, n_embd, xq, xs, n_tok, nb, stream)) return rc;
+    return launch_grouped<true>(xq, xs, n_tok, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used, stream);
 }
 
 int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids, const float *cw,
@@ -451,11 +524,12 @@ int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids
     const int64_t nb = n_ff / kQK;
     const int64_t slots = n_tok * n_used;
     if (int rc = launch_route(ids, ws, L, nullptr, slots, n_expert, n_ff, stream)) return rc;
-    uint8_t *hq = ws + L.hq;
-    if (int rc = launch_quantize_rows(h, n_ff, hq, slots, n_ff, stream)) return rc < 0 ? -6 : rc;
+    uint8_t *hq = ws + L.data;
+    float *hs = (float *)(ws + L.hq_scales);
+    if (int rc = launch_qa_quantize(h, n_ff, hq, hs, slots, nb, stream)) return rc;
     float *yslot = (float *)(ws + L.yslot);
-    if (int rc = launch_grouped<false>(hq, slots * nb * kBlockBytes, w, n_embd, nb, ws, L, yslot,
-                                       n_embd, n_used, stream))
+    if (int rc = launch_grouped<false>(hq, hs, slots, w, n_embd, nb, ws, L, yslot, n_embd, n_used,
+                                       stream))
         return rc;
     return launch_moe_combine(yslot, ids, cw, out, n_tok, n_embd, n_used, n_expert, stream);
 }

@@ -144,8 +144,10 @@ def test_moe_prefill_checks(lib):
     slots = n_tok * n_used
     max_tiles = slots // 32 + n_expert + 1
     data = 256 + a256((n_expert + 1) * 4) + a256(slots * 4) + a256(max_tiles * 16)
-    down = data + a256(slots * (n_ff // 32) * 34) + a256(slots * n_embd * 4)
-    up = data + a256(n_tok * (n_embd // 32) * 34)
+    # quantized rows in the tile layout: 32 code bytes per block, then fp32 scales
+    down = data + a256(slots * (n_ff // 32) * 32) + a256(slots * (n_ff // 32) * 4) \
+        + a256(slots * n_embd * 4)
+    up = data + a256(n_tok * (n_embd // 32) * 32) + a256(n_tok * (n_embd // 32) * 4)
     ws = q.moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used)
     assert ws == max(up, down)
     assert ws > q.moe_workspace_bytes(16, n_embd, n_ff, n_expert, n_used)

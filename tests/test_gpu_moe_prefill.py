@@ -35,7 +35,9 @@ def _case(orc, n_tok, n_embd, n_ff, n_expert, n_used, tag, ids=None):
     (40, 512, 256, 16, 4),      # several column blocks of 128
     (64, 128, 384, 1, 1),       # one expert: two full tiles of 32 slots, three column blocks
     (200, 256, 384, 32, 8),     # ragged tiles (counts not multiples of 32)
-    (100, 384, 128, 5, 3)])     # few experts, several tiles each
+    (100, 384, 128, 5, 3),      # few experts, several tiles each
+    (24, 4096, 256, 4, 2),      # up_gate K of 128 blocks: the token tile staged in two parts
+    (30, 256, 2560, 3, 2)])     # down K of 80 blocks: a full part and a padded one
 def test_prefill_small(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
     w_ug, w_d, xf, ids, cw = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used,
                                    f"pre-{n_tok}-{n_embd}-{n_ff}")
