@@ -857,6 +857,22 @@ def run_extra(args, q, synth):
                    pct_of_hbm_peak=round(active_bytes / t / 1e9 / HBM_PEAK_GBS * 100, 2),
                    tops=round(2 * macs / t / 1e12, 2),
                    us_up_gate_call=round(t_up * 1e6, 2), us_down_call=round(t_dn * 1e6, 2))
+        # the same layer over expert weights repacked once into the R8 layout
+        # (one moe_r8_ffn_batched call: routing, quantization, both grouped
+        # products and the combine)
+        r8 = dict(w_up_gate_r8=q.q8_0_repack_r8(wug, E * 2 * n_ff, n_embd),
+                  w_down_r8=q.q8_0_repack_r8(wd, E * n_embd, n_ff), x=xf, ids=ids, cw=cw,
+                  h=torch.empty_like(h), out=torch.empty_like(out),
+                  ws=q.moe_r8_workspace(n_tok, n_embd, n_ff, E, U, dev))
+        t8 = _time_launches(lambda: q.moe_r8_ffn_batched([r8], n_embd, n_ff, E), args.steps,
+                            args.warmup) / args.steps
+        res["r8_layout"] = dict(us_per_layer=round(t8 * 1e6, 2),
+                                prompt_tokens_per_s=round(n_tok / t8, 1),
+                                gbs=round(active_bytes / t8 / 1e9, 1),
+                                pct_of_hbm_peak=round(active_bytes / t8 / 1e9 / HBM_PEAK_GBS * 100, 2),
+                                tops=round(2 * macs / t8 / 1e12, 2),
+                                bitwise_equal_to_native=bool(torch.equal(r8["out"], out)
+                                                             and torch.equal(r8["h"], h)))
     return res
 
 

@@ -475,17 +475,24 @@ int moe_down_combine_batched(const moe_down_desc *descs, int64_t n_desc,
                              int64_t n_expert, int64_t n_used, void *stream);
 
 /* ---------------------------------------------------------------------------
- * moe_r8_ffn_batched -- the whole decode expert FFN (the moe_up_gate_swiglu
- * and moe_down_combine arithmetic, same h and out) over expert weights
- * repacked once into the R8 layout (q8_0_repack_r8): w_up_gate_r8 = the
- * combined tensor as n_expert*2*n_ff rows of n_embd values, w_down_r8 = the
- * down tensor as n_expert*n_embd rows of n_ff values.  Two launches per call,
- * several layers of one shape per launch.  h [n_tok][n_used][n_ff] and out
- * [n_tok][n_embd] are written; x, ids, cw as for the native calls.  Each
- * slot streams its expert's rows (repeated experts across tokens are read
- * once per slot), so it serves decode at one or a few tokens.
- * Limits: n_embd % 32 == 0, n_ff % 32 == 0, n_ff <= 2048, n_embd <= 32768,
- * n_tok*n_used <= 1024, n_used <= 16, n_expert <= 1024 (Q8_E_UNSUPPORTED).
+ * moe_r8_ffn_batched -- the whole expert FFN (the moe_up_gate_swiglu and
+ * moe_down_combine arithmetic, same h and out) over expert weights repacked
+ * once into the R8 layout (q8_0_repack_r8): w_up_gate_r8 = the combined tensor
+ * as n_expert*2*n_ff rows of n_embd values, w_down_r8 = the down tensor as
+ * n_expert*n_embd rows of n_ff values.  h [n_tok][n_used][n_ff] and out
+ * [n_tok][n_embd] are written; x, ids, cw as for the native calls.
+ * Up to 16 tokens (decode): two launches per call, several layers of one
+ * shape per launch; each slot streams its expert's rows (repeated experts
+ * across tokens are read once per slot).
+ * More than 16 tokens (prompt evaluation), where n_embd % 128 == 0 and
+ * n_ff % 128 == 0 and the limits of the native prefill path hold: per layer
+ * routing into tiles of up to 32 slots, then the two products on the int8
+ * matrix cores, each expert's rows read once per tile; h and out are bit for
+ * bit those of the native calls on the same weights; h must be 16-byte
+ * aligned on this path.
+ * Limits otherwise: n_embd % 32 == 0, n_ff % 32 == 0, n_ff <= 2048,
+ * n_embd <= 32768, n_tok*n_used <= 1024, n_used <= 16, n_expert <= 1024
+ * (Q8_E_UNSUPPORTED).
  * Out-of-range ids: the error word (first int32 of ws, set every call), NaN
  * h rows for such slots and NaN output rows for their tokens.
  * Workspace: moe_r8_workspace_bytes(...) bytes, 256-byte aligned (0 for an

@@ -579,7 +579,7 @@ size_t moe_r8_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64
 {
     if (n_tok < 0 || n_expert <= 0 || n_used <= 0 || check_k(n_embd) || check_k(n_ff)) return 0;
     if (!q8::moe_r8_ok(n_tok, n_embd, n_ff, n_expert, n_used)) return 0;
-    return q8::moe_r8_ws_bytes(n_tok, n_ff, n_used);
+    return q8::moe_r8_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
 }
 
 int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
@@ -592,7 +592,10 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
     if (n_desc == 0) return Q8_OK;
     if (!descs) return Q8_E_NULL;
     if (n_desc > 4096) return Q8_E_UNSUPPORTED;
-    const size_t need = q8::moe_r8_ws_bytes(n_tok, n_ff, n_used);
+    const size_t need = q8::moe_r8_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
+    // more than 16 tokens: h rows are read back with 16-byte loads
+    const uintptr_t h_align =
+        q8::moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used) ? 16 : 4;
     q8::MoeR8Layer l[4096 / 64];
     for (int64_t i0 = 0; i0 < n_desc; i0 += 64) {
         const int nl = (int)std::min<int64_t>(64, n_desc - i0);
@@ -605,7 +608,8 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
                               !d.h || !d.out))
                 return Q8_E_NULL;
             if (!aligned(d.w_up_gate_r8, 16) || !aligned(d.w_down_r8, 16) || !aligned(d.x, 16) ||
-                !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, 4) || !aligned(d.out, 4))
+                !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, h_align) ||
+                !aligned(d.out, 4))
                 return Q8_E_ALIGN;
             l[i] = {d.w_up_gate_r8, d.w_down_r8, d.x, d.ids, d.cw, d.h, d.out, d.ws};
         }

@@ -142,13 +142,14 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const Ro
 }
 
 // fp32 rows -> the tile layout of the A operand: codes [row][nb][32] (even
-// blocks rotated by two bytes), scales [row][nb] as fp32.  Eight lanes own a
-// block, four values each, with the rule and the bytes of q8_0_quantize_rows.
+// blocks rotated by two bytes when the weights are native rows; in code order
+// for R8 weights), scales [row][nb] as fp32.  Eight lanes own a block, four
+// values each, with the rule and the bytes of q8_0_quantize_rows.
 __global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restrict__ x,
                                                           int64_t row_stride,
                                                           uint8_t *__restrict__ codes,
                                                           float *__restrict__ scales, int64_t nb,
-                                                          int64_t total_blocks)
+                                                          int64_t total_blocks, int rotate)
 {
     const int tid = threadIdx.x;
     const int li = tid & 7;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restric
         // codes 4li+2 .. 4li+5: the upper half of this lane's word and the
         // lower half of the next lane's (lane 7 wraps to codes 0 and 1)
         const uint32_t nxt = (uint32_t)__shfl((int)c, (tid & ~7) | ((tid + 1) & 7));
-        const uint32_t out = (b & 1) ? c : __builtin_amdgcn_alignbyte(nxt, c, 2);
+        const uint32_t out = (b & 1) || !rotate ? c : __builtin_amdgcn_alignbyte(nxt, c, 2);
         if (live) {
             ((uint32_t *)codes)[g * 8 + li] = out;
             if (li == 0) scales[g] = half_bits_to_float(dbits);
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restric
 }
 
 int launch_qa_quantize(const float *x, int64_t row_stride, uint8_t *codes, float *scales,
-                       int64_t n_rows, int64_t nb, hipStream_t stream)
+                       int64_t n_rows, int64_t nb, bool rotate, hipStream_t stream)
 {
     const int64_t total = n_rows * nb;
     if (total == 0) return 0;
@@ -185,7 +186,7 @@ int launch_qa_quantize(const float *x, int64_t row_stride, uint8_t *codes, float
     const int64_t max_grid = 256 * 64;
     const unsigned grid = (unsigned)(tiles < max_grid ? tiles : max_grid);
     hipLaunchKernelGGL(qa_quantize_kernel, dim3(grid), dim3(256), 0, stream, x, row_stride, codes,
-                       scales, nb, total);
+                       scales, nb, total, rotate ? 1 : 0);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -403,6 +404,148 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
     }
 }
 
+// The same grouped product over expert weights in the R8 layout (r8.hip: 8
+// rows per group, scales first, 16-byte code chunks): a wave's 32 weight rows
+// are 4 whole groups, so for one block its 64 lanes load 4 runs of 256
+// contiguous bytes -- the MFMA operand itself, in code order -- straight into
+// registers, 8 blocks in flight, and the 16 scale bytes of each group.  The
+// token tile is staged in LDS once per 64 blocks (codes in code order).
+constexpr int kR8Chunk = 64;
+
+template <bool UG>
+__global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs a)
+{
+    __shared__ __align__(16) uint8_t la[kR8Chunk * 1024];
+    __shared__ __align__(16) float ldx[kR8Chunk * kPBM];
+    __shared__ int a_row[kPBM];
+    __shared__ int a_slot[kPBM];
+
+    const int tid = threadIdx.x;
+    const int wave = wave_uniform(tid >> 6);
+    const int lane = tid & 63;
+    const int h = lane >> 5;
+    const int li = lane & 31;
+
+    const int nwg = (int)gridDim.x;
+    const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int nt = work / a.max_tiles;
+    const int mt = work - nt * a.max_tiles;
+    if (nt >= a.tiles_n || mt >= a.hdr[1]) return;
+    const TileEntry te = a.tiles[mt];
+    const int nb = a.nb;
+
+    if (tid < kPBM) {
+        const bool live = tid < te.rows;
+        const int s = live ? a.pairs[te.row0 + tid] : -1;
+        a_slot[tid] = s;
+        a_row[tid] = live ? (UG ? s / a.n_used : s) : -1;
+    }
+
+    // this wave's 32 weight rows = groups wrow0/8 .. wrow0/8 + 3 of the expert;
+    // lane l takes row l%32 (group (l%32)/8, row l%8 of it), half l/32
+    const int cbase = pg_cols<UG>() * nt + 32 * (UG ? (wave & 3) : wave);
+    const int col = cbase + li;
+    const bool wave_live = cbase < a.n_out;
+    const int wrow0 = UG && wave >= 4 ? a.n_out + cbase : cbase;
+    const int gbytes = 8 * kBlockBytes * nb;
+    const int past = (int)a.expert_bytes;            // any offset here reads zero
+    const int goff = wave_live ? (wrow0 / 8 + (li >> 3)) * gbytes : past;
+    const int r = li & 7;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.w + (int64_t)te.expert * a.expert_bytes), 0, past, kBufferWord3);
+
+    u32x4 wc[kPDepth];
+    uint32_t ws16[kPDepth];
+    auto issue = [&](int b, int i) {
+        const bool in = b < nb;
+        wc[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, in ? goff + 16 * nb + 32 * (8 * b + r) + 16 * h : past, 0, kCacheNT);
+        ws16[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, in ? goff + 2 * (8 * b + r) : past, 0,
+                                                       kCacheNT);
+    };
+#pragma unroll
+    for (int i = 0; i < kPDepth; ++i) issue(i, i);
+
+    float acc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+
+    const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.a_codes, 0, a.a_rows * nb * 32, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.a_scales, 0, a.a_rows * nb * 4, kBufferWord3);
+    const int a_past = a.a_rows * nb * 32;
+
+    for (int kb0 = 0; kb0 < nb; kb0 += kR8Chunk) {
+        const int kc = min(kR8Chunk, (nb - kb0 + kPDepth - 1) / kPDepth * kPDepth);
+        __syncthreads();                 // a_row written; the previous chunk fully read
+        const int ar = a_row[li];
+        for (int bi = wave; bi < kc; bi += kPWaves) {
+            const int b = kb0 + bi;
+            const int off = ar >= 0 && b < nb ? (ar * nb + b) * 32 + 16 * h : a_past;
+            auto *dst = (__attribute__((address_space(3))) void *)(la + 1024 * bi);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, dst, 16, off, 0, 0, 0);
+        }
+        for (int q = wave; 2 * q < kc; q += kPWaves) {
+            const int b = kb0 + 2 * q + h;
+            const int off = ar >= 0 && b < nb ? (ar * nb + b) * 4 : a_past;
+            auto *dst = (__attribute__((address_space(3))) void *)(ldx + 64 * q);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, dst, 4, off, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's copies landed
+        __syncthreads();
+
+        for (int bi0 = 0; bi0 < kc; bi0 += kPDepth) {
+#pragma unroll
+            for (int i = 0; i < kPDepth; ++i) {
+                const int bi = bi0 + i;
+                const u32x4 av = *(const u32x4 *)(la + 1024 * bi + 16 * lane);
+                const u32x4 c = wc[i];
+                v16i sres = {0};
+                sres = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w},
+                    (v4i){(int)c.x, (int)c.y, (int)c.z, (int)c.w}, sres, 0, 0, 0);
+                const float dw = half_bits_to_float(ws16[i]);
+                float dx[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *(const float4 *)&ldx[kPBM * bi + 8 * q + 4 * h];
+                    dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[q] = fmaf(dx[q] * dw, (float)sres[q], acc[q]);
+                issue(kb0 + bi + kPDepth, i);
+            }
+        }
+    }
+
+    if (UG) {
+        float *xch = (float *)la;
+        __syncthreads();                       // every wave is done with the A tile
+        if (wave >= 4) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) xch[((wave - 4) * 16 + q) * kWave + lane] = acc[q];
+        }
+        __syncthreads();
+        if (wave >= 4 || !wave_live) return;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 8 * (q >> 2) + 4 * h + (q & 3);
+            if (row >= te.rows) continue;
+            const float g = acc[q];
+            const float u = xch[(wave * 16 + q) * kWave + lane];
+            a.out[(int64_t)a_slot[row] * a.n_out + col] = g / (1.0f + expf(-g)) * u;
+        }
+    } else {
+        if (!wave_live) return;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 8 * (q >> 2) + 4 * h + (q & 3);
+            if (row < te.rows) a.out[(int64_t)a_slot[row] * a.n_out + col] = acc[q];
+        }
+    }
+}
+
 size_t align256(size_t v)
 {
     return (v + 255) & ~(size_t)255;
@@ -452,7 +595,7 @@ int launch_route(const int32_t *ids, uint8_t *ws, const PrefillWs &L, float *h_n
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-template <bool UG>
+template <bool UG, bool R8>
 int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows, const uint8_t *w,
                    int64_t w_rows, int64_t nb, uint8_t *ws, const PrefillWs &L, float *out,
                    int64_t n_out, int64_t n_used, hipStream_t stream)
@@ -475,7 +618,10 @@ int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows
     int64_t grid = L.max_tiles * p.tiles_n;
     grid = (grid + 7) & ~(int64_t)7;
     if (grid > 0x7fffffff) return -4;
-    hipLaunchKernelGGL(moe_gemm_kernel<UG>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+    if (R8)
+        hipLaunchKernelGGL(moe_r8_gemm_kernel<UG>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(moe_gemm_kernel<UG>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -511,8 +657,8 @@ int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *
     if (int rc = launch_route(ids, ws, L, h, n_tok * n_used, n_expert, n_ff, stream)) return rc;
     uint8_t *xq = ws + L.data;
     float *xs = (float *)(ws + L.xq_scales);
-    if (int rc = launch_qa_quantize(x, n_embd, xq, xs, n_tok, nb, stream)) return rc;
-    return launch_grouped<true>(xq, xs, n_tok, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used, stream);
+    if (int rc = launch_qa_quantize(x, n_embd, xq, xs, n_tok, nb, true, stream)) return rc;
+    return launch_grouped<true, false>(xq, xs, n_tok, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used, stream);
 }
 
 int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids, const float *cw,
@@ -526,10 +672,38 @@ int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids
     if (int rc = launch_route(ids, ws, L, nullptr, slots, n_expert, n_ff, stream)) return rc;
     uint8_t *hq = ws + L.data;
     float *hs = (float *)(ws + L.hq_scales);
-    if (int rc = launch_qa_quantize(h, n_ff, hq, hs, slots, nb, stream)) return rc;
+    if (int rc = launch_qa_quantize(h, n_ff, hq, hs, slots, nb, true, stream)) return rc;
     float *yslot = (float *)(ws + L.yslot);
-    if (int rc = launch_grouped<false>(hq, hs, slots, w, n_embd, nb, ws, L, yslot, n_embd, n_used,
+    if (int rc = launch_grouped<false, false>(hq, hs, slots, w, n_embd, nb, ws, L, yslot, n_embd, n_used,
                                        stream))
+        return rc;
+    return launch_moe_combine(yslot, ids, cw, out, n_tok, n_embd, n_used, n_expert, stream);
+}
+
+int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float *x,
+                          const int32_t *ids, const float *cw, float *h, float *out, void *ws_,
+                          int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                          int64_t n_used, hipStream_t stream)
+{
+    uint8_t *ws = (uint8_t *)ws_;
+    const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
+    const int64_t nbe = n_embd / kQK, nbf = n_ff / kQK;
+    const int64_t slots = n_tok * n_used;
+    // one routing for both products (the tables stay in the workspace)
+    if (int rc = launch_route(ids, ws, L, h, slots, n_expert, n_ff, stream)) return rc;
+    uint8_t *q = ws + L.data;
+    if (int rc = launch_qa_quantize(x, n_embd, q, (float *)(ws + L.xq_scales), n_tok, nbe, false,
+                                    stream))
+        return rc;
+    if (int rc = launch_grouped<true, true>(q, (const float *)(ws + L.xq_scales), n_tok, w_ug,
+                                            2 * n_ff, nbe, ws, L, h, n_ff, n_used, stream))
+        return rc;
+    if (int rc = launch_qa_quantize(h, n_ff, q, (float *)(ws + L.hq_scales), slots, nbf, false,
+                                    stream))
+        return rc;
+    float *yslot = (float *)(ws + L.yslot);
+    if (int rc = launch_grouped<false, true>(q, (const float *)(ws + L.hq_scales), slots, w_dn,
+                                             n_embd, nbf, ws, L, yslot, n_embd, n_used, stream))
         return rc;
     return launch_moe_combine(yslot, ids, cw, out, n_tok, n_embd, n_used, n_expert, stream);
 }

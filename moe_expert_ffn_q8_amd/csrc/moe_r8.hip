@@ -394,15 +394,36 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 
 }  // namespace
 
-bool moe_r8_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used)
+namespace {
+
+bool r8_decode_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used)
 {
     return n_ff % 32 == 0 && n_embd % 32 == 0 && n_ff / 32 <= 64 && n_embd / 32 <= kR8MaxNb &&
            n_used >= 1 && n_used <= kMoeMaxUsed && n_tok * n_used <= kMoeMaxSlots &&
            n_expert <= kMoeMaxExperts;
 }
 
-size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_ff, int64_t n_used)
+}  // namespace
+
+// more than kMoeDecodeMaxTok tokens go to the grouped matrix-core path where
+// its shape conditions hold (as for native rows)
+bool moe_r8_prefill_path(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                         int64_t n_used)
 {
+    return n_tok > kMoeDecodeMaxTok && moe_prefill_ok(n_tok, n_embd, n_ff, n_expert, n_used);
+}
+
+bool moe_r8_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used)
+{
+    return moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used) ||
+           r8_decode_ok(n_tok, n_embd, n_ff, n_expert, n_used);
+}
+
+size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                       int64_t n_used)
+{
+    if (moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used))
+        return moe_prefill_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
     const size_t hq = (size_t)(n_tok * n_used) * (size_t)(n_ff / 32) * kBlockBytes;
     return 256 + (hq + 255) / 256 * 256;
 }
@@ -411,6 +432,16 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream)
 {
     if (n_tok == 0) return 0;
+    if (moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used)) {
+        for (int i = 0; i < n_layers; ++i) {
+            const MoeR8Layer &s = l[i];
+            if (int rc = launch_moe_r8_prefill((const uint8_t *)s.w_up_gate, (const uint8_t *)s.w_down,
+                                               s.x, s.ids, s.cw, s.h, s.out, s.ws, n_tok, n_embd,
+                                               n_ff, n_expert, n_used, stream))
+                return rc;
+        }
+        return 0;
+    }
     for (int l0 = 0; l0 < n_layers; l0 += kMoeMaxLayers) {
         const int nl = n_layers - l0 < kMoeMaxLayers ? n_layers - l0 : kMoeMaxLayers;
         MrUgArgs ug;

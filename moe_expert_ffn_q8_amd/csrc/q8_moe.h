@@ -87,7 +87,16 @@ struct MoeR8Layer {
     void *ws;
 };
 bool moe_r8_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
-size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_ff, int64_t n_used);
+size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                       int64_t n_used);
+bool moe_r8_prefill_path(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                         int64_t n_used);
+// More than kMoeDecodeMaxTok tokens over R8 weights (moe_prefill_ok shapes):
+// routing, quantization, the two grouped products and the combine of one layer.
+int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float *x,
+                          const int32_t *ids, const float *cw, float *h, float *out, void *ws,
+                          int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                          int64_t n_used, hipStream_t stream);
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream);
 

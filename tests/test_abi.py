@@ -453,3 +453,12 @@ def test_moe_r8_checks(lib):
     assert call(D(A, A + 8, A, A, A, A, A, WS, need)) == Q8_E_ALIGN
     assert call(D(A, A, A + 4, A, A, A, A, WS, need)) == Q8_E_ALIGN
     assert call(ok, n_tok=0) == Q8_OK
+    # more than 16 tokens: the grouped path and its workspace (that of the
+    # native-row prefill path); h rows need 16-byte alignment there
+    pre = lib.moe_r8_workspace_bytes(512, 2048, 768, 128, 8)
+    assert pre == lib.moe_workspace_bytes(512, 2048, 768, 128, 8)
+    assert lib.moe_r8_workspace_bytes(16, 2048, 768, 128, 8) == 256 + (128 * 24 * 34 + 255) // 256 * 256
+    big = D(A, A, A, A, A, A, A, WS, pre)
+    assert call(D(A, A, A, A, A, A + 4, A, WS, pre), n_tok=512) == Q8_E_ALIGN     # h
+    assert call(D(A, A, A, A, A, A, A, WS, pre - 1), n_tok=512) == Q8_E_WORKSPACE
+    assert call(big, n_tok=8193) == Q8_E_UNSUPPORTED                            # too many tokens

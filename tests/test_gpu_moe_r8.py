@@ -96,3 +96,77 @@ def test_moe_r8_ffn_invalid_ids(q, orc):
     d2["ws"] = d["ws"]
     q.moe_r8_ffn_batched([d2], n_embd, n_ff, n_expert)
     _check(q, orc, d2, c2, n_tok, n_embd, n_ff, n_expert, n_used)
+
+
+# More than 16 tokens: routing into tiles and the grouped int8 matrix-core
+# products over the R8 weights.
+@pytest.mark.parametrize("n_tok,n_embd,n_ff,n_expert,n_used", [
+    (17, 256, 128, 8, 2),       # fewest tokens on this path
+    (40, 512, 256, 16, 4),      # several column blocks
+    (64, 128, 384, 1, 1),       # one expert: two full tiles, waves past the output
+    (200, 256, 384, 32, 8),     # ragged tiles
+    (24, 4096, 256, 4, 2),      # up_gate K of 128 blocks: the token tile in two parts
+    (30, 256, 2560, 3, 2)])     # down K of 80 blocks: a full part and a padded one
+def test_moe_r8_ffn_prefill(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
+    d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used,
+                  f"r8pre-{n_tok}-{n_embd}-{n_ff}-{n_expert}-{n_used}")
+    q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+    _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
+
+
+def test_moe_r8_ffn_prefill_layers_and_invalid(q, orc):
+    """Two layers of 40 tokens in one call, the second with out-of-range ids
+    (NaN h rows and output rows, error word 1 in that layer's workspace)."""
+    shape = (40, 512, 128, 8, 4)
+    ids = synth.expert_ids(40, 4, 8, "r8pre-bad", "ids")
+    ids[5, 1] = 8
+    ids[33, 3] = -2
+    d0, c0 = _layer(q, orc, *shape, "r8pre-l0")
+    d1, c1 = _layer(q, orc, *shape, "r8pre-bad", ids=ids)
+    q.moe_r8_ffn_batched([d0, d1], shape[1], shape[2], shape[3])
+    _check(q, orc, d0, c0, *shape)
+    assert q.moe_error_word(d1["ws"]) == 1
+    h = d1["h"].cpu().numpy()
+    out = d1["out"].cpu().numpy()
+    assert np.all(np.isnan(h[5, 1])) and np.all(np.isnan(h[33, 3]))
+    assert np.all(np.isnan(out[5])) and np.all(np.isnan(out[33]))
+    good = np.array([t for t in range(40) if t not in (5, 33)])
+    h_ref = orc.moe_up_gate_swiglu(c1["w_ug"], c1["xq"][good], c1["ids"][good], shape[1],
+                                   shape[2], shape[3])
+    assert_rows_close(h[good].reshape(-1, shape[2]), h_ref.reshape(-1, shape[2]))
+    out_ref = orc.moe_down_combine(c1["w_d"], h[good], c1["ids"][good], c1["cw"][good], shape[2],
+                                   shape[1], shape[3])
+    assert_rows_close(out[good], out_ref)
+
+
+def test_moe_r8_ffn_prefill_full_layer(q, orc):
+    """The Gemma-4-26B-A4B expert FFN shape at 512 tokens: h and out bit for bit
+    equal to the native-row prefill path on the same weights (both sum each
+    element's exact block products in ascending block order), and sampled
+    tokens against the oracle."""
+    n_tok, n_embd, n_ff, n_expert, n_used = 512, 2048, 768, 128, 8
+    d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, "r8pre-full")
+    q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+    assert q.moe_error_word(d["ws"]) == 0
+    ws = q.moe_workspace(n_tok, n_embd, n_ff, n_expert, n_used, "cuda")
+    h_nat = torch_nan_like(d["h"])
+    q.moe_up_gate_swiglu(to_gpu(c["w_ug"]), d["x"], d["ids"], n_embd, n_ff, n_expert, ws, h=h_nat)
+    out_nat = torch_nan_like(d["out"])
+    q.moe_down_combine(to_gpu(c["w_d"]), h_nat, d["ids"], d["cw"], n_ff, n_embd, n_expert, ws,
+                       out=out_nat)
+    import torch
+    assert torch.equal(d["h"], h_nat)
+    assert torch.equal(d["out"], out_nat)
+    sel = np.array([0, 3, 200, 511])
+    h = d["h"].cpu().numpy()
+    h_ref = orc.moe_up_gate_swiglu(c["w_ug"], c["xq"][sel], c["ids"][sel], n_embd, n_ff,
+                                   n_expert)
+    assert_rows_close(h[sel].reshape(-1, n_ff), h_ref.reshape(-1, n_ff))
+    out_ref = orc.moe_down_combine(c["w_d"], h[sel], c["ids"][sel], c["cw"][sel], n_ff, n_embd,
+                                   n_expert)
+    assert_rows_close(d["out"].cpu().numpy()[sel], out_ref)
+
+
+def torch_nan_like(t):
+    import torch
+    return torch.full_like(t, float("nan"))
