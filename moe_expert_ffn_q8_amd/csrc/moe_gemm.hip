@@ -282,7 +282,10 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
         for (int u = 0; u < kPStageLoads; ++u) {
             const int off = boff[u] >= 0 && st < steps ? boff[u] + st * 4 * kBlockBytes : past;
             auto *dst = (__attribute__((address_space(3))) void *)(wbase + 1024 * u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off, 0, 0, kCacheNT);
+            // default cache policy: a 136-byte stage is not line-aligned, so
+            // consecutive stages of a row share a cache line (non-temporal
+            // loads fetched 1.29x the weight bytes from HBM)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off, 0, 0, 0);
         }
     };
     issue_b(0, bst0);
@@ -456,12 +459,13 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
 
     u32x4 wc[kPDepth];
     uint32_t ws16[kPDepth];
+    // default cache policy: the second tile of an expert (more than 32
+    // slots) runs beside the first on the same XCD and finds its rows in L2
     auto issue = [&](int b, int i) {
         const bool in = b < nb;
         wc[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            rw, in ? goff + 16 * nb + 32 * (8 * b + r) + 16 * h : past, 0, kCacheNT);
-        ws16[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, in ? goff + 2 * (8 * b + r) : past, 0,
-                                                       kCacheNT);
+            rw, in ? goff + 16 * nb + 32 * (8 * b + r) + 16 * h : past, 0, 0);
+        ws16[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, in ? goff + 2 * (8 * b + r) : past, 0, 0);
     };
 #pragma unroll
     for (int i = 0; i < kPDepth; ++i) issue(i, i);
