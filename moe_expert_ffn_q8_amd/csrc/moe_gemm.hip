@@ -26,17 +26,22 @@
 //     32 x 32 tile of v_mfma_i32_32x32x32_i8 per wave (K = 32 = one block, so
 //     each instruction gives exact int32 block sums, rescaled per block into
 //     fp32 accumulators).  A = the tile's quantized rows, copied into LDS once
-//     (up to 64 blocks at a time) by LDS-DMA loads, laid out so that every
-//     operand read is one conflict-free 16-byte read.  B = the wave's own 32
-//     weight rows, streamed straight from HBM into registers, 8 blocks in
-//     flight: a native 34-byte block holds its codes 2 bytes past a dword
-//     boundary in every other block, so a lane loads the dword-aligned 16
-//     bytes that the rotated order starts with plus the dword holding the
-//     scale (and, for the second half of an even block, codes 0 and 1).  No
-//     barrier inside the K loop.  up_gate: waves 0..3 hold gate tiles, waves
-//     4..7 the up tiles of the same 128 columns; the up tiles go through LDS
-//     and the epilogue writes silu(g) * u element by element.  down: per-slot
-//     rows [slot][n_embd] into the workspace.
+//     per 32 blocks (64 over R8 weights) by LDS-DMA loads, laid out so that
+//     every operand read is one conflict-free 16-byte read.  B = the wave's
+//     own 32 weight rows, no barrier inside the K loop:
+//       native rows (moe_gemm_kernel): a 34-byte block holds its codes 2
+//       bytes past a dword boundary in every other block, so each wave stages
+//       the dword-aligned 16-byte pieces of the rotated order plus the dwords
+//       holding the scales (and, for the second half of an even block, codes
+//       0 and 1) through two per-wave LDS stages of 4 blocks, with coalesced
+//       DMA at a row pitch of 11 slots;
+//       R8 rows (moe_r8_gemm_kernel): the wave's rows are 4 whole groups, so
+//       a block's operand is 4 runs of 256 contiguous bytes loaded straight
+//       into registers, 8 blocks in flight, codes in their own order.
+//     up_gate: waves 0..3 hold gate tiles, waves 4..7 the up tiles of the same
+//     128 columns; the up tiles go through LDS and the epilogue writes
+//     silu(g) * u element by element.  down: per-slot rows [slot][n_embd]
+//     into the workspace.
 //  4. down only: the decode path's combine kernel (ascending u per token).
 // Every output element is a sum over its own row and column only, so the
 // order of slots inside an expert's tiles does not change any result.
