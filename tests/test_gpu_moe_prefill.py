@@ -37,7 +37,9 @@ def _case(orc, n_tok, n_embd, n_ff, n_expert, n_used, tag, ids=None):
     (200, 256, 384, 32, 8),     # ragged tiles (counts not multiples of 32)
     (100, 384, 128, 5, 3),      # few experts, several tiles each
     (24, 4096, 256, 4, 2),      # up_gate K of 128 blocks: the token tile staged in two parts
-    (30, 256, 2560, 3, 2)])     # down K of 80 blocks: a full part and a padded one
+    (30, 256, 2560, 3, 2),      # down K of 80 blocks: a full part and a padded one
+    (300, 256, 128, 2, 2),      # two experts with about ten tiles each
+    (40, 256, 128, 1024, 16)])  # the most experts, 16 slots per token, most experts idle
 def test_prefill_small(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
     w_ug, w_d, xf, ids, cw = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used,
                                    f"pre-{n_tok}-{n_embd}-{n_ff}")

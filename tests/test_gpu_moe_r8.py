@@ -106,7 +106,9 @@ def test_moe_r8_ffn_invalid_ids(q, orc):
     (64, 128, 384, 1, 1),       # one expert: two full tiles, waves past the output
     (200, 256, 384, 32, 8),     # ragged tiles
     (24, 4096, 256, 4, 2),      # up_gate K of 128 blocks: the token tile in two parts
-    (30, 256, 2560, 3, 2)])     # down K of 80 blocks: a full part and a padded one
+    (30, 256, 2560, 3, 2),      # down K of 80 blocks: a full part and a padded one
+    (300, 256, 128, 2, 2),      # two experts with about ten tiles each
+    (40, 256, 128, 1024, 16)])  # the most experts, 16 slots per token, most experts idle
 def test_moe_r8_ffn_prefill(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
     d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used,
                   f"r8pre-{n_tok}-{n_embd}-{n_ff}-{n_expert}-{n_used}")
