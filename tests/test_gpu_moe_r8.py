@@ -172,3 +172,27 @@ def test_moe_r8_ffn_prefill_full_layer(q, orc):
 def torch_nan_like(t):
     import torch
     return torch.full_like(t, float("nan"))
+
+
+def test_moe_r8_ffn_workspace_reuse(q, orc):
+    """One workspace (sized for the largest call) across calls of different
+    sizes and paths: 200 tokens, then 40, then 4 (decode kernels), then 40
+    with an out-of-range id, then 40 again: every call's results and error
+    word are its own."""
+    import torch
+    n_embd, n_ff, n_expert, n_used = 256, 128, 16, 4
+    ws = q.moe_r8_workspace(200, n_embd, n_ff, n_expert, n_used, "cuda")
+    assert ws.numel() >= q.moe_r8_workspace(40, n_embd, n_ff, n_expert, n_used, "cuda").numel()
+    for i, n_tok in enumerate([200, 40, 4, 40, 40]):
+        ids = None
+        if i == 3:
+            ids = synth.expert_ids(n_tok, n_used, n_expert, "r8ws-bad", "ids")
+            ids[7, 2] = n_expert
+        d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, f"r8ws-{i}", ids=ids)
+        d["ws"] = ws
+        q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+        if i == 3:
+            assert q.moe_error_word(ws) == 1
+            assert bool(torch.isnan(d["out"][7]).all())
+            continue
+        _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
