@@ -578,9 +578,10 @@ def moe_r8_workspace(n_tok, n_embd, n_ff, n_expert, n_used, device):
 
 
 def moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert):
-    """The decode expert FFN over R8 expert weights for independent layers of
-    one shape.  layers: list of dicts with w_up_gate_r8, w_down_r8, x, ids, cw,
-    h (written), out (written), ws."""
+    """The expert FFN over R8 expert weights for independent layers of one
+    shape (decode kernels up to 16 tokens, the grouped matrix-core path above).
+    layers: list of dicts with w_up_gate_r8, w_down_r8, x, ids, cw, h
+    (written), out (written), ws."""
     if not layers:
         return
     for d in layers:
