@@ -136,3 +136,69 @@ def test_dequantization_error_bound(orc):
     err = np.abs(xb - dh[..., None] * codes)
     bound = d32[..., None] / 2 * (1 + 1e-6) + np.abs(codes) * np.abs(dh - d32)[..., None]
     assert np.all(err <= bound + 1e-12)
+
+
+def _round_half_away(r32):
+    """sign(r) * floor(|r| + 1/2) of fp32 quotients, evaluated in fp64 (exact:
+    an fp32 value plus one half is representable in fp64)."""
+    r = np.asarray(r32, dtype=np.float32).astype(np.float64)
+    return np.sign(r) * np.floor(np.abs(r) + 0.5)
+
+
+def _codes_by_division(x):
+    """Q8_0 codes of fp32 rows by the rule as written: d = amax / 127 and the
+    quotient x / d, both IEEE fp32 divisions (numpy's float32 divide), then
+    round half away from zero."""
+    x = np.asarray(x, dtype=np.float32)
+    xb = x.reshape(x.shape[0], -1, 32)
+    d = (np.abs(xb).max(axis=2) / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = _round_half_away(xb / d[..., None])
+    return np.where(d[..., None] > 0, q, 0.0)
+
+
+@pytest.mark.parametrize("sigma", [1.0, 0.02])
+def test_codes_equal_fp32_division_rule(orc, sigma):
+    """Every code equals round-half-away(x / d) with the quotient an fp32
+    division, exactly (not merely within half a unit): this separates the
+    division from a reciprocal multiply or a 127/amax multiply, which give
+    other codes for about one value in a million."""
+    x = synth.normal_f32((256, 4096), sigma, "test", "quant-division", int(sigma * 1000))
+    _, codes = orc.split_blocks(orc.quantize_rows(x))
+    assert np.array_equal(codes.astype(np.float64), _codes_by_division(x))
+
+
+def test_division_not_reciprocal_multiply(orc):
+    """Blocks built from values one to three fp32 ulps from a rounding tie,
+    chosen where x * (1/d) (and, for some, x * (127/amax)) rounds to another
+    integer than x / d: the oracle must give the division's codes on all."""
+    g = np.random.default_rng(11)
+    blocks, n_recip, n_ratio = [], 0, 0
+    while len(blocks) < 64:
+        amax = np.float32(g.uniform(0.25, 8.0))
+        d = amax / np.float32(127.0)
+        inv = np.float32(1.0) / d
+        ratio = np.float32(127.0) / amax
+        ties = ((np.arange(126) + 0.5) * np.float64(d)).astype(np.float32)
+        cand = []
+        for direction in (np.float32(np.inf), np.float32(-np.inf)):
+            x = ties.copy()
+            for _ in range(3):
+                x = np.nextafter(x, direction)
+                a = _round_half_away(x / d)
+                cand += [v for v, ok in zip(x, a != _round_half_away(x * inv)) if ok]
+        if len(cand) < 8:
+            continue
+        vals = np.array(cand[:31], dtype=np.float32)
+        sign = np.where(g.random(len(vals)) < 0.5, -1, 1).astype(np.float32)
+        blk = np.zeros(32, dtype=np.float32)
+        blk[0] = amax
+        blk[1:1 + len(vals)] = vals * sign
+        n_recip += int(np.sum(_round_half_away(blk / d) != _round_half_away(blk * inv)))
+        n_ratio += int(np.sum(_round_half_away(blk / d) != _round_half_away(blk * ratio)))
+        blocks.append(blk)
+    x = np.stack(blocks).reshape(1, -1)
+    _, codes = orc.split_blocks(orc.quantize_rows(x))
+    assert n_recip >= 64 * 8                 # the blocks really separate the two forms
+    assert n_ratio > 0
+    assert np.array_equal(codes.astype(np.float64).reshape(1, -1, 32), _codes_by_division(x))
