@@ -319,8 +319,19 @@ int q8_0_matmul_f32_batched(const q8_0_matmul_f32_desc *descs, int64_t n_desc, v
 /* q8_0_matmul_f32_step: the products of q8_0_matmul_f32_batched (same
  * descriptors and rules) for m <= 2, as one launch in which every activation
  * row is quantized once: the first workgroups quantize the rows into the
- * workspace, and each product tile waits (on a per-row ready counter in the
- * workspace) for the rows it reads.  This is the whole decode step of the
+ * workspace, and each product tile waits for the rows it reads.  Protocol:
+ * every batch entry's quantizer parts count themselves on a per-entry part
+ * counter; the entry's last part resets that counter and sets one flag per
+ * product tile of the entry; a tile takes its flag with one atomic exchange
+ * (read and clear in one access) and polls until it reads 1, so every flag
+ * and counter is zero again at the end of a call that completes.  Ordering
+ * rests on agent-scope accesses, not on release/acquire fences: the
+ * quantized rows are written with agent-scope stores and read with
+ * agent-scope loads (each coherent across the device's L2 caches by itself),
+ * counters and flags are relaxed agent-scope atomics, a quantizer waits for
+ * its stores to complete (s_waitcnt on the store counter) before it counts
+ * itself, and a tile issues its row loads only after its poll has returned
+ * 1.  The wait is bounded (see the error word below).  This is the whole decode step of the
  * narray-llm README's Llama 2 110M int8 table (every matvec's input
  * re-quantized, [NARR] sections on the measurement and on kernels per token)
  * in one launch.  Results are bitwise equal to q8_0_quantize_rows followed by

@@ -174,6 +174,60 @@ def _need(t, dtype, name):
         raise ValueError(f"{name}: must be a GPU tensor")
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _fit(t, nbytes, name):
+    """A contiguous GPU tensor that holds at least nbytes (the extent the
+    kernels touch for the shape arguments of the call)."""
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if nbytes > _nbytes(t):
+        raise ValueError(f"{name}: the shape arguments need {nbytes} bytes, the tensor holds "
+                         f"{_nbytes(t)}")
+
+
+def _one_device(*ts):
+    """Every tensor (or (tensor, offset) pair) of a call on one device."""
+    devs = {(t[0] if isinstance(t, tuple) else t).device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(map(str, devs))}")
+
+
+def _addr(t, unit, nbytes, name):
+    """Address of a descriptor operand: t is a tensor or a (tensor, offset)
+    pair with the offset in `unit` bytes; the tensor must hold nbytes from
+    that address on."""
+    base, off = (t if isinstance(t, tuple) else (t, 0))
+    if not base.is_contiguous() or not base.is_cuda:
+        raise ValueError(f"{name}: must be a contiguous GPU tensor")
+    if off < 0:
+        raise ValueError(f"{name}: negative offset")
+    avail = _nbytes(base) - off * unit
+    if nbytes > 0 and nbytes > avail:
+        raise ValueError(f"{name}: the descriptor needs {nbytes} bytes from its start, the "
+                         f"tensor holds {max(avail, 0)}")
+    return base.data_ptr() + off * unit
+
+
+def _span(batch, bstride, rows, rstride, last):
+    """Elements from the first to one past the last one touched: `batch`
+    entries `bstride` apart, each `rows` rows `rstride` apart of `last`
+    elements (0 when nothing is touched)."""
+    if batch <= 0 or rows <= 0 or last <= 0:
+        return 0
+    return (batch - 1) * bstride + (rows - 1) * rstride + last
+
+
+def _r8_bytes_py(n, k):
+    return (n + 7) // 8 * 272 * (k // QK)
+
+
 def status_str(status):
     return _lib.q8_status_str(int(status)).decode()
 
@@ -197,9 +251,13 @@ def q8_0_quantize_rows(x, y=None, k=None):
         raise ValueError("x: GPU fp32 with unit column stride")
     n_rows = x.shape[0]
     k = x.shape[1] if k is None else k
+    if x.shape[1] < k:
+        raise ValueError(f"x: rows of {x.shape[1]} values, k = {k}")
     if y is None:
         y = q8_empty(n_rows, k, x.device)
     _need(y, torch.uint8, "y")
+    _one_device(x, y)
+    _fit(y, n_rows * (k // QK) * BLOCK_BYTES, "y")
     _check("q8_0_quantize_rows", _lib.q8_0_quantize_rows(
         _ptr(x), x.stride(0) if n_rows > 1 else k, _ptr(y), n_rows, k, _stream(x)))
     return y
@@ -211,6 +269,11 @@ def q8_0_matvec(w, x, n, k, y=None):
     if y is None:
         y = torch.empty(n, dtype=torch.float32, device=w.device)
     _need(y, torch.float32, "y")
+    _one_device(w, x, y)
+    nb = k // QK
+    _fit(w, n * nb * BLOCK_BYTES, "w")
+    _fit(x, nb * BLOCK_BYTES, "x")
+    _fit(y, n * 4, "y")
     _check("q8_0_matvec", _lib.q8_0_matvec(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(w)))
     return y
 
@@ -227,6 +290,9 @@ def q8_0_repack_r8(w, n, k, out=None):
     if out is None:
         out = torch.empty(q8_0_r8_bytes(n, k), dtype=torch.uint8, device=w.device)
     _need(out, torch.uint8, "out")
+    _one_device(w, out)
+    _fit(w, n * (k // QK) * BLOCK_BYTES, "w")
+    _fit(out, q8_0_r8_bytes(n, k), "out")
     _check("q8_0_repack_r8", _lib.q8_0_repack_r8(_ptr(w), _ptr(out), n, k, _stream(w)))
     return out
 
@@ -237,6 +303,10 @@ def q8_0_matvec_r8(w_r8, x, n, k, y=None):
     if y is None:
         y = torch.empty(n, dtype=torch.float32, device=w_r8.device)
     _need(y, torch.float32, "y")
+    _one_device(w_r8, x, y)
+    _fit(w_r8, q8_0_r8_bytes(n, k), "w_r8")
+    _fit(x, (k // QK) * BLOCK_BYTES, "x")
+    _fit(y, n * 4, "y")
     _check("q8_0_matvec_r8", _lib.q8_0_matvec_r8(_ptr(w_r8), _ptr(x), _ptr(y), n, k,
                                                  _stream(w_r8)))
     return y
@@ -247,11 +317,12 @@ def make_r8_desc(w_r8, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride=0,
     """One q8_0_r8_desc.  w_r8 (bytes), x (blocks), y (floats) are (tensor,
     element offset) pairs or tensors; w_batch_stride in bytes, x_batch_stride
     in blocks, y_batch_stride in floats."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
-    return Q8R8Desc(addr(w_r8, 1), addr(x, BLOCK_BYTES), addr(y, 4), n, k, batch,
+    _one_device(w_r8, x, y)
+    nb = k // QK
+    wb = _span(batch, w_batch_stride, 1, 0, _r8_bytes_py(n, k)) if n > 0 else 0
+    return Q8R8Desc(_addr(w_r8, 1, wb, "w_r8"),
+                    _addr(x, BLOCK_BYTES, _span(batch, x_batch_stride, 1, 0, nb) * BLOCK_BYTES, "x"),
+                    _addr(y, 4, _span(batch, y_batch_stride, 1, 0, n) * 4, "y"), n, k, batch,
                     w_batch_stride, x_batch_stride, y_batch_stride)
 
 
@@ -267,11 +338,11 @@ def make_r8_f32_desc(w_r8, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride
     """One q8_0_r8_f32_desc.  w_r8 (bytes), x (floats), y (floats) are (tensor,
     element offset) pairs or tensors; w_batch_stride in bytes, the others in
     floats."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
-    return Q8R8F32Desc(addr(w_r8, 1), addr(x, 4), addr(y, 4), n, k, batch,
+    _one_device(w_r8, x, y)
+    wb = _span(batch, w_batch_stride, 1, 0, _r8_bytes_py(n, k)) if n > 0 else 0
+    return Q8R8F32Desc(_addr(w_r8, 1, wb, "w_r8"),
+                       _addr(x, 4, _span(batch, x_batch_stride, 1, 0, k) * 4 if n > 0 else 0, "x"),
+                       _addr(y, 4, _span(batch, y_batch_stride, 1, 0, n) * 4, "y"), n, k, batch,
                        w_batch_stride, x_batch_stride, y_batch_stride)
 
 
@@ -287,15 +358,16 @@ def make_r8_mm_desc(w_r8, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stri
     """One q8_0_r8_mm_desc.  w_r8 (bytes), x (blocks), y (floats) are (tensor,
     element offset) pairs or tensors; w_batch_stride in bytes, x strides in
     blocks, y strides in floats."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
     nb = k // QK
-    return Q8R8MmDesc(addr(w_r8, 1), addr(x, BLOCK_BYTES), addr(y, 4), n, k, m, batch,
-                      w_batch_stride, nb if x_row_stride is None else x_row_stride,
-                      x_batch_stride, n if y_row_stride is None else y_row_stride,
-                      y_batch_stride)
+    xrs = nb if x_row_stride is None else x_row_stride
+    yrs = n if y_row_stride is None else y_row_stride
+    _one_device(w_r8, x, y)
+    live = n > 0 and m > 0
+    wb = _span(batch, w_batch_stride, 1, 0, _r8_bytes_py(n, k)) if live else 0
+    xb = _span(batch, x_batch_stride, m, xrs, nb) * BLOCK_BYTES if live else 0
+    return Q8R8MmDesc(_addr(w_r8, 1, wb, "w_r8"), _addr(x, BLOCK_BYTES, xb, "x"),
+                      _addr(y, 4, _span(batch, y_batch_stride, m, yrs, n) * 4, "y"), n, k, m,
+                      batch, w_batch_stride, xrs, x_batch_stride, yrs, y_batch_stride)
 
 
 def q8_0_matmul_r8_batched(descs, stream_of):
@@ -316,9 +388,13 @@ def q8_1_quantize_rows(x, k=None, y=None):
         raise ValueError("x: GPU fp32 with unit column stride")
     n_rows = x.shape[0]
     k = x.shape[1] if k is None else k
+    if x.shape[1] < k:
+        raise ValueError(f"x: rows of {x.shape[1]} values, k = {k}")
     if y is None:
         y = torch.empty((n_rows, k // QK * Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
     _need(y, torch.uint8, "y")
+    _one_device(x, y)
+    _fit(y, n_rows * (k // QK) * Q8_1_BLOCK_BYTES, "y")
     _check("q8_1_quantize_rows", _lib.q8_1_quantize_rows(
         _ptr(x), x.stride(0) if n_rows > 1 else k, _ptr(y), n_rows, k, _stream(x)))
     return y
@@ -334,20 +410,28 @@ def kq_matvec(t, w, x, n, k, y=None):
     fn = {4: _lib.q4_k_matvec, 5: _lib.q5_k_matvec}.get(t)
     if fn is None:
         raise ValueError(f"unknown K-quant type {t}")
+    _one_device(w, x, y)
+    _fit(w, n * (k // 256) * KQ_BLOCK_BYTES[t], "w")
+    _fit(x, (k // QK) * Q8_1_BLOCK_BYTES, "x")
+    _fit(y, n * 4, "y")
     _check("q4_k_matvec" if t == 4 else "q5_k_matvec",
            fn(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(w)))
     return y
 
 
-def make_kq_desc(w, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride=0, y_batch_stride=0):
-    """One kq_matvec_desc.  w (bytes), x (bytes), y (floats) are (tensor, element
-    offset) pairs or tensors; strides in super-blocks, Q8_1 blocks, floats."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
-    return KqMatvecDesc(addr(w, 1), addr(x, 1), addr(y, 4), n, k, batch, w_batch_stride,
-                        x_batch_stride, y_batch_stride)
+def make_kq_desc(w, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride=0, y_batch_stride=0,
+                 t=4):
+    """One kq_matvec_desc for K-quant type t (4: Q4_K, 5: Q5_K).  w (bytes), x
+    (bytes), y (floats) are (tensor, element offset) pairs or tensors; strides
+    in super-blocks, Q8_1 blocks, floats."""
+    _one_device(w, x, y)
+    bb = KQ_BLOCK_BYTES[t]
+    live = n > 0
+    wb = _span(batch, w_batch_stride, 1, 0, n * (k // 256)) * bb if live else 0
+    xb = _span(batch, x_batch_stride, 1, 0, k // QK) * Q8_1_BLOCK_BYTES if live else 0
+    return KqMatvecDesc(_addr(w, 1, wb, "w"), _addr(x, 1, xb, "x"),
+                        _addr(y, 4, _span(batch, y_batch_stride, 1, 0, n) * 4, "y"), n, k, batch,
+                        w_batch_stride, x_batch_stride, y_batch_stride)
 
 
 def kq_matvec_batched(t, descs, stream_of):
@@ -361,6 +445,11 @@ def q8_0_matmul(w, x, n, k, m, y=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=w.device)
     _need(y, torch.float32, "y")
+    _one_device(w, x, y)
+    nb = k // QK
+    _fit(w, n * nb * BLOCK_BYTES, "w")
+    _fit(x, m * nb * BLOCK_BYTES, "x")
+    _fit(y, m * n * 4, "y")
     _check("q8_0_matmul", _lib.q8_0_matmul(_ptr(w), _ptr(x), _ptr(y), n, k, m, _stream(w)))
     return y
 
@@ -369,15 +458,16 @@ def make_desc(w, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
               x_batch_stride=0, y_row_stride=None, y_batch_stride=0):
     """One q8_0_matmul_desc.  w, x, y are (tensor, element offset) pairs or tensors;
     strides are in blocks (w, x) and floats (y)."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
     nb = k // QK
-    return Q8MatmulDesc(addr(w, BLOCK_BYTES), addr(x, BLOCK_BYTES), addr(y, 4), n, k, m, batch,
-                        w_batch_stride, nb if x_row_stride is None else x_row_stride,
-                        x_batch_stride, n if y_row_stride is None else y_row_stride,
-                        y_batch_stride)
+    xrs = nb if x_row_stride is None else x_row_stride
+    yrs = n if y_row_stride is None else y_row_stride
+    _one_device(w, x, y)
+    live = n > 0 and m > 0
+    wb = _span(batch, w_batch_stride, 1, 0, n * nb) * BLOCK_BYTES if live else 0
+    xb = _span(batch, x_batch_stride, m, xrs, nb) * BLOCK_BYTES if live else 0
+    return Q8MatmulDesc(_addr(w, BLOCK_BYTES, wb, "w"), _addr(x, BLOCK_BYTES, xb, "x"),
+                        _addr(y, 4, _span(batch, y_batch_stride, m, yrs, n) * 4, "y"), n, k, m,
+                        batch, w_batch_stride, xrs, x_batch_stride, yrs, y_batch_stride)
 
 
 def make_up_gate_desc(w, x, h, n_ff, n_embd, m=1, batch=1, w_batch_stride=0, x_row_stride=None,
@@ -385,14 +475,16 @@ def make_up_gate_desc(w, x, h, n_ff, n_embd, m=1, batch=1, w_batch_stride=0, x_r
     """One q8_0_up_gate_desc.  w (combined [2*n_ff][n_embd/32] blocks, gate rows
     first), x (Q8_0 rows), h are (tensor, element offset) pairs or tensors;
     strides are in blocks (w, x) and floats (h)."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
     nb = n_embd // QK
-    return Q8UpGateDesc(addr(w, BLOCK_BYTES), addr(x, BLOCK_BYTES), addr(h, 4), n_ff, n_embd, m,
-                        batch, w_batch_stride, nb if x_row_stride is None else x_row_stride,
-                        x_batch_stride, n_ff if h_row_stride is None else h_row_stride,
+    xrs = nb if x_row_stride is None else x_row_stride
+    hrs = n_ff if h_row_stride is None else h_row_stride
+    _one_device(w, x, h)
+    live = n_ff > 0 and m > 0
+    wb = _span(batch, w_batch_stride, 1, 0, 2 * n_ff * nb) * BLOCK_BYTES if live else 0
+    xb = _span(batch, x_batch_stride, m, xrs, nb) * BLOCK_BYTES if live else 0
+    return Q8UpGateDesc(_addr(w, BLOCK_BYTES, wb, "w"), _addr(x, BLOCK_BYTES, xb, "x"),
+                        _addr(h, 4, _span(batch, h_batch_stride, m, hrs, n_ff) * 4, "h"), n_ff,
+                        n_embd, m, batch, w_batch_stride, xrs, x_batch_stride, hrs,
                         h_batch_stride)
 
 
@@ -414,14 +506,15 @@ def make_f32_desc(w, x, y, n, k, m=1, batch=1, w_batch_stride=0, x_row_stride=No
     """One q8_0_matmul_f32_desc (fp32 activations, quantized inside).  w, x, y
     are (tensor, element offset) pairs or tensors; strides are in blocks (w)
     and floats (x, y)."""
-    def addr(t, unit):
-        if isinstance(t, tuple):
-            return t[0].data_ptr() + t[1] * unit
-        return t.data_ptr()
-    return Q8MatmulF32Desc(addr(w, BLOCK_BYTES), addr(x, 4), addr(y, 4), n, k, m, batch,
-                           w_batch_stride, k if x_row_stride is None else x_row_stride,
-                           x_batch_stride, n if y_row_stride is None else y_row_stride,
-                           y_batch_stride)
+    xrs = k if x_row_stride is None else x_row_stride
+    yrs = n if y_row_stride is None else y_row_stride
+    _one_device(w, x, y)
+    live = n > 0 and m > 0
+    wb = _span(batch, w_batch_stride, 1, 0, n * (k // QK)) * BLOCK_BYTES if live else 0
+    xb = _span(batch, x_batch_stride, m, xrs, k) * 4 if live else 0
+    return Q8MatmulF32Desc(_addr(w, BLOCK_BYTES, wb, "w"), _addr(x, 4, xb, "x"),
+                           _addr(y, 4, _span(batch, y_batch_stride, m, yrs, n) * 4, "y"), n, k,
+                           m, batch, w_batch_stride, xrs, x_batch_stride, yrs, y_batch_stride)
 
 
 def q8_0_matmul_f32_batched(descs, stream_of):
@@ -458,11 +551,45 @@ def q8_0_matmul_f32_step(descs, ws, stream_of=None):
 def q8_0_matmul_blocksums(w, x, n, k, m):
     _need(w, torch.uint8, "w")
     _need(x, torch.uint8, "x")
+    _one_device(w, x)
+    _fit(w, n * (k // QK) * BLOCK_BYTES, "w")
+    _fit(x, m * (k // QK) * BLOCK_BYTES, "x")
     y = torch.empty((m, n), dtype=torch.float32, device=w.device)
     s = torch.empty((m, n, k // QK), dtype=torch.int32, device=w.device)
     _check("q8_0_matmul_blocksums", _lib.q8_0_matmul_blocksums(
         _ptr(w), _ptr(x), _ptr(y), _ptr(s), n, k, m, _stream(w)))
     return y, s
+
+
+def _ids_shape(ids):
+    if ids.dim() != 2:
+        raise ValueError(f"ids: expected [n_tok][n_used], got shape {tuple(ids.shape)}")
+    return int(ids.shape[0]), int(ids.shape[1])
+
+
+def _check_up_gate(w, x, ids, h, n_tok, n_used, n_embd, n_ff, n_expert, r8=False):
+    """Extents of one expert-FFN up_gate layer (native rows, or R8 with r8=True)."""
+    _one_device(w, x, ids, h)
+    if tuple(ids.shape) != (n_tok, n_used):
+        raise ValueError(f"ids: shape {tuple(ids.shape)}, expected {(n_tok, n_used)}")
+    rows = n_expert * 2 * n_ff
+    _fit(w, _r8_bytes_py(rows, n_embd) if r8 else rows * (n_embd // QK) * BLOCK_BYTES,
+         "w_up_gate_r8" if r8 else "w_up_gate")
+    _fit(x, n_tok * n_embd * 4, "x")
+    _fit(h, n_tok * n_used * n_ff * 4, "h")
+
+
+def _check_down(w, h, ids, cw, out, n_tok, n_used, n_ff, n_embd, n_expert, r8=False):
+    """Extents of one expert-FFN down + combine layer."""
+    _one_device(w, h, ids, cw, out)
+    if tuple(ids.shape) != (n_tok, n_used):
+        raise ValueError(f"ids: shape {tuple(ids.shape)}, expected {(n_tok, n_used)}")
+    rows = n_expert * n_embd
+    _fit(w, _r8_bytes_py(rows, n_ff) if r8 else rows * (n_ff // QK) * BLOCK_BYTES,
+         "w_down_r8" if r8 else "w_down")
+    _fit(h, n_tok * n_used * n_ff * 4, "h")
+    _fit(cw, n_tok * n_used * 4, "cw")
+    _fit(out, n_tok * n_embd * 4, "out")
 
 
 def moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used):
@@ -483,10 +610,12 @@ def moe_up_gate_swiglu(w_up_gate, x, ids, n_embd, n_ff, n_expert, ws, h=None):
     _need(x, torch.float32, "x")
     _need(ids, torch.int32, "ids")
     _need(ws, torch.uint8, "ws")
-    n_tok, n_used = ids.shape
+    n_tok, n_used = _ids_shape(ids)
     if h is None:
         h = torch.empty((n_tok, n_used, n_ff), dtype=torch.float32, device=ids.device)
     _need(h, torch.float32, "h")
+    _check_up_gate(w_up_gate, x, ids, h, n_tok, n_used, n_embd, n_ff, n_expert)
+    _one_device(ids, ws)
     _check("moe_up_gate_swiglu", _lib.moe_up_gate_swiglu(
         _ptr(w_up_gate), _ptr(x), _ptr(ids), _ptr(h), n_tok, n_embd, n_ff, n_expert, n_used,
         _ptr(ws), ws.numel(), _stream(ids)))
@@ -500,10 +629,12 @@ def moe_down_combine(w_down, h, ids, cw, n_ff, n_embd, n_expert, ws, out=None):
     _need(ids, torch.int32, "ids")
     _need(cw, torch.float32, "cw")
     _need(ws, torch.uint8, "ws")
-    n_tok, n_used = ids.shape
+    n_tok, n_used = _ids_shape(ids)
     if out is None:
         out = torch.empty((n_tok, n_embd), dtype=torch.float32, device=ids.device)
     _need(out, torch.float32, "out")
+    _check_down(w_down, h, ids, cw, out, n_tok, n_used, n_ff, n_embd, n_expert)
+    _one_device(ids, ws)
     _check("moe_down_combine", _lib.moe_down_combine(
         _ptr(w_down), _ptr(h), _ptr(ids), _ptr(cw), _ptr(out), n_tok, n_ff, n_embd, n_expert,
         n_used, _ptr(ws), ws.numel(), _stream(ids)))
@@ -521,7 +652,11 @@ def moe_up_gate_swiglu_batched(layers, n_embd, n_ff, n_expert):
         _need(d["ids"], torch.int32, "ids")
         _need(d["h"], torch.float32, "h")
         _need(d["ws"], torch.uint8, "ws")
-    n_tok, n_used = layers[0]["ids"].shape
+    n_tok, n_used = _ids_shape(layers[0]["ids"])
+    for d in layers:
+        _check_up_gate(d["w_up_gate"], d["x"], d["ids"], d["h"], n_tok, n_used, n_embd, n_ff,
+                       n_expert)
+        _one_device(layers[0]["ids"], d["ids"], d["ws"])
     arr = (MoeUpGateDesc * len(layers))(*[
         MoeUpGateDesc(_ptr(d["w_up_gate"]), _ptr(d["x"]), _ptr(d["ids"]), _ptr(d["h"]),
                       _ptr(d["ws"]), d["ws"].numel()) for d in layers])
@@ -542,7 +677,11 @@ def moe_down_combine_batched(layers, n_ff, n_embd, n_expert):
         _need(d["cw"], torch.float32, "cw")
         _need(d["out"], torch.float32, "out")
         _need(d["ws"], torch.uint8, "ws")
-    n_tok, n_used = layers[0]["ids"].shape
+    n_tok, n_used = _ids_shape(layers[0]["ids"])
+    for d in layers:
+        _check_down(d["w_down"], d["h"], d["ids"], d["cw"], d["out"], n_tok, n_used, n_ff, n_embd,
+                    n_expert)
+        _one_device(layers[0]["ids"], d["ids"], d["ws"])
     arr = (MoeDownDesc * len(layers))(*[
         MoeDownDesc(_ptr(d["w_down"]), _ptr(d["h"]), _ptr(d["ids"]), _ptr(d["cw"]), _ptr(d["out"]),
                     _ptr(d["ws"]), d["ws"].numel()) for d in layers])
@@ -553,7 +692,9 @@ def moe_down_combine_batched(layers, n_ff, n_embd, n_expert):
 
 def moe_route(ids, n_expert, ws):
     _need(ids, torch.int32, "ids")
-    n_tok, n_used = ids.shape
+    _need(ws, torch.uint8, "ws")
+    _one_device(ids, ws)
+    n_tok, n_used = _ids_shape(ids)
     dev = ids.device
     counts = torch.empty(n_expert, dtype=torch.int32, device=dev)
     offsets = torch.empty(n_expert + 1, dtype=torch.int32, device=dev)
@@ -566,6 +707,9 @@ def moe_route(ids, n_expert, ws):
 
 def q8_read_probe(buf, sink):
     """Stream-read the bytes of `buf` (a GPU tensor); sink: int32 GPU tensor."""
+    _need(sink, torch.int32, "sink")
+    _fit(buf, 0, "buf")
+    _one_device(buf, sink)
     _check("q8_read_probe", _lib.q8_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
                                                _ptr(sink), sink.numel(), _stream(buf)))
 
@@ -593,7 +737,13 @@ def moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert):
         _need(d["h"], torch.float32, "h")
         _need(d["out"], torch.float32, "out")
         _need(d["ws"], torch.uint8, "ws")
-    n_tok, n_used = layers[0]["ids"].shape
+    n_tok, n_used = _ids_shape(layers[0]["ids"])
+    for d in layers:
+        _check_up_gate(d["w_up_gate_r8"], d["x"], d["ids"], d["h"], n_tok, n_used, n_embd, n_ff,
+                       n_expert, r8=True)
+        _check_down(d["w_down_r8"], d["h"], d["ids"], d["cw"], d["out"], n_tok, n_used, n_ff,
+                    n_embd, n_expert, r8=True)
+        _one_device(layers[0]["ids"], d["ids"], d["ws"])
     arr = (MoeR8FfnDesc * len(layers))(*[
         MoeR8FfnDesc(_ptr(d["w_up_gate_r8"]), _ptr(d["w_down_r8"]), _ptr(d["x"]), _ptr(d["ids"]),
                      _ptr(d["cw"]), _ptr(d["h"]), _ptr(d["out"]), _ptr(d["ws"]), d["ws"].numel())

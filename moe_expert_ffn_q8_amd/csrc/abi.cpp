@@ -596,21 +596,25 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
     // more than 16 tokens: h rows are read back with 16-byte loads
     const uintptr_t h_align =
         q8::moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used) ? 16 : 4;
-    q8::MoeR8Layer l[4096 / 64];
+    // every descriptor is checked before the first launch
+    for (int64_t i = 0; i < n_desc; ++i) {
+        const moe_r8_ffn_desc &d = descs[i];
+        if (!d.ws) return Q8_E_WORKSPACE;
+        if (d.ws_bytes < need) return Q8_E_WORKSPACE;
+        if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
+        if (n_tok > 0 && (!d.w_up_gate_r8 || !d.w_down_r8 || !d.x || !d.ids || !d.cw || !d.h ||
+                          !d.out))
+            return Q8_E_NULL;
+        if (!aligned(d.w_up_gate_r8, 16) || !aligned(d.w_down_r8, 16) || !aligned(d.x, 16) ||
+            !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, h_align) || !aligned(d.out, 4))
+            return Q8_E_ALIGN;
+    }
+    if (int rc = q8::moe_r8_ffn_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    q8::MoeR8Layer l[64];
     for (int64_t i0 = 0; i0 < n_desc; i0 += 64) {
         const int nl = (int)std::min<int64_t>(64, n_desc - i0);
         for (int i = 0; i < nl; ++i) {
             const moe_r8_ffn_desc &d = descs[i0 + i];
-            if (!d.ws) return Q8_E_WORKSPACE;
-            if (d.ws_bytes < need) return Q8_E_WORKSPACE;
-            if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
-            if (n_tok > 0 && (!d.w_up_gate_r8 || !d.w_down_r8 || !d.x || !d.ids || !d.cw ||
-                              !d.h || !d.out))
-                return Q8_E_NULL;
-            if (!aligned(d.w_up_gate_r8, 16) || !aligned(d.w_down_r8, 16) || !aligned(d.x, 16) ||
-                !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, h_align) ||
-                !aligned(d.out, 4))
-                return Q8_E_ALIGN;
             l[i] = {d.w_up_gate_r8, d.w_down_r8, d.x, d.ids, d.cw, d.h, d.out, d.ws};
         }
         if (int rc = hip_status(q8::launch_moe_r8_ffn(l, nl, n_tok, n_embd, n_ff, n_expert, n_used,

@@ -650,6 +650,17 @@ bool moe_prefill_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_exper
     return ug_expert < lim && dn_expert < lim && xq < lim && hq < lim && n_expert <= kMoeMaxExperts;
 }
 
+int moe_prefill_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                      int64_t n_used)
+{
+    // the launch-shape limit of the two grouped products (checked again at
+    // each launch; here before the call enqueues anything)
+    const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
+    const int64_t ug = L.max_tiles * ((n_ff + pg_cols<true>() - 1) / pg_cols<true>());
+    const int64_t dn = L.max_tiles * ((n_embd + pg_cols<false>() - 1) / pg_cols<false>());
+    return (ug + 7 > 0x7fffffffLL || dn + 7 > 0x7fffffffLL) ? -4 : 0;
+}
+
 size_t moe_prefill_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                             int64_t n_used)
 {

@@ -432,6 +432,20 @@ size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_ex
     return 256 + (hq + 255) / 256 * 256;
 }
 
+int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                     int64_t n_used)
+{
+    if (n_tok == 0) return 0;
+    if (moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used))
+        return moe_prefill_check(n_tok, n_embd, n_ff, n_expert, n_used);
+    const size_t ug_lds = (size_t)(34 * (n_embd / 32) + 15) / 16 * 16 + 64 * 4;
+    const size_t dn_lds = (size_t)16 * ((34 * (n_ff / 32) + 15) / 16 * 16) + 16 * 8 * kDnG * 4;
+    if (ug_lds > (size_t)max_lds_bytes() || dn_lds > (size_t)max_lds_bytes()) return -4;
+    const int64_t ug_wgs = kMoeMaxLayers * n_tok * n_used * (n_ff / 32);
+    const int64_t dn_wgs = kMoeMaxLayers * n_tok * (n_embd / (8 * kDnG));
+    return (ug_wgs > 0x7fffffffLL || dn_wgs > 0x7fffffffLL) ? -4 : 0;
+}
+
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream)
 {
@@ -465,7 +479,7 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
         ug.wg_per_layer = (int)(n_tok * n_used * (n_ff / 32));
         const int64_t nb = n_embd / 32;
         const size_t ug_lds = (size_t)(34 * nb + 15) / 16 * 16 + 64 * 4;
-        if (ug_lds > (size_t)max_lds_bytes()) return -4;
+        if (ug_lds > (size_t)max_lds_bytes()) return -4;   // also checked by moe_r8_ffn_check
         // cache policy of the weight loads: at one token every slot names a
         // different expert and nothing is read twice (non-temporal loads);
         // with several tokens slots repeat experts, and the default policy

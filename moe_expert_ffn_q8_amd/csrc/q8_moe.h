@@ -65,6 +65,9 @@ int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, 
 bool moe_prefill_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
 size_t moe_prefill_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                             int64_t n_used);
+// The launch-shape limits of the prefill path's launches: 0 or -4 (unsupported).
+int moe_prefill_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                      int64_t n_used);
 int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *ids, float *h,
                                void *ws, int64_t n_tok, int64_t n_embd, int64_t n_ff,
                                int64_t n_expert, int64_t n_used, hipStream_t stream);
@@ -97,6 +100,9 @@ int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float 
                           const int32_t *ids, const float *cw, float *h, float *out, void *ws,
                           int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                           int64_t n_used, hipStream_t stream);
+// The launch-shape limits of launch_moe_r8_ffn for this shape: 0 or -4.
+int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                     int64_t n_used);
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream);
 

@@ -731,8 +731,13 @@ static int launch_fast(const StreamDesc *d, int n, hipStream_t stream)
 
 int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
 {
+    // Every limit is checked before anything is enqueued: the generic
+    // descriptors' grid limits first, then the fast launch (whose own checks
+    // precede its launch), and only then the generic launches, so a rejected
+    // call has enqueued nothing.
     StreamDesc fast[kStreamMaxJobs];
-    int nf = 0;
+    int generic[kStreamMaxJobs];
+    int nf = 0, ng = 0;
     for (int i = 0; i < n; ++i) {
         if (d[i].n == 0 || d[i].m == 0 || d[i].batch == 0) continue;
         if (stream_fast_ok(d[i])) {
@@ -741,19 +746,27 @@ int launch_stream(const StreamDesc *d, int n, hipStream_t stream)
             return -4;                 // checked by the caller: fast shapes only
         } else {
             if (d[i].n > 0x7fffffff || d[i].batch > 65535) return -4;
-            hipLaunchKernelGGL(stream_generic_kernel, dim3((unsigned)d[i].n, (unsigned)d[i].batch),
-                               dim3(kWave), 0, stream, d[i]);
-            if (hipGetLastError() != hipSuccess) return -6;
+            generic[ng++] = i;
         }
     }
-    if (nf == 0) return 0;
-    int mmax = 1;
-    for (int i = 0; i < nf; ++i)
-        if (fast[i].m > mmax) mmax = (int)fast[i].m;
-    if (mmax <= 2) return launch_flat(fast, nf, stream);
-    if (small_m_ok(fast, nf)) return launch_small_m(fast, nf, stream);
-    if (fast[0].x_f32) return -4;      // fp32 activations: matrix-core engine only
-    return launch_fast(fast, nf, stream);
+    if (nf > 0) {
+        int mmax = 1;
+        for (int i = 0; i < nf; ++i)
+            if (fast[i].m > mmax) mmax = (int)fast[i].m;
+        int rc;
+        if (mmax <= 2) rc = launch_flat(fast, nf, stream);
+        else if (small_m_ok(fast, nf)) rc = launch_small_m(fast, nf, stream);
+        else if (fast[0].x_f32) rc = -4;      // fp32 activations: matrix-core engine only
+        else rc = launch_fast(fast, nf, stream);
+        if (rc) return rc;
+    }
+    for (int g = 0; g < ng; ++g) {
+        const StreamDesc &s = d[generic[g]];
+        hipLaunchKernelGGL(stream_generic_kernel, dim3((unsigned)s.n, (unsigned)s.batch),
+                           dim3(kWave), 0, stream, s);
+        if (hipGetLastError() != hipSuccess) return -6;
+    }
+    return 0;
 }
 
 }  // namespace q8

@@ -194,5 +194,21 @@ def test_moe_r8_ffn_workspace_reuse(q, orc):
         if i == 3:
             assert q.moe_error_word(ws) == 1
             assert bool(torch.isnan(d["out"][7]).all())
+            assert bool(torch.isnan(d["h"][7, 2]).all())
+            # every other result of the call is intact: the valid tokens' h
+            # and out, and token 7's h rows of its valid slots
+            sel = np.array([t for t in range(n_tok) if t != 7])
+            h = d["h"].cpu().numpy()
+            h_ref = orc.moe_up_gate_swiglu(c["w_ug"], c["xq"][sel], c["ids"][sel], n_embd, n_ff,
+                                           n_expert)
+            assert_rows_close(h[sel].reshape(-1, n_ff), h_ref.reshape(-1, n_ff))
+            ok = [0, 1, 3]
+            h7 = orc.moe_up_gate_swiglu(c["w_ug"], c["xq"][7:8],
+                                        np.ascontiguousarray(c["ids"][7:8, ok]), n_embd, n_ff,
+                                        n_expert)
+            assert_rows_close(h[7, ok], h7.reshape(-1, n_ff))
+            out_ref = orc.moe_down_combine(c["w_d"], h[sel], c["ids"][sel], c["cw"][sel], n_ff,
+                                           n_embd, n_expert)
+            assert_rows_close(d["out"].cpu().numpy()[sel], out_ref)
             continue
         _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
