@@ -99,10 +99,13 @@ def test_r8_full_size_vocab(q, orc):
 
 
 def test_r8_limits(q):
+    """k above 32768 is refused by the library (its LDS staging limit); the
+    call goes through the C ABI directly, since the binding would already
+    refuse the undersized tensors."""
     import torch
     w = torch.zeros(64, dtype=torch.uint8, device="cuda")
-    with pytest.raises(q.Q8Error):
-        q.q8_0_matvec_r8(w, w, 1, 32768 + 32)
+    p = w.data_ptr()
+    assert q.raw.q8_0_matvec_r8(p, p, p, 1, 32768 + 32, None) == -4
 
 
 def test_r8_batched_step(q, orc):
