@@ -527,6 +527,27 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
                        int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
                        void *stream);
 
+/* moe_r8_ffn_batched_noalloc -- moe_r8_ffn_batched for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels, h and out bit for bit,
+ * with the workspaces taken from an array the library holds on each device
+ * (8 MiB per device, held until the process ends; looked up once per device
+ * at the first call on it, which is the only call that can return Q8_E_HIP
+ * for that lookup).  The call allocates and frees nothing.
+ *   descs  as for moe_r8_ffn_batched; ws and ws_bytes are ignored.
+ * Decode shapes only: n_tok <= 16 (more tokens: Q8_E_UNSUPPORTED).  Layer i
+ * uses the i-th slice of moe_r8_workspace_bytes(...) rounded up to 256 bytes;
+ * n_desc slices beyond 8 MiB: Q8_E_WORKSPACE (split the call).  Every call on
+ * a device shares that device's array and leaves its contents behind: two
+ * calls that may run at the same time on one device race (order them on one
+ * stream).  Nothing in the array needs clearing: every call rewrites what it
+ * reads.  The error word of the workspace is not visible to the caller; an
+ * out-of-range id shows as NaN h rows for its slot and NaN output rows for
+ * its token, as in moe_r8_ffn_batched. */
+int moe_r8_ffn_batched_noalloc(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                               int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                               void *stream);
+
 /* ---------------------------------------------------------------------------
  * Validation exports (same kernels, with an extra output), for testing.
  *

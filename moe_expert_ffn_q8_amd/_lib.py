@@ -125,6 +125,8 @@ _SIGS = {
     "moe_r8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
     "moe_r8_ffn_batched": (_int, [ctypes.POINTER(MoeR8FfnDesc), _i64, _i64, _i64, _i64, _i64,
                                   _i64, _vp]),
+    "moe_r8_ffn_batched_noalloc": (_int, [ctypes.POINTER(MoeR8FfnDesc), _i64, _i64, _i64, _i64,
+                                          _i64, _i64, _vp]),
     "kq_matvec_batched": (_int, [_int, ctypes.POINTER(KqMatvecDesc), _i64, _vp]),
     "q4_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "q5_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
@@ -721,13 +723,7 @@ def moe_r8_workspace(n_tok, n_embd, n_ff, n_expert, n_used, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert):
-    """The expert FFN over R8 expert weights for independent layers of one
-    shape (decode kernels up to 16 tokens, the grouped matrix-core path above).
-    layers: list of dicts with w_up_gate_r8, w_down_r8, x, ids, cw, h
-    (written), out (written), ws."""
-    if not layers:
-        return
+def _r8_ffn_descs(layers, n_embd, n_ff, n_expert, with_ws):
     for d in layers:
         _need(d["w_up_gate_r8"], torch.uint8, "w_up_gate_r8")
         _need(d["w_down_r8"], torch.uint8, "w_down_r8")
@@ -736,19 +732,43 @@ def moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert):
         _need(d["cw"], torch.float32, "cw")
         _need(d["h"], torch.float32, "h")
         _need(d["out"], torch.float32, "out")
-        _need(d["ws"], torch.uint8, "ws")
+        if with_ws:
+            _need(d["ws"], torch.uint8, "ws")
     n_tok, n_used = _ids_shape(layers[0]["ids"])
     for d in layers:
         _check_up_gate(d["w_up_gate_r8"], d["x"], d["ids"], d["h"], n_tok, n_used, n_embd, n_ff,
                        n_expert, r8=True)
         _check_down(d["w_down_r8"], d["h"], d["ids"], d["cw"], d["out"], n_tok, n_used, n_ff,
                     n_embd, n_expert, r8=True)
-        _one_device(layers[0]["ids"], d["ids"], d["ws"])
+        _one_device(layers[0]["ids"], d["ids"], d["ws"] if with_ws else None)
     arr = (MoeR8FfnDesc * len(layers))(*[
         MoeR8FfnDesc(_ptr(d["w_up_gate_r8"]), _ptr(d["w_down_r8"]), _ptr(d["x"]), _ptr(d["ids"]),
-                     _ptr(d["cw"]), _ptr(d["h"]), _ptr(d["out"]), _ptr(d["ws"]), d["ws"].numel())
+                     _ptr(d["cw"]), _ptr(d["h"]), _ptr(d["out"]),
+                     _ptr(d["ws"]) if with_ws else None, d["ws"].numel() if with_ws else 0)
         for d in layers])
+    return arr, n_tok, n_used
+
+
+def moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert):
+    """The expert FFN over R8 expert weights for independent layers of one
+    shape (decode kernels up to 16 tokens, the grouped matrix-core path above).
+    layers: list of dicts with w_up_gate_r8, w_down_r8, x, ids, cw, h
+    (written), out (written), ws."""
+    if not layers:
+        return
+    arr, n_tok, n_used = _r8_ffn_descs(layers, n_embd, n_ff, n_expert, True)
     _check("moe_r8_ffn_batched", _lib.moe_r8_ffn_batched(
+        arr, len(layers), n_tok, n_embd, n_ff, n_expert, n_used, _stream(layers[0]["ids"])))
+
+
+def moe_r8_ffn_batched_noalloc(layers, n_embd, n_ff, n_expert):
+    """moe_r8_ffn_batched without a caller workspace (the library's own
+    per-device array; decode shapes, up to 16 tokens).  layers: dicts as for
+    moe_r8_ffn_batched; a "ws" entry, if present, is ignored."""
+    if not layers:
+        return
+    arr, n_tok, n_used = _r8_ffn_descs(layers, n_embd, n_ff, n_expert, False)
+    _check("moe_r8_ffn_batched_noalloc", _lib.moe_r8_ffn_batched_noalloc(
         arr, len(layers), n_tok, n_embd, n_ff, n_expert, n_used, _stream(layers[0]["ids"])))
 
 

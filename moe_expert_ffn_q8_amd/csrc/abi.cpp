@@ -582,9 +582,14 @@ size_t moe_r8_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64
     return q8::moe_r8_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
 }
 
-int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
-                       int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
-                       void *stream)
+}  // extern "C"
+
+// Checks shared by moe_r8_ffn_batched and its no-alloc variant: the shape,
+// every descriptor (its workspace too when with_ws) and the launch-shape
+// limits, before anything is enqueued.
+static int r8_ffn_checks(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                         int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                         bool with_ws)
 {
     if (n_desc < 0 || n_tok < 0 || n_expert <= 0 || n_used <= 0) return Q8_E_SHAPE;
     if (check_k(n_embd) || check_k(n_ff)) return Q8_E_SHAPE;
@@ -596,12 +601,13 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
     // more than 16 tokens: h rows are read back with 16-byte loads
     const uintptr_t h_align =
         q8::moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used) ? 16 : 4;
-    // every descriptor is checked before the first launch
     for (int64_t i = 0; i < n_desc; ++i) {
         const moe_r8_ffn_desc &d = descs[i];
-        if (!d.ws) return Q8_E_WORKSPACE;
-        if (d.ws_bytes < need) return Q8_E_WORKSPACE;
-        if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
+        if (with_ws) {
+            if (!d.ws) return Q8_E_WORKSPACE;
+            if (d.ws_bytes < need) return Q8_E_WORKSPACE;
+            if (!aligned(d.ws, 256)) return Q8_E_ALIGN;
+        }
         if (n_tok > 0 && (!d.w_up_gate_r8 || !d.w_down_r8 || !d.x || !d.ids || !d.cw || !d.h ||
                           !d.out))
             return Q8_E_NULL;
@@ -609,19 +615,58 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
             !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, h_align) || !aligned(d.out, 4))
             return Q8_E_ALIGN;
     }
-    if (int rc = q8::moe_r8_ffn_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    return q8::moe_r8_ffn_check(n_tok, n_embd, n_ff, n_expert, n_used);
+}
+
+// Launches in groups of 64 layers; layer i's workspace is ws_of(i).
+template <class WsOf>
+static int r8_ffn_launch(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                         int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                         WsOf ws_of, void *stream)
+{
     q8::MoeR8Layer l[64];
     for (int64_t i0 = 0; i0 < n_desc; i0 += 64) {
         const int nl = (int)std::min<int64_t>(64, n_desc - i0);
         for (int i = 0; i < nl; ++i) {
             const moe_r8_ffn_desc &d = descs[i0 + i];
-            l[i] = {d.w_up_gate_r8, d.w_down_r8, d.x, d.ids, d.cw, d.h, d.out, d.ws};
+            l[i] = {d.w_up_gate_r8, d.w_down_r8, d.x, d.ids, d.cw, d.h, d.out, ws_of(i0 + i)};
         }
         if (int rc = hip_status(q8::launch_moe_r8_ffn(l, nl, n_tok, n_embd, n_ff, n_expert, n_used,
                                                       as_stream(stream))))
             return rc;
     }
     return Q8_OK;
+}
+
+extern "C" {
+
+int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                       int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                       void *stream)
+{
+    if (int rc = r8_ffn_checks(descs, n_desc, n_tok, n_embd, n_ff, n_expert, n_used, true))
+        return rc;
+    if (n_desc == 0) return Q8_OK;
+    return r8_ffn_launch(descs, n_desc, n_tok, n_embd, n_ff, n_expert, n_used,
+                         [&](int64_t i) { return descs[i].ws; }, stream);
+}
+
+int moe_r8_ffn_batched_noalloc(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,
+                               int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                               void *stream)
+{
+    if (int rc = r8_ffn_checks(descs, n_desc, n_tok, n_embd, n_ff, n_expert, n_used, false))
+        return rc;
+    if (n_desc == 0 || n_tok == 0) return Q8_OK;
+    // decode shapes only: the prefill path's workspace is far larger
+    if (q8::moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used)) return Q8_E_UNSUPPORTED;
+    const size_t per = (q8::moe_r8_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used) + 255) &
+                       ~(size_t)255;
+    if ((uint64_t)n_desc * per > q8::kMoeR8ScratchBytes) return Q8_E_WORKSPACE;
+    uint8_t *base = nullptr;
+    if (q8::moe_r8_scratch(&base)) return Q8_E_HIP;
+    return r8_ffn_launch(descs, n_desc, n_tok, n_embd, n_ff, n_expert, n_used,
+                         [&](int64_t i) { return (void *)(base + i * per); }, stream);
 }
 
 int q8_read_probe(const void *p, int64_t bytes, uint32_t *sink, int64_t sink_words, void *stream)

@@ -30,6 +30,8 @@
 // NaN, and every output row of its token is NaN.
 #include <string.h>
 
+#include <mutex>
+
 #include "q8_device.h"
 #include "q8_internal.h"
 #include "q8_moe.h"
@@ -430,6 +432,30 @@ size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_ex
         return moe_prefill_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
     const size_t hq = (size_t)(n_tok * n_used) * (size_t)(n_ff / 32) * kBlockBytes;
     return 256 + (hq + 255) / 256 * 256;
+}
+
+// The no-alloc entry point's workspace: one array per device for the life of
+// the process.  In host code `moe_r8_scratch_array` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns (one per
+// device, the device current) is passed to kernels.
+static __device__ __align__(256) uint8_t moe_r8_scratch_array[kMoeR8ScratchBytes];
+
+constexpr int kScratchMaxDevices = 64;
+static uint8_t *g_scratch[kScratchMaxDevices];
+static std::mutex g_scratch_mu;
+
+int moe_r8_scratch(uint8_t **base)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return -6;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(moe_r8_scratch_array)) != hipSuccess || !p) return -6;
+        g_scratch[dev] = (uint8_t *)p;
+    }
+    *base = g_scratch[dev];
+    return 0;
 }
 
 int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,

@@ -100,6 +100,13 @@ int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float 
                           const int32_t *ids, const float *cw, float *h, float *out, void *ws,
                           int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                           int64_t n_used, hipStream_t stream);
+// The library's own workspace for callers that cannot allocate
+// (moe_r8_ffn_batched_noalloc): a file-scope device array of
+// kMoeR8ScratchBytes per device.  moe_r8_scratch sets *base to the current
+// device's copy (looked up once per device); 0, or -6 if the lookup fails.
+constexpr size_t kMoeR8ScratchBytes = (size_t)8 << 20;
+int moe_r8_scratch(uint8_t **base);
+
 // The launch-shape limits of launch_moe_r8_ffn for this shape: 0 or -4.
 int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                      int64_t n_used);

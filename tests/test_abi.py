@@ -462,3 +462,32 @@ def test_moe_r8_checks(lib):
     assert call(D(A, A, A, A, A, A + 4, A, WS, pre), n_tok=512) == Q8_E_ALIGN     # h
     assert call(D(A, A, A, A, A, A, A, WS, pre - 1), n_tok=512) == Q8_E_WORKSPACE
     assert call(big, n_tok=8193) == Q8_E_UNSUPPORTED                            # too many tokens
+
+
+def test_moe_r8_noalloc_checks(lib):
+    """The no-alloc variant: the shape and descriptor checks of
+    moe_r8_ffn_batched (its ws fields ignored), decode shapes only, and a
+    clear status when the layers' workspaces exceed the library's 8 MiB
+    array -- all before any HIP call."""
+    import moe_expert_ffn_q8_amd as q
+    f = lib.moe_r8_ffn_batched_noalloc
+    D = q.MoeR8FfnDesc
+
+    def call(ds, n_tok=1, n_embd=2048, n_ff=768, n_expert=128, n_used=8):
+        arr = (D * max(1, len(ds)))(*ds)
+        return f(arr, len(ds), n_tok, n_embd, n_ff, n_expert, n_used, None)
+
+    ok = D(A, A, A, A, A, A, A, None, 0)            # no workspace: ignored
+    assert call([ok], n_ff=4096) == Q8_E_UNSUPPORTED
+    assert call([ok], n_embd=2047) == Q8_E_SHAPE
+    assert call([D(None, A, A, A, A, A, A, None, 0)]) == Q8_E_NULL
+    assert call([D(A, A, A + 4, A, A, A, A, None, 0)]) == Q8_E_ALIGN
+    assert call([ok], n_tok=0) == Q8_OK
+    assert call([]) == Q8_OK
+    assert call([ok], n_tok=17) == Q8_E_UNSUPPORTED   # the prefill path: not in this variant
+    # 16 tokens x 16 slots x n_ff 2048: 557,312 bytes per layer -> 15 layers fit
+    per = (lib.moe_r8_workspace_bytes(16, 2048, 2048, 64, 16) + 255) // 256 * 256
+    assert per == 557312
+    fit = (8 << 20) // per
+    assert call([ok] * (fit + 1), 16, 2048, 2048, 64, 16) == Q8_E_WORKSPACE
+    assert call([ok] * 3 + [D(A, A, A, A, A, None, A, None, 0)], 16, 2048, 2048, 64, 16) == Q8_E_NULL
