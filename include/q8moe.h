@@ -549,15 +549,40 @@ int moe_r8_ffn_batched_noalloc(const moe_r8_ffn_desc *descs, int64_t n_desc, int
                                void *stream);
 
 /* ---------------------------------------------------------------------------
- * Validation exports (same kernels, with an extra output), for testing.
+ * Validation exports, for testing: the kernels of the product path, built
+ * with an extra output (a compile-time flag, so the product path itself is
+ * unchanged), that write the exact int32 block sums s = sum_j qw[j]*qx[j] of
+ * every (token row, weight row, block) they form -- the quantity the block
+ * dot of ggml_vec_dot_q8_0_q8_0 computes ([XEON] section on narrowing down
+ * the cause) -- and, for the expert FFN, the routing and the quantized h rows
+ * they used.  Each takes the arguments of its product call plus the extra
+ * outputs, computes the same fp32 results, and follows the same kernel
+ * selection (so a shape is checked on the kernel the product call runs).
  *
- * q8_0_matmul_blocksums: the per-block int32 sums s[m][n][b] that q8_0_matmul
- * forms for W[n][k], X[m][k] (m <= 16), written to sums (int32 [m][n][k/32]).
- * y receives the usual fp32 result.
+ * q8_0_matmul_blocksums: the sums s[m][n][b] of q8_0_matmul for W[n][k],
+ * X[m][k] (any m: the streaming engines up to 16 rows, the matrix-core
+ * kernel above), written to sums (int32 [m][n][k/32]); y receives the usual
+ * fp32 result.
  */
 int q8_0_matmul_blocksums(const q8_0_block *w, const q8_0_block *x, float *y,
                           int32_t *sums, int64_t n, int64_t k, int64_t m,
                           void *stream);
+
+/* q8v_matvec_r8_batched_blocksums / q8v_matvec_r8_f32_batched_blocksums: the
+ * products of q8_0_matvec_r8_batched / q8_0_matvec_r8_f32_batched (same
+ * descriptors, same kernel) and, for descriptor i, the block sums in sums[i]
+ * (int32 [batch][n][k/32]; sums is a HOST array of n_desc device pointers).
+ * The f32 form's sums are those of the activation row quantized inside the
+ * launch. */
+int q8v_matvec_r8_batched_blocksums(const q8_0_r8_desc *descs, int64_t n_desc,
+                                    int32_t *const *sums, void *stream);
+int q8v_matvec_r8_f32_batched_blocksums(const q8_0_r8_f32_desc *descs, int64_t n_desc,
+                                        int32_t *const *sums, void *stream);
+
+/* q8v_matmul_r8_batched_blocksums: q8_0_matmul_r8_batched with the block sums
+ * of descriptor i in sums[i] (int32 [batch][m][n][k/32]). */
+int q8v_matmul_r8_batched_blocksums(const q8_0_r8_mm_desc *descs, int64_t n_desc,
+                                    int32_t *const *sums, void *stream);
 
 /* moe_route: the grouping of (t,u) slots by expert that the MoE kernels use:
  * counts[e] (int32 [n_expert]), offsets[e] (int32 [n_expert+1], exclusive

@@ -9,7 +9,7 @@ from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDes
                    make_up_gate_desc, q8_0_up_gate_swiglu_batched, moe_down_combine, moe_down_combine_batched,
                    moe_error_word, moe_route, moe_up_gate_swiglu, moe_up_gate_swiglu_batched,
                    moe_workspace, moe_workspace_bytes, q8_0_matmul, q8_0_matmul_batched,
-                   q8_0_matmul_blocksums, q8_0_matmul_f32_batched, q8_0_matmul_f32_step,
+                   q8_0_matmul_blocksums, q8v_matvec_r8_batched_blocksums, q8v_matvec_r8_f32_batched_blocksums, q8v_matmul_r8_batched_blocksums, q8_0_matmul_f32_batched, q8_0_matmul_f32_step,
                    q8_0_matmul_f32_step_workspace, q8_0_matmul_f32_step_ws_bytes, q8_0_matvec,
                    q8_0_matvec_r8, q8_0_matvec_r8_batched, make_r8_desc, Q8R8Desc,
                    q8_0_matvec_r8_f32_batched, make_r8_f32_desc, Q8R8F32Desc,
@@ -22,7 +22,7 @@ __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGate
            "make_up_gate_desc", "q8_0_up_gate_swiglu_batched", "moe_down_combine", "moe_down_combine_batched",
            "moe_error_word", "moe_route", "moe_up_gate_swiglu", "moe_up_gate_swiglu_batched",
            "moe_workspace", "moe_workspace_bytes", "q8_0_matmul", "q8_0_matmul_batched",
-           "q8_0_matmul_blocksums", "q8_0_matmul_f32_batched", "q8_0_matmul_f32_step",
+           "q8_0_matmul_blocksums", "q8v_matvec_r8_batched_blocksums", "q8v_matvec_r8_f32_batched_blocksums", "q8v_matmul_r8_batched_blocksums", "q8_0_matmul_f32_batched", "q8_0_matmul_f32_step",
            "q8_0_matmul_f32_step_workspace", "q8_0_matmul_f32_step_ws_bytes", "q8_0_matvec",
            "q8_0_matvec_r8", "q8_0_matvec_r8_batched", "make_r8_desc", "Q8R8Desc",
            "q8_0_matvec_r8_f32_batched", "make_r8_f32_desc", "Q8R8F32Desc",

@@ -113,6 +113,12 @@ _SIGS = {
     "moe_down_combine_batched": (_int, [ctypes.POINTER(MoeDownDesc), _i64, _i64, _i64, _i64, _i64,
                                         _i64, _vp]),
     "q8_0_matmul_blocksums": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q8v_matvec_r8_batched_blocksums": (_int, [ctypes.POINTER(Q8R8Desc), _i64,
+                                               ctypes.POINTER(_vp), _vp]),
+    "q8v_matvec_r8_f32_batched_blocksums": (_int, [ctypes.POINTER(Q8R8F32Desc), _i64,
+                                                   ctypes.POINTER(_vp), _vp]),
+    "q8v_matmul_r8_batched_blocksums": (_int, [ctypes.POINTER(Q8R8MmDesc), _i64,
+                                               ctypes.POINTER(_vp), _vp]),
     "moe_route": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]),
     "q8_read_probe": (_int, [_vp, _i64, _vp, _i64, _vp]),
     "q8_0_r8_bytes": (_i64, [_i64, _i64]),
@@ -346,6 +352,42 @@ def make_r8_f32_desc(w_r8, x, y, n, k, batch=1, w_batch_stride=0, x_batch_stride
                        _addr(x, 4, _span(batch, x_batch_stride, 1, 0, k) * 4 if n > 0 else 0, "x"),
                        _addr(y, 4, _span(batch, y_batch_stride, 1, 0, n) * 4, "y"), n, k, batch,
                        w_batch_stride, x_batch_stride, y_batch_stride)
+
+
+def _sum_ptrs(sums):
+    for i, t in enumerate(sums):
+        _need(t, torch.int32, f"sums[{i}]")
+    return (_vp * max(1, len(sums)))(*[t.data_ptr() for t in sums])
+
+
+def q8v_matvec_r8_batched_blocksums(descs, sums, stream_of):
+    """q8_0_matvec_r8_batched plus the int32 block sums of descriptor i in
+    sums[i] (a GPU int32 tensor of batch*n*(k/32) elements)."""
+    for d, t in zip(descs, sums):
+        _fit(t, max(d.batch, 0) * max(d.n, 0) * (d.k // QK) * 4, "sums")
+    arr = (Q8R8Desc * max(1, len(descs)))(*descs)
+    _check("q8v_matvec_r8_batched_blocksums", _lib.q8v_matvec_r8_batched_blocksums(
+        arr, len(descs), _sum_ptrs(sums), _stream(stream_of)))
+
+
+def q8v_matvec_r8_f32_batched_blocksums(descs, sums, stream_of):
+    """q8_0_matvec_r8_f32_batched plus the int32 block sums of descriptor i in
+    sums[i] (batch*n*(k/32) elements)."""
+    for d, t in zip(descs, sums):
+        _fit(t, max(d.batch, 0) * max(d.n, 0) * (d.k // QK) * 4, "sums")
+    arr = (Q8R8F32Desc * max(1, len(descs)))(*descs)
+    _check("q8v_matvec_r8_f32_batched_blocksums", _lib.q8v_matvec_r8_f32_batched_blocksums(
+        arr, len(descs), _sum_ptrs(sums), _stream(stream_of)))
+
+
+def q8v_matmul_r8_batched_blocksums(descs, sums, stream_of):
+    """q8_0_matmul_r8_batched plus the int32 block sums of descriptor i in
+    sums[i] (batch*m*n*(k/32) elements)."""
+    for d, t in zip(descs, sums):
+        _fit(t, max(d.batch, 0) * max(d.m, 0) * max(d.n, 0) * (d.k // QK) * 4, "sums")
+    arr = (Q8R8MmDesc * max(1, len(descs)))(*descs)
+    _check("q8v_matmul_r8_batched_blocksums", _lib.q8v_matmul_r8_batched_blocksums(
+        arr, len(descs), _sum_ptrs(sums), _stream(stream_of)))
 
 
 def q8_0_matvec_r8_f32_batched(descs, stream_of):

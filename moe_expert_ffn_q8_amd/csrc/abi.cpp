@@ -29,6 +29,15 @@ int check_k(int64_t k)
     return Q8_OK;
 }
 
+// validation calls: every descriptor needs its block-sum array
+bool sums_required(int32_t *const *sums, int64_t n_desc)
+{
+    if (!sums) return false;
+    for (int64_t i = 0; i < n_desc; ++i)
+        if (!sums[i]) return true;
+    return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,10 +80,9 @@ static int matmul_impl(const q8_0_block *w, const q8_0_block *x, float *y, int32
         return Q8_E_ALIGN;
     const int64_t nb = k / kQK;
     // many token rows: the matrix-core kernel (weights read once per 128 rows)
-    if (!sums && m > q8::kStreamMaxM && aligned(w, 16) && aligned(x, 16) &&
-        q8::gemm_ok(n, nb, m))
+    if (m > q8::kStreamMaxM && aligned(w, 16) && aligned(x, 16) && q8::gemm_ok(n, nb, m))
         return hip_status(q8::launch_gemm((const uint8_t *)w, (const uint8_t *)x, y, n, nb, m, n,
-                                          as_stream(stream)));
+                                          as_stream(stream), sums));
     for (int64_t m0 = 0; m0 < m; m0 += q8::kStreamMaxM) {
         const int64_t mc = (m - m0) < q8::kStreamMaxM ? (m - m0) : q8::kStreamMaxM;
         q8::StreamDesc d;
@@ -109,7 +117,6 @@ int q8_0_matmul_blocksums(const q8_0_block *w, const q8_0_block *x, float *y, in
                           int64_t n, int64_t k, int64_t m, void *stream)
 {
     if (!sums && n > 0 && m > 0) return Q8_E_NULL;
-    if (m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
     return matmul_impl(w, x, y, sums, n, k, m, stream);
 }
 
@@ -410,7 +417,7 @@ int q8_0_repack_r8(const q8_0_block *w, void *w_r8, int64_t n, int64_t k, void *
 static int r8_launch(const void *const *w, const void *const *x, float *const *y,
                      const int64_t *n, const int64_t *k, const int64_t *batch, const int64_t *ws,
                      const int64_t *xs, const int64_t *ys, int64_t n_desc, bool x_f32,
-                     void *stream)
+                     int32_t *const *sums, void *stream)
 {
     q8::R8Desc d[q8::kStreamMaxJobs];
     int nd = 0;
@@ -418,10 +425,11 @@ static int r8_launch(const void *const *w, const void *const *x, float *const *y
         if (int rc = check_k(k[i])) return rc;
         if (n[i] < 0 || batch[i] < 0) return Q8_E_SHAPE;
         if (n[i] == 0 || batch[i] == 0) continue;
-        if (!w[i] || !x[i] || !y[i]) return Q8_E_NULL;
+        if (!w[i] || !x[i] || !y[i] || (sums && !sums[i])) return Q8_E_NULL;
         const int64_t nb = k[i] / kQK;
         if (batch[i] > 1 && (ws[i] < q8::r8_bytes(n[i], nb) || xs[i] < 0 || ys[i] < n[i]))
             return Q8_E_SHAPE;
+        if (sums && !aligned(sums[i], 4)) return Q8_E_ALIGN;
         if (!aligned(w[i], 16) || !aligned(x[i], x_f32 ? 16 : 2) || !aligned(y[i], 4) ||
             (batch[i] > 1 && (ws[i] % 16 != 0 || (x_f32 && xs[i] % 4 != 0))))
             return Q8_E_ALIGN;
@@ -434,18 +442,21 @@ static int r8_launch(const void *const *w, const void *const *x, float *const *y
         o.w_bstride = batch[i] > 1 ? ws[i] : 0;
         o.x_bstride = batch[i] > 1 ? xs[i] * (x_f32 ? 4 : kBB) : 0;
         o.y_bstride = batch[i] > 1 ? ys[i] : 0;
+        o.sums = sums ? sums[i] : nullptr;
     }
     if (nd == 0) return Q8_OK;
     return hip_status(q8::launch_r8_matvec(d, nd, x_f32, as_stream(stream)));
 }
 
 template <class Desc>
-static int r8_batched(const Desc *descs, int64_t n_desc, bool x_f32, void *stream)
+static int r8_batched(const Desc *descs, int64_t n_desc, bool x_f32, int32_t *const *sums,
+                      void *stream)
 {
     if (n_desc < 0) return Q8_E_SHAPE;
     if (n_desc == 0) return Q8_OK;
     if (!descs) return Q8_E_NULL;
     if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    if (sums_required(sums, n_desc)) return Q8_E_NULL;
     const void *w[q8::kStreamMaxJobs], *x[q8::kStreamMaxJobs];
     float *y[q8::kStreamMaxJobs];
     int64_t n[q8::kStreamMaxJobs], k[q8::kStreamMaxJobs], b[q8::kStreamMaxJobs];
@@ -456,27 +467,45 @@ static int r8_batched(const Desc *descs, int64_t n_desc, bool x_f32, void *strea
         ws[i] = descs[i].w_batch_stride; xs[i] = descs[i].x_batch_stride;
         ys[i] = descs[i].y_batch_stride;
     }
-    return r8_launch(w, x, y, n, k, b, ws, xs, ys, n_desc, x_f32, stream);
+    return r8_launch(w, x, y, n, k, b, ws, xs, ys, n_desc, x_f32, sums, stream);
 }
 
 extern "C" {
 
 int q8_0_matvec_r8_batched(const q8_0_r8_desc *descs, int64_t n_desc, void *stream)
 {
-    return r8_batched(descs, n_desc, false, stream);
+    return r8_batched(descs, n_desc, false, nullptr, stream);
 }
 
 int q8_0_matvec_r8_f32_batched(const q8_0_r8_f32_desc *descs, int64_t n_desc, void *stream)
 {
-    return r8_batched(descs, n_desc, true, stream);
+    return r8_batched(descs, n_desc, true, nullptr, stream);
 }
 
-int q8_0_matmul_r8_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, void *stream)
+int q8v_matvec_r8_batched_blocksums(const q8_0_r8_desc *descs, int64_t n_desc,
+                                    int32_t *const *sums, void *stream)
+{
+    if (n_desc > 0 && !sums) return Q8_E_NULL;
+    return r8_batched(descs, n_desc, false, sums, stream);
+}
+
+int q8v_matvec_r8_f32_batched_blocksums(const q8_0_r8_f32_desc *descs, int64_t n_desc,
+                                        int32_t *const *sums, void *stream)
+{
+    if (n_desc > 0 && !sums) return Q8_E_NULL;
+    return r8_batched(descs, n_desc, true, sums, stream);
+}
+
+}  // extern "C"
+
+static int r8_mm_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, int32_t *const *sums,
+                         void *stream)
 {
     if (n_desc < 0) return Q8_E_SHAPE;
     if (n_desc == 0) return Q8_OK;
     if (!descs) return Q8_E_NULL;
     if (n_desc > q8::kStreamMaxJobs) return Q8_E_UNSUPPORTED;
+    if (sums_required(sums, n_desc)) return Q8_E_NULL;
     q8::R8MmDesc d[q8::kStreamMaxJobs];
     int nd = 0;
     for (int64_t i = 0; i < n_desc; ++i) {
@@ -486,6 +515,7 @@ int q8_0_matmul_r8_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, void *s
         if (s.m > q8::kStreamMaxM) return Q8_E_UNSUPPORTED;
         if (s.n == 0 || s.m == 0 || s.batch == 0) continue;
         if (!s.w_r8 || !s.x || !s.y) return Q8_E_NULL;
+        if (sums && !aligned(sums[i], 4)) return Q8_E_ALIGN;
         const int64_t nb = s.k / kQK;
         if (s.m > 1 && (s.x_row_stride < nb || s.y_row_stride < s.n)) return Q8_E_SHAPE;
         if (s.batch > 1 && (s.w_batch_stride < q8::r8_bytes(s.n, nb) || s.x_batch_stride < 0 ||
@@ -505,9 +535,24 @@ int q8_0_matmul_r8_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, void *s
         o.x_bstride = s.batch > 1 ? s.x_batch_stride * kBB : 0;
         o.y_rstride = s.m > 1 ? s.y_row_stride : s.n;
         o.y_bstride = s.batch > 1 ? s.y_batch_stride : 0;
+        o.sums = sums ? sums[i] : nullptr;
     }
     if (nd == 0) return Q8_OK;
     return hip_status(q8::launch_r8_mm(d, nd, as_stream(stream)));
+}
+
+extern "C" {
+
+int q8_0_matmul_r8_batched(const q8_0_r8_mm_desc *descs, int64_t n_desc, void *stream)
+{
+    return r8_mm_batched(descs, n_desc, nullptr, stream);
+}
+
+int q8v_matmul_r8_batched_blocksums(const q8_0_r8_mm_desc *descs, int64_t n_desc,
+                                    int32_t *const *sums, void *stream)
+{
+    if (n_desc > 0 && !sums) return Q8_E_NULL;
+    return r8_mm_batched(descs, n_desc, sums, stream);
 }
 
 int q8_0_matvec_r8(const void *w_r8, const q8_0_block *x, float *y, int64_t n, int64_t k,

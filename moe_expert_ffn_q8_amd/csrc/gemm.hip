@@ -75,6 +75,7 @@ struct GemmArgs {
     const uint8_t *w;      // [n][nb] blocks
     const uint8_t *x;      // [m][nb] blocks
     float *y;              // [m][ldy]
+    int32_t *sums;         // validation (SUMS kernel): int32 [m][n][nb] block sums
     int m, n, nb, ldy;
     int tiles_n, tiles_m;
 };
@@ -90,6 +91,9 @@ __device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
                  (int)__builtin_amdgcn_alignbyte(d3, d2, 2), (int)__builtin_amdgcn_alignbyte(d4, d3, 2)};
 }
 
+// SUMS (validation build of the same kernel): every exact int32 block sum is
+// also written out.
+template <bool SUMS>
 __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
 {
     // Two K-step buffers as separate LDS objects: the compiler then orders an
@@ -215,6 +219,15 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
                 for (int j = 0; j < 2; ++j) {
                     v16i s = {0};
                     s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], s, 0, 0, 0);
+                    if (SUMS) {
+                        const int n = n0 + 64 * wn + 32 * j + li;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                            if (m < a.m && n < a.n)
+                                a.sums[((int64_t)m * a.n + n) * a.nb + st * kStepBlocks + b] = s[r];
+                        }
+                    }
                     if (Q8_GEMM_OUTER) {
                         v16f pz = {0.f};
                         const v16f P = __builtin_amdgcn_mfma_f32_32x32x2f32(adx[i], bdw[j], pz, 0, 0, 0);
@@ -265,16 +278,19 @@ bool gemm_ok(int64_t n, int64_t nb, int64_t m)
 }
 
 int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t nb, int64_t m,
-                int64_t ldy, hipStream_t stream)
+                int64_t ldy, hipStream_t stream, int32_t *sums)
 {
     GemmArgs a;
-    a.w = w; a.x = x; a.y = y;
+    a.w = w; a.x = x; a.y = y; a.sums = sums;
     a.m = (int)m; a.n = (int)n; a.nb = (int)nb; a.ldy = (int)ldy;
     a.tiles_n = (int)((n + kBN - 1) / kBN);
     a.tiles_m = (int)((m + kBM - 1) / kBM);
     const int64_t grid = (int64_t)a.tiles_n * a.tiles_m;
     if (grid > 0x7fffffff) return -4;
-    hipLaunchKernelGGL(gemm_q8_kernel, dim3((unsigned)grid), dim3(kGThreads), 0, stream, a);
+    if (sums)
+        hipLaunchKernelGGL(gemm_q8_kernel<true>, dim3((unsigned)grid), dim3(kGThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(gemm_q8_kernel<false>, dim3((unsigned)grid), dim3(kGThreads), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

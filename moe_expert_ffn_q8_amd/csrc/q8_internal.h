@@ -54,8 +54,9 @@ int launch_quantize_rows(const float *x, int64_t row_stride, void *y, int64_t n_
 
 // Prefill product on the int8 matrix cores (m token rows, any m >= 1).
 bool gemm_ok(int64_t n, int64_t nb, int64_t m);
+// sums: validation, int32 [m][n][nb] block sums (null in the product path).
 int launch_gemm(const uint8_t *w, const uint8_t *x, float *y, int64_t n, int64_t nb, int64_t m,
-                int64_t ldy, hipStream_t stream);
+                int64_t ldy, hipStream_t stream, int32_t *sums = nullptr);
 
 // Row-interleaved weight layout (R8): 8-row groups of 272*nb bytes, the
 // group's scales first, ordered by (block, row), then its codes, ordered by
@@ -73,6 +74,7 @@ struct R8Desc {
     float *y;
     int64_t n, nb, batch;
     int64_t w_bstride, x_bstride, y_bstride;
+    int32_t *sums;         // validation: int32 [batch][n][nb] block sums, else null
 };
 bool r8_matvec_ok(int64_t n, int64_t nb, int64_t batch);
 int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream);
@@ -85,6 +87,7 @@ struct R8MmDesc {
     float *y;
     int64_t n, nb, m, batch;
     int64_t w_bstride, x_rstride, x_bstride, y_rstride, y_bstride;
+    int32_t *sums;         // validation: int32 [batch][m][n][nb] block sums, else null
 };
 bool r8_mm_ok(int64_t n, int64_t nb, int64_t m, int64_t batch);
 int launch_r8_mm(const R8MmDesc *d, int n_desc, hipStream_t stream);

@@ -58,6 +58,7 @@ struct R8Job {
     int64_t w_bstride;     // bytes between matrices
     int64_t x_bstride;     // bytes between activation rows
     int64_t y_bstride;     // floats between output vectors
+    int32_t *sums;         // validation: int32 [batch][n][nb] block sums (SUMS kernels only)
     int64_t n;
     int nb;
     int gpm;               // groups per matrix
@@ -100,8 +101,9 @@ __global__ __launch_bounds__(256) void r8_repack_kernel(const uint8_t *__restric
 
 // XF: the activation rows are fp32 and every workgroup quantizes its row
 // into LDS itself (the bytes of q8_0_quantize_rows), so a decode step needs no
-// separate quantization launch.
-template <bool XF>
+// separate quantization launch.  SUMS (validation builds of the same kernel):
+// every exact int32 block sum is also written out.
+template <bool XF, bool SUMS>
 __global__ __launch_bounds__(kR8Threads) void r8_matvec_kernel(const R8Args a)
 {
     const int wave = threadIdx.x >> 6;
@@ -222,6 +224,10 @@ __global__ __launch_bounds__(kR8Threads) void r8_matvec_kernel(const R8Args a)
             s = sdot4(c[u].w, xv.w, s);
             // the other half of the block from the neighbouring lane (quad_perm 1,0,3,2)
             s += __builtin_amdgcn_mov_dpp(s, 0xB1, 0xF, 0xF, false);
+            if (SUMS && half == 0 && live) {
+                const int64_t row = (int64_t)g * kR8Rows + ((lane >> 1) & 7);
+                if (row < jb.n) jb.sums[((int64_t)mb * jb.n + row) * nb + b] = s;
+            }
             const float dw = live ? half_bits_to_float(sb[u]) : 0.0f;
             acc = fmaf(dw * half_bits_to_float(xd16[bb]), (float)s, acc);
         }
@@ -270,11 +276,14 @@ int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream
     int64_t wg = 0;
     int nb_max = 1;
     int nj = 0;
+    bool sums = false;
     for (int i = 0; i < n_desc; ++i) {
         if (d[i].n == 0 || d[i].batch == 0) continue;
         R8Job &j = a.job[nj++];
         j.w = d[i].w; j.x = d[i].x; j.y = d[i].y;
         j.w_bstride = d[i].w_bstride; j.x_bstride = d[i].x_bstride; j.y_bstride = d[i].y_bstride;
+        j.sums = d[i].sums;
+        if (d[i].sums) sums = true;
         j.n = d[i].n;
         j.nb = (int)d[i].nb;
         j.gpm = (int)((d[i].n + kR8Rows - 1) / kR8Rows);
@@ -286,12 +295,21 @@ int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream
     }
     if (nj == 0) return 0;
     a.n_jobs = nj;
-    if (x_f32)
-        hipLaunchKernelGGL(r8_matvec_kernel<true>, dim3((unsigned)wg), dim3(kR8Threads),
-                           (size_t)34 * nb_max, stream, a);
-    else
-        hipLaunchKernelGGL(r8_matvec_kernel<false>, dim3((unsigned)wg), dim3(kR8Threads),
-                           (size_t)34 * nb_max, stream, a);
+    const size_t lds = (size_t)34 * nb_max;
+    if (sums) {
+        if (x_f32)
+            hipLaunchKernelGGL((r8_matvec_kernel<true, true>), dim3((unsigned)wg), dim3(kR8Threads),
+                               lds, stream, a);
+        else
+            hipLaunchKernelGGL((r8_matvec_kernel<false, true>), dim3((unsigned)wg), dim3(kR8Threads),
+                               lds, stream, a);
+    } else if (x_f32) {
+        hipLaunchKernelGGL((r8_matvec_kernel<true, false>), dim3((unsigned)wg), dim3(kR8Threads),
+                           lds, stream, a);
+    } else {
+        hipLaunchKernelGGL((r8_matvec_kernel<false, false>), dim3((unsigned)wg), dim3(kR8Threads),
+                           lds, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

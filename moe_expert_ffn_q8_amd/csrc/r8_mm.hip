@@ -64,6 +64,7 @@ struct MmJob {
     int64_t x_bstride;     // bytes between matrices
     int64_t y_rstride;     // floats
     int64_t y_bstride;     // floats
+    int32_t *sums;         // validation: int32 [batch][m][n][nb] block sums (SUMS kernels)
     int64_t n;
     int nb, m;
     int gpm;               // groups per matrix
@@ -79,7 +80,9 @@ struct MmArgs {
     int n_jobs;
 };
 
-template <int MT>
+// SUMS (validation builds of the same kernel): every exact int32 block sum is
+// also written out.
+template <int MT, bool SUMS>
 __global__ __launch_bounds__(kMmThreads) void r8_mm_kernel(const MmArgs a)
 {
     const int wave = threadIdx.x >> 6;
@@ -191,6 +194,15 @@ __global__ __launch_bounds__(kMmThreads) void r8_mm_kernel(const MmArgs a)
                                   : (v4i){0, 0, 0, 0};
             v16i s = {0};
             s = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, c[u], s, 0, 0, 0);
+            if (SUMS && b0 + u < bend) {
+                const int64_t row = (int64_t)g0 * 8 + nl;
+#pragma unroll
+                for (int v = 0; v < kLive; ++v) {
+                    const int t = 8 * (v >> 2) + 4 * hi + (v & 3);
+                    if (t < m && row < jb.n)
+                        jb.sums[(((int64_t)mb * m + t) * jb.n + row) * nb + b] = s[v];
+                }
+            }
             const float dw = b0 + u < bend ? half_bits_to_float(sb[u]) : 0.0f;
             const float *dxb = xd + MT * b;
 #pragma unroll
@@ -239,20 +251,20 @@ __global__ __launch_bounds__(kMmThreads) void r8_mm_kernel(const MmArgs a)
 
 size_t mm_lds_bytes(int mt, int64_t nb) { return (size_t)36 * mt * nb + (size_t)kMmWaves * kWave * (mt / 2) * 4; }
 
-template <int MT>
+template <int MT, bool SUMS>
 int launch_mt(const MmArgs &a, unsigned grid, size_t lds, hipStream_t stream)
 {
     if (lds > 65536) {
         static bool attr_set = false;
         if (!attr_set) {
-            if (hipFuncSetAttribute((const void *)r8_mm_kernel<MT>,
+            if (hipFuncSetAttribute((const void *)r8_mm_kernel<MT, SUMS>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                     max_lds_bytes()) != hipSuccess)
                 return -6;
             attr_set = true;
         }
     }
-    hipLaunchKernelGGL(r8_mm_kernel<MT>, dim3(grid), dim3(kMmThreads), lds, stream, a);
+    hipLaunchKernelGGL((r8_mm_kernel<MT, SUMS>), dim3(grid), dim3(kMmThreads), lds, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -285,12 +297,15 @@ int launch_r8_mm(const R8MmDesc *d, int n_desc, hipStream_t stream)
     int64_t nb_max = 1;
     int m_max = 1;
     int nj = 0;
+    bool sums = false;
     for (int i = 0; i < n_desc; ++i) {
         if (d[i].n == 0 || d[i].m == 0 || d[i].batch == 0) continue;
         MmJob &j = a.job[nj++];
         j.w = d[i].w; j.x = d[i].x; j.y = d[i].y;
         j.w_bstride = d[i].w_bstride; j.x_rstride = d[i].x_rstride; j.x_bstride = d[i].x_bstride;
         j.y_rstride = d[i].y_rstride; j.y_bstride = d[i].y_bstride;
+        j.sums = d[i].sums;
+        if (d[i].sums) sums = true;
         j.n = d[i].n;
         j.nb = (int)d[i].nb;
         j.m = (int)d[i].m;
@@ -308,8 +323,11 @@ int launch_r8_mm(const R8MmDesc *d, int n_desc, hipStream_t stream)
     }
     if (nj == 0) return 0;
     a.n_jobs = nj;
-    if (m_max <= 8) return launch_mt<8>(a, (unsigned)wg, mm_lds_bytes(8, nb_max), stream);
-    return launch_mt<16>(a, (unsigned)wg, mm_lds_bytes(16, nb_max), stream);
+    if (sums)
+        return m_max <= 8 ? launch_mt<8, true>(a, (unsigned)wg, mm_lds_bytes(8, nb_max), stream)
+                          : launch_mt<16, true>(a, (unsigned)wg, mm_lds_bytes(16, nb_max), stream);
+    if (m_max <= 8) return launch_mt<8, false>(a, (unsigned)wg, mm_lds_bytes(8, nb_max), stream);
+    return launch_mt<16, false>(a, (unsigned)wg, mm_lds_bytes(16, nb_max), stream);
 }
 
 }  // namespace q8
