@@ -584,6 +584,52 @@ int q8v_matvec_r8_f32_batched_blocksums(const q8_0_r8_f32_desc *descs, int64_t n
 int q8v_matmul_r8_batched_blocksums(const q8_0_r8_mm_desc *descs, int64_t n_desc,
                                     int32_t *const *sums, void *stream);
 
+/* q8v_moe_up_gate: moe_up_gate_swiglu (same arguments, same path and
+ * kernels for the shape: the decode kernels up to 16 tokens, the grouped
+ * matrix-core path above) with validation outputs, each optional (NULL):
+ *   sums    int32 [n_tok*n_used][2*n_ff][n_embd/32]: the block sums of every
+ *           gate row (index j) and up row (n_ff + j) of each slot's expert
+ *           against its token's quantized row (slots with an out-of-range id
+ *           are not written);
+ *   counts  int32 [n_expert], offsets int32 [n_expert + 1], pairs int32
+ *           [n_tok*n_used]: the expert-major grouping the kernels served
+ *           (slot t*n_used+u listed under its expert, experts ascending,
+ *           slots ascending within an expert; out-of-range ids left out) --
+ *           written by the kernels that group the slots (the ownership scan
+ *           of the decode kernels, the routing tables of the grouped path);
+ *           all three or none, and Q8_E_UNSUPPORTED for the shapes that run
+ *           on the generic kernels, which serve every slot on its own.
+ * h and the workspace are written as by moe_up_gate_swiglu. */
+int q8v_moe_up_gate(const q8_0_block *w_up_gate, const float *x, const int32_t *ids, float *h,
+                    int32_t *sums, int32_t *counts, int32_t *offsets, int32_t *pairs,
+                    int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* q8v_moe_hq: moe_down_combine (same arguments and kernels) with validation
+ * outputs, each optional (NULL):
+ *   hq    Q8_0 [n_tok*n_used][n_ff/32]: the quantized h rows the down
+ *         products used (the bytes of q8_0_quantize_rows of the h rows; rows
+ *         of slots with an out-of-range id are unspecified);
+ *   sums  int32 [n_tok*n_used][n_embd][n_ff/32]: the block sums of every
+ *         down row of each slot's expert against that slot's q(h) row.
+ * out and the workspace are written as by moe_down_combine. */
+int q8v_moe_hq(const q8_0_block *w_down, const float *h, const int32_t *ids, const float *cw,
+               float *out, q8_0_block *hq, int32_t *sums, int64_t n_tok, int64_t n_ff,
+               int64_t n_embd, int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* q8v_moe_r8_ffn: moe_r8_ffn_batched for one layer (desc, with its
+ * workspace) with the validation outputs of both products: ug_sums and
+ * dn_sums laid out as the sums of q8v_moe_up_gate and q8v_moe_hq, hq the
+ * quantized h rows the down product used, and the routing (counts, offsets,
+ * pairs as in q8v_moe_up_gate) on the grouped path only (more than 16
+ * tokens; the decode kernels stream each slot's expert on its own:
+ * Q8_E_UNSUPPORTED there).  Each output optional (NULL). */
+int q8v_moe_r8_ffn(const moe_r8_ffn_desc *desc, int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                   int64_t n_expert, int64_t n_used, int32_t *ug_sums, int32_t *dn_sums,
+                   q8_0_block *hq, int32_t *counts, int32_t *offsets, int32_t *pairs,
+                   void *stream);
+
 /* moe_route: the grouping of (t,u) slots by expert that the MoE kernels use:
  * counts[e] (int32 [n_expert]), offsets[e] (int32 [n_expert+1], exclusive
  * prefix of counts), pairs (int32 [n_tok*n_used]): t*n_used+u of every slot,

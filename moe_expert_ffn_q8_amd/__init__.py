@@ -7,7 +7,7 @@ fails if the library has not been built: there is no CPU fallback.
 from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDesc, Q8Error,
                    Q8MatmulDesc, Q8MatmulF32Desc, Q8UpGateDesc, make_desc, make_f32_desc,
                    make_up_gate_desc, q8_0_up_gate_swiglu_batched, moe_down_combine, moe_down_combine_batched,
-                   moe_error_word, moe_route, moe_up_gate_swiglu, moe_up_gate_swiglu_batched,
+                   moe_error_word, moe_route, q8v_moe_up_gate, q8v_moe_hq, q8v_moe_r8_ffn, moe_up_gate_swiglu, moe_up_gate_swiglu_batched,
                    moe_workspace, moe_workspace_bytes, q8_0_matmul, q8_0_matmul_batched,
                    q8_0_matmul_blocksums, q8v_matvec_r8_batched_blocksums, q8v_matvec_r8_f32_batched_blocksums, q8v_matmul_r8_batched_blocksums, q8_0_matmul_f32_batched, q8_0_matmul_f32_step,
                    q8_0_matmul_f32_step_workspace, q8_0_matmul_f32_step_ws_bytes, q8_0_matvec,
@@ -20,7 +20,7 @@ from ._lib import (BLOCK_BYTES, EXPORTS, LIB_PATH, QK, MoeDownDesc, MoeUpGateDes
 __all__ = ["BLOCK_BYTES", "EXPORTS", "LIB_PATH", "QK", "MoeDownDesc", "MoeUpGateDesc", "Q8Error",
            "Q8MatmulDesc", "Q8MatmulF32Desc", "Q8UpGateDesc", "make_desc", "make_f32_desc",
            "make_up_gate_desc", "q8_0_up_gate_swiglu_batched", "moe_down_combine", "moe_down_combine_batched",
-           "moe_error_word", "moe_route", "moe_up_gate_swiglu", "moe_up_gate_swiglu_batched",
+           "moe_error_word", "moe_route", "q8v_moe_up_gate", "q8v_moe_hq", "q8v_moe_r8_ffn", "moe_up_gate_swiglu", "moe_up_gate_swiglu_batched",
            "moe_workspace", "moe_workspace_bytes", "q8_0_matmul", "q8_0_matmul_batched",
            "q8_0_matmul_blocksums", "q8v_matvec_r8_batched_blocksums", "q8v_matvec_r8_f32_batched_blocksums", "q8v_matmul_r8_batched_blocksums", "q8_0_matmul_f32_batched", "q8_0_matmul_f32_step",
            "q8_0_matmul_f32_step_workspace", "q8_0_matmul_f32_step_ws_bytes", "q8_0_matvec",

@@ -120,6 +120,12 @@ _SIGS = {
     "q8v_matmul_r8_batched_blocksums": (_int, [ctypes.POINTER(Q8R8MmDesc), _i64,
                                                ctypes.POINTER(_vp), _vp]),
     "moe_route": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]),
+    "q8v_moe_up_gate": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                               _i64, _vp, _size, _vp]),
+    "q8v_moe_hq": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                          _size, _vp]),
+    "q8v_moe_r8_ffn": (_int, [ctypes.POINTER(MoeR8FfnDesc), _i64, _i64, _i64, _i64, _i64, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp]),
     "q8_read_probe": (_int, [_vp, _i64, _vp, _i64, _vp]),
     "q8_0_r8_bytes": (_i64, [_i64, _i64]),
     "q8_0_repack_r8": (_int, [_vp, _vp, _i64, _i64, _vp]),
@@ -732,6 +738,74 @@ def moe_down_combine_batched(layers, n_ff, n_embd, n_expert):
     _check("moe_down_combine_batched", _lib.moe_down_combine_batched(
         arr, len(layers), n_tok, n_ff, n_embd, n_expert, n_used, _stream(layers[0]["ids"])))
     return [d["out"] for d in layers]
+
+
+def q8v_moe_up_gate(w_up_gate, x, ids, n_embd, n_ff, n_expert, ws, sums=True, route=True):
+    """moe_up_gate_swiglu plus its validation outputs: returns (h, sums, counts,
+    offsets, pairs) -- sums int32 [n_tok*n_used][2*n_ff][n_embd/32] and the
+    expert-major grouping the kernels served (None where not asked for)."""
+    _need(w_up_gate, torch.uint8, "w_up_gate")
+    _need(x, torch.float32, "x")
+    _need(ids, torch.int32, "ids")
+    _need(ws, torch.uint8, "ws")
+    n_tok, n_used = _ids_shape(ids)
+    dev = ids.device
+    h = torch.full((n_tok, n_used, n_ff), float("nan"), dtype=torch.float32, device=dev)
+    _check_up_gate(w_up_gate, x, ids, h, n_tok, n_used, n_embd, n_ff, n_expert)
+    _one_device(ids, ws)
+    slots = n_tok * n_used
+    s = (torch.full((slots, 2 * n_ff, n_embd // QK), -(1 << 31), dtype=torch.int32, device=dev)
+         if sums else None)
+    c = torch.full((n_expert,), -1, dtype=torch.int32, device=dev) if route else None
+    o = torch.full((n_expert + 1,), -1, dtype=torch.int32, device=dev) if route else None
+    p = torch.full((max(slots, 1),), -1, dtype=torch.int32, device=dev) if route else None
+    _check("q8v_moe_up_gate", _lib.q8v_moe_up_gate(
+        _ptr(w_up_gate), _ptr(x), _ptr(ids), _ptr(h), _ptr(s), _ptr(c), _ptr(o), _ptr(p), n_tok,
+        n_embd, n_ff, n_expert, n_used, _ptr(ws), ws.numel(), _stream(ids)))
+    return h, s, c, o, (p[:slots] if p is not None else None)
+
+
+def q8v_moe_hq(w_down, h, ids, cw, n_ff, n_embd, n_expert, ws, sums=True):
+    """moe_down_combine plus its validation outputs: returns (out, hq, sums) --
+    hq uint8 [n_tok*n_used][n_ff/32*34] (the Q8_0 bytes of h the down products
+    used), sums int32 [n_tok*n_used][n_embd][n_ff/32] (None if not asked)."""
+    _need(w_down, torch.uint8, "w_down")
+    _need(h, torch.float32, "h")
+    _need(ids, torch.int32, "ids")
+    _need(cw, torch.float32, "cw")
+    _need(ws, torch.uint8, "ws")
+    n_tok, n_used = _ids_shape(ids)
+    dev = ids.device
+    out = torch.full((n_tok, n_embd), float("nan"), dtype=torch.float32, device=dev)
+    _check_down(w_down, h, ids, cw, out, n_tok, n_used, n_ff, n_embd, n_expert)
+    _one_device(ids, ws)
+    slots = n_tok * n_used
+    hq = torch.zeros((slots, n_ff // QK * BLOCK_BYTES), dtype=torch.uint8, device=dev)
+    s = (torch.full((slots, n_embd, n_ff // QK), -(1 << 31), dtype=torch.int32, device=dev)
+         if sums else None)
+    _check("q8v_moe_hq", _lib.q8v_moe_hq(
+        _ptr(w_down), _ptr(h), _ptr(ids), _ptr(cw), _ptr(out), _ptr(hq), _ptr(s), n_tok, n_ff,
+        n_embd, n_expert, n_used, _ptr(ws), ws.numel(), _stream(ids)))
+    return out, hq, s
+
+
+def q8v_moe_r8_ffn(layer, n_embd, n_ff, n_expert, route=False):
+    """moe_r8_ffn_batched for one layer (a dict as for moe_r8_ffn_batched) plus
+    the validation outputs: returns (ug_sums, dn_sums, hq, counts, offsets,
+    pairs); the routing only with route=True (grouped path only)."""
+    arr, n_tok, n_used = _r8_ffn_descs([layer], n_embd, n_ff, n_expert, True)
+    dev = layer["ids"].device
+    slots = n_tok * n_used
+    ug = torch.full((slots, 2 * n_ff, n_embd // QK), -(1 << 31), dtype=torch.int32, device=dev)
+    dn = torch.full((slots, n_embd, n_ff // QK), -(1 << 31), dtype=torch.int32, device=dev)
+    hq = torch.zeros((slots, n_ff // QK * BLOCK_BYTES), dtype=torch.uint8, device=dev)
+    c = torch.full((n_expert,), -1, dtype=torch.int32, device=dev) if route else None
+    o = torch.full((n_expert + 1,), -1, dtype=torch.int32, device=dev) if route else None
+    p = torch.full((max(slots, 1),), -1, dtype=torch.int32, device=dev) if route else None
+    _check("q8v_moe_r8_ffn", _lib.q8v_moe_r8_ffn(
+        arr, n_tok, n_embd, n_ff, n_expert, n_used, _ptr(ug), _ptr(dn), _ptr(hq), _ptr(c), _ptr(o),
+        _ptr(p), _stream(layer["ids"])))
+    return ug, dn, hq, c, o, (p[:slots] if p is not None else None)
 
 
 def moe_route(ids, n_expert, ws):

@@ -392,6 +392,54 @@ int moe_down_combine(const q8_0_block *w_down, const float *h, const int32_t *id
     return moe_down_combine_batched(&d, 1, n_tok, n_ff, n_embd, n_expert, n_used, stream);
 }
 
+// The routing outputs of a validation call: all three or none.
+static int route_outputs(const int32_t *counts, const int32_t *offsets, const int32_t *pairs)
+{
+    const int given = (counts != nullptr) + (offsets != nullptr) + (pairs != nullptr);
+    if (given != 0 && given != 3) return Q8_E_NULL;
+    if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pairs, 4)) return Q8_E_ALIGN;
+    return Q8_OK;
+}
+
+int q8v_moe_up_gate(const q8_0_block *w_up_gate, const float *x, const int32_t *ids, float *h,
+                    int32_t *sums, int32_t *counts, int32_t *offsets, int32_t *pairs,
+                    int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
+                    void *ws, size_t ws_bytes, void *stream)
+{
+    if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    const moe_up_gate_desc d = {w_up_gate, x, ids, h, ws, ws_bytes};
+    if (int rc = check_up_gate_desc(d, n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    if (int rc = route_outputs(counts, offsets, pairs)) return rc;
+    if (!aligned(sums, 4)) return Q8_E_ALIGN;
+    if (n_tok == 0) return Q8_OK;
+    q8::MoeEmit e = {sums, nullptr, counts, offsets, pairs};
+    q8::MoeUpGateArgs a;
+    a.n_layers = 1;
+    a.layer[0] = {(const uint8_t *)w_up_gate, x, ids, h, ws};
+    a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert; a.n_used = n_used;
+    a.emit = &e;
+    return hip_status(q8::launch_moe_up_gate(a, as_stream(stream)));
+}
+
+int q8v_moe_hq(const q8_0_block *w_down, const float *h, const int32_t *ids, const float *cw,
+               float *out, q8_0_block *hq, int32_t *sums, int64_t n_tok, int64_t n_ff,
+               int64_t n_embd, int64_t n_expert, int64_t n_used, void *ws, size_t ws_bytes,
+               void *stream)
+{
+    if (int rc = moe_check(n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    const moe_down_desc d = {w_down, h, ids, cw, out, ws, ws_bytes};
+    if (int rc = check_down_desc(d, n_tok, n_embd, n_ff, n_expert, n_used)) return rc;
+    if (!aligned(hq, 2) || !aligned(sums, 4)) return Q8_E_ALIGN;
+    if (n_tok == 0) return Q8_OK;
+    q8::MoeEmit e = {sums, hq, nullptr, nullptr, nullptr};
+    q8::MoeDownArgs a;
+    a.n_layers = 1;
+    a.layer[0] = {(const uint8_t *)w_down, h, ids, cw, out, ws};
+    a.n_tok = n_tok; a.n_embd = n_embd; a.n_ff = n_ff; a.n_expert = n_expert; a.n_used = n_used;
+    a.emit = &e;
+    return hip_status(q8::launch_moe_down(a, as_stream(stream)));
+}
+
 int64_t q8_0_r8_bytes(int64_t n, int64_t k)
 {
     if (int rc = check_k(k)) return rc;
@@ -694,6 +742,26 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
     if (n_desc == 0) return Q8_OK;
     return r8_ffn_launch(descs, n_desc, n_tok, n_embd, n_ff, n_expert, n_used,
                          [&](int64_t i) { return descs[i].ws; }, stream);
+}
+
+int q8v_moe_r8_ffn(const moe_r8_ffn_desc *desc, int64_t n_tok, int64_t n_embd, int64_t n_ff,
+                   int64_t n_expert, int64_t n_used, int32_t *ug_sums, int32_t *dn_sums,
+                   q8_0_block *hq, int32_t *counts, int32_t *offsets, int32_t *pairs,
+                   void *stream)
+{
+    if (int rc = r8_ffn_checks(desc, 1, n_tok, n_embd, n_ff, n_expert, n_used, true)) return rc;
+    if (int rc = route_outputs(counts, offsets, pairs)) return rc;
+    if (!aligned(ug_sums, 4) || !aligned(dn_sums, 4) || !aligned(hq, 2)) return Q8_E_ALIGN;
+    // the decode kernels serve every slot on its own: no grouping to report
+    if (counts && !q8::moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used))
+        return Q8_E_UNSUPPORTED;
+    if (n_tok == 0) return Q8_OK;
+    q8::MoeEmit eu = {ug_sums, nullptr, counts, offsets, pairs};
+    q8::MoeEmit ed = {dn_sums, hq, nullptr, nullptr, nullptr};
+    const q8::MoeR8Layer l = {desc->w_up_gate_r8, desc->w_down_r8, desc->x, desc->ids, desc->cw,
+                              desc->h, desc->out, desc->ws};
+    return hip_status(q8::launch_moe_r8_ffn(&l, 1, n_tok, n_embd, n_ff, n_expert, n_used,
+                                            as_stream(stream), &eu, &ed));
 }
 
 int moe_r8_ffn_batched_noalloc(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_tok,

@@ -110,17 +110,21 @@ __device__ __forceinline__ void preload_ids(const int32_t *ids, int n_slots, Ids
 // every slot routed to e (listed in ascending (t,u) order).  One ballot pass
 // of wave 0 over the ids finds ownership, the slot list and whether any id is
 // out of range.  Sets ps.expert (-1: nothing to do), ps.count, ps.slots,
-// ps.invalid; ends with a workgroup barrier.
+// ps.invalid (LESS: also ps.pad = the number of in-range slots with an id
+// below e, the start of e's group in the expert-major slot order); ends with
+// a workgroup barrier.
+template <bool LESS>
 __device__ void pick_by_slot(const int32_t *ids, int n_slots, int n_expert, int s, int e,
                              const IdsPre &ip, PickShared &ps)
 {
     const int tid = threadIdx.x;
     if (tid < kWave) {
-        int cnt = 0;
+        int cnt = 0, less = 0;
         bool first = true, bad = false;
         auto step = [&](int i, int v) {
             const bool in = i < n_slots;
             bad |= __ballot(in && (v < 0 || v >= n_expert)) != 0;
+            if (LESS) less += __popcll(__ballot(in && v >= 0 && v < e));
             const bool hit = in && v == e;
             const uint64_t m = __ballot(hit);
             first &= __ballot(hit && i < s) == 0;
@@ -138,9 +142,39 @@ __device__ void pick_by_slot(const int32_t *ids, int n_slots, int n_expert, int 
             ps.invalid = bad ? 1 : 0;
             ps.expert = (e >= 0 && e < n_expert && first) ? e : -1;
             ps.count = cnt;
+            if (LESS) ps.pad = less;
         }
     }
     __syncthreads();
+}
+
+// Validation outputs of the expert kernels (null in the product path): the
+// exact int32 block sums [slot][weight row][block], the Q8_0 bytes of the h
+// rows the down kernels used [slot][n_ff/32], and the expert-major grouping
+// the up_gate kernels served (counts per expert, slots at their group's
+// start).  Written only by the EMIT instances of the kernels.
+struct MoeEmitPtrs {
+    int32_t *sums;
+    uint8_t *hq;
+    int32_t *counts;
+    int32_t *pairs;
+};
+
+// Write the Q8_0 bytes of image rows [0, mc) (masked image + fp32 scales, as
+// quantize_rows_to_image leaves them) to hq rows slot_of(m): the scale bits
+// are those of the fp32 scale (a binary16 value, converted exactly).
+template <class SlotOf>
+__device__ void emit_hq_rows(const uint8_t *ximg, const float *xsc, int mc, int nb, uint8_t *hq,
+                             SlotOf slot_of)
+{
+    for (int i = threadIdx.x; i < mc * nb * 17; i += blockDim.x) {
+        const int m = i / (nb * 17);
+        const int r = i - m * nb * 17;
+        const int b = r / 17, w = r - b * 17;
+        uint16_t v = ((const uint16_t *)(ximg + (m * nb + b) * kBlockBytes))[w];
+        if (w == 0) v = __builtin_bit_cast(uint16_t, (_Float16)xsc[m * nb + b]);
+        ((uint16_t *)(hq + ((int64_t)slot_of(m) * nb + b) * kBlockBytes))[w] = v;
+    }
 }
 
 // Quantize one 32-value block held as 4 values by each of 8 lanes into image
@@ -218,6 +252,7 @@ struct UgLayer {
 
 struct UgParams {
     UgLayer layer[kMoeMaxLayers];
+    MoeEmitPtrs emit;
     int n_layers;
     int wgs_per_layer;     // n_slots * wgs_per_expert
     int n_slots, n_used, n_expert, nb, n_ff;
@@ -229,7 +264,9 @@ struct UgParams {
 
 static_assert(sizeof(UgParams) <= 4000, "kernel arguments must stay below 4 KB");
 
-template <int MT>
+// EMIT (validation builds of the same kernel): p.emit's block sums and
+// routing are written as well.
+template <int MT, bool EMIT>
 __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
 {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -283,7 +320,11 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
         tile_issue(We + (int64_t)(real ? p.n_ff + j0 : 0) * row_bytes, chunks, lane, gu);
     };
     if (!issue_after_pick<MT>()) issue(t0 + wave, e0_ok && t0 + wave < t1);
-    pick_by_slot(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
+    pick_by_slot<EMIT>(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
+    if (EMIT && ps.expert >= 0 && part == 0 && p.emit.counts) {
+        if (tid == 0) p.emit.counts[ps.expert] = ps.count;
+        for (int i = tid; i < ps.count; i += kThreads) p.emit.pairs[ps.pad + i] = ps.slots[i];
+    }
 
     if (wl == 0) {
         if (tid == 0) *L.err = ps.invalid ? 1 : 0;
@@ -347,6 +388,12 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_kernel(const UgParams p)
                     int sb[4];
                     const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, sb);
                     red[m * kWave + lane] = (lane < live) ? acc : 0.0f;
+                    if (EMIT && p.emit.sums && lane < live) {
+                        const int64_t wrow = (int64_t)half * p.n_ff + j0 + lane / Q;
+                        int32_t *o = p.emit.sums +
+                                     ((int64_t)ps.slots[c0 + m] * 2 * p.n_ff + wrow) * nb + 4 * c;
+                        o[0] = sb[0]; o[1] = sb[1]; o[2] = sb[2]; o[3] = sb[3];
+                    }
                 }
             }
             wave_lds_sync();
@@ -378,6 +425,7 @@ struct DnLayer {
 
 struct DnParams {
     DnLayer layer[kMoeMaxLayers];
+    MoeEmitPtrs emit;
     int n_layers;
     int wgs_per_layer;
     int n_slots, n_used, n_expert, nb, n_ff, n_rows;
@@ -386,7 +434,7 @@ struct DnParams {
 
 static_assert(sizeof(DnParams) <= 4000, "kernel arguments must stay below 4 KB");
 
-template <int MT>
+template <int MT, bool EMIT>
 __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
 {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -428,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
     preload_ids(L.ids, p.n_slots, ip);
     // depends only on ids[slot]: issue before the scan and the h round trip
     if (!issue_after_pick<MT>()) issue(t0 + wave, e0_ok && t0 + wave < t1);
-    pick_by_slot(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
+    pick_by_slot<false>(L.ids, p.n_slots, p.n_expert, slot, e0, ip, ps);
     if (wl == 0 && tid == 0) *L.err = ps.invalid ? 1 : 0;
     if (ps.expert < 0) return;
     const int count = ps.count;
@@ -441,6 +489,8 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
         // quantize the h rows of this chunk's slots into the masked image
         quantize_rows_to_image(L.h, p.n_ff, ps.slots + c0, 0, mc, nb, ximg, xsc);
         __syncthreads();
+        if (EMIT && p.emit.hq && part == 0)
+            emit_hq_rows(ximg, xsc, mc, nb, p.emit.hq, [&](int m) { return ps.slots[c0 + m]; });
         if (issue_after_pick<MT>() && c0 == 0) issue(t, t < t1);
 
         uint32_t xr[kQuadDwords];
@@ -473,6 +523,11 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const DnParams p)
                     int s[4];
                     const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, s);
                     red[m * kWave + lane] = (lane < live) ? acc : 0.0f;
+                    if (EMIT && p.emit.sums && lane < live) {
+                        int32_t *o = p.emit.sums + ((int64_t)ps.slots[c0 + m] * p.n_rows + row0 +
+                                                    lane / Q) * nb + 4 * c;
+                        o[0] = s[0]; o[1] = s[1]; o[2] = s[2]; o[3] = s[3];
+                    }
                 }
             }
             wave_lds_sync();
@@ -511,6 +566,7 @@ struct DrLayer {
 
 struct DrParams {
     DrLayer layer[kMoeMaxLayers];
+    MoeEmitPtrs emit;
     int n_layers;
     int wgs_per_layer;     // ceil(n_rows / R)
     int n_used, n_slots, n_expert, nb, n_ff, n_rows, R;
@@ -518,6 +574,7 @@ struct DrParams {
 
 static_assert(sizeof(DrParams) <= 4000, "kernel arguments must stay below 4 KB");
 
+template <bool EMIT>
 __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrParams p)
 {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -583,6 +640,8 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
     if (h_pre) quantize_prefetched<kDnPrePass>(hv, p.n_slots, nb, 0, ximg, xsc);
     else quantize_rows_to_image(L.h, p.n_ff, s_rows, 0, p.n_slots, nb, ximg, xsc);
     __syncthreads();
+    if (EMIT && p.emit.hq && wl == 0)
+        emit_hq_rows(ximg, xsc, p.n_slots, nb, p.emit.hq, [](int m) { return m; });
 
     while (s < p.n_slots) {
         uint32_t wq[kQuadDwords];
@@ -597,6 +656,10 @@ __global__ __launch_bounds__(kRowThreads) void moe_down_rows_kernel(const DrPara
         int sb[4];
         const float acc = quad_dot(wq, xq, dw0, dw1, dw2, dw3, dx, sb);
         red[wave][lane] = (lane < live) ? acc : 0.0f;
+        if (EMIT && p.emit.sums && lane < live) {
+            int32_t *o = p.emit.sums + ((int64_t)s * p.n_rows + row0 + lane / Q) * nb + 4 * c;
+            o[0] = sb[0]; o[1] = sb[1]; o[2] = sb[2]; o[3] = sb[3];
+        }
         wave_lds_sync();
         if (lane < rows) {
             const float *pr = &red[wave][lane * Q];
@@ -701,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void moe_route_kernel(const int32_t *ids,
 // loads; fixed-order xor-tree reduction.
 
 __device__ __forceinline__ float generic_row_dot(const uint8_t *w, const uint8_t *x, int nb,
-                                                 int lane)
+                                                 int lane, int32_t *sums = nullptr)
 {
     float acc = 0.0f;
     for (int b = lane; b < nb; b += kWave) {
@@ -714,6 +777,7 @@ __device__ __forceinline__ float generic_row_dot(const uint8_t *w, const uint8_t
             s += (int)(int8_t)(wv & 0xff) * (int)(int8_t)(xv & 0xff);
             s += (int)(int8_t)(wv >> 8) * (int)(int8_t)(xv >> 8);
         }
+        if (sums) sums[b] = s;        // validation output (null in the product path)
         acc = fmaf(half_bits_to_float(load_u16(wb)) * half_bits_to_float(load_u16(xb)),
                    (float)s, acc);
     }
@@ -767,8 +831,10 @@ __global__ __launch_bounds__(kThreads) void moe_up_gate_generic_kernel(const UgP
     const int64_t row_bytes = (int64_t)p.nb * kBlockBytes;
     const uint8_t *We = L.w + (int64_t)e * 2 * p.n_ff * row_bytes;
     const uint8_t *xr = xq;
-    const float g = generic_row_dot(We + (int64_t)j * row_bytes, xr, p.nb, lane);
-    const float u = generic_row_dot(We + (int64_t)(p.n_ff + j) * row_bytes, xr, p.nb, lane);
+    int32_t *sg = p.emit.sums ? p.emit.sums + ((int64_t)s * 2 * p.n_ff + j) * p.nb : nullptr;
+    const float g = generic_row_dot(We + (int64_t)j * row_bytes, xr, p.nb, lane, sg);
+    const float u = generic_row_dot(We + (int64_t)(p.n_ff + j) * row_bytes, xr, p.nb, lane,
+                                    sg ? sg + (int64_t)p.n_ff * p.nb : nullptr);
     if (lane == 0) *dst = g / (1.0f + expf(-g)) * u;
 }
 
@@ -785,13 +851,37 @@ __global__ __launch_bounds__(kThreads) void moe_down_generic_kernel(const DnPara
     const int tid = threadIdx.x;
     quantize_row_to_blocks(L.h + (int64_t)s * p.n_ff, p.nb, hq);
     __syncthreads();
+    if (p.emit.hq && blockIdx.y == 0)          // validation: the bytes of q(h) used
+        for (int i = tid; i < p.nb * kBlockBytes / 2; i += kThreads)
+            ((uint16_t *)(p.emit.hq + (int64_t)s * p.nb * kBlockBytes))[i] = ((const uint16_t *)hq)[i];
     const int row = blockIdx.y * kWaves + (tid >> 6);
     const int lane = tid & 63;
     if (row >= p.n_rows) return;
     const int64_t row_bytes = (int64_t)p.nb * kBlockBytes;
     const uint8_t *wr = L.w + ((int64_t)e * p.n_rows + row) * row_bytes;
-    const float y = generic_row_dot(wr, hq, p.nb, lane);
+    const float y = generic_row_dot(wr, hq, p.nb, lane,
+                                    p.emit.sums ? p.emit.sums + ((int64_t)s * p.n_rows + row) * p.nb
+                                                : nullptr);
     if (lane == 0) L.yslot[(int64_t)s * p.n_rows + row] = y;
+}
+
+// Validation helpers: fill an int32 array; exclusive offsets [n_expert + 1]
+// from per-expert counts (one workgroup, sequential scan by one thread).
+__global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ void route_offsets_kernel(const int32_t *counts, int32_t *offsets, int n_expert)
+{
+    if (threadIdx.x != 0) return;
+    int acc = 0;
+    for (int e = 0; e < n_expert; ++e) {
+        offsets[e] = acc;
+        acc += counts[e];
+    }
+    offsets[n_expert] = acc;
 }
 
 int pick_mt(int64_t n_tok)
@@ -802,6 +892,21 @@ int pick_mt(int64_t n_tok)
 }
 
 }  // namespace
+
+int launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream)
+{
+    if (n <= 0) return 0;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int launch_route_offsets(const int32_t *counts, int32_t *offsets, int64_t n_expert,
+                         hipStream_t stream)
+{
+    hipLaunchKernelGGL(route_offsets_kernel, dim3(1), dim3(64), 0, stream, counts, offsets,
+                       (int)n_expert);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, float *out,
                        int64_t n_tok, int64_t n_rows, int64_t n_used, int64_t n_expert,
@@ -831,13 +936,16 @@ size_t moe_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_exper
 }
 
 template <int MT>
-static int launch_ug_mt(const UgParams &p, int grid, hipStream_t stream)
+static int launch_ug_mt(const UgParams &p, int grid, hipStream_t stream, bool emit)
 {
     const size_t lds = (size_t)kWaves * kStageBytes + (size_t)kWaves * 2 * MT * kWave * 4 +
                        (size_t)MT * p.nb * kBlockBytes + (size_t)MT * p.nb * 4 +
                        sizeof(PickShared) + MT * sizeof(int);
     if (lds > (size_t)max_lds_bytes()) return -4;
-    hipLaunchKernelGGL(moe_up_gate_kernel<MT>, dim3(grid), dim3(kThreads), lds, stream, p);
+    if (emit)
+        hipLaunchKernelGGL((moe_up_gate_kernel<MT, true>), dim3(grid), dim3(kThreads), lds, stream, p);
+    else
+        hipLaunchKernelGGL((moe_up_gate_kernel<MT, false>), dim3(grid), dim3(kThreads), lds, stream, p);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -863,7 +971,8 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
         for (int l = 0; l < a.n_layers; ++l) {
             const MoeUpGateArgs::Layer &L = a.layer[l];
             if (int rc = launch_moe_prefill_up_gate(L.w, L.x, L.ids, L.h, L.ws, a.n_tok, a.n_embd,
-                                                    a.n_ff, a.n_expert, a.n_used, stream))
+                                                    a.n_ff, a.n_expert, a.n_used, stream,
+                                                    a.emit))
                 return rc;
         }
         return 0;
@@ -882,6 +991,15 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
     p.n_expert = (int)a.n_expert;
     p.nb = (int)nb;
     p.n_ff = (int)a.n_ff;
+    const bool emit = a.emit != nullptr;
+    if (emit) {
+        p.emit = MoeEmitPtrs{a.emit->sums, nullptr, a.emit->counts, a.emit->pairs};
+        // the generic kernels serve every slot on its own: no grouping to report
+        if (!fast && a.emit->counts) return -4;
+        if (a.emit->counts) {
+            if (int rc = launch_fill_i32(a.emit->counts, a.n_expert, 0, stream)) return rc;
+        }
+    }
     p.R = fast ? (int)(64 / (nb / 4)) : 1;
     p.tiles_per_expert = (p.n_ff + p.R - 1) / p.R;
     const int64_t active = a.n_layers * (a.n_expert < p.n_slots ? a.n_expert : p.n_slots);
@@ -897,21 +1015,27 @@ int launch_moe_up_gate(const MoeUpGateArgs &a, hipStream_t stream)
         return hipGetLastError() == hipSuccess ? 0 : -6;
     }
     if (grid > 0x7fffffff) return -4;
+    int rc;
     switch (pick_mt(a.n_tok)) {
-        case 1: return launch_ug_mt<1>(p, (int)grid, stream);
-        case 2: return launch_ug_mt<2>(p, (int)grid, stream);
-        default: return launch_ug_mt<4>(p, (int)grid, stream);
+        case 1: rc = launch_ug_mt<1>(p, (int)grid, stream, emit); break;
+        case 2: rc = launch_ug_mt<2>(p, (int)grid, stream, emit); break;
+        default: rc = launch_ug_mt<4>(p, (int)grid, stream, emit); break;
     }
+    if (rc || !emit || !a.emit->counts) return rc;
+    return launch_route_offsets(a.emit->counts, a.emit->offsets, a.n_expert, stream);
 }
 
 template <int MT>
-static int launch_dn_mt(const DnParams &p, int grid, hipStream_t stream)
+static int launch_dn_mt(const DnParams &p, int grid, hipStream_t stream, bool emit)
 {
     const size_t lds = (size_t)kWaves * kStageBytes + (size_t)kWaves * MT * kWave * 4 +
                        (size_t)MT * p.nb * kBlockBytes + (size_t)MT * p.nb * 4 +
                        sizeof(PickShared);
     if (lds > (size_t)max_lds_bytes()) return -4;
-    hipLaunchKernelGGL(moe_down_kernel<MT>, dim3(grid), dim3(kThreads), lds, stream, p);
+    if (emit)
+        hipLaunchKernelGGL((moe_down_kernel<MT, true>), dim3(grid), dim3(kThreads), lds, stream, p);
+    else
+        hipLaunchKernelGGL((moe_down_kernel<MT, false>), dim3(grid), dim3(kThreads), lds, stream, p);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -922,7 +1046,8 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
         for (int l = 0; l < a.n_layers; ++l) {
             const MoeDownArgs::Layer &L = a.layer[l];
             if (int rc = launch_moe_prefill_down(L.w, L.h, L.ids, L.cw, L.out, L.ws, a.n_tok,
-                                                 a.n_embd, a.n_ff, a.n_expert, a.n_used, stream))
+                                                 a.n_embd, a.n_ff, a.n_expert, a.n_used, stream,
+                                                 a.emit))
                 return rc;
         }
         return 0;
@@ -930,6 +1055,9 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
     const int64_t nb = a.n_ff / kQK;
     const bool fast = (nb % 8 == 0) && nb <= kStreamMaxNb;
     const int64_t n_slots = a.n_tok * a.n_used;
+    const bool emit = a.emit != nullptr;
+    const MoeEmitPtrs ep = emit ? MoeEmitPtrs{a.emit->sums, (uint8_t *)a.emit->hq, nullptr, nullptr}
+                                : MoeEmitPtrs{nullptr, nullptr, nullptr, nullptr};
     // The row-major kernel (combine fused, one launch) wins for a single layer,
     // where the call is latency-bound; over many layers the expert-major
     // kernel streams better (measured on 30 one-token layers: 198 us per step
@@ -942,6 +1070,7 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
             r.layer[l] = DrLayer{A.w, A.h, A.ids, A.cw, A.out, (int32_t *)A.ws};
         }
         r.n_layers = a.n_layers;
+        r.emit = ep;
         r.n_used = (int)a.n_used; r.n_slots = (int)n_slots; r.n_expert = (int)a.n_expert;
         r.nb = (int)nb; r.n_ff = (int)a.n_ff; r.n_rows = (int)a.n_embd;
         r.R = (int)(64 / (nb / 4));
@@ -951,7 +1080,12 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
         if (lds > (size_t)max_lds_bytes()) return -4;
         const int64_t grid = (int64_t)a.n_layers * r.wgs_per_layer;
         if (grid > 0x7fffffff) return -4;
-        hipLaunchKernelGGL(moe_down_rows_kernel, dim3((unsigned)grid), dim3(kRowThreads), lds, stream, r);
+        if (emit)
+            hipLaunchKernelGGL(moe_down_rows_kernel<true>, dim3((unsigned)grid), dim3(kRowThreads), lds,
+                               stream, r);
+        else
+            hipLaunchKernelGGL(moe_down_rows_kernel<false>, dim3((unsigned)grid), dim3(kRowThreads), lds,
+                               stream, r);
         return hipGetLastError() == hipSuccess ? 0 : -6;
     }
     DnParams p;
@@ -965,6 +1099,7 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
         cb.layer[l] = CbLayer{yslot, A.ids, A.cw, A.out};
     }
     p.n_layers = a.n_layers;
+    p.emit = ep;
     p.n_slots = (int)(a.n_tok * a.n_used);
     p.n_used = (int)a.n_used;
     p.n_expert = (int)a.n_expert;
@@ -987,9 +1122,9 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
         hipLaunchKernelGGL(moe_down_generic_kernel, g, dim3(kThreads), lds, stream, p);
         rc = hipGetLastError() == hipSuccess ? 0 : -6;
     } else switch (pick_mt(a.n_tok)) {
-        case 1: rc = launch_dn_mt<1>(p, (int)grid, stream); break;
-        case 2: rc = launch_dn_mt<2>(p, (int)grid, stream); break;
-        default: rc = launch_dn_mt<4>(p, (int)grid, stream); break;
+        case 1: rc = launch_dn_mt<1>(p, (int)grid, stream, emit); break;
+        case 2: rc = launch_dn_mt<2>(p, (int)grid, stream, emit); break;
+        default: rc = launch_dn_mt<4>(p, (int)grid, stream, emit); break;
     }
     if (rc) return rc;
     cb.n_rows = (int)a.n_embd;

@@ -84,17 +84,29 @@ struct RouteArgs {
     int n_slots, n_expert, n_ff;
 };
 
+constexpr int kRouteWaves = kRouteThreads / kWave;      // 16
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const RouteArgs a)
 {
     __shared__ int cnt[kMoeMaxExperts];
     __shared__ int scan_c[kMoeMaxExperts];
     __shared__ int scan_t[kMoeMaxExperts];
+    // per wave and expert, two 16-bit fields per word (expert e in word e/2,
+    // bits 16*(e&1)): the wave's slot count, then its running position
+    // within the expert's group
+    __shared__ uint32_t wcnt[kRouteWaves][kMoeMaxExperts / 2];
     __shared__ int bad;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    // wave w owns the contiguous slot range [w*span, (w+1)*span)
+    const int span = (a.n_slots + kRouteWaves - 1) / kRouteWaves;
+    const int s_beg = min(wave * span, a.n_slots), s_end = min(s_beg + span, a.n_slots);
     for (int e = tid; e < kMoeMaxExperts; e += kRouteThreads) cnt[e] = 0;
+    for (int i = tid; i < kRouteWaves * kMoeMaxExperts / 2; i += kRouteThreads)
+        (&wcnt[0][0])[i] = 0;
     if (tid == 0) bad = 0;
     __syncthreads();
-    for (int s = tid; s < a.n_slots; s += kRouteThreads) {
+    for (int s = s_beg + lane; s < s_end; s += kWave) {
         const int e = a.ids[s];
         if (e < 0 || e >= a.n_expert) {
             atomicOr(&bad, 1);
@@ -102,6 +114,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const Ro
                 for (int j = 0; j < a.n_ff; ++j) a.h_nan[(int64_t)s * a.n_ff + j] = __builtin_nanf("");
         } else {
             atomicAdd(&cnt[e], 1);
+            atomicAdd(&wcnt[wave][e >> 1], (e & 1) ? 0x10000u : 1u);
         }
     }
     __syncthreads();
@@ -133,16 +146,44 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const Ro
         a.hdr[0] = bad;
         a.hdr[1] = scan_t[a.n_expert - 1];
     }
-    __syncthreads();
-    // scatter the slots (the fill counters reuse cnt)
-    for (int e = tid; e < kMoeMaxExperts; e += kRouteThreads) cnt[e] = 0;
-    __syncthreads();
-    for (int s = tid; s < a.n_slots; s += kRouteThreads) {
-        const int e = a.ids[s];
-        if (e >= 0 && e < a.n_expert) {
-            const int p = atomicAdd(&cnt[e], 1);
-            a.pairs[(e > 0 ? scan_c[e - 1] : 0) + p] = s;
+    // each wave's start within every expert's group: the counts of the waves
+    // before it (exclusive prefix over waves, in place)
+    if (tid < kMoeMaxExperts) {
+        const int e = tid, sh = 16 * (e & 1);
+        uint32_t run = 0;
+        for (int w = 0; w < kRouteWaves; ++w) {
+            uint32_t *word = &wcnt[w][e >> 1];
+            const uint32_t c = (*word >> sh) & 0xffffu;
+            atomicAnd(word, ~(0xffffu << sh));
+            atomicOr(word, run << sh);
+            run += c;
         }
+    }
+    __syncthreads();
+    // scatter in slot order: a wave walks its range 64 slots at a time; a lane
+    // takes the next position of its expert after the lanes below it naming
+    // the same expert (found by matching the 10 bits of the id)
+    for (int s0 = s_beg; s0 < s_end; s0 += kWave) {
+        const int s = s0 + lane;
+        const int e = s < s_end ? a.ids[s] : -1;
+        const bool ok = e >= 0 && e < a.n_expert;
+        uint64_t peers = __ballot(ok);
+#pragma unroll
+        for (int bit = 0; bit < 10; ++bit) {
+            const uint64_t m = __ballot(((e >> bit) & 1) != 0);
+            peers &= ((e >> bit) & 1) ? m : ~m;
+        }
+        if (ok) {
+            const int sh = 16 * (e & 1);
+            const int run = (int)((wcnt[wave][e >> 1] >> sh) & 0xffffu);
+            const int rank = __popcll(peers & __lanemask_lt());
+            a.pairs[(e > 0 ? scan_c[e - 1] : 0) + run + rank] = s;
+        }
+        wave_lds_sync();
+        // the lowest lane of each group of peers advances the group's position
+        if (ok && (peers & __lanemask_lt()) == 0)
+            atomicAdd(&wcnt[wave][e >> 1], (uint32_t)__popcll(peers) << (16 * (e & 1)));
+        wave_lds_sync();
     }
 }
 
@@ -209,6 +250,7 @@ struct PgArgs {
     int nb;                  // blocks per A / weight row (K / 32)
     int n_used;              // up_gate: A row of slot s is token s / n_used
     int max_tiles, tiles_n;
+    int32_t *sums;           // validation (EMIT kernels): [slot][w_rows][nb] block sums
 };
 
 // Output columns per workgroup: up_gate pairs waves w and w + 4 (gate and up
@@ -219,7 +261,9 @@ constexpr int pg_cols()
     return UG ? 32 * kPWaves / 2 : 32 * kPWaves;
 }
 
-template <bool UG>
+// EMIT (validation builds of the same kernel): every exact int32 block sum is
+// also written to a.sums.
+template <bool UG, bool EMIT>
 __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
 {
     // A tile: codes [b][half][row][16 bytes] (1 KB per block), scales [b][row]
@@ -309,7 +353,20 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
     // The 4 blocks of a stage: every LDS operand is read first (the weight
     // halves from slot 11 li + 2j + h, the scale dwords, the token codes and
     // scales), then the 4 products are formed and rescaled in block order.
-    auto compute = [&](const uint8_t *stage, int bi0) {
+    // validation: the slot row of every result register, and this lane's
+    // weight row within the expert (gate rows, then up rows, for up_gate)
+    const int64_t w_rows = UG ? 2 * (int64_t)a.n_out : a.n_out;
+    const int64_t wrow = (UG && wave >= 4 ? a.n_out : 0) + col;
+    auto emit = [&](const v16i &sr, int b) {
+        if (!EMIT || !wave_live || b >= nb) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row < te.rows) a.sums[((int64_t)a_slot[row] * w_rows + wrow) * nb + b] = sr[r];
+        }
+    };
+
+    auto compute = [&](const uint8_t *stage, int bi0, int bglob0) {
         const uint8_t *wb = stage + wave * kPWaveStage;
         u32x4 c[4], av[4];
         uint32_t d[4];
@@ -344,6 +401,7 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
         for (int j = 0; j < 4; ++j) {
             const uint32_t sbits = (j & 1) == 0 ? (d[j] & 0xffffu) : (d[j] >> 16);
             const float dw = half_bits_to_float(sbits);
+            emit(sres[j], bglob0 + j);
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = fmaf(dx[j][r] * dw, (float)sres[j][r], acc[r]);
         }
@@ -376,10 +434,10 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
         for (int bi0 = 0; bi0 < kc; bi0 += kPDepth) {
             const int st = (kb0 + bi0) / 4;
             __builtin_amdgcn_s_waitcnt(0x3f70 | kPStageLoads);
-            compute(bst0, bi0);
+            compute(bst0, bi0, kb0 + bi0);
             issue_b(st + 2, bst0);
             __builtin_amdgcn_s_waitcnt(0x3f70 | kPStageLoads);
-            compute(bst1, bi0 + 4);
+            compute(bst1, bi0 + 4, kb0 + bi0 + 4);
             issue_b(st + 3, bst1);
         }
     }
@@ -420,7 +478,7 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
 // token tile is staged in LDS once per 64 blocks (codes in code order).
 constexpr int kR8Chunk = 64;
 
-template <bool UG>
+template <bool UG, bool EMIT>
 __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs a)
 {
     __shared__ __align__(16) uint8_t la[kR8Chunk * 1024];
@@ -514,6 +572,16 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
                 sres = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                     (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w},
                     (v4i){(int)c.x, (int)c.y, (int)c.z, (int)c.w}, sres, 0, 0, 0);
+                if (EMIT && wave_live && kb0 + bi < nb) {
+                    const int64_t w_rows = UG ? 2 * (int64_t)a.n_out : a.n_out;
+                    const int64_t wr = (UG && wave >= 4 ? a.n_out : 0) + col;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int row = 8 * (q >> 2) + 4 * h + (q & 3);
+                        if (row < te.rows)
+                            a.sums[((int64_t)a_slot[row] * w_rows + wr) * nb + kb0 + bi] = sres[q];
+                    }
+                }
                 const float dw = half_bits_to_float(ws16[i]);
                 float dx[16];
 #pragma unroll
@@ -607,9 +675,10 @@ int launch_route(const int32_t *ids, uint8_t *ws, const PrefillWs &L, float *h_n
 template <bool UG, bool R8>
 int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows, const uint8_t *w,
                    int64_t w_rows, int64_t nb, uint8_t *ws, const PrefillWs &L, float *out,
-                   int64_t n_out, int64_t n_used, hipStream_t stream)
+                   int64_t n_out, int64_t n_used, hipStream_t stream, int32_t *sums = nullptr)
 {
     PgArgs p;
+    p.sums = sums;
     p.a_codes = a_codes;
     p.a_scales = a_scales;
     p.a_rows = (int)a_rows;
@@ -627,10 +696,67 @@ int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows
     int64_t grid = L.max_tiles * p.tiles_n;
     grid = (grid + 7) & ~(int64_t)7;
     if (grid > 0x7fffffff) return -4;
-    if (R8)
-        hipLaunchKernelGGL(moe_r8_gemm_kernel<UG>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+    if (R8 && sums)
+        hipLaunchKernelGGL((moe_r8_gemm_kernel<UG, true>), dim3((unsigned)grid), dim3(kPThreads), 0,
+                           stream, p);
+    else if (R8)
+        hipLaunchKernelGGL((moe_r8_gemm_kernel<UG, false>), dim3((unsigned)grid), dim3(kPThreads), 0,
+                           stream, p);
+    else if (sums)
+        hipLaunchKernelGGL((moe_gemm_kernel<UG, true>), dim3((unsigned)grid), dim3(kPThreads), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL(moe_gemm_kernel<UG>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+        hipLaunchKernelGGL((moe_gemm_kernel<UG, false>), dim3((unsigned)grid), dim3(kPThreads), 0,
+                           stream, p);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Validation: the routing tables of the workspace as counts [n_expert],
+// offsets [n_expert + 1] and pairs [offsets[n_expert]] (one workgroup).
+__global__ void route_export_kernel(const int32_t *ws_offsets, const int32_t *ws_pairs,
+                                    int32_t *counts, int32_t *offsets, int32_t *pairs, int n_expert)
+{
+    const int total = ws_offsets[n_expert];
+    for (int e = threadIdx.x; e <= n_expert; e += blockDim.x) {
+        offsets[e] = ws_offsets[e];
+        if (e < n_expert) counts[e] = ws_offsets[e + 1] - ws_offsets[e];
+    }
+    for (int i = threadIdx.x; i < total; i += blockDim.x) pairs[i] = ws_pairs[i];
+}
+
+// Validation: the Q8_0 bytes of rows in the A-operand layout (fp32 scales;
+// codes of even blocks stored rotated, code j at byte (j - 2) mod 32, when
+// `rotate`), one thread per block.
+__global__ void qa_export_kernel(const uint8_t *codes, const float *scales, int64_t total_blocks,
+                                 int64_t nb, int rotate, uint8_t *out)
+{
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= total_blocks) return;
+    const bool rot = rotate && ((g % nb) & 1) == 0;
+    const uint8_t *src = codes + g * 32;
+    uint8_t *dst = out + g * kBlockBytes;
+    const uint16_t d = __builtin_bit_cast(uint16_t, (_Float16)scales[g]);
+    dst[0] = (uint8_t)(d & 0xff);
+    dst[1] = (uint8_t)(d >> 8);
+    for (int j = 0; j < 32; ++j) dst[2 + j] = src[rot ? (j + 30) & 31 : j];
+}
+
+int launch_qa_export(const uint8_t *codes, const float *scales, int64_t n_rows, int64_t nb,
+                     bool rotate, void *out, hipStream_t stream)
+{
+    const int64_t total = n_rows * nb;
+    if (total == 0) return 0;
+    hipLaunchKernelGGL(qa_export_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       codes, scales, total, nb, rotate ? 1 : 0, (uint8_t *)out);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int launch_route_export(const uint8_t *ws, const PrefillWs &L, const MoeEmit &e, int64_t n_expert,
+                        hipStream_t stream)
+{
+    hipLaunchKernelGGL(route_export_kernel, dim3(1), dim3(1024), 0, stream,
+                       (const int32_t *)(ws + L.offsets), (const int32_t *)(ws + L.pairs), e.counts,
+                       e.offsets, e.pairs, (int)n_expert);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -669,21 +795,26 @@ size_t moe_prefill_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t
 
 int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *ids, float *h,
                                void *ws_, int64_t n_tok, int64_t n_embd, int64_t n_ff,
-                               int64_t n_expert, int64_t n_used, hipStream_t stream)
+                               int64_t n_expert, int64_t n_used, hipStream_t stream,
+                               const MoeEmit *emit)
 {
     uint8_t *ws = (uint8_t *)ws_;
     const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
     const int64_t nb = n_embd / kQK;
     if (int rc = launch_route(ids, ws, L, h, n_tok * n_used, n_expert, n_ff, stream)) return rc;
+    if (emit && emit->counts)
+        if (int rc = launch_route_export(ws, L, *emit, n_expert, stream)) return rc;
     uint8_t *xq = ws + L.data;
     float *xs = (float *)(ws + L.xq_scales);
     if (int rc = launch_qa_quantize(x, n_embd, xq, xs, n_tok, nb, true, stream)) return rc;
-    return launch_grouped<true, false>(xq, xs, n_tok, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used, stream);
+    return launch_grouped<true, false>(xq, xs, n_tok, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used, stream,
+                                       emit ? emit->sums : nullptr);
 }
 
 int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids, const float *cw,
                             float *out, void *ws_, int64_t n_tok, int64_t n_embd, int64_t n_ff,
-                            int64_t n_expert, int64_t n_used, hipStream_t stream)
+                            int64_t n_expert, int64_t n_used, hipStream_t stream,
+                            const MoeEmit *emit)
 {
     uint8_t *ws = (uint8_t *)ws_;
     const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
@@ -693,9 +824,11 @@ int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids
     uint8_t *hq = ws + L.data;
     float *hs = (float *)(ws + L.hq_scales);
     if (int rc = launch_qa_quantize(h, n_ff, hq, hs, slots, nb, true, stream)) return rc;
+    if (emit && emit->hq)
+        if (int rc = launch_qa_export(hq, hs, slots, nb, true, emit->hq, stream)) return rc;
     float *yslot = (float *)(ws + L.yslot);
     if (int rc = launch_grouped<false, false>(hq, hs, slots, w, n_embd, nb, ws, L, yslot, n_embd, n_used,
-                                       stream))
+                                              stream, emit ? emit->sums : nullptr))
         return rc;
     return launch_moe_combine(yslot, ids, cw, out, n_tok, n_embd, n_used, n_expert, stream);
 }
@@ -703,7 +836,8 @@ int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids
 int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float *x,
                           const int32_t *ids, const float *cw, float *h, float *out, void *ws_,
                           int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
-                          int64_t n_used, hipStream_t stream)
+                          int64_t n_used, hipStream_t stream, const MoeEmit *emit_ug,
+                          const MoeEmit *emit_dn)
 {
     uint8_t *ws = (uint8_t *)ws_;
     const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
@@ -711,19 +845,27 @@ int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float 
     const int64_t slots = n_tok * n_used;
     // one routing for both products (the tables stay in the workspace)
     if (int rc = launch_route(ids, ws, L, h, slots, n_expert, n_ff, stream)) return rc;
+    if (emit_ug && emit_ug->counts)
+        if (int rc = launch_route_export(ws, L, *emit_ug, n_expert, stream)) return rc;
     uint8_t *q = ws + L.data;
     if (int rc = launch_qa_quantize(x, n_embd, q, (float *)(ws + L.xq_scales), n_tok, nbe, false,
                                     stream))
         return rc;
     if (int rc = launch_grouped<true, true>(q, (const float *)(ws + L.xq_scales), n_tok, w_ug,
-                                            2 * n_ff, nbe, ws, L, h, n_ff, n_used, stream))
+                                            2 * n_ff, nbe, ws, L, h, n_ff, n_used, stream,
+                                            emit_ug ? emit_ug->sums : nullptr))
         return rc;
     if (int rc = launch_qa_quantize(h, n_ff, q, (float *)(ws + L.hq_scales), slots, nbf, false,
                                     stream))
         return rc;
+    if (emit_dn && emit_dn->hq)
+        if (int rc = launch_qa_export(q, (const float *)(ws + L.hq_scales), slots, nbf, false,
+                                      emit_dn->hq, stream))
+            return rc;
     float *yslot = (float *)(ws + L.yslot);
     if (int rc = launch_grouped<false, true>(q, (const float *)(ws + L.hq_scales), slots, w_dn,
-                                             n_embd, nbf, ws, L, yslot, n_embd, n_used, stream))
+                                             n_embd, nbf, ws, L, yslot, n_embd, n_used, stream,
+                                             emit_dn ? emit_dn->sums : nullptr))
         return rc;
     return launch_moe_combine(yslot, ids, cw, out, n_tok, n_embd, n_used, n_expert, stream);
 }

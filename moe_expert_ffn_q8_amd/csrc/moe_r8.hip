@@ -47,10 +47,13 @@ constexpr int kMrSlices = 8;              // 1 KB slices of a group in flight pe
 // realigned to 32 bytes per block, binary16 scale bits); slice i, lane l:
 // row (l>>1)&7, block 4i + (l>>4), half l&1.  Returns the lane's partial sum
 // (blocks of its residue, ascending); the caller adds lanes l, l^16, l^32.
-template <int POL>
+// EMIT (validation): every exact block sum is also written to srow[b], the
+// sums row of this lane's weight row (lanes that hold a whole sum).
+template <int POL, bool EMIT = false>
 struct GroupStream {
     __amdgpu_buffer_rsrc_t rs;
     int code0, scale0, nb;
+    int32_t *srow = nullptr;
     u32x4 c[kMrSlices];
     uint32_t sb[kMrSlices];
 
@@ -88,6 +91,7 @@ struct GroupStream {
             s = sdot4(c[u].z, xv.z, s);
             s = sdot4(c[u].w, xv.w, s);
             s += __builtin_amdgcn_mov_dpp(s, 0xB1, 0xF, 0xF, false);   // the other half
+            if (EMIT && half == 0 && live) srow[b] = s;
             const float dw = live ? half_bits_to_float(sb[u]) : 0.0f;
             acc = fmaf(dw * half_bits_to_float(xd16[bb]), (float)s, acc);
         }
@@ -115,10 +119,12 @@ struct GroupStream {
 // group accumulates its own blocks in ascending order.
 constexpr int kDnG = 4;
 
-template <int POL>
+// EMIT (validation): block sums to sbase[(8q + r) * nb + b] for group q, row r.
+template <int POL, bool EMIT = false>
 struct MultiStream {
     __amdgpu_buffer_rsrc_t rs;
     int nb, S, total, gb;
+    int32_t *sbase = nullptr;
     u32x4 c[kMrSlices];
     uint32_t sb[kMrSlices];
 
@@ -165,6 +171,7 @@ struct MultiStream {
             s = sdot4(c[u].z, xv.z, s);
             s = sdot4(c[u].w, xv.w, s);
             s += __builtin_amdgcn_mov_dpp(s, 0xB1, 0xF, 0xF, false);   // the other half
+            if (EMIT && half == 0 && live) sbase[(8 * q + ((lane >> 1) & 7)) * nb + b] = s;
             const float dw = live ? half_bits_to_float(sb[u]) : 0.0f;
             const float p = dw * half_bits_to_float(xd16[bb]);
 #pragma unroll
@@ -208,9 +215,10 @@ struct MrUgArgs {
     } layer[kMoeMaxLayers];
     int n_used, n_slots, n_embd, n_ff, n_expert;
     int wg_per_layer;
+    int32_t *sums;             // validation: [slot][2*n_ff][n_embd/32] (layer 0 only)
 };
 
-template <int POL>
+template <int POL, bool EMIT>
 __global__ __launch_bounds__(kUgThreads) void moe_r8_up_gate_kernel(const MrUgArgs a)
 {
     const int tid = threadIdx.x;
@@ -268,8 +276,9 @@ __global__ __launch_bounds__(kUgThreads) void moe_r8_up_gate_kernel(const MrUgAr
             if (q8 == 0) xd16[b] = (uint16_t)dbits;
         }
     };
-    GroupStream<POL> gs;
+    GroupStream<POL, EMIT> gs;
     gs.init(gbase, nb, lane, true);
+    if (EMIT) gs.srow = a.sums + ((int64_t)slot * 2 * a.n_ff + 8 * grp + ((lane >> 1) & 7)) * nb;
     if (passes <= 2) {
         const float4 v0 = load_pass(0);
         const float4 v1 = load_pass(passes > 1 ? 1 : 0);
@@ -324,9 +333,10 @@ struct MrDnArgs {
     } layer[kMoeMaxLayers];
     int n_used, n_embd, n_ff, n_expert;
     int wg_per_layer;
+    int32_t *sums;             // validation: [slot][n_embd][n_ff/32] (layer 0 only)
 };
 
-template <int POL>
+template <int POL, bool EMIT>
 __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 {
     const int tid = threadIdx.x;
@@ -371,8 +381,9 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
         hv[i] = *(const uint16_t *)(hq + (e2 >> 4) * kBlockBytes + 2 + 2 * (e2 & 15));
     }
     const uint32_t hs = *(const uint16_t *)(hq + min(lane, nb - 1) * kBlockBytes);
-    MultiStream<POL> ms;
+    MultiStream<POL, EMIT> ms;
     ms.init(gbase, nb);
+    if (EMIT) ms.sbase = a.sums + ((int64_t)(t * U + wave) * a.n_embd + 8 * kDnG * g) * nb;
     __builtin_amdgcn_sched_barrier(0);
     ms.issue(0, lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -473,7 +484,8 @@ int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expe
 }
 
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
-                      int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream)
+                      int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream,
+                      const MoeEmit *emit_ug, const MoeEmit *emit_dn)
 {
     if (n_tok == 0) return 0;
     if (moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used)) {
@@ -481,11 +493,15 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
             const MoeR8Layer &s = l[i];
             if (int rc = launch_moe_r8_prefill((const uint8_t *)s.w_up_gate, (const uint8_t *)s.w_down,
                                                s.x, s.ids, s.cw, s.h, s.out, s.ws, n_tok, n_embd,
-                                               n_ff, n_expert, n_used, stream))
+                                               n_ff, n_expert, n_used, stream, emit_ug, emit_dn))
                 return rc;
         }
         return 0;
     }
+    // the decode kernels serve every slot on its own: no grouping to report
+    if (emit_ug && emit_ug->counts) return -4;
+    int32_t *ug_sums = emit_ug ? emit_ug->sums : nullptr;
+    int32_t *dn_sums = emit_dn ? emit_dn->sums : nullptr;
     for (int l0 = 0; l0 < n_layers; l0 += kMoeMaxLayers) {
         const int nl = n_layers - l0 < kMoeMaxLayers ? n_layers - l0 : kMoeMaxLayers;
         MrUgArgs ug;
@@ -503,6 +519,7 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
         ug.n_ff = (int)n_ff;
         ug.n_expert = (int)n_expert;
         ug.wg_per_layer = (int)(n_tok * n_used * (n_ff / 32));
+        ug.sums = ug_sums;
         const int64_t nb = n_embd / 32;
         const size_t ug_lds = (size_t)(34 * nb + 15) / 16 * 16 + 64 * 4;
         if (ug_lds > (size_t)max_lds_bytes()) return -4;   // also checked by moe_r8_ffn_check
@@ -513,26 +530,37 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
         // (measured, 30 layers: 1 token 182.8 against 205.6 us, 16 tokens
         // 2449 against 2694 us)
         const bool reuse = n_tok > 1;
-        if (reuse)
-            hipLaunchKernelGGL(moe_r8_up_gate_kernel<0>, dim3((unsigned)(nl * ug.wg_per_layer)),
-                               dim3(kUgThreads), ug_lds, stream, ug);
-        else
-            hipLaunchKernelGGL(moe_r8_up_gate_kernel<kCacheNT>,
-                               dim3((unsigned)(nl * ug.wg_per_layer)), dim3(kUgThreads), ug_lds,
+        const dim3 ug_grid((unsigned)(nl * ug.wg_per_layer));
+        if (ug_sums)
+            hipLaunchKernelGGL((moe_r8_up_gate_kernel<0, true>), ug_grid, dim3(kUgThreads), ug_lds,
                                stream, ug);
+        else if (reuse)
+            hipLaunchKernelGGL((moe_r8_up_gate_kernel<0, false>), ug_grid, dim3(kUgThreads), ug_lds,
+                               stream, ug);
+        else
+            hipLaunchKernelGGL((moe_r8_up_gate_kernel<kCacheNT, false>), ug_grid, dim3(kUgThreads),
+                               ug_lds, stream, ug);
         if (hipGetLastError() != hipSuccess) return -6;
+        if (emit_dn && emit_dn->hq &&
+            hipMemcpyAsync(emit_dn->hq, (const uint8_t *)l[0].ws + 256,
+                           (size_t)(n_tok * n_used) * (n_ff / 32) * kBlockBytes,
+                           hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return -6;
         dn.n_used = (int)n_used;
         dn.n_embd = (int)n_embd;
         dn.n_ff = (int)n_ff;
         dn.n_expert = (int)n_expert;
         dn.wg_per_layer = (int)(n_tok * (n_embd / (8 * kDnG)));
+        dn.sums = dn_sums;
         const size_t dn_lds = (size_t)16 * ((34 * (n_ff / 32) + 15) / 16 * 16) + 16 * 8 * kDnG * 4;
-        if (reuse)
-            hipLaunchKernelGGL(moe_r8_down_kernel<0>, dim3((unsigned)(nl * dn.wg_per_layer)),
-                               dim3((unsigned)(64 * n_used)), dn_lds, stream, dn);
+        const dim3 dn_grid((unsigned)(nl * dn.wg_per_layer)), dn_block((unsigned)(64 * n_used));
+        if (dn_sums)
+            hipLaunchKernelGGL((moe_r8_down_kernel<0, true>), dn_grid, dn_block, dn_lds, stream, dn);
+        else if (reuse)
+            hipLaunchKernelGGL((moe_r8_down_kernel<0, false>), dn_grid, dn_block, dn_lds, stream, dn);
         else
-            hipLaunchKernelGGL(moe_r8_down_kernel<kCacheNT>, dim3((unsigned)(nl * dn.wg_per_layer)),
-                               dim3((unsigned)(64 * n_used)), dn_lds, stream, dn);
+            hipLaunchKernelGGL((moe_r8_down_kernel<kCacheNT, false>), dn_grid, dn_block, dn_lds,
+                               stream, dn);
         if (hipGetLastError() != hipSuccess) return -6;
     }
     return 0;

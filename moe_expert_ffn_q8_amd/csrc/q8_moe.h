@@ -15,6 +15,17 @@ constexpr int kMoeDecodeMaxTok = 16;        // more tokens per call: the prefill
 constexpr int kMoePrefillMaxTok = 8192;
 constexpr int kMoePrefillMaxSlots = 65536;
 
+// Validation outputs of the expert FFN (single-layer calls only; every
+// pointer may be null): block sums int32 [slot][weight row][block], the Q8_0
+// bytes of the h rows the down products used [slot][n_ff/32], and the
+// expert-major slot grouping of the up_gate kernels (counts [n_expert],
+// offsets [n_expert + 1], pairs [slots]).
+struct MoeEmit {
+    int32_t *sums;
+    void *hq;
+    int32_t *counts, *offsets, *pairs;
+};
+
 // One launch covers n_layers independent layers of the same shape; every
 // layer has its own weights, inputs, outputs and workspace.
 struct MoeUpGateArgs {
@@ -27,6 +38,7 @@ struct MoeUpGateArgs {
     } layer[kMoeMaxLayers];
     int n_layers;
     int64_t n_tok, n_embd, n_ff, n_expert, n_used;
+    const MoeEmit *emit = nullptr;     // validation (n_layers == 1)
 };
 
 struct MoeDownArgs {
@@ -40,7 +52,14 @@ struct MoeDownArgs {
     } layer[kMoeMaxLayers];
     int n_layers;
     int64_t n_tok, n_embd, n_ff, n_expert, n_used;
+    const MoeEmit *emit = nullptr;     // validation (n_layers == 1)
 };
+
+// Validation helpers: fill n int32 with v; offsets[0..n_expert] = exclusive
+// prefix of counts.
+int launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
+int launch_route_offsets(const int32_t *counts, int32_t *offsets, int64_t n_expert,
+                         hipStream_t stream);
 
 // Workspace (decode path): [0, 256) error word; [256, ...) per-slot down
 // outputs fp32 [n_tok*n_used][n_embd].  The prefill path's layout is larger
@@ -70,10 +89,12 @@ int moe_prefill_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_exp
                       int64_t n_used);
 int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *ids, float *h,
                                void *ws, int64_t n_tok, int64_t n_embd, int64_t n_ff,
-                               int64_t n_expert, int64_t n_used, hipStream_t stream);
+                               int64_t n_expert, int64_t n_used, hipStream_t stream,
+                               const MoeEmit *emit = nullptr);
 int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids, const float *cw,
                             float *out, void *ws, int64_t n_tok, int64_t n_embd, int64_t n_ff,
-                            int64_t n_expert, int64_t n_used, hipStream_t stream);
+                            int64_t n_expert, int64_t n_used, hipStream_t stream,
+                            const MoeEmit *emit = nullptr);
 
 // Decode expert FFN over R8 weights (up_gate + SwiGLU, down + combine in two
 // launches per call): the combined up_gate tensor repacked as n_expert*2*n_ff
@@ -96,10 +117,12 @@ bool moe_r8_prefill_path(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_
                          int64_t n_used);
 // More than kMoeDecodeMaxTok tokens over R8 weights (moe_prefill_ok shapes):
 // routing, quantization, the two grouped products and the combine of one layer.
+// emit_ug / emit_dn: validation outputs of the up_gate and down products.
 int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float *x,
                           const int32_t *ids, const float *cw, float *h, float *out, void *ws,
                           int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
-                          int64_t n_used, hipStream_t stream);
+                          int64_t n_used, hipStream_t stream, const MoeEmit *emit_ug = nullptr,
+                          const MoeEmit *emit_dn = nullptr);
 // The library's own workspace for callers that cannot allocate
 // (moe_r8_ffn_batched_noalloc): a file-scope device array of
 // kMoeR8ScratchBytes per device.  moe_r8_scratch sets *base to the current
@@ -111,6 +134,7 @@ int moe_r8_scratch(uint8_t **base);
 int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                      int64_t n_used);
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
-                      int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream);
+                      int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream,
+                      const MoeEmit *emit_ug = nullptr, const MoeEmit *emit_dn = nullptr);
 
 }  // namespace q8
