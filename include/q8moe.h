@@ -109,8 +109,13 @@ int q8_0_matvec(const q8_0_block *w, const q8_0_block *x, float *y,
 
 /* ---------------------------------------------------------------------------
  * q8_0_matmul -- Y[m][n] = X[m][k] . W[n][k]^T for m token rows: batched decode
- * (small m, weights streamed once for all rows) and prefill (large m, int8
- * matrix cores).  Same arithmetic as q8_0_matvec for every (m, n).
+ * (small m, weights streamed once for all rows: the batch-of-8 decode of the
+ * [NARR] GPT-2 124M table) and prefill (large m, int8 matrix cores: prompt
+ * evaluation, which [XEON] reports apart from decode in its summary, and
+ * which a matrix library speeds up where sequential decode gains little: the
+ * ARM page, section on build optimisation, OpenBLAS offload).  Same
+ * arithmetic as q8_0_matvec for every (m, n): the block dot of
+ * ggml_vec_dot_q8_0_q8_0 ([XEON] section on narrowing down the cause).
  *   w  Q8_0 [n][k/32], x  Q8_0 [m][k/32], y  fp32 [m][n] (written)
  * m >= 0, n >= 0, k > 0, k % 32 == 0.
  */
@@ -431,7 +436,13 @@ size_t moe_workspace_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff,
  * n_tok*n_used <= 65536.  Other shapes with more than 16 tokens run on the
  * streaming kernels up to n_tok*n_used = 1024, else Q8_E_UNSUPPORTED.  Both
  * paths compute the same quantities; their fp32 sums may differ in the last
- * bits (different summation order), each within the stated tolerance. */
+ * bits (different summation order), each within the stated tolerance.
+ * x is taken in fp32, not as Q8_0 rows: activations reach mul_mat_id in fp32
+ * and are quantized for the Q8_0 x Q8_0 product ([XEON] three-part fix, where
+ * the compile fix names the activation quantizer), so the call quantizes each
+ * token row inside its own launch (the bytes of q8_0_quantize_rows) instead of
+ * needing a separate quantize launch and a Q8_0 buffer; every block sum and h
+ * value is that of q8_0_quantize_rows(x) against the weights. */
 int moe_up_gate_swiglu(const q8_0_block *w_up_gate, const float *x,
                        const int32_t *ids, float *h,
                        int64_t n_tok, int64_t n_embd, int64_t n_ff,
