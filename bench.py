@@ -13,7 +13,14 @@ matrix (the native-layout forms of the same step are timed beside it).
 Prints ONE JSON line: throughput (algorithmic bytes / s over the timed
 steps), tokens/s, the roofline of the dominant kernel (the step launch, timed
 with HIP events on the stream it runs on) and the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload.  Timing protocol: the K steps are one HIP
+graph; 11 rounds, the first dropped, each round the best of 3 replays of the
+headline, the cold form (rotating weight copies) and the headline again as a
+control series; value = the median of the rounds' bests; the control's
+per-round ratios to the headline must straddle 1x; GPU clocks are recorded
+(rocm-smi) before and after.  The same line carries the vocabulary projection
+(262144 x 2048) and the 30-layer MoE expert FFN at 1 and 16 tokens (layer
+after layer and grouped, native and R8 weights), timed in the same run.
 
 Other workloads (one JSON line each), for the per-configuration tables:
   --workload c1      768x768 matvec
@@ -274,6 +281,67 @@ def time_graph(g, reps=1):
     return a.elapsed_time(b) / 1e3 / reps
 
 
+def time_replay(g):
+    """Seconds of one replay of graph g, timed with HIP events on the current
+    stream (the stream the replayed launches run on)."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3
+
+
+def protocol(series, rounds=11, best_of=3):
+    """The timing protocol: `rounds` rounds, the first dropped; in every round
+    each series (name -> captured graph, in the given order) is replayed
+    `best_of` times and its best replay kept; the result per series is the
+    median of the per-round bests (and their spread).  Series rotate inside a
+    round, so slow drift of clocks or temperature reaches all of them alike."""
+    import statistics
+    per = {k: [] for k in series}
+    for g in series.values():          # untimed: first replay after instantiation
+        g.replay()
+    import torch
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        for k, g in series.items():
+            best = min(time_replay(g) for _ in range(best_of))
+            if r > 0:
+                per[k].append(best)
+    return {k: {"median": statistics.median(v), "min": min(v), "max": max(v), "rounds": v}
+            for k, v in per.items()}
+
+
+def control_check(prot, base, control):
+    """A control series (the headline graph replayed again inside every round)
+    against the headline: the per-round ratios must straddle 1x for the
+    headline median to be trusted as a stable figure."""
+    ratios = [c / b for b, c in zip(prot[base]["rounds"], prot[control]["rounds"])]
+    return {"control_over_headline_min": round(min(ratios), 4),
+            "control_over_headline_max": round(max(ratios), 4),
+            "straddles_1x": bool(min(ratios) <= 1.0 <= max(ratios))}
+
+
+def gpu_clocks():
+    """Current clocks as rocm-smi reports them (None where it is unavailable);
+    the clocks are recorded, not set."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    out = {}
+    for card, vals in data.items():
+        if isinstance(vals, dict):
+            out[card] = {k: v for k, v in vals.items() if "clock" in k.lower() or "clk" in k.lower()}
+    return out or None
+
+
 def time_steps(plan, xs, steps, warmup):
     """The K timed steps of each form are captured in one HIP graph and
     replayed once inside the timed region; per-kernel means come from graphs
@@ -300,16 +368,20 @@ def time_steps(plan, xs, steps, warmup):
             plan.step_r8_one(xs[i % n_in])
     torch.cuda.synchronize()
 
-    def graph_of(fn):
+    graphs = {}
+
+    def graph_of(fn, key):
         def body():
             for i in range(steps):
                 fn(xs[i % n_in])
-        return time_graph(capture(body))
+        graphs[key] = capture(body)
+        return time_graph(graphs[key])
 
-    out = dict(total=graph_of(plan.step), total_fused=graph_of(plan.step_fused),
-               total_one=graph_of(plan.step_one) if one else None,
-               total_r8=graph_of(plan.step_r8) if r8 else None,
-               total_r8_one=graph_of(plan.step_r8_one) if r8_one else None)
+    out = dict(total=graph_of(plan.step, "two"), total_fused=graph_of(plan.step_fused, "fused"),
+               total_one=graph_of(plan.step_one, "one") if one else None,
+               total_r8=graph_of(plan.step_r8, "r8") if r8 else None,
+               total_r8_one=graph_of(plan.step_r8_one, "r8_one") if r8_one else None)
+    out["graphs"] = graphs
 
     def eng_only():
         for _ in range(steps):
@@ -347,8 +419,8 @@ def time_steps(plan, xs, steps, warmup):
                 plan.q.q8_0_matmul_batched(sets[i % copies], plan.y)
         for i in range(copies):
             plan.q.q8_0_matmul_batched(sets[i], plan.y)
-    out["total_cold"] = time_graph(capture(all_cold))
-    plan._cold_w = []
+    graphs["cold"] = capture(all_cold)
+    out["total_cold"] = time_graph(graphs["cold"])
     return out
 
 
@@ -397,23 +469,33 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
     n_in = min(args.steps + args.warmup, n_steps_cfg)
     xs = synth.normal_f32_torch((n_in, m, plan.k_total), 1.0, dev, 0, name, "x")
     torch.cuda.synchronize()
+    clocks_before = gpu_clocks()
     t = time_steps(plan, xs, args.steps, args.warmup)
     K = args.steps
     two_bytes = plan.engine_bytes + plan.quant_bytes      # quantize launch + engine launch
+    # the protocol over the headline form: warm, cold (rotating weight
+    # copies), and the headline again as the control series
+    head = "r8_one" if m == 1 else "two"
+    prot = protocol({"headline": t["graphs"][head], "cold": t["graphs"]["cold"],
+                     "control": t["graphs"][head]})
     if m == 1:
         # headline: R8 weights, one launch per step (weights + fp32 rows read,
         # outputs written)
-        total, step_bytes, launch_bytes = t["total_r8_one"], plan.fused_bytes, plan.fused_bytes
+        total, step_bytes, launch_bytes = prot["headline"]["median"], plan.fused_bytes, plan.fused_bytes
         launch_s = total / K
         kernel = ("r8_matvec_kernel<true> (one launch per step over the R8 weights; every "
                   "workgroup quantizes the fp32 activation row of its matrix)")
         launches = 1
+        headline_series = "warm"
     else:
-        total, step_bytes, launch_bytes = t["total"], two_bytes, plan.engine_bytes
+        # the step's 131 MB of weights fit the 256 MB Infinity Cache: the
+        # cold series (rotating weight copies) is the headline
+        total, step_bytes, launch_bytes = prot["cold"]["median"], two_bytes, plan.engine_bytes
         launch_s = t["eng"]
         kernel = ("stream_flat_kernel (decode engine)" if m == 2 else
                   "stream_mfma_kernel (small-batch decode engine)")
         launches = 2
+        headline_series = "cold"
     value = step_bytes * K / total / 1e9
     achieved = launch_bytes / launch_s / 1e9
     out = {
@@ -429,9 +511,12 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
         "vs_baseline": None,
         "dtype": "int8 dot, fp32 scale (Q8_0)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init, no checkpoint)",
-        "config": {"workload": wl_desc, "batch": m, "products_per_step": sum(
+        "config": {"workload": wl_desc.format(K=K), "batch": m, "products_per_step": sum(
             b for _, _, _, b in stacks), "launches_per_step": launches,
-            "timing": "HIP graph of the K steps, one replay timed with HIP events",
+            "timing": ("HIP graph of the K sequential steps; 11 rounds, the first dropped, each "
+                       "round the best of 3 replays (HIP events) of the headline, cold and "
+                       "control series in turn; value = median of the rounds' bests "
+                       f"({headline_series} series)"),
             "weight_bytes_per_step": plan.w_bytes, "algorithmic_bytes_per_step": step_bytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(m * K / total, 1),
@@ -444,6 +529,14 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
     if m == 1:
         out["config"]["weights"] = ("Q8_0, repacked once at load (outside the timed region) into "
                                     "the row-interleaved R8 layout: the same bytes, moved")
+    out["protocol"] = {
+        "rounds": 11, "dropped": 1, "best_of": 3,
+        "headline_ms_per_step": {kk: round(prot["headline"][kk] / K * 1e3, 5)
+                                 for kk in ("median", "min", "max")},
+        "cold_ms_per_step": {kk: round(prot["cold"][kk] / K * 1e3, 5)
+                             for kk in ("median", "min", "max")},
+        "control": control_check(prot, "headline", "control"),
+        "gpu_clocks_before": clocks_before, "gpu_clocks_after": gpu_clocks()}
     # context: a plain streaming read of the same number of bytes per launch
     # (q8_read_probe; non-temporal 16-byte loads, no arithmetic)
     probe_bytes = (launch_bytes + 65535) // 65536 * 65536
@@ -456,9 +549,18 @@ def bench_decode(args, q, synth, stacks, m, name, wl_desc, n_steps_cfg):
         "kernel_over_probe": round(tp / launch_s, 4)}
     out["cold_reference"] = {
         "timing": f"the same steps reading {t['copies']} rotating copies of the weights "
-                  f"({t['copies'] * plan.w_bytes / 2**20:.0f} MiB, > the 256 MB Infinity Cache)",
-        "ms_per_step": round(t["total_cold"] / K * 1e3, 5),
-        "gbs": round(step_bytes * K / t["total_cold"] / 1e9, 1)}
+                  f"({t['copies'] * plan.w_bytes / 2**20:.0f} MiB, > the 256 MB Infinity Cache); "
+                  "median of the protocol's cold series",
+        "ms_per_step": round(prot["cold"]["median"] / K * 1e3, 5),
+        "gbs": round(step_bytes * K / prot["cold"]["median"] / 1e9, 1),
+        "pct_of_hbm_peak": round(step_bytes * K / prot["cold"]["median"] / 1e9 / HBM_PEAK_GBS * 100, 2)}
+    if m > 1:
+        out["warm_reference"] = {
+            "timing": "the same steps over one weight copy (cache-resident); median of the "
+                      "protocol's headline series",
+            "ms_per_step": round(prot["headline"]["median"] / K * 1e3, 5),
+            "gbs": round(step_bytes * K / prot["headline"]["median"] / 1e9, 1)}
+    plan._cold_w = []
     if m == 1:
         out["r8_two_launch_reference"] = {
             "timing": "R8 weights: quantize launch + one q8_0_matvec_r8_batched launch per step",
@@ -876,6 +978,124 @@ def run_extra(args, q, synth):
     return res
 
 
+def default_extras(args, q, synth):
+    """Keys of the default line beyond the decode step, timed in the same run
+    with the same protocol (fewer rounds): the vocabulary projection and the
+    30-layer MoE expert FFN at 1 and 16 tokens, layer after layer (as a model
+    runs it) and grouped."""
+    import torch
+    dev = "cuda"
+    out = {}
+    # --- the vocabulary projection 262144 x 2048 (571 MB > the Infinity Cache)
+    n, k = 262144, 2048
+    w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, "c5b", "w"))
+    x = q.q8_0_quantize_rows(synth.normal_f32_torch((1, k), 1.0, dev, 0, "c5b", "x"))
+    wr = q.q8_0_repack_r8(w, n, k)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    nbytes = q8_bytes(n, k) + q8_bytes(1, k) + 4 * n
+    reps = 20
+
+    def many(fn):
+        def body():
+            for _ in range(reps):
+                fn()
+        fn()
+        torch.cuda.synchronize()
+        return capture(body)
+    prot = protocol({"native": many(lambda: q.q8_0_matvec(w, x, n, k, y=y)),
+                     "r8": many(lambda: q.q8_0_matvec_r8(wr, x, n, k, y=y))}, rounds=6, best_of=3)
+    c5b = {"shape": [n, k], "bytes_per_launch": nbytes,
+           "timing": f"{reps} launches per graph; 6 rounds (first dropped), best of 3, median"}
+    for key, kern in (("native", "stream_pair_kernel"), ("r8", "r8_matvec_kernel<false>")):
+        tt = prot[key]["median"] / reps
+        c5b[key] = {"kernel": kern, "us": round(tt * 1e6, 3), "gbs": round(nbytes / tt / 1e9, 1),
+                    "frac": round(nbytes / tt / 1e9 / HBM_PEAK_GBS, 4),
+                    "tokens_per_s_equiv": round(1 / tt, 1)}
+    out["c5b_vocab_projection"] = c5b
+    del w, x, wr, y
+    # --- the MoE expert FFN: 30 layers of (n_embd 2048, n_ff 768, 128 experts, top-8)
+    L, E, n_embd, n_ff, U = 30, 128, 2048, 768, 8
+    wl = []
+    for l in range(L):
+        wug = q.q8_0_quantize_rows(synth.normal_f32_torch((E * 2 * n_ff, n_embd), 0.02, dev, 0,
+                                                          "c4", "ug", l))
+        wd = q.q8_0_quantize_rows(synth.normal_f32_torch((E * n_embd, n_ff), 0.02, dev, 0, "c4",
+                                                         "down", l))
+        wl.append(dict(wug=wug, wd=wd, wug_r8=q.q8_0_repack_r8(wug, E * 2 * n_ff, n_embd),
+                       wd_r8=q.q8_0_repack_r8(wd, E * n_embd, n_ff)))
+    torch.cuda.synchronize()
+    steps = 10
+    c4 = {"layers": L, "shape": {"n_embd": n_embd, "n_ff": n_ff, "n_expert": E, "n_used": U},
+          "timing": f"HIP graph of {steps} steps of all 30 layers; 6 rounds (first dropped), "
+                    "best of 3, median"}
+    for n_tok in (1, 16):
+        layers, active = [], 0
+        for l in range(L):
+            ids = synth.expert_ids(n_tok, U, E, 0, "c4", n_tok, "ids", l)
+            active += len(np.unique(ids)) * (q8_bytes(2 * n_ff, n_embd) + q8_bytes(n_embd, n_ff))
+            d = dict(wl[l], ids=torch.from_numpy(ids).to(dev),
+                     cw=torch.from_numpy(synth.combine_weights(n_tok, U, 0, "c4", n_tok, "cw", l)).to(dev),
+                     xf=synth.normal_f32_torch((n_tok, n_embd), 1.0, dev, 0, "c4", n_tok, "x", l),
+                     h=torch.empty((n_tok, U, n_ff), dtype=torch.float32, device=dev),
+                     out=torch.empty((n_tok, n_embd), dtype=torch.float32, device=dev),
+                     ws=q.moe_workspace(n_tok, n_embd, n_ff, E, U, dev),
+                     ws8=q.moe_r8_workspace(n_tok, n_embd, n_ff, E, U, dev))
+            d["r8"] = dict(w_up_gate_r8=d["wug_r8"], w_down_r8=d["wd_r8"], x=d["xf"], ids=d["ids"],
+                           cw=d["cw"], h=d["h"], out=d["out"], ws=d["ws8"])
+            layers.append(d)
+        ug = [dict(w_up_gate=d["wug"], x=d["xf"], ids=d["ids"], h=d["h"], ws=d["ws"]) for d in layers]
+        dn = [dict(w_down=d["wd"], h=d["h"], ids=d["ids"], cw=d["cw"], out=d["out"], ws=d["ws"])
+              for d in layers]
+        r8all = [d["r8"] for d in layers]
+
+        def chained_native():
+            for d in layers:
+                q.moe_up_gate_swiglu(d["wug"], d["xf"], d["ids"], n_embd, n_ff, E, d["ws"], h=d["h"])
+                q.moe_down_combine(d["wd"], d["h"], d["ids"], d["cw"], n_ff, n_embd, E, d["ws"],
+                                   out=d["out"])
+
+        def chained_r8():
+            for d in layers:
+                q.moe_r8_ffn_batched([d["r8"]], n_embd, n_ff, E)
+
+        def grouped_native():
+            q.moe_up_gate_swiglu_batched(ug, n_embd, n_ff, E)
+            q.moe_down_combine_batched(dn, n_ff, n_embd, E)
+
+        def grouped_r8():
+            q.moe_r8_ffn_batched(r8all, n_embd, n_ff, E)
+
+        forms = {"chained_native": (chained_native, "native rows, 2 launches per layer, layer "
+                                                    "after layer"),
+                 "chained_r8": (chained_r8, "R8 expert weights, 2 launches per layer, layer "
+                                            "after layer"),
+                 "grouped_native": (grouped_native, "native rows, all 30 layers in one up_gate "
+                                                    "and one down launch"),
+                 "grouped_r8": (grouped_r8, "R8 expert weights, all 30 layers in one call "
+                                            "(2 launches)")}
+        graphs = {}
+        for key, (fn, _) in forms.items():
+            fn()
+            torch.cuda.synchronize()
+
+            def body(fn=fn):
+                for _ in range(steps):
+                    fn()
+            graphs[key] = capture(body)
+        prot = protocol(graphs, rounds=6, best_of=3)
+        res = {"tokens": n_tok, "active_weight_bytes_per_step": active}
+        for key, (_, desc) in forms.items():
+            tt = prot[key]["median"] / steps
+            res[key] = {"timing": desc, "us_per_step": round(tt * 1e6, 2),
+                        "gbs": round(active / tt / 1e9, 1),
+                        "frac": round(active / tt / 1e9 / HBM_PEAK_GBS, 4),
+                        "tokens_per_s": round(n_tok / tt, 1)}
+        c4[f"tokens_{n_tok}"] = res
+        del layers, ug, dn, r8all, graphs
+    out["c4_moe_expert_ffn_30_layers"] = c4
+    return out
+
+
 def read_traffic(path):
     """HBM bytes per launch from a committed counter summary, or None when the
     kernel sources have changed since the counters were taken."""
@@ -949,6 +1169,8 @@ def main():
                     choices=["c1", "c2", "c3", "c4b1", "c4b16", "c4p", "c5a", "c5b", "copy", "readbw",
                              "ffn", "r8", "kq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default workload: leave out the vocabulary-projection and MoE keys")
     ap.add_argument("--read-bytes", type=int, default=0,
                     help="readbw workload: bytes per read launch (default 2 GiB)")
     ap.add_argument("--moe-mode", default="both", choices=["both", "layers", "grouped"],
@@ -981,11 +1203,15 @@ def main():
     if args.workload == "c2":
         out, plan = bench_decode(args, q, synth, LLAMA_STACKS, 1, "c2",
                                  "llama2-110m-shaped Q8_0 decode step, batch 1, 85 matvecs, "
-                                 "200 sequential steps", 200)
+                                 "{K} sequential steps timed", 200)
         stacks, m = LLAMA_STACKS, 1
+        del plan
+        if not args.no_extra:
+            out.update(default_extras(args, q, synth))
     elif args.workload == "c3":
         out, plan = bench_decode(args, q, synth, GPT2_STACKS, 8, "c3",
-                                 "gpt2-124m-shaped Q8_0 decode step, batch 8, 49 matmuls", 200)
+                                 "gpt2-124m-shaped Q8_0 decode step, batch 8, 49 matmuls, "
+                                 "{K} sequential steps timed", 200)
         stacks, m = GPT2_STACKS, 8
     else:
         print(json.dumps(run_extra(args, q, synth)))
