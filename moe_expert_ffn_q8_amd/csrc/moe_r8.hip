@@ -49,13 +49,13 @@ constexpr int kMrSlices = 8;              // 1 KB slices of a group in flight pe
 // (blocks of its residue, ascending); the caller adds lanes l, l^16, l^32.
 // EMIT (validation): every exact block sum is also written to srow[b], the
 // sums row of this lane's weight row (lanes that hold a whole sum).
-template <int POL, bool EMIT = false>
+template <int POL, bool EMIT = false, int SL = kMrSlices>
 struct GroupStream {
     __amdgpu_buffer_rsrc_t rs;
     int code0, scale0, nb;
     int32_t *srow = nullptr;
-    u32x4 c[kMrSlices];
-    uint32_t sb[kMrSlices];
+    u32x4 c[SL];
+    uint32_t sb[SL];
 
     __device__ __forceinline__ void init(const uint8_t *group, int nb_, int lane, bool live)
     {
@@ -68,10 +68,10 @@ struct GroupStream {
     __device__ __forceinline__ void issue(int i0)
     {
 #pragma unroll
-        for (int u = 0; u < kMrSlices; ++u)
+        for (int u = 0; u < SL; ++u)
             c[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, code0 + 1024 * (i0 + u), 0, POL);
 #pragma unroll
-        for (int u = 0; u < kMrSlices; ++u)
+        for (int u = 0; u < SL; ++u)
             sb[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, scale0 + 64 * (i0 + u), 0, POL);
     }
     // every slice is computed (a branch would make the compiler wait for each
@@ -81,7 +81,7 @@ struct GroupStream {
     {
         const int half = lane & 1, bs = lane >> 4;
 #pragma unroll
-        for (int u = 0; u < kMrSlices; ++u) {
+        for (int u = 0; u < SL; ++u) {
             const int b = 4 * (i0 + u) + bs;
             const bool live = b < nb;
             const int bb = live ? b : nb - 1;
@@ -103,7 +103,7 @@ struct GroupStream {
         float acc = 0.0f;
         for (int i0 = 0;;) {
             compute(i0, lane, xc, xd16, acc);
-            i0 += kMrSlices;
+            i0 += SL;
             if (i0 >= slices) break;
             issue(i0);
         }
@@ -120,7 +120,7 @@ struct GroupStream {
 constexpr int kDnG = 4;
 
 // EMIT (validation): block sums to sbase[(8q + r) * nb + b] for group q, row r.
-template <int POL, bool EMIT = false>
+template <int POL, bool EMIT = false, int G = kDnG>
 struct MultiStream {
     __amdgpu_buffer_rsrc_t rs;
     int nb, S, total, gb;
@@ -133,9 +133,9 @@ struct MultiStream {
         nb = nb_;
         gb = kGB * nb;
         S = (nb + 3) >> 2;
-        total = kDnG * S;
+        total = G * S;
         rs = __builtin_amdgcn_make_buffer_rsrc((void *)wave_uniform(base), 0,
-                                               wave_uniform(kDnG * gb), kBufferWord3);
+                                               wave_uniform(G * gb), kBufferWord3);
     }
     __device__ __forceinline__ void issue(int j0, int lane)
     {
@@ -155,7 +155,7 @@ struct MultiStream {
         }
     }
     __device__ __forceinline__ void compute(int j0, int lane, const uint8_t *xc,
-                                            const uint16_t *xd16, float (&acc)[kDnG])
+                                            const uint16_t *xd16, float (&acc)[G])
     {
         const int half = lane & 1, bs = lane >> 4;
 #pragma unroll
@@ -175,15 +175,15 @@ struct MultiStream {
             const float dw = live ? half_bits_to_float(sb[u]) : 0.0f;
             const float p = dw * half_bits_to_float(xd16[bb]);
 #pragma unroll
-            for (int g = 0; g < kDnG; ++g)
+            for (int g = 0; g < G; ++g)
                 if (q == g) acc[g] = fmaf(p, (float)s, acc[g]);
         }
     }
     __device__ __forceinline__ void run(int lane, const uint8_t *xc, const uint16_t *xd16,
-                                        float (&acc)[kDnG])
+                                        float (&acc)[G])
     {
 #pragma unroll
-        for (int g = 0; g < kDnG; ++g) acc[g] = 0.0f;
+        for (int g = 0; g < G; ++g) acc[g] = 0.0f;
         for (int j0 = 0;;) {
             compute(j0, lane, xc, xd16, acc);
             j0 += kMrSlices;
@@ -191,7 +191,7 @@ struct MultiStream {
             issue(j0, lane);
         }
 #pragma unroll
-        for (int g = 0; g < kDnG; ++g) {
+        for (int g = 0; g < G; ++g) {
             acc[g] += __shfl_xor(acc[g], 16);
             acc[g] += __shfl_xor(acc[g], 32);
         }
@@ -336,7 +336,9 @@ struct MrDnArgs {
     int32_t *sums;             // validation: [slot][n_embd][n_ff/32] (layer 0 only)
 };
 
-template <int POL, bool EMIT>
+// G: 8-row groups of the output per workgroup (4 normally; 1 when a launch
+// would otherwise have too few workgroups to keep the memory system busy).
+template <int POL, bool EMIT, int G>
 __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 {
     const int tid = threadIdx.x;
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
     const int lane = tid & 63;
     const int li = wave_uniform((int)blockIdx.x / a.wg_per_layer);
     const int rel = (int)blockIdx.x - li * a.wg_per_layer;
-    const int quads = a.n_embd / (8 * kDnG);      // 32-row bands of the output
+    const int quads = a.n_embd / (8 * G);      // bands of 8*G output rows
     const int t = rel / quads;
     const int g = rel - t * quads;
     const auto &L = a.layer[li];
@@ -357,13 +359,13 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
         const int v = L.ids[t * U + u];
         bad |= (v < 0 || v >= a.n_expert);
     }
-    float *orow = L.out + (int64_t)t * a.n_embd + 8 * kDnG * g;
+    float *orow = L.out + (int64_t)t * a.n_embd + 8 * G * g;
     if (bad) {
-        if (tid < 8 * kDnG) orow[tid] = __builtin_nanf("");
+        if (tid < 8 * G) orow[tid] = __builtin_nanf("");
         return;
     }
     const int e = wave_uniform(L.ids[t * U + wave]);
-    const uint8_t *gbase = L.w + ((int64_t)e * (a.n_embd / 8) + kDnG * g) * kGB * nb;
+    const uint8_t *gbase = L.w + ((int64_t)e * (a.n_embd / 8) + G * g) * kGB * nb;
 
     // this wave's q(h) row in its own LDS region: loads first, then the
     // weights, then the LDS writes (waves do not share these regions)
@@ -381,9 +383,9 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
         hv[i] = *(const uint16_t *)(hq + (e2 >> 4) * kBlockBytes + 2 + 2 * (e2 & 15));
     }
     const uint32_t hs = *(const uint16_t *)(hq + min(lane, nb - 1) * kBlockBytes);
-    MultiStream<POL, EMIT> ms;
+    MultiStream<POL, EMIT, G> ms;
     ms.init(gbase, nb);
-    if (EMIT) ms.sbase = a.sums + ((int64_t)(t * U + wave) * a.n_embd + 8 * kDnG * g) * nb;
+    if (EMIT) ms.sbase = a.sums + ((int64_t)(t * U + wave) * a.n_embd + 8 * G * g) * nb;
     __builtin_amdgcn_sched_barrier(0);
     ms.issue(0, lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -395,16 +397,16 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
     if (lane < nb) xd16[lane] = (uint16_t)hs;
     wave_lds_sync();
 
-    float acc[kDnG];
+    float acc[G];
     ms.run(lane, xc, xd16, acc);
     if ((lane & 0x31) == 0) {
 #pragma unroll
-        for (int q = 0; q < kDnG; ++q) ybuf[8 * kDnG * wave + 8 * q + ((lane >> 1) & 7)] = acc[q];
+        for (int q = 0; q < G; ++q) ybuf[8 * G * wave + 8 * q + ((lane >> 1) & 7)] = acc[q];
     }
     __syncthreads();
-    if (tid < 8 * kDnG) {
+    if (tid < 8 * G) {
         float o = 0.0f;
-        for (int u = 0; u < U; ++u) o = fmaf(L.cw[t * U + u], ybuf[8 * kDnG * u + tid], o);
+        for (int u = 0; u < U; ++u) o = fmaf(L.cw[t * U + u], ybuf[8 * G * u + tid], o);
         orow[tid] = o;
     }
 }
@@ -479,7 +481,7 @@ int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expe
     const size_t dn_lds = (size_t)16 * ((34 * (n_ff / 32) + 15) / 16 * 16) + 16 * 8 * kDnG * 4;
     if (ug_lds > (size_t)max_lds_bytes() || dn_lds > (size_t)max_lds_bytes()) return -4;
     const int64_t ug_wgs = kMoeMaxLayers * n_tok * n_used * (n_ff / 32);
-    const int64_t dn_wgs = kMoeMaxLayers * n_tok * (n_embd / (8 * kDnG));
+    const int64_t dn_wgs = kMoeMaxLayers * n_tok * (n_embd / 8);
     return (ug_wgs > 0x7fffffffLL || dn_wgs > 0x7fffffffLL) ? -4 : 0;
 }
 
@@ -550,17 +552,34 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
         dn.n_embd = (int)n_embd;
         dn.n_ff = (int)n_ff;
         dn.n_expert = (int)n_expert;
-        dn.wg_per_layer = (int)(n_tok * (n_embd / (8 * kDnG)));
+        // one group per workgroup where a launch of 4-group workgroups would be
+        // small (one token of one layer: 64 workgroups for 256 CUs; 13.4 MB
+        // then stream with 4x the workgroups, each wave's group in flight at once)
+        const int dn_g = (int64_t)nl * n_tok * (n_embd / (8 * kDnG)) < 512 ? 1 : kDnG;
+        dn.wg_per_layer = (int)(n_tok * (n_embd / (8 * dn_g)));
         dn.sums = dn_sums;
         const size_t dn_lds = (size_t)16 * ((34 * (n_ff / 32) + 15) / 16 * 16) + 16 * 8 * kDnG * 4;
         const dim3 dn_grid((unsigned)(nl * dn.wg_per_layer)), dn_block((unsigned)(64 * n_used));
-        if (dn_sums)
-            hipLaunchKernelGGL((moe_r8_down_kernel<0, true>), dn_grid, dn_block, dn_lds, stream, dn);
-        else if (reuse)
-            hipLaunchKernelGGL((moe_r8_down_kernel<0, false>), dn_grid, dn_block, dn_lds, stream, dn);
-        else
-            hipLaunchKernelGGL((moe_r8_down_kernel<kCacheNT, false>), dn_grid, dn_block, dn_lds,
+        if (dn_g == 1) {
+            if (dn_sums)
+                hipLaunchKernelGGL((moe_r8_down_kernel<0, true, 1>), dn_grid, dn_block, dn_lds, stream,
+                                   dn);
+            else if (reuse)
+                hipLaunchKernelGGL((moe_r8_down_kernel<0, false, 1>), dn_grid, dn_block, dn_lds,
+                                   stream, dn);
+            else
+                hipLaunchKernelGGL((moe_r8_down_kernel<kCacheNT, false, 1>), dn_grid, dn_block, dn_lds,
+                                   stream, dn);
+        } else if (dn_sums) {
+            hipLaunchKernelGGL((moe_r8_down_kernel<0, true, kDnG>), dn_grid, dn_block, dn_lds, stream,
+                               dn);
+        } else if (reuse) {
+            hipLaunchKernelGGL((moe_r8_down_kernel<0, false, kDnG>), dn_grid, dn_block, dn_lds, stream,
+                               dn);
+        } else {
+            hipLaunchKernelGGL((moe_r8_down_kernel<kCacheNT, false, kDnG>), dn_grid, dn_block, dn_lds,
                                stream, dn);
+        }
         if (hipGetLastError() != hipSuccess) return -6;
     }
     return 0;
