@@ -503,9 +503,12 @@ int moe_down_combine_batched(const moe_down_desc *descs, int64_t n_desc,
  * as n_expert*2*n_ff rows of n_embd values, w_down_r8 = the down tensor as
  * n_expert*n_embd rows of n_ff values.  h [n_tok][n_used][n_ff] and out
  * [n_tok][n_embd] are written; x, ids, cw as for the native calls.
- * Up to 16 tokens (decode): two launches per call, several layers of one
- * shape per launch; each slot streams its expert's rows (repeated experts
- * across tokens are read once per slot).
+ * Up to 16 tokens (decode), several layers of one shape per launch: at one
+ * token two launches per call, each slot streaming its expert's rows; at 2..16
+ * tokens three (up_gate, down, the combine of the native path), each active
+ * expert's rows streamed once per call for all of its slots (4 slots per pass
+ * over the rows).  h and out are the same bits either way: per slot the
+ * arithmetic and its order do not depend on how slots are grouped.
  * More than 16 tokens (prompt evaluation), where n_embd % 128 == 0 and
  * n_ff % 128 == 0 and the limits of the native prefill path hold: per layer
  * routing into tiles of up to 32 slots, then the two products on the int8
@@ -542,13 +545,13 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same kernels, h and out bit for bit,
  * with the workspaces taken from an array the library holds on each device
- * (8 MiB per device, held until the process ends; looked up once per device
+ * (48 MiB per device, held until the process ends; looked up once per device
  * at the first call on it, which is the only call that can return Q8_E_HIP
  * for that lookup).  The call allocates and frees nothing.
  *   descs  as for moe_r8_ffn_batched; ws and ws_bytes are ignored.
  * Decode shapes only: n_tok <= 16 (more tokens: Q8_E_UNSUPPORTED).  Layer i
  * uses the i-th slice of moe_r8_workspace_bytes(...) rounded up to 256 bytes;
- * n_desc slices beyond 8 MiB: Q8_E_WORKSPACE (split the call).  Every call on
+ * n_desc slices beyond 48 MiB: Q8_E_WORKSPACE (split the call).  Every call on
  * a device shares that device's array and leaves its contents behind: two
  * calls that may run at the same time on one device race (order them on one
  * stream).  Nothing in the array needs clearing: every call rewrites what it
@@ -633,8 +636,8 @@ int q8v_moe_hq(const q8_0_block *w_down, const float *h, const int32_t *ids, con
  * workspace) with the validation outputs of both products: ug_sums and
  * dn_sums laid out as the sums of q8v_moe_up_gate and q8v_moe_hq, hq the
  * quantized h rows the down product used, and the routing (counts, offsets,
- * pairs as in q8v_moe_up_gate) on the grouped path only (more than 16
- * tokens; the decode kernels stream each slot's expert on its own:
+ * pairs as in q8v_moe_up_gate) the kernels grouped the slots by (2 tokens or
+ * more; at one token each slot streams its expert on its own:
  * Q8_E_UNSUPPORTED there).  Each output optional (NULL). */
 int q8v_moe_r8_ffn(const moe_r8_ffn_desc *desc, int64_t n_tok, int64_t n_embd, int64_t n_ff,
                    int64_t n_expert, int64_t n_used, int32_t *ug_sums, int32_t *dn_sums,

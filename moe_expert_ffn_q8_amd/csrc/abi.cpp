@@ -752,9 +752,8 @@ int q8v_moe_r8_ffn(const moe_r8_ffn_desc *desc, int64_t n_tok, int64_t n_embd, i
     if (int rc = r8_ffn_checks(desc, 1, n_tok, n_embd, n_ff, n_expert, n_used, true)) return rc;
     if (int rc = route_outputs(counts, offsets, pairs)) return rc;
     if (!aligned(ug_sums, 4) || !aligned(dn_sums, 4) || !aligned(hq, 2)) return Q8_E_ALIGN;
-    // the decode kernels serve every slot on its own: no grouping to report
-    if (counts && !q8::moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used))
-        return Q8_E_UNSUPPORTED;
+    // one token: every slot is served on its own, no grouping to report
+    if (counts && n_tok == 1) return Q8_E_UNSUPPORTED;
     if (n_tok == 0) return Q8_OK;
     q8::MoeEmit eu = {ug_sums, nullptr, counts, offsets, pairs};
     q8::MoeEmit ed = {dn_sums, hq, nullptr, nullptr, nullptr};

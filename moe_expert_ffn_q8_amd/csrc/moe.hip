@@ -925,6 +925,22 @@ int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, 
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
+int launch_moe_combine_layers(const MoeCombineLayer *l, int n_layers, int64_t n_tok,
+                              int64_t n_rows, int64_t n_used, int64_t n_expert, hipStream_t stream)
+{
+    if (n_tok == 0 || n_layers == 0) return 0;
+    if (n_tok > 65535 || n_layers > kMoeMaxLayers) return -4;
+    CbParams cb;
+    memset(&cb, 0, sizeof(cb));
+    for (int i = 0; i < n_layers; ++i) cb.layer[i] = CbLayer{l[i].yslot, l[i].ids, l[i].cw, l[i].out};
+    cb.n_rows = (int)n_rows;
+    cb.n_used = (int)n_used;
+    cb.n_expert = (int)n_expert;
+    dim3 cgrid((unsigned)((n_rows + 255) / 256), (unsigned)n_tok, (unsigned)n_layers);
+    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, cb);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 size_t moe_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                     int64_t n_used)
 {

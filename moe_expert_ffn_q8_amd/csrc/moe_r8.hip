@@ -10,7 +10,7 @@
 // repacking bug): the combined up_gate tensor as n_expert*2*n_ff rows, the
 // down tensor as n_expert*n_embd rows (every expert starts on a group).
 //
-// Two launches per call (several layers of one shape per launch):
+// One token: two launches per call (several layers of one shape per launch):
 //  1. up_gate: workgroup = (slot, 32 columns of h), 8 waves, one 8-row group
 //     each: waves 0..3 the gate rows, waves 4..7 the up rows of the same
 //     columns.  The token row is quantized into LDS by the workgroup (bytes of
@@ -21,9 +21,10 @@
 //     slot of the token streaming that slot's expert rows (4 consecutive groups
 //     as one stream of slices) against the slot's quantized h row; the n_used
 //     results are combined in LDS in ascending u.
-// Each slot streams its expert's rows itself: at one token the 8 slots name
-// distinct experts; with several tokens repeated experts are read once per
-// slot (the expert-major kernels of moe.hip read them once per call).
+// At one token the slots name distinct experts and each streams its own.
+// Several tokens: three launches (the expert-major kernels below, then the
+// combine of the native path), each active expert's rows streamed once per
+// call for all of its slots.
 //
 // Ids outside [0, n_expert): the up_gate workgroup of slot 0 / columns 0 sets
 // the error word of the workspace (0 or 1, every call); such a slot's h row is
@@ -31,6 +32,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "q8_device.h"
 #include "q8_internal.h"
@@ -216,6 +218,8 @@ struct MrUgArgs {
     int n_used, n_slots, n_embd, n_ff, n_expert;
     int wg_per_layer;
     int32_t *sums;             // validation: [slot][2*n_ff][n_embd/32] (layer 0 only)
+    int32_t *counts, *pairs;   // validation, several tokens: the expert-major grouping
+    int ug_cols;               // several tokens: 8-column groups per wave
 };
 
 template <int POL, bool EMIT>
@@ -411,6 +415,462 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// several tokens: each active expert's rows streamed once per call
+//
+// With more than one token, slots repeat experts (at 16 tokens, 8 of 128
+// experts each, about a third of the slots).  The workgroups keep a
+// (slot, part) layout, but the workgroup of slot s works only when s is the
+// first slot naming its expert e (one ballot pass of wave 0 over the ids): it
+// then serves every slot routed to e, ascending, kGtMax slots against each
+// pass over its part of the rows; the other workgroups exit.  Each wave
+// streams several 8-row groups as one rolling stream (slice u of the next
+// batch is issued as soon as slice u of the current one is consumed, so about
+// 8 KB stay in flight per wave), and needs no other wave after the rows are
+// staged: up_gate pairs a gate group with the up group of the same 8 columns
+// in one wave, and the down kernel quantizes h itself.  Per slot the
+// arithmetic and its order are those of the one-token kernels above, so h,
+// q(h) and the outputs are the same bits.  The down kernel writes one fp32
+// row per slot to the workspace and the combine kernel of the native path
+// (ascending u) forms out.
+
+#ifndef Q8_GT_SLICES
+#define Q8_GT_SLICES 16
+#endif
+#ifndef Q8_GT_UG_OCC
+#define Q8_GT_UG_OCC 2
+#endif
+#ifndef Q8_GT_DN_OCC
+#define Q8_GT_DN_OCC 4
+#endif
+constexpr int kGtMax = 4;          // slots per pass over an expert's rows
+constexpr int kGtIdRegs = 4;       // ids held in registers per lane of wave 0
+#ifndef Q8_GT_DN_SLICES
+#define Q8_GT_DN_SLICES 6
+#endif
+constexpr int kGtSlices = Q8_GT_SLICES;      // up_gate: 1 KB slices in flight per wave
+constexpr int kGtDnSlices = Q8_GT_DN_SLICES; // down
+#ifndef Q8_GT_UG_WAVES
+#define Q8_GT_UG_WAVES 4
+#endif
+#ifndef Q8_GT_DN_WAVES
+#define Q8_GT_DN_WAVES 4
+#endif
+constexpr int kGtUgWaves = Q8_GT_UG_WAVES;        // waves of an up_gate workgroup
+constexpr int kGtDnWaves = Q8_GT_DN_WAVES;        // waves of a down workgroup
+constexpr int kGtOwnPre = 2;                      // blocks of the own row per 8 lanes, prefetched
+
+struct GtPick {
+    int count;                     // slots served (0: not the owner)
+    int less;                      // in-range slots with an id below e
+};
+
+// Wave 0 only: the ids in registers (loaded before anything else).
+struct GtIds {
+    int v[kGtIdRegs];
+};
+
+__device__ __forceinline__ void gt_load_ids(const int32_t *ids, int n_slots, GtIds &g)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int c = 0; c < kGtIdRegs; ++c) g.v[c] = ids[min(c * kWave + lane, n_slots - 1)];
+}
+
+// Wave 0 only.  list[] gets the slots naming e in ascending order.
+__device__ __forceinline__ void gt_pick(const int32_t *ids, const GtIds &g, int n_slots,
+                                        int n_expert, int s, int e, int *list, GtPick &pk)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int cnt = 0, less = 0;
+    bool first = true;
+    auto step = [&](int i, int id) {
+        const bool in = i < n_slots;
+        const bool hit = in && id == e;
+        const uint64_t m = __ballot(hit);
+        first &= __ballot(hit && i < s) == 0;
+        less += __popcll(__ballot(in && id >= 0 && id < e));
+        if (hit) list[cnt + __popcll(m & __lanemask_lt())] = i;
+        cnt += __popcll(m);
+    };
+#pragma unroll
+    for (int c = 0; c < kGtIdRegs; ++c)
+        if (c * kWave < n_slots) step(c * kWave + lane, g.v[c]);
+    for (int base = kGtIdRegs * kWave; base < n_slots; base += kWave) {
+        const int i = base + lane;
+        step(i, ids[min(i, n_slots - 1)]);
+    }
+    if (lane == 0) {
+        pk.count = first ? cnt : 0;
+        pk.less = less;
+    }
+}
+
+__host__ __device__ inline int gt_row_stride(int nb)
+{
+    return (34 * nb + 15) / 16 * 16;
+}
+
+// kGtMax activation rows, then the slot list
+size_t gt_lds(int64_t n_slots, int64_t nb)
+{
+    return (size_t)kGtMax * gt_row_stride((int)nb) + (size_t)n_slots * 4;
+}
+
+// Quantize one 32-value block (4 values in each of 8 lanes) into LDS row xc
+// (codes realigned to 32 bytes per block, binary16 scale bits at +32*nb).
+__device__ __forceinline__ void gt_put(uint8_t *xc, int nb, int b, float4 v)
+{
+    const int q8 = threadIdx.x & 7;
+    uint32_t codes, dbits;
+    quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+    if (b < nb) {
+        *(uint32_t *)(xc + 32 * b + 4 * q8) = codes;
+        if (q8 == 0) ((uint16_t *)(xc + 32 * nb))[b] = (uint16_t)dbits;
+    }
+}
+
+// The first kGtOwnPre*QB blocks of a row (QB = threads/8), 4 values per lane,
+// loaded into registers ahead of the ownership scan.
+template <int QB>
+__device__ __forceinline__ void gt_prefetch(const float *row, int nb, float4 (&v)[kGtOwnPre])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kGtOwnPre; ++i)
+        v[i] = *(const float4 *)(row + 32 * min((tid >> 3) + QB * i, nb - 1) + 4 * (tid & 7));
+}
+
+// Rows m = 0..ct-1 of a pass (fp32 row m at row_of(m)) into LDS, QB blocks
+// per pass of the workgroup; row 0 may already be in registers (have_own:
+// gt_prefetch of it, nb <= kGtOwnPre*QB).
+template <int QB, class RowOf>
+__device__ __forceinline__ void gt_stage(uint8_t *xr, int rstride, int nb, int ct, bool have_own,
+                                         const float4 (&vown)[kGtOwnPre], RowOf row_of)
+{
+    const int tid = threadIdx.x, q8 = tid & 7;
+    if (have_own) {
+#pragma unroll
+        for (int i = 0; i < kGtOwnPre; ++i) gt_put(xr, nb, (tid >> 3) + QB * i, vown[i]);
+    }
+    for (int bi = (tid >> 3) + (have_own ? nb : 0); bi < ct * nb; bi += QB) {
+        const int m = bi / nb;
+        const int b = bi - m * nb;
+        gt_put(xr + m * rstride, nb, b, *(const float4 *)(row_of(m) + 32 * b + 4 * q8));
+    }
+}
+
+// A wave's stream over ng 8-row groups of one buffer resource (group g at
+// byte offset goff_of(g)) against CT activation rows in LDS (row m at xr +
+// m*rstride, as gt_put leaves them).  A group is B batches of 8 slices of
+// GroupStream's layout (slices past its last are issued out of range: zeros,
+// no memory traffic, and masked).  Slice u of the next batch -- of this group
+// or the next -- is issued right after slice u of the current batch has been
+// consumed.  The first batch is issued by the caller: issue_batch(goff_of(0)).
+template <int POL, bool EMIT, int SL>
+struct GatherStream {
+    __amdgpu_buffer_rsrc_t rs;
+    int nb, S, B, size, code0, scale0;
+    u32x4 c[SL];
+    uint32_t sb[SL];
+
+    __device__ __forceinline__ void init(const uint8_t *base, int nb_, int bytes, int lane)
+    {
+        nb = nb_;
+        S = (nb + 3) >> 2;
+        B = (S + SL - 1) / SL;
+        size = bytes;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)wave_uniform(base), 0, wave_uniform(bytes),
+                                               kBufferWord3);
+        code0 = 16 * nb + 16 * lane;
+        scale0 = 2 * (lane >> 1);
+    }
+    // slice i of the group at goff (goff < 0: none) into slot u, scale first
+    __device__ __forceinline__ void issue_slice(int goff, int i, int u)
+    {
+        const bool in = goff >= 0 && i < S;
+        sb[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, in ? goff + scale0 + 64 * i : size, 0, POL);
+        c[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? goff + code0 + 1024 * i : size, 0, POL);
+    }
+    __device__ __forceinline__ void issue_batch(int goff)
+    {
+#pragma unroll
+        for (int u = 0; u < SL; ++u) issue_slice(goff, u, u);
+    }
+    // epi(g, acc): the group's CT row sums, lanes with (lane & 0x31) == 0
+    // holding row (lane >> 1) & 7; srow_of(g, m): the EMIT sums row
+    template <int CT, class GoffOf, class SrowOf, class Epi>
+    __device__ __forceinline__ void run(int ng, int lane, const uint8_t *xr, int rstride,
+                                        GoffOf goff_of, SrowOf srow_of, Epi epi)
+    {
+        const int half = lane & 1, bs = lane >> 4;
+        for (int g = 0; g < ng; ++g) {
+            int32_t *srows[CT];
+            float acc[CT];
+#pragma unroll
+            for (int m = 0; m < CT; ++m) {
+                srows[m] = EMIT ? srow_of(g, m) : nullptr;
+                acc[m] = 0.0f;
+            }
+            const int goff_next = g + 1 < ng ? goff_of(g + 1) : -1;
+            const int goff_cur = goff_of(g);
+            for (int kb = 0; kb < B; ++kb) {
+                const bool last = kb + 1 == B;
+                const int noff = last ? goff_next : goff_cur;
+                const int ni0 = last ? 0 : SL * (kb + 1);
+#pragma unroll
+                for (int u = 0; u < SL; ++u) {
+                    const int b = 4 * (SL * kb + u) + bs;
+                    const bool live = b < nb;
+                    const int bb = live ? b : nb - 1;
+                    const float dw = live ? half_bits_to_float(sb[u]) : 0.0f;
+                    const u32x4 cw = c[u];
+#pragma unroll
+                    for (int m = 0; m < CT; ++m) {
+                        const uint8_t *xc = xr + m * rstride;
+                        const u32x4 xv = *(const u32x4 *)(xc + 32 * bb + 16 * half);
+                        int s = sdot4(cw.x, xv.x, 0);
+                        s = sdot4(cw.y, xv.y, s);
+                        s = sdot4(cw.z, xv.z, s);
+                        s = sdot4(cw.w, xv.w, s);
+                        s += __builtin_amdgcn_mov_dpp(s, 0xB1, 0xF, 0xF, false);   // the other half
+                        if (EMIT && half == 0 && live) srows[m][b] = s;
+                        const float dx = half_bits_to_float(((const uint16_t *)(xc + 32 * nb))[bb]);
+                        acc[m] = fmaf(dw * dx, (float)s, acc[m]);
+                        // pin the sum into its slice (else the compiler sinks the
+                        // float work of every slice below the next issues)
+                        asm volatile("" : "+v"(acc[m]));
+                    }
+                    issue_slice(noff, ni0 + u, u);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < CT; ++m) {
+                acc[m] += __shfl_xor(acc[m], 16);
+                acc[m] += __shfl_xor(acc[m], 32);
+            }
+            epi(g, acc);
+        }
+    }
+};
+
+// Dispatch a pass of ct (1..kGtMax) rows to the instance for that count.
+template <class F>
+__device__ __forceinline__ void gt_dispatch(int ct, F f)
+{
+    switch (ct) {
+        case 1: f(std::integral_constant<int, 1>()); break;
+        case 2: f(std::integral_constant<int, 2>()); break;
+        case 3: f(std::integral_constant<int, 3>()); break;
+        default: f(std::integral_constant<int, 4>()); break;
+    }
+}
+
+// up_gate: workgroup = (slot, part of W*a.ug_cols 8-column groups of h, W the
+// waves); wave w takes column groups cg = W*(a.ug_cols*part + j) + w (j < a.ug_cols),
+// streaming for each the gate group cg, then the up group n_ff/8 + cg, and
+// writes h of those 8 columns itself.
+template <int POL, bool EMIT>
+__global__ __launch_bounds__(kGtUgWaves * kWave, Q8_GT_UG_OCC) void moe_r8_up_gate_gather_kernel(const MrUgArgs a)
+{
+    constexpr int W = kGtUgWaves, T = W * kWave, QB = T / 8;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int li = wave_uniform((int)blockIdx.x / a.wg_per_layer);
+    const int rel = (int)blockIdx.x - li * a.wg_per_layer;
+    const int cgs = a.n_ff / 8;                              // 8-column groups
+    const int parts = (cgs + W * a.ug_cols - 1) / (W * a.ug_cols);
+    const int slot = rel / parts;
+    const int part = rel - slot * parts;
+    const auto &L = a.layer[li];
+    const int nb = a.n_embd / 32;
+
+    // small loads first: the ids of the ownership scan and this slot's token
+    // row (the first row served when the slot owns its expert)
+    GtIds gi;
+    if (wave == 0) gt_load_ids(L.ids, a.n_slots, gi);
+    float4 vown[kGtOwnPre];
+    gt_prefetch<QB>(L.x + (int64_t)(slot / a.n_used) * a.n_embd, nb, vown);
+    const int e = wave_uniform(L.ids[slot]);
+    const bool valid = e >= 0 && e < a.n_expert;
+
+    if (slot == 0 && part == 0 && wave == 0) {
+        int bad = 0;
+        for (int s = lane; s < a.n_slots; s += kWave) {
+            const int v = L.ids[s];
+            bad |= (v < 0 || v >= a.n_expert);
+        }
+        bad = __any(bad);
+        if (lane == 0) *(int32_t *)L.ws = bad;
+    }
+    const int col0 = 8 * W * a.ug_cols * part;
+    const int ncol = min(8 * W * a.ug_cols, a.n_ff - col0);
+    if (!valid) {
+        for (int i = tid; i < ncol; i += T)
+            L.h[(int64_t)slot * a.n_ff + col0 + i] = __builtin_nanf("");
+        return;
+    }
+
+    extern __shared__ __align__(16) uint8_t mr_lds[];
+    const int rstride = gt_row_stride(nb);
+    uint8_t *xr = mr_lds;                                     // kGtMax token rows
+    int *list = (int *)(mr_lds + kGtMax * rstride);           // [n_slots]
+    __shared__ GtPick pk;
+    if (wave == 0) gt_pick(L.ids, gi, a.n_slots, a.n_expert, slot, e, list, pk);
+    __syncthreads();
+    const int cnt = pk.count;
+    if (cnt == 0) return;
+    if (EMIT && a.counts && part == 0) {
+        if (tid == 0) a.counts[e] = cnt;
+        for (int i = tid; i < cnt; i += T) a.pairs[pk.less + i] = list[i];
+    }
+
+    // this wave's column groups: a prefix j < ncg of cg = cg0 + W*j
+    const int cg0 = W * a.ug_cols * part + wave;
+    const int ncg = cg0 < cgs ? min(a.ug_cols, (cgs - 1 - cg0) / W + 1) : 0;
+    const int gb = kGB * nb;
+    // stream g: column group j = g/2, gate (g even) or up (g odd); offsets
+    // from the expert's first group
+    auto goff_of = [&](int g) { return ((g & 1) * cgs + cg0 + W * (g >> 1)) * gb; };
+    GatherStream<POL, EMIT, kGtSlices> gs;
+    gs.init(L.w + (int64_t)e * 2 * cgs * gb, nb, 2 * cgs * gb, lane);
+    const int r = (lane >> 1) & 7;
+
+    for (int c0 = 0; c0 < cnt; c0 += kGtMax) {
+        const int ct = min(kGtMax, cnt - c0);
+        gs.issue_batch(ncg > 0 ? goff_of(0) : -1);
+        gt_stage<QB>(xr, rstride, nb, ct, c0 == 0 && nb <= kGtOwnPre * QB, vown, [&](int m) {
+            return L.x + (int64_t)(list[c0 + m] / a.n_used) * a.n_embd;
+        });
+        __syncthreads();
+        if (ncg > 0) {
+            gt_dispatch(ct, [&](auto ctc) {
+                constexpr int CT = decltype(ctc)::value;
+                float accg[CT];
+                auto srow_of = [&](int g, int m) {
+                    const int row = 8 * ((g & 1) * cgs + cg0 + W * (g >> 1)) + r;
+                    return a.sums + ((int64_t)list[c0 + m] * 2 * a.n_ff + row) * nb;
+                };
+                gs.template run<CT>(2 * ncg, lane, xr, rstride, goff_of, srow_of,
+                                    [&](int g, float (&acc)[CT]) {
+                    if (!(g & 1)) {
+#pragma unroll
+                        for (int m = 0; m < CT; ++m) accg[m] = acc[m];
+                    } else if ((lane & 0x31) == 0) {
+                        const int col = 8 * (cg0 + W * (g >> 1)) + r;
+#pragma unroll
+                        for (int m = 0; m < CT; ++m) {
+                            const float gv = accg[m];
+                            L.h[(int64_t)list[c0 + m] * a.n_ff + col] = gv / (1.0f + expf(-gv)) * acc[m];
+                        }
+                    }
+                });
+            });
+        }
+        if (c0 + kGtMax < cnt) __syncthreads();   // the LDS rows are reused by the next pass
+    }
+}
+
+// Down for several tokens: workgroup = (slot, band of W*a.dn_groups*8 output
+// rows), wave w streaming a.dn_groups consecutive 8-row groups; the owner of the
+// slot's expert quantizes the h rows of every slot routed to it (the rule of
+// q8_0_quantize_rows) and writes their fp32 rows y[s][band] to the workspace.
+
+struct MrGdArgs {
+    struct Layer {
+        const uint8_t *w;      // R8 down
+        const int32_t *ids;
+        const float *h;        // [n_slots][n_ff]
+        float *yslot;          // [n_slots][n_embd]
+    } layer[kMoeMaxLayers];
+    int n_slots, n_embd, n_ff, n_expert;
+    int dn_groups;             // 8-row groups per wave
+    int bands;                 // ceil(n_embd / (8 * waves * dn_groups))
+    int wg_per_layer;          // n_slots * bands
+    int32_t *sums;             // validation: [slot][n_embd][n_ff/32] (layer 0 only)
+    uint8_t *hq;               // validation: the q(h) rows used [slot][n_ff/32] (layer 0 only)
+};
+
+template <int POL, bool EMIT>
+__global__ __launch_bounds__(kGtDnWaves * kWave, Q8_GT_DN_OCC) void moe_r8_down_gather_kernel(const MrGdArgs a)
+{
+    constexpr int W = kGtDnWaves, T = W * kWave, QB = T / 8;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int li = wave_uniform((int)blockIdx.x / a.wg_per_layer);
+    const int rel = (int)blockIdx.x - li * a.wg_per_layer;
+    const int slot = rel / a.bands;
+    const int band = rel - slot * a.bands;
+    const auto &L = a.layer[li];
+    const int nb = a.n_ff / 32;
+
+    // small loads first: the ids and this slot's own h row
+    GtIds gi;
+    if (wave == 0) gt_load_ids(L.ids, a.n_slots, gi);
+    float4 vown[kGtOwnPre];
+    gt_prefetch<QB>(L.h + (int64_t)slot * a.n_ff, nb, vown);
+    const int e = wave_uniform(L.ids[slot]);
+    if (e < 0 || e >= a.n_expert) return;          // the combine writes NaN for its token
+
+    extern __shared__ __align__(16) uint8_t mr_lds[];
+    const int rstride = gt_row_stride(nb);
+    uint8_t *xr = mr_lds;                            // kGtMax q(h) rows
+    int *list = (int *)(mr_lds + kGtMax * rstride);  // [n_slots]
+    __shared__ GtPick pk;
+    if (wave == 0) gt_pick(L.ids, gi, a.n_slots, a.n_expert, slot, e, list, pk);
+    __syncthreads();
+    const int cnt = pk.count;
+    if (cnt == 0) return;
+
+    const int groups = a.n_embd / 8;
+    const int g0 = (band * W + wave) * a.dn_groups;   // first group of the wave
+    const int ng = max(0, min(a.dn_groups, groups - g0));
+    const int gb = kGB * nb;
+    auto goff_of = [&](int g) { return g * gb; };
+    GatherStream<POL, EMIT, kGtDnSlices> gs;
+    gs.init(L.w + ((int64_t)e * groups + (ng > 0 ? g0 : 0)) * gb, nb, ng * gb, lane);
+    const int r = (lane >> 1) & 7;
+
+    for (int c0 = 0; c0 < cnt; c0 += kGtMax) {
+        const int ct = min(kGtMax, cnt - c0);
+        gs.issue_batch(ng > 0 ? 0 : -1);
+        gt_stage<QB>(xr, rstride, nb, ct, c0 == 0 && nb <= kGtOwnPre * QB, vown,
+                 [&](int m) { return L.h + (int64_t)list[c0 + m] * a.n_ff; });
+        __syncthreads();
+        if (EMIT && a.hq && band == 0) {
+            // the q(h) bytes this pass used, as Q8_0 blocks
+            for (int i = tid; i < ct * nb * 17; i += T) {
+                const int m = i / (nb * 17);
+                const int k = i - m * nb * 17;
+                const int b = k / 17, w = k - b * 17;
+                const uint8_t *xc = xr + m * rstride;
+                const uint16_t v = w == 0 ? ((const uint16_t *)(xc + 32 * nb))[b]
+                                          : ((const uint16_t *)xc)[16 * b + w - 1];
+                ((uint16_t *)(a.hq + (int64_t)list[c0 + m] * nb * kBlockBytes))[k] = v;
+            }
+        }
+        if (ng > 0) {
+            gt_dispatch(ct, [&](auto ctc) {
+                constexpr int CT = decltype(ctc)::value;
+                auto srow_of = [&](int g, int m) {
+                    return a.sums + ((int64_t)list[c0 + m] * a.n_embd + 8 * (g0 + g) + r) * nb;
+                };
+                gs.template run<CT>(ng, lane, xr, rstride, goff_of, srow_of,
+                                    [&](int g, float (&acc)[CT]) {
+                    if ((lane & 0x31) == 0) {
+#pragma unroll
+                        for (int m = 0; m < CT; ++m)
+                            L.yslot[(int64_t)list[c0 + m] * a.n_embd + 8 * (g0 + g) + r] = acc[m];
+                    }
+                });
+            });
+        }
+        if (c0 + kGtMax < cnt) __syncthreads();   // the LDS rows are reused by the next pass
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -420,6 +880,23 @@ bool r8_decode_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
     return n_ff % 32 == 0 && n_embd % 32 == 0 && n_ff / 32 <= 64 && n_embd / 32 <= kR8MaxNb &&
            n_used >= 1 && n_used <= kMoeMaxUsed && n_tok * n_used <= kMoeMaxSlots &&
            n_expert <= kMoeMaxExperts;
+}
+
+// Decode workspace: the error word, then at one token the q(h) rows
+// [slot][n_ff/32] blocks at +256, with several tokens the fp32 slot rows
+// [slot][n_embd] of the combine at +256.
+struct R8DecodeWs {
+    size_t yslot, total;
+};
+
+R8DecodeWs r8_decode_ws(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_used)
+{
+    const size_t slots = (size_t)(n_tok * n_used);
+    R8DecodeWs w;
+    w.yslot = 256;
+    w.total = 256 + (n_tok > 1 ? slots * (size_t)n_embd * 4
+                               : (slots * (size_t)(n_ff / 32) * kBlockBytes + 255) / 256 * 256);
+    return w;
 }
 
 }  // namespace
@@ -443,8 +920,7 @@ size_t moe_r8_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_ex
 {
     if (moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used))
         return moe_prefill_ws_bytes(n_tok, n_embd, n_ff, n_expert, n_used);
-    const size_t hq = (size_t)(n_tok * n_used) * (size_t)(n_ff / 32) * kBlockBytes;
-    return 256 + (hq + 255) / 256 * 256;
+    return r8_decode_ws(n_tok, n_embd, n_ff, n_used).total;
 }
 
 // The no-alloc entry point's workspace: one array per device for the life of
@@ -477,13 +953,109 @@ int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expe
     if (n_tok == 0) return 0;
     if (moe_r8_prefill_path(n_tok, n_embd, n_ff, n_expert, n_used))
         return moe_prefill_check(n_tok, n_embd, n_ff, n_expert, n_used);
-    const size_t ug_lds = (size_t)(34 * (n_embd / 32) + 15) / 16 * 16 + 64 * 4;
-    const size_t dn_lds = (size_t)16 * ((34 * (n_ff / 32) + 15) / 16 * 16) + 16 * 8 * kDnG * 4;
+    const int64_t n_slots = n_tok * n_used;
+    const size_t ug_lds = n_tok > 1 ? gt_lds(n_slots, n_embd / 32)
+                                    : (size_t)(34 * (n_embd / 32) + 15) / 16 * 16 + 64 * 4;
+    const size_t dn_lds = n_tok > 1 ? gt_lds(n_slots, n_ff / 32)
+                                    : (size_t)16 * ((34 * (n_ff / 32) + 15) / 16 * 16) +
+                                          16 * 8 * kDnG * 4;
     if (ug_lds > (size_t)max_lds_bytes() || dn_lds > (size_t)max_lds_bytes()) return -4;
-    const int64_t ug_wgs = kMoeMaxLayers * n_tok * n_used * (n_ff / 32);
-    const int64_t dn_wgs = kMoeMaxLayers * n_tok * (n_embd / 8);
+    const int64_t ug_wgs = kMoeMaxLayers * n_slots * (n_ff / 32);
+    const int64_t dn_wgs = kMoeMaxLayers * (n_tok > 1 ? n_slots * ((n_embd / 8 + kGtDnWaves - 1) / kGtDnWaves)
+                                                      : n_tok * (n_embd / 8));
     return (ug_wgs > 0x7fffffffLL || dn_wgs > 0x7fffffffLL) ? -4 : 0;
 }
+
+namespace {
+
+#ifndef Q8_GT_NT
+#define Q8_GT_NT 1
+#endif
+// cache policy of the expert-major kernels' weight loads: every active
+// expert's rows are read once per call
+constexpr int kGtPol = Q8_GT_NT ? kCacheNT : 0;
+
+int launch_r8_gather(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
+                     int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream,
+                     const MoeEmit *emit_ug, const MoeEmit *emit_dn)
+{
+    const bool route = emit_ug && emit_ug->counts;
+    int32_t *ug_sums = emit_ug ? emit_ug->sums : nullptr;
+    int32_t *dn_sums = emit_dn ? emit_dn->sums : nullptr;
+    const int64_t n_slots = n_tok * n_used;
+    const size_t ug_lds = gt_lds(n_slots, n_embd / 32);
+    const size_t dn_lds = gt_lds(n_slots, n_ff / 32);
+    if (ug_lds > (size_t)max_lds_bytes() || dn_lds > (size_t)max_lds_bytes()) return -4;
+    const R8DecodeWs W = r8_decode_ws(n_tok, n_embd, n_ff, n_used);
+    // Work per wave: as much as keeps about 4 rounds of the resident waves
+    // busy (8 per CU here) -- few layers per call (a model's layer after layer)
+    // want short streams spread over the whole chip, many layers long streams
+    // that pay the ownership scan and the row staging once.  The active
+    // experts are bounded by min(n_expert, slots) per layer.
+    const int64_t act = (int64_t)n_layers * (n_expert < n_slots ? n_expert : n_slots);
+    const int64_t target = 4 * 256 * 8;
+    int ug_cols = 4, dn_groups = 8;
+    while (ug_cols > 1 && act * (n_ff / 8) / ug_cols < target) ug_cols /= 2;
+    while (dn_groups > 1 && act * (n_embd / 8) / dn_groups < target) dn_groups /= 2;
+    if (route)
+        if (int rc = launch_fill_i32(emit_ug->counts, n_expert, 0, stream)) return rc;
+    for (int l0 = 0; l0 < n_layers; l0 += kMoeMaxLayers) {
+        const int nl = n_layers - l0 < kMoeMaxLayers ? n_layers - l0 : kMoeMaxLayers;
+        MrUgArgs ug;
+        memset(&ug, 0, sizeof(ug));
+        MrGdArgs gd;
+        memset(&gd, 0, sizeof(gd));
+        MoeCombineLayer cb[kMoeMaxLayers];
+        for (int i = 0; i < nl; ++i) {
+            const MoeR8Layer &s = l[l0 + i];
+            float *yslot = (float *)((uint8_t *)s.ws + W.yslot);
+            ug.layer[i] = {(const uint8_t *)s.w_up_gate, s.x, s.ids, s.h, (uint8_t *)s.ws};
+            gd.layer[i] = {(const uint8_t *)s.w_down, s.ids, s.h, yslot};
+            cb[i] = {yslot, s.ids, s.cw, s.out};
+        }
+        ug.n_used = (int)n_used;
+        ug.n_slots = (int)n_slots;
+        ug.n_embd = (int)n_embd;
+        ug.n_ff = (int)n_ff;
+        ug.n_expert = (int)n_expert;
+        ug.ug_cols = ug_cols;
+        ug.wg_per_layer =
+            (int)(n_slots * ((n_ff / 8 + kGtUgWaves * ug_cols - 1) / (kGtUgWaves * ug_cols)));
+        ug.sums = ug_sums;
+        ug.counts = route ? emit_ug->counts : nullptr;
+        ug.pairs = route ? emit_ug->pairs : nullptr;
+        const dim3 ug_grid((unsigned)(nl * ug.wg_per_layer));
+        if (ug_sums || route)
+            hipLaunchKernelGGL((moe_r8_up_gate_gather_kernel<kGtPol, true>), ug_grid,
+                               dim3(kGtUgWaves * kWave), ug_lds, stream, ug);
+        else
+            hipLaunchKernelGGL((moe_r8_up_gate_gather_kernel<kGtPol, false>), ug_grid,
+                               dim3(kGtUgWaves * kWave), ug_lds, stream, ug);
+        if (hipGetLastError() != hipSuccess) return -6;
+        gd.n_slots = (int)n_slots;
+        gd.n_embd = (int)n_embd;
+        gd.n_ff = (int)n_ff;
+        gd.n_expert = (int)n_expert;
+        gd.dn_groups = dn_groups;
+        gd.bands = (int)((n_embd / 8 + kGtDnWaves * dn_groups - 1) / (kGtDnWaves * dn_groups));
+        gd.wg_per_layer = (int)(n_slots * gd.bands);
+        gd.sums = dn_sums;
+        gd.hq = emit_dn ? (uint8_t *)emit_dn->hq : nullptr;
+        const dim3 dn_grid((unsigned)(nl * gd.wg_per_layer));
+        if (dn_sums || gd.hq)
+            hipLaunchKernelGGL((moe_r8_down_gather_kernel<kGtPol, true>), dn_grid,
+                               dim3(kGtDnWaves * kWave), dn_lds, stream, gd);
+        else
+            hipLaunchKernelGGL((moe_r8_down_gather_kernel<kGtPol, false>), dn_grid,
+                               dim3(kGtDnWaves * kWave), dn_lds, stream, gd);
+        if (hipGetLastError() != hipSuccess) return -6;
+        if (int rc = launch_moe_combine_layers(cb, nl, n_tok, n_embd, n_used, n_expert, stream))
+            return rc;
+    }
+    return route ? launch_route_offsets(emit_ug->counts, emit_ug->offsets, n_expert, stream) : 0;
+}
+
+}  // namespace
 
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream,
@@ -500,7 +1072,10 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
         }
         return 0;
     }
-    // the decode kernels serve every slot on its own: no grouping to report
+    if (n_tok > 1)
+        return launch_r8_gather(l, n_layers, n_tok, n_embd, n_ff, n_expert, n_used, stream, emit_ug,
+                                emit_dn);
+    // one token: every slot is served on its own, no grouping to report
     if (emit_ug && emit_ug->counts) return -4;
     int32_t *ug_sums = emit_ug ? emit_ug->sums : nullptr;
     int32_t *dn_sums = emit_dn ? emit_dn->sums : nullptr;

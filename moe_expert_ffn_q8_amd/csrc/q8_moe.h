@@ -79,6 +79,16 @@ int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, 
                        int64_t n_tok, int64_t n_rows, int64_t n_used, int64_t n_expert,
                        hipStream_t stream);
 
+// The same over several layers of one shape in one launch.
+struct MoeCombineLayer {
+    const float *yslot;
+    const int32_t *ids;
+    const float *cw;
+    float *out;
+};
+int launch_moe_combine_layers(const MoeCombineLayer *l, int n_layers, int64_t n_tok,
+                              int64_t n_rows, int64_t n_used, int64_t n_expert, hipStream_t stream);
+
 // Prefill path (n_tok > kMoeDecodeMaxTok, K = n_embd and n_ff in multiples of
 // 4 blocks): routing + quantization + grouped int8 GEMM per call.
 bool moe_prefill_ok(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
@@ -127,7 +137,7 @@ int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float 
 // (moe_r8_ffn_batched_noalloc): a file-scope device array of
 // kMoeR8ScratchBytes per device.  moe_r8_scratch sets *base to the current
 // device's copy (looked up once per device); 0, or -6 if the lookup fails.
-constexpr size_t kMoeR8ScratchBytes = (size_t)8 << 20;
+constexpr size_t kMoeR8ScratchBytes = (size_t)48 << 20;
 int moe_r8_scratch(uint8_t **base);
 
 // The launch-shape limits of launch_moe_r8_ffn for this shape: 0 or -4.

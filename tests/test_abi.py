@@ -458,7 +458,8 @@ def test_moe_r8_checks(lib):
     # native-row prefill path); h rows need 16-byte alignment there
     pre = lib.moe_r8_workspace_bytes(512, 2048, 768, 128, 8)
     assert pre == lib.moe_workspace_bytes(512, 2048, 768, 128, 8)
-    assert lib.moe_r8_workspace_bytes(16, 2048, 768, 128, 8) == 256 + (128 * 24 * 34 + 255) // 256 * 256
+    # 2..16 tokens: the fp32 slot rows of the combine after the error word
+    assert lib.moe_r8_workspace_bytes(16, 2048, 768, 128, 8) == 256 + 128 * 2048 * 4
     big = D(A, A, A, A, A, A, A, WS, pre)
     assert call(D(A, A, A, A, A, A + 4, A, WS, pre), n_tok=512) == Q8_E_ALIGN     # h
     assert call(D(A, A, A, A, A, A, A, WS, pre - 1), n_tok=512) == Q8_E_WORKSPACE
@@ -468,7 +469,7 @@ def test_moe_r8_checks(lib):
 def test_moe_r8_noalloc_checks(lib):
     """The no-alloc variant: the shape and descriptor checks of
     moe_r8_ffn_batched (its ws fields ignored), decode shapes only, and a
-    clear status when the layers' workspaces exceed the library's 8 MiB
+    clear status when the layers' workspaces exceed the library's 48 MiB
     array -- all before any HIP call."""
     import moe_expert_ffn_q8_amd as q
     f = lib.moe_r8_ffn_batched_noalloc
@@ -486,9 +487,11 @@ def test_moe_r8_noalloc_checks(lib):
     assert call([ok], n_tok=0) == Q8_OK
     assert call([]) == Q8_OK
     assert call([ok], n_tok=17) == Q8_E_UNSUPPORTED   # the prefill path: not in this variant
-    # 16 tokens x 16 slots x n_ff 2048: 557,312 bytes per layer -> 15 layers fit
+    # 16 tokens x 16 slots, n_embd 2048: error word + fp32 slot rows
+    # (2,097,152 bytes) per layer -> 23 layers fit
     per = (lib.moe_r8_workspace_bytes(16, 2048, 2048, 64, 16) + 255) // 256 * 256
-    assert per == 557312
-    fit = (8 << 20) // per
+    assert per == 256 + 256 * 2048 * 4
+    fit = (48 << 20) // per
+    assert fit == 23
     assert call([ok] * (fit + 1), 16, 2048, 2048, 64, 16) == Q8_E_WORKSPACE
     assert call([ok] * 3 + [D(A, A, A, A, A, None, A, None, 0)], 16, 2048, 2048, 64, 16) == Q8_E_NULL

@@ -55,12 +55,76 @@ def test_moe_r8_ffn(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
 
 
 def test_moe_r8_ffn_repeated_experts(q, orc):
-    """Every token names the same 4 experts (each expert read once per slot)."""
+    """Every token names the same 4 experts: 6 slots per expert, served by its
+    owner in two passes over the rows (4 slots, then 2)."""
     n_tok, n_embd, n_ff, n_expert, n_used = 6, 512, 128, 4, 4
     ids = np.tile(np.array([2, 0, 3, 1], dtype=np.int32), (n_tok, 1))
     d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, "r8moe-rep", ids=ids)
     q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
     _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
+
+
+@pytest.mark.parametrize("n_tok,n_embd,n_ff,n_expert,n_used,same", [
+    (16, 2048, 768, 32, 8, False), (16, 2048, 768, 32, 8, True), (5, 512, 96, 8, 3, False)])
+def test_moe_r8_gather_matches_one_token_calls(q, orc, n_tok, n_embd, n_ff, n_expert, n_used,
+                                               same):
+    """Several tokens go through the expert-major kernels (each active expert
+    read once per call); per slot the arithmetic and its order are those of the
+    one-token kernels, so h and out equal, bit for bit, one call per token.
+    same: every token names experts 0..n_used-1 (16 slots per expert, 4 passes
+    over its rows)."""
+    import torch
+    print(f"case: r8 gather {n_tok} {n_embd} {n_ff} {n_expert} {n_used} same={same}", flush=True)
+    tag = f"r8gt-{n_tok}-{n_embd}-{same}"
+    ids = None
+    if same:
+        ids = np.tile(np.arange(n_used, dtype=np.int32), (n_tok, 1))
+    d, c = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, tag, ids=ids)
+    q.moe_r8_ffn_batched([d], n_embd, n_ff, n_expert)
+    torch.cuda.synchronize()
+    for t in range(n_tok):
+        one = dict(d, x=d["x"][t:t + 1].contiguous(), ids=d["ids"][t:t + 1].contiguous(),
+                   cw=d["cw"][t:t + 1].contiguous(),
+                   h=torch.full((1, n_used, n_ff), 5.0, device="cuda"),
+                   out=torch.full((1, n_embd), 5.0, device="cuda"),
+                   ws=q.moe_r8_workspace(1, n_embd, n_ff, n_expert, n_used, "cuda"))
+        q.moe_r8_ffn_batched([one], n_embd, n_ff, n_expert)
+        assert torch.equal(one["h"][0].view(torch.int32), d["h"][t].view(torch.int32)), t
+        assert torch.equal(one["out"][0].view(torch.int32), d["out"][t].view(torch.int32)), t
+    _check(q, orc, d, c, n_tok, n_embd, n_ff, n_expert, n_used)
+
+
+def test_moe_r8_gather_grouped_matches_chained(q, orc):
+    """30 layers of 16 tokens in one call take longer streams per wave than one
+    layer per call (the work per wave follows the layers in the call); h and
+    out are the same bits either way.  The layers share one set of weights
+    (own ids, rows and combine weights each); layer 0 is also checked against
+    the oracle."""
+    import torch
+    n_layers, n_tok, n_embd, n_ff, n_expert, n_used = 30, 16, 512, 256, 128, 8
+    print("case: r8 gather 30 layers grouped vs chained", flush=True)
+    d0, c0 = _layer(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, "r8gt-30")
+    layers = []
+    for l in range(n_layers):
+        key = ("r8gt-30", str(l))
+        ids = np.ascontiguousarray(synth.expert_ids(n_tok, n_used, n_expert, *key, "ids"),
+                                   dtype=np.int32)
+        layers.append(dict(d0, x=to_gpu(synth.normal_f32((n_tok, n_embd), 1.0, *key, "x")),
+                           ids=to_gpu(ids), cw=to_gpu(synth.combine_weights(n_tok, n_used, *key, "cw")),
+                           h=torch.full((n_tok, n_used, n_ff), float("nan"), device="cuda"),
+                           out=torch.full((n_tok, n_embd), float("nan"), device="cuda"),
+                           ws=q.moe_r8_workspace(n_tok, n_embd, n_ff, n_expert, n_used, "cuda")))
+    q.moe_r8_ffn_batched(layers, n_embd, n_ff, n_expert)
+    torch.cuda.synchronize()
+    for l, d in enumerate(layers):
+        one = dict(d, h=torch.full_like(d["h"], 2.0), out=torch.full_like(d["out"], 2.0))
+        q.moe_r8_ffn_batched([one], n_embd, n_ff, n_expert)
+        assert torch.equal(one["h"].view(torch.int32), d["h"].view(torch.int32)), l
+        assert torch.equal(one["out"].view(torch.int32), d["out"].view(torch.int32)), l
+    ids0 = layers[0]["ids"].cpu().numpy()
+    c = dict(c0, xq=orc.quantize_rows(layers[0]["x"].cpu().numpy()), ids=ids0,
+             cw=layers[0]["cw"].cpu().numpy())
+    _check(q, orc, layers[0], c, n_tok, n_embd, n_ff, n_expert, n_used)
 
 
 def test_moe_r8_ffn_layers(q, orc):

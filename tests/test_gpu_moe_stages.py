@@ -237,14 +237,15 @@ def _r8_layer(q, c, n_embd, n_ff, n_expert):
     (40, 512, 256, 16, 4, False)])
 def test_stages_r8(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, full):
     """The expert FFN over R8 expert weights (decode kernels up to 16 tokens,
-    the grouped path above): sums of both products, q(h), the routing on the
-    grouped path; h and out bitwise those of moe_r8_ffn_batched."""
+    the matrix-core path above): sums of both products, q(h), the routing the
+    kernels grouped slots by (2 tokens or more); h and out bitwise those of
+    moe_r8_ffn_batched."""
     import torch
     print(f"case: stages r8 {n_tok} {n_embd} {n_ff} {n_expert} {n_used}", flush=True)
     c = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used, f"stg-r8-{n_tok}-{n_embd}",
               wtag="stg-w" if full else None)
     d = _r8_layer(q, c, n_embd, n_ff, n_expert)
-    grouped = n_tok > 16
+    grouped = n_tok > 1
     ug, dn, hq, counts, offsets, pairs = q.q8v_moe_r8_ffn(d, n_embd, n_ff, n_expert, route=grouped)
     assert q.moe_error_word(d["ws"]) == 0
     if grouped:

@@ -98,14 +98,14 @@ def test_noalloc_one_token_full_layer_shape(q):
 
 
 def test_noalloc_rejects_beyond_its_array(q):
-    """More layers than the library's 8 MiB array holds: Q8_E_WORKSPACE, and
+    """More layers than the library's 48 MiB array holds: Q8_E_WORKSPACE, and
     more than 16 tokens (the prefill path): Q8_E_UNSUPPORTED."""
     from moe_expert_ffn_q8_amd import MoeR8FfnDesc
     lib = q.raw
     A = 1 << 20
     n_tok, n_embd, n_ff, n_expert, n_used = 16, 2048, 2048, 64, 16
     per = (q.raw.moe_r8_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used) + 255) // 256 * 256
-    n_fit = (8 << 20) // per
+    n_fit = (48 << 20) // per
     descs = (MoeR8FfnDesc * (n_fit + 1))(*[MoeR8FfnDesc(A, A, A, A, A, A, A, None, 0)
                                            for _ in range(n_fit + 1)])
     assert lib.moe_r8_ffn_batched_noalloc(descs, n_fit + 1, n_tok, n_embd, n_ff, n_expert, n_used,
