@@ -729,6 +729,56 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const CbParams p)
     L.out[(int64_t)t * p.n_rows + n] = acc;
 }
 
+// The same with four consecutive outputs per thread (n_rows % 4 == 0, out
+// 16-byte aligned): one 16-byte load per slot row, the same arithmetic per
+// output.  grid (ceil(n_rows/1024), n_tok, n_layers).
+__global__ __launch_bounds__(256) void moe_combine4_kernel(const CbParams p)
+{
+    const CbLayer &L = p.layer[blockIdx.z];
+    const int t = blockIdx.y;
+    const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
+    if (n >= p.n_rows) return;
+    bool bad = false;
+    for (int u = 0; u < p.n_used; ++u) {
+        const int e = L.ids[t * p.n_used + u];
+        bad |= (e < 0 || e >= p.n_expert);
+    }
+    float4 acc;
+    if (bad) {
+        acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                          __builtin_nanf(""));
+    } else {
+        const float *y = L.yslot + (int64_t)t * p.n_used * p.n_rows + n;
+        const float c0 = L.cw[t * p.n_used];
+        const float4 y0 = *(const float4 *)y;
+        acc = make_float4(c0 * y0.x, c0 * y0.y, c0 * y0.z, c0 * y0.w);
+        for (int u = 1; u < p.n_used; ++u) {
+            const float c = L.cw[t * p.n_used + u];
+            const float4 v = *(const float4 *)(y + (int64_t)u * p.n_rows);
+            acc.x = fmaf(c, v.x, acc.x);
+            acc.y = fmaf(c, v.y, acc.y);
+            acc.z = fmaf(c, v.z, acc.z);
+            acc.w = fmaf(c, v.w, acc.w);
+        }
+    }
+    *(float4 *)(L.out + (int64_t)t * p.n_rows + n) = acc;
+}
+
+// Either combine kernel for cb (the four-wide one where rows and outputs allow).
+int launch_combine(const CbParams &cb, int n_layers, int64_t n_tok, hipStream_t stream)
+{
+    bool four = cb.n_rows % 4 == 0;
+    for (int i = 0; i < n_layers; ++i) four = four && ((uintptr_t)cb.layer[i].out % 16 == 0);
+    if (four) {
+        dim3 g((unsigned)((cb.n_rows + 1023) / 1024), (unsigned)n_tok, (unsigned)n_layers);
+        hipLaunchKernelGGL(moe_combine4_kernel, g, dim3(256), 0, stream, cb);
+    } else {
+        dim3 g((unsigned)((cb.n_rows + 255) / 256), (unsigned)n_tok, (unsigned)n_layers);
+        hipLaunchKernelGGL(moe_combine_kernel, g, dim3(256), 0, stream, cb);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 __global__ __launch_bounds__(kThreads) void moe_route_kernel(const int32_t *ids, int32_t *counts,
                                                              int32_t *offsets, int32_t *pairs,
                                                              int n_slots, int n_expert,
@@ -920,9 +970,7 @@ int launch_moe_combine(const float *yslot, const int32_t *ids, const float *cw, 
     cb.n_rows = (int)n_rows;
     cb.n_used = (int)n_used;
     cb.n_expert = (int)n_expert;
-    dim3 cgrid((unsigned)((n_rows + 255) / 256), (unsigned)n_tok, 1);
-    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, cb);
-    return hipGetLastError() == hipSuccess ? 0 : -6;
+    return launch_combine(cb, 1, n_tok, stream);
 }
 
 int launch_moe_combine_layers(const MoeCombineLayer *l, int n_layers, int64_t n_tok,
@@ -936,9 +984,7 @@ int launch_moe_combine_layers(const MoeCombineLayer *l, int n_layers, int64_t n_
     cb.n_rows = (int)n_rows;
     cb.n_used = (int)n_used;
     cb.n_expert = (int)n_expert;
-    dim3 cgrid((unsigned)((n_rows + 255) / 256), (unsigned)n_tok, (unsigned)n_layers);
-    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, cb);
-    return hipGetLastError() == hipSuccess ? 0 : -6;
+    return launch_combine(cb, n_layers, n_tok, stream);
 }
 
 size_t moe_ws_bytes(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
@@ -1146,9 +1192,7 @@ int launch_moe_down(const MoeDownArgs &a, hipStream_t stream)
     cb.n_rows = (int)a.n_embd;
     cb.n_used = (int)a.n_used;
     cb.n_expert = (int)a.n_expert;
-    dim3 cgrid((unsigned)((a.n_embd + 255) / 256), (unsigned)a.n_tok, (unsigned)a.n_layers);
-    hipLaunchKernelGGL(moe_combine_kernel, cgrid, dim3(256), 0, stream, cb);
-    return hipGetLastError() == hipSuccess ? 0 : -6;
+    return launch_combine(cb, a.n_layers, a.n_tok, stream);
 }
 
 int launch_moe_route(const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *pairs,

@@ -86,7 +86,7 @@ struct RouteArgs {
 
 constexpr int kRouteWaves = kRouteThreads / kWave;      // 16
 
-__global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const RouteArgs a)
+__device__ __forceinline__ void route_tiles(const RouteArgs &a)
 {
     __shared__ int cnt[kMoeMaxExperts];
     __shared__ int scan_c[kMoeMaxExperts];
@@ -187,20 +187,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const Ro
     }
 }
 
+__global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const RouteArgs a)
+{
+    route_tiles(a);
+}
+
 // fp32 rows -> the tile layout of the A operand: codes [row][nb][32] (even
 // blocks rotated by two bytes when the weights are native rows; in code order
 // for R8 weights), scales [row][nb] as fp32.  Eight lanes own a block, four
-// values each, with the rule and the bytes of q8_0_quantize_rows.
-__global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restrict__ x,
-                                                          int64_t row_stride,
-                                                          uint8_t *__restrict__ codes,
-                                                          float *__restrict__ scales, int64_t nb,
-                                                          int64_t total_blocks, int rotate)
+// values each, with the rule and the bytes of q8_0_quantize_rows; workgroup
+// wg of n_wg takes every n_wg-th pass of blockDim.x/8 blocks.
+__device__ __forceinline__ void qa_quantize_tiles(const float *__restrict__ x, int64_t row_stride,
+                                                  uint8_t *__restrict__ codes,
+                                                  float *__restrict__ scales, int64_t nb,
+                                                  int64_t total_blocks, int rotate, int64_t wg,
+                                                  int64_t n_wg)
 {
     const int tid = threadIdx.x;
     const int li = tid & 7;
-    for (int64_t blk0 = (int64_t)blockIdx.x * kQaTileBlocks; blk0 < total_blocks;
-         blk0 += (int64_t)gridDim.x * kQaTileBlocks) {
+    const int64_t per = blockDim.x / 8;
+    for (int64_t blk0 = wg * per; blk0 < total_blocks; blk0 += n_wg * per) {
         const int64_t g = blk0 + (tid >> 3);
         const bool live = g < total_blocks;
         int64_t b = 0;
@@ -221,6 +227,28 @@ __global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restric
             if (li == 0) scales[g] = half_bits_to_float(dbits);
         }
     }
+}
+
+__global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restrict__ x,
+                                                          int64_t row_stride,
+                                                          uint8_t *__restrict__ codes,
+                                                          float *__restrict__ scales, int64_t nb,
+                                                          int64_t total_blocks, int rotate)
+{
+    qa_quantize_tiles(x, row_stride, codes, scales, nb, total_blocks, rotate, blockIdx.x, gridDim.x);
+}
+
+// The two independent first steps of a prefill call in one launch: workgroup
+// 0 routes the slots, the others quantize the token rows.
+__global__ __launch_bounds__(kRouteThreads) void route_quantize_kernel(
+    const RouteArgs r, const float *__restrict__ x, int64_t row_stride, uint8_t *__restrict__ codes,
+    float *__restrict__ scales, int64_t nb, int64_t total_blocks, int rotate)
+{
+    if (blockIdx.x == 0)
+        route_tiles(r);
+    else
+        qa_quantize_tiles(x, row_stride, codes, scales, nb, total_blocks, rotate, blockIdx.x - 1,
+                          gridDim.x - 1);
 }
 
 int launch_qa_quantize(const float *x, int64_t row_stride, uint8_t *codes, float *scales,
@@ -251,6 +279,8 @@ struct PgArgs {
     int n_used;              // up_gate: A row of slot s is token s / n_used
     int max_tiles, tiles_n;
     int32_t *sums;           // validation (EMIT kernels): [slot][w_rows][nb] block sums
+    uint8_t *hq_codes;       // R8 up_gate: q(h) in the A layout of the down product, or null
+    float *hq_scales;
 };
 
 // Output columns per workgroup: up_gate pairs waves w and w + 4 (gate and up
@@ -476,10 +506,32 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
 // contiguous bytes -- the MFMA operand itself, in code order -- straight into
 // registers, 8 blocks in flight, and the 16 scale bytes of each group.  The
 // token tile is staged in LDS once per 64 blocks (codes in code order).
-constexpr int kR8Chunk = 64;
+#ifndef Q8_PG_R8_CHUNK
+#define Q8_PG_R8_CHUNK 64
+#endif
+constexpr int kR8Chunk = Q8_PG_R8_CHUNK;
+#ifndef Q8_PG_R8_DEPTH
+#define Q8_PG_R8_DEPTH 8
+#endif
+constexpr int kR8Depth = Q8_PG_R8_DEPTH;       // weight blocks in flight per wave
+static_assert(kR8Chunk % kR8Depth == 0, "whole prefetch batches per chunk");
+static_assert(kR8Chunk * 1024 >= 2 * 16384, "the up_gate epilogue's up sums and h tile fit the A tile");
+// Build options of the kernel below, kept for measurement (512-token layer,
+// R8 rows, per layer): Q8_PG_OUTER=1 forms the 16 scale products of a block as
+// an fp32 matrix-core outer product (2 VALU operations left per product
+// instead of 3): 208 against 206 us; Q8_PG_R8_DEPTH (weight blocks in flight
+// per wave) 4: 203, 16: 235 (3 waves per SIMD) and 274 us (4, with spills);
+// Q8_PG_R8_CHUNK=32 with Q8_PG_R8_OCC=6 (three workgroups per CU): 218 us.
+#ifndef Q8_PG_OUTER
+#define Q8_PG_OUTER 0           // scale products on the fp32 matrix core (1) or the VALU (0)
+#endif
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 template <bool UG, bool EMIT>
-__global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs a)
+#ifndef Q8_PG_R8_OCC
+#define Q8_PG_R8_OCC 2
+#endif
+__global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(const PgArgs a)
 {
     __shared__ __align__(16) uint8_t la[kR8Chunk * 1024];
     __shared__ __align__(16) float ldx[kR8Chunk * kPBM];
@@ -520,8 +572,8 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.w + (int64_t)te.expert * a.expert_bytes), 0, past, kBufferWord3);
 
-    u32x4 wc[kPDepth];
-    uint32_t ws16[kPDepth];
+    u32x4 wc[kR8Depth];
+    uint32_t ws16[kR8Depth];
     // default cache policy: the second tile of an expert (more than 32
     // slots) runs beside the first on the same XCD and finds its rows in L2
     auto issue = [&](int b, int i) {
@@ -531,7 +583,7 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
         ws16[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, in ? goff + 2 * (8 * b + r) : past, 0, 0);
     };
 #pragma unroll
-    for (int i = 0; i < kPDepth; ++i) issue(i, i);
+    for (int i = 0; i < kR8Depth; ++i) issue(i, i);
 
     float acc[16];
 #pragma unroll
@@ -544,7 +596,7 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
     const int a_past = a.a_rows * nb * 32;
 
     for (int kb0 = 0; kb0 < nb; kb0 += kR8Chunk) {
-        const int kc = min(kR8Chunk, (nb - kb0 + kPDepth - 1) / kPDepth * kPDepth);
+        const int kc = min(kR8Chunk, (nb - kb0 + kR8Depth - 1) / kR8Depth * kR8Depth);
         __syncthreads();                 // a_row written; the previous chunk fully read
         const int ar = a_row[li];
         for (int bi = wave; bi < kc; bi += kPWaves) {
@@ -562,9 +614,9 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
         __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's copies landed
         __syncthreads();
 
-        for (int bi0 = 0; bi0 < kc; bi0 += kPDepth) {
+        for (int bi0 = 0; bi0 < kc; bi0 += kR8Depth) {
 #pragma unroll
-            for (int i = 0; i < kPDepth; ++i) {
+            for (int i = 0; i < kR8Depth; ++i) {
                 const int bi = bi0 + i;
                 const u32x4 av = *(const u32x4 *)(la + 1024 * bi + 16 * lane);
                 const u32x4 c = wc[i];
@@ -583,35 +635,75 @@ __global__ __launch_bounds__(kPThreads, 2) void moe_r8_gemm_kernel(const PgArgs 
                     }
                 }
                 const float dw = half_bits_to_float(ws16[i]);
-                float dx[16];
+                if (Q8_PG_OUTER) {
+                    // P(r, c) = dx_r * dw_c as an outer product on the fp32 matrix
+                    // core (k = 2, the second k row zero): the same 32x32
+                    // register layout as the int32 tile, each product rounded once
+                    const float adx = h == 0 ? ldx[kPBM * bi + li] : 0.0f;
+                    v16f pz = {0.f};
+                    const v16f P = __builtin_amdgcn_mfma_f32_32x32x2f32(adx, dw, pz, 0, 0, 0);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *(const float4 *)&ldx[kPBM * bi + 8 * q + 4 * h];
-                    dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                    for (int q = 0; q < 16; ++q) {
+                        acc[q] = fmaf(P[q], (float)sres[q], acc[q]);
+                        // one block's sums at a time: left to itself the compiler
+                        // sinks every block's float work below the loop and holds
+                        // 32 matrix-core results per block
+                        asm volatile("" : "+v"(acc[q]));
+                    }
+                } else {
+                    float dx[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = *(const float4 *)&ldx[kPBM * bi + 8 * q + 4 * h];
+                        dx[4 * q + 0] = v.x; dx[4 * q + 1] = v.y; dx[4 * q + 2] = v.z; dx[4 * q + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[q] = fmaf(dx[q] * dw, (float)sres[q], acc[q]);
                 }
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[q] = fmaf(dx[q] * dw, (float)sres[q], acc[q]);
-                issue(kb0 + bi + kPDepth, i);
+                issue(kb0 + bi + kR8Depth, i);
             }
         }
     }
 
     if (UG) {
-        float *xch = (float *)la;
+        float *xch = (float *)la;                        // up sums [4 waves][16][64]
+        float *ht = (float *)(la + 4 * 16 * kWave * 4);  // h tile [kPBM][128]
         __syncthreads();                       // every wave is done with the A tile
         if (wave >= 4) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) xch[((wave - 4) * 16 + q) * kWave + lane] = acc[q];
         }
         __syncthreads();
-        if (wave >= 4 || !wave_live) return;
+        if (wave < 4 && wave_live) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int row = 8 * (q >> 2) + 4 * h + (q & 3);
-            if (row >= te.rows) continue;
-            const float g = acc[q];
-            const float u = xch[(wave * 16 + q) * kWave + lane];
-            a.out[(int64_t)a_slot[row] * a.n_out + col] = g / (1.0f + expf(-g)) * u;
+            for (int q = 0; q < 16; ++q) {
+                const int row = 8 * (q >> 2) + 4 * h + (q & 3);
+                if (row >= te.rows) continue;
+                const float g = acc[q];
+                const float u = xch[(wave * 16 + q) * kWave + lane];
+                const float hv = g / (1.0f + expf(-g)) * u;
+                a.out[(int64_t)a_slot[row] * a.n_out + col] = hv;
+                ht[row * 128 + 32 * wave + li] = hv;
+            }
+        }
+        if (!a.hq_codes) return;
+        __syncthreads();
+        // q(h) of the tile (its rows x 4 blocks of 32 columns) with the rule and
+        // the bytes of q8_0_quantize_rows, in the down product's A layout
+        const int c0 = pg_cols<UG>() * nt;
+        const int nbf = a.n_out / 32;
+        for (int k = tid >> 3; k < kPBM * 4; k += kPThreads / 8) {
+            const int row = k >> 2, cb = k & 3;
+            const bool live = row < te.rows && c0 + 32 * cb < a.n_out;
+            const float4 v = live ? *(const float4 *)&ht[row * 128 + 32 * cb + 4 * (tid & 7)]
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+            uint32_t codes, dbits;
+            quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+            if (live) {
+                const int64_t blk = (int64_t)a_slot[row] * nbf + c0 / 32 + cb;
+                ((uint32_t *)a.hq_codes)[blk * 8 + (tid & 7)] = codes;
+                if ((tid & 7) == 0) a.hq_scales[blk] = half_bits_to_float(dbits);
+            }
         }
     } else {
         if (!wave_live) return;
@@ -631,7 +723,7 @@ size_t align256(size_t v)
 // Workspace layout of the prefill path (the up_gate call's token rows and the
 // down call's slot rows share the data region).
 struct PrefillWs {
-    size_t offsets, pairs, tiles, data, xq_scales, hq_scales, yslot, total;
+    size_t offsets, pairs, tiles, data, xq_scales, hq_data, hq_scales, yslot, total;
     int64_t max_tiles;
 };
 
@@ -647,11 +739,12 @@ PrefillWs prefill_layout(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_
     L.tiles = L.pairs + align256((size_t)slots * 4);
     L.data = L.tiles + align256((size_t)L.max_tiles * sizeof(TileEntry));
     L.xq_scales = L.data + align256((size_t)n_tok * nbe * 32);
-    const size_t up_end = L.xq_scales + align256((size_t)n_tok * nbe * 4);
-    L.hq_scales = L.data + align256((size_t)slots * nbf * 32);
+    // the down product's A rows after the token rows: the R8 up_gate kernel
+    // writes them while other workgroups still read the token rows
+    L.hq_data = L.xq_scales + align256((size_t)n_tok * nbe * 4);
+    L.hq_scales = L.hq_data + align256((size_t)slots * nbf * 32);
     L.yslot = L.hq_scales + align256((size_t)slots * nbf * 4);
-    const size_t down_end = L.yslot + align256((size_t)slots * n_embd * 4);
-    L.total = down_end > up_end ? down_end : up_end;
+    L.total = L.yslot + align256((size_t)slots * n_embd * 4);
     return L;
 }
 
@@ -672,13 +765,41 @@ int launch_route(const int32_t *ids, uint8_t *ws, const PrefillWs &L, float *h_n
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
+// launch_route and launch_qa_quantize of the token rows in one launch
+int launch_route_quantize(const int32_t *ids, uint8_t *ws, const PrefillWs &L, float *h_nan,
+                          int64_t n_slots, int64_t n_expert, int64_t n_ff, const float *x,
+                          int64_t row_stride, uint8_t *codes, float *scales, int64_t n_rows,
+                          int64_t nb, bool rotate, hipStream_t stream)
+{
+    RouteArgs r;
+    r.ids = ids;
+    r.hdr = (int32_t *)ws;
+    r.offsets = (int32_t *)(ws + L.offsets);
+    r.pairs = (int32_t *)(ws + L.pairs);
+    r.tiles = (TileEntry *)(ws + L.tiles);
+    r.h_nan = h_nan;
+    r.n_slots = (int)n_slots;
+    r.n_expert = (int)n_expert;
+    r.n_ff = (int)n_ff;
+    const int64_t total = n_rows * nb;
+    const int64_t per = kRouteThreads / 8;
+    int64_t qwg = (total + per - 1) / per;
+    if (qwg > 256 * 16) qwg = 256 * 16;
+    hipLaunchKernelGGL(route_quantize_kernel, dim3((unsigned)(1 + qwg)), dim3(kRouteThreads), 0,
+                       stream, r, x, row_stride, codes, scales, nb, total, rotate ? 1 : 0);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 template <bool UG, bool R8>
 int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows, const uint8_t *w,
                    int64_t w_rows, int64_t nb, uint8_t *ws, const PrefillWs &L, float *out,
-                   int64_t n_out, int64_t n_used, hipStream_t stream, int32_t *sums = nullptr)
+                   int64_t n_out, int64_t n_used, hipStream_t stream, int32_t *sums = nullptr,
+                   uint8_t *hq_codes = nullptr, float *hq_scales = nullptr)
 {
     PgArgs p;
     p.sums = sums;
+    p.hq_codes = hq_codes;
+    p.hq_scales = hq_scales;
     p.a_codes = a_codes;
     p.a_scales = a_scales;
     p.a_rows = (int)a_rows;
@@ -801,12 +922,13 @@ int launch_moe_prefill_up_gate(const uint8_t *w, const float *x, const int32_t *
     uint8_t *ws = (uint8_t *)ws_;
     const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
     const int64_t nb = n_embd / kQK;
-    if (int rc = launch_route(ids, ws, L, h, n_tok * n_used, n_expert, n_ff, stream)) return rc;
-    if (emit && emit->counts)
-        if (int rc = launch_route_export(ws, L, *emit, n_expert, stream)) return rc;
     uint8_t *xq = ws + L.data;
     float *xs = (float *)(ws + L.xq_scales);
-    if (int rc = launch_qa_quantize(x, n_embd, xq, xs, n_tok, nb, true, stream)) return rc;
+    if (int rc = launch_route_quantize(ids, ws, L, h, n_tok * n_used, n_expert, n_ff, x, n_embd, xq,
+                                       xs, n_tok, nb, true, stream))
+        return rc;
+    if (emit && emit->counts)
+        if (int rc = launch_route_export(ws, L, *emit, n_expert, stream)) return rc;
     return launch_grouped<true, false>(xq, xs, n_tok, w, 2 * n_ff, nb, ws, L, h, n_ff, n_used, stream,
                                        emit ? emit->sums : nullptr);
 }
@@ -821,7 +943,7 @@ int launch_moe_prefill_down(const uint8_t *w, const float *h, const int32_t *ids
     const int64_t nb = n_ff / kQK;
     const int64_t slots = n_tok * n_used;
     if (int rc = launch_route(ids, ws, L, nullptr, slots, n_expert, n_ff, stream)) return rc;
-    uint8_t *hq = ws + L.data;
+    uint8_t *hq = ws + L.hq_data;
     float *hs = (float *)(ws + L.hq_scales);
     if (int rc = launch_qa_quantize(h, n_ff, hq, hs, slots, nb, true, stream)) return rc;
     if (emit && emit->hq)
@@ -843,27 +965,25 @@ int launch_moe_r8_prefill(const uint8_t *w_ug, const uint8_t *w_dn, const float 
     const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
     const int64_t nbe = n_embd / kQK, nbf = n_ff / kQK;
     const int64_t slots = n_tok * n_used;
-    // one routing for both products (the tables stay in the workspace)
-    if (int rc = launch_route(ids, ws, L, h, slots, n_expert, n_ff, stream)) return rc;
+    // one routing for both products (the tables stay in the workspace),
+    // launched with the quantization of the token rows
+    uint8_t *q = ws + L.data;
+    if (int rc = launch_route_quantize(ids, ws, L, h, slots, n_expert, n_ff, x, n_embd, q,
+                                       (float *)(ws + L.xq_scales), n_tok, nbe, false, stream))
+        return rc;
     if (emit_ug && emit_ug->counts)
         if (int rc = launch_route_export(ws, L, *emit_ug, n_expert, stream)) return rc;
-    uint8_t *q = ws + L.data;
-    if (int rc = launch_qa_quantize(x, n_embd, q, (float *)(ws + L.xq_scales), n_tok, nbe, false,
-                                    stream))
-        return rc;
+    // the up_gate kernel also writes q(h) in the down product's A layout
+    uint8_t *hq = ws + L.hq_data;
+    float *hs = (float *)(ws + L.hq_scales);
     if (int rc = launch_grouped<true, true>(q, (const float *)(ws + L.xq_scales), n_tok, w_ug,
                                             2 * n_ff, nbe, ws, L, h, n_ff, n_used, stream,
-                                            emit_ug ? emit_ug->sums : nullptr))
-        return rc;
-    if (int rc = launch_qa_quantize(h, n_ff, q, (float *)(ws + L.hq_scales), slots, nbf, false,
-                                    stream))
+                                            emit_ug ? emit_ug->sums : nullptr, hq, hs))
         return rc;
     if (emit_dn && emit_dn->hq)
-        if (int rc = launch_qa_export(q, (const float *)(ws + L.hq_scales), slots, nbf, false,
-                                      emit_dn->hq, stream))
-            return rc;
+        if (int rc = launch_qa_export(hq, hs, slots, nbf, false, emit_dn->hq, stream)) return rc;
     float *yslot = (float *)(ws + L.yslot);
-    if (int rc = launch_grouped<false, true>(q, (const float *)(ws + L.hq_scales), slots, w_dn,
+    if (int rc = launch_grouped<false, true>(hq, hs, slots, w_dn,
                                              n_embd, nbf, ws, L, yslot, n_embd, n_used, stream,
                                              emit_dn ? emit_dn->sums : nullptr))
         return rc;

@@ -44,6 +44,9 @@ namespace {
 
 constexpr int kGB = 8 * kBlockBytes;      // bytes per block column of an 8-row group
 constexpr int kMrSlices = 8;              // 1 KB slices of a group in flight per wave
+#ifndef Q8_MR_UG_SLICES
+#define Q8_MR_UG_SLICES 8
+#endif
 
 // One 8-row group of nb blocks against an activation row in LDS (codes
 // realigned to 32 bytes per block, binary16 scale bits); slice i, lane l:
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kUgThreads) void moe_r8_up_gate_kernel(const MrUgAr
             if (q8 == 0) xd16[b] = (uint16_t)dbits;
         }
     };
-    GroupStream<POL, EMIT> gs;
+    GroupStream<POL, EMIT, Q8_MR_UG_SLICES> gs;
     gs.init(gbase, nb, lane, true);
     if (EMIT) gs.srow = a.sums + ((int64_t)slot * 2 * a.n_ff + 8 * grp + ((lane >> 1) & 7)) * nb;
     if (passes <= 2) {

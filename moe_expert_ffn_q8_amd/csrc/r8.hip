@@ -103,8 +103,11 @@ __global__ __launch_bounds__(256) void r8_repack_kernel(const uint8_t *__restric
 // into LDS itself (the bytes of q8_0_quantize_rows), so a decode step needs no
 // separate quantization launch.  SUMS (validation builds of the same kernel):
 // every exact int32 block sum is also written out.
+#ifndef Q8_R8_OCC
+#define Q8_R8_OCC 1
+#endif
 template <bool XF, bool SUMS>
-__global__ __launch_bounds__(kR8Threads) void r8_matvec_kernel(const R8Args a)
+__global__ __launch_bounds__(kR8Threads, Q8_R8_OCC) void r8_matvec_kernel(const R8Args a)
 {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;

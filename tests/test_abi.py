@@ -134,7 +134,7 @@ def test_moe_checks(lib):
 
 def test_moe_prefill_checks(lib):
     """More than 16 tokens: the prefill path's workspace (routing tables, the
-    quantized token rows; or the quantized h rows and the per-slot outputs)
+    quantized token rows, then the quantized h rows and the per-slot outputs)
     and its shape limits."""
     import moe_expert_ffn_q8_amd as q
 
@@ -145,12 +145,13 @@ def test_moe_prefill_checks(lib):
     slots = n_tok * n_used
     max_tiles = slots // 32 + n_expert + 1
     data = 256 + a256((n_expert + 1) * 4) + a256(slots * 4) + a256(max_tiles * 16)
-    # quantized rows in the tile layout: 32 code bytes per block, then fp32 scales
-    down = data + a256(slots * (n_ff // 32) * 32) + a256(slots * (n_ff // 32) * 4) \
+    # quantized rows in the tile layout (32 code bytes per block, then fp32
+    # scales): the token rows, then the slot rows of h, then the slot outputs
+    up = a256(n_tok * (n_embd // 32) * 32) + a256(n_tok * (n_embd // 32) * 4)
+    down = a256(slots * (n_ff // 32) * 32) + a256(slots * (n_ff // 32) * 4) \
         + a256(slots * n_embd * 4)
-    up = data + a256(n_tok * (n_embd // 32) * 32) + a256(n_tok * (n_embd // 32) * 4)
     ws = q.moe_workspace_bytes(n_tok, n_embd, n_ff, n_expert, n_used)
-    assert ws == max(up, down)
+    assert ws == data + up + down
     assert ws > q.moe_workspace_bytes(16, n_embd, n_ff, n_expert, n_used)
     ug = lib.moe_up_gate_swiglu
     assert ug(A, A, A, A, n_tok, n_embd, n_ff, n_expert, n_used, A, ws - 1, None) == Q8_E_WORKSPACE
