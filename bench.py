@@ -895,7 +895,8 @@ def run_extra(args, q, synth):
             q.moe_down_combine_batched(dn, n_ff, n_embd, E)
         res.update(tokens=n_tok, layers=L, active_weight_bytes=active_bytes)
         # the same layers over expert weights repacked once into the R8 layout:
-        # one moe_r8_ffn_batched call (2 launches) per step
+        # one moe_r8_ffn_batched call per step (2 launches at one token; 3 at
+        # several: up_gate, down, combine)
         r8l = []
         for d in layers:
             r8l.append(dict(w_up_gate_r8=q.q8_0_repack_r8(d["wug"], E * 2 * n_ff, n_embd),
@@ -905,7 +906,8 @@ def run_extra(args, q, synth):
         tr = _time_launches(lambda: q.moe_r8_ffn_batched(r8l, n_embd, n_ff, E), args.steps,
                             args.warmup) / args.steps
         res.update(r8_layout={"timing": "expert weights repacked once into the R8 layout; "
-                                        "all layers in one moe_r8_ffn_batched call (2 launches)",
+                                        "all layers in one moe_r8_ffn_batched call (2 launches at "
+                                        "one token; 3 at several: up_gate, down, combine)",
                               "us_per_step": round(tr * 1e6, 2),
                               "gbs": round(active_bytes / tr / 1e9, 1),
                               "pct_of_hbm_peak": round(active_bytes / tr / 1e9 / HBM_PEAK_GBS * 100, 2),
@@ -1065,14 +1067,16 @@ def default_extras(args, q, synth):
         def grouped_r8():
             q.moe_r8_ffn_batched(r8all, n_embd, n_ff, E)
 
-        forms = {"chained_native": (chained_native, "native rows, 2 launches per layer, layer "
+        nl = 2 if n_tok == 1 else 3         # up_gate, down (+ combine from 2 tokens on)
+        forms = {"chained_native": (chained_native, f"native rows, {nl} launches per layer, layer "
                                                     "after layer"),
-                 "chained_r8": (chained_r8, "R8 expert weights, 2 launches per layer, layer "
+                 "chained_r8": (chained_r8, f"R8 expert weights, {nl} launches per layer, layer "
                                             "after layer"),
                  "grouped_native": (grouped_native, "native rows, all 30 layers in one up_gate "
-                                                    "and one down launch"),
+                                                    "and one down call (3 launches: up_gate, down, "
+                                                    "combine)"),
                  "grouped_r8": (grouped_r8, "R8 expert weights, all 30 layers in one call "
-                                            "(2 launches)")}
+                                            f"({nl} launches)")}
         graphs = {}
         for key, (fn, _) in forms.items():
             fn()
