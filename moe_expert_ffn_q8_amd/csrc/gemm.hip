@@ -14,12 +14,15 @@
 // its own scales into fp32 accumulators: per element and block a convert, a
 // scale product and a fused multiply-add on the VALU (3 operations against
 // 1/16 of an MFMA per lane), and that rescale, not the int8 matrix core,
-// bounds this kernel.  (Build option Q8_GEMM_OUTER=1 forms the rank-1 scale
-// products of a block as an outer product on the fp32 matrix core instead,
-// same register layout, leaving 2 VALU operations; with this compiler's
-// schedule it measured slower, so it is off.  The same outer product from a
-// K = 16 binary16 product (v_mfma_f32_32x32x16_f16, the scales' own bits)
-// measured 138.6 to 142.8 us against 133.4 us.)
+// bounds this kernel together with the operand reads from LDS (staged rows are
+// 144 bytes apart, so 32 rows of a fragment fall on 8 bank offsets: 4-way
+// conflicts on the 4-byte reads the 2-byte-offset codes need).  (Build option
+// Q8_GEMM_OUTER=1 forms the rank-1 scale products of a block as an outer
+// product on the fp32 matrix core instead, same register layout, leaving 2
+// VALU operations: 150.5 against 141.3 us with each tile's sums pinned in
+// place (Q8_GEMM_PIN, else 198 us at 1 wave per SIMD), so it is off.  The same
+// outer product from a K = 16 binary16 product (v_mfma_f32_32x32x16_f16, the
+// scales' own bits) measured 138.6 to 142.8 us against 133.4 us.)
 //
 // Work decomposition:
 //  * Workgroup = 4 waves, output tile 128 tokens x 128 weight rows; wave
@@ -62,6 +65,9 @@ constexpr int kStepChunks = (kStepRowBytes + 15) / 16;      // 9 or 17 16-byte c
 constexpr int kRowStride = 16 * kStepChunks;                // staged row: 144 or 272 B
 constexpr int kStageRows = kBM + kBN;                       // 256
 constexpr int kStageLoads = kStageRows * kStepChunks / kGThreads;   // 9 or 17 per thread
+#ifndef Q8_GEMM_PIN
+#define Q8_GEMM_PIN 1
+#endif
 #ifndef Q8_GEMM_OUTER
 #define Q8_GEMM_OUTER 0          // scale products on the fp32 matrix core (1) or the VALU (0)
 #endif
@@ -232,8 +238,12 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
                         v16f pz = {0.f};
                         const v16f P = __builtin_amdgcn_mfma_f32_32x32x2f32(adx[i], bdw[j], pz, 0, 0, 0);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
+                        for (int r = 0; r < 16; ++r) {
                             acc[i][j][r] = fmaf(P[r], (float)s[r], acc[i][j][r]);
+                            // one tile's sums at a time (else every tile's two
+                            // matrix-core results stay live across the block)
+                            if (Q8_GEMM_PIN) asm volatile("" : "+v"(acc[i][j][r]));
+                        }
                     } else {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
