@@ -14,9 +14,13 @@
 // its own scales into fp32 accumulators: per element and block a convert, a
 // scale product and a fused multiply-add on the VALU (3 operations against
 // 1/16 of an MFMA per lane), and that rescale, not the int8 matrix core,
-// bounds this kernel together with the operand reads from LDS (staged rows are
-// 144 bytes apart, so 32 rows of a fragment fall on 8 bank offsets: 4-way
-// conflicts on the 4-byte reads the 2-byte-offset codes need).  (Build option
+// bounds this kernel.  The staged rows are 144 bytes apart (16-byte DMA
+// granularity), so the 4-byte reads that codes 2 bytes past a dword boundary
+// need would put 32 rows on 8 bank offsets (4-way conflicts): each step, every
+// thread first realigns one staged row in place (codes of block b to bytes
+// 32b..32b+31, its scale to an fp32 array), and the fragments are then single
+// 16-byte reads, conflict-free for 8 rows 144 bytes apart (Q8_GEMM_REALIGN;
+// 130 against 143 us).  (Build option
 // Q8_GEMM_OUTER=1 forms the rank-1 scale products of a block as an outer
 // product on the fp32 matrix core instead, same register layout, leaving 2
 // VALU operations: 150.5 against 141.3 us with each tile's sums pinned in
@@ -65,13 +69,21 @@ constexpr int kStepChunks = (kStepRowBytes + 15) / 16;      // 9 or 17 16-byte c
 constexpr int kRowStride = 16 * kStepChunks;                // staged row: 144 or 272 B
 constexpr int kStageRows = kBM + kBN;                       // 256
 constexpr int kStageLoads = kStageRows * kStepChunks / kGThreads;   // 9 or 17 per thread
+#ifndef Q8_GEMM_REALIGN
+#define Q8_GEMM_REALIGN 1
+#endif
+static_assert(!Q8_GEMM_REALIGN || (kStepBlocks <= 4 && kStageRows == kGThreads),
+              "realigning: one staged row of up to 4 blocks per thread");
 #ifndef Q8_GEMM_PIN
 #define Q8_GEMM_PIN 1
+#endif
+#ifndef Q8_GEMM_PIN_VALU
+#define Q8_GEMM_PIN_VALU 0
 #endif
 #ifndef Q8_GEMM_OUTER
 #define Q8_GEMM_OUTER 0          // scale products on the fp32 matrix core (1) or the VALU (0)
 #endif
-static_assert(kStepBlocks == 4 || kStepBlocks == 8, "K step of 4 or 8 blocks");
+static_assert(kStepBlocks == 2 || kStepBlocks == 4 || kStepBlocks == 8, "K step of 2, 4 or 8 blocks");
 // the token/weight row boundary falls on a wave boundary of the load pattern
 static_assert((kBM * kStepChunks) % 64 == 0, "uniform buffer resource per load");
 
@@ -99,8 +111,11 @@ __device__ __forceinline__ v4i lds_codes16(const uint8_t *row, int off)
 
 // SUMS (validation build of the same kernel): every exact int32 block sum is
 // also written out.
+#ifndef Q8_GEMM_OCC
+#define Q8_GEMM_OCC 1
+#endif
 template <bool SUMS>
-__global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
+__global__ __launch_bounds__(kGThreads, Q8_GEMM_OCC) void gemm_q8_kernel(const GemmArgs a)
 {
     // Two K-step buffers as separate LDS objects: the compiler then orders an
     // LDS read only after the DMA loads into the buffer it reads (with one
@@ -176,16 +191,50 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
     // fills), issue st+1, unpack the scales, barrier, compute.  Raw barriers
     // with explicit waits: the workgroup fence of __syncthreads would also
     // wait for the loads of st+1.
-    auto body = [&](int st, const uint8_t *sb, uint8_t *next) {
+    auto body = [&](int st, uint8_t *sb, uint8_t *next) {
         __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's loads of st landed
         __builtin_amdgcn_s_barrier();
         issue(st + 1, next, st + 1 < steps);
+        if (Q8_GEMM_REALIGN) {
+            // thread t realigns staged row t in place: the codes of block b to
+            // bytes 32b .. 32b+31 (4-byte aligned, 16-byte reads from then on),
+            // its scale to sc[b][t]; the 16-byte reads of 8 consecutive rows
+            // (144 bytes apart) fall on distinct banks
+            uint8_t *rowp = sb + tid * kRowStride;
+            uint32_t d[4 * kStepChunks];
 #pragma unroll
-        for (int i = 0; i < kStepBlocks * kStageRows / kGThreads; ++i) {
-            const int e = tid + kGThreads * i;
-            const int r = e & (kStageRows - 1);
-            const int b = e >> 8;
-            sc[b][r] = half_bits_to_float(*(const uint16_t *)(sb + r * kRowStride + b * kBlockBytes));
+            for (int c = 0; c < kStepChunks; ++c) {
+                const u32x4 v = *(const u32x4 *)(rowp + 16 * c);
+                d[4 * c] = v.x; d[4 * c + 1] = v.y; d[4 * c + 2] = v.z; d[4 * c + 3] = v.w;
+            }
+            uint32_t cw[kStepBlocks][8];
+#pragma unroll
+            for (int b = 0; b < kStepBlocks; ++b) {
+                // block b at byte 34b: 34b = 4*(17b/2) (+2 when b is odd)
+                const int D = (17 * b) >> 1;
+                if ((b & 1) == 0) {
+                    sc[b][tid] = half_bits_to_float(d[D] & 0xffffu);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cw[b][j] = __builtin_amdgcn_alignbyte(d[D + j + 1], d[D + j], 2);
+                } else {
+                    sc[b][tid] = half_bits_to_float(d[D] >> 16);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cw[b][j] = d[D + 1 + j];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kStepBlocks; ++b) {
+                *(u32x4 *)(rowp + 32 * b) = (u32x4){cw[b][0], cw[b][1], cw[b][2], cw[b][3]};
+                *(u32x4 *)(rowp + 32 * b + 16) = (u32x4){cw[b][4], cw[b][5], cw[b][6], cw[b][7]};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kStepBlocks * kStageRows / kGThreads; ++i) {
+                const int e = tid + kGThreads * i;
+                const int r = e & (kStageRows - 1);
+                const int b = e >> 8;
+                sc[b][r] = half_bits_to_float(*(const uint16_t *)(sb + r * kRowStride + b * kBlockBytes));
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the scales are written
         __builtin_amdgcn_s_barrier();
@@ -196,12 +245,21 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
         for (int b = 0; b < kStepBlocks; ++b) {
             const int off = b * kBlockBytes + 2 + 16 * h;
             v4i A[2], B[2];
+            if (Q8_GEMM_REALIGN) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                A[i] = lds_codes16(sb + (64 * wm + 32 * i + li) * kRowStride, off);
+                for (int i = 0; i < 2; ++i)
+                    A[i] = *(const v4i *)(sb + (64 * wm + 32 * i + li) * kRowStride + 32 * b + 16 * h);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                B[j] = lds_codes16(sb + (kBM + 64 * wn + 32 * j + li) * kRowStride, off);
+                for (int j = 0; j < 2; ++j)
+                    B[j] = *(const v4i *)(sb + (kBM + 64 * wn + 32 * j + li) * kRowStride + 32 * b + 16 * h);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    A[i] = lds_codes16(sb + (64 * wm + 32 * i + li) * kRowStride, off);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    B[j] = lds_codes16(sb + (kBM + 64 * wn + 32 * j + li) * kRowStride, off);
+            }
             // Scale products of the block as outer products on the fp32 matrix
             // core: P(i,j) = dx_i (x) dw_j with k = 2 and the second k row zero,
             // so P lands in the same 32x32 register layout as the int32 tile
@@ -246,8 +304,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_q8_kernel(const GemmArgs a)
                         }
                     } else {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
+                        for (int r = 0; r < 16; ++r) {
                             acc[i][j][r] = fmaf(dx[r] * bdw[j], (float)s[r], acc[i][j][r]);
+                            if (Q8_GEMM_PIN_VALU) asm volatile("" : "+v"(acc[i][j][r]));
+                        }
                     }
                 }
             }
