@@ -277,7 +277,7 @@ struct PgArgs {
     int n_out;               // n_ff (up_gate) or n_embd (down)
     int nb;                  // blocks per A / weight row (K / 32)
     int n_used;              // up_gate: A row of slot s is token s / n_used
-    int max_tiles, tiles_n;
+    int tiles_n;             // column blocks
     int32_t *sums;           // validation (EMIT kernels): [slot][w_rows][nb] block sums
     uint8_t *hq_codes;       // R8 up_gate: q(h) in the A layout of the down product, or null
     float *hq_scales;
@@ -289,6 +289,28 @@ template <bool UG>
 constexpr int pg_cols()
 {
     return UG ? 32 * kPWaves / 2 : 32 * kPWaves;
+}
+
+// The work item (column block nt, tile mt) of this workgroup; false when it has
+// none.  The grid is sized for the largest tile count; the T * tiles_n items of
+// the tiles that exist (T, the routing's tile count, is known on the device
+// only) are cut into 8 equal contiguous ranges, one per XCD (workgroups reach
+// the XCDs round robin in launch order), so every XCD gets the same share, the
+// workgroups with items are the first launched on each XCD, and consecutive
+// items -- the tiles of one expert for one column block, which read the same
+// weight rows -- run on one XCD and share its L2.
+__device__ __forceinline__ bool pg_work(const PgArgs &a, int &nt, int &mt)
+{
+    const int T = a.hdr[1];
+    const int n = T * a.tiles_n;
+    const int per = (n + 7) >> 3;
+    const int j = (int)(blockIdx.x >> 3);
+    if (j >= per) return false;
+    const int w = (int)(blockIdx.x & 7) * per + j;
+    if (w >= n) return false;
+    nt = w / T;
+    mt = w - nt * T;
+    return true;
 }
 
 // EMIT (validation builds of the same kernel): every exact int32 block sum is
@@ -312,13 +334,8 @@ __global__ __launch_bounds__(kPThreads) void moe_gemm_kernel(const PgArgs a)
     const int h = lane >> 5;
     const int li = lane & 31;
 
-    // work = (column block, tile) with tiles fastest; consecutive work items
-    // (the tiles of one expert for one column block) share an XCD
-    const int nwg = (int)gridDim.x;
-    const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-    const int nt = work / a.max_tiles;
-    const int mt = work - nt * a.max_tiles;
-    if (nt >= a.tiles_n || mt >= a.hdr[1]) return;
+    int nt, mt;
+    if (!pg_work(a, nt, mt)) return;
     const TileEntry te = a.tiles[mt];
     const int nb = a.nb;
     const int steps = nb / 4;
@@ -514,27 +531,67 @@ constexpr int kR8Chunk = Q8_PG_R8_CHUNK;
 #define Q8_PG_R8_DEPTH 8
 #endif
 constexpr int kR8Depth = Q8_PG_R8_DEPTH;       // weight blocks in flight per wave
-static_assert(kR8Chunk % kR8Depth == 0, "whole prefetch batches per chunk");
-static_assert(kR8Chunk * 1024 >= 2 * 16384, "the up_gate epilogue's up sums and h tile fit the A tile");
+// s_waitcnt operand for vmcnt(2 * kR8Depth) with the other counters left
+// alone (vmcnt bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15)
+constexpr int kVmcntDepth = ((2 * kR8Depth) & 15) | (((2 * kR8Depth) >> 4) << 14) | 0x70 | 0xf00;
+static_assert(2 * kR8Depth < 64, "vmcnt holds at most 63");
 // Build options of the kernel below, kept for measurement (512-token layer,
-// R8 rows, per layer): Q8_PG_OUTER=1 forms the 16 scale products of a block as
-// an fp32 matrix-core outer product (2 VALU operations left per product
-// instead of 3): 208 against 206 us; Q8_PG_R8_DEPTH (weight blocks in flight
-// per wave) 4: 203, 16: 235 (3 waves per SIMD) and 274 us (4, with spills);
-// Q8_PG_R8_CHUNK=32 with Q8_PG_R8_OCC=6 (three workgroups per CU): 218 us.
+// R8 rows, per layer, 186 us with the defaults): Q8_PG_OUTER=1 forms the 16
+// scale products of a block as an fp32 matrix-core outer product (2 VALU
+// operations left per product instead of 3): 185 us; Q8_PG_R8_DEPTH (weight
+// blocks in flight per wave) 4: 184 us (16: 235 us and more with the earlier
+// work order); Q8_PG_R8_CHUNK=32 with Q8_PG_R8_OCC=6 and depth 4 (three
+// workgroups per CU): 187 us; down workgroups of 4 waves
+// (Q8_PG_R8_DN_WAVES=4, chunk 32, four workgroups per CU): 191 us.  Per
+// workgroup timestamps (s_memrealtime) put a workgroup's life at about 10 us
+// waiting for its first blocks, 21 us in the K loop and 8 us in the epilogue
+// (4 of them waiting for the last wave); the HBM reads (483 MB of the 428 MB
+// of up_gate weights: the second tile of an expert mostly hits L2) run near
+// what 64-lane loads of four 256-byte runs reach in a plain read (5.4 TB/s
+// against 6.1 TB/s for 1 KB runs).
 #ifndef Q8_PG_OUTER
 #define Q8_PG_OUTER 0           // scale products on the fp32 matrix core (1) or the VALU (0)
 #endif
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <bool UG, bool EMIT>
 #ifndef Q8_PG_R8_OCC
 #define Q8_PG_R8_OCC 2
 #endif
-__global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(const PgArgs a)
+// the down product's workgroups: waves (32 output columns each) and A-tile
+// chunk in blocks
+#ifndef Q8_PG_R8_DN_WAVES
+#define Q8_PG_R8_DN_WAVES 8
+#endif
+#ifndef Q8_PG_R8_DN_CHUNK
+#define Q8_PG_R8_DN_CHUNK 64
+#endif
+#ifndef Q8_PG_R8_DN_OCC
+#define Q8_PG_R8_DN_OCC 2
+#endif
+constexpr int kR8DnWaves = Q8_PG_R8_DN_WAVES;
+constexpr int kR8DnChunk = Q8_PG_R8_DN_CHUNK;
+static_assert(kR8DnChunk % kR8Depth == 0, "whole prefetch batches per chunk");
+
+// NW waves of 32 output columns (up_gate: 8, waves w and w + 4 the gate and
+// up rows of the same columns), the A tile staged CH blocks at a time
+template <bool UG, int NW>
+constexpr int pg_r8_cols()
 {
-    __shared__ __align__(16) uint8_t la[kR8Chunk * 1024];
-    __shared__ __align__(16) float ldx[kR8Chunk * kPBM];
+    return UG ? 32 * NW / 2 : 32 * NW;
+}
+
+template <bool UG, bool EMIT, int NW, int CH, int OCC>
+__global__ __launch_bounds__(NW * kWave, OCC) void moe_r8_gemm_kernel(const PgArgs a)
+{
+    static_assert(!UG || NW == 8, "up_gate pairs waves w and w + 4");
+    static_assert(!UG || CH * 1024 >= 2 * 16384, "the up_gate epilogue's up sums and h tile fit the A tile");
+    static_assert(CH % kR8Depth == 0, "whole prefetch batches per chunk");
+    // token scales first, then the token codes: every scale read of the K loop
+    // then has an address below 64 KB, which the LDS read's immediate offset
+    // field can hold (no vector address arithmetic per block)
+    __shared__ __align__(16) uint8_t smem[CH * kPBM * 4 + CH * 1024];
+    float *const ldx = (float *)smem;
+    uint8_t *const la = smem + CH * kPBM * 4;
     __shared__ int a_row[kPBM];
     __shared__ int a_slot[kPBM];
 
@@ -544,11 +601,8 @@ __global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(co
     const int h = lane >> 5;
     const int li = lane & 31;
 
-    const int nwg = (int)gridDim.x;
-    const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-    const int nt = work / a.max_tiles;
-    const int mt = work - nt * a.max_tiles;
-    if (nt >= a.tiles_n || mt >= a.hdr[1]) return;
+    int nt, mt;
+    if (!pg_work(a, nt, mt)) return;
     const TileEntry te = a.tiles[mt];
     const int nb = a.nb;
 
@@ -561,7 +615,7 @@ __global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(co
 
     // this wave's 32 weight rows = groups wrow0/8 .. wrow0/8 + 3 of the expert;
     // lane l takes row l%32 (group (l%32)/8, row l%8 of it), half l/32
-    const int cbase = pg_cols<UG>() * nt + 32 * (UG ? (wave & 3) : wave);
+    const int cbase = pg_r8_cols<UG, NW>() * nt + 32 * (UG ? (wave & 3) : wave);
     const int col = cbase + li;
     const bool wave_live = cbase < a.n_out;
     const int wrow0 = UG && wave >= 4 ? a.n_out + cbase : cbase;
@@ -573,17 +627,23 @@ __global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(co
         (void *)(a.w + (int64_t)te.expert * a.expert_bytes), 0, past, kBufferWord3);
 
     u32x4 wc[kR8Depth];
-    uint32_t ws16[kR8Depth];
+    uint32_t ws32[kR8Depth];         // the aligned dword holding the row's binary16 scale
     // default cache policy: the second tile of an expert (more than 32
-    // slots) runs beside the first on the same XCD and finds its rows in L2
+    // slots) runs beside the first on the same XCD and finds its rows in L2.
+    // The lane's part of an offset is fixed; block b adds the same 256 b
+    // (codes) and 16 b (scales) in every lane, passed as the scalar offset,
+    // so a block's loads cost no vector arithmetic.  The prefetches past the
+    // last block (never consumed) read the last block again.  The scale comes
+    // as the dword holding it (rows r and r ^ 1; a whole 32-bit register, so
+    // the compiler needs no zero-extension of it before the first use).
+    const int vcode = goff + 16 * nb + 32 * r + 16 * h;
+    const int vscale = goff + 2 * (r & 6);
+    const int sshift = 16 * (r & 1);
     auto issue = [&](int b, int i) {
-        const bool in = b < nb;
-        wc[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            rw, in ? goff + 16 * nb + 32 * (8 * b + r) + 16 * h : past, 0, 0);
-        ws16[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, in ? goff + 2 * (8 * b + r) : past, 0, 0);
+        const int bc = min(b, nb - 1);
+        ws32[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, vscale, 16 * bc, 0);
+        wc[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vcode, 256 * bc, 0);
     };
-#pragma unroll
-    for (int i = 0; i < kR8Depth; ++i) issue(i, i);
 
     float acc[16];
 #pragma unroll
@@ -594,24 +654,52 @@ __global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(co
     const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.a_scales, 0, a.a_rows * nb * 4, kBufferWord3);
     const int a_past = a.a_rows * nb * 32;
-
-    for (int kb0 = 0; kb0 < nb; kb0 += kR8Chunk) {
-        const int kc = min(kR8Chunk, (nb - kb0 + kR8Depth - 1) / kR8Depth * kR8Depth);
-        __syncthreads();                 // a_row written; the previous chunk fully read
-        const int ar = a_row[li];
-        for (int bi = wave; bi < kc; bi += kPWaves) {
+    auto chunk_blocks = [&](int kb0) {
+        return min(CH, (nb - kb0 + kR8Depth - 1) / kR8Depth * kR8Depth);
+    };
+    // the tile's codes and scales of blocks kb0 .. kb0 + kc - 1 into LDS
+    // (zeros past the row or for missing slots), this wave's share
+    auto stage = [&](int ar, int kb0, int kc) {
+        for (int bi = wave; bi < kc; bi += NW) {
             const int b = kb0 + bi;
             const int off = ar >= 0 && b < nb ? (ar * nb + b) * 32 + 16 * h : a_past;
             auto *dst = (__attribute__((address_space(3))) void *)(la + 1024 * bi);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, dst, 16, off, 0, 0, 0);
         }
-        for (int q = wave; 2 * q < kc; q += kPWaves) {
+        for (int q = wave; 2 * q < kc; q += NW) {
             const int b = kb0 + 2 * q + h;
             const int off = ar >= 0 && b < nb ? (ar * nb + b) * 4 : a_past;
             auto *dst = (__attribute__((address_space(3))) void *)(ldx + 64 * q);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, dst, 4, off, 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's copies landed
+    };
+
+    // The first chunk's copies go out before the weight prefetch: loads
+    // complete in issue order, so the wave waits for its copies only (at
+    // most the 2 * kR8Depth weight loads issued after them still in flight)
+    // and starts on block 0 while the later blocks are still arriving.
+    // The empty asm statements keep the compiler from reordering the loads.
+    __syncthreads();                     // a_row written
+    const int ar = a_row[li];
+    stage(ar, 0, chunk_blocks(0));
+    asm volatile("" ::: "memory");
+    // block by block, scale before codes: the order the K loop issues them
+    // in, so its waits count the same loads from the first block on
+#pragma unroll
+    for (int i = 0; i < kR8Depth; ++i) {
+        issue(i, i);
+        asm volatile("" ::: "memory");
+    }
+
+    for (int kb0 = 0; kb0 < nb; kb0 += CH) {
+        const int kc = chunk_blocks(kb0);
+        if (kb0 == 0) {
+            __builtin_amdgcn_s_waitcnt(kVmcntDepth);
+        } else {
+            __syncthreads();             // the previous chunk fully read
+            stage(ar, kb0, kc);
+            __builtin_amdgcn_s_waitcnt(0x3f70);    // vmcnt(0): this wave's copies landed
+        }
         __syncthreads();
 
         for (int bi0 = 0; bi0 < kc; bi0 += kR8Depth) {
@@ -634,7 +722,11 @@ __global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(co
                             a.sums[((int64_t)a_slot[row] * w_rows + wr) * nb + kb0 + bi] = sres[q];
                     }
                 }
-                const float dw = half_bits_to_float(ws16[i]);
+                // the pin keeps the shift here: hoisted to the top of the
+                // unrolled loop it would wait for every block in flight
+                uint32_t sw = ws32[i];
+                asm volatile("" : "+v"(sw));
+                const float dw = half_bits_to_float(sw >> sshift);
                 if (Q8_PG_OUTER) {
                     // P(r, c) = dx_r * dw_c as an outer product on the fp32 matrix
                     // core (k = 2, the second k row zero): the same 32x32
@@ -690,9 +782,9 @@ __global__ __launch_bounds__(kPThreads, Q8_PG_R8_OCC) void moe_r8_gemm_kernel(co
         __syncthreads();
         // q(h) of the tile (its rows x 4 blocks of 32 columns) with the rule and
         // the bytes of q8_0_quantize_rows, in the down product's A layout
-        const int c0 = pg_cols<UG>() * nt;
+        const int c0 = pg_r8_cols<UG, NW>() * nt;
         const int nbf = a.n_out / 32;
-        for (int k = tid >> 3; k < kPBM * 4; k += kPThreads / 8) {
+        for (int k = tid >> 3; k < kPBM * 4; k += NW * kWave / 8) {
             const int row = k >> 2, cb = k & 3;
             const bool live = row < te.rows && c0 + 32 * cb < a.n_out;
             const float4 v = live ? *(const float4 *)&ht[row * 128 + 32 * cb + 4 * (tid & 7)]
@@ -812,17 +904,20 @@ int launch_grouped(const uint8_t *a_codes, const float *a_scales, int64_t a_rows
     p.n_out = (int)n_out;
     p.nb = (int)nb;
     p.n_used = (int)n_used;
-    p.max_tiles = (int)L.max_tiles;
-    p.tiles_n = (int)((n_out + pg_cols<UG>() - 1) / pg_cols<UG>());
+    constexpr int NW = UG ? kPWaves : kR8DnWaves;
+    constexpr int CH = UG ? kR8Chunk : kR8DnChunk;
+    constexpr int OCC = UG ? Q8_PG_R8_OCC : Q8_PG_R8_DN_OCC;
+    const int cols = R8 ? pg_r8_cols<UG, NW>() : pg_cols<UG>();
+    p.tiles_n = (int)((n_out + cols - 1) / cols);
     int64_t grid = L.max_tiles * p.tiles_n;
     grid = (grid + 7) & ~(int64_t)7;
     if (grid > 0x7fffffff) return -4;
     if (R8 && sums)
-        hipLaunchKernelGGL((moe_r8_gemm_kernel<UG, true>), dim3((unsigned)grid), dim3(kPThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((moe_r8_gemm_kernel<UG, true, NW, CH, OCC>), dim3((unsigned)grid),
+                           dim3(NW * kWave), 0, stream, p);
     else if (R8)
-        hipLaunchKernelGGL((moe_r8_gemm_kernel<UG, false>), dim3((unsigned)grid), dim3(kPThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((moe_r8_gemm_kernel<UG, false, NW, CH, OCC>), dim3((unsigned)grid),
+                           dim3(NW * kWave), 0, stream, p);
     else if (sums)
         hipLaunchKernelGGL((moe_gemm_kernel<UG, true>), dim3((unsigned)grid), dim3(kPThreads), 0,
                            stream, p);
@@ -904,7 +999,9 @@ int moe_prefill_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_exp
     // each launch; here before the call enqueues anything)
     const PrefillWs L = prefill_layout(n_tok, n_embd, n_ff, n_expert, n_used);
     const int64_t ug = L.max_tiles * ((n_ff + pg_cols<true>() - 1) / pg_cols<true>());
-    const int64_t dn = L.max_tiles * ((n_embd + pg_cols<false>() - 1) / pg_cols<false>());
+    constexpr int dn_cols = pg_r8_cols<false, kR8DnWaves>() < pg_cols<false>()
+                                ? pg_r8_cols<false, kR8DnWaves>() : pg_cols<false>();
+    const int64_t dn = L.max_tiles * ((n_embd + dn_cols - 1) / dn_cols);
     return (ug + 7 > 0x7fffffffLL || dn + 7 > 0x7fffffffLL) ? -4 : 0;
 }
 
