@@ -26,7 +26,16 @@
 // VALU operations: 150.5 against 141.3 us with each tile's sums pinned in
 // place (Q8_GEMM_PIN, else 198 us at 1 wave per SIMD), so it is off.  The same
 // outer product from a K = 16 binary16 product (v_mfma_f32_32x32x16_f16, the
-// scales' own bits) measured 138.6 to 142.8 us against 133.4 us.)
+// scales' own bits) measured 138.6 to 142.8 us against 133.4 us.  A variant
+// with the codes themselves on the binary16 matrix cores -- a Q8_0 code is
+// exact in binary16 and a block's sums are exact in the fp32 accumulator of
+// v_mfma_f32_32x32x16_f16, so two such instructions give S with no
+// conversion, a third gives the scale products, and one fused multiply-add
+// per element and block is left (40% fewer VALU instructions, 3x the matrix
+// instructions, each thread converting its staged row to binary16 in 2-block
+// steps) -- measured 142-144 us against 131-132 us: at 2 waves per SIMD
+// (202 VGPRs, 76 KB of LDS) neither pipe fills (VALU 38%, matrix cores 27% of
+// the active cycles), the waves wait on LDS reads and result latencies.)
 //
 // Work decomposition:
 //  * Workgroup = 4 waves, output tile 128 tokens x 128 weight rows; wave
