@@ -1221,9 +1221,9 @@ def main():
         print(json.dumps(run_extra(args, q, synth)))
         return
 
-    traffic_file = args.traffic or (os.path.join(ROOT, "profiles",
-                                                "r8_matvec_kernel_llama110m_decode_step.traffic.json")
-                                    if args.workload == "c2" else None)
+    traffic_file = args.traffic or os.path.join(
+        ROOT, "profiles", "r8_matvec_kernel_llama110m_decode_step.traffic.json"
+        if args.workload == "c2" else "stream_mfma_kernel_gpt2_batch8_decode_step.traffic.json")
     if traffic_file and os.path.exists(traffic_file):
         t = read_traffic(traffic_file)
         out["roofline"]["traffic"] = t
