@@ -437,6 +437,9 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 // row per slot to the workspace and the combine kernel of the native path
 // (ascending u) forms out.
 
+#ifndef Q8_GT_ROUNDS
+#define Q8_GT_ROUNDS 8            // rounds of the resident waves the work per wave aims at
+#endif
 #ifndef Q8_GT_SLICES
 #define Q8_GT_SLICES 16
 #endif
@@ -990,13 +993,16 @@ int launch_r8_gather(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n
     const size_t dn_lds = gt_lds(n_slots, n_ff / 32);
     if (ug_lds > (size_t)max_lds_bytes() || dn_lds > (size_t)max_lds_bytes()) return -4;
     const R8DecodeWs W = r8_decode_ws(n_tok, n_embd, n_ff, n_used);
-    // Work per wave: as much as keeps about 4 rounds of the resident waves
-    // busy (8 per CU here) -- few layers per call (a model's layer after layer)
-    // want short streams spread over the whole chip, many layers long streams
-    // that pay the ownership scan and the row staging once.  The active
-    // experts are bounded by min(n_expert, slots) per layer.
+    // Work per wave: as much as keeps about Q8_GT_ROUNDS rounds of the
+    // resident waves busy (8 per CU here) -- few layers per call (a model's
+    // layer after layer) want short streams spread over the whole chip, many
+    // layers long streams that pay the ownership scan and the row staging
+    // once.  The active experts are bounded by min(n_expert, slots) per layer.
+    // One layer of 16 tokens per call, 30 calls: 8 rounds 2.75 ms, 4 rounds
+    // 2.78 ms, 2 rounds 2.82 ms, 1 round 3.18 ms, 16 rounds 2.94 ms (30 layers
+    // per call reach the longest streams at any of these).
     const int64_t act = (int64_t)n_layers * (n_expert < n_slots ? n_expert : n_slots);
-    const int64_t target = 4 * 256 * 8;
+    const int64_t target = (int64_t)Q8_GT_ROUNDS * 256 * 8;
     int ug_cols = 4, dn_groups = 8;
     while (ug_cols > 1 && act * (n_ff / 8) / ug_cols < target) ug_cols /= 2;
     while (dn_groups > 1 && act * (n_embd / 8) / dn_groups < target) dn_groups /= 2;
