@@ -997,13 +997,16 @@ def default_extras(args, q, synth):
     nbytes = q8_bytes(n, k) + q8_bytes(1, k) + 4 * n
     reps = 20
 
-    def many(fn):
+    def many_n(fn, count):
         def body():
-            for _ in range(reps):
+            for _ in range(count):
                 fn()
         fn()
         torch.cuda.synchronize()
         return capture(body)
+
+    def many(fn):
+        return many_n(fn, reps)
     prot = protocol({"native": many(lambda: q.q8_0_matvec(w, x, n, k, y=y)),
                      "r8": many(lambda: q.q8_0_matvec_r8(wr, x, n, k, y=y))}, rounds=6, best_of=3)
     c5b = {"shape": [n, k], "bytes_per_launch": nbytes,
@@ -1097,6 +1100,61 @@ def default_extras(args, q, synth):
         c4[f"tokens_{n_tok}"] = res
         del layers, ug, dn, r8all, graphs
     out["c4_moe_expert_ffn_30_layers"] = c4
+    del wl
+    torch.cuda.synchronize()
+    # --- the prefill GEMM 512 x 4096 x 14336 on the int8 matrix cores
+    m, n, k = 512, 14336, 4096
+    w = q.q8_0_quantize_rows(synth.normal_f32_torch((n, k), 0.02, dev, 0, "c5a", "w"))
+    x = q.q8_0_quantize_rows(synth.normal_f32_torch((m, k), 1.0, dev, 0, "c5a", "x"))
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    reps = 20
+    prot = protocol({"gemm": many(lambda: q.q8_0_matmul(w, x, n, k, m, y=y))}, rounds=6, best_of=3)
+    tt = prot["gemm"]["median"] / reps
+    ops = 2 * m * n * k
+    out["c5a_prefill_gemm"] = {
+        "shape": [m, n, k], "kernel": "gemm_q8_kernel",
+        "timing": f"{reps} launches per graph; 6 rounds (first dropped), best of 3, median",
+        "us": round(tt * 1e6, 2), "tops": round(ops / tt / 1e12, 1),
+        "frac_of_int8_peak": round(ops / tt / 1e12 / 5000.0, 4),
+        "prompt_tokens_per_s_equiv": round(m / tt, 1)}
+    del w, x, y
+    # --- the expert FFN for 512 prompt tokens of one layer (grouped matrix-core
+    # products), over native rows and over R8 rows
+    n_tok, E, n_embd, n_ff, U = 512, 128, 2048, 768, 8
+    wug = q.q8_0_quantize_rows(synth.normal_f32_torch((E * 2 * n_ff, n_embd), 0.02, dev, 0, "c4p", "ug"))
+    wd = q.q8_0_quantize_rows(synth.normal_f32_torch((E * n_embd, n_ff), 0.02, dev, 0, "c4p", "down"))
+    ids_h = synth.expert_ids(n_tok, U, E, 0, "c4p", "ids")
+    ids = torch.from_numpy(ids_h).to(dev)
+    cw = torch.from_numpy(synth.combine_weights(n_tok, U, 0, "c4p", "cw")).to(dev)
+    xf = synth.normal_f32_torch((n_tok, n_embd), 1.0, dev, 0, "c4p", "x")
+    h = torch.empty((n_tok, U, n_ff), dtype=torch.float32, device=dev)
+    o = torch.empty((n_tok, n_embd), dtype=torch.float32, device=dev)
+    ws = q.moe_workspace(n_tok, n_embd, n_ff, E, U, dev)
+    r8 = dict(w_up_gate_r8=q.q8_0_repack_r8(wug, E * 2 * n_ff, n_embd),
+              w_down_r8=q.q8_0_repack_r8(wd, E * n_embd, n_ff), x=xf, ids=ids, cw=cw,
+              h=torch.empty_like(h), out=torch.empty_like(o),
+              ws=q.moe_r8_workspace(n_tok, n_embd, n_ff, E, U, dev))
+    active = len(np.unique(ids_h)) * (q8_bytes(2 * n_ff, n_embd) + q8_bytes(n_embd, n_ff))
+    macs = n_tok * U * (n_embd * 2 * n_ff + n_ff * n_embd)
+    reps = 5
+
+    def native():
+        q.moe_up_gate_swiglu(wug, xf, ids, n_embd, n_ff, E, ws, h=h)
+        q.moe_down_combine(wd, h, ids, cw, n_ff, n_embd, E, ws, out=o)
+    prot = protocol({"r8": many_n(lambda: q.moe_r8_ffn_batched([r8], n_embd, n_ff, E), reps),
+                     "native": many_n(native, reps)}, rounds=6, best_of=3)
+    c4p = {"tokens": n_tok, "shape": {"n_embd": n_embd, "n_ff": n_ff, "n_expert": E, "n_used": U},
+           "active_weight_bytes": active,
+           "timing": f"{reps} layers per graph; 6 rounds (first dropped), best of 3, median"}
+    for key, desc in (("r8", "R8 expert weights, one moe_r8_ffn_batched call (4 launches)"),
+                      ("native", "native rows, moe_up_gate_swiglu + moe_down_combine (6 launches)")):
+        tt = prot[key]["median"] / reps
+        c4p[key] = {"timing": desc, "us_per_layer": round(tt * 1e6, 2),
+                    "prompt_tokens_per_s": round(n_tok / tt, 1),
+                    "gbs": round(active / tt / 1e9, 1),
+                    "frac": round(active / tt / 1e9 / HBM_PEAK_GBS, 4),
+                    "tops": round(2 * macs / tt / 1e12, 1)}
+    out["c4p_moe_expert_ffn_prefill_512_tokens"] = c4p
     return out
 
 
