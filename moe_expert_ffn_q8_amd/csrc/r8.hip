@@ -280,8 +280,21 @@ int launch_r8_matvec(const R8Desc *d, int n_desc, bool x_f32, hipStream_t stream
     int nb_max = 1;
     int nj = 0;
     bool sums = false;
+    // Descriptors with the longest rows (most blocks per group) get the first
+    // workgroups, the rest keep their order: workgroups start in launch order,
+    // so the long groups no longer start last and set the tail of the launch
+    // (Llama-110M-shaped step, the k = 2048 products moved to the front:
+    // 19.55-19.60 against 19.90 us).  Outputs do not depend on the order.
+    int order[kStreamMaxJobs];
+    int live = 0;
     for (int i = 0; i < n_desc; ++i) {
         if (d[i].n == 0 || d[i].batch == 0) continue;
+        int p = live++;
+        for (; p > 0 && d[order[p - 1]].nb < d[i].nb; --p) order[p] = order[p - 1];
+        order[p] = i;
+    }
+    for (int oi = 0; oi < live; ++oi) {
+        const int i = order[oi];
         R8Job &j = a.job[nj++];
         j.w = d[i].w; j.x = d[i].x; j.y = d[i].y;
         j.w_bstride = d[i].w_bstride; j.x_bstride = d[i].x_bstride; j.y_bstride = d[i].y_bstride;
