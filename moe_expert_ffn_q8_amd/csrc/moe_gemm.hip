@@ -85,6 +85,9 @@ struct RouteArgs {
 };
 
 constexpr int kRouteWaves = kRouteThreads / kWave;      // 16
+constexpr int kRouteBatch = 4;                          // slot ids in flight per lane
+static_assert(kMoePrefillMaxSlots / kRouteWaves * (kRouteWaves - 1) < 65536,
+              "a wave's start within an expert's group fits a 16-bit field");
 
 __device__ __forceinline__ void route_tiles(const RouteArgs &a)
 {
@@ -106,34 +109,75 @@ __device__ __forceinline__ void route_tiles(const RouteArgs &a)
         (&wcnt[0][0])[i] = 0;
     if (tid == 0) bad = 0;
     __syncthreads();
-    for (int s = s_beg + lane; s < s_end; s += kWave) {
-        const int e = a.ids[s];
-        if (e < 0 || e >= a.n_expert) {
-            atomicOr(&bad, 1);
-            if (a.h_nan)
-                for (int j = 0; j < a.n_ff; ++j) a.h_nan[(int64_t)s * a.n_ff + j] = __builtin_nanf("");
-        } else {
-            atomicAdd(&cnt[e], 1);
-            atomicAdd(&wcnt[wave][e >> 1], (e & 1) ? 0x10000u : 1u);
+    // the ids are read kRouteBatch slots per lane at a time, all loads issued
+    // before any is used (one memory latency per 256 slots of a wave, not one
+    // per 64)
+    for (int s0 = s_beg; s0 < s_end; s0 += kRouteBatch * kWave) {
+        int ev[kRouteBatch];
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int s = s0 + k * kWave + lane;
+            ev[k] = s < s_end ? a.ids[s] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int s = s0 + k * kWave + lane;
+            const int e = ev[k];
+            if (s >= s_end) continue;
+            if (e < 0 || e >= a.n_expert) {
+                atomicOr(&bad, 1);
+                if (a.h_nan)
+                    for (int j = 0; j < a.n_ff; ++j) a.h_nan[(int64_t)s * a.n_ff + j] = __builtin_nanf("");
+            } else {
+                atomicAdd(&cnt[e], 1);
+                atomicAdd(&wcnt[wave][e >> 1], (e & 1) ? 0x10000u : 1u);
+            }
         }
     }
     __syncthreads();
-    // inclusive scans of the counts and of the tile counts (Hillis-Steele)
+    // inclusive scans of the counts and of the tile counts (thread e holds
+    // expert e): within each wave by lane shuffles, then over the wave totals
+    static_assert(kRouteThreads == kMoeMaxExperts, "one thread per expert");
+    __shared__ int wtot_c[kRouteWaves], wtot_t[kRouteWaves];
     const int c = cnt[tid];
     int vc = c, vt = (c + kPBM - 1) / kPBM;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int ac = __shfl_up(vc, d), at = __shfl_up(vt, d);
+        if (lane >= d) {
+            vc += ac;
+            vt += at;
+        }
+    }
+    if (lane == kWave - 1) {
+        wtot_c[wave] = vc;
+        wtot_t[wave] = vt;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int xc = lane < kRouteWaves ? wtot_c[lane] : 0;
+        int xt = lane < kRouteWaves ? wtot_t[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kRouteWaves; d <<= 1) {
+            const int ac = __shfl_up(xc, d), at = __shfl_up(xt, d);
+            if (lane >= d) {
+                xc += ac;
+                xt += at;
+            }
+        }
+        if (lane < kRouteWaves) {
+            wtot_c[lane] = xc;
+            wtot_t[lane] = xt;
+        }
+    }
+    __syncthreads();
+    if (wave > 0) {
+        vc += wtot_c[wave - 1];
+        vt += wtot_t[wave - 1];
+    }
     scan_c[tid] = vc;
     scan_t[tid] = vt;
     __syncthreads();
-    for (int d = 1; d < kMoeMaxExperts; d <<= 1) {
-        const int ac = tid >= d ? scan_c[tid - d] : 0;
-        const int at = tid >= d ? scan_t[tid - d] : 0;
-        __syncthreads();
-        vc += ac;
-        vt += at;
-        scan_c[tid] = vc;
-        scan_t[tid] = vt;
-        __syncthreads();
-    }
     const int off = vc - c;                        // exclusive
     const int toff = vt - (c + kPBM - 1) / kPBM;
     if (tid < a.n_expert) {
@@ -148,42 +192,52 @@ __device__ __forceinline__ void route_tiles(const RouteArgs &a)
     }
     // each wave's start within every expert's group: the counts of the waves
     // before it (exclusive prefix over waves, in place)
-    if (tid < kMoeMaxExperts) {
-        const int e = tid, sh = 16 * (e & 1);
+    // One thread per word: both 16-bit fields advance in one 32-bit add, and
+    // neither carries (a field's prefix over the waves before the last is
+    // below 15 * 4096 slots).
+    if (tid < kMoeMaxExperts / 2) {
         uint32_t run = 0;
         for (int w = 0; w < kRouteWaves; ++w) {
-            uint32_t *word = &wcnt[w][e >> 1];
-            const uint32_t c = (*word >> sh) & 0xffffu;
-            atomicAnd(word, ~(0xffffu << sh));
-            atomicOr(word, run << sh);
+            const uint32_t c = wcnt[w][tid];
+            wcnt[w][tid] = run;
             run += c;
         }
     }
     __syncthreads();
-    // scatter in slot order: a wave walks its range 64 slots at a time; a lane
-    // takes the next position of its expert after the lanes below it naming
-    // the same expert (found by matching the 10 bits of the id)
-    for (int s0 = s_beg; s0 < s_end; s0 += kWave) {
-        const int s = s0 + lane;
-        const int e = s < s_end ? a.ids[s] : -1;
-        const bool ok = e >= 0 && e < a.n_expert;
-        uint64_t peers = __ballot(ok);
+    // scatter in slot order: a wave walks its range 64 slots at a time (their
+    // ids read kRouteBatch steps ahead); a lane takes the next position of its
+    // expert after the lanes below it naming the same expert (found by
+    // matching the 10 bits of the id)
+    for (int s0 = s_beg; s0 < s_end; s0 += kRouteBatch * kWave) {
+        int ev[kRouteBatch];
 #pragma unroll
-        for (int bit = 0; bit < 10; ++bit) {
-            const uint64_t m = __ballot(((e >> bit) & 1) != 0);
-            peers &= ((e >> bit) & 1) ? m : ~m;
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int s = s0 + k * kWave + lane;
+            ev[k] = s < s_end ? a.ids[s] : -1;
         }
-        if (ok) {
-            const int sh = 16 * (e & 1);
-            const int run = (int)((wcnt[wave][e >> 1] >> sh) & 0xffffu);
-            const int rank = __popcll(peers & __lanemask_lt());
-            a.pairs[(e > 0 ? scan_c[e - 1] : 0) + run + rank] = s;
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int s = s0 + k * kWave + lane;
+            const int e = ev[k];
+            const bool ok = e >= 0 && e < a.n_expert;
+            uint64_t peers = __ballot(ok);
+#pragma unroll
+            for (int bit = 0; bit < 10; ++bit) {
+                const uint64_t m = __ballot(((e >> bit) & 1) != 0);
+                peers &= ((e >> bit) & 1) ? m : ~m;
+            }
+            if (ok) {
+                const int sh = 16 * (e & 1);
+                const int run = (int)((wcnt[wave][e >> 1] >> sh) & 0xffffu);
+                const int rank = __popcll(peers & __lanemask_lt());
+                a.pairs[(e > 0 ? scan_c[e - 1] : 0) + run + rank] = s;
+            }
+            wave_lds_sync();
+            // the lowest lane of each group of peers advances the group's position
+            if (ok && (peers & __lanemask_lt()) == 0)
+                atomicAdd(&wcnt[wave][e >> 1], (uint32_t)__popcll(peers) << (16 * (e & 1)));
+            wave_lds_sync();
         }
-        wave_lds_sync();
-        // the lowest lane of each group of peers advances the group's position
-        if (ok && (peers & __lanemask_lt()) == 0)
-            atomicAdd(&wcnt[wave][e >> 1], (uint32_t)__popcll(peers) << (16 * (e & 1)));
-        wave_lds_sync();
     }
 }
 
