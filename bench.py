@@ -912,6 +912,28 @@ def run_extra(args, q, synth):
                               "gbs": round(active_bytes / tr / 1e9, 1),
                               "pct_of_hbm_peak": round(active_bytes / tr / 1e9 / HBM_PEAK_GBS * 100, 2),
                               "tokens_per_s": round(n_tok / tr, 1)})
+        if n_tok == 1:
+            # layer after layer over the R8 weights: two launches per layer
+            # (moe_r8_ffn_batched per layer) and one (moe_r8_ffn_fused)
+            fz = [dict(d, ws=q.moe_r8_fused_workspace(n_embd, n_ff, E, U, dev)) for d in r8l]
+
+            def chained_two():
+                for d in r8l:
+                    q.moe_r8_ffn_batched([d], n_embd, n_ff, E)
+
+            def chained_one():
+                for d in fz:
+                    q.moe_r8_ffn_fused(d, n_embd, n_ff, E)
+            for key, fn, desc in (("r8_layer_after_layer", chained_two,
+                                   "moe_r8_ffn_batched per layer (2 launches per layer)"),
+                                  ("r8_fused_layer_after_layer", chained_one,
+                                   "moe_r8_ffn_fused per layer (1 launch per layer)")):
+                tl = _time_launches(fn, args.steps, args.warmup) / args.steps
+                res[key] = {"timing": desc, "us_per_step": round(tl * 1e6, 2),
+                            "gbs": round(active_bytes / tl / 1e9, 1),
+                            "pct_of_hbm_peak": round(active_bytes / tl / 1e9 / HBM_PEAK_GBS * 100, 2),
+                            "tokens_per_s": round(n_tok / tl, 1)}
+            del fz
         del r8l
         if args.moe_mode in ("both", "layers"):
             t = _time_launches(step, args.steps, args.warmup) / args.steps
@@ -1047,6 +1069,8 @@ def default_extras(args, q, synth):
                      ws8=q.moe_r8_workspace(n_tok, n_embd, n_ff, E, U, dev))
             d["r8"] = dict(w_up_gate_r8=d["wug_r8"], w_down_r8=d["wd_r8"], x=d["xf"], ids=d["ids"],
                            cw=d["cw"], h=d["h"], out=d["out"], ws=d["ws8"])
+            if n_tok == 1:
+                d["r8f"] = dict(d["r8"], ws=q.moe_r8_fused_workspace(n_embd, n_ff, E, U, dev))
             layers.append(d)
         ug = [dict(w_up_gate=d["wug"], x=d["xf"], ids=d["ids"], h=d["h"], ws=d["ws"]) for d in layers]
         dn = [dict(w_down=d["wd"], h=d["h"], ids=d["ids"], cw=d["cw"], out=d["out"], ws=d["ws"])
@@ -1063,6 +1087,10 @@ def default_extras(args, q, synth):
             for d in layers:
                 q.moe_r8_ffn_batched([d["r8"]], n_embd, n_ff, E)
 
+        def chained_r8_fused():
+            for d in layers:
+                q.moe_r8_ffn_fused(d["r8f"], n_embd, n_ff, E)
+
         def grouped_native():
             q.moe_up_gate_swiglu_batched(ug, n_embd, n_ff, E)
             q.moe_down_combine_batched(dn, n_ff, n_embd, E)
@@ -1075,6 +1103,9 @@ def default_extras(args, q, synth):
                                                     "after layer"),
                  "chained_r8": (chained_r8, f"R8 expert weights, {nl} launches per layer, layer "
                                             "after layer"),
+                 **({"chained_r8_fused": (chained_r8_fused, "R8 expert weights, one launch per "
+                                                            "layer (moe_r8_ffn_fused), layer after "
+                                                            "layer")} if n_tok == 1 else {}),
                  "grouped_native": (grouped_native, "native rows, all 30 layers in one up_gate "
                                                     "and one down call (3 launches: up_gate, down, "
                                                     "combine)"),

@@ -541,6 +541,35 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
                        int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used,
                        void *stream);
 
+/* moe_r8_ffn_fused -- one token through one layer of the expert FFN over R8
+ * expert weights in ONE launch: the form for a model whose layers run one
+ * after another (each layer's input is the previous layer's output), where
+ * moe_r8_ffn_batched takes two launches per layer.  Same inputs and outputs
+ * as moe_r8_ffn_batched with n_tok = 1 and one descriptor (Gemma-4-on-Xeon
+ * page, "GPUなしで13年前のXeon上でGemma 4 26Bを毎秒5トークンで実行する", section
+ * on the broken op paths: the expert FFN with mul_mat_id and the combine).
+ * h is the same bits as moe_r8_ffn_batched's; out is the same sums of the
+ * same block terms (d_w * d_h) * s, added in another order (per slot over
+ * the blocks of h ascending, then over the slots ascending with cw), so it
+ * matches within rounding, not bit for bit.
+ * Measured on the Gemma-4-26B-A4B expert shape (30 layers, one after
+ * another): slower than moe_r8_ffn_batched per layer, 562 against 445 us per
+ * step.  The launch it saves costs less than the in-kernel summation: every
+ * workgroup's terms reach agent scope, a ticket, the last workgroups' wait,
+ * and their agent-scope reads are one chain of memory round trips.
+ * Limits: n_embd % 256 == 0 and those of moe_r8_ffn_batched's one-token path
+ * (Q8_E_UNSUPPORTED otherwise).
+ * Workspace: moe_r8_fused_workspace_bytes(...) bytes (0 for an unsupported
+ * shape), 256-byte aligned; its first 256 bytes must be zero before the
+ * first call (every call leaves them zero).  Word 0 is the error word: bit 0
+ * set when an id is out of range (then that slot's h row and every out row
+ * are NaN), bit 1 when the launch's final summation gave up waiting for its
+ * workgroups (out is then invalid).  One workspace per stream: two calls
+ * that may run at the same time must not share it. */
+size_t moe_r8_fused_workspace_bytes(int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
+int moe_r8_ffn_fused(const moe_r8_ffn_desc *desc, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                     int64_t n_used, void *stream);
+
 /* moe_r8_ffn_batched_noalloc -- moe_r8_ffn_batched for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same kernels, h and out bit for bit,

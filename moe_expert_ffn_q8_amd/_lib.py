@@ -139,6 +139,8 @@ _SIGS = {
                                   _i64, _vp]),
     "moe_r8_ffn_batched_noalloc": (_int, [ctypes.POINTER(MoeR8FfnDesc), _i64, _i64, _i64, _i64,
                                           _i64, _i64, _vp]),
+    "moe_r8_fused_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
+    "moe_r8_ffn_fused": (_int, [ctypes.POINTER(MoeR8FfnDesc), _i64, _i64, _i64, _i64, _vp]),
     "kq_matvec_batched": (_int, [_int, ctypes.POINTER(KqMatvecDesc), _i64, _vp]),
     "q4_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "q5_k_matvec": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
@@ -886,6 +888,26 @@ def moe_r8_ffn_batched_noalloc(layers, n_embd, n_ff, n_expert):
     arr, n_tok, n_used = _r8_ffn_descs(layers, n_embd, n_ff, n_expert, False)
     _check("moe_r8_ffn_batched_noalloc", _lib.moe_r8_ffn_batched_noalloc(
         arr, len(layers), n_tok, n_embd, n_ff, n_expert, n_used, _stream(layers[0]["ids"])))
+
+
+def moe_r8_fused_workspace(n_embd, n_ff, n_expert, n_used, device):
+    """A workspace for moe_r8_ffn_fused (zeroed: its counters must start at
+    zero; every call leaves them zero)."""
+    nbytes = _lib.moe_r8_fused_workspace_bytes(n_embd, n_ff, n_expert, n_used)
+    if nbytes == 0:
+        raise Q8Error("moe_r8_fused_workspace_bytes", -4)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_r8_ffn_fused(layer, n_embd, n_ff, n_expert):
+    """One token through one layer of the expert FFN over R8 weights in one
+    launch.  layer: a dict as for moe_r8_ffn_batched (one token) whose ws comes
+    from moe_r8_fused_workspace."""
+    arr, n_tok, n_used = _r8_ffn_descs([layer], n_embd, n_ff, n_expert, True)
+    if n_tok != 1:
+        raise Q8Error("moe_r8_ffn_fused", -4)
+    _check("moe_r8_ffn_fused", _lib.moe_r8_ffn_fused(arr, n_embd, n_ff, n_expert, n_used,
+                                                     _stream(layer["ids"])))
 
 
 def moe_error_word(ws):

@@ -744,6 +744,30 @@ int moe_r8_ffn_batched(const moe_r8_ffn_desc *descs, int64_t n_desc, int64_t n_t
                          [&](int64_t i) { return descs[i].ws; }, stream);
 }
 
+size_t moe_r8_fused_workspace_bytes(int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used)
+{
+    if (n_expert <= 0 || n_used <= 0 || check_k(n_embd) || check_k(n_ff)) return 0;
+    if (q8::moe_r8_fused_check(n_embd, n_ff, n_expert, n_used)) return 0;
+    return q8::moe_r8_fused_ws_bytes(n_embd, n_ff, n_used);
+}
+
+int moe_r8_ffn_fused(const moe_r8_ffn_desc *desc, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                     int64_t n_used, void *stream)
+{
+    if (n_expert <= 0 || n_used <= 0 || check_k(n_embd) || check_k(n_ff)) return Q8_E_SHAPE;
+    if (q8::moe_r8_fused_check(n_embd, n_ff, n_expert, n_used)) return Q8_E_UNSUPPORTED;
+    if (!desc) return Q8_E_NULL;
+    const moe_r8_ffn_desc &d = *desc;
+    if (!d.w_up_gate_r8 || !d.w_down_r8 || !d.x || !d.ids || !d.cw || !d.h || !d.out) return Q8_E_NULL;
+    if (!d.ws || d.ws_bytes < q8::moe_r8_fused_ws_bytes(n_embd, n_ff, n_used)) return Q8_E_WORKSPACE;
+    if (!aligned(d.ws, 256) || !aligned(d.w_up_gate_r8, 16) || !aligned(d.w_down_r8, 16) ||
+        !aligned(d.x, 16) || !aligned(d.ids, 4) || !aligned(d.cw, 4) || !aligned(d.h, 4) ||
+        !aligned(d.out, 4))
+        return Q8_E_ALIGN;
+    const q8::MoeR8Layer l = {d.w_up_gate_r8, d.w_down_r8, d.x, d.ids, d.cw, d.h, d.out, d.ws};
+    return hip_status(q8::launch_moe_r8_fused(l, n_embd, n_ff, n_expert, n_used, as_stream(stream)));
+}
+
 int q8v_moe_r8_ffn(const moe_r8_ffn_desc *desc, int64_t n_tok, int64_t n_embd, int64_t n_ff,
                    int64_t n_expert, int64_t n_used, int32_t *ug_sums, int32_t *dn_sums,
                    q8_0_block *hq, int32_t *counts, int32_t *offsets, int32_t *pairs,

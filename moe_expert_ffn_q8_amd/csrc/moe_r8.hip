@@ -419,6 +419,253 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// one token, one layer per launch (a model's layers one after another): the
+// up_gate product, q(h) and the down product in one launch
+//
+// Workgroup (slot u, h block p), as in moe_r8_up_gate_kernel up to the Q8_0
+// block of its 32 h values.  It then multiplies that block with block p of
+// every row of the slot's expert down matrix -- the block term (d_w * d_h) * s
+// of each row, s the exact int32 block sum -- and writes the n_embd terms to
+// terms[u][p][.] in the workspace (agent-scope stores: visible to every XCD
+// once complete).  The down rows' block p is prefetched with the up_gate
+// slices, before the token row is quantized, so the launch streams both
+// matrices from its start.  Then every workgroup takes a ticket (agent-scope
+// atomic add, after its stores have completed); the last R workgroups to
+// finish each sum bands of 32 output rows once every ticket is out:
+//   y[u][row] = terms[u][p][row] summed over p ascending,
+//   out[row]  = fused multiply-adds of cw[u] * y[u][row], u ascending,
+// and the last of them returns the two counters to zero for the next call.
+// A workgroup waits only after its own work, for workgroups that are running
+// or not yet started (all others are done), so the wait ends; it is bounded
+// anyway (kFzMaxPolls polls, then bit 1 of the error word).
+// Per block the arithmetic is that of the down kernel; the sum over the
+// blocks of a row is taken in another order, so out matches the two-launch
+// form within rounding, not bit for bit (h is the same bits).
+
+constexpr int kFzMaxPolls = 1 << 16;
+constexpr int kFzBatches = 8;     // down loads in flight per wave: 4 groups x 256 bytes each
+
+struct MrFzArgs {
+    const uint8_t *w_ug, *w_dn;    // R8 up_gate and down tensors
+    const float *x;                // [n_embd]
+    const int32_t *ids;            // [n_used]
+    const float *cw;               // [n_used]
+    float *h;                      // [n_used][n_ff]
+    float *out;                    // [n_embd]
+    uint8_t *ws;                   // error word, tickets, bands done; terms at +256
+    int n_used, n_embd, n_ff, n_expert;
+    int reducers;
+};
+
+__device__ __forceinline__ void st_agent_f32(float *p, float v)
+{
+    __hip_atomic_store((int32_t *)p, __builtin_bit_cast(int32_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float ld_agent_f32(const float *p)
+{
+    return __builtin_bit_cast(float, __hip_atomic_load((const int32_t *)p, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <int POL>
+__global__ __launch_bounds__(kUgThreads) void moe_r8_fused_kernel(const MrFzArgs a)
+{
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int cols = a.n_ff / 32;                  // h blocks per slot
+    const int slot = (int)blockIdx.x / cols;
+    const int p = (int)blockIdx.x - slot * cols;
+    const int total = a.n_used * cols;
+    const int nb = a.n_embd / 32;                  // blocks of the token row
+    const int e = wave_uniform(a.ids[slot]);
+    const bool valid = e >= 0 && e < a.n_expert;
+    int32_t *err = (int32_t *)a.ws;
+    int32_t *tickets = err + 1;
+    int32_t *bands_done = err + 2;
+    float *terms = (float *)(a.ws + 256);
+    float *trow = terms + (int64_t)(slot * cols + p) * a.n_embd;
+
+    if (blockIdx.x == 0 && tid < kWave) {
+        int bad = 0;
+        for (int s = lane; s < a.n_used; s += kWave) {
+            const int v = a.ids[s];
+            bad |= (v < 0 || v >= a.n_expert);
+        }
+        bad = __any(bad);
+        if (lane == 0) __hip_atomic_store(err, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    extern __shared__ __align__(16) uint8_t mr_lds[];
+    uint8_t *xc = mr_lds;
+    uint16_t *xd16 = (uint16_t *)(mr_lds + 32 * nb);
+    float *upv = (float *)(mr_lds + (34 * nb + 15) / 16 * 16);
+    float *hv = upv + 32;
+    uint32_t *hq = (uint32_t *)(hv + 32);          // the q(h) block: 8 code dwords, then the scale
+    float *ybuf = (float *)(hq + 12);              // reducer: [n_used][32]
+    float *hrow = a.h + (int64_t)slot * a.n_ff + 32 * p;
+
+    if (valid) {
+        // gate groups 4p..4p+3 (waves 0..3), up groups n_ff/8 + 4p.. (waves 4..7)
+        const int grp = wave < 4 ? 4 * p + wave : a.n_ff / 8 + 4 * p + (wave - 4);
+        const uint8_t *gbase = a.w_ug + ((int64_t)e * (2 * a.n_ff / 8) + grp) * kGB * nb;
+        // down rows of the expert: n_embd/8 groups of cols blocks (n_embd % 256
+        // == 0); wave w takes groups [gw0, gw0 + gpw), 4 per load, batch jj
+        // (lane: group gw0 + 4jj + (lane >> 4), row (lane >> 1) & 7, half
+        // lane & 1 of block p); a batch past the wave's groups reloads its
+        // last one and is not used
+        const int G = a.n_embd / 8;
+        const int gpw = G / kUgWaves;
+        const int gw0 = wave * gpw;
+        const int dgb = kGB * cols;
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.w_dn + (int64_t)e * G * dgb), 0, G * dgb, kBufferWord3);
+        const int nbat = gpw >> 2;
+        u32x4 dc[kFzBatches];
+        uint32_t ds[kFzBatches];
+        auto d_issue = [&](int j0) {
+#pragma unroll
+            for (int j = 0; j < kFzBatches; ++j) {
+                const int jj = min(j0 + j, nbat - 1);
+                const int g = gw0 + 4 * jj + (lane >> 4);
+                dc[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rd, g * dgb + 16 * cols + 256 * p + 16 * (lane & 15), 0, POL);
+                ds[j] = __builtin_amdgcn_raw_buffer_load_b16(rd, g * dgb + 16 * p + 2 * ((lane >> 1) & 7),
+                                                             0, POL);
+            }
+        };
+
+        const float *xf = a.x;
+        const int q8 = tid & 7;
+        const int passes = (nb + kUgQBlocks - 1) / kUgQBlocks;
+        auto load_pass = [&](int ps) {
+            const int b = min((tid >> 3) + kUgQBlocks * ps, nb - 1);
+            return *(const float4 *)(xf + 32 * b + 4 * q8);
+        };
+        auto quantize_pass = [&](int ps, float4 v) {
+            const int b = (tid >> 3) + kUgQBlocks * ps;
+            uint32_t codes, dbits;
+            quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+            if (b < nb) {
+                *(uint32_t *)(xc + 32 * b + 4 * q8) = codes;
+                if (q8 == 0) xd16[b] = (uint16_t)dbits;
+            }
+        };
+        GroupStream<POL, false, Q8_MR_UG_SLICES> gs;
+        gs.init(gbase, nb, lane, true);
+        if (passes <= 2) {
+            const float4 v0 = load_pass(0);
+            const float4 v1 = load_pass(passes > 1 ? 1 : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            gs.issue(0);
+            d_issue(0);
+            __builtin_amdgcn_sched_barrier(0);
+            quantize_pass(0, v0);
+            if (passes > 1) quantize_pass(1, v1);
+        } else {
+            for (int ps = 0; ps < passes; ++ps) quantize_pass(ps, load_pass(ps));
+            gs.issue(0);
+            d_issue(0);
+        }
+        __syncthreads();
+
+        const float acc = gs.run(lane, xc, xd16);
+        const bool holder = (lane & 0x31) == 0;
+        const int r = (lane >> 1) & 7;
+        if (wave >= 4 && holder) upv[8 * (wave - 4) + r] = acc;
+        __syncthreads();
+        if (wave < 4 && holder) {
+            const float g = acc;
+            const float hval = g / (1.0f + expf(-g)) * upv[8 * wave + r];
+            hrow[8 * wave + r] = hval;
+            hv[8 * wave + r] = hval;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int l8 = lane & 7;
+            const float4 v = *(const float4 *)(hv + 4 * l8);
+            uint32_t codes, dbits;
+            quantize_block8(v.x, v.y, v.z, v.w, codes, dbits);
+            if (lane < 8) hq[l8] = codes;
+            if (lane == 0) hq[8] = dbits;
+        }
+        __syncthreads();
+
+        // the down terms of block p: one 8-row group per 16 lanes and batch
+        const int half = lane & 1;
+        const u32x4 hx = *(const u32x4 *)(hq + 4 * half);
+        const float dh = half_bits_to_float(hq[8]);
+        for (int j0 = 0;;) {
+#pragma unroll
+            for (int j = 0; j < kFzBatches; ++j) {
+                int sum = sdot4(dc[j].x, hx.x, 0);
+                sum = sdot4(dc[j].y, hx.y, sum);
+                sum = sdot4(dc[j].z, hx.z, sum);
+                sum = sdot4(dc[j].w, hx.w, sum);
+                sum += __builtin_amdgcn_mov_dpp(sum, 0xB1, 0xF, 0xF, false);   // the other half
+                const int row = 8 * (gw0 + 4 * (j0 + j) + (lane >> 4)) + ((lane >> 1) & 7);
+                if (half == 0 && j0 + j < nbat)
+                    st_agent_f32(trow + row, fmaf(half_bits_to_float(ds[j]) * dh, (float)sum, 0.0f));
+            }
+            j0 += kFzBatches;
+            if (j0 >= nbat) break;
+            d_issue(j0);
+        }
+    } else {
+        if (tid < 32) hrow[tid] = __builtin_nanf("");
+        for (int i = tid; i < a.n_embd; i += kUgThreads) st_agent_f32(trow + i, __builtin_nanf(""));
+    }
+
+    // this workgroup's terms are complete at agent scope: take a ticket
+    __builtin_amdgcn_s_waitcnt(0);
+    __shared__ int s_ticket;
+    __syncthreads();
+    if (tid == 0)
+        s_ticket = __hip_atomic_fetch_add(tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int R = a.reducers;
+    const int ri = s_ticket - (total - R);
+    if (ri < 0) return;
+    if (tid == 0) {
+        int polls = 0;
+        while (__hip_atomic_load(tickets, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < total) {
+            if (++polls > kFzMaxPolls) {
+                __hip_atomic_fetch_or(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+    for (int band = ri; band < a.n_embd / 32; band += R) {
+        if (tid < 32 * a.n_used) {
+            const int u = tid >> 5, rr = tid & 31;
+            const float *src = terms + (int64_t)u * cols * a.n_embd + 32 * band + rr;
+            float y = 0.0f;
+#pragma unroll 8
+            for (int q = 0; q < cols; ++q) y += ld_agent_f32(src + (int64_t)q * a.n_embd);
+            ybuf[32 * u + rr] = y;
+        }
+        __syncthreads();
+        if (tid < 32) {
+            float o = 0.0f;
+            for (int u = 0; u < a.n_used; ++u) o = fmaf(a.cw[u], ybuf[32 * u + tid], o);
+            a.out[32 * band + tid] = o;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const int d = __hip_atomic_fetch_add(bands_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == R - 1) {
+            __hip_atomic_store(tickets, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(bands_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // several tokens: each active expert's rows streamed once per call
 //
 // With more than one token, slots repeat experts (at 16 tokens, 8 of 128
@@ -895,6 +1142,13 @@ struct R8DecodeWs {
     size_t yslot, total;
 };
 
+// LDS of the fused kernel: the token row, the up and h values, the q(h)
+// block, the reducer's slot rows
+size_t fused_lds(int64_t n_embd, int64_t n_used)
+{
+    return (size_t)(34 * (n_embd / 32) + 15) / 16 * 16 + 64 * 4 + 12 * 4 + (size_t)n_used * 32 * 4;
+}
+
 R8DecodeWs r8_decode_ws(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_used)
 {
     const size_t slots = (size_t)(n_tok * n_used);
@@ -1065,6 +1319,48 @@ int launch_r8_gather(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n
 }
 
 }  // namespace
+
+size_t moe_r8_fused_ws_bytes(int64_t n_embd, int64_t n_ff, int64_t n_used)
+{
+    return 256 + (size_t)n_used * (size_t)(n_ff / 32) * (size_t)n_embd * 4;
+}
+
+int moe_r8_fused_check(int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used)
+{
+    if (!r8_decode_ok(1, n_embd, n_ff, n_expert, n_used) || n_embd % 256 != 0) return -4;
+    const size_t lds = fused_lds(n_embd, n_used);
+    if (lds > (size_t)max_lds_bytes()) return -4;
+    // terms offsets are 32-bit element counts; the down rows' buffer range too
+    if ((int64_t)n_used * (n_ff / 32) * n_embd > 0x7fffffffLL ||
+        (int64_t)n_embd * (n_ff / 32) * kBlockBytes > 0x7f000000LL)
+        return -4;
+    return 0;
+}
+
+int launch_moe_r8_fused(const MoeR8Layer &l, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                        int64_t n_used, hipStream_t stream)
+{
+    if (int rc = moe_r8_fused_check(n_embd, n_ff, n_expert, n_used)) return rc;
+    MrFzArgs a;
+    a.w_ug = (const uint8_t *)l.w_up_gate;
+    a.w_dn = (const uint8_t *)l.w_down;
+    a.x = l.x;
+    a.ids = l.ids;
+    a.cw = l.cw;
+    a.h = l.h;
+    a.out = l.out;
+    a.ws = (uint8_t *)l.ws;
+    a.n_used = (int)n_used;
+    a.n_embd = (int)n_embd;
+    a.n_ff = (int)n_ff;
+    a.n_expert = (int)n_expert;
+    const int total = (int)(n_used * (n_ff / 32));
+    const int bands = (int)(n_embd / 32);
+    a.reducers = total < bands ? total : bands;
+    hipLaunchKernelGGL((moe_r8_fused_kernel<kCacheNT>), dim3((unsigned)total), dim3(kUgThreads),
+                       fused_lds(n_embd, n_used), stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream,

@@ -143,6 +143,12 @@ int moe_r8_scratch(uint8_t **base);
 // The launch-shape limits of launch_moe_r8_ffn for this shape: 0 or -4.
 int moe_r8_ffn_check(int64_t n_tok, int64_t n_embd, int64_t n_ff, int64_t n_expert,
                      int64_t n_used);
+// One token, one layer, one launch (moe_r8_ffn_fused): workspace bytes,
+// the shape limits (0 or -4), the launch.
+size_t moe_r8_fused_ws_bytes(int64_t n_embd, int64_t n_ff, int64_t n_used);
+int moe_r8_fused_check(int64_t n_embd, int64_t n_ff, int64_t n_expert, int64_t n_used);
+int launch_moe_r8_fused(const MoeR8Layer &l, int64_t n_embd, int64_t n_ff, int64_t n_expert,
+                        int64_t n_used, hipStream_t stream);
 int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t n_embd,
                       int64_t n_ff, int64_t n_expert, int64_t n_used, hipStream_t stream,
                       const MoeEmit *emit_ug = nullptr, const MoeEmit *emit_dn = nullptr);
