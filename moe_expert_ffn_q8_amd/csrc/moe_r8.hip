@@ -47,6 +47,9 @@ constexpr int kMrSlices = 8;              // 1 KB slices of a group in flight pe
 #ifndef Q8_MR_UG_SLICES
 #define Q8_MR_UG_SLICES 8
 #endif
+#ifndef Q8_MR_UG_ONE_LAYER_SLICES
+#define Q8_MR_UG_ONE_LAYER_SLICES 16   // up_gate launches of a single layer
+#endif
 
 // One 8-row group of nb blocks against an activation row in LDS (codes
 // realigned to 32 bytes per block, binary16 scale bits); slice i, lane l:
@@ -225,7 +228,7 @@ struct MrUgArgs {
     int ug_cols;               // several tokens: 8-column groups per wave
 };
 
-template <int POL, bool EMIT>
+template <int POL, bool EMIT, int SL = Q8_MR_UG_SLICES>
 __global__ __launch_bounds__(kUgThreads) void moe_r8_up_gate_kernel(const MrUgArgs a)
 {
     const int tid = threadIdx.x;
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(kUgThreads) void moe_r8_up_gate_kernel(const MrUgAr
             if (q8 == 0) xd16[b] = (uint16_t)dbits;
         }
     };
-    GroupStream<POL, EMIT, Q8_MR_UG_SLICES> gs;
+    GroupStream<POL, EMIT, SL> gs;
     gs.init(gbase, nb, lane, true);
     if (EMIT) gs.srow = a.sums + ((int64_t)slot * 2 * a.n_ff + 8 * grp + ((lane >> 1) & 7)) * nb;
     if (passes <= 2) {
@@ -442,6 +445,9 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 // blocks of a row is taken in another order, so out matches the two-launch
 // form within rounding, not bit for bit (h is the same bits).
 
+#ifndef Q8_FZ_SLICES
+#define Q8_FZ_SLICES 8            // up_gate slices in flight per wave
+#endif
 constexpr int kFzMaxPolls = 1 << 16;
 constexpr int kFzBatches = 8;     // down loads in flight per wave: 4 groups x 256 bytes each
 
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(kUgThreads) void moe_r8_fused_kernel(const MrFzArgs
                 if (q8 == 0) xd16[b] = (uint16_t)dbits;
             }
         };
-        GroupStream<POL, false, Q8_MR_UG_SLICES> gs;
+        GroupStream<POL, false, Q8_FZ_SLICES> gs;
         gs.init(gbase, nb, lane, true);
         if (passes <= 2) {
             const float4 v0 = load_pass(0);
@@ -1419,6 +1425,13 @@ int launch_moe_r8_ffn(const MoeR8Layer *l, int n_layers, int64_t n_tok, int64_t 
         else if (reuse)
             hipLaunchKernelGGL((moe_r8_up_gate_kernel<0, false>), ug_grid, dim3(kUgThreads), ug_lds,
                                stream, ug);
+        else if (nl == 1)
+            // one layer per launch (layers run one after another): a group's
+            // 64 blocks all in flight at once, 16 slices per wave (30 layers
+            // one per call: 434 against 443 us; all 30 in one call keep 8:
+            // 185 against 207 us)
+            hipLaunchKernelGGL((moe_r8_up_gate_kernel<kCacheNT, false, Q8_MR_UG_ONE_LAYER_SLICES>), ug_grid,
+                               dim3(kUgThreads), ug_lds, stream, ug);
         else
             hipLaunchKernelGGL((moe_r8_up_gate_kernel<kCacheNT, false>), ug_grid, dim3(kUgThreads),
                                ug_lds, stream, ug);
