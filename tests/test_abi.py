@@ -467,6 +467,40 @@ def test_moe_r8_checks(lib):
     assert call(big, n_tok=8193) == Q8_E_UNSUPPORTED                            # too many tokens
 
 
+def test_moe_r8_fused_checks(lib):
+    """moe_r8_ffn_fused (one token, one layer, one launch): its workspace size
+    (256 bytes of counters, then the block terms [n_used][n_ff/32][n_embd] in
+    fp32), the shape limits (n_embd % 256) and every argument check before any
+    launch."""
+    import moe_expert_ffn_q8_amd as q
+    f = lib.moe_r8_ffn_fused
+    need = lib.moe_r8_fused_workspace_bytes(2048, 768, 128, 8)
+    assert need == 256 + 8 * 24 * 2048 * 4
+    assert lib.moe_r8_fused_workspace_bytes(2048 - 32, 768, 128, 8) == 0      # n_embd % 256
+    assert lib.moe_r8_fused_workspace_bytes(2048, 4096, 128, 8) == 0          # n_ff > 2048
+    assert lib.moe_r8_fused_workspace_bytes(2048, 768, 128, 17) == 0          # n_used > 16
+    assert lib.moe_r8_fused_workspace_bytes(2048, 768, 0, 8) == 0
+
+    def call(d, n_embd=2048, n_ff=768, n_expert=128, n_used=8):
+        return f(ctypes.byref(d) if d is not None else None, n_embd, n_ff, n_expert, n_used, None)
+
+    D = q.MoeR8FfnDesc
+    ok = D(A, A, A, A, A, A, A, WS, need)
+    assert call(None) == Q8_E_NULL
+    assert call(ok, n_embd=2047) == Q8_E_SHAPE
+    assert call(ok, n_ff=40) == Q8_E_SHAPE
+    assert call(ok, n_used=0) == Q8_E_SHAPE
+    assert call(ok, n_embd=2048 - 32) == Q8_E_UNSUPPORTED
+    assert call(ok, n_used=17) == Q8_E_UNSUPPORTED
+    assert call(D(A, A, A, A, A, A, A, WS, need - 1)) == Q8_E_WORKSPACE
+    assert call(D(A, A, A, A, A, A, A, None, need)) == Q8_E_WORKSPACE
+    assert call(D(A, A, A, A, A, A, A, WS + 16, need)) == Q8_E_ALIGN
+    assert call(D(A, A, None, A, A, A, A, WS, need)) == Q8_E_NULL
+    assert call(D(A, A + 8, A, A, A, A, A, WS, need)) == Q8_E_ALIGN
+    assert call(D(A, A, A + 4, A, A, A, A, WS, need)) == Q8_E_ALIGN
+    assert call(D(A, A, A, A, A, A + 2, A, WS, need)) == Q8_E_ALIGN
+
+
 def test_moe_r8_noalloc_checks(lib):
     """The no-alloc variant: the shape and descriptor checks of
     moe_r8_ffn_batched (its ws fields ignored), decode shapes only, and a
