@@ -444,6 +444,11 @@ __global__ __launch_bounds__(1024) void moe_r8_down_kernel(const MrDnArgs a)
 // Per block the arithmetic is that of the down kernel; the sum over the
 // blocks of a row is taken in another order, so out matches the two-launch
 // form within rounding, not bit for bit (h is the same bits).
+// Measured on the Gemma-4-26B-A4B expert shape, 30 layers one after another:
+// 558-566 us per step against 437-457 us for two launches per layer; ending
+// every workgroup after its terms (timing-only copies) gave 402-417 us, so
+// the summation's chain of round trips (store completion, ticket, wait,
+// agent-scope reads) costs about 5 us per layer, more than the launch saved.
 
 #ifndef Q8_FZ_SLICES
 #define Q8_FZ_SLICES 8            // up_gate slices in flight per wave
