@@ -11,16 +11,20 @@
 // v_mfma_i32_32x32x32_i8 has K = 32, exactly one Q8_0 block: one instruction
 // gives the exact int32 block sums of a 32x32 (token x weight-row) tile, and
 // blocks never mix inside an integer sum, so every block's tile is rescaled by
-// its own scales into fp32 accumulators: per element and block a convert, a
-// scale product and a fused multiply-add on the VALU (3 operations against
-// 1/16 of an MFMA per lane), and that rescale, not the int8 matrix core,
-// bounds this kernel.  The staged rows are 144 bytes apart (16-byte DMA
+// its own scales into fp32 accumulators, and that rescale, not the int8
+// matrix core, bounds this kernel.  By default (Q8_GEMM_OUTER=2) the scale
+// products of a tile come from a second matrix instruction (an outer product
+// of the scales' binary16 bits), leaving a convert and a fused multiply-add
+// per element and block on the VALU, and the int8 sums are carried one block
+// ahead so that no rescale waits for them (see compute_pipelined); with the
+// products on the VALU (Q8_GEMM_OUTER=0) it is 3 operations per element and
+// block.  The staged rows are 144 bytes apart (16-byte DMA
 // granularity), so the 4-byte reads that codes 2 bytes past a dword boundary
 // need would put 32 rows on 8 bank offsets (4-way conflicts): each step, every
 // thread first realigns one staged row in place (codes of block b to bytes
 // 32b..32b+31, its scale to an fp32 array), and the fragments are then single
 // 16-byte reads, conflict-free for 8 rows 144 bytes apart (Q8_GEMM_REALIGN;
-// 130 against 143 us).  (Build option
+// 130 against 143 us).  (Measured before the pipelined form: build option
 // Q8_GEMM_OUTER=1 forms the rank-1 scale products of a block as an outer
 // product on the fp32 matrix core instead, same register layout, leaving 2
 // VALU operations: 150.5 against 141.3 us with each tile's sums pinned in
@@ -45,9 +49,8 @@
 //    goes straight from HBM to LDS with coalesced 16-byte buffer loads in LDS
 //    DMA mode (rows past m or n read as zero), double-buffered so the next
 //    step streams in while the current one is computed; the block scales are
-//    unpacked once per step into fp32 arrays.  Operand fragments are read back with 4-byte LDS reads and
-//    byte-aligned with v_alignbyte where a block's codes start 2 bytes past a
-//    dword.
+//    unpacked once per step (binary16 bits for the default form, fp32 for
+//    the VALU form) while each thread realigns its staged row.
 //  * Operand layout of the MFMA: lane l supplies row l%32 of its tile and the
 //    16 codes of k-group l/32 (A = tokens, B = weight rows, same byte order, so
 //    the integer sum covers the block's 32 codes once); result register r of
@@ -65,6 +68,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGThreads = 256;
 constexpr int kBM = 128;                 // tokens per workgroup tile
@@ -90,7 +94,9 @@ static_assert(!Q8_GEMM_REALIGN || (kStepBlocks <= 4 && kStageRows == kGThreads),
 #define Q8_GEMM_PIN_VALU 0
 #endif
 #ifndef Q8_GEMM_OUTER
-#define Q8_GEMM_OUTER 0          // scale products on the fp32 matrix core (1) or the VALU (0)
+// scale products on the VALU (0), on the fp32 matrix core (1), or on the
+// binary16 matrix core with the tiles software-pipelined (2)
+#define Q8_GEMM_OUTER 2
 #endif
 static_assert(kStepBlocks == 2 || kStepBlocks == 4 || kStepBlocks == 8, "K step of 2, 4 or 8 blocks");
 // the token/weight row boundary falls on a wave boundary of the load pattern
@@ -132,6 +138,8 @@ __global__ __launch_bounds__(kGThreads, Q8_GEMM_OCC) void gemm_q8_kernel(const G
     __shared__ __align__(16) uint8_t stage0[kStageRows * kRowStride];
     __shared__ __align__(16) uint8_t stage1[kStageRows * kRowStride];
     __shared__ __align__(16) float sc[kStepBlocks][kStageRows];              // 8192 B
+    __shared__ __align__(16) uint16_t sc16[kStepBlocks][kStageRows];         // binary16 bits
+    constexpr bool kPipe = Q8_GEMM_OUTER == 2;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -195,6 +203,97 @@ __global__ __launch_bounds__(kGThreads, Q8_GEMM_OCC) void gemm_q8_kernel(const G
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // Q8_GEMM_OUTER == 2: per tile and block two matrix instructions -- the
+    // exact int32 sums S of the block (int8, K = 32) and the scale products
+    // P = d_x * d_w as an outer product on the binary16 matrix core (each
+    // scale's own bits at k = 0, zeros elsewhere; a product of two binary16
+    // values is exact in fp32, so P has the bits of the VALU product) -- and
+    // 16 converts and 16 fused multiply-adds, acc = fma(P, float(S), acc), the
+    // same operation on the same values as the VALU form, with one VALU
+    // operation per element and block fewer.  The blocks of a step are a
+    // runtime loop whose sums S are carried into the next iteration: an
+    // iteration rescales block b tile by tile (P formed just before its
+    // rescale) and, right after each tile, issues that tile's int8 product
+    // for block b + 1 into the registers the rescale has just read, so no
+    // rescale waits for its sums and nothing is hoisted across iterations
+    // (256 VGPRs, two waves per SIMD).  Measured on 512 x 4096 x 14336:
+    // 125.5 against 131.5 us for the VALU form; carrying P as well (299
+    // VGPRs, one wave per SIMD): 151 us; the VALU form pipelined the same way:
+    // no change (129 us).
+    // kmask: all ones on the lanes of k-group 0, opaque to the compiler (a
+    // select there would become a branch around each scale read).
+    int kmask = h == 0 ? 0xffff : 0;
+    asm volatile("" : "+v"(kmask));
+    auto compute_pipelined = [&](int st, const uint8_t *sb) {
+        v4i A[2], B[2];
+        int sa_n[2], sb_n[2], sa_c[2], sb_c[2];     // scale bits of blocks b + 1 and b
+        auto load = [&](int b) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 64 * wm + 32 * i + li;
+                A[i] = *(const v4i *)(sb + r * kRowStride + 32 * b + 16 * h);
+                sa_n[i] = (int)sc16[b][r] & kmask;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = kBM + 64 * wn + 32 * j + li;
+                B[j] = *(const v4i *)(sb + r * kRowStride + 32 * b + 16 * h);
+                sb_n[j] = (int)sc16[b][r] & kmask;
+            }
+        };
+        auto advance = [&]() {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                sa_c[i] = sa_n[i];
+                sb_c[i] = sb_n[i];
+            }
+        };
+        v16i S[2][2];
+        auto issue = [&](int i, int j) {
+            const v16i zi = {0};
+            S[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], zi, 0, 0, 0);
+        };
+        auto rescale = [&](int b, int i, int j) {
+            if (SUMS) {
+                const int n = n0 + 64 * wn + 32 * j + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (m < a.m && n < a.n)
+                        a.sums[((int64_t)m * a.n + n) * a.nb + st * kStepBlocks + b] = S[i][j][r];
+                }
+            }
+            const v16f zf = {0.f};
+            const v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(h8, (v4i){sa_c[i], 0, 0, 0}),
+                __builtin_bit_cast(h8, (v4i){sb_c[j], 0, 0, 0}), zf, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(P[r], (float)S[i][j][r], acc[i][j][r]);
+        };
+        load(0);
+        advance();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) issue(i, j);
+#pragma unroll 1
+        for (int b = 0; b + 1 < kStepBlocks; ++b) {
+            load(b + 1);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    rescale(b, i, j);
+                    issue(i, j);
+                }
+            advance();
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) rescale(kStepBlocks - 1, i, j);
+    };
+
     // Step st: wait for this wave's loads of st, barrier (every wave's
     // landed; every wave is done with st-1, whose buffer the next issue
     // fills), issue st+1, unpack the scales, barrier, compute.  Raw barriers
@@ -221,7 +320,16 @@ __global__ __launch_bounds__(kGThreads, Q8_GEMM_OCC) void gemm_q8_kernel(const G
             for (int b = 0; b < kStepBlocks; ++b) {
                 // block b at byte 34b: 34b = 4*(17b/2) (+2 when b is odd)
                 const int D = (17 * b) >> 1;
-                if ((b & 1) == 0) {
+                if (kPipe) {
+                    sc16[b][tid] = (uint16_t)((b & 1) == 0 ? d[D] & 0xffffu : d[D] >> 16);
+                    if ((b & 1) == 0) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) cw[b][j] = __builtin_amdgcn_alignbyte(d[D + j + 1], d[D + j], 2);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) cw[b][j] = d[D + 1 + j];
+                    }
+                } else if ((b & 1) == 0) {
                     sc[b][tid] = half_bits_to_float(d[D] & 0xffffu);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) cw[b][j] = __builtin_amdgcn_alignbyte(d[D + j + 1], d[D + j], 2);
@@ -248,6 +356,10 @@ __global__ __launch_bounds__(kGThreads, Q8_GEMM_OCC) void gemm_q8_kernel(const G
         __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the scales are written
         __builtin_amdgcn_s_barrier();
 
+        if (kPipe) {
+            compute_pipelined(st, sb);
+            return;
+        }
         // two blocks per unrolled iteration: the full unroll of a step keeps
         // too many operands live (256 VGPRs and spills against 176)
 #pragma unroll 2
