@@ -85,165 +85,122 @@ struct RouteArgs {
 };
 
 constexpr int kRouteWaves = kRouteThreads / kWave;      // 16
-constexpr int kRouteBatch = 4;                          // slot ids in flight per lane
-static_assert(kMoePrefillMaxSlots / kRouteWaves * (kRouteWaves - 1) < 65536,
-              "a wave's start within an expert's group fits a 16-bit field");
+constexpr int kRouteBatch = 4;                          // slot ids in flight per thread
+constexpr int kRouteSuper = kRouteBatch * kRouteThreads;   // slots per pass of a workgroup
 
-__device__ __forceinline__ void route_tiles(const RouteArgs &a)
+// The routing of one expert, e = the workgroup's index (a launch has one
+// workgroup per expert).  Every workgroup reads all the ids and builds the
+// whole per-expert histogram in LDS (the same counts in every workgroup),
+// takes the exclusive prefixes of the counts and of the tile counts over the
+// experts below e, and writes expert e's offset, its slots in ascending slot
+// order and its tiles of at most kPBM slots; workgroup 0 also writes the
+// totals, the error word and the NaN h rows of out-of-range slots.  Slot s of
+// a pass starting at s0 is held by thread s - s0 - kRouteThreads k in its
+// k-th register, so ascending slot order is (k, wave, lane) order.
+__device__ __forceinline__ void route_tiles(const RouteArgs &a, int e)
 {
     __shared__ int cnt[kMoeMaxExperts];
-    __shared__ int scan_c[kMoeMaxExperts];
-    __shared__ int scan_t[kMoeMaxExperts];
-    // per wave and expert, two 16-bit fields per word (expert e in word e/2,
-    // bits 16*(e&1)): the wave's slot count, then its running position
-    // within the expert's group
-    __shared__ uint32_t wcnt[kRouteWaves][kMoeMaxExperts / 2];
+    __shared__ int wpre[kRouteBatch * kRouteWaves];      // hits per (k, wave), then their prefix
+    __shared__ int red[4][kRouteWaves];
     __shared__ int bad;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    // wave w owns the contiguous slot range [w*span, (w+1)*span)
-    const int span = (a.n_slots + kRouteWaves - 1) / kRouteWaves;
-    const int s_beg = min(wave * span, a.n_slots), s_end = min(s_beg + span, a.n_slots);
-    for (int e = tid; e < kMoeMaxExperts; e += kRouteThreads) cnt[e] = 0;
-    for (int i = tid; i < kRouteWaves * kMoeMaxExperts / 2; i += kRouteThreads)
-        (&wcnt[0][0])[i] = 0;
+    static_assert(kRouteThreads >= kMoeMaxExperts, "one thread per expert");
+    static_assert(kRouteBatch * kRouteWaves <= kWave, "one lane per (k, wave) in the prefix");
+    cnt[tid] = 0;
     if (tid == 0) bad = 0;
     __syncthreads();
-    // the ids are read kRouteBatch slots per lane at a time, all loads issued
-    // before any is used (one memory latency per 256 slots of a wave, not one
-    // per 64)
-    for (int s0 = s_beg; s0 < s_end; s0 += kRouteBatch * kWave) {
-        int ev[kRouteBatch];
+    int ev[kRouteBatch];
+    auto load = [&](int s0) {
 #pragma unroll
         for (int k = 0; k < kRouteBatch; ++k) {
-            const int s = s0 + k * kWave + lane;
-            ev[k] = s < s_end ? a.ids[s] : 0;
+            const int s = s0 + k * kRouteThreads + tid;
+            ev[k] = s < a.n_slots ? a.ids[s] : 0;
         }
+    };
+    for (int s0 = 0; s0 < a.n_slots; s0 += kRouteSuper) {
+        load(s0);
 #pragma unroll
         for (int k = 0; k < kRouteBatch; ++k) {
-            const int s = s0 + k * kWave + lane;
-            const int e = ev[k];
-            if (s >= s_end) continue;
-            if (e < 0 || e >= a.n_expert) {
-                atomicOr(&bad, 1);
-                if (a.h_nan)
-                    for (int j = 0; j < a.n_ff; ++j) a.h_nan[(int64_t)s * a.n_ff + j] = __builtin_nanf("");
+            const int s = s0 + k * kRouteThreads + tid;
+            if (s >= a.n_slots) continue;
+            if (ev[k] >= 0 && ev[k] < a.n_expert) {
+                atomicAdd(&cnt[ev[k]], 1);
             } else {
-                atomicAdd(&cnt[e], 1);
-                atomicAdd(&wcnt[wave][e >> 1], (e & 1) ? 0x10000u : 1u);
+                bad = 1;
+                if (e == 0 && a.h_nan)
+                    for (int j = 0; j < a.n_ff; ++j) a.h_nan[(int64_t)s * a.n_ff + j] = __builtin_nanf("");
             }
         }
     }
     __syncthreads();
-    // inclusive scans of the counts and of the tile counts (thread e holds
-    // expert e): within each wave by lane shuffles, then over the wave totals
-    static_assert(kRouteThreads == kMoeMaxExperts, "one thread per expert");
-    __shared__ int wtot_c[kRouteWaves], wtot_t[kRouteWaves];
-    const int c = cnt[tid];
-    int vc = c, vt = (c + kPBM - 1) / kPBM;
+    // exclusive prefixes below e and totals of the counts and tile counts
+    const int c = tid < a.n_expert ? cnt[tid] : 0;
+    const int t = (c + kPBM - 1) / kPBM;
+    int v[4] = {tid < e ? c : 0, tid < e ? t : 0, c, t};
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int ac = __shfl_up(vc, d), at = __shfl_up(vt, d);
-        if (lane >= d) {
-            vc += ac;
-            vt += at;
-        }
-    }
-    if (lane == kWave - 1) {
-        wtot_c[wave] = vc;
-        wtot_t[wave] = vt;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int xc = lane < kRouteWaves ? wtot_c[lane] : 0;
-        int xt = lane < kRouteWaves ? wtot_t[lane] : 0;
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int d = 1; d < kRouteWaves; d <<= 1) {
-            const int ac = __shfl_up(xc, d), at = __shfl_up(xt, d);
-            if (lane >= d) {
-                xc += ac;
-                xt += at;
-            }
-        }
-        if (lane < kRouteWaves) {
-            wtot_c[lane] = xc;
-            wtot_t[lane] = xt;
-        }
+        for (int d = 1; d < kWave; d <<= 1) v[q] += __shfl_xor(v[q], d);
+        if (lane == 0) red[q][wave] = v[q];
     }
     __syncthreads();
-    if (wave > 0) {
-        vc += wtot_c[wave - 1];
-        vt += wtot_t[wave - 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[q] = 0;
+        for (int w = 0; w < kRouteWaves; ++w) v[q] += red[q][w];
     }
-    scan_c[tid] = vc;
-    scan_t[tid] = vt;
-    __syncthreads();
-    const int off = vc - c;                        // exclusive
-    const int toff = vt - (c + kPBM - 1) / kPBM;
-    if (tid < a.n_expert) {
-        a.offsets[tid] = off;
-        for (int i = 0; i * kPBM < c; ++i)
-            a.tiles[toff + i] = TileEntry{tid, off + i * kPBM, min(kPBM, c - i * kPBM), 0};
-    }
-    if (tid == kRouteThreads - 1) {
-        a.offsets[a.n_expert] = scan_c[a.n_expert - 1];
+    const int off = v[0], toff = v[1];
+    const int ce = cnt[e];
+    if (tid == 0) a.offsets[e] = off;
+    for (int i = tid; i * kPBM < ce; i += kRouteThreads)
+        a.tiles[toff + i] = TileEntry{e, off + i * kPBM, min(kPBM, ce - i * kPBM), 0};
+    if (e == 0 && tid == 0) {
+        a.offsets[a.n_expert] = v[2];
         a.hdr[0] = bad;
-        a.hdr[1] = scan_t[a.n_expert - 1];
+        a.hdr[1] = v[3];
     }
-    // each wave's start within every expert's group: the counts of the waves
-    // before it (exclusive prefix over waves, in place)
-    // One thread per word: both 16-bit fields advance in one 32-bit add, and
-    // neither carries (a field's prefix over the waves before the last is
-    // below 15 * 4096 slots).
-    if (tid < kMoeMaxExperts / 2) {
-        uint32_t run = 0;
-        for (int w = 0; w < kRouteWaves; ++w) {
-            const uint32_t c = wcnt[w][tid];
-            wcnt[w][tid] = run;
-            run += c;
-        }
-    }
-    __syncthreads();
-    // scatter in slot order: a wave walks its range 64 slots at a time (their
-    // ids read kRouteBatch steps ahead); a lane takes the next position of its
-    // expert after the lanes below it naming the same expert (found by
-    // matching the 10 bits of the id)
-    for (int s0 = s_beg; s0 < s_end; s0 += kRouteBatch * kWave) {
-        int ev[kRouteBatch];
+    // expert e's slots in ascending order: per pass, the hits of every
+    // (k, wave) are counted by ballots, one lane per (k, wave) of wave 0 takes
+    // the exclusive prefix in slot order, and a hit's position is that prefix
+    // plus its rank among the hits below it in its wave
+    int run = 0;                             // hits of the passes before
+    for (int s0 = 0; s0 < a.n_slots; s0 += kRouteSuper) {
+        if (s0 > 0 || a.n_slots > kRouteSuper) load(s0);   // else the ids are still held
+        uint64_t m[kRouteBatch];
 #pragma unroll
         for (int k = 0; k < kRouteBatch; ++k) {
-            const int s = s0 + k * kWave + lane;
-            ev[k] = s < s_end ? a.ids[s] : -1;
+            const int s = s0 + k * kRouteThreads + tid;
+            m[k] = __ballot(s < a.n_slots && ev[k] == e);
+            if (lane == 0) wpre[k * kRouteWaves + wave] = __popcll(m[k]);
         }
+        __syncthreads();
+        if (wave == 0) {
+            const int x = lane < kRouteBatch * kRouteWaves ? wpre[lane] : 0;
+            int incl = x;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int y = __shfl_up(incl, d);
+                if (lane >= d) incl += y;
+            }
+            if (lane < kRouteBatch * kRouteWaves) wpre[lane] = incl - x;
+            red[0][0] = __shfl(incl, kWave - 1);
+        }
+        __syncthreads();
 #pragma unroll
         for (int k = 0; k < kRouteBatch; ++k) {
-            const int s = s0 + k * kWave + lane;
-            const int e = ev[k];
-            const bool ok = e >= 0 && e < a.n_expert;
-            uint64_t peers = __ballot(ok);
-#pragma unroll
-            for (int bit = 0; bit < 10; ++bit) {
-                const uint64_t m = __ballot(((e >> bit) & 1) != 0);
-                peers &= ((e >> bit) & 1) ? m : ~m;
-            }
-            if (ok) {
-                const int sh = 16 * (e & 1);
-                const int run = (int)((wcnt[wave][e >> 1] >> sh) & 0xffffu);
-                const int rank = __popcll(peers & __lanemask_lt());
-                a.pairs[(e > 0 ? scan_c[e - 1] : 0) + run + rank] = s;
-            }
-            wave_lds_sync();
-            // the lowest lane of each group of peers advances the group's position
-            if (ok && (peers & __lanemask_lt()) == 0)
-                atomicAdd(&wcnt[wave][e >> 1], (uint32_t)__popcll(peers) << (16 * (e & 1)));
-            wave_lds_sync();
+            if ((m[k] >> lane) & 1)
+                a.pairs[off + run + wpre[k * kRouteWaves + wave] + __popcll(m[k] & __lanemask_lt())] =
+                    s0 + k * kRouteThreads + tid;
         }
+        run += red[0][0];
+        __syncthreads();                     // wpre and red reused by the next pass
     }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void moe_route_tiles_kernel(const RouteArgs a)
 {
-    route_tiles(a);
+    route_tiles(a, blockIdx.x);
 }
 
 // fp32 rows -> the tile layout of the A operand: codes [row][nb][32] (even
@@ -292,17 +249,18 @@ __global__ __launch_bounds__(256) void qa_quantize_kernel(const float *__restric
     qa_quantize_tiles(x, row_stride, codes, scales, nb, total_blocks, rotate, blockIdx.x, gridDim.x);
 }
 
-// The two independent first steps of a prefill call in one launch: workgroup
-// 0 routes the slots, the others quantize the token rows.
+// The two independent first steps of a prefill call in one launch: the first
+// n_expert workgroups route the slots (one expert each), the others quantize
+// the token rows.
 __global__ __launch_bounds__(kRouteThreads) void route_quantize_kernel(
     const RouteArgs r, const float *__restrict__ x, int64_t row_stride, uint8_t *__restrict__ codes,
     float *__restrict__ scales, int64_t nb, int64_t total_blocks, int rotate)
 {
-    if (blockIdx.x == 0)
-        route_tiles(r);
+    if ((int)blockIdx.x < r.n_expert)
+        route_tiles(r, blockIdx.x);
     else
-        qa_quantize_tiles(x, row_stride, codes, scales, nb, total_blocks, rotate, blockIdx.x - 1,
-                          gridDim.x - 1);
+        qa_quantize_tiles(x, row_stride, codes, scales, nb, total_blocks, rotate,
+                          blockIdx.x - r.n_expert, gridDim.x - r.n_expert);
 }
 
 int launch_qa_quantize(const float *x, int64_t row_stride, uint8_t *codes, float *scales,
@@ -907,7 +865,7 @@ int launch_route(const int32_t *ids, uint8_t *ws, const PrefillWs &L, float *h_n
     r.n_slots = (int)n_slots;
     r.n_expert = (int)n_expert;
     r.n_ff = (int)n_ff;
-    hipLaunchKernelGGL(moe_route_tiles_kernel, dim3(1), dim3(kRouteThreads), 0, stream, r);
+    hipLaunchKernelGGL(moe_route_tiles_kernel, dim3((unsigned)n_expert), dim3(kRouteThreads), 0, stream, r);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -931,7 +889,7 @@ int launch_route_quantize(const int32_t *ids, uint8_t *ws, const PrefillWs &L, f
     const int64_t per = kRouteThreads / 8;
     int64_t qwg = (total + per - 1) / per;
     if (qwg > 256 * 16) qwg = 256 * 16;
-    hipLaunchKernelGGL(route_quantize_kernel, dim3((unsigned)(1 + qwg)), dim3(kRouteThreads), 0,
+    hipLaunchKernelGGL(route_quantize_kernel, dim3((unsigned)(n_expert + qwg)), dim3(kRouteThreads), 0,
                        stream, r, x, row_stride, codes, scales, nb, total, rotate ? 1 : 0);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
