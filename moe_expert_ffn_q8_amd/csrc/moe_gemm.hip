@@ -554,7 +554,11 @@ static_assert(2 * kR8Depth < 64, "vmcnt holds at most 63");
 // blocks in flight per wave) 4: 184 us (16: 235 us and more with the earlier
 // work order); Q8_PG_R8_CHUNK=32 with Q8_PG_R8_OCC=6 and depth 4 (three
 // workgroups per CU): 187 us; down workgroups of 4 waves
-// (Q8_PG_R8_DN_WAVES=4, chunk 32, four workgroups per CU): 191 us.  Per
+// (Q8_PG_R8_DN_WAVES=4, chunk 32, four workgroups per CU): 191 us; 16-wave
+// down workgroups (512 columns, one per CU): 188 us, no change.  A second
+// form of the K loop for tiles of at most 8 slots (the second tile of most
+// experts with more than 32 slots), rescaling only the accumulators of its
+// rows: 189 against 185 us (116 VGPRs, twice the code).  Per
 // workgroup timestamps (s_memrealtime) put a workgroup's life at about 10 us
 // waiting for its first blocks, 21 us in the K loop and 8 us in the epilogue
 // (4 of them waiting for the last wave); the HBM reads (483 MB of the 428 MB
