@@ -161,10 +161,12 @@ def test_stages_decode_shapes(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
 
 
 @pytest.mark.parametrize("n_tok,n_embd,n_ff,n_expert,n_used", [
-    (40, 512, 256, 16, 4), (200, 256, 128, 8, 8), (17, 1024, 384, 32, 2)])
+    (40, 512, 256, 16, 4), (200, 256, 128, 8, 8), (17, 1024, 384, 32, 2),
+    (700, 256, 128, 16, 8), (1100, 128, 128, 64, 8)])
 def test_stages_prefill(q, orc, n_tok, n_embd, n_ff, n_expert, n_used):
     """More than 16 tokens: the grouped matrix-core path; its routing is the
-    ascending (t,u) order within each expert."""
+    ascending (t,u) order within each expert (5600 and 8800 slots: the
+    routing reads the ids in 2 and 3 passes of 4096)."""
     print(f"case: stages prefill {n_tok} {n_embd} {n_ff} {n_expert} {n_used}", flush=True)
     c = _case(orc, n_tok, n_embd, n_ff, n_expert, n_used, f"stg-p-{n_tok}-{n_embd}")
     _stages(q, orc, c, n_embd, n_ff, n_expert)
@@ -234,7 +236,7 @@ def _r8_layer(q, c, n_embd, n_ff, n_expert):
 
 @pytest.mark.parametrize("n_tok,n_embd,n_ff,n_expert,n_used,full", [
     (1, 2048, 768, 128, 8, True), (16, 2048, 768, 128, 8, True), (3, 768, 256, 32, 8, False),
-    (40, 512, 256, 16, 4, False)])
+    (40, 512, 256, 16, 4, False), (700, 256, 128, 16, 8, False)])
 def test_stages_r8(q, orc, n_tok, n_embd, n_ff, n_expert, n_used, full):
     """The expert FFN over R8 expert weights (decode kernels up to 16 tokens,
     the matrix-core path above): sums of both products, q(h), the routing the
