@@ -30,7 +30,10 @@
 // launch, level with the native-layout matrix-core engine (27.1 us).  What
 // cost time on the way: activation loads made conditional (the compiler then
 // waited for each in turn: 35 us), staging before the weight issue (31 us);
-// more waves per unit and 8 or 16 waves per workgroup did not help.
+// more waves per unit and 8 or 16 waves per workgroup did not help.  The
+// batch-1 engine's weight stream (one group per wave, contiguous 1 KB slices)
+// with 4 v_dot4 and a DPP swap per slice and token instead of the matrix core
+// (8 tokens, 71 VGPRs) took 40 us: per 1 KB slice the VALU work grows with m.
 #include <string.h>
 
 #include "q8_device.h"
