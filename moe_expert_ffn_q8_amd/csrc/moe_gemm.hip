@@ -11,7 +11,7 @@
 // small GEMMs and run on the matrix cores.
 //
 // One call:
-//  1. routing (one workgroup): slot counts per expert, exclusive offsets, the
+//  1. routing (one workgroup per expert): slot counts per expert, exclusive offsets, the
 //     slots grouped by expert, and a tile table -- expert e's c_e slots make
 //     ceil(c_e / 32) tiles of at most 32 slots.  Slots with an out-of-range id
 //     are left out; they set the error word and (up_gate call) get NaN h rows.
